@@ -1,0 +1,113 @@
+"""Planted mistakes in the oracle (CPU only): each must be caught by at least one pin.
+
+Every mutant replaces one oracle function with a plausible wrong version (a dropped term, a wrong
+sign, a wrong index or a transposed operand). The pins are re-run with the mutant patched in, and
+the test passes only if some pin fails. The oracle itself is never modified on disk.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import lla_oracle as O
+import tests.test_oracle_pins as P
+
+
+def _encode_no_centre(x_stack, E, mu=None):
+    return np.asarray(x_stack, np.float64) @ np.asarray(E, np.float64).T
+
+
+def _encode_plus_mu(x_stack, E, mu=None):
+    x = np.asarray(x_stack, np.float64)
+    if mu is not None:
+        x = x + mu
+    return x @ np.asarray(E, np.float64).T
+
+
+def _reconstruct_no_mu(z, W_t, mu_t=None):
+    return np.asarray(z, np.float64) @ np.asarray(W_t, np.float64).T
+
+
+def _softmax_no_scale(q, K, V, scale):
+    return _orig["softmax_attention"](q, K, V, 1.0)
+
+
+def _softmax_sqrt_scale(q, K, V, scale):
+    return _orig["softmax_attention"](q, K, V, math.sqrt(scale))
+
+
+def _softmax_lse_no_max(q, K, V, scale):
+    o, lse = _orig["softmax_attention"](q, K, V, scale)
+    if K.shape[0] == 0:
+        return o, lse
+    return o, lse - float(np.max(scale * (np.asarray(K) @ np.asarray(q))))
+
+
+def _softmax_drop_last_key(q, K, V, scale):
+    return _orig["softmax_attention"](q, np.asarray(K)[:-1], np.asarray(V)[:-1], scale)
+
+
+def _loop_slices_wrong_loop(variant, Wk, Wv, mu_k, mu_v, t, h, H, d):
+    T = Wk.shape[0]
+    return _orig["_loop_slices"](variant, Wk, Wv, mu_k, mu_v, (t + 1) % T, h, H, d)
+
+
+def _loop_slices_wrong_head(variant, Wk, Wv, mu_k, mu_v, t, h, H, d):
+    return _orig["_loop_slices"](variant, Wk, Wv, mu_k, mu_v, t, (h + 1) % H, H, d)
+
+
+def _loop_slices_2d_head_major(variant, Wk, Wv, mu_k, mu_v, t, h, H, d):
+    if variant != "2d":
+        return _orig["_loop_slices"](variant, Wk, Wv, mu_k, mu_v, t, h, H, d)
+    wk, wv, _, _ = _orig["_loop_slices"](variant, Wk, Wv, mu_k, mu_v, t, h, H, d)
+    T = Wk.shape[0]
+    base = h * T * d + t * d          # (head, loop, channel) order instead of (loop, head, channel)
+    muk = None if mu_k is None else mu_k[base:base + d]
+    muv = None if mu_v is None else mu_v[base:base + d]
+    return wk, wv, muk, muv
+
+
+_orig = {
+    "encode_stack": O.encode_stack,
+    "reconstruct": O.reconstruct,
+    "softmax_attention": O.softmax_attention,
+    "_loop_slices": O._loop_slices,
+}
+
+MUTANTS = {
+    "encode drops the centring": ("encode_stack", _encode_no_centre),
+    "encode adds mu instead of subtracting": ("encode_stack", _encode_plus_mu),
+    "reconstruct drops mu_t": ("reconstruct", _reconstruct_no_mu),
+    "decode reads the next head's factors": ("_loop_slices", _loop_slices_wrong_head),
+    "softmax ignores the scale": ("softmax_attention", _softmax_no_scale),
+    "softmax uses sqrt(scale)": ("softmax_attention", _softmax_sqrt_scale),
+    "lse drops the running max": ("softmax_attention", _softmax_lse_no_max),
+    "attention drops the last key": ("softmax_attention", _softmax_drop_last_key),
+    "decode reads loop t+1's factors": ("_loop_slices", _loop_slices_wrong_loop),
+    "2d mu indexed head-major": ("_loop_slices", _loop_slices_2d_head_major),
+}
+
+PINS = [
+    lambda: P.test_full_rank_identity_per_head(True, True),
+    lambda: P.test_full_rank_identity_per_head(False, False),
+    P.test_full_rank_identity_2d,
+    P.test_final_loop_reuse_special_case,
+    P.test_zero_query_gives_mean_value,
+    P.test_sharp_query_selects_best_key,
+    P.test_empty_context_and_length_clamp,
+    P.test_prefill_full_rank_identity_causal_offset,
+    P.test_brute_force_tiny,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught.append(pin)
+    assert caught, f"no pin caught the mutant: {name}"
