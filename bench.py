@@ -1,0 +1,283 @@
+"""Decode-step throughput of the LLA latent-cache kernels on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload capacity]
+
+Default workload ("capacity"): a 24-layer looped model with H=16 heads of width 128, T=4 loops,
+per-head latent ranks r_k = r_v = 24 (21.3x compression), B=768 sequences at 4096 cached tokens,
+bf16 latents: 116 GB of latent cache resident in HBM, filled from a seeded device generator (the
+paper's capacity test also fabricates the decode cache; Section 7).
+
+One step = one decode token for every sequence: for each loop t and layer l, one
+lla_attend_decode read of that layer's latents (with the token's own loop-t K/V), then one
+lla_encode per layer folding the token's T per-loop K/V into slot N. Sequence lengths stay at N,
+so every step reads exactly N latents per (sequence, head). Inputs are resident before timing.
+
+Prints one JSON line. value = tokens/s = B / step time. roofline: the decode kernel's average
+launch time from HIP events on its stream, latent bytes per launch / that time, against 8 TB/s.
+cpu_baseline: the CPU oracle (explicit reconstruction, float64) timed on a bounded sample of the
+same step on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "LLA decode-attn tokens/s + latent HBM GB/s (% of peak), bf16, 4k ctx, 1 GPU"
+DECODE_SRC = os.path.join(ROOT, "decode_attention_lla_amd", "csrc", "decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_capacity_traffic.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="capacity",
+                    choices=["capacity", "ouro_layer", "deep_loop"])
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 4 GiB device copy (scale reference for HBM counters)")
+    return ap.parse_args()
+
+
+def source_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """Per-launch HBM bytes of the decode kernel from committed counter runs, if still valid."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("decode_src_sha256_16") != source_sha(DECODE_SRC):
+        return None  # the kernel changed since the counters were taken
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the LLA latent-cache path runs on a single MI355X "
+              "here (see DESIGN.md for how it would shard); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decode_attention_lla_amd import lla, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lla.library()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    s = synth.CASES[args.workload]
+    D = args.layers or s.D
+    B, H, d, T, rk, rv, N = s.B, s.H, s.d, s.T, s.r_k, s.r_v, s.N
+    n_max = N + 1
+    bf = torch.bfloat16
+    desc = lla.make_desc(lla.LLA_PER_HEAD, lla.LLA_BF16, H, d, T, rk, rv, n_max)
+    print(f"# workload {s.name}: D={D} H={H} d={d} T={T} r=({rk},{rv}) B={B} N={N}", file=sys.stderr, flush=True)
+
+    # ---- resident inputs --------------------------------------------------------------------
+    t0 = time.time()
+    zk, zv, Wk, Wv, Ek, Ev = [], [], [], [], [], []
+    for l in range(D):
+        zk.append(synth.device_normal_(torch.empty(B, H, n_max, rk, dtype=bf, device="cuda"),
+                                       synth.seed(s.case, synth.SEED_ZK, l)))
+        zv.append(synth.device_normal_(torch.empty(B, H, n_max, rv, dtype=bf, device="cuda"),
+                                       synth.seed(s.case, synth.SEED_ZV, l)))
+        wk = synth.orthonormal_W(T, H, d, rk, synth.seed(s.case, synth.SEED_WK, l), "bf16")
+        wv = synth.orthonormal_W(T, H, d, rv, synth.seed(s.case, synth.SEED_WV, l), "bf16")
+        Wk.append(torch.from_numpy(wk).to(bf).cuda())
+        Wv.append(torch.from_numpy(wv).to(bf).cuda())
+        Ek.append(torch.from_numpy(synth.pinv_E_from_W(wk, "bf16")).to(bf).cuda())
+        Ev.append(torch.from_numpy(synth.pinv_E_from_W(wv, "bf16")).to(bf).cuda())
+    q = synth.device_normal_(torch.empty(T, D, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_Q))
+    kself = synth.device_normal_(torch.empty(T, D, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF))
+    vself = synth.device_normal_(torch.empty(T, D, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF) + 1)
+    xk = synth.device_normal_(torch.empty(D, B, 1, T, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_XK))
+    xv = synth.device_normal_(torch.empty(D, B, 1, T, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_XV))
+    out = torch.empty(T, D, B, H, d, dtype=bf, device="cuda")
+    lens = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    ws = lla.workspace(desc, B, 1)
+    torch.cuda.synchronize()
+    resident = sum(t.numel() * t.element_size() for t in zk + zv)
+    print(f"# resident latents {resident / 1e9:.2f} GB, filled in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    ev = {}
+
+    def step(record=None):
+        for t in range(T):
+            for l in range(D):
+                if record is not None:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                lla.lla_attend_decode(desc, B, t, q[t, l], zk[l], zv[l], lens, Wk[l], Wv[l], None, None,
+                                      kself[t, l], vself[t, l], out[t, l], None, ws, stream)
+                if record is not None:
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e1.record(stream)
+                    record.append((e0, e1))
+        for l in range(D):
+            lla.lla_encode(desc, B, 1, xk[l], xv[l], Ek[l], Ev[l], None, None, lens, zk[l], zv[l], stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region -------------------------------------------------------------------------
+    pairs = []
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(pairs)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    launch_ms = np.array([a.elapsed_time(b) for a, b in pairs])
+    avg_launch_ms = float(np.mean(launch_ms))
+    print(f"# {args.steps} steps: {ms_step:.3f} ms/step; decode launch avg {avg_launch_ms * 1e3:.1f} us "
+          f"(min {launch_ms.min() * 1e3:.1f}, max {launch_ms.max() * 1e3:.1f})", file=sys.stderr, flush=True)
+
+    if args.copy_probe:
+        a = torch.empty(2 ** 31, dtype=bf, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    tokens_per_s = B / (ms_step / 1e3)
+    latent_bytes = B * H * N * (rk + rv) * 2  # per launch: every (sequence, head, token) latent pair
+    achieved = latent_bytes / (avg_launch_ms / 1e3) / 1e9
+    traffic = load_traffic() if args.workload == "capacity" and D == s.D else None
+
+    # ---- CPU oracle baseline --------------------------------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, s, D, zk, zv, Wk, Wv, Ek, Ev, q, kself, vself, xk, xv, lens)
+
+    res = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{s.name}: {D} layers, H={H}, d_head={d}, T={T}, r_k={rk}, r_v={rv}, "
+                        f"B={B}, N={N} cached tokens, bf16 latents",
+            "layers": D, "batch": B, "context": N, "heads": H, "d_head": d, "loops": T,
+            "r_k": rk, "r_v": rv, "variant": "per_head",
+            "compression": round(2 * T * d / (rk + rv), 2),
+            "resident_latent_bytes": resident,
+            "reads_per_step": D * T, "encodes_per_step": D,
+        },
+        "latent_GBps": round(achieved, 1),
+        "latent_frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"decode_partial_kernel<BF16,{rk},{rv}> (one launch per read)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": latent_bytes,
+            "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(args, s, D, zk, zv, Wk, Wv, Ek, Ev, q, kself, vself, xk, xv, lens):
+    """The CPU oracle on one sequence's decode step (all layers and loops, then the encodes),
+    stopped after about --cpu-seconds and extrapolated to the full step; tokens/s = 1 / step time
+    (each step emits one token for this sequence)."""
+    from oracle import lla_oracle as O
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+
+    T, N = s.T, s.N
+    b = 0
+    sl = slice(b, b + 1)
+    host = lambda t: t[sl].float().cpu().numpy()  # noqa: E731
+    lens_h = np.array([N], np.int32)
+    reads = 0
+    t_read = 0.0
+    enc_time = 0.0
+    budget = args.cpu_seconds
+    cache = {}
+    for t in range(T):
+        for l in range(D):
+            if l not in cache:
+                cache[l] = (host(zk[l]), host(zv[l]), Wk[l].float().cpu().numpy(), Wv[l].float().cpu().numpy())
+            zkh, zvh, wk, wv = cache[l]
+            qh = q[t, l][sl].float().cpu().numpy()
+            ks = kself[t, l][sl].float().cpu().numpy()
+            vs = vself[t, l][sl].float().cpu().numpy()
+            c0 = time.perf_counter()
+            O.attend_decode(qh, zkh, zvh, wk, wv, t, lens_h, None, None, ks, vs)
+            t_read += time.perf_counter() - c0
+            reads += 1
+            if t_read > budget:
+                break
+        if t_read > budget:
+            break
+    # one layer's encode for this sequence, timed and scaled by the layer count
+    zkh, zvh, _, _ = cache[0]
+    xkh = xk[0][sl].float().cpu().numpy()
+    xvh = xv[0][sl].float().cpu().numpy()
+    c0 = time.perf_counter()
+    O.encode_into_cache(zkh, zvh, xkh, xvh, Ek[0].float().cpu().numpy(), Ev[0].float().cpu().numpy(), lens_h)
+    enc_time = time.perf_counter() - c0
+    step_s = t_read / reads * (T * D) + enc_time * D
+    return {
+        "value": round(1.0 / step_s, 4),
+        "unit": "tokens/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"sequence 0 of {s.B}: {reads} of {T * D} loop reads (explicit reconstruction, "
+                  f"float64, {t_read:.1f} s) plus one layer's encode, extrapolated to the full "
+                  f"step of one sequence ({step_s:.1f} s per token)",
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+if __name__ == "__main__":
+    main()

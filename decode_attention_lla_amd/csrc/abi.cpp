@@ -1,0 +1,197 @@
+// C ABI of the LLA latent-cache library: host-side validation, planning and dispatch.
+// Declarations and the contract of every function are in include/lla.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "lla.h"
+#include "lla_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Null is allowed for optional pointers; any non-null device pointer must be 16-byte aligned.
+bool opt_ok(const void* p) { return p == nullptr || aligned16(p); }
+bool req_ok(const void* p) { return p != nullptr && aligned16(p); }
+
+bool desc_ok(const lla_desc* d) {
+  if (d == nullptr) return false;
+  if (d->variant != LLA_PER_HEAD && d->variant != LLA_2D) return false;
+  if (d->dtype != LLA_F32 && d->dtype != LLA_BF16) return false;
+  if (d->H <= 0 || d->T <= 0 || d->r_k <= 0 || d->r_v <= 0 || d->n_max <= 0) return false;
+  if (d->d_head <= 0 || d->d_head > 256 || (d->d_head % 8) != 0) return false;
+  if (!(d->scale >= 0.f) || std::isinf(d->scale)) return false;
+  // every flattened index below stays inside int32 per sequence
+  const int64_t per_seq = static_cast<int64_t>(d->H) * d->n_max * (d->r_k > d->r_v ? d->r_k : d->r_v);
+  if (per_seq >= (int64_t(1) << 31)) return false;
+  return true;
+}
+
+float scale_log2(const lla_desc* d) {
+  const float s = d->scale > 0.f ? d->scale : 1.0f / std::sqrt(static_cast<float>(d->d_head));
+  return s * 1.4426950408889634f;
+}
+
+lla_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return LLA_OK;
+  if (e == hipErrorNotSupported) return LLA_ERR_UNSUPPORTED;
+  return LLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lla_abi_version(void) { return LLA_ABI_VERSION; }
+
+const char* lla_status_string(lla_status s) {
+  switch (s) {
+    case LLA_OK: return "ok";
+    case LLA_ERR_INVALID_ARG: return "invalid argument";
+    case LLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LLA_ERR_WORKSPACE: return "workspace too small";
+    case LLA_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+size_t lla_workspace_bytes(const lla_desc* desc, int32_t B, int32_t C) {
+  if (!desc_ok(desc) || B <= 0 || C <= 0) return 0;
+  if (C == 1) return lla::decode_workspace_bytes(*desc, B);
+  return lla::prefill_workspace_bytes(*desc, B, C);
+}
+
+lla_status lla_encode(const lla_desc* desc, int32_t B, int32_t C, const void* xk, const void* xv,
+                      const void* Ek, const void* Ev, const void* mu_k, const void* mu_v,
+                      const int32_t* pos, void* zk, void* zv, void* stream) {
+  if (!desc_ok(desc) || B <= 0 || C <= 0) return LLA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * C * desc->T * desc->H * desc->d_head >= (int64_t(1) << 40))
+    return LLA_ERR_INVALID_ARG;
+  if (C > desc->n_max) return LLA_ERR_INVALID_ARG;
+  if (!req_ok(xk) || !req_ok(xv) || !req_ok(Ek) || !req_ok(Ev) || !req_ok(pos) || !req_ok(zk) ||
+      !req_ok(zv) || !opt_ok(mu_k) || !opt_ok(mu_v))
+    return LLA_ERR_INVALID_ARG;
+  if (!lla::encode_supported(desc->dtype, desc->r_k) || !lla::encode_supported(desc->dtype, desc->r_v))
+    return LLA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  lla::EncodeParams p{};
+  p.B = B;
+  p.C = C;
+  p.T = desc->T;
+  p.n_max = desc->n_max;
+  p.pos = pos;
+  if (desc->variant == LLA_PER_HEAD) {
+    p.H = desc->H;
+    p.d = desc->d_head;
+  } else {  // LLA-2D: the (loop, head, channel) stack of one token is T runs of H*d values
+    p.H = 1;
+    p.d = desc->H * desc->d_head;
+  }
+  p.x = xk;
+  p.E = Ek;
+  p.mu = mu_k;
+  p.z = zk;
+  p.r = desc->r_k;
+  lla_status st = from_hip(lla::launch_encode(p, desc->dtype, s));
+  if (st != LLA_OK) return st;
+  p.x = xv;
+  p.E = Ev;
+  p.mu = mu_v;
+  p.z = zv;
+  p.r = desc->r_v;
+  return from_hip(lla::launch_encode(p, desc->dtype, s));
+}
+
+lla_status lla_attend_decode(const lla_desc* desc, int32_t B, int32_t t, const void* q,
+                             const void* zk, const void* zv, const int32_t* seq_lens,
+                             const void* Wk, const void* Wv, const void* mu_k, const void* mu_v,
+                             const void* k_self, const void* v_self, void* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (!desc_ok(desc) || B <= 0 || t < 0 || t >= desc->T) return LLA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * desc->H >= (int64_t(1) << 31) / 64) return LLA_ERR_INVALID_ARG;
+  if (!req_ok(q) || !req_ok(zk) || !req_ok(zv) || !req_ok(Wk) || !req_ok(Wv) || !req_ok(out))
+    return LLA_ERR_INVALID_ARG;
+  if (!opt_ok(seq_lens) || !opt_ok(mu_k) || !opt_ok(mu_v) || !opt_ok(k_self) || !opt_ok(v_self) ||
+      !opt_ok(lse) || !opt_ok(ws))
+    return LLA_ERR_INVALID_ARG;
+  if ((k_self == nullptr) != (v_self == nullptr)) return LLA_ERR_INVALID_ARG;
+  if (!lla::decode_supported(desc->variant, desc->dtype, desc->r_k, desc->r_v))
+    return LLA_ERR_UNSUPPORTED;
+  const size_t need = lla::decode_workspace_bytes(*desc, B);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return LLA_ERR_WORKSPACE;
+
+  lla::DecodeParams p{};
+  p.q = q;
+  p.zk = zk;
+  p.zv = zv;
+  p.seq_lens = seq_lens;
+  p.Wk = Wk;
+  p.Wv = Wv;
+  p.mu_k = mu_k;
+  p.mu_v = mu_v;
+  p.k_self = k_self;
+  p.v_self = v_self;
+  p.out = out;
+  p.lse = lse;
+  p.ws = static_cast<float*>(ws);
+  p.B = B;
+  p.H = desc->H;
+  p.d = desc->d_head;
+  p.T = desc->T;
+  p.t = t;
+  p.n_max = desc->n_max;
+  p.r_k = desc->r_k;
+  p.r_v = desc->r_v;
+  p.rows_per_seq = 1;
+  p.causal = 0;
+  p.variant = desc->variant;
+  p.scale_log2 = scale_log2(desc);
+  lla::decode_plan(*desc, B, &p.splits, &p.chunk);
+  return from_hip(lla::launch_decode(p, desc->dtype, static_cast<hipStream_t>(stream)));
+}
+
+lla_status lla_attend_prefill(const lla_desc* desc, int32_t B, int32_t C, int32_t t,
+                              const void* q, const void* zk, const void* zv,
+                              const int32_t* ctx_lens, const void* Wk, const void* Wv,
+                              const void* mu_k, const void* mu_v, void* out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (!desc_ok(desc) || B <= 0 || C <= 0 || t < 0 || t >= desc->T) return LLA_ERR_INVALID_ARG;
+  if (C > desc->n_max) return LLA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * C * desc->H >= (int64_t(1) << 31) / 64) return LLA_ERR_INVALID_ARG;
+  if (!req_ok(q) || !req_ok(zk) || !req_ok(zv) || !req_ok(ctx_lens) || !req_ok(Wk) ||
+      !req_ok(Wv) || !req_ok(out))
+    return LLA_ERR_INVALID_ARG;
+  if (!opt_ok(mu_k) || !opt_ok(mu_v) || !opt_ok(ws)) return LLA_ERR_INVALID_ARG;
+  if (!lla::prefill_supported(desc->variant, desc->dtype, desc->r_k, desc->r_v))
+    return LLA_ERR_UNSUPPORTED;
+  const size_t need = lla::prefill_workspace_bytes(*desc, B, C);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return LLA_ERR_WORKSPACE;
+
+  lla::PrefillParams p{};
+  p.q = q;
+  p.zk = zk;
+  p.zv = zv;
+  p.ctx_lens = ctx_lens;
+  p.Wk = Wk;
+  p.Wv = Wv;
+  p.mu_k = mu_k;
+  p.mu_v = mu_v;
+  p.out = out;
+  p.ws = ws;
+  p.B = B;
+  p.C = C;
+  p.H = desc->H;
+  p.d = desc->d_head;
+  p.T = desc->T;
+  p.t = t;
+  p.n_max = desc->n_max;
+  p.r_k = desc->r_k;
+  p.r_v = desc->r_v;
+  p.variant = desc->variant;
+  p.scale_log2 = scale_log2(desc);
+  return from_hip(lla::launch_prefill(p, desc->dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

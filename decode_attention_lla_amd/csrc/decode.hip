@@ -1,0 +1,346 @@
+// Absorbed latent decode attention (per-head LLA, and LLA-2D on the VALU path).
+//
+// Method: O'Neill & Reid, "Looped Latent Attention", arXiv 2607.15456. Section 3, Eq. 3 rebuilds
+// loop t as k_t = W^K_t z^K + mu^K_t (column form). Section 7 ("Per-head LLA versus LLA-2D at
+// inference") notes that the score is bilinear, so q . k_t = (W^K_t^T q) . z^K + q . mu^K_t, and
+// that sum_i p_i W^V_t z^V_i = W^V_t sum_i p_i z^V_i. The kernels below therefore
+//   1. form q~ = scale*log2(e) * W^K_t^T q and beta = scale*log2(e) * q . mu^K_t once per (b, h);
+//   2. stream the bf16/fp32 latents of one (b, h, token range) from HBM, one token per LPT lanes,
+//      computing base-2 scores q~ . z^K_i + beta with a per-lane online softmax;
+//   3. accumulate sum_i 2^(s_i - m) z^V_i in r_v-wide fp32 registers (latent space);
+//   4. merge lanes, then either write a split partial (m, l, a) or finish: merge the optional
+//      self token, apply W^V_t once, add l * mu^V_t, normalise and store o and lse.
+// The reconstructed K/V of cached tokens are never formed.
+#include "lla_device.h"
+#include "lla_internal.h"
+
+namespace lla {
+namespace {
+
+// Largest growth of the running maximum tolerated before rescaling (base-2 units). Weights are
+// at most 2^kLazy = 256 relative to the stored maximum, which float32 sums absorb without loss of
+// range; skipping most rescales keeps the branch rare.
+constexpr float kLazy = 8.0f;
+
+// First latent row of sequence `seq` (head h): per-head cache [B][H][n_max][r], 2D [B][n_max][r].
+__device__ __forceinline__ size_t latent_row(const DecodeParams& p, int seq, int h) {
+  return p.variant == LLA_2D ? static_cast<size_t>(seq) * p.n_max
+                             : (static_cast<size_t>(seq) * p.H + h) * p.n_max;
+}
+
+// Keys visible to query row `row` (see DecodeParams), clamped to [0, n_max].
+__device__ __forceinline__ int row_keys(const DecodeParams& p, int row) {
+  const int seq = row / p.rows_per_seq;
+  int n = p.seq_lens != nullptr ? p.seq_lens[seq] : p.n_max;
+  if (p.causal) n += row - seq * p.rows_per_seq + 1;
+  return min(max(n, 0), p.n_max);
+}
+
+// Offset of mu_t restricted to head h: per-head [H][T*d] at (h, t*d); 2D [T*H*d] at t*H*d + h*d.
+__device__ __forceinline__ size_t mu_offset(const DecodeParams& p, int h) {
+  return p.variant == LLA_2D ? (static_cast<size_t>(p.t) * p.H + h) * p.d
+                             : (static_cast<size_t>(h) * p.T + p.t) * p.d;
+}
+
+// W_t restricted to head h: per-head [T][H][d][r] at (t, h); 2D [T][H*d][r] at rows t*H*d + h*d.
+// Both are element offset (t*H + h)*d*r.
+__device__ __forceinline__ size_t w_offset(const DecodeParams& p, int h, int r) {
+  return (static_cast<size_t>(p.t) * p.H + h) * p.d * r;
+}
+
+// Finish one (b, h): merge the latent part (M, l, a[] in LDS, base-2, relative to M) with the
+// optional self token, apply W^V_t once, add mu^V_t, normalise, store. Runs on one wave.
+template <class S>
+__device__ void finish_unit(const DecodeParams& p, int b, int h, float M, float l,
+                            const float* a_s, const float* q_s, int lane) {
+  const size_t bh = static_cast<size_t>(b) * p.H + h;
+  float s_self = kNegInf;
+  if (p.k_self != nullptr) {
+    float part = 0.f;
+    for (int j = lane; j < p.d; j += 64) part += q_s[j] * ld<S>(p.k_self, bh * p.d + j);
+    s_self = wave_sum(part) * p.scale_log2;
+  }
+  const float M2 = fmaxf(M, s_self);
+  const float f_lat = (M == kNegInf) ? 0.f : fast_exp2(M - M2);
+  const float p_self = (s_self == kNegInf) ? 0.f : fast_exp2(s_self - M2);
+  const float den = l * f_lat + p_self;
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const size_t woff = w_offset(p, h, p.r_v);
+  const size_t moff = mu_offset(p, h);
+  for (int j = lane; j < p.d; j += 64) {
+    float o = 0.f;
+    const size_t row = woff + static_cast<size_t>(j) * p.r_v;
+    for (int r = 0; r < p.r_v; ++r) o += ld<S>(p.Wv, row + r) * a_s[r];
+    if (p.mu_v != nullptr) o += l * ld<S>(p.mu_v, moff + j);
+    o *= f_lat;
+    if (p.v_self != nullptr) o += p_self * ld<S>(p.v_self, bh * p.d + j);
+    st<S>(p.out, bh * p.d + j, o * inv);
+  }
+  if (p.lse != nullptr && lane == 0)
+    p.lse[bh] = den > 0.f ? (M2 + fast_log2(den)) * kLn2 : kNegInf;
+}
+
+// One wave per (b, h, split). LPT lanes share a token; each holds EK = RK/LPT K elements and
+// EV = RV/LPT V elements. U tiles of 64/LPT tokens are loaded before any is consumed.
+template <class S, int RK, int RV, int LPT, int U>
+__global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
+  constexpr int EK = RK / LPT;
+  constexpr int EV = RV / LPT;
+  constexpr int TPW = 64 / LPT;
+  constexpr int VK = EK * S::kBytes / 16;
+  constexpr int VV = EV * S::kBytes / 16;
+  static_assert(EK * LPT == RK && EV * LPT == RV, "rank must split evenly over lanes");
+  static_assert(VK * 16 == EK * S::kBytes && VV * 16 == EV * S::kBytes, "16-byte fragments");
+
+  __shared__ float q_s[256];
+  __shared__ float qt_s[RK];
+  __shared__ float a_s[RV];
+
+  const int lane = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int split = unit % p.splits;
+  const int bh = unit / p.splits;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+
+  const int nb = row_keys(p, b);
+  const int tb = split * p.chunk;
+  const int te = min(nb, tb + p.chunk);
+
+  // --- 1. query absorption ------------------------------------------------------------------
+  const size_t qoff = static_cast<size_t>(bh) * p.d;
+  for (int j = lane; j < p.d; j += 64) q_s[j] = ld<S>(p.q, qoff + j);
+  __syncthreads();
+  const size_t wk = w_offset(p, h, RK);
+  for (int r = lane; r < RK; r += 64) {
+    float acc = 0.f;
+    for (int j = 0; j < p.d; ++j) acc += ld<S>(p.Wk, wk + static_cast<size_t>(j) * RK + r) * q_s[j];
+    qt_s[r] = acc * p.scale_log2;
+  }
+  float beta = 0.f;
+  if (p.mu_k != nullptr) {
+    const size_t moff = mu_offset(p, h);
+    float part = 0.f;
+    for (int j = lane; j < p.d; j += 64) part += q_s[j] * ld<S>(p.mu_k, moff + j);
+    beta = wave_sum(part) * p.scale_log2;
+  }
+  __syncthreads();
+
+  const int sub = lane % LPT;
+  const int grp = lane / LPT;
+  float qt[EK];
+#pragma unroll
+  for (int e = 0; e < EK; ++e) qt[e] = qt_s[sub * EK + e];
+
+  // --- 2-3. latent stream with online softmax -------------------------------------------------
+  const size_t lrow = latent_row(p, b / p.rows_per_seq, h);
+  const char* zkp = static_cast<const char*>(p.zk) + (lrow * RK + sub * EK) * S::kBytes;
+  const char* zvp = static_cast<const char*>(p.zv) + (lrow * RV + sub * EV) * S::kBytes;
+
+  float m = kNegInf;
+  float l = 0.f;
+  float acc[EV];
+#pragma unroll
+  for (int e = 0; e < EV; ++e) acc[e] = 0.f;
+
+  for (int t0 = tb; t0 < te; t0 += TPW * U) {
+    uint4 kr[U][VK];
+    uint4 vr[U][VV];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tok = t0 + u * TPW + grp;
+      ok[u] = tok < te;
+      if (ok[u]) {
+        const uint4* kp = reinterpret_cast<const uint4*>(zkp + static_cast<size_t>(tok) * RK * S::kBytes);
+        const uint4* vp = reinterpret_cast<const uint4*>(zvp + static_cast<size_t>(tok) * RV * S::kBytes);
+#pragma unroll
+        for (int i = 0; i < VK; ++i) kr[u][i] = kp[i];
+#pragma unroll
+        for (int i = 0; i < VV; ++i) vr[u][i] = vp[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < VK; ++i) kr[u][i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < VV; ++i) vr[u][i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float sc = 0.f;
+#pragma unroll
+      for (int e = 0; e < EK; ++e) sc += qt[e] * frag_elem<S>(kr[u], e);
+#pragma unroll
+      for (int o = 1; o < LPT; o <<= 1) sc += __shfl_xor(sc, o, 64);
+      sc += beta;
+      if (ok[u]) {
+        if (sc > m + kLazy) {
+          const float c = fast_exp2(m - sc);
+          l *= c;
+#pragma unroll
+          for (int e = 0; e < EV; ++e) acc[e] *= c;
+          m = sc;
+        }
+        const float pr = fast_exp2(sc - m);
+        l += pr;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) acc[e] += pr * frag_elem<S>(vr[u], e);
+      }
+    }
+  }
+
+  // --- 4. merge lanes ---------------------------------------------------------------------------
+  const float M = wave_max(m);
+  const float f = (m == kNegInf) ? 0.f : fast_exp2(m - M);
+  l *= f;
+#pragma unroll
+  for (int e = 0; e < EV; ++e) acc[e] *= f;
+#pragma unroll
+  for (int o = LPT; o < 64; o <<= 1) {
+    l += __shfl_xor(l, o, 64);
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+  }
+
+  if (p.splits > 1) {
+    float* w = p.ws + (static_cast<size_t>(bh) * p.splits + split) * (2 + RV);
+    if (lane == 0) {
+      w[0] = M;
+      w[1] = l;
+    }
+    if (lane < LPT) {
+#pragma unroll
+      for (int e = 0; e < EV; ++e) w[2 + lane * EV + e] = acc[e];
+    }
+    return;
+  }
+  if (lane < LPT) {
+#pragma unroll
+    for (int e = 0; e < EV; ++e) a_s[lane * EV + e] = acc[e];
+  }
+  __syncthreads();
+  finish_unit<S>(p, b, h, M, l, a_s, q_s, lane);
+}
+
+// Log-sum-exp merge of the S split partials of one (b, h), then the same finish. One wave.
+template <class S>
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
+  __shared__ float q_s[256];
+  __shared__ float a_s[512];
+  __shared__ float f_s[256];
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+  const int S_ = p.splits;
+  const int stride = 2 + p.r_v;
+  const float* w = p.ws + static_cast<size_t>(bh) * S_ * stride;
+
+  float mloc = kNegInf;
+  for (int s = lane; s < S_; s += 64) mloc = fmaxf(mloc, w[static_cast<size_t>(s) * stride]);
+  const float M = wave_max(mloc);
+  float lloc = 0.f;
+  for (int s = lane; s < S_; s += 64) {
+    const float ms = w[static_cast<size_t>(s) * stride];
+    const float fs = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
+    f_s[s] = fs;
+    lloc += fs * w[static_cast<size_t>(s) * stride + 1];
+  }
+  const float l = wave_sum(lloc);
+  for (int j = lane; j < p.d; j += 64) q_s[j] = ld<S>(p.q, static_cast<size_t>(bh) * p.d + j);
+  __syncthreads();
+  for (int r = lane; r < p.r_v; r += 64) {
+    float a = 0.f;
+    for (int s = 0; s < S_; ++s) a += f_s[s] * w[static_cast<size_t>(s) * stride + 2 + r];
+    a_s[r] = a;
+  }
+  __syncthreads();
+  finish_unit<S>(p, b, h, M, l, a_s, q_s, lane);
+}
+
+using PartialFn = void (*)(DecodeParams);
+
+template <class S, int RK, int RV, int LPT, int U>
+PartialFn partial_fn() {
+  return decode_partial_kernel<S, RK, RV, LPT, U>;
+}
+
+struct Entry {
+  int dtype, r_k, r_v;
+  PartialFn fn;
+};
+
+// Compiled (dtype, r_k, r_v) -> (lanes per token, tiles in flight).
+const Entry kTable[] = {
+    {LLA_BF16, 8, 8, partial_fn<BF16, 8, 8, 1, 4>()},
+    {LLA_BF16, 16, 16, partial_fn<BF16, 16, 16, 1, 4>()},
+    {LLA_BF16, 24, 24, partial_fn<BF16, 24, 24, 1, 2>()},
+    {LLA_BF16, 32, 32, partial_fn<BF16, 32, 32, 1, 2>()},
+    {LLA_BF16, 64, 64, partial_fn<BF16, 64, 64, 2, 2>()},
+    {LLA_BF16, 96, 96, partial_fn<BF16, 96, 96, 4, 2>()},
+    {LLA_BF16, 128, 128, partial_fn<BF16, 128, 128, 4, 2>()},
+    {LLA_BF16, 96, 160, partial_fn<BF16, 96, 160, 4, 2>()},
+    {LLA_BF16, 256, 256, partial_fn<BF16, 256, 256, 8, 2>()},
+    {LLA_F32, 8, 8, partial_fn<F32, 8, 8, 1, 2>()},
+    {LLA_F32, 16, 16, partial_fn<F32, 16, 16, 1, 2>()},
+    {LLA_F32, 24, 24, partial_fn<F32, 24, 24, 1, 1>()},
+    {LLA_F32, 32, 32, partial_fn<F32, 32, 32, 2, 1>()},
+    {LLA_F32, 64, 64, partial_fn<F32, 64, 64, 4, 1>()},
+    {LLA_F32, 96, 96, partial_fn<F32, 96, 96, 4, 1>()},
+    {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 8, 1>()},
+    {LLA_F32, 96, 160, partial_fn<F32, 96, 160, 8, 1>()},
+    {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 16, 1>()},
+};
+
+const Entry* find(int dtype, int r_k, int r_v) {
+  for (const Entry& e : kTable)
+    if (e.dtype == dtype && e.r_k == r_k && e.r_v == r_v) return &e;
+  return nullptr;
+}
+
+}  // namespace
+
+bool decode_supported(int variant, int dtype, int r_k, int r_v) {
+  if (variant != LLA_PER_HEAD && variant != LLA_2D) return false;
+  return find(dtype, r_k, r_v) != nullptr;
+}
+
+void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
+  // Enough waves to cover 256 CUs several times over, but no split shorter than 256 tokens.
+  const long units = static_cast<long>(B) * desc.H;
+  const int target_waves = 4096;
+  int s = static_cast<int>((target_waves + units - 1) / units);
+  const int max_by_len = desc.n_max / 256 > 0 ? desc.n_max / 256 : 1;
+  if (s > max_by_len) s = max_by_len;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  // tokens per split, a multiple of 128 so every tile but the last is full
+  int c = (desc.n_max + s - 1) / s;
+  c = (c + 127) / 128 * 128;
+  s = (desc.n_max + c - 1) / c;
+  *splits = s;
+  *chunk = c;
+}
+
+size_t decode_workspace_bytes(const lla_desc& desc, int B) {
+  int s, c;
+  decode_plan(desc, B, &s, &c);
+  if (s <= 1) return 0;
+  return static_cast<size_t>(B) * desc.H * s * (2 + desc.r_v) * sizeof(float);
+}
+
+hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream) {
+  const Entry* e = find(dtype, p.r_k, p.r_v);
+  if (e == nullptr) return hipErrorNotSupported;
+  const unsigned units = static_cast<unsigned>(p.B) * p.H * p.splits;
+  hipLaunchKernelGGL(e->fn, dim3(units), dim3(64), 0, stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.splits <= 1) return err;
+  if (dtype == LLA_BF16)
+    hipLaunchKernelGGL(decode_combine_kernel<BF16>, dim3(p.B * p.H), dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<F32>, dim3(p.B * p.H), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace lla

@@ -1,0 +1,86 @@
+// Device-side helpers shared by the LLA kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lla {
+
+// Storage tags. bf16 values are carried as raw 16-bit patterns.
+struct F32 {
+  using T = float;
+  static constexpr int kBytes = 4;
+};
+struct BF16 {
+  using T = uint16_t;
+  static constexpr int kBytes = 2;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bit pattern, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <class S>
+__device__ __forceinline__ float ld(const void* base, size_t i);
+template <>
+__device__ __forceinline__ float ld<F32>(const void* base, size_t i) {
+  return static_cast<const float*>(base)[i];
+}
+template <>
+__device__ __forceinline__ float ld<BF16>(const void* base, size_t i) {
+  return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[i]) << 16);
+}
+
+template <class S>
+__device__ __forceinline__ void st(void* base, size_t i, float v);
+template <>
+__device__ __forceinline__ void st<F32>(void* base, size_t i, float v) {
+  static_cast<float*>(base)[i] = v;
+}
+template <>
+__device__ __forceinline__ void st<BF16>(void* base, size_t i, float v) {
+  static_cast<uint16_t*>(base)[i] = f32_to_bf16(v);
+}
+
+// Element e of a register fragment holding E storage values as raw 16-byte words.
+template <class S>
+__device__ __forceinline__ float frag_elem(const uint4* f, int e);
+template <>
+__device__ __forceinline__ float frag_elem<F32>(const uint4* f, int e) {
+  const uint4 w = f[e >> 2];
+  const uint32_t x = (e & 3) == 0 ? w.x : (e & 3) == 1 ? w.y : (e & 3) == 2 ? w.z : w.w;
+  return __uint_as_float(x);
+}
+template <>
+__device__ __forceinline__ float frag_elem<BF16>(const uint4* f, int e) {
+  const uint4 w = f[e >> 3];
+  const int k = (e & 7) >> 1;
+  const uint32_t x = k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w;
+  return (e & 1) ? bf16_hi(x) : bf16_lo(x);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace lla

@@ -1,0 +1,76 @@
+// Host-side interface between the C ABI (abi.cpp) and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lla.h"
+
+namespace lla {
+
+// One decode read at loop t (lla_attend_decode after validation).
+struct DecodeParams {
+  const void* q;
+  const void* zk;
+  const void* zv;
+  const int32_t* seq_lens;
+  const void* Wk;
+  const void* Wv;
+  const void* mu_k;
+  const void* mu_v;
+  const void* k_self;
+  const void* v_self;
+  void* out;
+  float* lse;
+  float* ws;          // split partials [B][H][S][2 + r_v] (m, l, a[r_v]); unused when S == 1
+  int32_t B, H, d, T, t, n_max, r_k, r_v;
+  // Query rows: B rows per call; row i reads latent sequence i / rows_per_seq. For decode
+  // rows_per_seq = 1 and the key count is seq_lens[seq]. For prefill (causal = 1) row i is chunk
+  // row j = i % rows_per_seq and sees seq_lens[seq] + j + 1 latents. Counts clamp to [0, n_max].
+  int32_t rows_per_seq;
+  int32_t causal;
+  int32_t variant;    // LLA_PER_HEAD or LLA_2D
+  int32_t splits;     // S: token-range splits per (b, h)
+  int32_t chunk;      // tokens per split
+  float scale_log2;   // softmax scale * log2(e)
+};
+
+struct EncodeParams {
+  const void* x;      // [B][C][T][H][d]
+  const void* E;      // per-head [H][r][T*d]; 2D as per-head with H=1, d=H*d
+  const void* mu;     // per-head [H][T*d] or NULL
+  const int32_t* pos; // [B]
+  void* z;            // [B][H][n_max][r]
+  int32_t B, C, H, d, T, r, n_max;
+};
+
+struct PrefillParams {
+  const void* q;      // [B][C][H][d]
+  const void* zk;
+  const void* zv;
+  const int32_t* ctx_lens;
+  const void* Wk;
+  const void* Wv;
+  const void* mu_k;
+  const void* mu_v;
+  void* out;          // [B][C][H][d]
+  void* ws;
+  int32_t B, C, H, d, T, t, n_max, r_k, r_v, variant;
+  float scale_log2;
+};
+
+// Split heuristic shared by lla_workspace_bytes and lla_attend_decode.
+void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk);
+size_t decode_workspace_bytes(const lla_desc& desc, int B);
+size_t prefill_workspace_bytes(const lla_desc& desc, int B, int C);
+
+// Launchers: return hipSuccess, or hipErrorNotSupported when no kernel is compiled for the
+// requested (dtype, r_k, r_v); other errors come from the HIP launch.
+hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t s);
+hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t s);
+hipError_t launch_prefill(const PrefillParams& p, int dtype, hipStream_t s);
+
+bool decode_supported(int variant, int dtype, int r_k, int r_v);
+bool encode_supported(int dtype, int r);
+bool prefill_supported(int variant, int dtype, int r_k, int r_v);
+
+}  // namespace lla

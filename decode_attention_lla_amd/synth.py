@@ -252,3 +252,47 @@ def device_normal_(tensor, sd: int, std: float = 1.0):
     g.manual_seed(sd)
     tensor.normal_(0.0, std, generator=g)
     return tensor
+
+
+def random_case(variant: str, dtype: str, B: int, H: int, d: int, T: int, r_k: int, r_v: int,
+                n_max: int, sd: int, with_mu: bool = True, with_self: bool = True,
+                q_gain: float = 1.0):
+    """Generic seeded inputs for any shape (used by the shape sweeps).
+
+    Latents, queries and self K/V are N(0,1); W entries are N(0, 1/r) so rebuilt K/V have unit
+    variance; E entries are N(0, 1/(T*d)); mu (if any) has std 0.5. q_gain scales the query (a
+    gain of 8 sharpens the softmax). Returns float32 arrays holding storage values.
+    """
+    c = sd
+    if variant == "per_head":
+        zk_s, zv_s = (B, H, n_max, r_k), (B, H, n_max, r_v)
+        wk_s, wv_s = (T, H, d, r_k), (T, H, d, r_v)
+        ek_s, ev_s = (H, r_k, T * d), (H, r_v, T * d)
+        mu_s = (H, T * d)
+        K = T * d
+    else:
+        zk_s, zv_s = (B, n_max, r_k), (B, n_max, r_v)
+        wk_s, wv_s = (T, H * d, r_k), (T, H * d, r_v)
+        ek_s, ev_s = (r_k, T * H * d), (r_v, T * H * d)
+        mu_s = (T * H * d,)
+        K = T * H * d
+    out = {
+        "zk": normal(zk_s, seed(c, SEED_ZK), dtype),
+        "zv": normal(zv_s, seed(c, SEED_ZV), dtype),
+        "Wk": normal(wk_s, seed(c, SEED_WK), dtype, std=1 / math.sqrt(r_k)),
+        "Wv": normal(wv_s, seed(c, SEED_WV), dtype, std=1 / math.sqrt(r_v)),
+        "Ek": normal(ek_s, seed(c, SEED_EK), dtype, std=1 / math.sqrt(K)),
+        "Ev": normal(ev_s, seed(c, SEED_EV), dtype, std=1 / math.sqrt(K)),
+        "q": to_storage(q_gain * normal((T, B, H, d), seed(c, SEED_Q), "f32"), dtype),
+    }
+    if with_self:
+        kv = normal((2, T, B, H, d), seed(c, SEED_SELF), dtype)
+        out["k_self"], out["v_self"] = kv[0], kv[1]
+    else:
+        out["k_self"] = out["v_self"] = None
+    if with_mu:
+        m = normal((2,) + mu_s, seed(c, SEED_MU), dtype, std=0.5)
+        out["mu_k"], out["mu_v"] = m[0], m[1]
+    else:
+        out["mu_k"] = out["mu_v"] = None
+    return out

@@ -1,0 +1,157 @@
+/*
+ * lla.h - C ABI of the MI355X (gfx950) Looped Latent Attention (LLA) latent-cache library.
+ *
+ * Method: O'Neill & Reid, "Looped Latent Attention: Cross-Loop KV Compression for Looped
+ * Transformers" (arXiv 2607.15456). A looped (weight-tied) transformer writes T per-loop K/V
+ * vectors per token, layer and head. LLA stores one low-rank latent per (token, head, axis)
+ * instead, encoded once the token's last loop has run (Section 3, Eqs. 1-2), and rebuilds the
+ * loop-t K/V only when attention reads them (Eq. 3). This library performs that read in absorbed
+ * form (Section 7, "Per-head LLA versus LLA-2D at inference"): the K up-projection is moved to the
+ * query, and the V up-projection is applied once to the probability-weighted sum of latents.
+ *
+ * Conventions shared by every entry point
+ *   - Column-vector form of the paper's row form: E = W_down^T with shape [r][T*d_head], and
+ *     W_t = W_up,t with shape [d_head][r]. So z = E (x - mu) and x_hat_t = W_t z + mu_t.
+ *   - Loops are numbered t = 0 .. T-1 (the paper counts 1 .. T).
+ *   - Every array is dense, row-major and innermost-last, as written next to each argument.
+ *   - Storage dtype: desc->dtype (LLA_F32 or LLA_BF16) applies to every floating-point array
+ *     argument except `lse`, which is always float32. Accumulation is always float32. Stored
+ *     results are rounded to nearest-even once.
+ *   - Pointers marked [device] are HIP device addresses (or managed memory). Device pointers must
+ *     be 16-byte aligned. Pointers marked [host] are ordinary host memory.
+ *   - Ownership: the caller allocates and frees every buffer, including the workspace. The
+ *     library keeps no state between calls, allocates nothing, and never synchronises. Functions
+ *     are re-entrant.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default stream). All work is
+ *     enqueued on it in order. Calls return as soon as the work is enqueued.
+ *   - Errors: arguments are checked on the host before anything is enqueued. A failed check
+ *     returns a non-zero status and enqueues nothing. A failed kernel launch returns
+ *     LLA_ERR_HIP. Faults inside kernels surface at the caller's next synchronisation (HIP
+ *     semantics). Device-resident integer arrays (seq_lens, pos, ctx_lens) cannot be checked on
+ *     the host; their handling is stated per function and never reads or writes outside the
+ *     buffers described by desc.
+ */
+#ifndef LLA_H_
+#define LLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LLA_ABI_VERSION 1
+
+typedef enum {
+  LLA_OK = 0,
+  LLA_ERR_INVALID_ARG = 1, /* a null required pointer, bad size, t >= T, misaligned pointer */
+  LLA_ERR_UNSUPPORTED = 2, /* a (variant, dtype, d_head, r_k, r_v) combination not compiled in */
+  LLA_ERR_WORKSPACE = 3,   /* ws_bytes smaller than lla_workspace_bytes() */
+  LLA_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} lla_status;
+
+typedef enum { LLA_F32 = 0, LLA_BF16 = 1 } lla_dtype;
+
+/* LLA_PER_HEAD: one latent per (token, head, axis); Section 3, Eqs. 2-3.
+ * LLA_2D:       one latent per (token, axis) that rebuilds every head; Section 3, "The LLA-2D
+ *               variant". Its encoder input is the whole T*H*d_head stack, ordered (loop, head,
+ *               channel), so loop t's W^K_t is one [H*d_head][r_k] block whose rows h*d_head ..
+ *               (h+1)*d_head-1 rebuild head h. */
+typedef enum { LLA_PER_HEAD = 0, LLA_2D = 1 } lla_variant;
+
+typedef struct {
+  int32_t variant; /* lla_variant */
+  int32_t dtype;   /* lla_dtype */
+  int32_t H;       /* heads */
+  int32_t d_head;  /* channels per head, multiple of 8, <= 256 */
+  int32_t T;       /* loops (recurrence steps) */
+  int32_t r_k;     /* K latent rank */
+  int32_t r_v;     /* V latent rank (the paper uses r_v > r_k; any compiled pair is allowed) */
+  int32_t n_max;   /* latent slots per sequence in the cache */
+  float scale;     /* softmax scale; 0 means 1/sqrt(d_head) */
+} lla_desc;
+
+/* Compiled (r_k, r_v) pairs.
+ *   per-head, f32 and bf16: (8,8) (16,16) (24,24) (32,32) (64,64) (96,96) (128,128) (96,160)
+ *   2D, bf16:               (128,128) (256,256)      2D, f32: (8,8) (16,16) (32,32)
+ * Anything else returns LLA_ERR_UNSUPPORTED. */
+
+/* Bytes of device workspace that lla_attend_decode (C == 1) or lla_attend_prefill (C > 1) needs
+ * for this descriptor and batch. May be 0. Returns 0 as well for an invalid descriptor (the
+ * call itself then reports the error). */
+size_t lla_workspace_bytes(const lla_desc* desc, int32_t B, int32_t C);
+
+/* Encode C finished tokens per sequence into the latent cache (Section 3, Eq. 2, applied after
+ * loop T; Eq. 1 fixes the loop-major stack x = [x_1; ...; x_T]).
+ *
+ *   xk, xv  [device] [B][C][T][H][d_head]  per-loop K and V of the tokens being written.
+ *   Ek, Ev  [device] per-head [H][r][T*d_head]; 2D [r][T*H*d_head] (stack order loop, head,
+ *                    channel).
+ *   mu_k, mu_v [device] per-head [H][T*d_head]; 2D [T*H*d_head]; either may be NULL (mu = 0).
+ *   pos     [device] int32 [B]: token c of sequence b is written to slot pos[b] + c.
+ *   zk, zv  [device] the cache: per-head [B][H][n_max][r]; 2D [B][n_max][r]. Only the C slots
+ *                    per sequence (and head) are written.
+ * z = E (x - mu) is accumulated in float32 and rounded once to the storage dtype. A slot
+ * pos[b] + c outside [0, n_max) is not written (no fault). */
+lla_status lla_encode(const lla_desc* desc, int32_t B, int32_t C,
+                      const void* xk, const void* xv, const void* Ek, const void* Ev,
+                      const void* mu_k, const void* mu_v, const int32_t* pos,
+                      void* zk, void* zv, void* stream);
+
+/* Decode-time attention of one new token per sequence at loop t over the latent cache.
+ *
+ * Mathematically, for each (b, h): rebuild k_i = W^K_t z^K_i + mu^K_t and v_i = W^V_t z^V_i +
+ * mu^V_t for the cached tokens i < N_b (Eq. 3), append the token's own uncompressed loop-t
+ * (k_self, v_self) if given, and return softmax(scale * K q) V and its log-sum-exp. It is
+ * computed in absorbed form (Section 7): q~ = W^K_t^T q and beta = q . mu^K_t once per (b, h);
+ * scores scale * (q~ . z^K_i + beta) streamed over the latents with an online softmax; the weights
+ * applied to z^V in latent space; one W^V_t projection at the end, with mu^V_t entering through
+ * the total latent weight. The K/V of cached tokens are never formed.
+ *
+ *   t        loop index, 0 <= t < T.
+ *   q        [device] [B][H][d_head].
+ *   zk, zv   [device] cache as in lla_encode.
+ *   seq_lens [device] int32 [B] or NULL (all n_max). N_b is clamped to [0, n_max].
+ *   Wk, Wv   [device] per-head [T][H][d_head][r]; 2D [T][H*d_head][r].
+ *   mu_k, mu_v [device] as in lla_encode, or NULL.
+ *   k_self, v_self [device] [B][H][d_head], both given or both NULL.
+ *   out      [device] [B][H][d_head].
+ *   lse      [device] float32 [B][H] (natural log) or NULL.
+ *   ws       [device] workspace of at least lla_workspace_bytes(desc, B, 1) bytes (NULL if 0).
+ * An empty key set (N_b = 0 and no self token) gives out = 0 and lse = -inf. */
+lla_status lla_attend_decode(const lla_desc* desc, int32_t B, int32_t t, const void* q,
+                             const void* zk, const void* zv, const int32_t* seq_lens,
+                             const void* Wk, const void* Wv, const void* mu_k, const void* mu_v,
+                             const void* k_self, const void* v_self, void* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Chunked-prefill attention at loop t: C query rows per sequence over the latent cache, causal.
+ *
+ * The chunk's own latents must already be in slots ctx_lens[b] .. ctx_lens[b]+C-1 (written by
+ * lla_encode: the two-pass order of the paper's cached decoder, Appendix A, "Decoding and
+ * caching"). Row j sits at position ctx_lens[b] + j and attends latents 0 .. ctx_lens[b] + j,
+ * inclusive. Same absorbed arithmetic as lla_attend_decode, without a self token.
+ *
+ *   q   [device] [B][C][H][d_head];  out [device] [B][C][H][d_head].
+ *   ctx_lens [device] int32 [B]; a row whose position is outside [0, n_max) attends the clamped
+ *            range 0 .. min(position, n_max-1), and an empty range gives 0.
+ *   ws  [device] at least lla_workspace_bytes(desc, B, C) bytes.
+ *   Other arguments as in lla_attend_decode. */
+lla_status lla_attend_prefill(const lla_desc* desc, int32_t B, int32_t C, int32_t t,
+                              const void* q, const void* zk, const void* zv,
+                              const int32_t* ctx_lens, const void* Wk, const void* Wv,
+                              const void* mu_k, const void* mu_v, void* out,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* lla_status_string(lla_status s);
+
+/* LLA_ABI_VERSION of the built library. */
+int32_t lla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLA_H_ */

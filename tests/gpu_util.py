@@ -1,0 +1,73 @@
+"""Helpers for the GPU parity tests: device transfer, comparison and the tolerances.
+
+Tolerances (norm-wise per call output, max|gpu - ref| / max|ref|):
+  fp32 storage: 1e-5 (fp32 accumulation of exact fp32 inputs);
+  bf16 storage: 1e-2 (bf16 inputs are exact on both sides; the GPU rounds its result to bf16 once,
+                a relative change of at most 2^-9, plus fp32 accumulation).
+lse is always float32: |gpu - ref| <= 2e-5 * max(1, |ref|).
+"""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_lla_amd import lla
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+LSE_TOL = 2e-5
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+LLA_DT = {"f32": lla.LLA_F32, "bf16": lla.LLA_BF16}
+LLA_VAR = {"per_head": lla.LLA_PER_HEAD, "2d": lla.LLA_2D}
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import os
+    if not os.path.exists(lla.LIB_PATH):
+        pytest.fail("liblla.so is not built; the GPU tests need the HIP library")
+
+
+def dev(a, dtype="f32"):
+    """numpy (float32 holding storage values) -> device tensor of the storage dtype (exact)."""
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if t.dtype in (torch.int32, torch.int64):
+        return t.to(torch.int32).cuda()
+    return t.to(TORCH_DT[dtype]).cuda().contiguous()
+
+
+def host(t):
+    return None if t is None else t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.max(np.abs(ref))
+    if den == 0:
+        return float(np.max(np.abs(got)))
+    return float(np.max(np.abs(got - ref)) / den)
+
+
+def assert_close(got, ref, dtype, what=""):
+    e = rel_err(got, ref)
+    assert e <= TOL[dtype], f"{what}: relative error {e:.3e} > {TOL[dtype]:.0e}"
+    return e
+
+
+def assert_lse(got, ref, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    inf_ref = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), inf_ref), f"{what}: -inf pattern differs"
+    g, r = got[~inf_ref], ref[~inf_ref]
+    if g.size:
+        err = np.max(np.abs(g - r) / np.maximum(1.0, np.abs(r)))
+        assert err <= LSE_TOL, f"{what}: lse error {err:.3e}"
+
+
+def desc_for(s, n_max=None, scale=0.0):
+    return lla.make_desc(LLA_VAR[s.variant], LLA_DT[s.dtype], s.H, s.d, s.T, s.r_k, s.r_v,
+                         s.n_max if n_max is None else n_max, scale)

@@ -1,0 +1,138 @@
+"""The C ABI on the CPU: the library loads, exports what include/lla.h declares, and rejects bad
+arguments on the host before launching anything (no GPU needed, no kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_lla_amd import lla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+if not os.path.exists(lla.LIB_PATH):
+    pytest.skip("liblla.so not built (run __graft_entry__.build())", allow_module_level=True)
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "lla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lla_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert {"lla_encode", "lla_attend_decode", "lla_attend_prefill", "lla_workspace_bytes",
+            "lla_status_string", "lla_abi_version"} <= set(names)
+    lib = ctypes.CDLL(lla.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert lla.lla_abi_version() == 1
+    assert lla.lla_status_string(lla.LLA_OK) == "ok"
+    assert "workspace" in lla.lla_status_string(lla.LLA_ERR_WORKSPACE)
+    assert lla.lla_status_string(99) == "unknown status"
+
+
+# fake, aligned, never-dereferenced addresses: every call below fails validation first
+A = ctypes.c_void_p(0x10000)
+M = ctypes.c_void_p(0x10008)  # misaligned
+N = None
+S = ctypes.c_void_p(0)
+
+
+def desc(**kw):
+    base = dict(variant=lla.LLA_PER_HEAD, dtype=lla.LLA_BF16, H=16, d_head=128, T=4, r_k=32,
+                r_v=32, n_max=4097, scale=0.0)
+    base.update(kw)
+    return lla.make_desc(**base)
+
+
+def decode(d, B=2, t=0, q=A, zk=A, zv=A, lens=N, Wk=A, Wv=A, muk=N, muv=N, ks=N, vs=N, out=A,
+           lse=N, ws=N, wsb=0):
+    lib = lla.library()
+    return lib.lla_attend_decode(ctypes.byref(d), B, t, q, zk, zv, lens, Wk, Wv, muk, muv, ks, vs,
+                                 out, lse, ws, ctypes.c_size_t(wsb), S)
+
+
+def encode(d, B=2, C=1, xk=A, xv=A, Ek=A, Ev=A, muk=N, muv=N, pos=A, zk=A, zv=A):
+    lib = lla.library()
+    return lib.lla_encode(ctypes.byref(d), B, C, xk, xv, Ek, Ev, muk, muv, pos, zk, zv, S)
+
+
+def prefill(d, B=2, C=4, t=0, q=A, zk=A, zv=A, ctx=A, Wk=A, Wv=A, out=A, ws=N, wsb=0):
+    lib = lla.library()
+    return lib.lla_attend_prefill(ctypes.byref(d), B, C, t, q, zk, zv, ctx, Wk, Wv, N, N, out, ws,
+                                  ctypes.c_size_t(wsb), S)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(t=4), dict(t=-1), dict(B=0), dict(q=N), dict(zk=N), dict(Wv=N), dict(out=N),
+    dict(q=M), dict(lse=M), dict(ks=A), dict(vs=A),
+])
+def test_decode_rejects_bad_arguments(kw):
+    d = desc(n_max=100)  # small cache: no split, no workspace needed
+    assert decode(d, **kw) == lla.LLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(H=0), dict(d_head=12), dict(d_head=264), dict(T=0), dict(n_max=0), dict(variant=3),
+    dict(dtype=7), dict(scale=-1.0), dict(scale=float("inf")),
+])
+def test_bad_descriptor(kw):
+    d = desc(**kw)
+    assert decode(d) == lla.LLA_ERR_INVALID_ARG
+    assert encode(d) == lla.LLA_ERR_INVALID_ARG
+    assert lla.lla_workspace_bytes(d, 2, 1) == 0
+
+
+def test_unsupported_ranks():
+    assert decode(desc(r_k=33, r_v=33, n_max=100)) == lla.LLA_ERR_UNSUPPORTED
+    assert decode(desc(r_k=24, r_v=32, n_max=100)) == lla.LLA_ERR_UNSUPPORTED
+
+
+def test_workspace_checked_before_launch():
+    d = desc()  # 32 x 16 units over 4097 slots: split-K, needs a workspace
+    need = lla.lla_workspace_bytes(d, 32, 1)
+    assert need > 0
+    assert decode(d, B=32) == lla.LLA_ERR_WORKSPACE
+    assert decode(d, B=32, ws=A, wsb=need - 4) == lla.LLA_ERR_WORKSPACE
+
+
+def test_workspace_sizes():
+    # no split when B*H alone fills the chip (capacity shape)
+    assert lla.lla_workspace_bytes(desc(r_k=24, r_v=24), 768, 1) == 0
+    # split partials are (m, l, a[r_v]) floats per (b, h, split)
+    n = lla.lla_workspace_bytes(desc(), 32, 1)
+    assert n % (32 * 16 * (2 + 32) * 4) == 0
+    splits = n // (32 * 16 * (2 + 32) * 4)
+    assert 2 <= splits <= 64
+
+
+def test_encode_rejects_bad_arguments():
+    d = desc()
+    assert encode(d, C=0) == lla.LLA_ERR_INVALID_ARG
+    assert encode(d, C=5000) == lla.LLA_ERR_INVALID_ARG
+    assert encode(d, pos=N) == lla.LLA_ERR_INVALID_ARG
+    assert encode(d, xk=M) == lla.LLA_ERR_INVALID_ARG
+    assert encode(d, muk=M) == lla.LLA_ERR_INVALID_ARG
+    assert encode(d, zv=N) == lla.LLA_ERR_INVALID_ARG
+
+
+def test_prefill_rejects_bad_arguments():
+    d = desc(n_max=64)
+    assert prefill(d, t=4) == lla.LLA_ERR_INVALID_ARG
+    assert prefill(d, C=0) == lla.LLA_ERR_INVALID_ARG
+    assert prefill(d, C=65) == lla.LLA_ERR_INVALID_ARG
+    assert prefill(d, ctx=N) == lla.LLA_ERR_INVALID_ARG
+    assert prefill(desc(n_max=64, r_k=33, r_v=33)) == lla.LLA_ERR_UNSUPPORTED
+
+
+def test_binding_checks_shapes_without_gpu():
+    torch = pytest.importorskip("torch")
+    d = desc(n_max=8)
+    q = torch.zeros(2, 16, 128)  # CPU tensor: rejected before any library call
+    with pytest.raises(ValueError):
+        lla.lla_attend_decode(d, 2, 0, q, q, q, None, q, q, None, None, None, None, q)

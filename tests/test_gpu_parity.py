@@ -1,0 +1,351 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle, element by element.
+
+Small shapes span several tiles, several token splits and a ragged tail; the five synthetic
+workloads run at full size with outputs sampled where the oracle would be too slow. Tolerances
+are in tests/gpu_util.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_lla_amd import lla, synth
+from oracle import lla_oracle as O
+from tests.gpu_util import (LLA_DT, LLA_VAR, assert_close, assert_lse, dev, host, rel_err,
+                            require_gpu)
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [(8, 8), (16, 16), (24, 24), (32, 32), (64, 64), (96, 96), (128, 128), (96, 160),
+         (256, 256)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def mk_desc(variant, dtype, H, d, T, rk, rv, n_max, scale=0.0):
+    return lla.make_desc(LLA_VAR[variant], LLA_DT[dtype], H, d, T, rk, rv, n_max, scale)
+
+
+def gpu_decode(desc, B, t, c, dtype, lens, self_token=True, mu=True, want_lse=True):
+    """Run lla_attend_decode on device copies of case c at loop t; returns (o, lse) on host."""
+    H, d = desc.H, desc.d_head
+    q = dev(c["q"][t], dtype)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H, dtype=torch.float32, device="cuda") if want_lse else None
+    ws = lla.workspace(desc, B, 1)
+    ks = dev(c["k_self"][t], dtype) if self_token else None
+    vs = dev(c["v_self"][t], dtype) if self_token else None
+    lla.lla_attend_decode(desc, B, t, q, c["_zk"], c["_zv"], dev(lens), c["_Wk"], c["_Wv"],
+                          c["_muk"] if mu else None, c["_muv"] if mu else None, ks, vs, out, lse, ws)
+    torch.cuda.synchronize()
+    return host(out), (host(lse) if want_lse else None)
+
+
+def upload(c, dtype):
+    for k in ("zk", "zv", "Wk", "Wv"):
+        c["_" + k] = dev(c[k], dtype)
+    c["_muk"] = dev(c["mu_k"], dtype)
+    c["_muv"] = dev(c["mu_v"], dtype)
+    return c
+
+
+def oracle_decode(c, t, lens, variant, self_token=True, mu=True, b_sel=None, absorbed=False):
+    fn = O.attend_decode_absorbed if absorbed else O.attend_decode
+    sl = slice(None) if b_sel is None else b_sel
+    return fn(c["q"][t][sl], c["zk"][sl], c["zv"][sl], c["Wk"], c["Wv"], t, np.asarray(lens)[sl],
+              c["mu_k"] if mu else None, c["mu_v"] if mu else None,
+              c["k_self"][t][sl] if self_token else None, c["v_self"][t][sl] if self_token else None,
+              variant=variant)
+
+
+# --------------------------------------------------------------------------------------------
+# shape sweep: every compiled rank pair, both storage types, ragged lengths, split-K
+# --------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rk,rv", PAIRS)
+def test_decode_sweep_per_head(dtype, rk, rv):
+    B, H, d, T, n_max = 3, 2, 64, 3, 1301
+    lens = [1301, 517, 0]
+    for gain, mu, self_token in ((1.0, True, True), (8.0, False, True), (1.0, True, False)):
+        c = upload(synth.random_case("per_head", dtype, B, H, d, T, rk, rv, n_max,
+                                     7000 + rk + rv, with_mu=mu, q_gain=gain), dtype)
+        desc = mk_desc("per_head", dtype, H, d, T, rk, rv, n_max)
+        assert lla.lla_workspace_bytes(desc, B) > 0  # this shape runs split-K plus the combine
+        for t in range(T):
+            o, lse = gpu_decode(desc, B, t, c, dtype, lens, self_token, mu)
+            ro, rl = oracle_decode(c, t, lens, "per_head", self_token, mu)
+            what = f"{dtype} r=({rk},{rv}) gain={gain} mu={mu} self={self_token} t={t}"
+            assert_close(o, ro, dtype, what)
+            assert_lse(lse, rl, what)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rk,rv", [(8, 8), (32, 32), (256, 256)])
+def test_decode_sweep_2d(dtype, rk, rv):
+    B, H, d, T, n_max = 2, 3, 32, 2, 777
+    lens = [777, 130]
+    c = upload(synth.random_case("2d", dtype, B, H, d, T, rk, rv, n_max, 7100 + rk), dtype)
+    desc = mk_desc("2d", dtype, H, d, T, rk, rv, n_max)
+    for t in range(T):
+        o, lse = gpu_decode(desc, B, t, c, dtype, lens)
+        ro, rl = oracle_decode(c, t, lens, "2d")
+        assert_close(o, ro, dtype, f"2d {dtype} t={t}")
+        assert_lse(lse, rl, f"2d {dtype} t={t}")
+
+
+def test_decode_empty_and_clamped_lengths():
+    dtype = "f32"
+    B, H, d, T, n_max = 4, 2, 16, 2, 40
+    c = upload(synth.random_case("per_head", dtype, B, H, d, T, 8, 8, n_max, 7200), dtype)
+    desc = mk_desc("per_head", dtype, H, d, T, 8, 8, n_max)
+    lens = [0, 99, -5, 40]
+    o, lse = gpu_decode(desc, B, 1, c, dtype, lens, self_token=True)
+    ro, rl = oracle_decode(c, 1, lens, "per_head", True)
+    assert_close(o, ro, dtype)
+    assert_lse(lse, rl)
+    np.testing.assert_allclose(o[0], c["v_self"][1][0], rtol=0, atol=1e-6)
+    o, lse = gpu_decode(desc, B, 1, c, dtype, lens, self_token=False)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0])) and np.all(np.isneginf(lse[2]))
+    ro, rl = oracle_decode(c, 1, lens, "per_head", False)
+    assert_close(o, ro, dtype)
+    assert_lse(lse, rl)
+
+
+def test_decode_null_seq_lens_means_n_max_and_is_deterministic():
+    dtype = "bf16"
+    B, H, d, T, n_max = 2, 4, 128, 2, 2000
+    c = upload(synth.random_case("per_head", dtype, B, H, d, T, 32, 32, n_max, 7300), dtype)
+    desc = mk_desc("per_head", dtype, H, d, T, 32, 32, n_max)
+    q = dev(c["q"][0], dtype)
+    outs = []
+    for _ in range(2):
+        out = torch.empty_like(q)
+        lla.lla_attend_decode(desc, B, 0, q, c["_zk"], c["_zv"], None, c["_Wk"], c["_Wv"],
+                              c["_muk"], c["_muv"], None, None, out, None, lla.workspace(desc, B))
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    ro, _ = oracle_decode(c, 0, [n_max] * B, "per_head", False)
+    assert_close(host(outs[0]), ro, dtype)
+
+
+# --------------------------------------------------------------------------------------------
+# encode
+# --------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant,H,d,T,r", [("per_head", 3, 32, 4, 24), ("per_head", 2, 96, 32, 96),
+                                             ("2d", 2, 16, 3, 32), ("per_head", 2, 64, 2, 160)])
+def test_encode(dtype, variant, H, d, T, r):
+    B, C, n_max = 3, 5, 12
+    pos = np.array([0, 7, 10], np.int32)  # sequence 2 runs past the end: slots 12.. are skipped
+    g = np.random.default_rng(r + T)
+    xk = synth.normal((B, C, T, H, d), 900 + r, dtype)
+    xv = synth.normal((B, C, T, H, d), 901 + r, dtype)
+    K = T * d if variant == "per_head" else T * H * d
+    es = (H, r, K) if variant == "per_head" else (r, K)
+    ms = (H, K) if variant == "per_head" else (K,)
+    zs = (B, H, n_max, r) if variant == "per_head" else (B, n_max, r)
+    Ek = synth.normal(es, 902 + r, dtype, 1 / math.sqrt(K))
+    Ev = synth.normal(es, 903 + r, dtype, 1 / math.sqrt(K))
+    mk = synth.normal(ms, 904 + r, dtype, 0.5)
+    mv = synth.normal(ms, 905 + r, dtype, 0.5)
+    z0 = synth.normal(zs, 906 + r, dtype)  # pre-existing cache contents must survive
+    desc = mk_desc(variant, dtype, H, d, T, r, r, n_max)
+    for mu in (True, False):
+        zk, zv = dev(z0, dtype), dev(z0, dtype)
+        lla.lla_encode(desc, B, C, dev(xk, dtype), dev(xv, dtype), dev(Ek, dtype), dev(Ev, dtype),
+                       dev(mk, dtype) if mu else None, dev(mv, dtype) if mu else None, dev(pos),
+                       zk, zv)
+        torch.cuda.synchronize()
+        # oracle writes only the in-range slots, like the kernel
+        keep = np.array([min(C, n_max - p) for p in pos])
+        rk_, rv_ = z0.copy(), z0.copy()
+        for b in range(B):
+            sub = slice(b, b + 1)
+            a, bb = O.encode_into_cache(z0[sub], z0[sub], xk[sub, :keep[b]], xv[sub, :keep[b]], Ek, Ev,
+                                        pos[sub], mk if mu else None, mv if mu else None, variant)
+            rk_[sub], rv_[sub] = a, bb
+        assert_close(host(zk), rk_, dtype, f"encode zk {variant} mu={mu}")
+        assert_close(host(zv), rv_, dtype, f"encode zv {variant} mu={mu}")
+        # untouched slots are bit-identical
+        mask = np.ones(zs[:-1], bool)
+        for b in range(B):
+            for cc in range(keep[b]):
+                if variant == "per_head":
+                    mask[b, :, pos[b] + cc] = False
+                else:
+                    mask[b, pos[b] + cc] = False
+        assert np.array_equal(host(zk)[mask], z0.astype(np.float64)[mask])
+
+
+# --------------------------------------------------------------------------------------------
+# prefill
+# --------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant,rk,rv", [("per_head", 24, 24), ("per_head", 96, 160), ("2d", 32, 32)])
+def test_prefill(dtype, variant, rk, rv):
+    B, C, H, d, T, n_max = 2, 37, 3, 32, 2, 400
+    ctx = np.array([300, 0], np.int32)
+    c = upload(synth.random_case(variant, dtype, B, H, d, T, rk, rv, n_max, 7400 + rk), dtype)
+    q = synth.normal((B, C, H, d), 7401, dtype)
+    desc = mk_desc(variant, dtype, H, d, T, rk, rv, n_max)
+    for t in range(T):
+        out = torch.empty(B, C, H, d, dtype=dev(q, dtype).dtype, device="cuda")
+        lla.lla_attend_prefill(desc, B, C, t, dev(q, dtype), c["_zk"], c["_zv"], dev(ctx), c["_Wk"],
+                               c["_Wv"], c["_muk"], c["_muv"], out, lla.workspace(desc, B, C))
+        torch.cuda.synchronize()
+        ref = O.attend_prefill(q, c["zk"], c["zv"], c["Wk"], c["Wv"], t, ctx, c["mu_k"], c["mu_v"],
+                               variant=variant)
+        assert_close(host(out), ref, dtype, f"prefill {variant} t={t}")
+
+
+# --------------------------------------------------------------------------------------------
+# the tiny fp32 workload: encode the 64-token context, decode with the self token, encode it
+# --------------------------------------------------------------------------------------------
+
+def test_tiny_fp32_pipeline():
+    s = synth.CASES["tiny_fp32"]
+    c = synth.tiny_fp32_case(s)
+    B, H, d, T, N, r = s.B, s.H, s.d, s.T, s.N, s.r_k
+    n_max = N + 1
+    desc = mk_desc("per_head", "f32", H, d, T, r, r, n_max)
+    dt = "f32"
+    zk = torch.zeros(B, H, n_max, r, device="cuda")
+    zv = torch.zeros_like(zk)
+    # context: 64 tokens encoded from their per-loop trajectories
+    lla.lla_encode(desc, B, N, dev(c["xk"][:, :N]), dev(c["xv"][:, :N]), dev(c["Ek"]), dev(c["Ev"]),
+                   None, None, dev(np.zeros(B, np.int32)), zk, zv)
+    z0 = np.zeros((B, H, n_max, r))
+    rzk, rzv = O.encode_into_cache(z0, z0, c["xk"][:, :N], c["xv"][:, :N], c["Ek"], c["Ev"], [0])
+    assert_close(host(zk), rzk, dt, "context encode")
+    assert_close(host(zv), rzv, dt, "context encode")
+    lens = np.full(B, N, np.int32)
+    for t in range(T):
+        q = dev(c["q"][t])
+        ks = dev(c["xk"][:, N, t])  # the new token's own loop-t K/V, uncompressed
+        vs = dev(c["xv"][:, N, t])
+        out = torch.empty_like(q)
+        lse = torch.empty(B, H, device="cuda")
+        lla.lla_attend_decode(desc, B, t, q, zk, zv, dev(lens), dev(c["Wk"]), dev(c["Wv"]), None,
+                              None, ks, vs, out, lse, lla.workspace(desc, B))
+        torch.cuda.synchronize()
+        ro, rl = O.attend_decode(c["q"][t], rzk, rzv, c["Wk"], c["Wv"], t, lens, None, None,
+                                 c["xk"][:, N, t], c["xv"][:, N, t])
+        assert_close(host(out), ro, dt, f"tiny decode t={t}")
+        assert_lse(host(lse), rl, f"tiny decode t={t}")
+    # after loop T the new token's 4 K/V vectors are folded into slot 64
+    lla.lla_encode(desc, B, 1, dev(c["xk"][:, N:N + 1]), dev(c["xv"][:, N:N + 1]), dev(c["Ek"]),
+                   dev(c["Ev"]), None, None, dev(lens), zk, zv)
+    rzk, rzv = O.encode_into_cache(rzk, rzv, c["xk"][:, N:N + 1], c["xv"][:, N:N + 1], c["Ek"], c["Ev"], lens)
+    assert_close(host(zk), rzk, dt, "new-token encode")
+    assert_close(host(zv), rzv, dt, "new-token encode")
+    # a second step reads all 65 latents
+    q2 = synth.normal((B, H, d), 5555)
+    out = torch.empty(B, H, d, device="cuda")
+    lla.lla_attend_decode(desc, B, 2, dev(q2), zk, zv, dev(lens + 1), dev(c["Wk"]), dev(c["Wv"]),
+                          None, None, None, None, out, None, lla.workspace(desc, B))
+    torch.cuda.synchronize()
+    ro, _ = O.attend_decode(q2, rzk, rzv, c["Wk"], c["Wv"], 2, lens + 1)
+    assert_close(host(out), ro, dt, "second step")
+
+
+# --------------------------------------------------------------------------------------------
+# full-size workloads (sampled rows where the oracle is slow)
+# --------------------------------------------------------------------------------------------
+
+def test_ouro_layer_full_size():
+    """One Ouro-1.4B-shaped layer at full size (B=32, N=4096, r=32): all loops, sampled rows."""
+    s = synth.CASES["ouro_layer"]
+    c = upload(synth.host_case(s), s.dtype)
+    desc = mk_desc("per_head", s.dtype, s.H, s.d, s.T, s.r_k, s.r_v, s.n_max)
+    lens = c["seq_lens"]
+    rows = sorted({0, s.B - 1, *np.random.default_rng(synth.seed(s.case, synth.SEED_SAMPLE)).choice(s.B, 2, replace=False).tolist()})
+    for t in range(s.T):
+        o, lse = gpu_decode(desc, s.B, t, c, s.dtype, lens, True, False)
+        ro, rl = oracle_decode(c, t, lens, "per_head", True, False, b_sel=rows)
+        assert_close(o[rows], ro, s.dtype, f"ouro t={t}")
+        assert_lse(lse[rows], rl, f"ouro t={t}")
+    # encode of the new token into slot N for every sequence
+    zk, zv = c["_zk"], c["_zv"]
+    lla.lla_encode(desc, s.B, 1, dev(c["xk"], s.dtype), dev(c["xv"], s.dtype), dev(c["Ek"], s.dtype),
+                   dev(c["Ev"], s.dtype), None, None, dev(lens), zk, zv)
+    torch.cuda.synchronize()
+    for ax, x, E, z in (("k", c["xk"], c["Ek"], zk), ("v", c["xv"], c["Ev"], zv)):
+        got = host(z[:, :, s.N])
+        ref = np.stack([[O.encode_stack(x[b, 0, :, h, :].reshape(-1), E[h]) for h in range(s.H)] for b in range(s.B)])
+        assert_close(got, ref, s.dtype, f"ouro encode {ax}")
+
+
+def _fill_device_case(s, layer=0):
+    """Device-resident inputs of a large workload (latents from a seeded device generator)."""
+    dt = torch.bfloat16
+    g = {}
+    zshape_k = (s.B, s.H, s.n_max, s.r_k) if s.variant == "per_head" else (s.B, s.n_max, s.r_k)
+    zshape_v = (s.B, s.H, s.n_max, s.r_v) if s.variant == "per_head" else (s.B, s.n_max, s.r_v)
+    g["zk"] = synth.device_normal_(torch.empty(zshape_k, dtype=dt, device="cuda"), synth.seed(s.case, synth.SEED_ZK, layer))
+    g["zv"] = synth.device_normal_(torch.empty(zshape_v, dtype=dt, device="cuda"), synth.seed(s.case, synth.SEED_ZV, layer))
+    if s.variant == "per_head":
+        Wk = synth.orthonormal_W(s.T, s.H, s.d, s.r_k, synth.seed(s.case, synth.SEED_WK, layer), "bf16")
+        Wv = synth.orthonormal_W(s.T, s.H, s.d, s.r_v, synth.seed(s.case, synth.SEED_WV, layer), "bf16")
+    else:
+        Wk = synth.orthonormal_W_2d(s.T, s.H, s.d, s.r_k, synth.seed(s.case, synth.SEED_WK, layer), "bf16")
+        Wv = synth.orthonormal_W_2d(s.T, s.H, s.d, s.r_v, synth.seed(s.case, synth.SEED_WV, layer), "bf16")
+    g["Wk"], g["Wv"] = Wk, Wv
+    g["q"] = synth.normal((s.T, s.B, s.H, s.d), synth.seed(s.case, synth.SEED_Q, layer), "bf16")
+    kv = synth.normal((2, s.T, s.B, s.H, s.d), synth.seed(s.case, synth.SEED_SELF, layer), "bf16")
+    g["k_self"], g["v_self"] = kv[0], kv[1]
+    return g
+
+
+def _check_sampled(s, rows, loops, what):
+    g = _fill_device_case(s)
+    desc = mk_desc(s.variant, s.dtype, s.H, s.d, s.T, s.r_k, s.r_v, s.n_max)
+    lens = np.full(s.B, s.N, np.int32)
+    Wk, Wv = dev(g["Wk"], "bf16"), dev(g["Wv"], "bf16")
+    ws = lla.workspace(desc, s.B, 1)
+    zk_rows = host(g["zk"][rows])
+    zv_rows = host(g["zv"][rows])
+    for t in loops:
+        q = dev(g["q"][t], "bf16")
+        out = torch.empty_like(q)
+        lse = torch.empty(s.B, s.H, device="cuda")
+        lla.lla_attend_decode(desc, s.B, t, q, g["zk"], g["zv"], dev(lens), Wk, Wv, None, None,
+                              dev(g["k_self"][t], "bf16"), dev(g["v_self"][t], "bf16"), out, lse, ws)
+        torch.cuda.synchronize()
+        ro, rl = O.attend_decode_absorbed(g["q"][t][rows], zk_rows, zv_rows, g["Wk"], g["Wv"], t,
+                                          lens[rows], None, None, g["k_self"][t][rows],
+                                          g["v_self"][t][rows], variant=s.variant)
+        assert_close(host(out)[rows], ro, s.dtype, f"{what} t={t}")
+        assert_lse(host(lse)[rows], rl, f"{what} t={t}")
+    del g
+    torch.cuda.empty_cache()
+
+
+def test_capacity_layer_full_size_sampled():
+    """Capacity shape, one layer at the benchmark's launch shape (B=768, N=4096, r=24)."""
+    s = synth.CASES["capacity"]
+    rows = sorted({0, 383, 767, *np.random.default_rng(synth.seed(s.case, synth.SEED_SAMPLE)).choice(768, 5, replace=False).tolist()})
+    _check_sampled(s, rows, range(s.T), "capacity")
+
+
+def test_deep_loop_full_size_sampled():
+    """Deep-recurrence shape (H=40, d=96, T=32, r=96, B=64, N=4096): sampled rows and loops."""
+    s = synth.CASES["deep_loop"]
+    rows = sorted({0, 63, *np.random.default_rng(synth.seed(s.case, synth.SEED_SAMPLE)).choice(64, 2, replace=False).tolist()})
+    _check_sampled(s, rows, [0, 1, 17, 31], "deep_loop")
+
+
+def test_lla2d_decode_full_size_sampled():
+    """LLA-2D decode (r=256+256, B=128, N=8192): rows 0 and 127, all loops."""
+    s = synth.CASES["lla2d"].with_(C=1)
+    _check_sampled(s, [0, 127], range(s.T), "lla2d")
