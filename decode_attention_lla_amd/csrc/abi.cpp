@@ -117,7 +117,7 @@ lla_status lla_attend_decode(const lla_desc* desc, int32_t B, int32_t t, const v
       !opt_ok(lse) || !opt_ok(ws))
     return LLA_ERR_INVALID_ARG;
   if ((k_self == nullptr) != (v_self == nullptr)) return LLA_ERR_INVALID_ARG;
-  if (!lla::decode_supported(desc->variant, desc->dtype, desc->r_k, desc->r_v))
+  if (!lla::decode_supported(desc->variant, desc->dtype, desc->r_k, desc->r_v, desc->d_head))
     return LLA_ERR_UNSUPPORTED;
   const size_t need = lla::decode_workspace_bytes(*desc, B);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return LLA_ERR_WORKSPACE;

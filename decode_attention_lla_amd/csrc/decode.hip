@@ -300,9 +300,18 @@ const Entry* find(int dtype, int r_k, int r_v) {
 
 }  // namespace
 
-bool decode_supported(int variant, int dtype, int r_k, int r_v) {
+bool valu_supported(int variant, int dtype, int r_k, int r_v) {
   if (variant != LLA_PER_HEAD && variant != LLA_2D) return false;
   return find(dtype, r_k, r_v) != nullptr;
+}
+
+bool decode_supported(int variant, int dtype, int r_k, int r_v, int d_head) {
+  return valu_supported(variant, dtype, r_k, r_v) ||
+         (variant == LLA_2D && decode2d_mfma_supported(dtype, r_k, r_v, d_head));
+}
+
+bool decode_uses_mfma2d(const lla_desc& desc) {
+  return desc.variant == LLA_2D && decode2d_mfma_supported(desc.dtype, desc.r_k, desc.r_v, desc.d_head);
 }
 
 void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
@@ -323,6 +332,11 @@ void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
 }
 
 size_t decode_workspace_bytes(const lla_desc& desc, int B) {
+  if (decode_uses_mfma2d(desc)) return decode2d_workspace_bytes(desc, B);
+  return valu_workspace_bytes(desc, B);
+}
+
+size_t valu_workspace_bytes(const lla_desc& desc, int B) {
   int s, c;
   decode_plan(desc, B, &s, &c);
   if (s <= 1) return 0;
@@ -330,6 +344,10 @@ size_t decode_workspace_bytes(const lla_desc& desc, int B) {
 }
 
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream) {
+  // LLA-2D decode rows (one query per sequence) take the MFMA path when it is compiled
+  if (p.variant == LLA_2D && p.rows_per_seq == 1 && !p.causal &&
+      decode2d_mfma_supported(dtype, p.r_k, p.r_v, p.d))
+    return launch_decode2d(p, stream);
   const Entry* e = find(dtype, p.r_k, p.r_v);
   if (e == nullptr) return hipErrorNotSupported;
   const unsigned units = static_cast<unsigned>(p.B) * p.H * p.splits;

@@ -1,0 +1,454 @@
+// LLA-2D absorbed decode on bf16 MFMA.
+//
+// Method: O'Neill & Reid, "Looped Latent Attention", arXiv 2607.15456. Section 3, "The LLA-2D
+// variant": one latent per token and layer rebuilds every head, so head h's loop-t key is rows
+// h*d .. (h+1)*d-1 of W^K_t z^K. With the absorbed form of Section 7 every head scores the same
+// latent with its own q~_h = W^K_t[h]^T q_h, and the V side accumulates sum_i p_hi z^V_i per head
+// in latent space before one W^V_t[h] projection. Unlike per-head LLA this contraction is dense:
+// 16 heads x r against every latent, so it runs on MFMA:
+//
+//   1. qproj2d_kernel: q~ (fp32, pre-scaled by scale*log2 e) and beta = q . mu^K_t per (b, h).
+//   2. decode2d_partial_kernel: a workgroup owns (sequence b, token split, group of 16 heads);
+//      each wave takes 16-token tiles. Scores S^T[token][head] = Z^K (16 x r_k) . Q~^T come from
+//      v_mfma_f32_16x16x32_bf16 with q~ split into bf16 hi + lo parts (two MFMAs per k-step), so
+//      the scores keep ~16 mantissa bits of q~. The accumulator layout puts head (lane % 16) and
+//      four tokens in each lane, which is exactly the B-operand layout of
+//      v_mfma_f32_16x16x16bf16_1k for P^T (tokens x heads): A^T[r][head] += Z^V^T (r x 16 tokens)
+//      . P^T needs no data movement for P. Z^V is staged per wave in LDS (coalesced 16-byte
+//      loads, rows padded so the transposed 16-bit reads are bank-conflict free). Online softmax
+//      per head, rescaling only when the running max grows by more than 8 (base 2). The four
+//      waves merge through LDS and the workgroup writes one (m, l, a[r_v]) partial per head.
+//   3. combine2d_kernel: per (head, block of sequences), W^V_t[h] staged once in LDS; merges the
+//      split partials by log-sum-exp, adds the optional self token, projects, adds mu^V_t,
+//      normalises, writes o and lse.
+#include "lla_device.h"
+#include "lla_internal.h"
+
+namespace lla {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLazy2d = 8.0f;
+constexpr int kQB = 8;     // sequences per qproj / combine workgroup
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int seq_keys(const DecodeParams& p, int b) {
+  int n = p.seq_lens != nullptr ? p.seq_lens[b] : p.n_max;
+  return min(max(n, 0), p.n_max);
+}
+
+// ---- 1. query absorption for every (b, h) ------------------------------------------------------
+// grid (H, ceil(B / kQB)); thread k computes q~[b][h][k] for kQB sequences.
+template <int RK>
+__global__ __launch_bounds__(256) void qproj2d_kernel(DecodeParams p, float* qt, float* beta) {
+  __shared__ float q_s[kQB][256];
+  const int h = blockIdx.x;
+  const int b0 = blockIdx.y * kQB;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kQB * p.d; i += 256) {
+    const int bb = i / p.d;
+    const int j = i - bb * p.d;
+    const int b = b0 + bb;
+    q_s[bb][j] = b < p.B ? ld<BF16>(p.q, (static_cast<size_t>(b) * p.H + h) * p.d + j) : 0.f;
+  }
+  __syncthreads();
+  // W^K_t rows of head h: [T][H*d][RK] at row t*H*d + h*d
+  const size_t wrow = (static_cast<size_t>(p.t) * p.H + h) * p.d;
+  for (int k = tid; k < RK; k += 256) {
+    float acc[kQB];
+#pragma unroll
+    for (int bb = 0; bb < kQB; ++bb) acc[bb] = 0.f;
+    for (int j = 0; j < p.d; ++j) {
+      const float w = ld<BF16>(p.Wk, (wrow + j) * RK + k);
+#pragma unroll
+      for (int bb = 0; bb < kQB; ++bb) acc[bb] += w * q_s[bb][j];
+    }
+#pragma unroll
+    for (int bb = 0; bb < kQB; ++bb)
+      if (b0 + bb < p.B) qt[(static_cast<size_t>(b0 + bb) * p.H + h) * RK + k] = acc[bb] * p.scale_log2;
+  }
+  // beta = scale*log2e * q . mu^K_t (2D mu is [T*H*d], loop t head h at (t*H + h)*d)
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  for (int bb = wave; bb < kQB; bb += 4) {
+    float part = 0.f;
+    if (p.mu_k != nullptr)
+      for (int j = lane; j < p.d; j += 64) part += q_s[bb][j] * ld<BF16>(p.mu_k, wrow + j);
+    part = wave_sum(part);
+    if (lane == 0 && b0 + bb < p.B) beta[static_cast<size_t>(b0 + bb) * p.H + h] = part * p.scale_log2;
+  }
+}
+
+// ---- 2. MFMA latent stream ---------------------------------------------------------------------
+template <int RK, int RV>
+struct Smem2d {
+  static constexpr int kVRow = RV * 2 + 8;                  // bytes per staged V row
+  static constexpr int kVStage = 16 * kVRow;                // one wave's 16-token V tile
+  static constexpr int kPart = 16 * (2 + RV) * 4;           // one (m, l, a) partial for 16 heads
+  static constexpr int kUnion = (4 * kVStage > 2 * kPart) ? 4 * kVStage : 2 * kPart;
+};
+
+template <int RK, int RV>
+__global__ __launch_bounds__(256) void decode2d_partial_kernel(DecodeParams p, const float* qt,
+                                                               const float* beta, float* part) {
+  constexpr int KS = RK / 32;
+  constexpr int RT = RV / 16;
+  constexpr int VCH = 2 * RV;         // 16-byte chunks in a 16-token V tile
+  constexpr int VPL = VCH / 64;       // chunks per lane
+  constexpr int CPR = RV / 8;         // chunks per V row
+  using SM = Smem2d<RK, RV>;
+  static_assert(RK % 32 == 0 && RV % 32 == 0, "ranks must be multiples of 32");
+
+  __shared__ __attribute__((aligned(16))) uint16_t qhi[16 * RK];
+  __shared__ __attribute__((aligned(16))) uint16_t qlo[16 * RK];
+  __shared__ float beta_s[16];
+  __shared__ __attribute__((aligned(16))) char smem[SM::kUnion];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int h0 = blockIdx.z * 16;
+  const int h = h0 + col;
+  const bool hvalid = h < p.H;
+
+  const int nb = seq_keys(p, b);
+  const int tb = split * p.chunk;
+  const int te = min(nb, tb + p.chunk);
+
+  for (int i = tid; i < 16 * RK; i += 256) {
+    const int hh = i / RK;
+    const int k = i - hh * RK;
+    const float v = (h0 + hh < p.H) ? qt[(static_cast<size_t>(b) * p.H + h0 + hh) * RK + k] : 0.f;
+    const uint16_t hi = f32_to_bf16(v);
+    qhi[i] = hi;
+    qlo[i] = f32_to_bf16(v - __uint_as_float(static_cast<uint32_t>(hi) << 16));
+  }
+  if (tid < 16) beta_s[tid] = (h0 + tid < p.H) ? beta[static_cast<size_t>(b) * p.H + h0 + tid] : 0.f;
+  __syncthreads();
+
+  const float bt = beta_s[col];
+  const char* zkb = static_cast<const char*>(p.zk) + static_cast<size_t>(b) * p.n_max * RK * 2;
+  const char* zvb = static_cast<const char*>(p.zv) + static_cast<size_t>(b) * p.n_max * RV * 2;
+  char* vs = smem + wave * SM::kVStage;
+
+  floatx4_t D[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) D[rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf;
+  float l = 0.f;
+
+  for (int tok0 = tb + wave * 16; tok0 < te; tok0 += 64) {
+    // V tile loads first (consumed after the scores)
+    uint4 vreg[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int f = i * 64 + lane;
+      const int row = f / CPR;
+      const int cc = f - row * CPR;
+      const int tok = tok0 + row;
+      vreg[i] = tok < te ? *reinterpret_cast<const uint4*>(zvb + (static_cast<size_t>(tok) * RV + cc * 8) * 2)
+                         : make_uint4(0, 0, 0, 0);
+    }
+    // scores: S^T[token tok0 + i][head h0 + j]
+    const int tokA = tok0 + col;
+    const bool okA = tokA < te;
+    const char* arow = zkb + static_cast<size_t>(tokA) * RK * 2;
+    floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 a = okA ? *reinterpret_cast<const uint4*>(arow + (32 * ks + 8 * g) * 2) : make_uint4(0, 0, 0, 0);
+      const uint4 bh = *reinterpret_cast<const uint4*>(&qhi[col * RK + 32 * ks + 8 * g]);
+      const uint4 bl = *reinterpret_cast<const uint4*>(&qlo[col * RK + 32 * ks + 8 * g]);
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bh), s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bl), s, 0, 0, 0);
+    }
+    // this lane: head h, tokens tok0 + 4g + e
+    float sc[4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = hvalid && (tok0 + 4 * g + e) < te;
+      sc[e] = ok ? s[e] + bt : kNegInf;
+      tmax = fmaxf(tmax, sc[e]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    if (tmax > m + kLazy2d) {
+      const float c = fast_exp2(m - tmax);
+      l *= c;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) D[rt] *= c;
+      m = tmax;
+    }
+    short4_t bp;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pe = (sc[e] == kNegInf) ? 0.f : fast_exp2(sc[e] - m);
+      l += pe;
+      bp[e] = static_cast<short>(f32_to_bf16(pe));
+    }
+    // stage V rows in LDS (two 8-byte writes per 16-byte chunk; rows are 8-byte aligned)
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int f = i * 64 + lane;
+      const int row = f / CPR;
+      const int cc = f - row * CPR;
+      uint2* dst = reinterpret_cast<uint2*>(vs + row * SM::kVRow + cc * 16);
+      dst[0] = make_uint2(vreg[i].x, vreg[i].y);
+      dst[1] = make_uint2(vreg[i].z, vreg[i].w);
+    }
+    wave_lds_sync();
+    // A^T[r][head] += Z^V^T[r][tokens 4g+e] . P^T[tokens][head]
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      short4_t av;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        av[e] = *reinterpret_cast<const short*>(vs + (4 * g + e) * SM::kVRow + (16 * rt + col) * 2);
+      D[rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bp, D[rt], 0, 0, 0);
+    }
+    wave_lds_sync();
+  }
+  // per-head totals: the four lanes of head h hold disjoint token sums
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+
+  // merge the four waves through LDS: (2,3) -> (0,1), then 1 -> 0
+  __syncthreads();
+  float* ps = reinterpret_cast<float*>(smem);
+  constexpr int PS = 16 * (2 + RV);
+  auto put = [&](float* dst) {
+    if (g == 0) {
+      dst[col * (2 + RV)] = m;
+      dst[col * (2 + RV) + 1] = l;
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[col * (2 + RV) + 2 + 16 * rt + 4 * g + e] = D[rt][e];
+  };
+  auto take = [&](const float* src) {
+    const float mo = src[col * (2 + RV)];
+    const float lo = src[col * (2 + RV) + 1];
+    const float M = fmaxf(m, mo);
+    const float fa = (m == kNegInf) ? 0.f : fast_exp2(m - M);
+    const float fb = (mo == kNegInf) ? 0.f : fast_exp2(mo - M);
+    l = l * fa + lo * fb;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) D[rt][e] = D[rt][e] * fa + src[col * (2 + RV) + 2 + 16 * rt + 4 * g + e] * fb;
+    m = M;
+  };
+  if (wave >= 2) put(ps + (wave - 2) * PS);
+  __syncthreads();
+  if (wave < 2) take(ps + wave * PS);
+  __syncthreads();
+  if (wave == 1) put(ps);
+  __syncthreads();
+  if (wave != 0) return;
+  take(ps);
+  if (!hvalid) return;
+  // partial layout [B][H][S][2 + RV]
+  float* w = part + ((static_cast<size_t>(b) * p.H + h) * p.splits + split) * (2 + RV);
+  if (g == 0) {
+    w[0] = m;
+    w[1] = l;
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[2 + 16 * rt + 4 * g + e] = D[rt][e];
+}
+
+// ---- 3. merge splits, project once through W^V_t[h], finish ------------------------------------
+// grid (H, ceil(B / kQB)), 256 threads. W^V_t[h] is staged in LDS 64 rows at a time, as
+// [64][RV + 2] bf16 (the padding keeps the column reads of consecutive rows in distinct banks).
+constexpr int kWRows = 64;
+
+template <int RV>
+__global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const float* part) {
+  constexpr int WROW = RV + 2;
+  __shared__ __attribute__((aligned(16))) uint16_t w_s[kWRows * WROW];
+  __shared__ float a_s[kQB][RV];
+  __shared__ float q_s[kQB][128];
+  __shared__ float fin_s[kQB][4];  // f_lat, p_self, 1/den, l
+  const int h = blockIdx.x;
+  const int b0 = blockIdx.y * kQB;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int S_ = p.splits;
+
+  for (int i = tid; i < kQB * p.d; i += 256) {
+    const int bb = i / p.d;
+    const int j = i - bb * p.d;
+    const int b = b0 + bb;
+    q_s[bb][j] = b < p.B ? ld<BF16>(p.q, (static_cast<size_t>(b) * p.H + h) * p.d + j) : 0.f;
+  }
+  __syncthreads();
+  for (int bb = wave; bb < kQB; bb += 4) {
+    const int b = b0 + bb;
+    if (b >= p.B) continue;
+    const float* pw = part + (static_cast<size_t>(b) * p.H + h) * S_ * (2 + RV);
+    float ms = kNegInf;
+    float ls = 0.f;
+    if (lane < S_) {
+      ms = pw[static_cast<size_t>(lane) * (2 + RV)];
+      ls = pw[static_cast<size_t>(lane) * (2 + RV) + 1];
+    }
+    const float M = wave_max(ms);
+    const float fs = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
+    const float l = wave_sum(fs * ls);
+    for (int r = lane; r < RV; r += 64) {
+      float a = 0.f;
+      for (int s = 0; s < S_; ++s) a += __shfl(fs, s, 64) * pw[static_cast<size_t>(s) * (2 + RV) + 2 + r];
+      a_s[bb][r] = a;
+    }
+    float s_self = kNegInf;
+    if (p.k_self != nullptr) {
+      float pt = 0.f;
+      for (int j = lane; j < p.d; j += 64)
+        pt += q_s[bb][j] * ld<BF16>(p.k_self, (static_cast<size_t>(b) * p.H + h) * p.d + j);
+      s_self = wave_sum(pt) * p.scale_log2;
+    }
+    const float M2 = fmaxf(M, s_self);
+    const float f_lat = (M == kNegInf) ? 0.f : fast_exp2(M - M2);
+    const float p_self = (s_self == kNegInf) ? 0.f : fast_exp2(s_self - M2);
+    const float den = l * f_lat + p_self;
+    if (lane == 0) {
+      fin_s[bb][0] = f_lat;
+      fin_s[bb][1] = p_self;
+      fin_s[bb][2] = den > 0.f ? 1.0f / den : 0.f;
+      fin_s[bb][3] = l;
+      if (p.lse != nullptr)
+        p.lse[static_cast<size_t>(b) * p.H + h] = den > 0.f ? (M2 + fast_log2(den)) * kLn2 : kNegInf;
+    }
+  }
+  const size_t wrow = (static_cast<size_t>(p.t) * p.H + h) * p.d;  // W^V_t rows of head h; also mu offset
+  const uint32_t* wsrc = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.Wv) + wrow * RV);
+  for (int j0 = 0; j0 < p.d; j0 += kWRows) {
+    const int rows = min(kWRows, p.d - j0);
+    __syncthreads();  // previous chunk consumed (and, first time, a_s / fin_s written)
+    for (int i = tid; i < rows * (RV / 2); i += 256) {
+      const int j = i / (RV / 2);
+      const int c = i - j * (RV / 2);
+      reinterpret_cast<uint32_t*>(w_s)[j * (WROW / 2) + c] = wsrc[static_cast<size_t>(j0) * (RV / 2) + i];
+    }
+    __syncthreads();
+    for (int i = tid; i < kQB * rows; i += 256) {
+      const int bb = i / rows;
+      const int jj = i - bb * rows;
+      const int b = b0 + bb;
+      if (b >= p.B) continue;
+      const uint32_t* wr = reinterpret_cast<const uint32_t*>(w_s) + jj * (WROW / 2);
+      float o = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < RV / 2; ++c) {
+        const uint32_t wv = wr[c];
+        o += bf16_lo(wv) * a_s[bb][2 * c] + bf16_hi(wv) * a_s[bb][2 * c + 1];
+      }
+      const int j = j0 + jj;
+      if (p.mu_v != nullptr) o += fin_s[bb][3] * ld<BF16>(p.mu_v, wrow + j);
+      o *= fin_s[bb][0];
+      const size_t oi = (static_cast<size_t>(b) * p.H + h) * p.d + j;
+      if (p.v_self != nullptr) o += fin_s[bb][1] * ld<BF16>(p.v_self, oi);
+      st<BF16>(p.out, oi, o * fin_s[bb][2]);
+    }
+  }
+}
+
+struct Entry2d {
+  int r_k, r_v;
+  void (*qproj)(DecodeParams, float*, float*);
+  void (*partial)(DecodeParams, const float*, const float*, float*);
+  void (*combine)(DecodeParams, const float*);
+};
+
+template <int RK, int RV>
+constexpr Entry2d entry2d() {
+  return {RK, RV, qproj2d_kernel<RK>, decode2d_partial_kernel<RK, RV>, combine2d_kernel<RV>};
+}
+
+const Entry2d kTable2d[] = {
+    entry2d<32, 32>(), entry2d<64, 64>(), entry2d<128, 128>(), entry2d<256, 256>(),
+    entry2d<96, 160>(),
+};
+
+const Entry2d* find2d(int r_k, int r_v) {
+  for (const Entry2d& e : kTable2d)
+    if (e.r_k == r_k && e.r_v == r_v) return &e;
+  return nullptr;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+bool decode2d_mfma_supported(int dtype, int r_k, int r_v, int d_head) {
+  return dtype == LLA_BF16 && d_head <= 128 && find2d(r_k, r_v) != nullptr;
+}
+
+void decode2d_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
+  const int hg = (desc.H + 15) / 16;
+  const long wgs = static_cast<long>(B) * hg;
+  const long target = 768;  // three 256-thread workgroups on each of 256 CUs
+  int s = static_cast<int>((target + wgs - 1) / wgs);
+  const int max_by_len = desc.n_max / 256 > 0 ? desc.n_max / 256 : 1;
+  if (s > max_by_len) s = max_by_len;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  int c = (desc.n_max + s - 1) / s;
+  c = (c + 63) / 64 * 64;
+  s = (desc.n_max + c - 1) / c;
+  *splits = s;
+  *chunk = c;
+}
+
+size_t decode2d_workspace_bytes(const lla_desc& desc, int B) {
+  int s, c;
+  decode2d_plan(desc, B, &s, &c);
+  const size_t bh = static_cast<size_t>(B) * desc.H;
+  return align256(bh * desc.r_k * 4) + align256(bh * 4) + bh * s * (2 + desc.r_v) * 4;
+}
+
+hipError_t launch_decode2d(const DecodeParams& p0, hipStream_t stream) {
+  const Entry2d* e = find2d(p0.r_k, p0.r_v);
+  if (e == nullptr || p0.d > 128) return hipErrorNotSupported;
+  DecodeParams p = p0;
+  lla_desc d{};
+  d.H = p.H;
+  d.n_max = p.n_max;
+  decode2d_plan(d, p.B, &p.splits, &p.chunk);
+  const size_t bh = static_cast<size_t>(p.B) * p.H;
+  char* ws = reinterpret_cast<char*>(p.ws);
+  float* qt = reinterpret_cast<float*>(ws);
+  float* beta = reinterpret_cast<float*>(ws + align256(bh * p.r_k * 4));
+  float* part = reinterpret_cast<float*>(ws + align256(bh * p.r_k * 4) + align256(bh * 4));
+  const unsigned qb = (p.B + kQB - 1) / kQB;
+  hipLaunchKernelGGL(e->qproj, dim3(p.H, qb), dim3(256), 0, stream, p, qt, beta);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(e->partial, dim3(p.splits, p.B, (p.H + 15) / 16), dim3(256), 0, stream, p, qt,
+                     beta, part);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(e->combine, dim3(p.H, qb), dim3(256), 0, stream, p, part);
+  return hipGetLastError();
+}
+
+}  // namespace lla

@@ -58,9 +58,19 @@ struct PrefillParams {
   float scale_log2;
 };
 
-// Split heuristic shared by lla_workspace_bytes and lla_attend_decode.
+// Split heuristic of the streaming (VALU) decode, shared by lla_workspace_bytes and the launchers.
 void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk);
+// Workspace of one lla_attend_decode call (dispatches to the 2D MFMA sizing when that path runs).
 size_t decode_workspace_bytes(const lla_desc& desc, int B);
+// Workspace of the streaming decode kernels for `rows` query rows (decode or prefill rows).
+size_t valu_workspace_bytes(const lla_desc& desc, int rows);
+bool valu_supported(int variant, int dtype, int r_k, int r_v);
+bool decode_uses_mfma2d(const lla_desc& desc);
+// LLA-2D MFMA decode (decode2d.hip).
+bool decode2d_mfma_supported(int dtype, int r_k, int r_v, int d_head);
+void decode2d_plan(const lla_desc& desc, int B, int* splits, int* chunk);
+size_t decode2d_workspace_bytes(const lla_desc& desc, int B);
+hipError_t launch_decode2d(const DecodeParams& p, hipStream_t s);
 size_t prefill_workspace_bytes(const lla_desc& desc, int B, int C);
 
 // Launchers: return hipSuccess, or hipErrorNotSupported when no kernel is compiled for the
@@ -69,7 +79,7 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t s);
 hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, hipStream_t s);
 
-bool decode_supported(int variant, int dtype, int r_k, int r_v);
+bool decode_supported(int variant, int dtype, int r_k, int r_v, int d_head);
 bool encode_supported(int dtype, int r);
 bool prefill_supported(int variant, int dtype, int r_k, int r_v);
 

@@ -14,11 +14,11 @@
 namespace lla {
 
 bool prefill_supported(int variant, int dtype, int r_k, int r_v) {
-  return decode_supported(variant, dtype, r_k, r_v);
+  return valu_supported(variant, dtype, r_k, r_v);
 }
 
 size_t prefill_workspace_bytes(const lla_desc& desc, int B, int C) {
-  return decode_workspace_bytes(desc, B * C);
+  return valu_workspace_bytes(desc, B * C);
 }
 
 hipError_t launch_prefill(const PrefillParams& pp, int dtype, hipStream_t stream) {

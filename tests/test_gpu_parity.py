@@ -349,3 +349,22 @@ def test_lla2d_decode_full_size_sampled():
     """LLA-2D decode (r=256+256, B=128, N=8192): rows 0 and 127, all loops."""
     s = synth.CASES["lla2d"].with_(C=1)
     _check_sampled(s, [0, 127], range(s.T), "lla2d")
+
+
+@pytest.mark.parametrize("rk,rv", [(32, 32), (64, 64), (128, 128), (96, 160), (256, 256)])
+def test_decode_2d_mfma(rk, rv):
+    """LLA-2D bf16 decode on the MFMA path: two head groups (H=20), ragged lengths, mu, self token,
+    plain and 8x sharpened queries."""
+    dtype = "bf16"
+    B, H, d, T, n_max = 5, 20, 64, 2, 1000
+    lens = [1000, 999, 17, 0, 640]
+    for gain, mu, self_token in ((1.0, True, True), (8.0, False, True), (1.0, True, False)):
+        c = upload(synth.random_case("2d", dtype, B, H, d, T, rk, rv, n_max, 7600 + rk + rv,
+                                     with_mu=mu, q_gain=gain), dtype)
+        desc = mk_desc("2d", dtype, H, d, T, rk, rv, n_max)
+        for t in range(T):
+            o, lse = gpu_decode(desc, B, t, c, dtype, lens, self_token, mu)
+            ro, rl = oracle_decode(c, t, lens, "2d", self_token, mu)
+            what = f"2d mfma r=({rk},{rv}) gain={gain} mu={mu} self={self_token} t={t}"
+            assert_close(o, ro, dtype, what)
+            assert_lse(lse, rl, what)
