@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="capacity",
-                    choices=["capacity", "ouro_layer", "deep_loop"])
+                    choices=["capacity", "ouro_layer", "deep_loop", "lla2d"])
     ap.add_argument("--layers", type=int, default=None, help="override the layer count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -94,23 +94,32 @@ def main():
     B, H, d, T, rk, rv, N = s.B, s.H, s.d, s.T, s.r_k, s.r_v, s.N
     n_max = N + 1
     bf = torch.bfloat16
-    desc = lla.make_desc(lla.LLA_PER_HEAD, lla.LLA_BF16, H, d, T, rk, rv, n_max)
+    two_d = s.variant == "2d"
+    desc = lla.make_desc(lla.LLA_2D if two_d else lla.LLA_PER_HEAD, lla.LLA_BF16, H, d, T, rk, rv, n_max)
     print(f"# workload {s.name}: D={D} H={H} d={d} T={T} r=({rk},{rv}) B={B} N={N}", file=sys.stderr, flush=True)
 
     # ---- resident inputs --------------------------------------------------------------------
     t0 = time.time()
     zk, zv, Wk, Wv, Ek, Ev = [], [], [], [], [], []
+    zsk = (B, n_max, rk) if two_d else (B, H, n_max, rk)
+    zsv = (B, n_max, rv) if two_d else (B, H, n_max, rv)
     for l in range(D):
-        zk.append(synth.device_normal_(torch.empty(B, H, n_max, rk, dtype=bf, device="cuda"),
+        zk.append(synth.device_normal_(torch.empty(zsk, dtype=bf, device="cuda"),
                                        synth.seed(s.case, synth.SEED_ZK, l)))
-        zv.append(synth.device_normal_(torch.empty(B, H, n_max, rv, dtype=bf, device="cuda"),
+        zv.append(synth.device_normal_(torch.empty(zsv, dtype=bf, device="cuda"),
                                        synth.seed(s.case, synth.SEED_ZV, l)))
-        wk = synth.orthonormal_W(T, H, d, rk, synth.seed(s.case, synth.SEED_WK, l), "bf16")
-        wv = synth.orthonormal_W(T, H, d, rv, synth.seed(s.case, synth.SEED_WV, l), "bf16")
+        if two_d:
+            wk = synth.orthonormal_W_2d(T, H, d, rk, synth.seed(s.case, synth.SEED_WK, l), "bf16")
+            wv = synth.orthonormal_W_2d(T, H, d, rv, synth.seed(s.case, synth.SEED_WV, l), "bf16")
+            ek, ev = synth.pinv_E_from_W_2d(wk, "bf16"), synth.pinv_E_from_W_2d(wv, "bf16")
+        else:
+            wk = synth.orthonormal_W(T, H, d, rk, synth.seed(s.case, synth.SEED_WK, l), "bf16")
+            wv = synth.orthonormal_W(T, H, d, rv, synth.seed(s.case, synth.SEED_WV, l), "bf16")
+            ek, ev = synth.pinv_E_from_W(wk, "bf16"), synth.pinv_E_from_W(wv, "bf16")
         Wk.append(torch.from_numpy(wk).to(bf).cuda())
         Wv.append(torch.from_numpy(wv).to(bf).cuda())
-        Ek.append(torch.from_numpy(synth.pinv_E_from_W(wk, "bf16")).to(bf).cuda())
-        Ev.append(torch.from_numpy(synth.pinv_E_from_W(wv, "bf16")).to(bf).cuda())
+        Ek.append(torch.from_numpy(ek).to(bf).cuda())
+        Ev.append(torch.from_numpy(ev).to(bf).cuda())
     q = synth.device_normal_(torch.empty(T, D, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_Q))
     kself = synth.device_normal_(torch.empty(T, D, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF))
     vself = synth.device_normal_(torch.empty(T, D, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF) + 1)
@@ -171,13 +180,21 @@ def main():
         del a, b
 
     tokens_per_s = B / (ms_step / 1e3)
-    latent_bytes = B * H * N * (rk + rv) * 2  # per launch: every (sequence, head, token) latent pair
+    H_lat = 1 if two_d else H
+    latent_bytes = B * H_lat * N * (rk + rv) * 2  # per read: every cached latent pair, once
     achieved = latent_bytes / (avg_launch_ms / 1e3) / 1e9
     traffic = load_traffic() if args.workload == "capacity" and D == s.D else None
 
     # ---- CPU oracle baseline --------------------------------------------------------------------
     cpu = None
-    if not args.no_cpu_baseline:
+    if two_d:
+        # MFMA work per read: scores and latent-V products for every (sequence, head, token)
+        flops = 2.0 * B * H * N * (rk + rv)
+        res_extra = {"mfma_tflops": round(flops / (avg_launch_ms / 1e3) / 1e12, 2),
+                     "mfma_util_bf16_dense": round(flops / (avg_launch_ms / 1e3) / 2.5e15, 4)}
+    else:
+        res_extra = {}
+    if not args.no_cpu_baseline and not two_d:
         cpu = cpu_baseline(args, s, D, zk, zv, Wk, Wv, Ek, Ev, q, kself, vself, xk, xv, lens)
 
     res = {
@@ -197,8 +214,8 @@ def main():
             "workload": f"{s.name}: {D} layers, H={H}, d_head={d}, T={T}, r_k={rk}, r_v={rv}, "
                         f"B={B}, N={N} cached tokens, bf16 latents",
             "layers": D, "batch": B, "context": N, "heads": H, "d_head": d, "loops": T,
-            "r_k": rk, "r_v": rv, "variant": "per_head",
-            "compression": round(2 * T * d / (rk + rv), 2),
+            "r_k": rk, "r_v": rv, "variant": s.variant,
+            "compression": round(2 * T * d * (H if two_d else 1) / (rk + rv), 2),
             "resident_latent_bytes": resident,
             "reads_per_step": D * T, "encodes_per_step": D,
         },
@@ -206,7 +223,8 @@ def main():
         "latent_frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": f"decode_partial_kernel<BF16,{rk},{rv}> (one launch per read)",
+            "kernel": (f"decode2d qproj + partial<{rk},{rv}> (MFMA) + combine per read" if two_d else
+                       f"decode_partial_kernel<BF16,{rk},{rv}> (one launch per read)"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -217,6 +235,7 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    res.update(res_extra)
     print(json.dumps(res), flush=True)
 
 

@@ -37,6 +37,7 @@ float scale_log2(const lla_desc* d) {
 lla_status from_hip(hipError_t e) {
   if (e == hipSuccess) return LLA_OK;
   if (e == hipErrorNotSupported) return LLA_ERR_UNSUPPORTED;
+  if (e == hipErrorInvalidValue) return LLA_ERR_WORKSPACE;  // a launcher refused an unfitting plan
   return LLA_ERR_HIP;
 }
 
@@ -148,6 +149,7 @@ lla_status lla_attend_decode(const lla_desc* desc, int32_t B, int32_t t, const v
   p.causal = 0;
   p.variant = desc->variant;
   p.scale_log2 = scale_log2(desc);
+  p.ws_bytes = ws == nullptr ? 0 : ws_bytes;
   lla::decode_plan(*desc, B, &p.splits, &p.chunk);
   return from_hip(lla::launch_decode(p, desc->dtype, static_cast<hipStream_t>(stream)));
 }
@@ -191,6 +193,8 @@ lla_status lla_attend_prefill(const lla_desc* desc, int32_t B, int32_t C, int32_
   p.r_v = desc->r_v;
   p.variant = desc->variant;
   p.scale_log2 = scale_log2(desc);
+  p.ws_bytes = ws == nullptr ? 0 : ws_bytes;
+  lla::prefill_plan(*desc, B, C, &p.splits, &p.chunk);
   return from_hip(lla::launch_prefill(p, desc->dtype, static_cast<hipStream_t>(stream)));
 }
 

@@ -314,7 +314,7 @@ bool decode_uses_mfma2d(const lla_desc& desc) {
   return desc.variant == LLA_2D && decode2d_mfma_supported(desc.dtype, desc.r_k, desc.r_v, desc.d_head);
 }
 
-void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
+void valu_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
   // Enough waves to cover 256 CUs several times over, but no split shorter than 256 tokens.
   const long units = static_cast<long>(B) * desc.H;
   const int target_waves = 4096;
@@ -331,16 +331,23 @@ void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
   *chunk = c;
 }
 
-size_t decode_workspace_bytes(const lla_desc& desc, int B) {
-  if (decode_uses_mfma2d(desc)) return decode2d_workspace_bytes(desc, B);
-  return valu_workspace_bytes(desc, B);
+void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
+  if (decode_uses_mfma2d(desc))
+    decode2d_plan(desc, B, splits, chunk);
+  else
+    valu_plan(desc, B, splits, chunk);
 }
 
-size_t valu_workspace_bytes(const lla_desc& desc, int B) {
+size_t decode_workspace_bytes(const lla_desc& desc, int B) {
   int s, c;
   decode_plan(desc, B, &s, &c);
-  if (s <= 1) return 0;
-  return static_cast<size_t>(B) * desc.H * s * (2 + desc.r_v) * sizeof(float);
+  if (decode_uses_mfma2d(desc)) return decode2d_workspace_bytes(desc, B, s);
+  return valu_workspace_bytes(desc, B, s);
+}
+
+size_t valu_workspace_bytes(const lla_desc& desc, int rows, int splits) {
+  if (splits <= 1) return 0;
+  return static_cast<size_t>(rows) * desc.H * splits * (2 + desc.r_v) * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream) {
@@ -350,6 +357,9 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream) {
     return launch_decode2d(p, stream);
   const Entry* e = find(dtype, p.r_k, p.r_v);
   if (e == nullptr) return hipErrorNotSupported;
+  if (p.splits > 1 &&
+      static_cast<size_t>(p.B) * p.H * p.splits * (2 + p.r_v) * sizeof(float) > p.ws_bytes)
+    return hipErrorInvalidValue;  // the plan does not fit the workspace: never launch
   const unsigned units = static_cast<unsigned>(p.B) * p.H * p.splits;
   hipLaunchKernelGGL(e->fn, dim3(units), dim3(64), 0, stream, p);
   hipError_t err = hipGetLastError();

@@ -67,6 +67,7 @@ __global__ __launch_bounds__(256) void qproj2d_kernel(DecodeParams p, float* qt,
     float acc[kQB];
 #pragma unroll
     for (int bb = 0; bb < kQB; ++bb) acc[bb] = 0.f;
+#pragma unroll 8
     for (int j = 0; j < p.d; ++j) {
       const float w = ld<BF16>(p.Wk, (wrow + j) * RK + k);
 #pragma unroll
@@ -276,98 +277,80 @@ __global__ __launch_bounds__(256) void decode2d_partial_kernel(DecodeParams p, c
 }
 
 // ---- 3. merge splits, project once through W^V_t[h], finish ------------------------------------
-// grid (H, ceil(B / kQB)), 256 threads. W^V_t[h] is staged in LDS 64 rows at a time, as
-// [64][RV + 2] bf16 (the padding keeps the column reads of consecutive rows in distinct banks).
-constexpr int kWRows = 64;
-
+// One 256-thread workgroup per (b, h): wave 0 merges the split partials by log-sum-exp and scores
+// the optional self token; all threads form a = sum_s f_s a_s; then thread pair (j, half) dots
+// row j of W^V_t[h] (read as 16-byte runs) with half of a, and the pair's sum finishes o[j].
 template <int RV>
 __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const float* part) {
-  constexpr int WROW = RV + 2;
-  __shared__ __attribute__((aligned(16))) uint16_t w_s[kWRows * WROW];
-  __shared__ float a_s[kQB][RV];
-  __shared__ float q_s[kQB][128];
-  __shared__ float fin_s[kQB][4];  // f_lat, p_self, 1/den, l
-  const int h = blockIdx.x;
-  const int b0 = blockIdx.y * kQB;
+  constexpr int HALF = RV / 2;
+  static_assert(HALF % 8 == 0, "half a W^V row must be whole 16-byte runs");
+  __shared__ float a_s[RV];
+  __shared__ float f_s[64];
+  __shared__ float fin_s[4];  // f_lat, p_self, 1/den, l
+  const int b = blockIdx.x;
+  const int h = blockIdx.y;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
   const int lane = tid & 63;
   const int S_ = p.splits;
+  const size_t bh = static_cast<size_t>(b) * p.H + h;
+  const float* pw = part + bh * S_ * (2 + RV);
 
-  for (int i = tid; i < kQB * p.d; i += 256) {
-    const int bb = i / p.d;
-    const int j = i - bb * p.d;
-    const int b = b0 + bb;
-    q_s[bb][j] = b < p.B ? ld<BF16>(p.q, (static_cast<size_t>(b) * p.H + h) * p.d + j) : 0.f;
-  }
-  __syncthreads();
-  for (int bb = wave; bb < kQB; bb += 4) {
-    const int b = b0 + bb;
-    if (b >= p.B) continue;
-    const float* pw = part + (static_cast<size_t>(b) * p.H + h) * S_ * (2 + RV);
+  if (tid < 64) {
     float ms = kNegInf;
     float ls = 0.f;
     if (lane < S_) {
       ms = pw[static_cast<size_t>(lane) * (2 + RV)];
       ls = pw[static_cast<size_t>(lane) * (2 + RV) + 1];
     }
+    float pt = 0.f;
+    if (p.k_self != nullptr)
+      for (int j = lane; j < p.d; j += 64) pt += ld<BF16>(p.q, bh * p.d + j) * ld<BF16>(p.k_self, bh * p.d + j);
     const float M = wave_max(ms);
     const float fs = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
     const float l = wave_sum(fs * ls);
-    for (int r = lane; r < RV; r += 64) {
-      float a = 0.f;
-      for (int s = 0; s < S_; ++s) a += __shfl(fs, s, 64) * pw[static_cast<size_t>(s) * (2 + RV) + 2 + r];
-      a_s[bb][r] = a;
-    }
-    float s_self = kNegInf;
-    if (p.k_self != nullptr) {
-      float pt = 0.f;
-      for (int j = lane; j < p.d; j += 64)
-        pt += q_s[bb][j] * ld<BF16>(p.k_self, (static_cast<size_t>(b) * p.H + h) * p.d + j);
-      s_self = wave_sum(pt) * p.scale_log2;
-    }
+    const float s_self = p.k_self != nullptr ? wave_sum(pt) * p.scale_log2 : kNegInf;
+    f_s[lane] = fs;
     const float M2 = fmaxf(M, s_self);
     const float f_lat = (M == kNegInf) ? 0.f : fast_exp2(M - M2);
     const float p_self = (s_self == kNegInf) ? 0.f : fast_exp2(s_self - M2);
     const float den = l * f_lat + p_self;
     if (lane == 0) {
-      fin_s[bb][0] = f_lat;
-      fin_s[bb][1] = p_self;
-      fin_s[bb][2] = den > 0.f ? 1.0f / den : 0.f;
-      fin_s[bb][3] = l;
-      if (p.lse != nullptr)
-        p.lse[static_cast<size_t>(b) * p.H + h] = den > 0.f ? (M2 + fast_log2(den)) * kLn2 : kNegInf;
+      fin_s[0] = f_lat;
+      fin_s[1] = p_self;
+      fin_s[2] = den > 0.f ? 1.0f / den : 0.f;
+      fin_s[3] = l;
+      if (p.lse != nullptr) p.lse[bh] = den > 0.f ? (M2 + fast_log2(den)) * kLn2 : kNegInf;
     }
   }
-  const size_t wrow = (static_cast<size_t>(p.t) * p.H + h) * p.d;  // W^V_t rows of head h; also mu offset
-  const uint32_t* wsrc = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.Wv) + wrow * RV);
-  for (int j0 = 0; j0 < p.d; j0 += kWRows) {
-    const int rows = min(kWRows, p.d - j0);
-    __syncthreads();  // previous chunk consumed (and, first time, a_s / fin_s written)
-    for (int i = tid; i < rows * (RV / 2); i += 256) {
-      const int j = i / (RV / 2);
-      const int c = i - j * (RV / 2);
-      reinterpret_cast<uint32_t*>(w_s)[j * (WROW / 2) + c] = wsrc[static_cast<size_t>(j0) * (RV / 2) + i];
+  __syncthreads();
+  for (int r = tid; r < RV; r += 256) {
+    float a = 0.f;
+    for (int s = 0; s < S_; ++s) a += f_s[s] * pw[static_cast<size_t>(s) * (2 + RV) + 2 + r];
+    a_s[r] = a;
+  }
+  __syncthreads();
+  const int half = tid & 1;
+  const size_t wrow = (static_cast<size_t>(p.t) * p.H + h) * p.d;  // W^V_t rows of head h; mu offset
+  for (int j = tid >> 1; j < p.d; j += 128) {
+    const uint4* wr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.Wv) + (wrow + j) * RV + half * HALF);
+    const float* ah = a_s + half * HALF;
+    uint4 w[HALF / 8];
+#pragma unroll
+    for (int i = 0; i < HALF / 8; ++i) w[i] = wr[i];
+    float o = 0.f;
+#pragma unroll
+    for (int i = 0; i < HALF / 8; ++i) {
+      o += bf16_lo(w[i].x) * ah[8 * i + 0] + bf16_hi(w[i].x) * ah[8 * i + 1];
+      o += bf16_lo(w[i].y) * ah[8 * i + 2] + bf16_hi(w[i].y) * ah[8 * i + 3];
+      o += bf16_lo(w[i].z) * ah[8 * i + 4] + bf16_hi(w[i].z) * ah[8 * i + 5];
+      o += bf16_lo(w[i].w) * ah[8 * i + 6] + bf16_hi(w[i].w) * ah[8 * i + 7];
     }
-    __syncthreads();
-    for (int i = tid; i < kQB * rows; i += 256) {
-      const int bb = i / rows;
-      const int jj = i - bb * rows;
-      const int b = b0 + bb;
-      if (b >= p.B) continue;
-      const uint32_t* wr = reinterpret_cast<const uint32_t*>(w_s) + jj * (WROW / 2);
-      float o = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < RV / 2; ++c) {
-        const uint32_t wv = wr[c];
-        o += bf16_lo(wv) * a_s[bb][2 * c] + bf16_hi(wv) * a_s[bb][2 * c + 1];
-      }
-      const int j = j0 + jj;
-      if (p.mu_v != nullptr) o += fin_s[bb][3] * ld<BF16>(p.mu_v, wrow + j);
-      o *= fin_s[bb][0];
-      const size_t oi = (static_cast<size_t>(b) * p.H + h) * p.d + j;
-      if (p.v_self != nullptr) o += fin_s[bb][1] * ld<BF16>(p.v_self, oi);
-      st<BF16>(p.out, oi, o * fin_s[bb][2]);
+    o += __shfl_xor(o, 1, 64);
+    if (half == 0) {
+      if (p.mu_v != nullptr) o += fin_s[3] * ld<BF16>(p.mu_v, wrow + j);
+      o *= fin_s[0];
+      if (p.v_self != nullptr) o += fin_s[1] * ld<BF16>(p.v_self, bh * p.d + j);
+      st<BF16>(p.out, bh * p.d + j, o * fin_s[2]);
     }
   }
 }
@@ -406,7 +389,8 @@ bool decode2d_mfma_supported(int dtype, int r_k, int r_v, int d_head) {
 void decode2d_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
   const int hg = (desc.H + 15) / 16;
   const long wgs = static_cast<long>(B) * hg;
-  const long target = 768;  // three 256-thread workgroups on each of 256 CUs
+  // one full round of resident workgroups: the r_v = 256 kernel fits two per CU, smaller three
+  const long target = 256L * (desc.r_v > 160 ? 2 : 3);
   int s = static_cast<int>((target + wgs - 1) / wgs);
   const int max_by_len = desc.n_max / 256 > 0 ? desc.n_max / 256 : 1;
   if (s > max_by_len) s = max_by_len;
@@ -419,21 +403,21 @@ void decode2d_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
   *chunk = c;
 }
 
-size_t decode2d_workspace_bytes(const lla_desc& desc, int B) {
-  int s, c;
-  decode2d_plan(desc, B, &s, &c);
+size_t decode2d_workspace_bytes(const lla_desc& desc, int B, int splits) {
   const size_t bh = static_cast<size_t>(B) * desc.H;
-  return align256(bh * desc.r_k * 4) + align256(bh * 4) + bh * s * (2 + desc.r_v) * 4;
+  return align256(bh * desc.r_k * 4) + align256(bh * 4) + bh * splits * (2 + desc.r_v) * 4;
 }
 
 hipError_t launch_decode2d(const DecodeParams& p0, hipStream_t stream) {
   const Entry2d* e = find2d(p0.r_k, p0.r_v);
   if (e == nullptr || p0.d > 128) return hipErrorNotSupported;
-  DecodeParams p = p0;
+  const DecodeParams& p = p0;  // splits and chunk were planned by the caller with decode2d_plan
   lla_desc d{};
   d.H = p.H;
-  d.n_max = p.n_max;
-  decode2d_plan(d, p.B, &p.splits, &p.chunk);
+  d.r_k = p.r_k;
+  d.r_v = p.r_v;
+  if (p.splits < 1 || p.splits > 64 || decode2d_workspace_bytes(d, p.B, p.splits) > p.ws_bytes)
+    return hipErrorInvalidValue;  // the plan does not fit the workspace: never launch
   const size_t bh = static_cast<size_t>(p.B) * p.H;
   char* ws = reinterpret_cast<char*>(p.ws);
   float* qt = reinterpret_cast<float*>(ws);
@@ -447,7 +431,7 @@ hipError_t launch_decode2d(const DecodeParams& p0, hipStream_t stream) {
                      beta, part);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(e->combine, dim3(p.H, qb), dim3(256), 0, stream, p, part);
+  hipLaunchKernelGGL(e->combine, dim3(p.B, p.H), dim3(256), 0, stream, p, part);
   return hipGetLastError();
 }
 

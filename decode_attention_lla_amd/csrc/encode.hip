@@ -7,9 +7,18 @@
 // this kernel as one "head" of width H*d.
 //
 // The input x is [B][C][T][H][d]: for fixed (b, c, h) the stack is T runs of d contiguous values,
-// H*d apart. One workgroup of 256 threads handles NTOK consecutive tokens (b, c) of one head: it
-// stages x - mu for those tokens in LDS as float32, then each wave produces whole latent rows,
-// reading E once per row for all NTOK tokens.
+// H*d apart.
+//
+// bf16 storage: a GEMM per head on MFMA, Z^T[token][r] = X[token][k] . E[r][k]^T with
+// v_mfma_f32_16x16x32_bf16. Both operands are read straight from memory as 16-byte runs along k
+// (a run of 8 never straddles two loops because d_head is a multiple of 8). A wave owns 32 tokens x
+// 16*NT latent rows. For small token counts (decode) the four waves of a workgroup split K and
+// reduce through LDS; for large ones (prefill chunks) they take four token tiles. E mu is computed
+// by the same MFMA (mu as the only non-zero row of an A tile) and subtracted from the float32
+// accumulators, so x - mu is never rounded.
+//
+// fp32 storage: one 256-thread workgroup handles NTOK tokens of one head: x - mu for those tokens
+// is staged in LDS as float32 and each wave produces whole latent rows.
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -78,6 +87,177 @@ __global__ __launch_bounds__(kThreads) void encode_valu_kernel(EncodeParams p) {
   }
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4_t mfma(uint4 a, uint4 b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// NT: 16-column latent tiles per wave. KSPLIT 4: the 4 waves share 32 tokens and split K;
+// KSPLIT 1: each wave has its own 32 tokens and the whole K.
+template <int NT, int KSPLIT>
+__global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeParams p) {
+  constexpr int U = 4;  // k-steps whose loads are issued together
+  constexpr int TOK_WG = KSPLIT == 4 ? 32 : 128;
+  __shared__ float red[KSPLIT == 4 ? 3 : 1][64][2 * NT * 4];
+  __shared__ float emu_s[4][16 * NT];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int K = p.T * p.d;
+  const int nk = (K + 31) / 32;
+  const int ntok = p.B * p.C;
+  const int h = blockIdx.z;
+  const int r0 = blockIdx.y * 16 * NT;
+  const int n_base = blockIdx.x * TOK_WG + (KSPLIT == 4 ? 0 : wave * 32);
+  const size_t HD = static_cast<size_t>(p.H) * p.d;
+  const uint16_t* x = static_cast<const uint16_t*>(p.x);
+  const uint16_t* E = static_cast<const uint16_t*>(p.E);
+
+  // E mu for this lane's latent rows, summed over the four waves' K quarters
+  float emu[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) emu[nt] = 0.f;
+  if (p.mu != nullptr) {
+    const uint16_t* mu = static_cast<const uint16_t*>(p.mu) + static_cast<size_t>(h) * K;
+    const int q4 = (nk + 3) / 4;
+    floatx4_t am[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) am[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ks = wave * q4; ks < min(nk, (wave + 1) * q4); ++ks) {
+      const int kk = 32 * ks + 8 * g;
+      const uint4 a = (col == 0 && kk < K) ? *reinterpret_cast<const uint4*>(mu + kk) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int r = r0 + 16 * nt + col;
+        const uint4 b = (r < p.r && kk < K) ? *reinterpret_cast<const uint4*>(E + (static_cast<size_t>(h) * p.r + r) * K + kk)
+                                           : make_uint4(0, 0, 0, 0);
+        am[nt] = mfma(a, b, am[nt]);
+      }
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) emu_s[wave][16 * nt + col] = am[nt][0];  // row 0 of C
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      emu[nt] = emu_s[0][16 * nt + col] + emu_s[1][16 * nt + col] + emu_s[2][16 * nt + col] + emu_s[3][16 * nt + col];
+  }
+
+  // token rows of the two A tiles, latent rows of the NT B tiles
+  const uint16_t* xrow[2];
+  bool nok[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int n = n_base + 16 * mt + col;
+    nok[mt] = n < ntok;
+    xrow[mt] = x + static_cast<size_t>(nok[mt] ? n : 0) * p.T * HD + static_cast<size_t>(h) * p.d;
+  }
+  const uint16_t* erow[NT];
+  bool rok[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = r0 + 16 * nt + col;
+    rok[nt] = r < p.r;
+    erow[nt] = E + (static_cast<size_t>(h) * p.r + (rok[nt] ? r : 0)) * K;
+  }
+
+  int kb = 0, ke = nk;
+  if (KSPLIT == 4) {
+    const int q4 = (nk + 3) / 4;
+    kb = min(nk, wave * q4);
+    ke = min(nk, kb + q4);
+  }
+  floatx4_t acc[2][NT];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int ks = kb; ks < ke; ks += U) {
+    uint4 a[U][2];
+    uint4 b[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = 32 * (ks + u) + 8 * g;
+      const bool kok = (ks + u) < ke && kk < K;
+      const int t = kok ? kk / p.d : 0;
+      const int j = kk - t * p.d;
+      const size_t xo = static_cast<size_t>(t) * HD + j;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        a[u][mt] = (kok && nok[mt]) ? *reinterpret_cast<const uint4*>(xrow[mt] + xo) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        b[u][nt] = (kok && rok[nt]) ? *reinterpret_cast<const uint4*>(erow[nt] + kk) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma(a[u][mt], b[u][nt], acc[mt][nt]);
+  }
+
+  if (KSPLIT == 4) {
+    if (wave > 0) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) red[wave - 1][lane][(mt * NT + nt) * 4 + e] = acc[mt][nt][e];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[mt][nt][e] += red[w][lane][(mt * NT + nt) * 4 + e];
+  }
+
+  // C layout: lane holds latent row r = r0 + 16 nt + col for tokens n_base + 16 mt + 4 g + e
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int n = n_base + 16 * mt + 4 * g + e;
+      if (n >= ntok) continue;
+      const int b = n / p.C;
+      const int c = n - b * p.C;
+      const int slot = p.pos[b] + c;
+      if (slot < 0 || slot >= p.n_max) continue;
+      uint16_t* z = static_cast<uint16_t*>(p.z) + ((static_cast<size_t>(b) * p.H + h) * p.n_max + slot) * p.r;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        if (rok[nt]) z[r0 + 16 * nt + col] = f32_to_bf16(acc[mt][nt][e] - emu[nt]);
+    }
+}
+
+template <int KSPLIT>
+hipError_t launch_encode_mfma(const EncodeParams& p, int nt_tiles, hipStream_t stream) {
+  constexpr int TOK_WG = KSPLIT == 4 ? 32 : 128;
+  const unsigned ntok = static_cast<unsigned>(p.B) * p.C;
+  dim3 grid((ntok + TOK_WG - 1) / TOK_WG, (p.r + 16 * nt_tiles - 1) / (16 * nt_tiles), p.H);
+  if (nt_tiles == 1)
+    hipLaunchKernelGGL((encode_mfma_kernel<1, KSPLIT>), grid, dim3(256), 0, stream, p);
+  else if (nt_tiles == 2)
+    hipLaunchKernelGGL((encode_mfma_kernel<2, KSPLIT>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((encode_mfma_kernel<4, KSPLIT>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool encode_supported(int dtype, int r) {
@@ -86,6 +266,14 @@ bool encode_supported(int dtype, int r) {
 
 hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t stream) {
   const int K = p.T * p.d;
+  if (dtype == LLA_BF16) {
+    const int nt_tiles = p.r <= 16 ? 1 : p.r <= 32 ? 2 : 4;
+    const long ntok = static_cast<long>(p.B) * p.C;
+    const long wgs1 = (ntok + 127) / 128 * ((p.r + 16 * nt_tiles - 1) / (16 * nt_tiles)) * p.H;
+    // few workgroups with whole-K waves would leave most of the chip idle: split K instead
+    return wgs1 < 1024 ? launch_encode_mfma<4>(p, nt_tiles, stream)
+                       : launch_encode_mfma<1>(p, nt_tiles, stream);
+  }
   if (K > kMaxK) return hipErrorNotSupported;
   const unsigned ntok = static_cast<unsigned>(p.B) * p.C;
   const int nt = K <= 1024 ? 8 : K <= 2048 ? 4 : K <= 4096 ? 2 : 1;

@@ -29,9 +29,10 @@ struct DecodeParams {
   int32_t rows_per_seq;
   int32_t causal;
   int32_t variant;    // LLA_PER_HEAD or LLA_2D
-  int32_t splits;     // S: token-range splits per (b, h)
+  int32_t splits;     // S: token-range splits per (b, h), from decode_plan / prefill_plan
   int32_t chunk;      // tokens per split
   float scale_log2;   // softmax scale * log2(e)
+  size_t ws_bytes;    // bytes available at ws; launchers refuse a plan that does not fit
 };
 
 struct EncodeParams {
@@ -55,21 +56,26 @@ struct PrefillParams {
   void* out;          // [B][C][H][d]
   void* ws;
   int32_t B, C, H, d, T, t, n_max, r_k, r_v, variant;
+  int32_t splits, chunk;  // from prefill_plan
   float scale_log2;
+  size_t ws_bytes;
 };
 
-// Split heuristic of the streaming (VALU) decode, shared by lla_workspace_bytes and the launchers.
+// Token-split plan of one lla_attend_decode call. The C ABI computes it once per call, sizes the
+// workspace from it and hands it to the launchers, which never re-plan.
 void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk);
-// Workspace of one lla_attend_decode call (dispatches to the 2D MFMA sizing when that path runs).
+void valu_plan(const lla_desc& desc, int rows, int* splits, int* chunk);
+void prefill_plan(const lla_desc& desc, int B, int C, int* splits, int* chunk);
+// Workspace of one lla_attend_decode call under decode_plan.
 size_t decode_workspace_bytes(const lla_desc& desc, int B);
-// Workspace of the streaming decode kernels for `rows` query rows (decode or prefill rows).
-size_t valu_workspace_bytes(const lla_desc& desc, int rows);
+// Workspace of the streaming decode kernels for `rows` query rows and a given split count.
+size_t valu_workspace_bytes(const lla_desc& desc, int rows, int splits);
 bool valu_supported(int variant, int dtype, int r_k, int r_v);
 bool decode_uses_mfma2d(const lla_desc& desc);
 // LLA-2D MFMA decode (decode2d.hip).
 bool decode2d_mfma_supported(int dtype, int r_k, int r_v, int d_head);
 void decode2d_plan(const lla_desc& desc, int B, int* splits, int* chunk);
-size_t decode2d_workspace_bytes(const lla_desc& desc, int B);
+size_t decode2d_workspace_bytes(const lla_desc& desc, int B, int splits);
 hipError_t launch_decode2d(const DecodeParams& p, hipStream_t s);
 size_t prefill_workspace_bytes(const lla_desc& desc, int B, int C);
 

@@ -17,8 +17,14 @@ bool prefill_supported(int variant, int dtype, int r_k, int r_v) {
   return valu_supported(variant, dtype, r_k, r_v);
 }
 
+void prefill_plan(const lla_desc& desc, int B, int C, int* splits, int* chunk) {
+  valu_plan(desc, B * C, splits, chunk);
+}
+
 size_t prefill_workspace_bytes(const lla_desc& desc, int B, int C) {
-  return valu_workspace_bytes(desc, B * C);
+  int s, c;
+  prefill_plan(desc, B, C, &s, &c);
+  return valu_workspace_bytes(desc, B * C, s);
 }
 
 hipError_t launch_prefill(const PrefillParams& pp, int dtype, hipStream_t stream) {
@@ -45,11 +51,9 @@ hipError_t launch_prefill(const PrefillParams& pp, int dtype, hipStream_t stream
   p.causal = 1;
   p.variant = pp.variant;
   p.scale_log2 = pp.scale_log2;
-  lla_desc d{};
-  d.H = pp.H;
-  d.n_max = pp.n_max;
-  d.r_v = pp.r_v;
-  decode_plan(d, p.B, &p.splits, &p.chunk);
+  p.splits = pp.splits;  // planned by the caller with prefill_plan
+  p.chunk = pp.chunk;
+  p.ws_bytes = pp.ws_bytes;
   return launch_decode(p, dtype, stream);
 }
 

@@ -136,3 +136,25 @@ def test_binding_checks_shapes_without_gpu():
     q = torch.zeros(2, 16, 128)  # CPU tensor: rejected before any library call
     with pytest.raises(ValueError):
         lla.lla_attend_decode(d, 2, 0, q, q, q, None, q, q, None, None, None, None, q)
+
+
+def test_2d_mfma_workspace_matches_its_plan():
+    """The LLA-2D MFMA decode needs q~, beta and split partials; the call refuses any smaller
+    workspace before launching (the split plan is computed once, by the call that sizes it)."""
+    d = desc(variant=lla.LLA_2D, r_k=256, r_v=256, n_max=8193)
+    need = lla.lla_workspace_bytes(d, 128, 1)
+    bh = 128 * 16
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    fixed = al(bh * 256 * 4) + al(bh * 4)
+    assert (need - fixed) % (bh * 258 * 4) == 0
+    splits = (need - fixed) // (bh * 258 * 4)
+    assert 1 <= splits <= 64
+    assert decode(d, B=128, ws=A, wsb=need - 1) == lla.LLA_ERR_WORKSPACE
+    assert decode(d, B=128) == lla.LLA_ERR_WORKSPACE
+
+
+def test_prefill_workspace_checked_before_launch():
+    d = desc(n_max=4097, r_k=24, r_v=24)
+    need = lla.lla_workspace_bytes(d, 2, 64)
+    if need > 0:
+        assert prefill(d, B=2, C=64, ws=A, wsb=need - 4) == lla.LLA_ERR_WORKSPACE
