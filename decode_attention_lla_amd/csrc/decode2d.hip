@@ -31,6 +31,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
+typedef const __attribute__((address_space(1))) void* gptr_t;  // global address space
+typedef __attribute__((address_space(3))) void* lptr_t;         // LDS address space
+
 constexpr float kLazy2d = 8.0f;
 constexpr int kQB = 8;     // sequences per qproj / combine workgroup
 
@@ -90,29 +93,41 @@ __global__ __launch_bounds__(256) void qproj2d_kernel(DecodeParams p, float* qt,
 }
 
 // ---- 2. MFMA latent stream ---------------------------------------------------------------------
+// One workgroup of kW waves per (sequence, token split, 16-head group); wave w takes the 16-token
+// tiles w, w + kW, ... of the split. Per tile:
+//   * the next tile's K rows are loaded into registers and its V rows go straight to LDS with
+//     global_load_lds (each lane's 16 bytes land at base + 16*lane), into the other half of the
+//     wave's double-buffered ring, so both loads overlap the current tile's MFMAs;
+//   * V rows are stored unpadded with 16-byte chunks XOR-swizzled by the row group: chunk c of
+//     row rho sits at (c & ~7) | ((c & 7) ^ 2*((rho >> 2) & 3)), which puts the four lane groups of
+//     the transposed 16-bit reads on disjoint banks. The swizzle is applied by choosing each lane's
+//     global source address;
+//   * rows past the valid range are clamped to the last valid token (finite data times a zero
+//     weight), so a partial tail tile needs no separate zeroing.
 template <int RK, int RV>
-struct Smem2d {
-  static constexpr int kVRow = RV * 2 + 8;                  // bytes per staged V row
-  static constexpr int kVStage = 16 * kVRow;                // one wave's 16-token V tile
-  static constexpr int kPart = 16 * (2 + RV) * 4;           // one (m, l, a) partial for 16 heads
-  static constexpr int kUnion = (4 * kVStage > 2 * kPart) ? 4 * kVStage : 2 * kPart;
+struct Cfg2d {
+  static constexpr int kW = 8;                          // waves per workgroup
+  static constexpr int kVTile = 16 * RV * 2;            // bytes of one 16-token V tile
+  static constexpr int kPart = 16 * (2 + RV) * 4;       // one (m, l, a) partial for 16 heads
+  static constexpr int kRing = kW * 2 * kVTile;         // all waves' double-buffered V rings
+  static_assert(kRing >= 4 * kPart, "the final merge reuses the V rings");
 };
 
 template <int RK, int RV>
-__global__ __launch_bounds__(256) void decode2d_partial_kernel(DecodeParams p, const float* qt,
+__global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, const float* qt,
                                                                const float* beta, float* part) {
+  using CF = Cfg2d<RK, RV>;
+  constexpr int kW = CF::kW;
   constexpr int KS = RK / 32;
   constexpr int RT = RV / 16;
-  constexpr int VCH = 2 * RV;         // 16-byte chunks in a 16-token V tile
-  constexpr int VPL = VCH / 64;       // chunks per lane
-  constexpr int CPR = RV / 8;         // chunks per V row
-  using SM = Smem2d<RK, RV>;
-  static_assert(RK % 32 == 0 && RV % 32 == 0, "ranks must be multiples of 32");
+  constexpr int CPR = RV / 8;          // 16-byte chunks per V row
+  constexpr int VPL = CPR / 4;         // chunks per lane for a 16-row tile (16*CPR / 64)
+  static_assert(RK % 32 == 0 && RV % 64 == 0, "r_k multiple of 32, r_v multiple of 64");
 
   __shared__ __attribute__((aligned(16))) uint16_t qhi[16 * RK];
   __shared__ __attribute__((aligned(16))) uint16_t qlo[16 * RK];
   __shared__ float beta_s[16];
-  __shared__ __attribute__((aligned(16))) char smem[SM::kUnion];
+  __shared__ __attribute__((aligned(16))) char ring[CF::kRing];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -129,7 +144,7 @@ __global__ __launch_bounds__(256) void decode2d_partial_kernel(DecodeParams p, c
   const int tb = split * p.chunk;
   const int te = min(nb, tb + p.chunk);
 
-  for (int i = tid; i < 16 * RK; i += 256) {
+  for (int i = tid; i < 16 * RK; i += 64 * kW) {
     const int hh = i / RK;
     const int k = i - hh * RK;
     const float v = (h0 + hh < p.H) ? qt[(static_cast<size_t>(b) * p.H + h0 + hh) * RK + k] : 0.f;
@@ -143,7 +158,25 @@ __global__ __launch_bounds__(256) void decode2d_partial_kernel(DecodeParams p, c
   const float bt = beta_s[col];
   const char* zkb = static_cast<const char*>(p.zk) + static_cast<size_t>(b) * p.n_max * RK * 2;
   const char* zvb = static_cast<const char*>(p.zv) + static_cast<size_t>(b) * p.n_max * RV * 2;
-  char* vs = smem + wave * SM::kVStage;
+  char* myring = ring + wave * 2 * CF::kVTile;
+
+  // issue the loads of the tile starting at tok0 (tok0 < te): K into kr, V into ring half `buf`
+  auto issue = [&](int tok0, int buf, uint4 (&kr)[KS]) {
+    const int last = te - 1;
+    char* dst = myring + buf * CF::kVTile;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int f = i * 64 + lane;               // LDS slot of this lane
+      const int row = f / CPR;
+      const int pc = f - row * CPR;
+      const int lc = (pc & ~7) | ((pc & 7) ^ (2 * ((row >> 2) & 3)));
+      const char* src = zvb + (static_cast<size_t>(min(tok0 + row, last)) * RV + lc * 8) * 2;
+      __builtin_amdgcn_global_load_lds((const gptr_t)src, (lptr_t)(dst + i * 1024), 16, 0, 0);
+    }
+    const char* arow = zkb + static_cast<size_t>(min(tok0 + col, last)) * RK * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kr[ks] = *reinterpret_cast<const uint4*>(arow + (32 * ks + 8 * g) * 2);
+  };
 
   floatx4_t D[RT];
 #pragma unroll
@@ -151,39 +184,32 @@ __global__ __launch_bounds__(256) void decode2d_partial_kernel(DecodeParams p, c
   float m = kNegInf;
   float l = 0.f;
 
-  for (int tok0 = tb + wave * 16; tok0 < te; tok0 += 64) {
-    // V tile loads first (consumed after the scores)
-    uint4 vreg[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int f = i * 64 + lane;
-      const int row = f / CPR;
-      const int cc = f - row * CPR;
-      const int tok = tok0 + row;
-      vreg[i] = tok < te ? *reinterpret_cast<const uint4*>(zvb + (static_cast<size_t>(tok) * RV + cc * 8) * 2)
-                         : make_uint4(0, 0, 0, 0);
-    }
-    // scores: S^T[token tok0 + i][head h0 + j]
-    const int tokA = tok0 + col;
-    const bool okA = tokA < te;
-    const char* arow = zkb + static_cast<size_t>(tokA) * RK * 2;
-    floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+  uint4 kc[KS];
+  int tok0 = tb + wave * 16;
+  int buf = 0;
+  if (tok0 < te) issue(tok0, 0, kc);
+  for (; tok0 < te; tok0 += 16 * kW) {
+    uint4 kn[KS];
+    const bool more = tok0 + 16 * kW < te;
+    if (more) issue(tok0 + 16 * kW, buf ^ 1, kn);
+    // scores S^T[token tok0 + i][head h0 + j]: hi and lo parts of q~ in two independent chains
+    __asm__ volatile("" ::: "memory");
+    floatx4_t sh = {0.f, 0.f, 0.f, 0.f};
+    floatx4_t sl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const uint4 a = okA ? *reinterpret_cast<const uint4*>(arow + (32 * ks + 8 * g) * 2) : make_uint4(0, 0, 0, 0);
       const uint4 bh = *reinterpret_cast<const uint4*>(&qhi[col * RK + 32 * ks + 8 * g]);
       const uint4 bl = *reinterpret_cast<const uint4*>(&qlo[col * RK + 32 * ks + 8 * g]);
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bh), s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bl), s, 0, 0, 0);
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, kc[ks]);
+      sh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bh), sh, 0, 0, 0);
+      sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bl), sl, 0, 0, 0);
     }
-    // this lane: head h, tokens tok0 + 4g + e
     float sc[4];
     float tmax = kNegInf;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool ok = hvalid && (tok0 + 4 * g + e) < te;
-      sc[e] = ok ? s[e] + bt : kNegInf;
+      sc[e] = ok ? (sh[e] + sl[e]) + bt : kNegInf;
       tmax = fmaxf(tmax, sc[e]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
@@ -202,35 +228,37 @@ __global__ __launch_bounds__(256) void decode2d_partial_kernel(DecodeParams p, c
       l += pe;
       bp[e] = static_cast<short>(f32_to_bf16(pe));
     }
-    // stage V rows in LDS (two 8-byte writes per 16-byte chunk; rows are 8-byte aligned)
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int f = i * 64 + lane;
-      const int row = f / CPR;
-      const int cc = f - row * CPR;
-      uint2* dst = reinterpret_cast<uint2*>(vs + row * SM::kVRow + cc * 16);
-      dst[0] = make_uint2(vreg[i].x, vreg[i].y);
-      dst[1] = make_uint2(vreg[i].z, vreg[i].w);
-    }
-    wave_lds_sync();
+    // this tile's V must have landed in LDS: at most the next tile's loads may be outstanding
+    if (more)
+      __builtin_amdgcn_s_waitcnt((KS + VPL) >= 16 ? 0x4f70 | (((KS + VPL) - 16) & 15)
+                                                  : 0x0f70 | (KS + VPL));
+    else
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __asm__ volatile("" ::: "memory");
+    const char* vt = myring + buf * CF::kVTile;
     // A^T[r][head] += Z^V^T[r][tokens 4g+e] . P^T[tokens][head]
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
+      const int c = 2 * rt + (col >> 3);
+      const int pc = (c & ~7) | ((c & 7) ^ (2 * g));
+      const int off = pc * 16 + (col & 7) * 2;
       short4_t av;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        av[e] = *reinterpret_cast<const short*>(vs + (4 * g + e) * SM::kVRow + (16 * rt + col) * 2);
+      for (int e = 0; e < 4; ++e) av[e] = *reinterpret_cast<const short*>(vt + (4 * g + e) * RV * 2 + off);
       D[rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bp, D[rt], 0, 0, 0);
     }
+    // the ring half just read is refilled two tiles from now; finish the reads first
     wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < KS; ++i) kc[i] = kn[i];
+    buf ^= 1;
   }
-  // per-head totals: the four lanes of head h hold disjoint token sums
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
 
-  // merge the four waves through LDS: (2,3) -> (0,1), then 1 -> 0
+  // merge the waves through LDS (the V rings are free now): 8 -> 4 -> 2 -> 1
   __syncthreads();
-  float* ps = reinterpret_cast<float*>(smem);
+  float* ps = reinterpret_cast<float*>(ring);
   constexpr int PS = 16 * (2 + RV);
   auto put = [&](float* dst) {
     if (g == 0) {
@@ -255,15 +283,14 @@ __global__ __launch_bounds__(256) void decode2d_partial_kernel(DecodeParams p, c
       for (int e = 0; e < 4; ++e) D[rt][e] = D[rt][e] * fa + src[col * (2 + RV) + 2 + 16 * rt + 4 * g + e] * fb;
     m = M;
   };
-  if (wave >= 2) put(ps + (wave - 2) * PS);
-  __syncthreads();
-  if (wave < 2) take(ps + wave * PS);
-  __syncthreads();
-  if (wave == 1) put(ps);
-  __syncthreads();
-  if (wave != 0) return;
-  take(ps);
-  if (!hvalid) return;
+#pragma unroll
+  for (int half = kW / 2; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half) put(ps + (wave - half) * PS);
+    __syncthreads();
+    if (wave < half) take(ps + wave * PS);
+    __syncthreads();
+  }
+  if (wave != 0 || !hvalid) return;
   // partial layout [B][H][S][2 + RV]
   float* w = part + ((static_cast<size_t>(b) * p.H + h) * p.splits + split) * (2 + RV);
   if (g == 0) {
@@ -368,8 +395,7 @@ constexpr Entry2d entry2d() {
 }
 
 const Entry2d kTable2d[] = {
-    entry2d<32, 32>(), entry2d<64, 64>(), entry2d<128, 128>(), entry2d<256, 256>(),
-    entry2d<96, 160>(),
+    entry2d<64, 64>(), entry2d<128, 128>(), entry2d<256, 256>(),
 };
 
 const Entry2d* find2d(int r_k, int r_v) {
@@ -389,8 +415,8 @@ bool decode2d_mfma_supported(int dtype, int r_k, int r_v, int d_head) {
 void decode2d_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
   const int hg = (desc.H + 15) / 16;
   const long wgs = static_cast<long>(B) * hg;
-  // one full round of resident workgroups: the r_v = 256 kernel fits two per CU, smaller three
-  const long target = 256L * (desc.r_v > 160 ? 2 : 3);
+  // one full round of resident 8-wave workgroups: one per CU at r_v = 256 (LDS), two below
+  const long target = 256L * (desc.r_v > 128 ? 1 : 2);
   int s = static_cast<int>((target + wgs - 1) / wgs);
   const int max_by_len = desc.n_max / 256 > 0 ? desc.n_max / 256 : 1;
   if (s > max_by_len) s = max_by_len;
@@ -427,8 +453,8 @@ hipError_t launch_decode2d(const DecodeParams& p0, hipStream_t stream) {
   hipLaunchKernelGGL(e->qproj, dim3(p.H, qb), dim3(256), 0, stream, p, qt, beta);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(e->partial, dim3(p.splits, p.B, (p.H + 15) / 16), dim3(256), 0, stream, p, qt,
-                     beta, part);
+  hipLaunchKernelGGL(e->partial, dim3(p.splits, p.B, (p.H + 15) / 16), dim3(64 * Cfg2d<64, 64>::kW), 0,
+                     stream, p, qt, beta, part);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(e->combine, dim3(p.B, p.H), dim3(256), 0, stream, p, part);

@@ -69,6 +69,16 @@ __device__ __forceinline__ float frag_elem<BF16>(const uint4* f, int e) {
   return (e & 1) ? bf16_hi(x) : bf16_lo(x);
 }
 
+// 16-byte load of data that is read exactly once, for loads whose 64 lanes cover whole cache
+// lines (one instruction reads 1 KiB contiguous): a non-temporal hint keeps the stream from
+// displacing reused data. Partial-line patterns must use ordinary loads, which let the next
+// instruction hit the same lines.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  const u32x4_t t = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
