@@ -50,29 +50,40 @@ __device__ __forceinline__ int seq_keys(const DecodeParams& p, int b) {
 }
 
 // ---- 1. query absorption for every (b, h) ------------------------------------------------------
-// grid (H, ceil(B / kQB)); thread k computes q~[b][h][k] for kQB sequences.
+// grid (H, ceil(B / kQB)), 256 threads. W^K_t[h] (d x RK bf16) is staged in LDS with one round of
+// 16-byte loads; thread k then forms q~[b][h][k] for kQB sequences from LDS.
 template <int RK>
 __global__ __launch_bounds__(256) void qproj2d_kernel(DecodeParams p, float* qt, float* beta) {
-  __shared__ float q_s[kQB][256];
+  __shared__ float q_s[kQB][128];
+  __shared__ __attribute__((aligned(16))) uint16_t w_s[128 * RK];
   const int h = blockIdx.x;
   const int b0 = blockIdx.y * kQB;
   const int tid = threadIdx.x;
+  const size_t wrow = (static_cast<size_t>(p.t) * p.H + h) * p.d;  // rows of W^K_t for head h
+  const uint4* wsrc = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.Wk) + wrow * RK);
+  constexpr int kChunks = 128 * RK / 8;
+  const int nchunk = p.d * RK / 8;
+  uint4 wreg[kChunks / 256 > 0 ? kChunks / 256 : 1];
+#pragma unroll
+  for (int i = 0; i < kChunks / 256; ++i) {
+    const int c = i * 256 + tid;
+    wreg[i] = c < nchunk ? wsrc[c] : make_uint4(0, 0, 0, 0);
+  }
   for (int i = tid; i < kQB * p.d; i += 256) {
     const int bb = i / p.d;
     const int j = i - bb * p.d;
     const int b = b0 + bb;
     q_s[bb][j] = b < p.B ? ld<BF16>(p.q, (static_cast<size_t>(b) * p.H + h) * p.d + j) : 0.f;
   }
+#pragma unroll
+  for (int i = 0; i < kChunks / 256; ++i) reinterpret_cast<uint4*>(w_s)[i * 256 + tid] = wreg[i];
   __syncthreads();
-  // W^K_t rows of head h: [T][H*d][RK] at row t*H*d + h*d
-  const size_t wrow = (static_cast<size_t>(p.t) * p.H + h) * p.d;
   for (int k = tid; k < RK; k += 256) {
     float acc[kQB];
 #pragma unroll
     for (int bb = 0; bb < kQB; ++bb) acc[bb] = 0.f;
-#pragma unroll 8
     for (int j = 0; j < p.d; ++j) {
-      const float w = ld<BF16>(p.Wk, (wrow + j) * RK + k);
+      const float w = __uint_as_float(static_cast<uint32_t>(w_s[j * RK + k]) << 16);
 #pragma unroll
       for (int bb = 0; bb < kQB; ++bb) acc[bb] += w * q_s[bb][j];
     }
@@ -304,13 +315,15 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
 }
 
 // ---- 3. merge splits, project once through W^V_t[h], finish ------------------------------------
-// One 256-thread workgroup per (b, h): wave 0 merges the split partials by log-sum-exp and scores
-// the optional self token; all threads form a = sum_s f_s a_s; then thread pair (j, half) dots
-// row j of W^V_t[h] (read as 16-byte runs) with half of a, and the pair's sum finishes o[j].
+// One 256-thread workgroup per (b, h). Every load that does not depend on the merge (the split
+// partials, q, the self K/V, mu^V_t, the W^V_t[h] rows) is issued first, so the workgroup waits for
+// memory once. Thread pair (j, half) then dots row j of W^V_t[h] with half of the merged latent
+// sum, and the pair's sum finishes o[j].
 template <int RV>
 __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const float* part) {
   constexpr int HALF = RV / 2;
   static_assert(HALF % 8 == 0, "half a W^V row must be whole 16-byte runs");
+  constexpr int RPT = (RV + 255) / 256;  // latent entries per thread
   __shared__ float a_s[RV];
   __shared__ float f_s[64];
   __shared__ float fin_s[4];  // f_lat, p_self, 1/den, l
@@ -321,17 +334,33 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
   const int S_ = p.splits;
   const size_t bh = static_cast<size_t>(b) * p.H + h;
   const float* pw = part + bh * S_ * (2 + RV);
+  const size_t wrow = (static_cast<size_t>(p.t) * p.H + h) * p.d;  // W^V_t rows of head h; mu offset
 
+  // ---- issue: W^V row half of this thread (d <= 128: one row per thread pair) ----
+  const int half = tid & 1;
+  const int j = tid >> 1;
+  const bool jok = j < p.d;
+  uint4 w[HALF / 8];
+  {
+    const uint4* wr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.Wv) +
+                                                     (wrow + (jok ? j : 0)) * RV + half * HALF);
+#pragma unroll
+    for (int i = 0; i < HALF / 8; ++i) w[i] = wr[i];
+  }
+  float mu_j = 0.f, vs_j = 0.f;
+  if (jok && half == 0) {
+    if (p.mu_v != nullptr) mu_j = ld<BF16>(p.mu_v, wrow + j);
+    if (p.v_self != nullptr) vs_j = ld<BF16>(p.v_self, bh * p.d + j);
+  }
+  // wave 0: split maxima and sums, self score
+  float ms = kNegInf, ls = 0.f, pt = 0.f;
   if (tid < 64) {
-    float ms = kNegInf;
-    float ls = 0.f;
     if (lane < S_) {
       ms = pw[static_cast<size_t>(lane) * (2 + RV)];
       ls = pw[static_cast<size_t>(lane) * (2 + RV) + 1];
     }
-    float pt = 0.f;
     if (p.k_self != nullptr)
-      for (int j = lane; j < p.d; j += 64) pt += ld<BF16>(p.q, bh * p.d + j) * ld<BF16>(p.k_self, bh * p.d + j);
+      for (int jj = lane; jj < p.d; jj += 64) pt += ld<BF16>(p.q, bh * p.d + jj) * ld<BF16>(p.k_self, bh * p.d + jj);
     const float M = wave_max(ms);
     const float fs = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
     const float l = wave_sum(fs * ls);
@@ -350,35 +379,32 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
     }
   }
   __syncthreads();
-  for (int r = tid; r < RV; r += 256) {
-    float a = 0.f;
-    for (int s = 0; s < S_; ++s) a += f_s[s] * pw[static_cast<size_t>(s) * (2 + RV) + 2 + r];
-    a_s[r] = a;
+  // merged latent sum a = sum_s f_s a_s (the S loads of each entry are independent)
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = tid + 256 * i;
+    if (r < RV) {
+      float a = 0.f;
+      for (int s2 = 0; s2 < S_; ++s2) a += f_s[s2] * pw[static_cast<size_t>(s2) * (2 + RV) + 2 + r];
+      a_s[r] = a;
+    }
   }
   __syncthreads();
-  const int half = tid & 1;
-  const size_t wrow = (static_cast<size_t>(p.t) * p.H + h) * p.d;  // W^V_t rows of head h; mu offset
-  for (int j = tid >> 1; j < p.d; j += 128) {
-    const uint4* wr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.Wv) + (wrow + j) * RV + half * HALF);
-    const float* ah = a_s + half * HALF;
-    uint4 w[HALF / 8];
+  const float* ah = a_s + half * HALF;
+  float o = 0.f;
 #pragma unroll
-    for (int i = 0; i < HALF / 8; ++i) w[i] = wr[i];
-    float o = 0.f;
-#pragma unroll
-    for (int i = 0; i < HALF / 8; ++i) {
-      o += bf16_lo(w[i].x) * ah[8 * i + 0] + bf16_hi(w[i].x) * ah[8 * i + 1];
-      o += bf16_lo(w[i].y) * ah[8 * i + 2] + bf16_hi(w[i].y) * ah[8 * i + 3];
-      o += bf16_lo(w[i].z) * ah[8 * i + 4] + bf16_hi(w[i].z) * ah[8 * i + 5];
-      o += bf16_lo(w[i].w) * ah[8 * i + 6] + bf16_hi(w[i].w) * ah[8 * i + 7];
-    }
-    o += __shfl_xor(o, 1, 64);
-    if (half == 0) {
-      if (p.mu_v != nullptr) o += fin_s[3] * ld<BF16>(p.mu_v, wrow + j);
-      o *= fin_s[0];
-      if (p.v_self != nullptr) o += fin_s[1] * ld<BF16>(p.v_self, bh * p.d + j);
-      st<BF16>(p.out, bh * p.d + j, o * fin_s[2]);
-    }
+  for (int i = 0; i < HALF / 8; ++i) {
+    o += bf16_lo(w[i].x) * ah[8 * i + 0] + bf16_hi(w[i].x) * ah[8 * i + 1];
+    o += bf16_lo(w[i].y) * ah[8 * i + 2] + bf16_hi(w[i].y) * ah[8 * i + 3];
+    o += bf16_lo(w[i].z) * ah[8 * i + 4] + bf16_hi(w[i].z) * ah[8 * i + 5];
+    o += bf16_lo(w[i].w) * ah[8 * i + 6] + bf16_hi(w[i].w) * ah[8 * i + 7];
+  }
+  o += __shfl_xor(o, 1, 64);
+  if (jok && half == 0) {
+    o += fin_s[3] * mu_j;
+    o *= fin_s[0];
+    o += fin_s[1] * vs_j;
+    st<BF16>(p.out, bh * p.d + j, o * fin_s[2]);
   }
 }
 

@@ -95,14 +95,17 @@ __device__ __forceinline__ floatx4_t mfma(uint4 a, uint4 b, floatx4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// NT: 16-column latent tiles per wave. KSPLIT 4: the 4 waves share 32 tokens and split K;
-// KSPLIT 1: each wave has its own 32 tokens and the whole K.
-template <int NT, int KSPLIT>
-__global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeParams p) {
+// NT: 16-column latent tiles per wave; MT: 16-token tiles per wave. KSPLIT 1: each of the 4 waves
+// owns its own 16*MT tokens over the whole K; KSPLIT 4 or 8: that many waves share 16*MT tokens
+// and split K, reducing through LDS (KSPLIT 8 runs 8-wave workgroups).
+template <int NT, int MT, int KSPLIT>
+__global__ __launch_bounds__(KSPLIT == 8 ? 512 : 256) void encode_mfma_kernel(EncodeParams p) {
   constexpr int U = 4;  // k-steps whose loads are issued together
-  constexpr int TOK_WG = KSPLIT == 4 ? 32 : 128;
-  __shared__ float red[KSPLIT == 4 ? 3 : 1][64][2 * NT * 4];
-  __shared__ float emu_s[4][16 * NT];
+  constexpr int NW = KSPLIT == 8 ? 8 : 4;  // waves per workgroup
+  constexpr int TOK_WG = KSPLIT == 1 ? NW * 16 * MT : 16 * MT;
+  constexpr int NACC = MT * NT * 4;
+  __shared__ float red[KSPLIT == 1 ? 1 : KSPLIT - 1][64][NACC];
+  __shared__ float emu_s[NW][16 * NT];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -114,22 +117,22 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeParams p) {
   const int ntok = p.B * p.C;
   const int h = blockIdx.z;
   const int r0 = blockIdx.y * 16 * NT;
-  const int n_base = blockIdx.x * TOK_WG + (KSPLIT == 4 ? 0 : wave * 32);
+  const int n_base = blockIdx.x * TOK_WG + (KSPLIT == 1 ? wave * 16 * MT : 0);
   const size_t HD = static_cast<size_t>(p.H) * p.d;
   const uint16_t* x = static_cast<const uint16_t*>(p.x);
   const uint16_t* E = static_cast<const uint16_t*>(p.E);
 
-  // E mu for this lane's latent rows, summed over the four waves' K quarters
+  // E mu for this lane's latent rows, summed over the waves' shares of K
   float emu[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) emu[nt] = 0.f;
   if (p.mu != nullptr) {
     const uint16_t* mu = static_cast<const uint16_t*>(p.mu) + static_cast<size_t>(h) * K;
-    const int q4 = (nk + 3) / 4;
+    const int qw = (nk + NW - 1) / NW;
     floatx4_t am[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) am[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    for (int ks = wave * q4; ks < min(nk, (wave + 1) * q4); ++ks) {
+    for (int ks = wave * qw; ks < min(nk, (wave + 1) * qw); ++ks) {
       const int kk = 32 * ks + 8 * g;
       const uint4 a = (col == 0 && kk < K) ? *reinterpret_cast<const uint4*>(mu + kk) : make_uint4(0, 0, 0, 0);
 #pragma unroll
@@ -147,14 +150,14 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeParams p) {
     __syncthreads();
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      emu[nt] = emu_s[0][16 * nt + col] + emu_s[1][16 * nt + col] + emu_s[2][16 * nt + col] + emu_s[3][16 * nt + col];
+      for (int w = 0; w < NW; ++w) emu[nt] += emu_s[w][16 * nt + col];
   }
 
-  // token rows of the two A tiles, latent rows of the NT B tiles
-  const uint16_t* xrow[2];
-  bool nok[2];
+  // token rows of the MT A tiles, latent rows of the NT B tiles
+  const uint16_t* xrow[MT];
+  bool nok[MT];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     const int n = n_base + 16 * mt + col;
     nok[mt] = n < ntok;
     xrow[mt] = x + static_cast<size_t>(nok[mt] ? n : 0) * p.T * HD + static_cast<size_t>(h) * p.d;
@@ -169,19 +172,19 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeParams p) {
   }
 
   int kb = 0, ke = nk;
-  if (KSPLIT == 4) {
-    const int q4 = (nk + 3) / 4;
-    kb = min(nk, wave * q4);
-    ke = min(nk, kb + q4);
+  if (KSPLIT > 1) {
+    const int qs = (nk + KSPLIT - 1) / KSPLIT;
+    kb = min(nk, wave * qs);
+    ke = min(nk, kb + qs);
   }
-  floatx4_t acc[2][NT];
+  floatx4_t acc[MT][NT];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int ks = kb; ks < ke; ks += U) {
-    uint4 a[U][2];
+    uint4 a[U][MT];
     uint4 b[U][NT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeParams p) {
       const int j = kk - t * p.d;
       const size_t xo = static_cast<size_t>(t) * HD + j;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
         a[u][mt] = (kok && nok[mt]) ? *reinterpret_cast<const uint4*>(xrow[mt] + xo) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -200,15 +203,15 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma(a[u][mt], b[u][nt], acc[mt][nt]);
   }
 
-  if (KSPLIT == 4) {
+  if (KSPLIT > 1) {
     if (wave > 0) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -216,10 +219,9 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeParams p) {
     }
     __syncthreads();
     if (wave > 0) return;
+    for (int w = 0; w < KSPLIT - 1; ++w)
 #pragma unroll
-    for (int w = 0; w < 3; ++w)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeParams p) {
 
   // C layout: lane holds latent row r = r0 + 16 nt + col for tokens n_base + 16 mt + 4 g + e
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int n = n_base + 16 * mt + 4 * g + e;
@@ -244,17 +246,19 @@ __global__ __launch_bounds__(256) void encode_mfma_kernel(EncodeParams p) {
     }
 }
 
-template <int KSPLIT>
+template <int MT, int KSPLIT>
 hipError_t launch_encode_mfma(const EncodeParams& p, int nt_tiles, hipStream_t stream) {
-  constexpr int TOK_WG = KSPLIT == 4 ? 32 : 128;
+  constexpr int NW = KSPLIT == 8 ? 8 : 4;
+  constexpr int TOK_WG = KSPLIT == 1 ? NW * 16 * MT : 16 * MT;
   const unsigned ntok = static_cast<unsigned>(p.B) * p.C;
   dim3 grid((ntok + TOK_WG - 1) / TOK_WG, (p.r + 16 * nt_tiles - 1) / (16 * nt_tiles), p.H);
+  dim3 block(64 * NW);
   if (nt_tiles == 1)
-    hipLaunchKernelGGL((encode_mfma_kernel<1, KSPLIT>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((encode_mfma_kernel<1, MT, KSPLIT>), grid, block, 0, stream, p);
   else if (nt_tiles == 2)
-    hipLaunchKernelGGL((encode_mfma_kernel<2, KSPLIT>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((encode_mfma_kernel<2, MT, KSPLIT>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((encode_mfma_kernel<4, KSPLIT>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((encode_mfma_kernel<4, MT, KSPLIT>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
@@ -270,9 +274,11 @@ hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t stream) {
     const int nt_tiles = p.r <= 16 ? 1 : p.r <= 32 ? 2 : 4;
     const long ntok = static_cast<long>(p.B) * p.C;
     const long wgs1 = (ntok + 127) / 128 * ((p.r + 16 * nt_tiles - 1) / (16 * nt_tiles)) * p.H;
-    // few workgroups with whole-K waves would leave most of the chip idle: split K instead
-    return wgs1 < 1024 ? launch_encode_mfma<4>(p, nt_tiles, stream)
-                       : launch_encode_mfma<1>(p, nt_tiles, stream);
+    // few workgroups with whole-K waves would leave most of the chip idle: split K instead,
+    // eight ways for decode-size token counts
+    if (ntok <= 256) return launch_encode_mfma<1, 8>(p, nt_tiles, stream);
+    return wgs1 < 1024 ? launch_encode_mfma<2, 4>(p, nt_tiles, stream)
+                       : launch_encode_mfma<2, 1>(p, nt_tiles, stream);
   }
   if (K > kMaxK) return hipErrorNotSupported;
   const unsigned ntok = static_cast<unsigned>(p.B) * p.C;

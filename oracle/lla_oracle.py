@@ -155,19 +155,19 @@ def encode_into_cache(zk, zv, xk, xv, Ek, Ev, pos, mu_k=None, mu_v=None, variant
     B, C, T, H, d = xk.shape
     pos = np.asarray(pos, dtype=np.int64)
     for b in range(B):
-        for c in range(C):
-            slot = int(pos[b]) + c
-            if variant == "per_head":
-                for h in range(H):
-                    sk = xk[b, c, :, h, :].reshape(T * d)
-                    sv = xv[b, c, :, h, :].reshape(T * d)
-                    zk[b, h, slot] = encode_stack(sk, Ek[h], None if mu_k is None else mu_k[h])
-                    zv[b, h, slot] = encode_stack(sv, Ev[h], None if mu_v is None else mu_v[h])
-            elif variant == "2d":
-                zk[b, slot] = encode_stack(xk[b, c].reshape(T * H * d), Ek, mu_k)
-                zv[b, slot] = encode_stack(xv[b, c].reshape(T * H * d), Ev, mu_v)
-            else:
-                raise ValueError(variant)
+        slots = int(pos[b]) + np.arange(C)
+        if variant == "per_head":
+            for h in range(H):
+                # the Eq. 1 stacks of all C tokens of (b, h), loop-major: [C, T*d]
+                sk = xk[b, :, :, h, :].reshape(C, T * d)
+                sv = xv[b, :, :, h, :].reshape(C, T * d)
+                zk[b, h, slots] = encode_stack(sk, Ek[h], None if mu_k is None else mu_k[h])
+                zv[b, h, slots] = encode_stack(sv, Ev[h], None if mu_v is None else mu_v[h])
+        elif variant == "2d":
+            zk[b, slots] = encode_stack(xk[b].reshape(C, T * H * d), Ek, mu_k)
+            zv[b, slots] = encode_stack(xv[b].reshape(C, T * H * d), Ev, mu_v)
+        else:
+            raise ValueError(variant)
     return zk, zv
 
 

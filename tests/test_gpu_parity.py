@@ -368,3 +368,33 @@ def test_decode_2d_mfma(rk, rv):
             what = f"2d mfma r=({rk},{rv}) gain={gain} mu={mu} self={self_token} t={t}"
             assert_close(o, ro, dtype, what)
             assert_lse(lse, rl, what)
+
+
+@pytest.mark.parametrize("variant,H,d,T,r,B,C", [
+    ("per_head", 16, 128, 4, 32, 8, 160),     # 1280 tokens: K split over the 4 waves
+    ("per_head", 16, 128, 4, 32, 16, 512),    # 8192 tokens: whole-K waves
+    ("2d", 16, 128, 4, 256, 2, 512),          # a 2D prefill chunk's encode
+])
+def test_encode_large_token_counts(variant, H, d, T, r, B, C):
+    dtype = "bf16"
+    n_max = C + 7
+    pos = np.array([7] * B, np.int32)
+    K = T * d if variant == "per_head" else T * H * d
+    es = (H, r, K) if variant == "per_head" else (r, K)
+    ms = (H, K) if variant == "per_head" else (K,)
+    zs = (B, H, n_max, r) if variant == "per_head" else (B, n_max, r)
+    xk = synth.normal((B, C, T, H, d), 950 + r, dtype)
+    xv = synth.normal((B, C, T, H, d), 951 + r, dtype)
+    Ek = synth.normal(es, 952 + r, dtype, 1 / math.sqrt(K))
+    Ev = synth.normal(es, 953 + r, dtype, 1 / math.sqrt(K))
+    mk = synth.normal(ms, 954 + r, dtype, 0.5)
+    desc = mk_desc(variant, dtype, H, d, T, r, r, n_max)
+    zk = torch.zeros(zs, dtype=torch.bfloat16, device="cuda")
+    zv = torch.zeros_like(zk)
+    lla.lla_encode(desc, B, C, dev(xk, dtype), dev(xv, dtype), dev(Ek, dtype), dev(Ev, dtype),
+                   dev(mk, dtype), None, dev(pos), zk, zv)
+    torch.cuda.synchronize()
+    z0 = np.zeros(zs)
+    rk_, rv_ = O.encode_into_cache(z0, z0, xk, xv, Ek, Ev, pos, mk, None, variant)
+    assert_close(host(zk), rk_, dtype, f"encode zk {variant} B={B} C={C}")
+    assert_close(host(zv), rv_, dtype, f"encode zv {variant} B={B} C={C}")
