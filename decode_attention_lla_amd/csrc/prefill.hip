@@ -4,30 +4,452 @@
 // caching") describes the latent-store decoder's prefill as two passes: the chunk's per-loop K/V
 // are captured and encoded first, and attention then runs against the cache. Here the chunk's
 // latents are already in slots ctx .. ctx+C-1, and chunk row j (position ctx + j) attends latents
-// 0 .. ctx + j. The arithmetic per row is the absorbed decode of Section 7.
+// 0 .. ctx + j. The arithmetic per row is the absorbed form of Section 7: scores q~ . z^K with
+// q~ = W^K_t^T q (plus q . mu^K_t), softmax, latent-space sum of z^V, one W^V_t projection.
 //
-// Streaming path: every (row, head) is one query row of the absorbed split-K decode kernels, with
-// its own causal key count. Rows of one sequence re-read the same latents, which mostly hit in
-// cache for modest chunks.
+// MFMA path (bf16 storage, r_k and r_v in {64, 128, 256}, d_head a multiple of 32): a chunk of C
+// rows against N_ctx + C latents is a dense contraction, so it runs as four kernels:
+//   P0 transpose W^K_t[h] to [r_k][d] so the projection's B operand is contiguous;
+//   P1 Q~ = scale*log2(e) * Q . W^K_t[h] on v_mfma_f32_16x16x32_bf16, stored as bf16 hi + lo;
+//   P2 causal flash attention over the latents: a workgroup of 8 waves owns 128 consecutive chunk
+//      rows of one head; each wave keeps its 16 rows of Q~ (hi and lo) in registers; 32-latent K
+//      and V tiles are fetched with global_load_lds into XOR-swizzled, double-buffered LDS and
+//      shared by the 8 waves; S^T = Z^K . Q~^T, online softmax per row with a causal mask, then
+//      A^T += Z^V^T . P^T with P taken straight from the S^T accumulator layout (the B operand of
+//      v_mfma_f32_16x16x16bf16_1k); the normalised latent sums are stored as bf16 hi + lo;
+//   P3 O = A . W^V_t[h]^T (+ mu^V_t when the row saw any latent) on MFMA, both A parts.
+// Rows are numbered rho = (b*H + h)*C + j. LLA-2D and per-head differ only in which latent
+// sequence a head reads (b, or (b, h)) and in the factor and mu offsets.
+//
+// Streaming path (everything else): every (row, head) is one query row of the absorbed split-K
+// decode kernels, with its own causal key count.
+#include "lla_device.h"
 #include "lla_internal.h"
 
 namespace lla {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+constexpr float kLazyP = 8.0f;
+constexpr int kRowsWG = 128;  // chunk rows per attention workgroup (8 waves x 16)
+constexpr int kKeyTile = 32;  // latents per K/V tile
+
+__device__ __forceinline__ floatx4_t mfma32(uint4 a, uint4 b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace segments of the MFMA path.
+struct PrefillWs {
+  uint16_t* wkt;   // [H][RK][d]
+  uint16_t* qhi;   // [R][RK]
+  uint16_t* qlo;
+  uint16_t* ahi;   // [R][RV]
+  uint16_t* alo;
+  float* wrow;     // [R]: 1 if the row attended any latent
+};
+
+size_t prefill_mfma_bytes(int B, int C, int H, int d, int rk, int rv) {
+  const size_t R = static_cast<size_t>(B) * H * C;
+  return align256(static_cast<size_t>(H) * rk * d * 2) + 2 * align256(R * rk * 2) +
+         2 * align256(R * rv * 2) + align256(R * 4);
+}
+
+PrefillWs carve(void* ws, int B, int C, int H, int d, int rk, int rv) {
+  const size_t R = static_cast<size_t>(B) * H * C;
+  char* p = static_cast<char*>(ws);
+  PrefillWs w;
+  w.wkt = reinterpret_cast<uint16_t*>(p);
+  p += align256(static_cast<size_t>(H) * rk * d * 2);
+  w.qhi = reinterpret_cast<uint16_t*>(p);
+  p += align256(R * rk * 2);
+  w.qlo = reinterpret_cast<uint16_t*>(p);
+  p += align256(R * rk * 2);
+  w.ahi = reinterpret_cast<uint16_t*>(p);
+  p += align256(R * rv * 2);
+  w.alo = reinterpret_cast<uint16_t*>(p);
+  p += align256(R * rv * 2);
+  w.wrow = reinterpret_cast<float*>(p);
+  return w;
+}
+
+// offset of W_t restricted to head h (per-head [T][H][d][r], 2D [T][H*d][r]): (t*H + h)*d*r
+__device__ __forceinline__ size_t wofs(const PrefillParams& p, int h, int r) {
+  return (static_cast<size_t>(p.t) * p.H + h) * p.d * r;
+}
+// offset of mu_t restricted to head h (per-head [H][T*d], 2D [T*H*d])
+__device__ __forceinline__ size_t mofs(const PrefillParams& p, int h) {
+  return p.variant == LLA_2D ? (static_cast<size_t>(p.t) * p.H + h) * p.d
+                             : (static_cast<size_t>(h) * p.T + p.t) * p.d;
+}
+
+// ---- P0: W^K_t[h] [d][RK] -> [RK][d] ------------------------------------------------------------
+template <int RK>
+__global__ __launch_bounds__(256) void wk_transpose_kernel(PrefillParams p, uint16_t* wkt) {
+  const int h = blockIdx.x;
+  const uint16_t* src = static_cast<const uint16_t*>(p.Wk) + wofs(p, h, RK);
+  uint16_t* dst = wkt + static_cast<size_t>(h) * RK * p.d;
+  for (int i = threadIdx.x; i < p.d * RK; i += 256) {
+    const int j = i / RK;
+    const int k = i - j * RK;
+    dst[static_cast<size_t>(k) * p.d + j] = src[i];
+  }
+}
+
+// ---- P1: Q~ = scale*log2e * q . W^K_t[h] -> bf16 hi + lo ------------------------------------
+// grid (ceil(B*C / 64), RK / 64, H); each of the 4 waves owns 16 chunk rows x 64 columns.
+template <int RK>
+__global__ __launch_bounds__(256) void qproj_prefill_kernel(PrefillParams p, PrefillWs w) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int h = blockIdx.z;
+  const int k0 = blockIdx.y * 64;
+  const int n0 = blockIdx.x * 64 + wave * 16;  // flattened (b, j)
+  const int ntok = p.B * p.C;
+  const int n = n0 + col;
+  const bool nok = n < ntok;
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (static_cast<size_t>(nok ? n : 0) * p.H + h) * p.d;
+  const uint16_t* wt = w.wkt + static_cast<size_t>(h) * RK * p.d;
+  floatx4_t acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < p.d; j0 += 32) {
+    const uint4 a = nok ? *reinterpret_cast<const uint4*>(qrow + j0 + 8 * g) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const uint4 b = *reinterpret_cast<const uint4*>(wt + static_cast<size_t>(k0 + 16 * nt + col) * p.d + j0 + 8 * g);
+      acc[nt] = mfma32(a, b, acc[nt]);
+    }
+  }
+  // C layout: lane holds column k0 + 16 nt + col for rows n0 + 4 g + e
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int nn = n0 + 4 * g + e;
+    if (nn >= ntok) continue;
+    const int b = nn / p.C;
+    const int j = nn - b * p.C;
+    const size_t rho = (static_cast<size_t>(b) * p.H + h) * p.C + j;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const float v = acc[nt][e] * p.scale_log2;
+      const uint16_t hi = f32_to_bf16(v);
+      w.qhi[rho * RK + k0 + 16 * nt + col] = hi;
+      w.qlo[rho * RK + k0 + 16 * nt + col] = f32_to_bf16(v - __uint_as_float(static_cast<uint32_t>(hi) << 16));
+    }
+  }
+}
+
+// ---- P2: causal flash attention over the latents ----------------------------------------------
+// grid (ceil(C / 128), H, B); 512 threads. Wave w owns chunk rows j0 + 16 w .. + 15.
+template <int RK, int RV>
+__global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, PrefillWs w) {
+  constexpr int KS = RK / 32;
+  constexpr int RT = RV / 16;
+  constexpr int CPK = RK / 8;                 // 16-byte chunks per K row
+  constexpr int CPV = RV / 8;                 // per V row
+  constexpr int KT_BYTES = kKeyTile * RK * 2;
+  constexpr int VT_BYTES = kKeyTile * RV * 2;
+  constexpr int IK = KT_BYTES / 1024;         // 1 KiB global_load_lds instructions per K tile
+  constexpr int IV = VT_BYTES / 1024;
+  static_assert(RK % 64 == 0 && RV % 64 == 0, "swizzle windows need 8 chunks per row");
+  __shared__ __attribute__((aligned(16))) char kbuf[2][KT_BYTES];
+  __shared__ __attribute__((aligned(16))) char vbuf[2][VT_BYTES];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int j0 = blockIdx.x * kRowsWG;
+  const int ctx = p.ctx_lens[b];
+
+  // this lane's query row (for scores and accumulators): chunk row jr
+  const int jr = j0 + wave * 16 + col;
+  const bool rvalid = jr < p.C;
+  const int lim = rvalid ? min(ctx + jr, p.n_max - 1) : -1;  // last visible latent (inclusive)
+  // last latent any row of this workgroup sees
+  const int j_last = min(j0 + kRowsWG, p.C) - 1;
+  const int kmax = min(ctx + j_last, p.n_max - 1);
+  const int ntiles = kmax >= 0 ? kmax / kKeyTile + 1 : 0;
+
+  const size_t lat = p.variant == LLA_2D ? static_cast<size_t>(b) * p.n_max
+                                         : (static_cast<size_t>(b) * p.H + h) * p.n_max;
+  const char* zk = static_cast<const char*>(p.zk) + lat * RK * 2;
+  const char* zv = static_cast<const char*>(p.zv) + lat * RV * 2;
+
+  // Q~ (hi, lo) of this lane's row as B-operand fragments, and beta = scale*log2e * q . mu^K_t
+  const size_t rho = (static_cast<size_t>(b) * p.H + h) * p.C + (rvalid ? jr : 0);
+  uint4 qh[KS], ql[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qh[ks] = *reinterpret_cast<const uint4*>(w.qhi + rho * RK + 32 * ks + 8 * g);
+    ql[ks] = *reinterpret_cast<const uint4*>(w.qlo + rho * RK + 32 * ks + 8 * g);
+  }
+  float beta = 0.f;
+  if (p.mu_k != nullptr) {
+    const size_t qoff = ((static_cast<size_t>(b) * p.C + (rvalid ? jr : 0)) * p.H + h) * p.d;
+    const size_t mo = mofs(p, h);
+    float part = 0.f;
+    for (int jd = g; jd < p.d; jd += 4)
+      part += ld<BF16>(p.q, qoff + jd) * ld<BF16>(p.mu_k, mo + jd);
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    beta = part * p.scale_log2;
+  }
+
+  // cooperative tile fetch into ring half `buf`; rows past kmax are clamped to kmax
+  auto issue = [&](int tile, int buf) {
+    const int key0 = tile * kKeyTile;
+    for (int i = wave; i < IK; i += 8) {
+      const int f = i * 64 + lane;
+      const int row = f / CPK;
+      const int pc = f - row * CPK;
+      const int lc = (pc & ~7) | ((pc & 7) ^ (row & 7));
+      const char* src = zk + (static_cast<size_t>(min(key0 + row, kmax)) * RK + lc * 8) * 2;
+      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(&kbuf[buf][i * 1024]), 16, 0, 0);
+    }
+    for (int i = wave; i < IV; i += 8) {
+      const int f = i * 64 + lane;
+      const int row = f / CPV;
+      const int pc = f - row * CPV;
+      const int lc = (pc & ~7) | ((pc & 7) ^ (2 * ((row >> 2) & 3)));
+      const char* src = zv + (static_cast<size_t>(min(key0 + row, kmax)) * RV + lc * 8) * 2;
+      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(&vbuf[buf][i * 1024]), 16, 0, 0);
+    }
+  };
+
+  floatx4_t D[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) D[rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf;
+  float l = 0.f;
+
+  if (ntiles > 0) issue(0, 0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of `tile` have landed
+    __syncthreads();                     // ... and every other wave's
+    if (tile + 1 < ntiles) issue(tile + 1, buf ^ 1);
+    __asm__ volatile("" ::: "memory");
+    const char* kt = kbuf[buf];
+    const char* vt = vbuf[buf];
+    const int key0 = tile * kKeyTile;
+    float sc[2][4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int kt16 = 0; kt16 < 2; ++kt16) {
+      // S^T[key 16*kt16 + i][row]: A = K rows (swizzled chunks), B = Q~^T fragments
+      const int row = 16 * kt16 + col;
+      floatx4_t sh = {0.f, 0.f, 0.f, 0.f};
+      floatx4_t sl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c = 4 * ks + g;
+        const int pc = (c & ~7) | ((c & 7) ^ (row & 7));
+        const uint4 a = *reinterpret_cast<const uint4*>(kt + row * RK * 2 + pc * 16);
+        sh = mfma32(a, qh[ks], sh);
+        sl = mfma32(a, ql[ks], sl);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = key0 + 16 * kt16 + 4 * g + e;
+        sc[kt16][e] = key <= lim ? (sh[e] + sl[e]) + beta : kNegInf;
+        tmax = fmaxf(tmax, sc[kt16][e]);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    if (tmax > m + kLazyP) {
+      const float c = fast_exp2(m - tmax);
+      l *= c;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) D[rt] *= c;
+      m = tmax;
+    }
+#pragma unroll
+    for (int kt16 = 0; kt16 < 2; ++kt16) {
+      short4_t bp;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pe = (sc[kt16][e] == kNegInf) ? 0.f : fast_exp2(sc[kt16][e] - m);
+        l += pe;
+        bp[e] = static_cast<short>(f32_to_bf16(pe));
+      }
+      // A^T[r][row] += Z^V^T[r][keys 16 kt16 + 4 g + e] . P^T
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int c = 2 * rt + (col >> 3);
+        const int pc = (c & ~7) | ((c & 7) ^ (2 * g));
+        const int off = pc * 16 + (col & 7) * 2;
+        short4_t av;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          av[e] = *reinterpret_cast<const short*>(vt + (16 * kt16 + 4 * g + e) * RV * 2 + off);
+        D[rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bp, D[rt], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done with ring half `buf` before it is refilled
+  }
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (!rvalid) return;
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  // lane holds row jr, latent entries r = 16 rt + 4 g + e
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = D[rt][e] * inv;
+      hi[e] = f32_to_bf16(v);
+      lo[e] = f32_to_bf16(v - __uint_as_float(static_cast<uint32_t>(hi[e]) << 16));
+    }
+    const size_t o = rho * RV + 16 * rt + 4 * g;
+    *reinterpret_cast<uint2*>(w.ahi + o) = make_uint2(hi[0] | (static_cast<uint32_t>(hi[1]) << 16),
+                                                      hi[2] | (static_cast<uint32_t>(hi[3]) << 16));
+    *reinterpret_cast<uint2*>(w.alo + o) = make_uint2(lo[0] | (static_cast<uint32_t>(lo[1]) << 16),
+                                                      lo[2] | (static_cast<uint32_t>(lo[3]) << 16));
+  }
+  if (g == 0) w.wrow[rho] = l > 0.f ? 1.f : 0.f;
+}
+
+// ---- P3: O = A . W^V_t[h]^T (+ mu^V_t) ---------------------------------------------------------
+// grid (ceil(B*C / 64), ceil(d / 64), H); each of the 4 waves owns 16 rows x 64 output channels.
+template <int RV>
+__global__ __launch_bounds__(256) void oproj_prefill_kernel(PrefillParams p, PrefillWs w) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int h = blockIdx.z;
+  const int c0 = blockIdx.y * 64;
+  const int n0 = blockIdx.x * 64 + wave * 16;
+  const int ntok = p.B * p.C;
+  const int n = n0 + col;
+  const bool nok = n < ntok;
+  size_t rho_a = 0;
+  if (nok) {
+    const int b = n / p.C;
+    rho_a = (static_cast<size_t>(b) * p.H + h) * p.C + (n - b * p.C);
+  }
+  const uint16_t* wv = static_cast<const uint16_t*>(p.Wv) + wofs(p, h, RV);
+  floatx4_t acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < RV; r0 += 32) {
+    const uint4 ah = nok ? *reinterpret_cast<const uint4*>(w.ahi + rho_a * RV + r0 + 8 * g) : make_uint4(0, 0, 0, 0);
+    const uint4 al = nok ? *reinterpret_cast<const uint4*>(w.alo + rho_a * RV + r0 + 8 * g) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int jd = c0 + 16 * nt + col;
+      const uint4 bw = jd < p.d ? *reinterpret_cast<const uint4*>(wv + static_cast<size_t>(jd) * RV + r0 + 8 * g)
+                                : make_uint4(0, 0, 0, 0);
+      acc[nt] = mfma32(ah, bw, acc[nt]);
+      acc[nt] = mfma32(al, bw, acc[nt]);
+    }
+  }
+  const size_t mo = mofs(p, h);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int nn = n0 + 4 * g + e;
+    if (nn >= ntok) continue;
+    const int b = nn / p.C;
+    const int j = nn - b * p.C;
+    const float wr = w.wrow[(static_cast<size_t>(b) * p.H + h) * p.C + j];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int jd = c0 + 16 * nt + col;
+      if (jd >= p.d) continue;
+      float o = acc[nt][e];
+      if (p.mu_v != nullptr) o += wr * ld<BF16>(p.mu_v, mo + jd);
+      st<BF16>(p.out, (static_cast<size_t>(nn) * p.H + h) * p.d + jd, o);
+    }
+  }
+}
+
+struct EntryP {
+  int r_k, r_v;
+  void (*wkt)(PrefillParams, uint16_t*);
+  void (*qproj)(PrefillParams, PrefillWs);
+  void (*attn)(PrefillParams, PrefillWs);
+  void (*oproj)(PrefillParams, PrefillWs);
+};
+
+template <int RK, int RV>
+constexpr EntryP entryP() {
+  return {RK, RV, wk_transpose_kernel<RK>, qproj_prefill_kernel<RK>, prefill_attn_kernel<RK, RV>,
+          oproj_prefill_kernel<RV>};
+}
+
+const EntryP kTableP[] = {
+    entryP<64, 64>(), entryP<128, 128>(), entryP<256, 256>(), entryP<64, 128>(), entryP<128, 256>(),
+};
+
+const EntryP* findP(int r_k, int r_v) {
+  for (const EntryP& e : kTableP)
+    if (e.r_k == r_k && e.r_v == r_v) return &e;
+  return nullptr;
+}
+
+bool mfma_prefill(int dtype, int r_k, int r_v, int d_head) {
+  return dtype == LLA_BF16 && d_head % 32 == 0 && findP(r_k, r_v) != nullptr;
+}
+
+}  // namespace
 
 bool prefill_supported(int variant, int dtype, int r_k, int r_v) {
-  return valu_supported(variant, dtype, r_k, r_v);
+  return valu_supported(variant, dtype, r_k, r_v) || (dtype == LLA_BF16 && findP(r_k, r_v) != nullptr);
 }
 
 void prefill_plan(const lla_desc& desc, int B, int C, int* splits, int* chunk) {
+  if (mfma_prefill(desc.dtype, desc.r_k, desc.r_v, desc.d_head)) {
+    *splits = 1;
+    *chunk = desc.n_max;
+    return;
+  }
   valu_plan(desc, B * C, splits, chunk);
 }
 
 size_t prefill_workspace_bytes(const lla_desc& desc, int B, int C) {
+  if (mfma_prefill(desc.dtype, desc.r_k, desc.r_v, desc.d_head))
+    return prefill_mfma_bytes(B, C, desc.H, desc.d_head, desc.r_k, desc.r_v);
   int s, c;
   prefill_plan(desc, B, C, &s, &c);
   return valu_workspace_bytes(desc, B * C, s);
 }
 
 hipError_t launch_prefill(const PrefillParams& pp, int dtype, hipStream_t stream) {
+  if (mfma_prefill(dtype, pp.r_k, pp.r_v, pp.d)) {
+    const EntryP* e = findP(pp.r_k, pp.r_v);
+    if (prefill_mfma_bytes(pp.B, pp.C, pp.H, pp.d, pp.r_k, pp.r_v) > pp.ws_bytes)
+      return hipErrorInvalidValue;  // the plan does not fit the workspace: never launch
+    const PrefillWs w = carve(pp.ws, pp.B, pp.C, pp.H, pp.d, pp.r_k, pp.r_v);
+    const unsigned ntok = static_cast<unsigned>(pp.B) * pp.C;
+    hipLaunchKernelGGL(e->wkt, dim3(pp.H), dim3(256), 0, stream, pp, w.wkt);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(e->qproj, dim3((ntok + 63) / 64, pp.r_k / 64, pp.H), dim3(256), 0, stream, pp, w);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(e->attn, dim3((pp.C + kRowsWG - 1) / kRowsWG, pp.H, pp.B), dim3(512), 0, stream, pp, w);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(e->oproj, dim3((ntok + 63) / 64, (pp.d + 63) / 64, pp.H), dim3(256), 0, stream, pp, w);
+    return hipGetLastError();
+  }
   DecodeParams p{};
   p.q = pp.q;
   p.zk = pp.zk;

@@ -398,3 +398,64 @@ def test_encode_large_token_counts(variant, H, d, T, r, B, C):
     rk_, rv_ = O.encode_into_cache(z0, z0, xk, xv, Ek, Ev, pos, mk, None, variant)
     assert_close(host(zk), rk_, dtype, f"encode zk {variant} B={B} C={C}")
     assert_close(host(zv), rv_, dtype, f"encode zv {variant} B={B} C={C}")
+
+
+@pytest.mark.parametrize("variant", ["per_head", "2d"])
+@pytest.mark.parametrize("rk,rv", [(64, 64), (128, 128), (256, 256), (64, 128), (128, 256)])
+def test_prefill_mfma(variant, rk, rv):
+    """MFMA chunked prefill: two row blocks with a ragged tail (C=150), one sequence with context
+    and one without, mu on/off, plain and 8x sharpened queries."""
+    dtype = "bf16"
+    B, C, H, d, T = 2, 150, 3, 64, 2
+    ctx = np.array([300, 0], np.int32)
+    n_max = 460
+    for gain, mu in ((1.0, True), (8.0, False)):
+        c = upload(synth.random_case(variant, dtype, B, H, d, T, rk, rv, n_max, 7800 + rk + rv, with_mu=mu), dtype)
+        q = synth.to_storage(gain * synth.normal((B, C, H, d), 7801), dtype)
+        desc = mk_desc(variant, dtype, H, d, T, rk, rv, n_max)
+        for t in range(T):
+            out = torch.empty(B, C, H, d, dtype=torch.bfloat16, device="cuda")
+            lla.lla_attend_prefill(desc, B, C, t, dev(q, dtype), c["_zk"], c["_zv"], dev(ctx), c["_Wk"],
+                                   c["_Wv"], c["_muk"] if mu else None, c["_muv"] if mu else None, out,
+                                   lla.workspace(desc, B, C))
+            torch.cuda.synchronize()
+            ref = O.attend_prefill(q, c["zk"], c["zv"], c["Wk"], c["Wv"], t, ctx,
+                                   c["mu_k"] if mu else None, c["mu_v"] if mu else None, variant=variant)
+            assert_close(host(out), ref, dtype, f"prefill mfma {variant} r=({rk},{rv}) gain={gain} t={t}")
+
+
+def test_lla2d_prefill_full_size_sampled():
+    """LLA-2D chunked prefill at full size (B=128, C=512, N_ctx=8192, r=256): the chunk is encoded
+    into slots 8192..8703, then loop 0 attends causally; rows {0, 255, 511} of sequence 0 (all
+    heads) are checked against the oracle (a row j at position ctx + j is a one-row prefill)."""
+    s = synth.CASES["lla2d"]
+    B, C, H, d, T, r, N = s.B, s.C, s.H, s.d, s.T, s.r_k, s.N
+    n_max = N + C
+    desc = mk_desc("2d", "bf16", H, d, T, r, r, n_max)
+    g = {}
+    g["zk"] = synth.device_normal_(torch.empty(B, n_max, r, dtype=torch.bfloat16, device="cuda"), synth.seed(s.case, synth.SEED_ZK))
+    g["zv"] = synth.device_normal_(torch.empty(B, n_max, r, dtype=torch.bfloat16, device="cuda"), synth.seed(s.case, synth.SEED_ZV))
+    Wk = synth.orthonormal_W_2d(T, H, d, r, synth.seed(s.case, synth.SEED_WK), "bf16")
+    Wv = synth.orthonormal_W_2d(T, H, d, r, synth.seed(s.case, synth.SEED_WV), "bf16")
+    Ek, Ev = synth.pinv_E_from_W_2d(Wk, "bf16"), synth.pinv_E_from_W_2d(Wv, "bf16")
+    xk = synth.device_normal_(torch.empty(B, C, T, H, d, dtype=torch.bfloat16, device="cuda"), synth.seed(s.case, synth.SEED_XK))
+    xv = synth.device_normal_(torch.empty(B, C, T, H, d, dtype=torch.bfloat16, device="cuda"), synth.seed(s.case, synth.SEED_XV))
+    q = synth.device_normal_(torch.empty(B, C, H, d, dtype=torch.bfloat16, device="cuda"), synth.seed(s.case, synth.SEED_Q))
+    ctx = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    lla.lla_encode(desc, B, C, xk, xv, dev(Ek, "bf16"), dev(Ev, "bf16"), None, None, ctx, g["zk"], g["zv"])
+    out = torch.empty(B, C, H, d, dtype=torch.bfloat16, device="cuda")
+    lla.lla_attend_prefill(desc, B, C, 0, q, g["zk"], g["zv"], ctx, dev(Wk, "bf16"), dev(Wv, "bf16"),
+                           None, None, out, lla.workspace(desc, B, C))
+    torch.cuda.synchronize()
+    zk0, zv0 = host(g["zk"][:1]), host(g["zv"][:1])
+    # the encoded chunk slots match the oracle's encode of the same per-loop K/V
+    ek, _ = O.encode_into_cache(np.zeros((1, n_max, r)), np.zeros((1, n_max, r)), host(xk[:1]), host(xv[:1]),
+                                Ek, Ev, [N], variant="2d")
+    assert_close(zk0[:, N:], ek[:, N:], "bf16", "2d chunk encode")
+    q0 = host(q[:1])
+    o0 = host(out[:1])
+    for j in (0, 255, 511):
+        ref = O.attend_prefill(q0[:, j:j + 1], zk0, zv0, Wk, Wv, 0, [N + j], variant="2d")
+        assert_close(o0[:, j:j + 1], ref, "bf16", f"2d prefill row {j}")
+    del g, xk, xv, q, out
+    torch.cuda.empty_cache()
