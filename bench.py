@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 4 GiB device copy (scale reference for HBM counters)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the LLA-2D decode and chunked-prefill figures")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="measure only the LLA-2D chunked prefill (for profiling)")
     return ap.parse_args()
 
 
@@ -89,6 +93,9 @@ def main():
         sys.exit(1)
     lla.library()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
+    if args.only_prefill:
+        print(json.dumps({"lla2d_prefill": lla2d_prefill(args)}), flush=True)
+        return
     s = synth.CASES[args.workload]
     D = args.layers or s.D
     B, H, d, T, rk, rv, N = s.B, s.H, s.d, s.T, s.r_k, s.r_v, s.N
@@ -197,6 +204,12 @@ def main():
     if not args.no_cpu_baseline and not two_d:
         cpu = cpu_baseline(args, s, D, zk, zv, Wk, Wv, Ek, Ev, q, kself, vself, xk, xv, lens)
 
+    extras = None
+    if not args.no_extras and args.workload == "capacity":
+        del zk, zv, q, kself, vself, xk, xv, out
+        torch.cuda.empty_cache()
+        extras = {"lla2d_decode": lla2d_decode(args), "lla2d_prefill": lla2d_prefill(args)}
+
     res = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -236,7 +249,122 @@ def main():
         "cpu_baseline": cpu,
     }
     res.update(res_extra)
+    if extras is not None:
+        res["extras"] = extras
     print(json.dumps(res), flush=True)
+
+
+def _timed(fn, steps, warmup):
+    """HIP-event time of fn() per call on the current stream (ms), after warm-up calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def lla2d_decode(args):
+    """LLA-2D decode step (H=16, d=128, T=4, r=256/256, B=128, N=8192): 4 loop reads + encode."""
+    import torch
+    from decode_attention_lla_amd import lla, synth
+    s = synth.CASES["lla2d"]
+    B, H, d, T, r, N = s.B, s.H, s.d, s.T, s.r_k, s.N
+    n_max = N + 1
+    bf = torch.bfloat16
+    desc = lla.make_desc(lla.LLA_2D, lla.LLA_BF16, H, d, T, r, r, n_max)
+    zk = synth.device_normal_(torch.empty(B, n_max, r, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZK))
+    zv = synth.device_normal_(torch.empty(B, n_max, r, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZV))
+    wk = synth.orthonormal_W_2d(T, H, d, r, synth.seed(s.case, synth.SEED_WK), "bf16")
+    wv = synth.orthonormal_W_2d(T, H, d, r, synth.seed(s.case, synth.SEED_WV), "bf16")
+    Wk, Wv = torch.from_numpy(wk).to(bf).cuda(), torch.from_numpy(wv).to(bf).cuda()
+    Ek = torch.from_numpy(synth.pinv_E_from_W_2d(wk, "bf16")).to(bf).cuda()
+    Ev = torch.from_numpy(synth.pinv_E_from_W_2d(wv, "bf16")).to(bf).cuda()
+    q = synth.device_normal_(torch.empty(T, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_Q))
+    ks = synth.device_normal_(torch.empty(T, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF))
+    vs = synth.device_normal_(torch.empty(T, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF) + 1)
+    x = synth.device_normal_(torch.empty(2, B, 1, T, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_XK))
+    out = torch.empty(T, B, H, d, dtype=bf, device="cuda")
+    lens = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    ws = lla.workspace(desc, B, 1)
+
+    def read(t):
+        lla.lla_attend_decode(desc, B, t, q[t], zk, zv, lens, Wk, Wv, None, None, ks[t], vs[t], out[t], None, ws)
+
+    def step():
+        for t in range(T):
+            read(t)
+        lla.lla_encode(desc, B, 1, x[0], x[1], Ek, Ev, None, None, lens, zk, zv)
+
+    ms_read = _timed(lambda: read(0), 20, 3)
+    ms_step = _timed(step, 10, 2)
+    latent = B * N * 2 * r * 2
+    flops = 2.0 * B * H * N * 2 * r
+    return {"workload": f"lla2d: H={H}, d_head={d}, T={T}, r_k=r_v={r}, B={B}, N={N}, bf16",
+            "tokens_per_s": round(B / (ms_step / 1e3), 1), "ms_per_step": round(ms_step, 4),
+            "read_us": round(ms_read * 1e3, 2),
+            "latent_GBps": round(latent / (ms_read / 1e3) / 1e9, 1),
+            "latent_frac_of_peak": round(latent / (ms_read / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_TFLOPs": round(flops / (ms_read / 1e3) / 1e12, 2),
+            "mfma_util_bf16_dense": round(flops / (ms_read / 1e3) / 2.5e15, 4)}
+
+
+def lla2d_prefill(args):
+    """LLA-2D chunked prefill (B=128, C=512, N_ctx=8192, r=256/256): encode the chunk, then one
+    causal prefill read per loop (T=4)."""
+    import torch
+    from decode_attention_lla_amd import lla, synth
+    s = synth.CASES["lla2d"]
+    B, H, d, T, r, N, C = s.B, s.H, s.d, s.T, s.r_k, s.N, s.C
+    n_max = N + C
+    bf = torch.bfloat16
+    desc = lla.make_desc(lla.LLA_2D, lla.LLA_BF16, H, d, T, r, r, n_max)
+    zk = synth.device_normal_(torch.empty(B, n_max, r, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZK))
+    zv = synth.device_normal_(torch.empty(B, n_max, r, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZV))
+    wk = synth.orthonormal_W_2d(T, H, d, r, synth.seed(s.case, synth.SEED_WK), "bf16")
+    wv = synth.orthonormal_W_2d(T, H, d, r, synth.seed(s.case, synth.SEED_WV), "bf16")
+    Wk, Wv = torch.from_numpy(wk).to(bf).cuda(), torch.from_numpy(wv).to(bf).cuda()
+    Ek = torch.from_numpy(synth.pinv_E_from_W_2d(wk, "bf16")).to(bf).cuda()
+    Ev = torch.from_numpy(synth.pinv_E_from_W_2d(wv, "bf16")).to(bf).cuda()
+    xk = synth.device_normal_(torch.empty(B, C, T, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_XK))
+    xv = synth.device_normal_(torch.empty(B, C, T, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_XV))
+    q = synth.device_normal_(torch.empty(T, B, C, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_Q))
+    out = torch.empty(B, C, H, d, dtype=bf, device="cuda")
+    ctx = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    ws = lla.workspace(desc, B, C)
+
+    def encode():
+        lla.lla_encode(desc, B, C, xk, xv, Ek, Ev, None, None, ctx, zk, zv)
+
+    def attend(t):
+        lla.lla_attend_prefill(desc, B, C, t, q[t], zk, zv, ctx, Wk, Wv, None, None, out, ws)
+
+    def step():
+        encode()
+        for t in range(T):
+            attend(t)
+
+    ms_enc = _timed(encode, 3, 1)
+    ms_att = _timed(lambda: attend(0), 3, 1)
+    ms_step = _timed(step, 2, 1)
+    keys = sum(N + j + 1 for j in range(C))                  # per (sequence, head)
+    att_flops = 2.0 * B * H * keys * 2 * r                   # scores + latent-V products
+    proj_flops = 2.0 * B * C * H * d * 2 * r                 # q~ and output projections
+    enc_flops = 2.0 * B * C * 2 * r * T * H * d              # both axes
+    return {"workload": f"lla2d prefill: C={C} per sequence, B={B}, N_ctx={N}, H={H}, d_head={d}, "
+                        f"T={T}, r_k=r_v={r}, bf16",
+            "tokens_per_s": round(B * C / (ms_step / 1e3), 1), "ms_per_chunk": round(ms_step, 3),
+            "encode_ms": round(ms_enc, 3), "attend_ms_per_loop": round(ms_att, 3),
+            "attend_TFLOPs": round((att_flops + proj_flops) / (ms_att / 1e3) / 1e12, 1),
+            "attend_mfma_util_bf16_dense": round((att_flops + proj_flops) / (ms_att / 1e3) / 2.5e15, 4),
+            "encode_TFLOPs": round(enc_flops / (ms_enc / 1e3) / 1e12, 1),
+            "encode_mfma_util_bf16_dense": round(enc_flops / (ms_enc / 1e3) / 2.5e15, 4)}
 
 
 def cpu_baseline(args, s, D, zk, zv, Wk, Wv, Ek, Ev, q, kself, vself, xk, xv, lens):

@@ -35,6 +35,31 @@ typedef const __attribute__((address_space(1))) void* gptr_t;  // global address
 typedef __attribute__((address_space(3))) void* lptr_t;         // LDS address space
 
 constexpr float kLazy2d = 8.0f;
+
+// XOR swizzle of the 16-byte chunks of V row `row` inside each aligned 8-chunk window. Every four
+// consecutive rows land on four distinct chunk pairs (the transposed read below touches one
+// adjacent pair in each of four consecutive rows per 16-lane group), and every eight consecutive
+// rows on eight distinct chunks.
+__device__ __forceinline__ int vswz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// A operand of v_mfma_f32_16x16x16bf16_1k holding Z^V^T[r0 + i][kb + k] (i, k < 16) from a
+// row-major [key][RV] bf16 tile whose 16-byte chunks are XOR-swizzled by vswz(key). One
+// ds_read_b64_tr_b16: in each 16-lane group q, source lane 4e + c points at the 8 bytes
+// V[kb + 4q + e][r0 + 4c .. +3]; the transposed read hands lane i of the group element e =
+// V[kb + 4q + e][r0 + i], which is the MFMA's A layout (row i, k = 4q + e). (Lane mapping of the
+// instruction checked on the hardware.)
+typedef __attribute__((address_space(3))) short4_t* lds_short4_ptr;
+template <int RV>
+__device__ __forceinline__ short4_t v_operand_tr(const char* vt, int kb, int r0, int lane) {
+  const int q = lane >> 4;
+  const int j = lane & 15;
+  const int row = kb + 4 * q + (j >> 2);
+  const int r = r0 + 4 * (j & 3);
+  const int lc = r >> 3;
+  const int pc = (lc & ~7) | ((lc & 7) ^ vswz(row));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_ptr)(vt + row * RV * 2 + pc * 16 + (r & 7) * 2));
+}
+
 constexpr int kQB = 8;     // sequences per qproj / combine workgroup
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -109,10 +134,10 @@ __global__ __launch_bounds__(256) void qproj2d_kernel(DecodeParams p, float* qt,
 //   * the next tile's K rows are loaded into registers and its V rows go straight to LDS with
 //     global_load_lds (each lane's 16 bytes land at base + 16*lane), into the other half of the
 //     wave's double-buffered ring, so both loads overlap the current tile's MFMAs;
-//   * V rows are stored unpadded with 16-byte chunks XOR-swizzled by the row group: chunk c of
-//     row rho sits at (c & ~7) | ((c & 7) ^ 2*((rho >> 2) & 3)), which puts the four lane groups of
-//     the transposed 16-bit reads on disjoint banks. The swizzle is applied by choosing each lane's
-//     global source address;
+//   * V rows are stored unpadded with 16-byte chunks XOR-swizzled by the row: chunk c of row rho
+//     sits at (c & ~7) | ((c & 7) ^ vswz(rho)), so the transposed reads of the MFMA's V operand
+//     (ds_read_b64_tr_b16, 16 rows x 32 bytes per read) spread evenly over the banks. The swizzle
+//     is applied by choosing each lane's global source address;
 //   * rows past the valid range are clamped to the last valid token (finite data times a zero
 //     weight), so a partial tail tile needs no separate zeroing.
 template <int RK, int RV>
@@ -180,7 +205,7 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
       const int f = i * 64 + lane;               // LDS slot of this lane
       const int row = f / CPR;
       const int pc = f - row * CPR;
-      const int lc = (pc & ~7) | ((pc & 7) ^ (2 * ((row >> 2) & 3)));
+      const int lc = (pc & ~7) | ((pc & 7) ^ vswz(row));
       const char* src = zvb + (static_cast<size_t>(min(tok0 + row, last)) * RV + lc * 8) * 2;
       __builtin_amdgcn_global_load_lds((const gptr_t)src, (lptr_t)(dst + i * 1024), 16, 0, 0);
     }
@@ -249,15 +274,8 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
     const char* vt = myring + buf * CF::kVTile;
     // A^T[r][head] += Z^V^T[r][tokens 4g+e] . P^T[tokens][head]
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int c = 2 * rt + (col >> 3);
-      const int pc = (c & ~7) | ((c & 7) ^ (2 * g));
-      const int off = pc * 16 + (col & 7) * 2;
-      short4_t av;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) av[e] = *reinterpret_cast<const short*>(vt + (4 * g + e) * RV * 2 + off);
-      D[rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bp, D[rt], 0, 0, 0);
-    }
+    for (int rt = 0; rt < RT; ++rt)
+      D[rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v_operand_tr<RV>(vt, 0, 16 * rt, lane), bp, D[rt], 0, 0, 0);
     // the ring half just read is refilled two tiles from now; finish the reads first
     wave_lds_sync();
 #pragma unroll

@@ -16,7 +16,8 @@
 //      and V tiles are fetched with global_load_lds into XOR-swizzled, double-buffered LDS and
 //      shared by the 8 waves; S^T = Z^K . Q~^T, online softmax per row with a causal mask, then
 //      A^T += Z^V^T . P^T with P taken straight from the S^T accumulator layout (the B operand of
-//      v_mfma_f32_16x16x16bf16_1k); the normalised latent sums are stored as bf16 hi + lo;
+//      v_mfma_f32_16x16x16bf16_1k) and Z^V^T read with the transposing ds_read_b64_tr_b16; the
+//      normalised latent sums are stored as bf16 hi + lo;
 //   P3 O = A . W^V_t[h]^T (+ mu^V_t when the row saw any latent) on MFMA, both A parts.
 // Rows are numbered rho = (b*H + h)*C + j. LLA-2D and per-head differ only in which latent
 // sequence a head reads (b, or (b, h)) and in the factor and mu offsets.
@@ -36,6 +37,31 @@ typedef const __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 constexpr float kLazyP = 8.0f;
+
+// XOR swizzle of the 16-byte chunks of V row `row` inside each aligned 8-chunk window. Every four
+// consecutive rows land on four distinct chunk pairs (the transposed read below touches one
+// adjacent pair in each of four consecutive rows per 16-lane group), and every eight consecutive
+// rows on eight distinct chunks.
+__device__ __forceinline__ int vswz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// A operand of v_mfma_f32_16x16x16bf16_1k holding Z^V^T[r0 + i][kb + k] (i, k < 16) from a
+// row-major [key][RV] bf16 tile whose 16-byte chunks are XOR-swizzled by vswz(key). One
+// ds_read_b64_tr_b16: in each 16-lane group q, source lane 4e + c points at the 8 bytes
+// V[kb + 4q + e][r0 + 4c .. +3]; the transposed read hands lane i of the group element e =
+// V[kb + 4q + e][r0 + i], which is the MFMA's A layout (row i, k = 4q + e). (Lane mapping of the
+// instruction checked on the hardware.)
+typedef __attribute__((address_space(3))) short4_t* lds_short4_ptr;
+template <int RV>
+__device__ __forceinline__ short4_t v_operand_tr(const char* vt, int kb, int r0, int lane) {
+  const int q = lane >> 4;
+  const int j = lane & 15;
+  const int row = kb + 4 * q + (j >> 2);
+  const int r = r0 + 4 * (j & 3);
+  const int lc = r >> 3;
+  const int pc = (lc & ~7) | ((lc & 7) ^ vswz(row));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_ptr)(vt + row * RV * 2 + pc * 16 + (r & 7) * 2));
+}
+
 constexpr int kRowsWG = 128;  // chunk rows per attention workgroup (8 waves x 16)
 constexpr int kKeyTile = 32;  // latents per K/V tile
 
@@ -150,7 +176,27 @@ __global__ __launch_bounds__(256) void qproj_prefill_kernel(PrefillParams p, Pre
 }
 
 // ---- P2: causal flash attention over the latents ----------------------------------------------
-// grid (ceil(C / 128), H, B); 512 threads. Wave w owns chunk rows j0 + 16 w .. + 15.
+// 1D grid of RB*H*B workgroups (RB = ceil(C / 128) row blocks), 512 threads; wave w owns chunk
+// rows j0 + 16 w .. + 15. Workgroups are dispatched round-robin over the 8 XCDs; when B is a
+// multiple of 8 the id is remapped so that every workgroup of one sequence runs on the same XCD
+// and its latents are shared through that XCD's L2.
+// K/V tiles go through a kStages-deep LDS ring: tile i+kStages-1 is fetched while tile i is
+// computed, one barrier per tile. Every wave issues the same number of loads per tile (small tiles
+// repeat an instruction on two waves, writing identical bytes), so the vmcnt thresholds are
+// compile-time constants.
+constexpr int kStages = 4;
+
+template <int N>
+__device__ __forceinline__ void wait_vm_tiles(int ahead) {
+  // vmcnt(ahead * N) for ahead in 0..kStages-1, N loads per tile and wave
+  switch (ahead) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * N) & 15) | (((2 * N) >> 4) << 14)); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0f70 | ((3 * N) & 15) | (((3 * N) >> 4) << 14)); break;
+  }
+}
+
 template <int RK, int RV>
 __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, PrefillWs w) {
   constexpr int KS = RK / 32;
@@ -161,18 +207,34 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   constexpr int VT_BYTES = kKeyTile * RV * 2;
   constexpr int IK = KT_BYTES / 1024;         // 1 KiB global_load_lds instructions per K tile
   constexpr int IV = VT_BYTES / 1024;
+  constexpr int LK = IK >= 8 ? IK / 8 : 1;    // K loads per wave and tile
+  constexpr int LV = IV >= 8 ? IV / 8 : 1;
   static_assert(RK % 64 == 0 && RV % 64 == 0, "swizzle windows need 8 chunks per row");
-  __shared__ __attribute__((aligned(16))) char kbuf[2][KT_BYTES];
-  __shared__ __attribute__((aligned(16))) char vbuf[2][VT_BYTES];
+  static_assert(IK % 8 == 0 || 8 % IK == 0, "K tile instructions spread evenly over 8 waves");
+  static_assert(IV % 8 == 0 || 8 % IV == 0, "V tile instructions spread evenly over 8 waves");
+  static_assert(3 * (LK + LV) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) char kbuf[kStages][KT_BYTES];
+  __shared__ __attribute__((aligned(16))) char vbuf[kStages][VT_BYTES];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  const int j0 = blockIdx.x * kRowsWG;
+  const int RB = (p.C + kRowsWG - 1) / kRowsWG;
+  const int NB = RB * p.H;                    // workgroups per sequence
+  int b, k;
+  if ((p.B & 7) == 0) {
+    const int P = blockIdx.x;
+    const int rest = P >> 3;
+    k = rest % NB;
+    b = (rest / NB) * 8 + (P & 7);
+  } else {
+    b = blockIdx.x / NB;
+    k = blockIdx.x - b * NB;
+  }
+  const int h = k / RB;
+  const int j0 = (k - h * RB) * kRowsWG;
   const int ctx = p.ctx_lens[b];
 
   // this lane's query row (for scores and accumulators): chunk row jr
@@ -209,24 +271,28 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     beta = part * p.scale_log2;
   }
 
-  // cooperative tile fetch into ring half `buf`; rows past kmax are clamped to kmax
-  auto issue = [&](int tile, int buf) {
+  // cooperative tile fetch into ring stage `st`; rows past kmax are clamped to kmax
+  auto issue = [&](int tile, int st) {
     const int key0 = tile * kKeyTile;
-    for (int i = wave; i < IK; i += 8) {
+#pragma unroll
+    for (int u = 0; u < LK; ++u) {
+      const int i = IK >= 8 ? wave + 8 * u : wave % IK;
       const int f = i * 64 + lane;
       const int row = f / CPK;
       const int pc = f - row * CPK;
       const int lc = (pc & ~7) | ((pc & 7) ^ (row & 7));
       const char* src = zk + (static_cast<size_t>(min(key0 + row, kmax)) * RK + lc * 8) * 2;
-      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(&kbuf[buf][i * 1024]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(&kbuf[st][i * 1024]), 16, 0, 0);
     }
-    for (int i = wave; i < IV; i += 8) {
+#pragma unroll
+    for (int u = 0; u < LV; ++u) {
+      const int i = IV >= 8 ? wave + 8 * u : wave % IV;
       const int f = i * 64 + lane;
       const int row = f / CPV;
       const int pc = f - row * CPV;
-      const int lc = (pc & ~7) | ((pc & 7) ^ (2 * ((row >> 2) & 3)));
+      const int lc = (pc & ~7) | ((pc & 7) ^ vswz(row));
       const char* src = zv + (static_cast<size_t>(min(key0 + row, kmax)) * RV + lc * 8) * 2;
-      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(&vbuf[buf][i * 1024]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(&vbuf[st][i * 1024]), 16, 0, 0);
     }
   };
 
@@ -236,15 +302,20 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   float m = kNegInf;
   float l = 0.f;
 
-  if (ntiles > 0) issue(0, 0);
+#pragma unroll
+  for (int s0 = 0; s0 < kStages - 1; ++s0)
+    if (s0 < ntiles) issue(s0, s0);
   for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of `tile` have landed
-    __syncthreads();                     // ... and every other wave's
-    if (tile + 1 < ntiles) issue(tile + 1, buf ^ 1);
+    const int st = tile % kStages;
+    // this wave's loads of `tile` have landed (later tiles may still be in flight) ...
+    wait_vm_tiles<LK + LV>(min(kStages - 2, ntiles - 1 - tile));
+    // ... and every other wave's; everyone has also finished computing tile - 1, whose stage is
+    // the one refilled next
+    __syncthreads();
+    if (tile + kStages - 1 < ntiles) issue(tile + kStages - 1, (tile + kStages - 1) % kStages);
     __asm__ volatile("" ::: "memory");
-    const char* kt = kbuf[buf];
-    const char* vt = vbuf[buf];
+    const char* kt = kbuf[st];
+    const char* vt = vbuf[st];
     const int key0 = tile * kKeyTile;
     float sc[2][4];
     float tmax = kNegInf;
@@ -289,18 +360,10 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
       }
       // A^T[r][row] += Z^V^T[r][keys 16 kt16 + 4 g + e] . P^T
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int c = 2 * rt + (col >> 3);
-        const int pc = (c & ~7) | ((c & 7) ^ (2 * g));
-        const int off = pc * 16 + (col & 7) * 2;
-        short4_t av;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          av[e] = *reinterpret_cast<const short*>(vt + (16 * kt16 + 4 * g + e) * RV * 2 + off);
-        D[rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bp, D[rt], 0, 0, 0);
-      }
+      for (int rt = 0; rt < RT; ++rt)
+        D[rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v_operand_tr<RV>(vt, 16 * kt16, 16 * rt, lane), bp,
+                                                          D[rt], 0, 0, 0);
     }
-    __syncthreads();  // every wave is done with ring half `buf` before it is refilled
   }
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
@@ -444,7 +507,8 @@ hipError_t launch_prefill(const PrefillParams& pp, int dtype, hipStream_t stream
     hipLaunchKernelGGL(e->qproj, dim3((ntok + 63) / 64, pp.r_k / 64, pp.H), dim3(256), 0, stream, pp, w);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(e->attn, dim3((pp.C + kRowsWG - 1) / kRowsWG, pp.H, pp.B), dim3(512), 0, stream, pp, w);
+    const unsigned nwg = static_cast<unsigned>((pp.C + kRowsWG - 1) / kRowsWG) * pp.H * pp.B;
+    hipLaunchKernelGGL(e->attn, dim3(nwg), dim3(512), 0, stream, pp, w);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(e->oproj, dim3((ntok + 63) / 64, (pp.d + 63) / 64, pp.H), dim3(256), 0, stream, pp, w);

@@ -403,11 +403,12 @@ def test_encode_large_token_counts(variant, H, d, T, r, B, C):
 @pytest.mark.parametrize("variant", ["per_head", "2d"])
 @pytest.mark.parametrize("rk,rv", [(64, 64), (128, 128), (256, 256), (64, 128), (128, 256)])
 def test_prefill_mfma(variant, rk, rv):
-    """MFMA chunked prefill: two row blocks with a ragged tail (C=150), one sequence with context
-    and one without, mu on/off, plain and 8x sharpened queries."""
+    """MFMA chunked prefill: two row blocks with a ragged tail (C=150), eight sequences (the
+    workgroup order that groups a sequence on one XCD) with different context lengths including
+    none, mu on/off, plain and 8x sharpened queries."""
     dtype = "bf16"
-    B, C, H, d, T = 2, 150, 3, 64, 2
-    ctx = np.array([300, 0], np.int32)
+    B, C, H, d, T = 8, 150, 3, 64, 2
+    ctx = np.array([300, 0, 17, 299, 1, 64, 128, 250], np.int32)
     n_max = 460
     for gain, mu in ((1.0, True), (8.0, False)):
         c = upload(synth.random_case(variant, dtype, B, H, d, T, rk, rv, n_max, 7800 + rk + rv, with_mu=mu), dtype)
