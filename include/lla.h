@@ -73,9 +73,13 @@ typedef struct {
 } lla_desc;
 
 /* Compiled (r_k, r_v) pairs.
- *   per-head, f32 and bf16: (8,8) (16,16) (24,24) (32,32) (64,64) (96,96) (128,128) (96,160)
- *   2D, bf16:               (128,128) (256,256)      2D, f32: (8,8) (16,16) (32,32)
- * Anything else returns LLA_ERR_UNSUPPORTED. */
+ *   Streaming (VALU) kernels, every variant and storage type:
+ *       (8,8) (16,16) (24,24) (32,32) (64,64) (96,96) (128,128) (96,160) (256,256)
+ *   LLA-2D decode, bf16, d_head <= 128, on MFMA:              (64,64) (128,128) (256,256)
+ *   Chunked prefill, bf16, d_head a multiple of 32, on MFMA:  (64,64) (128,128) (256,256)
+ *                                                              (64,128) (128,256)
+ *   Encode: any r <= 512 (bf16 on MFMA, fp32 on the VALU).
+ * A decode or prefill call with a pair that none of these covers returns LLA_ERR_UNSUPPORTED. */
 
 /* Bytes of device workspace that lla_attend_decode (C == 1) or lla_attend_prefill (C > 1) needs
  * for this descriptor and batch. May be 0. Returns 0 as well for an invalid descriptor (the
