@@ -18,9 +18,9 @@
 //      loads, rows padded so the transposed 16-bit reads are bank-conflict free). Online softmax
 //      per head, rescaling only when the running max grows by more than 8 (base 2). The four
 //      waves merge through LDS and the workgroup writes one (m, l, a[r_v]) partial per head.
-//   3. combine2d_kernel: per (head, block of sequences), W^V_t[h] staged once in LDS; merges the
-//      split partials by log-sum-exp, adds the optional self token, projects, adds mu^V_t,
-//      normalises, writes o and lse.
+//   3. combine2d_kernel: per (sequence, head); merges the split partials by log-sum-exp, adds the
+//      optional self token, projects once through W^V_t[h], adds mu^V_t, normalises, writes o
+//      and lse.
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -370,6 +370,16 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
     if (p.mu_v != nullptr) mu_j = ld<BF16>(p.mu_v, wrow + j);
     if (p.v_self != nullptr) vs_j = ld<BF16>(p.v_self, bh * p.d + j);
   }
+  // the split latent sums do not depend on the merge: the first kPre splits are loaded now
+  constexpr int kPre = 4;
+  float pa[RPT][kPre];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = tid + 256 * i;
+#pragma unroll
+    for (int s2 = 0; s2 < kPre; ++s2)
+      pa[i][s2] = (r < RV && s2 < S_) ? pw[static_cast<size_t>(s2) * (2 + RV) + 2 + r] : 0.f;
+  }
   // wave 0: split maxima and sums, self score
   float ms = kNegInf, ls = 0.f, pt = 0.f;
   if (tid < 64) {
@@ -397,13 +407,15 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
     }
   }
   __syncthreads();
-  // merged latent sum a = sum_s f_s a_s (the S loads of each entry are independent)
+  // merged latent sum a = sum_s f_s a_s (f_s is 0 for splits >= S)
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = tid + 256 * i;
     if (r < RV) {
       float a = 0.f;
-      for (int s2 = 0; s2 < S_; ++s2) a += f_s[s2] * pw[static_cast<size_t>(s2) * (2 + RV) + 2 + r];
+#pragma unroll
+      for (int s2 = 0; s2 < kPre; ++s2) a += f_s[s2] * pa[i][s2];
+      for (int s2 = kPre; s2 < S_; ++s2) a += f_s[s2] * pw[static_cast<size_t>(s2) * (2 + RV) + 2 + r];
       a_s[r] = a;
     }
   }

@@ -15,9 +15,9 @@
 //      rows of one head; each wave keeps its 16 rows of Q~ (hi and lo) in registers; 32-latent K
 //      and V tiles are fetched with global_load_lds into XOR-swizzled, double-buffered LDS and
 //      shared by the 8 waves; S^T = Z^K . Q~^T, online softmax per row with a causal mask, then
-//      A^T += Z^V^T . P^T with P taken straight from the S^T accumulator layout (the B operand of
-//      v_mfma_f32_16x16x16bf16_1k) and Z^V^T read with the transposing ds_read_b64_tr_b16; the
-//      normalised latent sums are stored as bf16 hi + lo;
+//      A^T += Z^V^T . P^T on v_mfma_f32_16x16x32_bf16 with P taken straight from the S^T
+//      accumulators (two 16-key halves form one K=32 step) and Z^V^T read with the transposing
+//      ds_read_b64_tr_b16; the normalised latent sums are stored as bf16 hi + lo;
 //   P3 O = A . W^V_t[h]^T (+ mu^V_t when the row saw any latent) on MFMA, both A parts.
 // Rows are numbered rho = (b*H + h)*C + j. LLA-2D and per-head differ only in which latent
 // sequence a head reads (b, or (b, h)) and in the factor and mu offsets.
@@ -349,20 +349,27 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
       for (int rt = 0; rt < RT; ++rt) D[rt] *= c;
       m = tmax;
     }
+    // P^T as the B operand of one K=32 step: the order of keys inside a contraction is free, so
+    // lane group g's 8 entries are keys 4g .. 4g+3 (elements 0-3) and 16+4g .. 16+4g+3 (4-7),
+    // exactly what the S^T accumulators hold; the A operand takes the same key order from two
+    // transposed reads of the 16-key halves.
+    short4_t bp[2];
 #pragma unroll
-    for (int kt16 = 0; kt16 < 2; ++kt16) {
-      short4_t bp;
+    for (int kt16 = 0; kt16 < 2; ++kt16)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float pe = (sc[kt16][e] == kNegInf) ? 0.f : fast_exp2(sc[kt16][e] - m);
         l += pe;
-        bp[e] = static_cast<short>(f32_to_bf16(pe));
+        bp[kt16][e] = static_cast<short>(f32_to_bf16(pe));
       }
-      // A^T[r][row] += Z^V^T[r][keys 16 kt16 + 4 g + e] . P^T
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(bp[0], bp[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    // A^T[r][row] += Z^V^T[r][keys] . P^T
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        D[rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v_operand_tr<RV>(vt, 16 * kt16, 16 * rt, lane), bp,
-                                                          D[rt], 0, 0, 0);
+    for (int rt = 0; rt < RT; ++rt) {
+      const short4_t v0 = v_operand_tr<RV>(vt, 0, 16 * rt, lane);
+      const short4_t v1 = v_operand_tr<RV>(vt, 16, 16 * rt, lane);
+      D[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7)), pb, D[rt], 0, 0, 0);
     }
   }
   l += __shfl_xor(l, 16, 64);
