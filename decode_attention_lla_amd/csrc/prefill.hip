@@ -183,8 +183,28 @@ __global__ __launch_bounds__(256) void qproj_prefill_kernel(PrefillParams p, Pre
 // K/V tiles go through a kStages-deep LDS ring: tile i+kStages-1 is fetched while tile i is
 // computed, one barrier per tile. Every wave issues the same number of loads per tile (small tiles
 // repeat an instruction on two waves, writing identical bytes), so the vmcnt thresholds are
-// compile-time constants.
+// compile-time constants. Each stage is its own __shared__ object and the tile loop is unrolled
+// by the ring depth, so every LDS access names its stage statically: the compiler can then tell
+// the stage being read from the stages still being filled by global_load_lds, and does not add a
+// wait for all outstanding loads before each tile's first LDS read (it cannot prove that for
+// offsets into one array). The explicit vmcnt waits below are what orders the ring.
 constexpr int kStages = 4;
+
+template <int N>
+struct StageIdx {
+  static constexpr int value = N;
+};
+
+// Workgroup barrier of the ring: this wave's LDS reads have all returned, then every wave arrives.
+// Unlike __syncthreads() it does not wait for the global_load_lds transfers still in flight into
+// later stages (a workgroup-scope release fence counts them as pending LDS writes and waits for
+// all of them). The memory clobbers keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vm_tiles(int ahead) {
@@ -213,8 +233,20 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   static_assert(IK % 8 == 0 || 8 % IK == 0, "K tile instructions spread evenly over 8 waves");
   static_assert(IV % 8 == 0 || 8 % IV == 0, "V tile instructions spread evenly over 8 waves");
   static_assert(3 * (LK + LV) < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) char kbuf[kStages][KT_BYTES];
-  __shared__ __attribute__((aligned(16))) char vbuf[kStages][VT_BYTES];
+  // one __shared__ object per ring stage, always named statically (see StageIdx)
+  __shared__ __attribute__((aligned(16))) char kb0[KT_BYTES], kb1[KT_BYTES], kb2[KT_BYTES], kb3[KT_BYTES];
+  __shared__ __attribute__((aligned(16))) char vb0[VT_BYTES], vb1[VT_BYTES], vb2[VT_BYTES], vb3[VT_BYTES];
+  static_assert(kStages == 4, "four named stages");
+  auto kstage = [&](auto S) -> char* {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return kb0; else if constexpr (st == 1) return kb1;
+    else if constexpr (st == 2) return kb2; else return kb3;
+  };
+  auto vstage = [&](auto S) -> char* {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return vb0; else if constexpr (st == 1) return vb1;
+    else if constexpr (st == 2) return vb2; else return vb3;
+  };
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -271,8 +303,8 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     beta = part * p.scale_log2;
   }
 
-  // cooperative tile fetch into ring stage `st`; rows past kmax are clamped to kmax
-  auto issue = [&](int tile, int st) {
+  // cooperative tile fetch into ring stage (kd, vd); rows past kmax are clamped to kmax
+  auto issue = [&](int tile, char* kd, char* vd) {
     const int key0 = tile * kKeyTile;
 #pragma unroll
     for (int u = 0; u < LK; ++u) {
@@ -282,7 +314,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
       const int pc = f - row * CPK;
       const int lc = (pc & ~7) | ((pc & 7) ^ (row & 7));
       const char* src = zk + (static_cast<size_t>(min(key0 + row, kmax)) * RK + lc * 8) * 2;
-      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(&kbuf[st][i * 1024]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(kd + i * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < LV; ++u) {
@@ -292,7 +324,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
       const int pc = f - row * CPV;
       const int lc = (pc & ~7) | ((pc & 7) ^ vswz(row));
       const char* src = zv + (static_cast<size_t>(min(key0 + row, kmax)) * RV + lc * 8) * 2;
-      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(&vbuf[st][i * 1024]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(vd + i * 1024), 16, 0, 0);
     }
   };
 
@@ -302,20 +334,23 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   float m = kNegInf;
   float l = 0.f;
 
-#pragma unroll
-  for (int s0 = 0; s0 < kStages - 1; ++s0)
-    if (s0 < ntiles) issue(s0, s0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int st = tile % kStages;
-    // this wave's loads of `tile` have landed (later tiles may still be in flight) ...
-    wait_vm_tiles<LK + LV>(min(kStages - 2, ntiles - 1 - tile));
+  // Tile `tile` lives in stage tile % kStages. The ring runs without conditions: the prologue
+  // fetches three tiles, every step fetches tile + 3, and the loop runs whole groups of four steps
+  // (rows past kmax are clamped, so fetches past the last tile re-read valid latents, and the
+  // spare steps see only keys above every row's causal limit: their weights are 0). With no
+  // conditional transfers the compiler can follow which stage each outstanding load fills and
+  // adds no waits of its own; the explicit ones below keep exactly two tiles in flight.
+  auto step = [&](auto S, int tile) {
+    constexpr int st = decltype(S)::value;
+    // this wave's loads of `tile` have landed (tiles + 1 and + 2 may still be in flight) ...
+    wait_vm_tiles<LK + LV>(kStages - 2);
     // ... and every other wave's; everyone has also finished computing tile - 1, whose stage is
     // the one refilled next
-    __syncthreads();
-    if (tile + kStages - 1 < ntiles) issue(tile + kStages - 1, (tile + kStages - 1) % kStages);
-    __asm__ volatile("" ::: "memory");
-    const char* kt = kbuf[st];
-    const char* vt = vbuf[st];
+    ring_barrier();
+    issue(tile + kStages - 1, kstage(StageIdx<(st + kStages - 1) % kStages>{}),
+          vstage(StageIdx<(st + kStages - 1) % kStages>{}));
+    const char* kt = kstage(S);
+    const char* vt = vstage(S);
     const int key0 = tile * kKeyTile;
     float sc[2][4];
     float tmax = kNegInf;
@@ -371,6 +406,21 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
       D[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
           __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7)), pb, D[rt], 0, 0, 0);
     }
+  };
+  if (ntiles > 0) {
+    // the Q~ and beta loads land before any tile is requested, so the tile loop never has to
+    // wait for them
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    issue(0, kb0, vb0);
+    issue(1, kb1, vb1);
+    issue(2, kb2, vb2);
+    for (int tile = 0; tile < ntiles; tile += kStages) {
+      step(StageIdx<0>{}, tile);
+      step(StageIdx<1>{}, tile + 1);
+      step(StageIdx<2>{}, tile + 2);
+      step(StageIdx<3>{}, tile + 3);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // the spare fetches have landed before the wave ends
   }
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
