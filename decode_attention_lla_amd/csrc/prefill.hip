@@ -38,28 +38,30 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 
 constexpr float kLazyP = 8.0f;
 
-// XOR swizzle of the 16-byte chunks of V row `row` inside each aligned 8-chunk window. Every four
-// consecutive rows land on four distinct chunk pairs (the transposed read below touches one
-// adjacent pair in each of four consecutive rows per 16-lane group), and every eight consecutive
-// rows on eight distinct chunks.
-__device__ __forceinline__ int vswz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
-
-// A operand of v_mfma_f32_16x16x16bf16_1k holding Z^V^T[r0 + i][kb + k] (i, k < 16) from a
-// row-major [key][RV] bf16 tile whose 16-byte chunks are XOR-swizzled by vswz(key). One
-// ds_read_b64_tr_b16: in each 16-lane group q, source lane 4e + c points at the 8 bytes
-// V[kb + 4q + e][r0 + 4c .. +3]; the transposed read hands lane i of the group element e =
-// V[kb + 4q + e][r0 + i], which is the MFMA's A layout (row i, k = 4q + e). (Lane mapping of the
-// instruction checked on the hardware.)
 typedef __attribute__((address_space(3))) short4_t* lds_short4_ptr;
+
+// LDS layout of a V tile (kKeyTile keys x RV latent entries, bf16): 128-byte blocks of 4 keys x 16
+// entries, row-major inside the block (16-byte unit = 8 entries of one key, units ordered key,
+// half), blocks ordered key quad major. Byte offset of unit (key, 8-entry group r8):
+template <int RV>
+__device__ __forceinline__ int v_unit_offset(int key, int r8) {
+  constexpr int NRQ = RV / 16;  // entry blocks per key quad
+  return ((key >> 2) * NRQ + (r8 >> 1)) * 128 + ((key & 3) * 2 + (r8 & 1)) * 16;
+}
+
+// A operand of v_mfma_f32_16x16x16bf16_1k-style 4-key slices holding Z^V^T[r0 + i][kb + 4q + e]
+// (16-lane group q, lane i of the group, element e < 4), r0 a multiple of 16, kb a multiple of 4.
+// One ds_read_b64_tr_b16: source lane j = 4e + c of group q points at the 8 bytes
+// V[kb + 4q + e][r0 + 4c .. + 3]; the transposed read hands lane i element e = V[kb + 4q + e][r0 + i].
+// In the blocked layout the 16 source lanes of a group cover one whole 128-byte block in lane
+// order, and the four groups cover four blocks of consecutive key quads. (Lane mapping of the
+// instruction checked on the hardware.)
 template <int RV>
 __device__ __forceinline__ short4_t v_operand_tr(const char* vt, int kb, int r0, int lane) {
   const int q = lane >> 4;
   const int j = lane & 15;
-  const int row = kb + 4 * q + (j >> 2);
-  const int r = r0 + 4 * (j & 3);
-  const int lc = r >> 3;
-  const int pc = (lc & ~7) | ((lc & 7) ^ vswz(row));
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_ptr)(vt + row * RV * 2 + pc * 16 + (r & 7) * 2));
+  const char* blk = vt + v_unit_offset<RV>(kb + 4 * q, r0 >> 3);  // unit (key quad start, r0)
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_ptr)(blk + 8 * j));
 }
 
 constexpr int kRowsWG = 128;  // chunk rows per attention workgroup (8 waves x 16)
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   constexpr int KS = RK / 32;
   constexpr int RT = RV / 16;
   constexpr int CPK = RK / 8;                 // 16-byte chunks per K row
-  constexpr int CPV = RV / 8;                 // per V row
+  constexpr int NRQ = RV / 16;                // 16-entry blocks per key quad of a V tile
   constexpr int KT_BYTES = kKeyTile * RK * 2;
   constexpr int VT_BYTES = kKeyTile * RV * 2;
   constexpr int IK = KT_BYTES / 1024;         // 1 KiB global_load_lds instructions per K tile
@@ -283,24 +285,15 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   const char* zk = static_cast<const char*>(p.zk) + lat * RK * 2;
   const char* zv = static_cast<const char*>(p.zv) + lat * RV * 2;
 
-  // Q~ (hi, lo) of this lane's row as B-operand fragments, and beta = scale*log2e * q . mu^K_t
+  // Q~ (hi, lo) of this lane's row as B-operand fragments. The mu^K_t part of every score of the
+  // row, scale*log2e * q . mu^K_t, is one constant per row: softmax does not depend on it, and
+  // this path returns no log-sum-exp, so it is never formed here.
   const size_t rho = (static_cast<size_t>(b) * p.H + h) * p.C + (rvalid ? jr : 0);
   uint4 qh[KS], ql[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     qh[ks] = *reinterpret_cast<const uint4*>(w.qhi + rho * RK + 32 * ks + 8 * g);
     ql[ks] = *reinterpret_cast<const uint4*>(w.qlo + rho * RK + 32 * ks + 8 * g);
-  }
-  float beta = 0.f;
-  if (p.mu_k != nullptr) {
-    const size_t qoff = ((static_cast<size_t>(b) * p.C + (rvalid ? jr : 0)) * p.H + h) * p.d;
-    const size_t mo = mofs(p, h);
-    float part = 0.f;
-    for (int jd = g; jd < p.d; jd += 4)
-      part += ld<BF16>(p.q, qoff + jd) * ld<BF16>(p.mu_k, mo + jd);
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
-    beta = part * p.scale_log2;
   }
 
   // cooperative tile fetch into ring stage (kd, vd); rows past kmax are clamped to kmax
@@ -318,12 +311,15 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     }
 #pragma unroll
     for (int u = 0; u < LV; ++u) {
+      // LDS unit U = 64 i + lane of the blocked V layout; its source is (key, 8-entry group)
       const int i = IV >= 8 ? wave + 8 * u : wave % IV;
-      const int f = i * 64 + lane;
-      const int row = f / CPV;
-      const int pc = f - row * CPV;
-      const int lc = (pc & ~7) | ((pc & 7) ^ vswz(row));
-      const char* src = zv + (static_cast<size_t>(min(key0 + row, kmax)) * RV + lc * 8) * 2;
+      const int U = i * 64 + lane;
+      const int block = U >> 3;
+      const int kq = block / NRQ;
+      const int rq = block - kq * NRQ;
+      const int key = 4 * kq + ((U >> 1) & 3);
+      const int r8 = 2 * rq + (U & 1);
+      const char* src = zv + (static_cast<size_t>(min(key0 + key, kmax)) * RV + r8 * 8) * 2;
       __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(vd + i * 1024), 16, 0, 0);
     }
   };
@@ -331,8 +327,18 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   floatx4_t D[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) D[rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf;
+  // Running maximum m of this row's scores (q~ . z in log2 units), kept as the offset bm = -m that
+  // the score accumulators start from, so that they hold score - m directly. m starts at 0 and is
+  // re-based on the first tile that shows the row any latent, whatever that tile's maximum; after
+  // that only when the maximum grows by more than kLazyP. Until the first re-base every weight is
+  // exp2(-inf) = 0, so l and D are still exactly 0 and need no rescale then.
+  float bm = 0.f;
+  bool based = false;
   float l = 0.f;
+  // The wave's rows are j0 + 16 wave + (0 .. 15). When all of them are inside the chunk, the
+  // smallest causal limit is that of the first row, and a tile wholly at or below it needs no mask.
+  const int jw = j0 + wave * 16;
+  const int wave_lim = (jw + 15 < p.C) ? min(ctx + jw, p.n_max - 1) : -1;
 
   // Tile `tile` lives in stage tile % kStages. The ring runs without conditions: the prologue
   // fetches three tiles, every step fetches tile + 3, and the loop runs whole groups of four steps
@@ -354,11 +360,12 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     const int key0 = tile * kKeyTile;
     float sc[2][4];
     float tmax = kNegInf;
+    const bool masked = key0 + kKeyTile - 1 > wave_lim;  // wave-uniform
 #pragma unroll
     for (int kt16 = 0; kt16 < 2; ++kt16) {
-      // S^T[key 16*kt16 + i][row]: A = K rows (swizzled chunks), B = Q~^T fragments
+      // S^T[key 16*kt16 + i][row] - m: A = K rows (swizzled chunks), B = Q~^T fragments
       const int row = 16 * kt16 + col;
-      floatx4_t sh = {0.f, 0.f, 0.f, 0.f};
+      floatx4_t sh = {bm, bm, bm, bm};
       floatx4_t sl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -369,35 +376,46 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
         sl = mfma32(a, ql[ks], sl);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = key0 + 16 * kt16 + 4 * g + e;
-        sc[kt16][e] = key <= lim ? (sh[e] + sl[e]) + beta : kNegInf;
-        tmax = fmaxf(tmax, sc[kt16][e]);
+      for (int e = 0; e < 4; ++e) sc[kt16][e] = sh[e] + sl[e];
+      if (masked) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (key0 + 16 * kt16 + 4 * g + e > lim) sc[kt16][e] = kNegInf;
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sc[kt16][e]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    if (tmax > m + kLazyP) {
-      const float c = fast_exp2(m - tmax);
-      l *= c;
+    if (tmax > kLazyP || (!based && tmax > kNegInf)) {
+      if (based) {
+        const float c = fast_exp2(-tmax);
+        l *= c;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) D[rt] *= c;
-      m = tmax;
+        for (int rt = 0; rt < RT; ++rt) D[rt] *= c;
+      }
+      based = true;
+      bm -= tmax;
+#pragma unroll
+      for (int kt16 = 0; kt16 < 2; ++kt16)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[kt16][e] -= tmax;
     }
     // P^T as the B operand of one K=32 step: the order of keys inside a contraction is free, so
     // lane group g's 8 entries are keys 4g .. 4g+3 (elements 0-3) and 16+4g .. 16+4g+3 (4-7),
     // exactly what the S^T accumulators hold; the A operand takes the same key order from two
     // transposed reads of the 16-key halves.
-    short4_t bp[2];
+    float pe[2][4];
 #pragma unroll
     for (int kt16 = 0; kt16 < 2; ++kt16)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float pe = (sc[kt16][e] == kNegInf) ? 0.f : fast_exp2(sc[kt16][e] - m);
-        l += pe;
-        bp[kt16][e] = static_cast<short>(f32_to_bf16(pe));
+        pe[kt16][e] = fast_exp2(sc[kt16][e]);  // exp2(-inf) = 0 for masked keys
+        l += pe[kt16][e];
       }
-    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(bp[0], bp[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    const bf16x8_t pb = __builtin_bit_cast(
+        bf16x8_t, make_uint4(f32x2_to_bf16x2(pe[0][0], pe[0][1]), f32x2_to_bf16x2(pe[0][2], pe[0][3]),
+                             f32x2_to_bf16x2(pe[1][0], pe[1][1]), f32x2_to_bf16x2(pe[1][2], pe[1][3])));
     // A^T[r][row] += Z^V^T[r][keys] . P^T
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -408,7 +426,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     }
   };
   if (ntiles > 0) {
-    // the Q~ and beta loads land before any tile is requested, so the tile loop never has to
+    // the Q~ loads land before any tile is requested, so the tile loop never has to
     // wait for them
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     issue(0, kb0, vb0);
