@@ -262,6 +262,266 @@ hipError_t launch_encode_mfma(const EncodeParams& p, int nt_tiles, hipStream_t s
   return hipGetLastError();
 }
 
+// ---- LDS-tiled GEMM for large token counts -----------------------------------------------------
+// Z^T[token][r] = X[token][k] . E[r][k]^T as one dense product per head: a workgroup of 8 waves owns
+// 256 tokens x TN latent rows and walks k in steps of 32. The X tile (256 x 32) and the E tile
+// (TN x 32) of a step go straight from memory to LDS with global_load_lds into a 4-deep ring of
+// named stages (one __shared__ object each, so the compiler tells the stage being read from those
+// being filled). Tiles are stored as 64-byte rows whose 16-byte chunks are XOR-swizzled by
+// (row / 4) mod 4: the MFMA operand reads (ds_read_b128, 16 rows x one chunk per 16 lanes) then
+// touch every LDS bank once. Waves form a 4 x 2 grid of 64 x TN/2 tiles on
+// v_mfma_f32_32x32x16_bf16 (A[i][k] at lane i + 32 (k / 8), element k % 8; B[k][j] likewise;
+// C[i][j] at lane j + 32 ((i / 4) % 2), element 4 (i / 8) + i % 4). A 32-wide k chunk stays inside
+// one loop t when d is a multiple of 32, so each lane's 16 bytes are contiguous in x.
+constexpr int kGM = 256;     // tokens per workgroup
+constexpr int kGK = 32;      // k per stage
+constexpr int kGStages = 4;  // ring depth
+
+template <int N>
+struct GStage {
+  static constexpr int value = N;
+};
+
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+__device__ __forceinline__ floatx16_t mfma3232(uint4 a, uint4 b, floatx16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// workgroup barrier of the ring: this wave's LDS reads have returned, then all waves arrive. It
+// does not wait for the global_load_lds transfers in flight into other stages (a workgroup-scope
+// release fence, as in __syncthreads(), would count them as pending LDS writes).
+__device__ __forceinline__ void ring_barrier_g() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int gswz(int row, int c) { return c ^ ((row >> 2) & 3); }
+
+// 16-byte LDS DMA of each lane's bytes at base + voffset + soffset into lds + 16 * lane, through a
+// raw buffer descriptor (stride 0, 31-bit range, 32-bit data format word). The lane offset and the
+// wave-uniform offset stay separate operands, so the lane offset's register is never rewritten.
+__device__ __forceinline__ void buffer_lds16(const void* base, lptr_t lds, uint32_t voffset, uint32_t soffset) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voffset, soffset, 0, 0);
+}
+
+// An LDS offset the compiler must treat as unknown. Reads of a ring stage whose addresses it
+// derives from one another lose the information that tells that stage from the stages still
+// being filled, and the compiler then waits for every outstanding transfer before them.
+__device__ __forceinline__ int opaque(int v) {
+  __asm__ volatile("" : "+v"(v));
+  return v;
+}
+
+template <int TN>
+__global__ __launch_bounds__(512) void encode_gemm_kernel(EncodeParams p) {
+  constexpr int WN = TN / 2;           // latent rows per wave
+  constexpr int MT = 2;                // 32-token tiles per wave (64 tokens)
+  constexpr int NT = WN / 32;          // 32-row latent tiles per wave
+  constexpr int A_BYTES = kGM * kGK * 2;
+  constexpr int B_BYTES = TN * kGK * 2;
+  constexpr int IA = A_BYTES / 1024;   // 1 KiB load instructions per stage
+  constexpr int IB = B_BYTES / 1024;
+  static_assert(IA % 8 == 0 && (IB % 8 == 0 || IB == 8), "loads spread evenly over 8 waves");
+  constexpr int LA = IA / 8;
+  constexpr int LB = IB / 8;
+  constexpr int LPW = LA + LB;         // loads per wave and stage
+  static_assert(2 * LPW < 16, "vmcnt encoding below");
+  __shared__ __attribute__((aligned(16))) char a0[A_BYTES], a1[A_BYTES], a2[A_BYTES], a3[A_BYTES];
+  __shared__ __attribute__((aligned(16))) char b0[B_BYTES], b1[B_BYTES], b2[B_BYTES], b3[B_BYTES];
+  __shared__ float emu_s[TN];
+  __shared__ int2 tok_s[kGM];  // (sequence, cache slot) of each token row; slot -1: not written
+  auto astage = [&](auto S) -> char* {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return a0; else if constexpr (st == 1) return a1;
+    else if constexpr (st == 2) return a2; else return a3;
+  };
+  auto bstage = [&](auto S) -> char* {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return b0; else if constexpr (st == 1) return b1;
+    else if constexpr (st == 2) return b2; else return b3;
+  };
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wm = wave & 3;
+  const int wn = wave >> 2;
+  const int h = blockIdx.z;
+  const int r0 = blockIdx.y * TN;
+  const int n0 = blockIdx.x * kGM;
+  const int ntok = p.B * p.C;
+  const int K = p.T * p.d;
+  const int nst = K / kGK;  // stages, a multiple of kGStages
+  const uint16_t* x = static_cast<const uint16_t*>(p.x);
+  const uint16_t* E = static_cast<const uint16_t*>(p.E) + static_cast<size_t>(h) * p.r * K;
+
+  if (tid < kGM) {
+    const int n = n0 + tid;
+    int2 ts = make_int2(0, -1);
+    if (n < ntok) {
+      const int b = n / p.C;
+      const int slot = p.pos[b] + (n - b * p.C);
+      if (slot >= 0 && slot < p.n_max) ts = make_int2(b, slot);
+    }
+    tok_s[tid] = ts;
+  }
+  // E mu for this workgroup's latent rows (only with centering): 16-row groups on
+  // v_mfma_f32_16x16x32_bf16 with mu as row 0 of the A operand
+  if (p.mu != nullptr) {
+    const uint16_t* mu = static_cast<const uint16_t*>(p.mu) + static_cast<size_t>(h) * K;
+    const int col = lane & 15;
+    const int g = lane >> 4;
+    for (int grp = wave; grp < TN / 16; grp += 8) {
+      const int er = min(r0 + 16 * grp + col, p.r - 1);
+      const uint16_t* erow = E + static_cast<size_t>(er) * K;
+      floatx4_t am = {0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < K; k += 32) {
+        const uint4 a = col == 0 ? *reinterpret_cast<const uint4*>(mu + k + 8 * g) : make_uint4(0, 0, 0, 0);
+        const uint4 bb = *reinterpret_cast<const uint4*>(erow + k + 8 * g);
+        am = mfma(a, bb, am);
+      }
+      if (g == 0) emu_s[16 * grp + col] = am[0];  // row 0 of C: lane j, element 0
+    }
+  } else {
+    for (int i = tid; i < TN; i += 512) emu_s[i] = 0.f;
+  }
+  __syncthreads();
+
+  // Loads of stage `s` (k0 = s * kGK, clamped to the last stage for the spare fetches past the
+  // end). Each lane's byte offset inside the workgroup's X rows and E rows never changes; the step
+  // only moves the wave-uniform base. Keeping the per-lane offsets fixed keeps their registers from
+  // being rewritten while a transfer that reads them may still be in flight (the compiler would
+  // wait for every outstanding load before such a rewrite).
+  const char* xw = reinterpret_cast<const char*>(x) +
+                   (static_cast<size_t>(n0) * p.T * p.H + h) * p.d * 2;   // token n0, head h, k = 0
+  const char* ew = reinterpret_cast<const char*>(E) + static_cast<size_t>(r0) * K * 2;
+  uint32_t aoff[LA], boff[LB];
+#pragma unroll
+  for (int u = 0; u < LA; ++u) {
+    const int unit = (wave + 8 * u) * 64 + lane;
+    const int row = unit >> 2;
+    const int n = min(n0 + row, ntok - 1) - n0;  // rows past the last token re-read it
+    aoff[u] = (static_cast<uint32_t>(n) * p.T * p.H * p.d + 8 * gswz(row, unit & 3)) * 2;
+  }
+#pragma unroll
+  for (int u = 0; u < LB; ++u) {
+    const int i = IB >= 8 ? wave + 8 * u : wave % IB;
+    const int unit = i * 64 + lane;
+    const int row = unit >> 2;
+    const int er = min(r0 + row, p.r - 1) - r0;
+    boff[u] = (static_cast<uint32_t>(er) * K + 8 * gswz(row, unit & 3)) * 2;
+  }
+  // the lane offset goes in voffset and the step's k offset in soffset, so the address registers
+  // are never rewritten
+  auto issue = [&](int s, char* ad, char* bd) {
+    const int k0 = min(s, nst - 1) * kGK;
+    const int t = k0 / p.d;
+    const int j0 = k0 - t * p.d;
+    const int xso = (t * p.H * p.d + j0) * 2;
+    const int eso = k0 * 2;
+#pragma unroll
+    for (int u = 0; u < LA; ++u)
+      buffer_lds16(xw, (lptr_t)(ad + (wave + 8 * u) * 1024), aoff[u], xso);
+#pragma unroll
+    for (int u = 0; u < LB; ++u) {
+      const int i = IB >= 8 ? wave + 8 * u : wave % IB;
+      buffer_lds16(ew, (lptr_t)(bd + i * 1024), boff[u], eso);
+    }
+  };
+
+  floatx16_t acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mt][nt][e] = 0.f;
+
+  // one stage: wait for this wave's loads of stage s (two stages may stay in flight) and for the
+  // other waves, refill the stage computed last, then 2 k-steps of MT x NT MFMAs
+  auto step = [&](auto S, int s) {
+    constexpr int st = decltype(S)::value;
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * LPW));  // vmcnt(2 * LPW)
+    ring_barrier_g();
+    issue(s + 3, astage(GStage<(st + 3) % kGStages>{}), bstage(GStage<(st + 3) % kGStages>{}));
+    const char* at = astage(S);
+    const char* bt = bstage(S);
+#pragma unroll
+    for (int ks = 0; ks < kGK / 16; ++ks) {
+      const int c = 2 * ks + (lane >> 5);
+      uint4 av[MT], bv[NT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = 64 * wm + 32 * mt + (lane & 31);
+        av[mt] = *reinterpret_cast<const uint4*>(at + opaque(row * 64 + gswz(row, c) * 16));
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int row = WN * wn + 32 * nt + (lane & 31);
+        bv[nt] = *reinterpret_cast<const uint4*>(bt + opaque(row * 64 + gswz(row, c) * 16));
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma3232(av[mt], bv[nt], acc[mt][nt]);
+    }
+  };
+
+  issue(0, a0, b0);
+  issue(1, a1, b1);
+  issue(2, a2, b2);
+  for (int s = 0; s < nst; s += kGStages) {
+    step(GStage<0>{}, s);
+    step(GStage<1>{}, s + 1);
+    step(GStage<2>{}, s + 2);
+    step(GStage<3>{}, s + 3);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // the spare fetches have landed before the wave ends
+
+  // C layout: lane (j + 32 hh) element e holds token row 8 (e / 4) + 4 hh + e % 4, latent row j
+  const int hh = lane >> 5;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int2 ts = tok_s[64 * wm + 32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3)];
+      if (ts.y < 0) continue;
+      uint16_t* z = static_cast<uint16_t*>(p.z) + ((static_cast<size_t>(ts.x) * p.H + h) * p.n_max + ts.y) * p.r;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int rl = WN * wn + 32 * nt + (lane & 31);
+        if (r0 + rl < p.r) z[r0 + rl] = f32_to_bf16(acc[mt][nt][e] - emu_s[rl]);
+      }
+    }
+}
+
+template <int TN>
+hipError_t launch_encode_gemm(const EncodeParams& p, hipStream_t stream) {
+  const unsigned ntok = static_cast<unsigned>(p.B) * p.C;
+  dim3 grid((ntok + kGM - 1) / kGM, (p.r + TN - 1) / TN, p.H);
+  hipLaunchKernelGGL(encode_gemm_kernel<TN>, grid, dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+// the tiled GEMM applies when a 32-wide k chunk stays inside one loop, the k extent is whole
+// groups of four stages, the latent rank fills 128-row tiles and there are enough tokens
+bool encode_gemm_ok(const EncodeParams& p) {
+  const long ntok = static_cast<long>(p.B) * p.C;
+  // byte offsets inside a workgroup's rows must fit the 31-bit buffer range
+  const long stack = static_cast<long>(p.T) * p.H * p.d * 2;
+  const long xspan = kGM * stack;
+  const long espan = 256L * p.T * p.d * 2;
+  return p.d % kGK == 0 && (p.T * p.d) % (kGK * kGStages) == 0 && p.r % 128 == 0 && ntok >= kGM &&
+         xspan < 0x7fffffffL && espan < 0x7fffffffL;
+}
+
 }  // namespace
 
 bool encode_supported(int dtype, int r) {
@@ -271,6 +531,8 @@ bool encode_supported(int dtype, int r) {
 hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t stream) {
   const int K = p.T * p.d;
   if (dtype == LLA_BF16) {
+    if (encode_gemm_ok(p))
+      return p.r % 256 == 0 ? launch_encode_gemm<256>(p, stream) : launch_encode_gemm<128>(p, stream);
     const int nt_tiles = p.r <= 16 ? 1 : p.r <= 32 ? 2 : 4;
     const long ntok = static_cast<long>(p.B) * p.C;
     const long wgs1 = (ntok + 127) / 128 * ((p.r + 16 * nt_tiles - 1) / (16 * nt_tiles)) * p.H;

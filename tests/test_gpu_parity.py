@@ -373,12 +373,16 @@ def test_decode_2d_mfma(rk, rv):
 @pytest.mark.parametrize("variant,H,d,T,r,B,C", [
     ("per_head", 16, 128, 4, 32, 8, 160),     # 1280 tokens: K split over the 4 waves
     ("per_head", 16, 128, 4, 32, 16, 512),    # 8192 tokens: whole-K waves
-    ("2d", 16, 128, 4, 256, 2, 512),          # a 2D prefill chunk's encode
+    ("2d", 16, 128, 4, 256, 2, 512),          # a 2D prefill chunk's encode (tiled GEMM)
+    ("per_head", 16, 128, 4, 128, 3, 300),    # tiled GEMM, 128-row latent tiles, ragged tokens
+    ("per_head", 8, 64, 4, 256, 2, 257),      # tiled GEMM, one token past a 256-token tile
+    ("2d", 8, 64, 4, 512, 1, 700),            # tiled GEMM, two 256-row latent tiles
 ])
 def test_encode_large_token_counts(variant, H, d, T, r, B, C):
     dtype = "bf16"
     n_max = C + 7
-    pos = np.array([7] * B, np.int32)
+    # the last sequence starts 5 slots later: its last 5 tokens fall past n_max and are not written
+    pos = np.array([7] * (B - 1) + [12], np.int32)
     K = T * d if variant == "per_head" else T * H * d
     es = (H, r, K) if variant == "per_head" else (r, K)
     ms = (H, K) if variant == "per_head" else (K,)
@@ -395,7 +399,13 @@ def test_encode_large_token_counts(variant, H, d, T, r, B, C):
                    dev(mk, dtype), None, dev(pos), zk, zv)
     torch.cuda.synchronize()
     z0 = np.zeros(zs)
-    rk_, rv_ = O.encode_into_cache(z0, z0, xk, xv, Ek, Ev, pos, mk, None, variant)
+    # the oracle writes only the in-range slots, like the kernel
+    rk_, rv_ = z0.copy(), z0.copy()
+    for b in range(B):
+        keep = min(C, n_max - int(pos[b]))
+        sub = slice(b, b + 1)
+        rk_[sub], rv_[sub] = O.encode_into_cache(z0[sub], z0[sub], xk[sub, :keep], xv[sub, :keep], Ek, Ev,
+                                                 pos[sub], mk, None, variant)
     assert_close(host(zk), rk_, dtype, f"encode zk {variant} B={B} C={C}")
     assert_close(host(zv), rv_, dtype, f"encode zv {variant} B={B} C={C}")
 
