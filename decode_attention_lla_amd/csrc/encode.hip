@@ -303,14 +303,6 @@ __device__ __forceinline__ void ring_barrier_g() {
 
 __device__ __forceinline__ int gswz(int row, int c) { return c ^ ((row >> 2) & 3); }
 
-// 16-byte LDS DMA of each lane's bytes at base + voffset + soffset into lds + 16 * lane, through a
-// raw buffer descriptor (stride 0, 31-bit range, 32-bit data format word). The lane offset and the
-// wave-uniform offset stay separate operands, so the lane offset's register is never rewritten.
-__device__ __forceinline__ void buffer_lds16(const void* base, lptr_t lds, uint32_t voffset, uint32_t soffset) {
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voffset, soffset, 0, 0);
-}
-
 // An LDS offset the compiler must treat as unknown. Reads of a ring stage whose addresses it
 // derives from one another lose the information that tells that stage from the stages still
 // being filled, and the compiler then waits for every outstanding transfer before them.
@@ -428,11 +420,11 @@ __global__ __launch_bounds__(512) void encode_gemm_kernel(EncodeParams p) {
     const int eso = k0 * 2;
 #pragma unroll
     for (int u = 0; u < LA; ++u)
-      buffer_lds16(xw, (lptr_t)(ad + (wave + 8 * u) * 1024), aoff[u], xso);
+      buffer_lds16(xw, 0x7fffffff, (lptr_t)(ad + (wave + 8 * u) * 1024), aoff[u], xso);
 #pragma unroll
     for (int u = 0; u < LB; ++u) {
       const int i = IB >= 8 ? wave + 8 * u : wave % IB;
-      buffer_lds16(ew, (lptr_t)(bd + i * 1024), boff[u], eso);
+      buffer_lds16(ew, 0x7fffffff, (lptr_t)(bd + i * 1024), boff[u], eso);
     }
   };
 

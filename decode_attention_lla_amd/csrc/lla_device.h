@@ -22,6 +22,16 @@ constexpr float kNegInf = -__builtin_huge_valf();
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// 16-byte LDS DMA of each lane's bytes at base + voffset + soffset into lds + 16 * lane, through a
+// raw buffer descriptor of `bytes` bytes (stride 0, 32-bit data format word). A lane whose offset
+// falls past `bytes` gets zeros. The lane offset and the wave-uniform offset stay separate
+// operands, so the lane offset's register is never rewritten while a transfer may read it.
+__device__ __forceinline__ void buffer_lds16(const void* base, int bytes, __attribute__((address_space(3))) void* lds,
+                                             uint32_t voffset, uint32_t soffset) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voffset, soffset, 0, 0);
+}
+
 // float32 -> bf16 bits, round to nearest, ties to even; NaN stays NaN (gfx950's v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));

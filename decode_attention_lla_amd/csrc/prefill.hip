@@ -296,31 +296,45 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     ql[ks] = *reinterpret_cast<const uint4*>(w.qlo + rho * RK + 32 * ks + 8 * g);
   }
 
-  // cooperative tile fetch into ring stage (kd, vd); rows past kmax are clamped to kmax
+  // Cooperative tile fetch into ring stage (kd, vd) as buffer loads over this sequence's latents
+  // 0 .. kmax: each lane's byte offset inside a tile is fixed, the tile's position moves in the
+  // wave-uniform offset, and latents past kmax (the tail of the last tile, the spare fetches past
+  // the end) land as zeros. Keys past a row's limit are masked, so those zeros are never weighed.
+  const int kbytes = (kmax + 1) * RK * 2;
+  const int vbytes = (kmax + 1) * RV * 2;
+  uint32_t koff[LK], voff[LV];
+#pragma unroll
+  for (int u = 0; u < LK; ++u) {
+    const int i = IK >= 8 ? wave + 8 * u : wave % IK;
+    const int f = i * 64 + lane;
+    const int row = f / CPK;
+    const int pc = f - row * CPK;
+    const int lc = (pc & ~7) | ((pc & 7) ^ (row & 7));
+    koff[u] = (row * RK + lc * 8) * 2;
+  }
+#pragma unroll
+  for (int u = 0; u < LV; ++u) {
+    // LDS unit U = 64 i + lane of the blocked V layout; its source is (key, 8-entry group)
+    const int i = IV >= 8 ? wave + 8 * u : wave % IV;
+    const int U = i * 64 + lane;
+    const int block = U >> 3;
+    const int kq = block / NRQ;
+    const int rq = block - kq * NRQ;
+    const int key = 4 * kq + ((U >> 1) & 3);
+    const int r8 = 2 * rq + (U & 1);
+    voff[u] = (key * RV + r8 * 8) * 2;
+  }
   auto issue = [&](int tile, char* kd, char* vd) {
-    const int key0 = tile * kKeyTile;
+    const uint32_t key0 = tile * kKeyTile;
 #pragma unroll
     for (int u = 0; u < LK; ++u) {
       const int i = IK >= 8 ? wave + 8 * u : wave % IK;
-      const int f = i * 64 + lane;
-      const int row = f / CPK;
-      const int pc = f - row * CPK;
-      const int lc = (pc & ~7) | ((pc & 7) ^ (row & 7));
-      const char* src = zk + (static_cast<size_t>(min(key0 + row, kmax)) * RK + lc * 8) * 2;
-      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(kd + i * 1024), 16, 0, 0);
+      buffer_lds16(zk, kbytes, (lptr_t)(kd + i * 1024), koff[u], key0 * RK * 2);
     }
 #pragma unroll
     for (int u = 0; u < LV; ++u) {
-      // LDS unit U = 64 i + lane of the blocked V layout; its source is (key, 8-entry group)
       const int i = IV >= 8 ? wave + 8 * u : wave % IV;
-      const int U = i * 64 + lane;
-      const int block = U >> 3;
-      const int kq = block / NRQ;
-      const int rq = block - kq * NRQ;
-      const int key = 4 * kq + ((U >> 1) & 3);
-      const int r8 = 2 * rq + (U & 1);
-      const char* src = zv + (static_cast<size_t>(min(key0 + key, kmax)) * RV + r8 * 8) * 2;
-      __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(vd + i * 1024), 16, 0, 0);
+      buffer_lds16(zv, vbytes, (lptr_t)(vd + i * 1024), voff[u], key0 * RV * 2);
     }
   };
 
@@ -542,8 +556,10 @@ const EntryP* findP(int r_k, int r_v) {
   return nullptr;
 }
 
-bool mfma_prefill(int dtype, int r_k, int r_v, int d_head) {
-  return dtype == LLA_BF16 && d_head % 32 == 0 && findP(r_k, r_v) != nullptr;
+// The MFMA path fetches a sequence's latents through buffer descriptors with a 31-bit byte range.
+bool mfma_prefill(int dtype, int r_k, int r_v, int d_head, int n_max) {
+  return dtype == LLA_BF16 && d_head % 32 == 0 && findP(r_k, r_v) != nullptr &&
+         static_cast<long>(n_max) * (r_k > r_v ? r_k : r_v) * 2 < 0x7fffffffL;
 }
 
 }  // namespace
@@ -553,7 +569,7 @@ bool prefill_supported(int variant, int dtype, int r_k, int r_v) {
 }
 
 void prefill_plan(const lla_desc& desc, int B, int C, int* splits, int* chunk) {
-  if (mfma_prefill(desc.dtype, desc.r_k, desc.r_v, desc.d_head)) {
+  if (mfma_prefill(desc.dtype, desc.r_k, desc.r_v, desc.d_head, desc.n_max)) {
     *splits = 1;
     *chunk = desc.n_max;
     return;
@@ -562,7 +578,7 @@ void prefill_plan(const lla_desc& desc, int B, int C, int* splits, int* chunk) {
 }
 
 size_t prefill_workspace_bytes(const lla_desc& desc, int B, int C) {
-  if (mfma_prefill(desc.dtype, desc.r_k, desc.r_v, desc.d_head))
+  if (mfma_prefill(desc.dtype, desc.r_k, desc.r_v, desc.d_head, desc.n_max))
     return prefill_mfma_bytes(B, C, desc.H, desc.d_head, desc.r_k, desc.r_v);
   int s, c;
   prefill_plan(desc, B, C, &s, &c);
@@ -570,7 +586,7 @@ size_t prefill_workspace_bytes(const lla_desc& desc, int B, int C) {
 }
 
 hipError_t launch_prefill(const PrefillParams& pp, int dtype, hipStream_t stream) {
-  if (mfma_prefill(dtype, pp.r_k, pp.r_v, pp.d)) {
+  if (mfma_prefill(dtype, pp.r_k, pp.r_v, pp.d, pp.n_max)) {
     const EntryP* e = findP(pp.r_k, pp.r_v);
     if (prefill_mfma_bytes(pp.B, pp.C, pp.H, pp.d, pp.r_k, pp.r_v) > pp.ws_bytes)
       return hipErrorInvalidValue;  // the plan does not fit the workspace: never launch
