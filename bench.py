@@ -34,7 +34,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "LLA decode-attn tokens/s + latent HBM GB/s (% of peak), bf16, 4k ctx, 1 GPU"
-DECODE_SRC = os.path.join(ROOT, "decode_attention_lla_amd", "csrc", "decode.hip")
+# the sources the per-head decode kernel is compiled from (the measured traffic is valid for them)
+DECODE_SRC = [os.path.join(ROOT, "decode_attention_lla_amd", "csrc", f)
+              for f in ("decode.hip", "lla_device.h", "lla_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_capacity_traffic.txt")
 
 
@@ -57,8 +59,11 @@ def parse():
     return ap.parse_args()
 
 
-def source_sha(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_sha(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic():
