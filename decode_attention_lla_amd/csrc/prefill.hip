@@ -8,19 +8,18 @@
 // q~ = W^K_t^T q (plus q . mu^K_t), softmax, latent-space sum of z^V, one W^V_t projection.
 //
 // MFMA path (bf16 storage, r_k and r_v in {64, 128, 256}, d_head a multiple of 32): a chunk of C
-// rows against N_ctx + C latents is a dense contraction, so it runs as four kernels:
-//   P0 transpose W^K_t[h] to [r_k][d] so the projection's B operand is contiguous;
-//   P1 Q~ = scale*log2(e) * Q . W^K_t[h] on v_mfma_f32_16x16x32_bf16, stored as bf16 hi + lo;
-//   P2 causal flash attention over the latents: a workgroup of 8 waves owns 128 consecutive chunk
-//      rows of one head; each wave keeps its 16 rows of Q~ (hi and lo) in registers; 32-latent K
-//      and V tiles are fetched with global_load_lds into XOR-swizzled, double-buffered LDS and
-//      shared by the 8 waves; S^T = Z^K . Q~^T, online softmax per row with a causal mask, then
-//      A^T += Z^V^T . P^T on v_mfma_f32_16x16x32_bf16 with P taken straight from the S^T
-//      accumulators (two 16-key halves form one K=32 step) and Z^V^T read with the transposing
-//      ds_read_b64_tr_b16; the normalised latent sums are stored as bf16 hi + lo;
-//   P3 O = A . W^V_t[h]^T (+ mu^V_t when the row saw any latent) on MFMA, both A parts.
-// Rows are numbered rho = (b*H + h)*C + j. LLA-2D and per-head differ only in which latent
-// sequence a head reads (b, or (b, h)) and in the factor and mu offsets.
+// rows against N_ctx + C latents is a dense contraction, so it runs as two kernels:
+//   P0 transpose W^K_t[h] to [r_k][d] so the q~ projection reads 16-byte runs of d;
+//   P1 causal flash attention over the latents: a workgroup of 8 waves owns 128 consecutive chunk
+//      rows of one head; each wave first forms Q~ = scale*log2(e) * Q . W^K_t[h] of its 16 rows on
+//      MFMA (kept as bf16 hi + lo in registers); 32-latent K and V tiles are fetched with buffer
+//      LDS-DMA loads into a 4-deep ring of named LDS stages shared by the 8 waves; S^T = Z^K . Q~^T,
+//      online softmax per row with a causal mask, then A^T += Z^V^T . P^T on
+//      v_mfma_f32_16x16x32_bf16 with P taken straight from the S^T accumulators (two 16-key halves
+//      form one K=32 step) and Z^V^T read with the transposing ds_read_b64_tr_b16; finally
+//      O = A . W^V_t[h]^T (+ mu^V_t when the row saw any latent) on MFMA from the accumulators.
+// LLA-2D and per-head differ only in which latent sequence a head reads (b, or (b, h)) and in the
+// factor and mu offsets.
 //
 // Streaming path (everything else): every (row, head) is one query row of the absorbed split-K
 // decode kernels, with its own causal key count.
@@ -76,35 +75,19 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace segments of the MFMA path.
 struct PrefillWs {
-  uint16_t* wkt;   // [H][RK][d]
-  uint16_t* qhi;   // [R][RK]
-  uint16_t* qlo;
-  uint16_t* ahi;   // [R][RV]
-  uint16_t* alo;
-  float* wrow;     // [R]: 1 if the row attended any latent
+  uint16_t* wkt;   // [H][RK][d]: W^K_t[h] transposed, so the q~ projection reads 16-byte runs of d
 };
 
 size_t prefill_mfma_bytes(int B, int C, int H, int d, int rk, int rv) {
-  const size_t R = static_cast<size_t>(B) * H * C;
-  return align256(static_cast<size_t>(H) * rk * d * 2) + 2 * align256(R * rk * 2) +
-         2 * align256(R * rv * 2) + align256(R * 4);
+  (void)B;
+  (void)C;
+  (void)rv;
+  return align256(static_cast<size_t>(H) * rk * d * 2);
 }
 
-PrefillWs carve(void* ws, int B, int C, int H, int d, int rk, int rv) {
-  const size_t R = static_cast<size_t>(B) * H * C;
-  char* p = static_cast<char*>(ws);
+PrefillWs carve(void* ws) {
   PrefillWs w;
-  w.wkt = reinterpret_cast<uint16_t*>(p);
-  p += align256(static_cast<size_t>(H) * rk * d * 2);
-  w.qhi = reinterpret_cast<uint16_t*>(p);
-  p += align256(R * rk * 2);
-  w.qlo = reinterpret_cast<uint16_t*>(p);
-  p += align256(R * rk * 2);
-  w.ahi = reinterpret_cast<uint16_t*>(p);
-  p += align256(R * rv * 2);
-  w.alo = reinterpret_cast<uint16_t*>(p);
-  p += align256(R * rv * 2);
-  w.wrow = reinterpret_cast<float*>(p);
+  w.wkt = static_cast<uint16_t*>(ws);
   return w;
 }
 
@@ -128,52 +111,6 @@ __global__ __launch_bounds__(256) void wk_transpose_kernel(PrefillParams p, uint
     const int j = i / RK;
     const int k = i - j * RK;
     dst[static_cast<size_t>(k) * p.d + j] = src[i];
-  }
-}
-
-// ---- P1: Q~ = scale*log2e * q . W^K_t[h] -> bf16 hi + lo ------------------------------------
-// grid (ceil(B*C / 64), RK / 64, H); each of the 4 waves owns 16 chunk rows x 64 columns.
-template <int RK>
-__global__ __launch_bounds__(256) void qproj_prefill_kernel(PrefillParams p, PrefillWs w) {
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int col = lane & 15;
-  const int g = lane >> 4;
-  const int h = blockIdx.z;
-  const int k0 = blockIdx.y * 64;
-  const int n0 = blockIdx.x * 64 + wave * 16;  // flattened (b, j)
-  const int ntok = p.B * p.C;
-  const int n = n0 + col;
-  const bool nok = n < ntok;
-  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (static_cast<size_t>(nok ? n : 0) * p.H + h) * p.d;
-  const uint16_t* wt = w.wkt + static_cast<size_t>(h) * RK * p.d;
-  floatx4_t acc[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < p.d; j0 += 32) {
-    const uint4 a = nok ? *reinterpret_cast<const uint4*>(qrow + j0 + 8 * g) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const uint4 b = *reinterpret_cast<const uint4*>(wt + static_cast<size_t>(k0 + 16 * nt + col) * p.d + j0 + 8 * g);
-      acc[nt] = mfma32(a, b, acc[nt]);
-    }
-  }
-  // C layout: lane holds column k0 + 16 nt + col for rows n0 + 4 g + e
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int nn = n0 + 4 * g + e;
-    if (nn >= ntok) continue;
-    const int b = nn / p.C;
-    const int j = nn - b * p.C;
-    const size_t rho = (static_cast<size_t>(b) * p.H + h) * p.C + j;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const float v = acc[nt][e] * p.scale_log2;
-      const uint16_t hi = f32_to_bf16(v);
-      w.qhi[rho * RK + k0 + 16 * nt + col] = hi;
-      w.qlo[rho * RK + k0 + 16 * nt + col] = f32_to_bf16(v - __uint_as_float(static_cast<uint32_t>(hi) << 16));
-    }
   }
 }
 
@@ -285,15 +222,45 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   const char* zk = static_cast<const char*>(p.zk) + lat * RK * 2;
   const char* zv = static_cast<const char*>(p.zv) + lat * RV * 2;
 
-  // Q~ (hi, lo) of this lane's row as B-operand fragments. The mu^K_t part of every score of the
-  // row, scale*log2e * q . mu^K_t, is one constant per row: softmax does not depend on it, and
-  // this path returns no log-sum-exp, so it is never formed here.
-  const size_t rho = (static_cast<size_t>(b) * p.H + h) * p.C + (rvalid ? jr : 0);
+  // Q~ = scale*log2e * W^K_t[h]^T q of this wave's 16 rows, formed here on MFMA as
+  // Q~^T[k][row] = W^K_t^T . Q^T over d. For each 32-wide k chunk ks two 16x16 accumulator tiles
+  // take the k-values 32 ks + 8 m + (0..3) and 32 ks + 8 m + 4 + (0..3) as their rows 4 m + (0..3);
+  // lane (row + 16 g) then holds elements g of both, k = 32 ks + 8 g + (0..7): exactly the B-operand
+  // fragment of the score product. Rows of the transposed W^K are picked in that order. q~ is kept
+  // as bf16 hi + lo (two MFMA chains), so scores keep float32 accuracy. The mu^K_t part of every
+  // score of a row, scale*log2e * q . mu^K_t, is one constant per row: softmax does not depend on
+  // it and this path returns no log-sum-exp, so it is never formed.
+  const size_t tok = static_cast<size_t>(b) * p.C + (rvalid ? jr : 0);  // (b, chunk row) of this lane
   uint4 qh[KS], ql[KS];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (tok * p.H + h) * p.d;
+    const uint16_t* wkt = w.wkt + static_cast<size_t>(h) * RK * p.d;
+    for (int ks = 0; ks < KS; ++ks) {
+      floatx4_t c0 = {0.f, 0.f, 0.f, 0.f};
+      floatx4_t c1 = {0.f, 0.f, 0.f, 0.f};
+      const int k0 = 32 * ks + 8 * (col >> 2) + (col & 3);  // tile row col of the first tile
+      for (int dd = 0; dd < p.d; dd += 32) {
+        const uint4 bq = *reinterpret_cast<const uint4*>(qrow + dd + 8 * g);
+        const uint4 a0 = *reinterpret_cast<const uint4*>(wkt + static_cast<size_t>(k0) * p.d + dd + 8 * g);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(wkt + static_cast<size_t>(k0 + 4) * p.d + dd + 8 * g);
+        c0 = mfma32(a0, bq, c0);
+        c1 = mfma32(a1, bq, c1);
+      }
+      float v[8];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qh[ks] = *reinterpret_cast<const uint4*>(w.qhi + rho * RK + 32 * ks + 8 * g);
-    ql[ks] = *reinterpret_cast<const uint4*>(w.qlo + rho * RK + 32 * ks + 8 * g);
+      for (int e = 0; e < 4; ++e) {
+        v[e] = c0[e] * p.scale_log2;
+        v[4 + e] = c1[e] * p.scale_log2;
+      }
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        hw[e2] = f32x2_to_bf16x2(v[2 * e2], v[2 * e2 + 1]);
+        lw[e2] = f32x2_to_bf16x2(v[2 * e2] - bf16_lo(hw[e2]), v[2 * e2 + 1] - bf16_hi(hw[e2]));
+      }
+      qh[ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      ql[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
   }
 
   // Cooperative tile fetch into ring stage (kd, vd) as buffer loads over this sequence's latents
@@ -456,94 +423,70 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   }
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (!rvalid) return;
+  // O = A . W^V_t[h]^T (+ mu^V_t when the row saw any latent), A = D / l, on MFMA as
+  // O^T[j][row] = W^V . A^T. The B operand of each 32-wide r chunk comes straight from the
+  // accumulators: lane (row + 16 g) holds r = 16 rt + 4 g + (0..3), so elements 0-3 take chunk half
+  // rt = 2 ks and elements 4-7 rt = 2 ks + 1 (the order of r inside a contraction is free); the
+  // A operand, rows j of W^V_t[h], is read in the same order as two 8-byte pieces. A is split into
+  // bf16 hi + lo parts, like q~.
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  // lane holds row jr, latent entries r = 16 rt + 4 g + e
+  uint4 ahv[RT / 2], alv[RT / 2];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    uint16_t hi[4], lo[4];
+  for (int ks = 0; ks < RT / 2; ++ks) {
+    float v[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float v = D[rt][e] * inv;
-      hi[e] = f32_to_bf16(v);
-      lo[e] = f32_to_bf16(v - __uint_as_float(static_cast<uint32_t>(hi[e]) << 16));
+      v[e] = D[2 * ks][e] * inv;
+      v[4 + e] = D[2 * ks + 1][e] * inv;
     }
-    const size_t o = rho * RV + 16 * rt + 4 * g;
-    *reinterpret_cast<uint2*>(w.ahi + o) = make_uint2(hi[0] | (static_cast<uint32_t>(hi[1]) << 16),
-                                                      hi[2] | (static_cast<uint32_t>(hi[3]) << 16));
-    *reinterpret_cast<uint2*>(w.alo + o) = make_uint2(lo[0] | (static_cast<uint32_t>(lo[1]) << 16),
-                                                      lo[2] | (static_cast<uint32_t>(lo[3]) << 16));
-  }
-  if (g == 0) w.wrow[rho] = l > 0.f ? 1.f : 0.f;
-}
-
-// ---- P3: O = A . W^V_t[h]^T (+ mu^V_t) ---------------------------------------------------------
-// grid (ceil(B*C / 64), ceil(d / 64), H); each of the 4 waves owns 16 rows x 64 output channels.
-template <int RV>
-__global__ __launch_bounds__(256) void oproj_prefill_kernel(PrefillParams p, PrefillWs w) {
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int col = lane & 15;
-  const int g = lane >> 4;
-  const int h = blockIdx.z;
-  const int c0 = blockIdx.y * 64;
-  const int n0 = blockIdx.x * 64 + wave * 16;
-  const int ntok = p.B * p.C;
-  const int n = n0 + col;
-  const bool nok = n < ntok;
-  size_t rho_a = 0;
-  if (nok) {
-    const int b = n / p.C;
-    rho_a = (static_cast<size_t>(b) * p.H + h) * p.C + (n - b * p.C);
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      hw[e2] = f32x2_to_bf16x2(v[2 * e2], v[2 * e2 + 1]);
+      lw[e2] = f32x2_to_bf16x2(v[2 * e2] - bf16_lo(hw[e2]), v[2 * e2 + 1] - bf16_hi(hw[e2]));
+    }
+    ahv[ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    alv[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
   const uint16_t* wv = static_cast<const uint16_t*>(p.Wv) + wofs(p, h, RV);
-  floatx4_t acc[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  for (int r0 = 0; r0 < RV; r0 += 32) {
-    const uint4 ah = nok ? *reinterpret_cast<const uint4*>(w.ahi + rho_a * RV + r0 + 8 * g) : make_uint4(0, 0, 0, 0);
-    const uint4 al = nok ? *reinterpret_cast<const uint4*>(w.alo + rho_a * RV + r0 + 8 * g) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int jd = c0 + 16 * nt + col;
-      const uint4 bw = jd < p.d ? *reinterpret_cast<const uint4*>(wv + static_cast<size_t>(jd) * RV + r0 + 8 * g)
-                                : make_uint4(0, 0, 0, 0);
-      acc[nt] = mfma32(ah, bw, acc[nt]);
-      acc[nt] = mfma32(al, bw, acc[nt]);
-    }
-  }
+  const float wr = l > 0.f ? 1.f : 0.f;
   const size_t mo = mofs(p, h);
+  uint16_t* orow = static_cast<uint16_t*>(p.out) + (tok * p.H + h) * p.d;
+  for (int j0 = 0; j0 < p.d; j0 += 16) {
+    // A operand rows: output channel j0 + col
+    const uint16_t* wrow_j = wv + static_cast<size_t>(j0 + col) * RV + 4 * g;
+    floatx4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int nn = n0 + 4 * g + e;
-    if (nn >= ntok) continue;
-    const int b = nn / p.C;
-    const int j = nn - b * p.C;
-    const float wr = w.wrow[(static_cast<size_t>(b) * p.H + h) * p.C + j];
+    for (int ks = 0; ks < RT / 2; ++ks) {
+      const uint2 p0 = *reinterpret_cast<const uint2*>(wrow_j + 32 * ks);
+      const uint2 p1 = *reinterpret_cast<const uint2*>(wrow_j + 32 * ks + 16);
+      const uint4 aw = make_uint4(p0.x, p0.y, p1.x, p1.y);
+      o = mfma32(aw, ahv[ks], o);
+      o = mfma32(aw, alv[ks], o);
+    }
+    // C layout: lane (row + 16 g) holds channels j0 + 4 g + (0..3) of its row
+    if (rvalid) {
+      float r4[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int jd = c0 + 16 * nt + col;
-      if (jd >= p.d) continue;
-      float o = acc[nt][e];
-      if (p.mu_v != nullptr) o += wr * ld<BF16>(p.mu_v, mo + jd);
-      st<BF16>(p.out, (static_cast<size_t>(nn) * p.H + h) * p.d + jd, o);
+      for (int e = 0; e < 4; ++e) {
+        r4[e] = o[e];
+        if (p.mu_v != nullptr) r4[e] += wr * ld<BF16>(p.mu_v, mo + j0 + 4 * g + e);
+      }
+      *reinterpret_cast<uint2*>(orow + j0 + 4 * g) = make_uint2(f32x2_to_bf16x2(r4[0], r4[1]), f32x2_to_bf16x2(r4[2], r4[3]));
     }
   }
 }
+
 
 struct EntryP {
   int r_k, r_v;
   void (*wkt)(PrefillParams, uint16_t*);
-  void (*qproj)(PrefillParams, PrefillWs);
   void (*attn)(PrefillParams, PrefillWs);
-  void (*oproj)(PrefillParams, PrefillWs);
 };
 
 template <int RK, int RV>
 constexpr EntryP entryP() {
-  return {RK, RV, wk_transpose_kernel<RK>, qproj_prefill_kernel<RK>, prefill_attn_kernel<RK, RV>,
-          oproj_prefill_kernel<RV>};
+  return {RK, RV, wk_transpose_kernel<RK>, prefill_attn_kernel<RK, RV>};
 }
 
 const EntryP kTableP[] = {
@@ -590,19 +533,12 @@ hipError_t launch_prefill(const PrefillParams& pp, int dtype, hipStream_t stream
     const EntryP* e = findP(pp.r_k, pp.r_v);
     if (prefill_mfma_bytes(pp.B, pp.C, pp.H, pp.d, pp.r_k, pp.r_v) > pp.ws_bytes)
       return hipErrorInvalidValue;  // the plan does not fit the workspace: never launch
-    const PrefillWs w = carve(pp.ws, pp.B, pp.C, pp.H, pp.d, pp.r_k, pp.r_v);
-    const unsigned ntok = static_cast<unsigned>(pp.B) * pp.C;
+    const PrefillWs w = carve(pp.ws);
     hipLaunchKernelGGL(e->wkt, dim3(pp.H), dim3(256), 0, stream, pp, w.wkt);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(e->qproj, dim3((ntok + 63) / 64, pp.r_k / 64, pp.H), dim3(256), 0, stream, pp, w);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
     const unsigned nwg = static_cast<unsigned>((pp.C + kRowsWG - 1) / kRowsWG) * pp.H * pp.B;
     hipLaunchKernelGGL(e->attn, dim3(nwg), dim3(512), 0, stream, pp, w);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(e->oproj, dim3((ntok + 63) / 64, (pp.d + 63) / 64, pp.H), dim3(256), 0, stream, pp, w);
     return hipGetLastError();
   }
   DecodeParams p{};
