@@ -333,25 +333,26 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
 }
 
 // ---- 3. merge splits, project once through W^V_t[h], finish ------------------------------------
-// One 256-thread workgroup per (b, h). Every load that does not depend on the merge (the split
-// partials, q, the self K/V, mu^V_t, the W^V_t[h] rows) is issued first, so the workgroup waits for
-// memory once. Thread pair (j, half) then dots row j of W^V_t[h] with half of the merged latent
-// sum, and the pair's sum finishes o[j].
+// One 256-thread workgroup per (head, block of kQB sequences): W^V_t[h] is read once for the block
+// (thread pair (j, half) holds half of row j in registers). Every load that does not depend on the
+// merge (W^V rows, the split partials of all kQB sequences, q, the self K/V, mu^V_t) is issued
+// first; wave w merges sequences w and w + 4 (log-sum-exp over the splits, the self token), the
+// merged latent sums go to LDS, and each thread pair dots its row with every sequence's sum.
 template <int RV>
 __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const float* part) {
   constexpr int HALF = RV / 2;
   static_assert(HALF % 8 == 0, "half a W^V row must be whole 16-byte runs");
   constexpr int RPT = (RV + 255) / 256;  // latent entries per thread
-  __shared__ float a_s[RV];
-  __shared__ float f_s[64];
-  __shared__ float fin_s[4];  // f_lat, p_self, 1/den, l
-  const int b = blockIdx.x;
-  const int h = blockIdx.y;
+  constexpr int kPre = 2;                // splits whose partial sums are loaded up front
+  __shared__ float a_s[kQB][RV];
+  __shared__ float f_s[kQB][64];
+  __shared__ float fin_s[kQB][4];  // f_lat, p_self, 1/den, l
+  const int h = blockIdx.x;
+  const int b0 = blockIdx.y * kQB;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6;
   const int lane = tid & 63;
   const int S_ = p.splits;
-  const size_t bh = static_cast<size_t>(b) * p.H + h;
-  const float* pw = part + bh * S_ * (2 + RV);
   const size_t wrow = (static_cast<size_t>(p.t) * p.H + h) * p.d;  // W^V_t rows of head h; mu offset
 
   // ---- issue: W^V row half of this thread (d <= 128: one row per thread pair) ----
@@ -365,24 +366,29 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
 #pragma unroll
     for (int i = 0; i < HALF / 8; ++i) w[i] = wr[i];
   }
-  float mu_j = 0.f, vs_j = 0.f;
-  if (jok && half == 0) {
-    if (p.mu_v != nullptr) mu_j = ld<BF16>(p.mu_v, wrow + j);
-    if (p.v_self != nullptr) vs_j = ld<BF16>(p.v_self, bh * p.d + j);
-  }
-  // the split latent sums do not depend on the merge: the first kPre splits are loaded now
-  constexpr int kPre = 4;
-  float pa[RPT][kPre];
+  float mu_j = 0.f;
+  if (jok && half == 0 && p.mu_v != nullptr) mu_j = ld<BF16>(p.mu_v, wrow + j);
+  // split latent sums of the first kPre splits for every sequence of the block
+  float pa[kQB][RPT][kPre];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = tid + 256 * i;
+  for (int bb = 0; bb < kQB; ++bb) {
+    const bool bok = b0 + bb < p.B;
+    const float* pw = part + ((static_cast<size_t>(bok ? b0 + bb : 0)) * p.H + h) * S_ * (2 + RV);
 #pragma unroll
-    for (int s2 = 0; s2 < kPre; ++s2)
-      pa[i][s2] = (r < RV && s2 < S_) ? pw[static_cast<size_t>(s2) * (2 + RV) + 2 + r] : 0.f;
+    for (int i = 0; i < RPT; ++i) {
+      const int r = tid + 256 * i;
+#pragma unroll
+      for (int s2 = 0; s2 < kPre; ++s2)
+        pa[bb][i][s2] = (bok && r < RV && s2 < S_) ? pw[static_cast<size_t>(s2) * (2 + RV) + 2 + r] : 0.f;
+    }
   }
-  // wave 0: split maxima and sums, self score
-  float ms = kNegInf, ls = 0.f, pt = 0.f;
-  if (tid < 64) {
+  // wave w: split maxima and sums, self score, of sequences w and w + 4
+  for (int bb = wave; bb < kQB; bb += 4) {
+    const int b = b0 + bb;
+    if (b >= p.B) break;
+    const size_t bh = static_cast<size_t>(b) * p.H + h;
+    const float* pw = part + bh * S_ * (2 + RV);
+    float ms = kNegInf, ls = 0.f, pt = 0.f;
     if (lane < S_) {
       ms = pw[static_cast<size_t>(lane) * (2 + RV)];
       ls = pw[static_cast<size_t>(lane) * (2 + RV) + 1];
@@ -393,48 +399,59 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
     const float fs = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
     const float l = wave_sum(fs * ls);
     const float s_self = p.k_self != nullptr ? wave_sum(pt) * p.scale_log2 : kNegInf;
-    f_s[lane] = fs;
+    f_s[bb][lane] = fs;
     const float M2 = fmaxf(M, s_self);
     const float f_lat = (M == kNegInf) ? 0.f : fast_exp2(M - M2);
     const float p_self = (s_self == kNegInf) ? 0.f : fast_exp2(s_self - M2);
     const float den = l * f_lat + p_self;
     if (lane == 0) {
-      fin_s[0] = f_lat;
-      fin_s[1] = p_self;
-      fin_s[2] = den > 0.f ? 1.0f / den : 0.f;
-      fin_s[3] = l;
+      fin_s[bb][0] = f_lat;
+      fin_s[bb][1] = p_self;
+      fin_s[bb][2] = den > 0.f ? 1.0f / den : 0.f;
+      fin_s[bb][3] = l;
       if (p.lse != nullptr) p.lse[bh] = den > 0.f ? (M2 + fast_log2(den)) * kLn2 : kNegInf;
     }
   }
   __syncthreads();
-  // merged latent sum a = sum_s f_s a_s (f_s is 0 for splits >= S)
+  // merged latent sums a = sum_s f_s a_s (f_s is 0 for splits >= S)
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = tid + 256 * i;
-    if (r < RV) {
-      float a = 0.f;
+  for (int bb = 0; bb < kQB; ++bb) {
+    if (b0 + bb >= p.B) break;
+    const float* pw = part + ((static_cast<size_t>(b0 + bb)) * p.H + h) * S_ * (2 + RV);
 #pragma unroll
-      for (int s2 = 0; s2 < kPre; ++s2) a += f_s[s2] * pa[i][s2];
-      for (int s2 = kPre; s2 < S_; ++s2) a += f_s[s2] * pw[static_cast<size_t>(s2) * (2 + RV) + 2 + r];
-      a_s[r] = a;
+    for (int i = 0; i < RPT; ++i) {
+      const int r = tid + 256 * i;
+      if (r < RV) {
+        float a = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < kPre; ++s2) a += f_s[bb][s2] * pa[bb][i][s2];
+        for (int s2 = kPre; s2 < S_; ++s2) a += f_s[bb][s2] * pw[static_cast<size_t>(s2) * (2 + RV) + 2 + r];
+        a_s[bb][r] = a;
+      }
     }
   }
   __syncthreads();
-  const float* ah = a_s + half * HALF;
-  float o = 0.f;
+  // o[b][j] = (W^V_t[h] row j . a_b + l_b mu^V_t[j]) f_lat + p_self v_self[j], normalised
+  for (int bb = 0; bb < kQB; ++bb) {
+    const int b = b0 + bb;
+    if (b >= p.B) break;
+    const float* ah = a_s[bb] + half * HALF;
+    float o = 0.f;
 #pragma unroll
-  for (int i = 0; i < HALF / 8; ++i) {
-    o += bf16_lo(w[i].x) * ah[8 * i + 0] + bf16_hi(w[i].x) * ah[8 * i + 1];
-    o += bf16_lo(w[i].y) * ah[8 * i + 2] + bf16_hi(w[i].y) * ah[8 * i + 3];
-    o += bf16_lo(w[i].z) * ah[8 * i + 4] + bf16_hi(w[i].z) * ah[8 * i + 5];
-    o += bf16_lo(w[i].w) * ah[8 * i + 6] + bf16_hi(w[i].w) * ah[8 * i + 7];
-  }
-  o += __shfl_xor(o, 1, 64);
-  if (jok && half == 0) {
-    o += fin_s[3] * mu_j;
-    o *= fin_s[0];
-    o += fin_s[1] * vs_j;
-    st<BF16>(p.out, bh * p.d + j, o * fin_s[2]);
+    for (int i = 0; i < HALF / 8; ++i) {
+      o += bf16_lo(w[i].x) * ah[8 * i + 0] + bf16_hi(w[i].x) * ah[8 * i + 1];
+      o += bf16_lo(w[i].y) * ah[8 * i + 2] + bf16_hi(w[i].y) * ah[8 * i + 3];
+      o += bf16_lo(w[i].z) * ah[8 * i + 4] + bf16_hi(w[i].z) * ah[8 * i + 5];
+      o += bf16_lo(w[i].w) * ah[8 * i + 6] + bf16_hi(w[i].w) * ah[8 * i + 7];
+    }
+    o += __shfl_xor(o, 1, 64);
+    if (jok && half == 0) {
+      const size_t bh = static_cast<size_t>(b) * p.H + h;
+      o += fin_s[bb][3] * mu_j;
+      o *= fin_s[bb][0];
+      if (p.v_self != nullptr) o += fin_s[bb][1] * ld<BF16>(p.v_self, bh * p.d + j);
+      st<BF16>(p.out, bh * p.d + j, o * fin_s[bb][2]);
+    }
   }
 }
 
@@ -513,7 +530,7 @@ hipError_t launch_decode2d(const DecodeParams& p0, hipStream_t stream) {
                      stream, p, qt, beta, part);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(e->combine, dim3(p.B, p.H), dim3(256), 0, stream, p, part);
+  hipLaunchKernelGGL(e->combine, dim3(p.H, qb), dim3(256), 0, stream, p, part);
   return hipGetLastError();
 }
 

@@ -525,12 +525,17 @@ hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t stream) {
   if (dtype == LLA_BF16) {
     if (encode_gemm_ok(p))
       return p.r % 256 == 0 ? launch_encode_gemm<256>(p, stream) : launch_encode_gemm<128>(p, stream);
-    const int nt_tiles = p.r <= 16 ? 1 : p.r <= 32 ? 2 : 4;
+    int nt_tiles = p.r <= 16 ? 1 : p.r <= 32 ? 2 : 4;
     const long ntok = static_cast<long>(p.B) * p.C;
-    const long wgs1 = (ntok + 127) / 128 * ((p.r + 16 * nt_tiles - 1) / (16 * nt_tiles)) * p.H;
     // few workgroups with whole-K waves would leave most of the chip idle: split K instead,
-    // eight ways for decode-size token counts
-    if (ntok <= 256) return launch_encode_mfma<1, 8>(p, nt_tiles, stream);
+    // eight ways for decode-size token counts, and narrow the latent tiles until the launch has a
+    // workgroup per CU (fewer latent rows per workgroup re-read x more often, from L2)
+    if (ntok <= 256) {
+      auto wgs = [&](int nt) { return (ntok + 15) / 16 * ((p.r + 16 * nt - 1) / (16 * nt)) * p.H; };
+      while (nt_tiles > 1 && wgs(nt_tiles) < 256) nt_tiles /= 2;
+      return launch_encode_mfma<1, 8>(p, nt_tiles, stream);
+    }
+    const long wgs1 = (ntok + 127) / 128 * ((p.r + 16 * nt_tiles - 1) / (16 * nt_tiles)) * p.H;
     return wgs1 < 1024 ? launch_encode_mfma<2, 4>(p, nt_tiles, stream)
                        : launch_encode_mfma<2, 1>(p, nt_tiles, stream);
   }
