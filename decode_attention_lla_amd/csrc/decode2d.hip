@@ -60,7 +60,7 @@ __device__ __forceinline__ short4_t v_operand_tr(const char* vt, int kb, int r0,
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_ptr)(vt + row * RV * 2 + pc * 16 + (r & 7) * 2));
 }
 
-constexpr int kQB = 8;     // sequences per qproj / combine workgroup
+constexpr int kQB = 4;     // sequences per qproj / combine workgroup
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
 // One 256-thread workgroup per (head, block of kQB sequences): W^V_t[h] is read once for the block
 // (thread pair (j, half) holds half of row j in registers). Every load that does not depend on the
 // merge (W^V rows, the split partials of all kQB sequences, q, the self K/V, mu^V_t) is issued
-// first; wave w merges sequences w and w + 4 (log-sum-exp over the splits, the self token), the
+// first; wave w merges sequences w, w + 4, ... (log-sum-exp over the splits, the self token), the
 // merged latent sums go to LDS, and each thread pair dots its row with every sequence's sum.
 template <int RV>
 __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const float* part) {
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
         pa[bb][i][s2] = (bok && r < RV && s2 < S_) ? pw[static_cast<size_t>(s2) * (2 + RV) + 2 + r] : 0.f;
     }
   }
-  // wave w: split maxima and sums, self score, of sequences w and w + 4
+  // wave w: split maxima and sums, self score, of sequences w, w + 4, ...
   for (int bb = wave; bb < kQB; bb += 4) {
     const int b = b0 + bb;
     if (b >= p.B) break;
