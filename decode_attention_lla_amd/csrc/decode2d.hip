@@ -248,8 +248,7 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
       sc[e] = ok ? (sh[e] + sl[e]) + bt : kNegInf;
       tmax = fmaxf(tmax, sc[e]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = max_over_groups(tmax);
     if (tmax > m + kLazy2d) {
       const float c = fast_exp2(m - tmax);
       l *= c;
@@ -282,8 +281,7 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
     for (int i = 0; i < KS; ++i) kc[i] = kn[i];
     buf ^= 1;
   }
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = sum_over_groups(l);
 
   // merge the waves through LDS (the V rings are free now): 8 -> 4 -> 2 -> 1
   __syncthreads();

@@ -108,4 +108,20 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Max and sum over lanes l, l^16, l^32, l^48 (the four 16-lane groups of a wave) with the gfx950
+// lane-swap instructions: VALU only, no LDS round trip. Each swap hands every lane its partner's
+// value in one of the two results and its own value in the other.
+__device__ __forceinline__ float max_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 }  // namespace lla

@@ -42,10 +42,24 @@ typedef __attribute__((address_space(3))) short4_t* lds_short4_ptr;
 // LDS layout of a V tile (kKeyTile keys x RV latent entries, bf16): 128-byte blocks of 4 keys x 16
 // entries, row-major inside the block (16-byte unit = 8 entries of one key, units ordered key,
 // half), blocks ordered key quad major. Byte offset of unit (key, 8-entry group r8):
+// The entry block index is XORed with the key quad's parity: the two 16-lane groups of a 32-lane
+// half of a transposed read take consecutive key quads, whose blocks would otherwise lie a multiple
+// of 256 bytes apart, on the same LDS banks.
 template <int RV>
 __device__ __forceinline__ int v_unit_offset(int key, int r8) {
   constexpr int NRQ = RV / 16;  // entry blocks per key quad
-  return ((key >> 2) * NRQ + (r8 >> 1)) * 128 + ((key & 3) * 2 + (r8 & 1)) * 16;
+  const int kq = key >> 2;
+  return (kq * NRQ + ((r8 >> 1) ^ (kq & 1))) * 128 + ((key & 3) * 2 + (r8 & 1)) * 16;
+}
+
+// LDS placement of 16-byte chunk c of K tile row `row` (CPK chunks per row). A K operand read is a
+// ds_read_b128 whose 16-lane groups take 16 consecutive rows at one chunk; it touches every LDS bank
+// once when those 16 chunks fall in 16 distinct 16-byte slots of a 256-byte bank window: an XOR by
+// the row inside 16-chunk windows for rows of >= 256 bytes, and by row / 2 for 128-byte rows.
+template <int CPK>
+__device__ __forceinline__ int k_chunk_slot(int row, int c) {
+  if constexpr (CPK >= 16) return (c & ~15) | ((c & 15) ^ (row & 15));
+  else return c ^ ((row >> 1) & 7);
 }
 
 // A operand of v_mfma_f32_16x16x16bf16_1k-style 4-key slices holding Z^V^T[r0 + i][kb + 4q + e]
@@ -276,8 +290,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     const int f = i * 64 + lane;
     const int row = f / CPK;
     const int pc = f - row * CPK;
-    const int lc = (pc & ~7) | ((pc & 7) ^ (row & 7));
-    koff[u] = (row * RK + lc * 8) * 2;
+    koff[u] = (row * RK + k_chunk_slot<CPK>(row, pc) * 8) * 2;  // the slot map is an involution
   }
 #pragma unroll
   for (int u = 0; u < LV; ++u) {
@@ -286,7 +299,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     const int U = i * 64 + lane;
     const int block = U >> 3;
     const int kq = block / NRQ;
-    const int rq = block - kq * NRQ;
+    const int rq = (block - kq * NRQ) ^ (kq & 1);  // inverse of the block XOR of v_unit_offset
     const int key = 4 * kq + ((U >> 1) & 3);
     const int r8 = 2 * rq + (U & 1);
     voff[u] = (key * RV + r8 * 8) * 2;
@@ -344,14 +357,14 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     const bool masked = key0 + kKeyTile - 1 > wave_lim;  // wave-uniform
 #pragma unroll
     for (int kt16 = 0; kt16 < 2; ++kt16) {
-      // S^T[key 16*kt16 + i][row] - m: A = K rows (swizzled chunks), B = Q~^T fragments
+      // S^T[key 16*kt16 + i][row] - m: A = K rows (chunks at their slots), B = Q~^T fragments
       const int row = 16 * kt16 + col;
       floatx4_t sh = {bm, bm, bm, bm};
       floatx4_t sl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int c = 4 * ks + g;
-        const int pc = (c & ~7) | ((c & 7) ^ (row & 7));
+        const int pc = k_chunk_slot<CPK>(row, c);
         const uint4 a = *reinterpret_cast<const uint4*>(kt + row * RK * 2 + pc * 16);
         sh = mfma32(a, qh[ks], sh);
         sl = mfma32(a, ql[ks], sl);
@@ -366,8 +379,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
 #pragma unroll
       for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sc[kt16][e]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = max_over_groups(tmax);
     if (tmax > kLazyP || (!based && tmax > kNegInf)) {
       if (based) {
         const float c = fast_exp2(-tmax);
@@ -421,8 +433,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // the spare fetches have landed before the wave ends
   }
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = sum_over_groups(l);
   // O = A . W^V_t[h]^T (+ mu^V_t when the row saw any latent), A = D / l, on MFMA as
   // O^T[j][row] = W^V . A^T. The B operand of each 32-wide r chunk comes straight from the
   // accumulators: lane (row + 16 g) holds r = 16 rt + 4 g + (0..3), so elements 0-3 take chunk half
