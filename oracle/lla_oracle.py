@@ -317,3 +317,57 @@ def attend_prefill(q, zk, zv, Wk, Wv, t, ctx_lens, mu_k=None, mu_v=None, scale=N
                 n = min(base + j + 1, n_max)
                 o[b, j, h], _ = softmax_attention(q[b, j, h], K[:n], V[:n], scale)
     return o
+
+
+def streaming_kept_slots(n, sink, window):
+    """Slots that a StreamingLLM-style eviction policy keeps out of n cached tokens.
+
+    The first `sink` tokens (attention sinks) and the `window` most recent ones, each slot once, in
+    increasing order. The paper composes LLA with this sequence-axis eviction (Section 7,
+    "Memory, capacity and latency": a 1024-token budget on top of the 21.3x codec; Appendix C,
+    Table 9: sink 4 + window 256).
+    """
+    n = max(int(n), 0)
+    keep = set(range(min(int(sink), n))) | set(range(max(n - int(window), 0), n))
+    return sorted(keep)
+
+
+def attend_decode_gather(q, zk, zv, Wk, Wv, t, slots, counts=None, mu_k=None, mu_v=None,
+                         k_self=None, v_self=None, scale=None, variant="per_head"):
+    """Decode attention at loop t over a listed subset of the cached latents (token eviction
+    composed with LLA: Section 7, "Memory, capacity and latency", and Appendix C).
+
+    Row b attends the cached tokens at slots[b, 0 .. counts[b]-1] (counts clamped to [0, budget],
+    None meaning the whole budget), in any order, plus the optional self token. A slot outside
+    [0, n_max) is skipped; a slot listed twice is two keys. Each listed key is rebuilt explicitly
+    (Eq. 3) and attended with textbook softmax.
+
+    slots [B, budget] int; counts [B] int or None; the rest as attend_decode.
+    Returns (o [B,H,d], lse [B,H]) in float64.
+    """
+    _check_variant(variant)
+    q = _f64(q)
+    zk, zv, Wk, Wv = _f64(zk), _f64(zv), _f64(Wk), _f64(Wv)
+    mu_k, mu_v, k_self, v_self = _f64(mu_k), _f64(mu_v), _f64(k_self), _f64(v_self)
+    slots = np.asarray(slots)
+    B, H, d = q.shape
+    budget = slots.shape[1]
+    n_max = zk.shape[2] if variant == "per_head" else zk.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = np.zeros((B, H, d), dtype=np.float64)
+    lse = np.zeros((B, H), dtype=np.float64)
+    for b in range(B):
+        cnt = budget if counts is None else int(min(max(int(counts[b]), 0), budget))
+        listed = [int(s) for s in slots[b, :cnt] if 0 <= int(s) < n_max]
+        for h in range(H):
+            wk, wv, muk, muv = _loop_slices(variant, Wk, Wv, mu_k, mu_v, t, h, H, d)
+            lat_k = zk[b, h] if variant == "per_head" else zk[b]
+            lat_v = zv[b, h] if variant == "per_head" else zv[b]
+            K = reconstruct(lat_k[listed], wk, muk)
+            V = reconstruct(lat_v[listed], wv, muv)
+            if k_self is not None:
+                K = np.concatenate([K, k_self[b, h][None, :]], axis=0)
+                V = np.concatenate([V, v_self[b, h][None, :]], axis=0)
+            o[b, h], lse[b, h] = softmax_attention(q[b, h], K, V, scale)
+    return o, lse

@@ -11,6 +11,7 @@ import pytest
 
 from oracle import lla_oracle as O
 import tests.test_oracle_pins as P
+import tests.test_oracle_gather as G
 
 
 def _encode_no_centre(x_stack, E, mu=None):
@@ -67,11 +68,35 @@ def _loop_slices_2d_head_major(variant, Wk, Wv, mu_k, mu_v, t, h, H, d):
     return wk, wv, muk, muv
 
 
+def _gather_drop_last(q, zk, zv, Wk, Wv, t, slots, counts=None, **kw):
+    slots = np.asarray(slots)
+    c = np.full(slots.shape[0], slots.shape[1]) if counts is None else np.asarray(counts)
+    return _orig["attend_decode_gather"](q, zk, zv, Wk, Wv, t, slots, np.maximum(c - 1, 0), **kw)
+
+
+def _gather_dedup(q, zk, zv, Wk, Wv, t, slots, counts=None, **kw):
+    slots = np.asarray(slots).copy()
+    for b in range(slots.shape[0]):
+        seen = set()
+        for j in range(slots.shape[1]):
+            if int(slots[b, j]) in seen:
+                slots[b, j] = -1
+            seen.add(int(slots[b, j]))
+    return _orig["attend_decode_gather"](q, zk, zv, Wk, Wv, t, slots, counts, **kw)
+
+
+def _gather_wraps_out_of_range(q, zk, zv, Wk, Wv, t, slots, counts=None, variant="per_head", **kw):
+    n_max = np.asarray(zk).shape[2 if variant == "per_head" else 1]
+    return _orig["attend_decode_gather"](q, zk, zv, Wk, Wv, t, np.asarray(slots) % n_max, counts,
+                                         variant=variant, **kw)
+
+
 _orig = {
     "encode_stack": O.encode_stack,
     "reconstruct": O.reconstruct,
     "softmax_attention": O.softmax_attention,
     "_loop_slices": O._loop_slices,
+    "attend_decode_gather": O.attend_decode_gather,
 }
 
 MUTANTS = {
@@ -85,6 +110,9 @@ MUTANTS = {
     "attention drops the last key": ("softmax_attention", _softmax_drop_last_key),
     "decode reads loop t+1's factors": ("_loop_slices", _loop_slices_wrong_loop),
     "2d mu indexed head-major": ("_loop_slices", _loop_slices_2d_head_major),
+    "gather drops the last listed slot": ("attend_decode_gather", _gather_drop_last),
+    "gather attends a repeated slot once": ("attend_decode_gather", _gather_dedup),
+    "gather wraps out-of-range slots": ("attend_decode_gather", _gather_wraps_out_of_range),
 }
 
 PINS = [
@@ -97,6 +125,9 @@ PINS = [
     P.test_empty_context_and_length_clamp,
     P.test_prefill_full_rank_identity_causal_offset,
     P.test_brute_force_tiny,
+    G.test_full_rank_codec_equals_sdpa_on_kept_tokens,
+    G.test_brute_force_tiny_with_duplicates_and_skips,
+    G.test_empty_lists,
 ]
 
 
