@@ -56,6 +56,8 @@ def parse():
                     help="skip the LLA-2D decode and chunked-prefill figures")
     ap.add_argument("--only-prefill", action="store_true",
                     help="measure only the LLA-2D chunked prefill (for profiling)")
+    ap.add_argument("--only-eviction", action="store_true",
+                    help="measure only the gather-indexed (token-eviction) decode read")
     return ap.parse_args()
 
 
@@ -100,6 +102,9 @@ def main():
     torch.cuda.set_device(0)
     if args.only_prefill:
         print(json.dumps({"lla2d_prefill": lla2d_prefill(args)}), flush=True)
+        return
+    if args.only_eviction:
+        print(json.dumps({"eviction_decode": eviction_decode(args)}), flush=True)
         return
     s = synth.CASES[args.workload]
     D = args.layers or s.D
@@ -213,7 +218,8 @@ def main():
     if not args.no_extras and args.workload == "capacity":
         del zk, zv, q, kself, vself, xk, xv, out
         torch.cuda.empty_cache()
-        extras = {"lla2d_decode": lla2d_decode(args), "lla2d_prefill": lla2d_prefill(args)}
+        extras = {"lla2d_decode": lla2d_decode(args), "lla2d_prefill": lla2d_prefill(args),
+                  "eviction_decode": eviction_decode(args)}
 
     res = {
         "metric": METRIC,
@@ -318,6 +324,65 @@ def lla2d_decode(args):
             "latent_frac_of_peak": round(latent / (ms_read / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "mfma_TFLOPs": round(flops / (ms_read / 1e3) / 1e12, 2),
             "mfma_util_bf16_dense": round(flops / (ms_read / 1e3) / 2.5e15, 4)}
+
+
+def eviction_decode(args):
+    """Token eviction composed with LLA at the capacity shape (one layer: B=768, H=16, d=128, T=4,
+    r=24/24, 4096 cached tokens): each read attends a 1024-slot StreamingLLM list (4 sinks + the
+    1020 most recent tokens) through lla_attend_decode_gather, beside the contiguous read of a
+    1024-token cache of the same shape and a read of 1024 random slots (H2O-like scattered rows)."""
+    import torch
+    from decode_attention_lla_amd import lla, synth
+    s = synth.CASES["capacity"]
+    B, H, d, T, r, N = s.B, s.H, s.d, s.T, s.r_k, s.N
+    keep = 1024
+    n_max = N + 1
+    bf = torch.bfloat16
+    desc = lla.make_desc(lla.LLA_PER_HEAD, lla.LLA_BF16, H, d, T, r, r, n_max)
+    zk = synth.device_normal_(torch.empty(B, H, n_max, r, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZK))
+    zv = synth.device_normal_(torch.empty(B, H, n_max, r, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZV))
+    Wk = torch.from_numpy(synth.orthonormal_W(T, H, d, r, synth.seed(s.case, synth.SEED_WK), "bf16")).to(bf).cuda()
+    Wv = torch.from_numpy(synth.orthonormal_W(T, H, d, r, synth.seed(s.case, synth.SEED_WV), "bf16")).to(bf).cuda()
+    q = synth.device_normal_(torch.empty(B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_Q))
+    ks = synth.device_normal_(torch.empty(B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF))
+    vs = synth.device_normal_(torch.empty(B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF) + 1)
+    out = torch.empty(B, H, d, dtype=bf, device="cuda")
+    sink, window = 4, keep - 4
+    row = torch.cat([torch.arange(sink), torch.arange(N - window, N)]).to(torch.int32)
+    slots = row.repeat(B, 1).contiguous().cuda()
+    ws = lla.gather_workspace(desc, B, keep)
+    lens = torch.full((B,), keep, dtype=torch.int32, device="cuda")
+    desc_c = lla.make_desc(lla.LLA_PER_HEAD, lla.LLA_BF16, H, d, T, r, r, keep)
+    zk_c, zv_c = zk[:, :, :keep].contiguous(), zv[:, :, :keep].contiguous()
+    ws_c = lla.workspace(desc_c, B, 1)
+
+    def gathered():
+        lla.lla_attend_decode_gather(desc, B, 0, q, zk, zv, slots, None, Wk, Wv, None, None, ks, vs,
+                                     out, None, ws)
+
+    def contiguous():
+        lla.lla_attend_decode(desc_c, B, 0, q, zk_c, zv_c, lens, Wk, Wv, None, None, ks, vs, out,
+                              None, ws_c)
+
+    rnd = torch.from_numpy(synth.random_slots(B, keep, N, synth.seed(s.case, synth.SEED_SLOTS))).cuda()
+
+    def gathered_random():
+        lla.lla_attend_decode_gather(desc, B, 0, q, zk, zv, rnd, None, Wk, Wv, None, None, ks, vs,
+                                     out, None, ws)
+
+    ms_g = _timed(gathered, 20, 3)
+    ms_r = _timed(gathered_random, 20, 3)
+    ms_c = _timed(contiguous, 20, 3)
+    kept_bytes = B * H * keep * 2 * r * 2
+    return {"workload": f"capacity layer read through a {keep}-slot sink {sink} + window {window} "
+                        f"list of a {N}-token cache: H={H}, d_head={d}, r_k=r_v={r}, B={B}, bf16",
+            "read_us": round(ms_g * 1e3, 2),
+            "kept_latent_GBps": round(kept_bytes / (ms_g / 1e3) / 1e9, 1),
+            "kept_latent_frac_of_peak": round(kept_bytes / (ms_g / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "contiguous_read_of_the_same_count_us": round(ms_c * 1e3, 2),
+            "random_1024_of_4096_read_us": round(ms_r * 1e3, 2),
+            "cache_bytes_per_sequence_and_layer": {"cached": H * n_max * 2 * r * 2,
+                                                   "read": H * keep * 2 * r * 2}}
 
 
 def lla2d_prefill(args):

@@ -41,6 +41,58 @@ lla_status from_hip(hipError_t e) {
   return LLA_ERR_HIP;
 }
 
+// Argument checks shared by the two decode entry points.
+lla_status decode_args_ok(const lla_desc* desc, int32_t B, int32_t t, const void* q,
+                          const void* zk, const void* zv, const int32_t* lens, const void* Wk,
+                          const void* Wv, const void* mu_k, const void* mu_v, const void* k_self,
+                          const void* v_self, const void* out, const float* lse, const void* ws) {
+  if (!desc_ok(desc) || B <= 0 || t < 0 || t >= desc->T) return LLA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * desc->H >= (int64_t(1) << 31) / 64) return LLA_ERR_INVALID_ARG;
+  if (!req_ok(q) || !req_ok(zk) || !req_ok(zv) || !req_ok(Wk) || !req_ok(Wv) || !req_ok(out))
+    return LLA_ERR_INVALID_ARG;
+  if (!opt_ok(lens) || !opt_ok(mu_k) || !opt_ok(mu_v) || !opt_ok(k_self) || !opt_ok(v_self) ||
+      !opt_ok(lse) || !opt_ok(ws))
+    return LLA_ERR_INVALID_ARG;
+  if ((k_self == nullptr) != (v_self == nullptr)) return LLA_ERR_INVALID_ARG;
+  return LLA_OK;
+}
+
+lla::DecodeParams decode_params(const lla_desc* desc, int32_t B, int32_t t, const void* q,
+                                const void* zk, const void* zv, const int32_t* lens,
+                                const void* Wk, const void* Wv, const void* mu_k,
+                                const void* mu_v, const void* k_self, const void* v_self,
+                                void* out, float* lse, void* ws, size_t ws_bytes) {
+  lla::DecodeParams p{};
+  p.q = q;
+  p.zk = zk;
+  p.zv = zv;
+  p.seq_lens = lens;
+  p.Wk = Wk;
+  p.Wv = Wv;
+  p.mu_k = mu_k;
+  p.mu_v = mu_v;
+  p.k_self = k_self;
+  p.v_self = v_self;
+  p.out = out;
+  p.lse = lse;
+  p.ws = static_cast<float*>(ws);
+  p.B = B;
+  p.H = desc->H;
+  p.d = desc->d_head;
+  p.T = desc->T;
+  p.t = t;
+  p.n_max = desc->n_max;
+  p.r_k = desc->r_k;
+  p.r_v = desc->r_v;
+  p.rows_per_seq = 1;
+  p.causal = 0;
+  p.variant = desc->variant;
+  p.scale_log2 = scale_log2(desc);
+  p.ws_bytes = ws == nullptr ? 0 : ws_bytes;
+  return p;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -105,54 +157,55 @@ lla_status lla_encode(const lla_desc* desc, int32_t B, int32_t C, const void* xk
   return from_hip(lla::launch_encode(p, desc->dtype, s));
 }
 
+
 lla_status lla_attend_decode(const lla_desc* desc, int32_t B, int32_t t, const void* q,
                              const void* zk, const void* zv, const int32_t* seq_lens,
                              const void* Wk, const void* Wv, const void* mu_k, const void* mu_v,
                              const void* k_self, const void* v_self, void* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream) {
-  if (!desc_ok(desc) || B <= 0 || t < 0 || t >= desc->T) return LLA_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(B) * desc->H >= (int64_t(1) << 31) / 64) return LLA_ERR_INVALID_ARG;
-  if (!req_ok(q) || !req_ok(zk) || !req_ok(zv) || !req_ok(Wk) || !req_ok(Wv) || !req_ok(out))
-    return LLA_ERR_INVALID_ARG;
-  if (!opt_ok(seq_lens) || !opt_ok(mu_k) || !opt_ok(mu_v) || !opt_ok(k_self) || !opt_ok(v_self) ||
-      !opt_ok(lse) || !opt_ok(ws))
-    return LLA_ERR_INVALID_ARG;
-  if ((k_self == nullptr) != (v_self == nullptr)) return LLA_ERR_INVALID_ARG;
+  const lla_status st = decode_args_ok(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v,
+                                       k_self, v_self, out, lse, ws);
+  if (st != LLA_OK) return st;
   if (!lla::decode_supported(desc->variant, desc->dtype, desc->r_k, desc->r_v, desc->d_head))
     return LLA_ERR_UNSUPPORTED;
   const size_t need = lla::decode_workspace_bytes(*desc, B);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return LLA_ERR_WORKSPACE;
 
-  lla::DecodeParams p{};
-  p.q = q;
-  p.zk = zk;
-  p.zv = zv;
-  p.seq_lens = seq_lens;
-  p.Wk = Wk;
-  p.Wv = Wv;
-  p.mu_k = mu_k;
-  p.mu_v = mu_v;
-  p.k_self = k_self;
-  p.v_self = v_self;
-  p.out = out;
-  p.lse = lse;
-  p.ws = static_cast<float*>(ws);
-  p.B = B;
-  p.H = desc->H;
-  p.d = desc->d_head;
-  p.T = desc->T;
-  p.t = t;
-  p.n_max = desc->n_max;
-  p.r_k = desc->r_k;
-  p.r_v = desc->r_v;
-  p.rows_per_seq = 1;
-  p.causal = 0;
-  p.variant = desc->variant;
-  p.scale_log2 = scale_log2(desc);
-  p.ws_bytes = ws == nullptr ? 0 : ws_bytes;
+  lla::DecodeParams p = decode_params(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_self,
+                                      v_self, out, lse, ws, ws_bytes);
   lla::decode_plan(*desc, B, &p.splits, &p.chunk);
   return from_hip(lla::launch_decode(p, desc->dtype, static_cast<hipStream_t>(stream)));
 }
+
+size_t lla_gather_workspace_bytes(const lla_desc* desc, int32_t B, int32_t budget) {
+  if (!desc_ok(desc) || B <= 0 || budget <= 0) return 0;
+  return lla::gather_workspace_bytes(*desc, B, budget);
+}
+
+lla_status lla_attend_decode_gather(const lla_desc* desc, int32_t B, int32_t t, const void* q,
+                                    const void* zk, const void* zv, const int32_t* slots,
+                                    int32_t budget, const int32_t* counts, const void* Wk,
+                                    const void* Wv, const void* mu_k, const void* mu_v,
+                                    const void* k_self, const void* v_self, void* out, float* lse,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  const lla_status st = decode_args_ok(desc, B, t, q, zk, zv, counts, Wk, Wv, mu_k, mu_v, k_self,
+                                       v_self, out, lse, ws);
+  if (st != LLA_OK) return st;
+  if (!req_ok(slots) || budget <= 0) return LLA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * budget >= (int64_t(1) << 31)) return LLA_ERR_INVALID_ARG;
+  if (!lla::valu_supported(desc->variant, desc->dtype, desc->r_k, desc->r_v))
+    return LLA_ERR_UNSUPPORTED;
+  const size_t need = lla::gather_workspace_bytes(*desc, B, budget);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return LLA_ERR_WORKSPACE;
+
+  lla::DecodeParams p = decode_params(desc, B, t, q, zk, zv, counts, Wk, Wv, mu_k, mu_v, k_self,
+                                      v_self, out, lse, ws, ws_bytes);
+  p.slots = slots;
+  p.budget = budget;
+  lla::gather_plan(*desc, B, budget, &p.splits, &p.chunk);
+  return from_hip(lla::launch_decode_gather(p, desc->dtype, static_cast<hipStream_t>(stream)));
+}
+
 
 lla_status lla_attend_prefill(const lla_desc* desc, int32_t B, int32_t C, int32_t t,
                               const void* q, const void* zk, const void* zv,

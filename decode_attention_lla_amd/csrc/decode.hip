@@ -28,6 +28,12 @@ __device__ __forceinline__ size_t latent_row(const DecodeParams& p, int seq, int
                              : (static_cast<size_t>(seq) * p.H + h) * p.n_max;
 }
 
+// Listed slots of a gather-indexed row, clamped to [0, budget].
+__device__ __forceinline__ int gather_keys(const DecodeParams& p, int row) {
+  const int n = p.seq_lens != nullptr ? p.seq_lens[row] : p.budget;
+  return min(max(n, 0), p.budget);
+}
+
 // Keys visible to query row `row` (see DecodeParams), clamped to [0, n_max].
 __device__ __forceinline__ int row_keys(const DecodeParams& p, int row) {
   const int seq = row / p.rows_per_seq;
@@ -81,8 +87,10 @@ __device__ void finish_unit(const DecodeParams& p, int b, int h, float M, float 
 }
 
 // One wave per (b, h, split). LPT lanes share a token; each holds EK = RK/LPT K elements and
-// EV = RV/LPT V elements. U tiles of 64/LPT tokens are loaded before any is consumed.
-template <class S, int RK, int RV, int LPT, int U>
+// EV = RV/LPT V elements. U tiles of 64/LPT tokens are loaded before any is consumed. With G the
+// split ranges over the row's slot list instead of its first N latents: each token's slot is read
+// first, and a slot outside [0, n_max) counts as masked.
+template <class S, int RK, int RV, int LPT, int U, bool G>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   constexpr int EK = RK / LPT;
   constexpr int EV = RV / LPT;
@@ -103,7 +111,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   const int h = bh % p.H;
   const int b = bh / p.H;
 
-  const int nb = row_keys(p, b);
+  const int nb = G ? gather_keys(p, b) : row_keys(p, b);
   const int tb = split * p.chunk;
   const int te = min(nb, tb + p.chunk);
 
@@ -137,6 +145,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   const char* zkp = static_cast<const char*>(p.zk) + (lrow * RK + sub * EK) * S::kBytes;
   const char* zvp = static_cast<const char*>(p.zv) + (lrow * RV + sub * EV) * S::kBytes;
 
+  const int32_t* srow = G ? p.slots + static_cast<size_t>(b) * p.budget : nullptr;
+
   float m = kNegInf;
   float l = 0.f;
   float acc[EV];
@@ -147,13 +157,22 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     uint4 kr[U][VK];
     uint4 vr[U][VV];
     bool ok[U];
+    int slot[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int tok = t0 + u * TPW + grp;
       ok[u] = tok < te;
+      slot[u] = tok;
+      if (G) {
+        slot[u] = ok[u] ? srow[tok] : 0;
+        ok[u] = ok[u] && static_cast<unsigned>(slot[u]) < static_cast<unsigned>(p.n_max);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       if (ok[u]) {
-        const uint4* kp = reinterpret_cast<const uint4*>(zkp + static_cast<size_t>(tok) * RK * S::kBytes);
-        const uint4* vp = reinterpret_cast<const uint4*>(zvp + static_cast<size_t>(tok) * RV * S::kBytes);
+        const uint4* kp = reinterpret_cast<const uint4*>(zkp + static_cast<size_t>(slot[u]) * RK * S::kBytes);
+        const uint4* vp = reinterpret_cast<const uint4*>(zvp + static_cast<size_t>(slot[u]) * RV * S::kBytes);
 #pragma unroll
         for (int i = 0; i < VK; ++i) kr[u][i] = kp[i];
 #pragma unroll
@@ -262,34 +281,39 @@ using PartialFn = void (*)(DecodeParams);
 
 template <class S, int RK, int RV, int LPT, int U>
 PartialFn partial_fn() {
-  return decode_partial_kernel<S, RK, RV, LPT, U>;
+  return decode_partial_kernel<S, RK, RV, LPT, U, false>;
+}
+template <class S, int RK, int RV, int LPT, int U>
+PartialFn gather_fn() {
+  return decode_partial_kernel<S, RK, RV, LPT, U, true>;
 }
 
 struct Entry {
   int dtype, r_k, r_v;
-  PartialFn fn;
+  PartialFn fn;   // contiguous read
+  PartialFn gfn;  // gather-indexed read
 };
 
 // Compiled (dtype, r_k, r_v) -> (lanes per token, tiles in flight).
 const Entry kTable[] = {
-    {LLA_BF16, 8, 8, partial_fn<BF16, 8, 8, 1, 4>()},
-    {LLA_BF16, 16, 16, partial_fn<BF16, 16, 16, 1, 4>()},
-    {LLA_BF16, 24, 24, partial_fn<BF16, 24, 24, 1, 2>()},
-    {LLA_BF16, 32, 32, partial_fn<BF16, 32, 32, 1, 2>()},
-    {LLA_BF16, 64, 64, partial_fn<BF16, 64, 64, 2, 2>()},
-    {LLA_BF16, 96, 96, partial_fn<BF16, 96, 96, 4, 2>()},
-    {LLA_BF16, 128, 128, partial_fn<BF16, 128, 128, 4, 2>()},
-    {LLA_BF16, 96, 160, partial_fn<BF16, 96, 160, 4, 2>()},
-    {LLA_BF16, 256, 256, partial_fn<BF16, 256, 256, 8, 2>()},
-    {LLA_F32, 8, 8, partial_fn<F32, 8, 8, 1, 2>()},
-    {LLA_F32, 16, 16, partial_fn<F32, 16, 16, 1, 2>()},
-    {LLA_F32, 24, 24, partial_fn<F32, 24, 24, 1, 1>()},
-    {LLA_F32, 32, 32, partial_fn<F32, 32, 32, 2, 1>()},
-    {LLA_F32, 64, 64, partial_fn<F32, 64, 64, 4, 1>()},
-    {LLA_F32, 96, 96, partial_fn<F32, 96, 96, 4, 1>()},
-    {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 8, 1>()},
-    {LLA_F32, 96, 160, partial_fn<F32, 96, 160, 8, 1>()},
-    {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 16, 1>()},
+    {LLA_BF16, 8, 8, partial_fn<BF16, 8, 8, 1, 4>(), gather_fn<BF16, 8, 8, 1, 4>()},
+    {LLA_BF16, 16, 16, partial_fn<BF16, 16, 16, 1, 4>(), gather_fn<BF16, 16, 16, 1, 4>()},
+    {LLA_BF16, 24, 24, partial_fn<BF16, 24, 24, 1, 2>(), gather_fn<BF16, 24, 24, 1, 2>()},
+    {LLA_BF16, 32, 32, partial_fn<BF16, 32, 32, 1, 2>(), gather_fn<BF16, 32, 32, 1, 2>()},
+    {LLA_BF16, 64, 64, partial_fn<BF16, 64, 64, 2, 2>(), gather_fn<BF16, 64, 64, 2, 2>()},
+    {LLA_BF16, 96, 96, partial_fn<BF16, 96, 96, 4, 2>(), gather_fn<BF16, 96, 96, 4, 2>()},
+    {LLA_BF16, 128, 128, partial_fn<BF16, 128, 128, 4, 2>(), gather_fn<BF16, 128, 128, 4, 2>()},
+    {LLA_BF16, 96, 160, partial_fn<BF16, 96, 160, 4, 2>(), gather_fn<BF16, 96, 160, 4, 2>()},
+    {LLA_BF16, 256, 256, partial_fn<BF16, 256, 256, 8, 2>(), gather_fn<BF16, 256, 256, 8, 2>()},
+    {LLA_F32, 8, 8, partial_fn<F32, 8, 8, 1, 2>(), gather_fn<F32, 8, 8, 1, 2>()},
+    {LLA_F32, 16, 16, partial_fn<F32, 16, 16, 1, 2>(), gather_fn<F32, 16, 16, 1, 2>()},
+    {LLA_F32, 24, 24, partial_fn<F32, 24, 24, 1, 1>(), gather_fn<F32, 24, 24, 1, 1>()},
+    {LLA_F32, 32, 32, partial_fn<F32, 32, 32, 2, 1>(), gather_fn<F32, 32, 32, 2, 1>()},
+    {LLA_F32, 64, 64, partial_fn<F32, 64, 64, 4, 1>(), gather_fn<F32, 64, 64, 4, 1>()},
+    {LLA_F32, 96, 96, partial_fn<F32, 96, 96, 4, 1>(), gather_fn<F32, 96, 96, 4, 1>()},
+    {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 8, 1>(), gather_fn<F32, 128, 128, 8, 1>()},
+    {LLA_F32, 96, 160, partial_fn<F32, 96, 160, 8, 1>(), gather_fn<F32, 96, 160, 8, 1>()},
+    {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 16, 1>(), gather_fn<F32, 256, 256, 16, 1>()},
 };
 
 const Entry* find(int dtype, int r_k, int r_v) {
@@ -350,18 +374,15 @@ size_t valu_workspace_bytes(const lla_desc& desc, int rows, int splits) {
   return static_cast<size_t>(rows) * desc.H * splits * (2 + desc.r_v) * sizeof(float);
 }
 
-hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream) {
-  // LLA-2D decode rows (one query per sequence) take the MFMA path when it is compiled
-  if (p.variant == LLA_2D && p.rows_per_seq == 1 && !p.causal &&
-      decode2d_mfma_supported(dtype, p.r_k, p.r_v, p.d))
-    return launch_decode2d(p, stream);
-  const Entry* e = find(dtype, p.r_k, p.r_v);
-  if (e == nullptr) return hipErrorNotSupported;
+namespace {
+
+// Streaming partial kernel (contiguous or gather-indexed), then the split combine when S > 1.
+hipError_t launch_valu(const DecodeParams& p, int dtype, PartialFn fn, hipStream_t stream) {
   if (p.splits > 1 &&
       static_cast<size_t>(p.B) * p.H * p.splits * (2 + p.r_v) * sizeof(float) > p.ws_bytes)
     return hipErrorInvalidValue;  // the plan does not fit the workspace: never launch
   const unsigned units = static_cast<unsigned>(p.B) * p.H * p.splits;
-  hipLaunchKernelGGL(e->fn, dim3(units), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL(fn, dim3(units), dim3(64), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;
   if (dtype == LLA_BF16)
@@ -369,6 +390,38 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream) {
   else
     hipLaunchKernelGGL(decode_combine_kernel<F32>, dim3(p.B * p.H), dim3(64), 0, stream, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream) {
+  // LLA-2D decode rows (one query per sequence) take the MFMA path when it is compiled
+  if (p.variant == LLA_2D && p.rows_per_seq == 1 && !p.causal &&
+      decode2d_mfma_supported(dtype, p.r_k, p.r_v, p.d))
+    return launch_decode2d(p, stream);
+  const Entry* e = find(dtype, p.r_k, p.r_v);
+  if (e == nullptr) return hipErrorNotSupported;
+  return launch_valu(p, dtype, e->fn, stream);
+}
+
+void gather_plan(const lla_desc& desc, int B, int budget, int* splits, int* chunk) {
+  lla_desc g = desc;
+  g.n_max = budget;  // splits range over list positions
+  valu_plan(g, B, splits, chunk);
+}
+
+size_t gather_workspace_bytes(const lla_desc& desc, int B, int budget) {
+  int s, c;
+  gather_plan(desc, B, budget, &s, &c);
+  return valu_workspace_bytes(desc, B, s);
+}
+
+hipError_t launch_decode_gather(const DecodeParams& p, int dtype, hipStream_t stream) {
+  const Entry* e = find(dtype, p.r_k, p.r_v);
+  if (e == nullptr) return hipErrorNotSupported;
+  if (p.slots == nullptr || p.budget <= 0 || p.rows_per_seq != 1 || p.causal)
+    return hipErrorInvalidValue;
+  return launch_valu(p, dtype, e->gfn, stream);
 }
 
 }  // namespace lla

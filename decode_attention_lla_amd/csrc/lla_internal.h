@@ -33,6 +33,11 @@ struct DecodeParams {
   int32_t chunk;      // tokens per split
   float scale_log2;   // softmax scale * log2(e)
   size_t ws_bytes;    // bytes available at ws; launchers refuse a plan that does not fit
+  // Gather-indexed read (lla_attend_decode_gather): row b attends the latents at
+  // slots[b * budget + j], j < seq_lens[b] clamped to [0, budget] (all budget when seq_lens is
+  // null); a slot outside [0, n_max) is skipped. slots == nullptr: the contiguous read above.
+  const int32_t* slots;
+  int32_t budget;
 };
 
 struct EncodeParams {
@@ -82,6 +87,10 @@ size_t prefill_workspace_bytes(const lla_desc& desc, int B, int C);
 // Launchers: return hipSuccess, or hipErrorNotSupported when no kernel is compiled for the
 // requested (dtype, r_k, r_v); other errors come from the HIP launch.
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t s);
+// Gather-indexed decode (streaming kernels, both variants): plan, workspace and launch.
+void gather_plan(const lla_desc& desc, int B, int budget, int* splits, int* chunk);
+size_t gather_workspace_bytes(const lla_desc& desc, int B, int budget);
+hipError_t launch_decode_gather(const DecodeParams& p, int dtype, hipStream_t s);
 hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, hipStream_t s);
 

@@ -72,6 +72,11 @@ def _load():
     lib.lla_attend_decode.restype = _I
     lib.lla_attend_decode.argtypes = [_D, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, ctypes.c_size_t, _P]
+    lib.lla_gather_workspace_bytes.restype = ctypes.c_size_t
+    lib.lla_gather_workspace_bytes.argtypes = [_D, _I, _I]
+    lib.lla_attend_decode_gather.restype = _I
+    lib.lla_attend_decode_gather.argtypes = [_D, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P, _P,
+                                             _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.lla_attend_prefill.restype = _I
     lib.lla_attend_prefill.argtypes = [_D, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]
@@ -184,6 +189,44 @@ def lla_attend_decode(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_sel
     st = _load().lla_attend_decode(ctypes.byref(desc), int(B), int(t), *args,
                                    ctypes.c_size_t(ws_bytes), _stream_ptr(stream))
     _check(st, "lla_attend_decode")
+
+
+def lla_gather_workspace_bytes(desc, B, budget):
+    return int(_load().lla_gather_workspace_bytes(ctypes.byref(desc), int(B), int(budget)))
+
+
+def lla_attend_decode_gather(desc, B, t, q, zk, zv, slots, counts, Wk, Wv, mu_k, mu_v, k_self,
+                             v_self, out, lse=None, ws=None, stream=None):
+    dt = _TORCH_DTYPE[desc.dtype]
+    s = _shapes(desc, B)
+    qs = (B, desc.H, desc.d_head)
+    if not isinstance(slots, torch.Tensor) or slots.dim() != 2:
+        raise ValueError("slots must be a [B, budget] int32 device tensor")
+    budget = int(slots.shape[1])
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    if ws is not None and (ws.device.type != "cuda" or not ws.is_contiguous()):
+        raise ValueError("ws must be a contiguous device tensor")
+    args = [
+        _ptr(q, "q", qs, dt), _ptr(zk, "zk", s["zk"], dt), _ptr(zv, "zv", s["zv"], dt),
+        _ptr(slots, "slots", (B, budget), torch.int32), ctypes.c_int32(budget),
+        _ptr(counts, "counts", (B,), torch.int32, True),
+        _ptr(Wk, "Wk", s["Wk"], dt), _ptr(Wv, "Wv", s["Wv"], dt),
+        _ptr(mu_k, "mu_k", s["mu"], dt, True), _ptr(mu_v, "mu_v", s["mu"], dt, True),
+        _ptr(k_self, "k_self", qs, dt, True), _ptr(v_self, "v_self", qs, dt, True),
+        _ptr(out, "out", qs, dt), _ptr(lse, "lse", (B, desc.H), torch.float32, True),
+        None if ws is None else ws.data_ptr(),
+    ]
+    st = _load().lla_attend_decode_gather(ctypes.byref(desc), int(B), int(t), *args,
+                                          ctypes.c_size_t(ws_bytes), _stream_ptr(stream))
+    _check(st, "lla_attend_decode_gather")
+
+
+def gather_workspace(desc, B, budget, device="cuda"):
+    """A device workspace tensor of lla_gather_workspace_bytes(desc, B, budget) bytes (None if 0)."""
+    n = lla_gather_workspace_bytes(desc, B, budget)
+    if n == 0:
+        return None
+    return torch.empty((n + 3) // 4, dtype=torch.float32, device=device)
 
 
 def lla_attend_prefill(desc, B, C, t, q, zk, zv, ctx_lens, Wk, Wv, mu_k, mu_v, out, ws=None,

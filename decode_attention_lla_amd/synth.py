@@ -29,7 +29,7 @@ import numpy as np
 
 # tensor ids inside a case's seed block
 SEED_Q, SEED_ZK, SEED_ZV, SEED_WK, SEED_WV, SEED_EK, SEED_EV, SEED_XK, SEED_XV, SEED_SELF = range(1, 11)
-SEED_MU, SEED_LENS, SEED_SAMPLE = 11, 12, 13
+SEED_MU, SEED_LENS, SEED_SAMPLE, SEED_SLOTS = 11, 12, 13, 14
 
 
 @dataclasses.dataclass(frozen=True)
@@ -296,3 +296,27 @@ def random_case(variant: str, dtype: str, B: int, H: int, d: int, T: int, r_k: i
     else:
         out["mu_k"] = out["mu_v"] = None
     return out
+
+
+def random_slots(B: int, budget: int, n_max: int, sd: int, p_skip: float = 0.0,
+                 p_repeat: float = 0.0):
+    """Seeded slot lists [B, budget] int32 for gather-indexed reads (H2O-like arbitrary subsets).
+
+    Slots are drawn uniformly from [0, n_max) without replacement where budget <= n_max. A fraction
+    p_skip is then replaced by out-of-range values (-1 or n_max + k) and a fraction p_repeat by a
+    copy of another entry of the same row.
+    """
+    rng = np.random.default_rng(sd)
+    out = np.empty((B, budget), dtype=np.int32)
+    for b in range(B):
+        if budget <= n_max:
+            row = rng.choice(n_max, size=budget, replace=False)
+        else:
+            row = rng.integers(0, n_max, size=budget)
+        skip = rng.random(budget) < p_skip
+        row[skip] = np.where(rng.random(int(skip.sum())) < 0.5, -1, n_max + rng.integers(0, 7, int(skip.sum())))
+        rep = rng.random(budget) < p_repeat
+        row[rep] = row[rng.integers(0, budget, int(rep.sum()))]
+        out[b] = row
+    return out
+

@@ -130,6 +130,31 @@ lla_status lla_attend_decode(const lla_desc* desc, int32_t B, int32_t t, const v
                              const void* k_self, const void* v_self, void* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of device workspace that lla_attend_decode_gather needs for B rows of `budget` listed
+ * slots. May be 0; 0 as well for an invalid descriptor or size. */
+size_t lla_gather_workspace_bytes(const lla_desc* desc, int32_t B, int32_t budget);
+
+/* Decode-time attention over a listed subset of the cached latents: token eviction composed with
+ * LLA (Section 7, "Memory, capacity and latency", and Appendix C, where a StreamingLLM/H2O-style
+ * policy keeps attention sinks plus a recent window). Same arithmetic as lla_attend_decode, with
+ * row b's key set given by a slot list instead of the first N_b slots.
+ *
+ *   slots   [device] int32 [B][budget]: row b attends the cached latents at slots[b][0 ..
+ *           counts[b]-1], in any order. A slot outside [0, n_max) is skipped (never read); a slot
+ *           listed twice is two keys.
+ *   budget  list capacity per row, >= 1.
+ *   counts  [device] int32 [B] or NULL (all budget); clamped to [0, budget].
+ *   ws      [device] at least lla_gather_workspace_bytes(desc, B, budget) bytes (NULL if 0).
+ *   Other arguments as in lla_attend_decode. Both variants run on the streaming kernels, so the
+ *   compiled (r_k, r_v) pairs are the streaming ones. An empty key set (no listed slot in range and
+ *   no self token) gives out = 0 and lse = -inf. */
+lla_status lla_attend_decode_gather(const lla_desc* desc, int32_t B, int32_t t, const void* q,
+                                    const void* zk, const void* zv, const int32_t* slots,
+                                    int32_t budget, const int32_t* counts, const void* Wk,
+                                    const void* Wv, const void* mu_k, const void* mu_v,
+                                    const void* k_self, const void* v_self, void* out, float* lse,
+                                    void* ws, size_t ws_bytes, void* stream);
+
 /* Chunked-prefill attention at loop t: C query rows per sequence over the latent cache, causal.
  *
  * The chunk's own latents must already be in slots ctx_lens[b] .. ctx_lens[b]+C-1 (written by

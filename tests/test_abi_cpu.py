@@ -158,3 +158,33 @@ def test_prefill_workspace_checked_before_launch():
     need = lla.lla_workspace_bytes(d, 2, 64)
     if need > 0:
         assert prefill(d, B=2, C=64, ws=A, wsb=need - 4) == lla.LLA_ERR_WORKSPACE
+
+
+def gather(d, B=2, t=0, q=A, zk=A, zv=A, slots=A, budget=64, counts=N, Wk=A, Wv=A, ks=N, vs=N,
+           out=A, lse=N, ws=N, wsb=0):
+    lib = lla.library()
+    return lib.lla_attend_decode_gather(ctypes.byref(d), B, t, q, zk, zv, slots, budget, counts,
+                                        Wk, Wv, N, N, ks, vs, out, lse, ws, ctypes.c_size_t(wsb), S)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(slots=N), dict(slots=M), dict(budget=0), dict(budget=-4), dict(counts=M), dict(t=4),
+    dict(B=0), dict(q=N), dict(out=M), dict(ks=A), dict(B=1 << 20, budget=1 << 12),
+])
+def test_gather_rejects_bad_arguments(kw):
+    assert gather(desc(n_max=100), **kw) == lla.LLA_ERR_INVALID_ARG
+
+
+def test_gather_unsupported_and_workspace():
+    # the LLA-2D MFMA-only pairs have no streaming kernel, so no gather path
+    assert gather(desc(variant=lla.LLA_2D, r_k=64, r_v=128, n_max=100)) == lla.LLA_ERR_UNSUPPORTED
+    assert gather(desc(r_k=24, r_v=32, n_max=100)) == lla.LLA_ERR_UNSUPPORTED
+    d = desc()  # 2 x 16 units over a 4096-slot list: split-K, needs a workspace
+    need = lla.lla_gather_workspace_bytes(d, 2, 4096)
+    assert need > 0 and need % (2 * 16 * (2 + 32) * 4) == 0
+    assert gather(d, budget=4096) == lla.LLA_ERR_WORKSPACE
+    assert gather(d, budget=4096, ws=A, wsb=need - 4) == lla.LLA_ERR_WORKSPACE
+    # the split plan follows the list length, not the cache size
+    assert lla.lla_gather_workspace_bytes(d, 2, 64) == 0
+    assert lla.lla_gather_workspace_bytes(desc(H=0), 2, 64) == 0
+    assert lla.lla_gather_workspace_bytes(d, 2, 0) == 0
