@@ -371,3 +371,51 @@ def attend_decode_gather(q, zk, zv, Wk, Wv, t, slots, counts=None, mu_k=None, mu
                 V = np.concatenate([V, v_self[b, h][None, :]], axis=0)
             o[b, h], lse[b, h] = softmax_attention(q[b, h], K, V, scale)
     return o, lse
+
+
+# --------------------------------------------------------------------------------------------
+# Low-bit latent storage: the precision axis stacked on the loop axis (Section 8,
+# "Compositionality": quantisation changes a different tensor dimension and can be stacked;
+# Appendix C evaluates an 8-bit codec)
+# --------------------------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_round(v):
+    """Round to the nearest OCP FP8 E4M3 value (4 exponent bits with bias 7, 3 mantissa bits,
+    subnormals, largest finite 448, no infinities), ties to even.
+
+    Inside a binade [2^e, 2^(e+1)) with e >= -6 the spacing is 2^(e-3); below 2^-6 it is the
+    subnormal spacing 2^-9. A value whose rounding would exceed 448 has no E4M3 encoding and
+    becomes NaN. Returns float64 values.
+    """
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.clip(e, -6, 8)
+    step = 2.0 ** (e - 3)
+    r = np.round(a / step) * step  # numpy rounds halves to even; a / step is exact
+    r = np.where(r > E4M3_MAX, np.nan, r)
+    return np.copysign(r, v)
+
+
+def quantize_latent_rows(z):
+    """Low-bit latent rows: each row of r latent values (the last axis) is stored as r E4M3 codes
+    and one float32 scale s = max|z| / 448, code_j = e4m3(z_j / s), both divisions in float32
+    (a row of zeros has s = 0 and zero codes). Returns (codes as float64 values, scales as float64
+    holding float32 values)."""
+    z32 = np.asarray(z, np.float32)
+    amax = np.max(np.abs(z32), axis=-1)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    v = (z32 / safe[..., None]).astype(np.float32)
+    codes = e4m3_round(v.astype(np.float64))
+    codes = np.where((s > 0)[..., None], codes, 0.0)
+    return codes, s.astype(np.float64)
+
+
+def dequantize_latent_rows(codes, scales):
+    """The latent values a low-bit row stands for: code_j * s (exact in float64)."""
+    return np.asarray(codes, np.float64) * np.asarray(scales, np.float64)[..., None]

@@ -12,6 +12,7 @@ import pytest
 from oracle import lla_oracle as O
 import tests.test_oracle_pins as P
 import tests.test_oracle_gather as G
+import tests.test_oracle_q8 as Q
 
 
 def _encode_no_centre(x_stack, E, mu=None):
@@ -91,12 +92,39 @@ def _gather_wraps_out_of_range(q, zk, zv, Wk, Wv, t, slots, counts=None, variant
                                          variant=variant, **kw)
 
 
+def _e4m3_truncates(v):
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    with np.errstate(divide="ignore"):
+        e = np.clip(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6, 8)
+    step = 2.0 ** (e - 3)
+    r = np.floor(a / step) * step
+    return np.copysign(np.where(r > 448, np.nan, r), v)
+
+
+def _e4m3_bias8(v):
+    # the exponent bias of the other FP8 E4M3 family (largest finite 240)
+    r = _orig["e4m3_round"](np.asarray(v, np.float64) * 2.0) / 2.0
+    return np.where(np.abs(r) > 240, np.nan, r)
+
+
+def _quantize_scale_for_240(z):
+    # scale sized for the other family's largest finite value (240) instead of 448
+    z32 = np.asarray(z, np.float32)
+    s = (np.max(np.abs(z32), axis=-1) / np.float32(240.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    codes = O.e4m3_round((z32 / safe[..., None]).astype(np.float32).astype(np.float64))
+    return np.where((s > 0)[..., None], codes, 0.0), s.astype(np.float64)
+
+
 _orig = {
     "encode_stack": O.encode_stack,
     "reconstruct": O.reconstruct,
     "softmax_attention": O.softmax_attention,
     "_loop_slices": O._loop_slices,
     "attend_decode_gather": O.attend_decode_gather,
+    "e4m3_round": O.e4m3_round,
+    "quantize_latent_rows": O.quantize_latent_rows,
 }
 
 MUTANTS = {
@@ -113,6 +141,9 @@ MUTANTS = {
     "gather drops the last listed slot": ("attend_decode_gather", _gather_drop_last),
     "gather attends a repeated slot once": ("attend_decode_gather", _gather_dedup),
     "gather wraps out-of-range slots": ("attend_decode_gather", _gather_wraps_out_of_range),
+    "e4m3 truncates instead of rounding": ("e4m3_round", _e4m3_truncates),
+    "e4m3 uses exponent bias 8": ("e4m3_round", _e4m3_bias8),
+    "quantiser scales for 240 instead of 448": ("quantize_latent_rows", _quantize_scale_for_240),
 }
 
 PINS = [
@@ -128,6 +159,9 @@ PINS = [
     G.test_full_rank_codec_equals_sdpa_on_kept_tokens,
     G.test_brute_force_tiny_with_duplicates_and_skips,
     G.test_empty_lists,
+    Q.test_every_e4m3_value_rounds_to_itself,
+    Q.test_rounding_matches_torch_float8_e4m3fn,
+    Q.test_quantized_rows_bound_and_extremes,
 ]
 
 
