@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblla.so")
 
-SOURCES = ["abi.cpp", "decode.hip", "decode2d.hip", "encode.hip", "prefill.hip"]
+SOURCES = ["abi.cpp", "decode.hip", "decode2d.hip", "encode.hip", "prefill.hip", "quant.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -19,7 +19,7 @@ bool req_ok(const void* p) { return p != nullptr && aligned16(p); }
 bool desc_ok(const lla_desc* d) {
   if (d == nullptr) return false;
   if (d->variant != LLA_PER_HEAD && d->variant != LLA_2D) return false;
-  if (d->dtype != LLA_F32 && d->dtype != LLA_BF16) return false;
+  if (d->dtype != LLA_F32 && d->dtype != LLA_BF16 && d->dtype != LLA_BF16_Q8) return false;
   if (d->H <= 0 || d->T <= 0 || d->r_k <= 0 || d->r_v <= 0 || d->n_max <= 0) return false;
   if (d->d_head <= 0 || d->d_head > 256 || (d->d_head % 8) != 0) return false;
   if (!(d->scale >= 0.f) || std::isinf(d->scale)) return false;
@@ -108,6 +108,43 @@ const char* lla_status_string(lla_status s) {
     case LLA_ERR_HIP: return "HIP launch error";
   }
   return "unknown status";
+}
+
+size_t lla_latent_row_bytes(int32_t dtype, int32_t r) {
+  if (r <= 0) return 0;
+  switch (dtype) {
+    case LLA_F32: return 4 * static_cast<size_t>(r);
+    case LLA_BF16: return 2 * static_cast<size_t>(r);
+    case LLA_BF16_Q8: return (static_cast<size_t>(r) + 4 + 15) / 16 * 16;
+  }
+  return 0;
+}
+
+lla_status lla_quantize_latents(const lla_desc* desc, int32_t B, int32_t C, const void* zk_src,
+                                const void* zv_src, const int32_t* pos, void* zk, void* zv,
+                                void* stream) {
+  if (!desc_ok(desc) || desc->dtype != LLA_BF16_Q8 || B <= 0 || C <= 0 || C > desc->n_max)
+    return LLA_ERR_INVALID_ARG;
+  if (desc->r_k > 512 || desc->r_v > 512) return LLA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * C * desc->H >= (int64_t(1) << 31)) return LLA_ERR_INVALID_ARG;
+  if (!req_ok(zk_src) || !req_ok(zv_src) || !req_ok(pos) || !req_ok(zk) || !req_ok(zv))
+    return LLA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  lla::QuantParams p{};
+  p.pos = pos;
+  p.B = B;
+  p.C = C;
+  p.H = desc->variant == LLA_PER_HEAD ? desc->H : 1;
+  p.n_max = desc->n_max;
+  p.src = zk_src;
+  p.dst = zk;
+  p.r = desc->r_k;
+  lla_status st = from_hip(lla::launch_quantize(p, s));
+  if (st != LLA_OK) return st;
+  p.src = zv_src;
+  p.dst = zv;
+  p.r = desc->r_v;
+  return from_hip(lla::launch_quantize(p, s));
 }
 
 size_t lla_workspace_bytes(const lla_desc* desc, int32_t B, int32_t C) {

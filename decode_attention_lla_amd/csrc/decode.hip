@@ -11,6 +11,8 @@
 //   4. merge lanes, then either write a split partial (m, l, a) or finish: merge the optional
 //      self token, apply W^V_t once, add l * mu^V_t, normalise and store o and lse.
 // The reconstructed K/V of cached tokens are never formed.
+#include <type_traits>
+
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -89,16 +91,23 @@ __device__ void finish_unit(const DecodeParams& p, int b, int h, float M, float 
 // One wave per (b, h, split). LPT lanes share a token; each holds EK = RK/LPT K elements and
 // EV = RV/LPT V elements. U tiles of 64/LPT tokens are loaded before any is consumed. With G the
 // split ranges over the row's slot list instead of its first N latents: each token's slot is read
-// first, and a slot outside [0, n_max) counts as masked.
-template <class S, int RK, int RV, int LPT, int U, bool G>
+// first, and a slot outside [0, n_max) counts as masked. S is the storage of q, W, mu, the self
+// token and out; LS that of the latent rows (S itself, or Q8 low-bit rows read whole by one lane:
+// the K row scale multiplies the score, the V row scale the token's weight).
+template <class S, class LS, int RK, int RV, int LPT, int U, bool G>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
+  constexpr bool kQ8 = std::is_same<LS, Q8>::value;
   constexpr int EK = RK / LPT;
   constexpr int EV = RV / LPT;
   constexpr int TPW = 64 / LPT;
-  constexpr int VK = EK * S::kBytes / 16;
-  constexpr int VV = EV * S::kBytes / 16;
+  constexpr int RKB = LS::row(RK);  // bytes per latent row
+  constexpr int RVB = LS::row(RV);
+  constexpr int VK = kQ8 ? RKB / 16 : EK * LS::kBytes / 16;
+  constexpr int VV = kQ8 ? RVB / 16 : EV * LS::kBytes / 16;
   static_assert(EK * LPT == RK && EV * LPT == RV, "rank must split evenly over lanes");
-  static_assert(VK * 16 == EK * S::kBytes && VV * 16 == EV * S::kBytes, "16-byte fragments");
+  static_assert(!kQ8 || LPT == 1, "low-bit rows are read whole by one lane");
+  static_assert(kQ8 || (VK * 16 == EK * LS::kBytes && VV * 16 == EV * LS::kBytes),
+                "16-byte fragments");
 
   __shared__ float q_s[256];
   __shared__ float qt_s[RK];
@@ -142,8 +151,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
 
   // --- 2-3. latent stream with online softmax -------------------------------------------------
   const size_t lrow = latent_row(p, b / p.rows_per_seq, h);
-  const char* zkp = static_cast<const char*>(p.zk) + (lrow * RK + sub * EK) * S::kBytes;
-  const char* zvp = static_cast<const char*>(p.zv) + (lrow * RV + sub * EV) * S::kBytes;
+  const char* zkp = static_cast<const char*>(p.zk) + lrow * RKB + sub * EK * LS::kBytes;
+  const char* zvp = static_cast<const char*>(p.zv) + lrow * RVB + sub * EV * LS::kBytes;
 
   const int32_t* srow = G ? p.slots + static_cast<size_t>(b) * p.budget : nullptr;
 
@@ -171,8 +180,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (ok[u]) {
-        const uint4* kp = reinterpret_cast<const uint4*>(zkp + static_cast<size_t>(slot[u]) * RK * S::kBytes);
-        const uint4* vp = reinterpret_cast<const uint4*>(zvp + static_cast<size_t>(slot[u]) * RV * S::kBytes);
+        const uint4* kp = reinterpret_cast<const uint4*>(zkp + static_cast<size_t>(slot[u]) * RKB);
+        const uint4* vp = reinterpret_cast<const uint4*>(zvp + static_cast<size_t>(slot[u]) * RVB);
 #pragma unroll
         for (int i = 0; i < VK; ++i) kr[u][i] = kp[i];
 #pragma unroll
@@ -186,9 +195,16 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if constexpr (kQ8) {
+        // the last 16 bytes of a low-bit row hold padding the arithmetic never reads; without
+        // this the compiler narrows their load and a row takes three partial loads, not two
+        asm("" : "+v"(kr[u][VK - 1].x), "+v"(kr[u][VK - 1].y), "+v"(kr[u][VK - 1].z));
+        asm("" : "+v"(vr[u][VV - 1].x), "+v"(vr[u][VV - 1].y), "+v"(vr[u][VV - 1].z));
+      }
       float sc = 0.f;
 #pragma unroll
-      for (int e = 0; e < EK; ++e) sc += qt[e] * frag_elem<S>(kr[u], e);
+      for (int e = 0; e < EK; ++e) sc += qt[e] * frag_elem<LS>(kr[u], e);
+      if (kQ8) sc *= q8_row_scale(kr[u], VK);
 #pragma unroll
       for (int o = 1; o < LPT; o <<= 1) sc += __shfl_xor(sc, o, 64);
       sc += beta;
@@ -202,8 +218,9 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
         }
         const float pr = fast_exp2(sc - m);
         l += pr;
+        const float pv = kQ8 ? pr * q8_row_scale(vr[u], VV) : pr;
 #pragma unroll
-        for (int e = 0; e < EV; ++e) acc[e] += pr * frag_elem<S>(vr[u], e);
+        for (int e = 0; e < EV; ++e) acc[e] += pv * frag_elem<LS>(vr[u], e);
       }
     }
   }
@@ -281,11 +298,19 @@ using PartialFn = void (*)(DecodeParams);
 
 template <class S, int RK, int RV, int LPT, int U>
 PartialFn partial_fn() {
-  return decode_partial_kernel<S, RK, RV, LPT, U, false>;
+  return decode_partial_kernel<S, S, RK, RV, LPT, U, false>;
 }
 template <class S, int RK, int RV, int LPT, int U>
 PartialFn gather_fn() {
-  return decode_partial_kernel<S, RK, RV, LPT, U, true>;
+  return decode_partial_kernel<S, S, RK, RV, LPT, U, true>;
+}
+template <int RK, int RV, int U>
+PartialFn q8_fn() {
+  return decode_partial_kernel<BF16, Q8, RK, RV, 1, U, false>;
+}
+template <int RK, int RV, int U>
+PartialFn q8_gather_fn() {
+  return decode_partial_kernel<BF16, Q8, RK, RV, 1, U, true>;
 }
 
 struct Entry {
@@ -314,6 +339,10 @@ const Entry kTable[] = {
     {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 8, 1>(), gather_fn<F32, 128, 128, 8, 1>()},
     {LLA_F32, 96, 160, partial_fn<F32, 96, 160, 8, 1>(), gather_fn<F32, 96, 160, 8, 1>()},
     {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 16, 1>(), gather_fn<F32, 256, 256, 16, 1>()},
+    {LLA_BF16_Q8, 8, 8, q8_fn<8, 8, 4>(), q8_gather_fn<8, 8, 4>()},
+    {LLA_BF16_Q8, 16, 16, q8_fn<16, 16, 4>(), q8_gather_fn<16, 16, 4>()},
+    {LLA_BF16_Q8, 24, 24, q8_fn<24, 24, 3>(), q8_gather_fn<24, 24, 3>()},
+    {LLA_BF16_Q8, 32, 32, q8_fn<32, 32, 2>(), q8_gather_fn<32, 32, 2>()},
 };
 
 const Entry* find(int dtype, int r_k, int r_v) {
@@ -385,7 +414,7 @@ hipError_t launch_valu(const DecodeParams& p, int dtype, PartialFn fn, hipStream
   hipLaunchKernelGGL(fn, dim3(units), dim3(64), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;
-  if (dtype == LLA_BF16)
+  if (dtype == LLA_BF16 || dtype == LLA_BF16_Q8)
     hipLaunchKernelGGL(decode_combine_kernel<BF16>, dim3(p.B * p.H), dim3(64), 0, stream, p);
   else
     hipLaunchKernelGGL(decode_combine_kernel<F32>, dim3(p.B * p.H), dim3(64), 0, stream, p);

@@ -5,14 +5,22 @@
 
 namespace lla {
 
-// Storage tags. bf16 values are carried as raw 16-bit patterns.
+// Storage tags. bf16 values are carried as raw 16-bit patterns. row(r): bytes of a latent row.
 struct F32 {
   using T = float;
   static constexpr int kBytes = 4;
+  static constexpr int row(int r) { return 4 * r; }
 };
 struct BF16 {
   using T = uint16_t;
   static constexpr int kBytes = 2;
+  static constexpr int row(int r) { return 2 * r; }
+};
+// Low-bit latent rows: r OCP FP8 E4M3 codes, zero padding, the row's float32 scale in the last 4
+// bytes, rounded up to 16 bytes. Only latent caches use it; the other arrays of such a call are bf16.
+struct Q8 {
+  static constexpr int kBytes = 1;
+  static constexpr int row(int r) { return (r + 4 + 15) / 16 * 16; }
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -83,6 +91,22 @@ __device__ __forceinline__ float frag_elem<BF16>(const uint4* f, int e) {
   const uint32_t x = k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w;
   return (e & 1) ? bf16_hi(x) : bf16_lo(x);
 }
+
+template <>
+__device__ __forceinline__ float frag_elem<Q8>(const uint4* f, int e) {
+  const uint4 w = f[e >> 4];
+  const int k = (e & 15) >> 2;
+  const uint32_t x = k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w;
+  // hardware E4M3 -> f32 of byte e % 4 (the byte select must be a literal)
+  switch (e & 3) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(x), 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(x), 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(x), 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(x), 3);
+  }
+}
+// The float32 scale of a low-bit row held as V 16-byte words.
+__device__ __forceinline__ float q8_row_scale(const uint4* f, int V) { return __uint_as_float(f[V - 1].w); }
 
 // 16-byte load of data that is read exactly once, for loads whose 64 lanes cover whole cache
 // lines (one instruction reads 1 KiB contiguous): a non-temporal hint keeps the stream from

@@ -49,6 +49,14 @@ struct EncodeParams {
   int32_t B, C, H, d, T, r, n_max;
 };
 
+// Quantisation of bf16 latent rows into a low-bit cache (lla_quantize_latents, one axis).
+struct QuantParams {
+  const void* src;     // bf16 [B][H][C][r] (LLA-2D: H = 1)
+  void* dst;           // low-bit cache [B][H][n_max][Q8::row(r)] bytes
+  const int32_t* pos;  // [B]
+  int32_t B, C, H, r, n_max;
+};
+
 struct PrefillParams {
   const void* q;      // [B][C][H][d]
   const void* zk;
@@ -92,6 +100,7 @@ void gather_plan(const lla_desc& desc, int B, int budget, int* splits, int* chun
 size_t gather_workspace_bytes(const lla_desc& desc, int B, int budget);
 hipError_t launch_decode_gather(const DecodeParams& p, int dtype, hipStream_t s);
 hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t s);
+hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, hipStream_t s);
 
 bool decode_supported(int variant, int dtype, int r_k, int r_v, int d_head);

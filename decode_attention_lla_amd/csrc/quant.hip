@@ -1,0 +1,69 @@
+// Low-bit latent rows (LLA_BF16_Q8): bf16 latent rows quantised to OCP FP8 E4M3 codes with one
+// float32 scale per row, written into a low-bit cache.
+//
+// Method context: O'Neill & Reid, "Looped Latent Attention", arXiv 2607.15456. Section 8
+// ("Compositionality") notes that quantisation acts on a different tensor dimension than the loop
+// codec and can be stacked on it; Appendix C evaluates an 8-bit codec. The row format is stated at
+// LLA_BF16_Q8 in lla.h: s = max|z| / 448, code_j = e4m3(z_j / s), both divisions in float32 and
+// rounded to nearest even (gfx950's v_cvt_pk_fp8_f32 rounds to nearest even in the OCP E4M3
+// format), codes at bytes [0, r), zero padding, s in the last 4 bytes of a 16-byte-aligned row.
+#include <hip/hip_runtime.h>
+
+#include "lla_device.h"
+#include "lla_internal.h"
+
+namespace lla {
+namespace {
+
+constexpr int kThreads = 256;
+
+// One thread per source row (b, h, c): per-head source [B][H][C][r] (LLA-2D: H = 1).
+__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QuantParams p) {
+  const long row = static_cast<long>(blockIdx.x) * kThreads + threadIdx.x;
+  const long rows = static_cast<long>(p.B) * p.H * p.C;
+  if (row >= rows) return;
+  const int c = static_cast<int>(row % p.C);
+  const long bh = row / p.C;
+  const int h = static_cast<int>(bh % p.H);
+  const int b = static_cast<int>(bh / p.H);
+  const int slot = p.pos[b] + c;
+  if (slot < 0 || slot >= p.n_max) return;
+
+  const uint16_t* src = static_cast<const uint16_t*>(p.src) + row * p.r;
+  float amax = 0.f;
+  for (int j = 0; j < p.r; ++j) amax = fmaxf(amax, fabsf(__uint_as_float(uint32_t(src[j]) << 16)));
+  const float s = amax / 448.0f;
+
+  const int row_bytes = Q8::row(p.r);
+  uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(p.dst) +
+                                        ((static_cast<size_t>(b) * p.H + h) * p.n_max + slot) * row_bytes);
+  const int chunks = row_bytes / 16;
+  for (int k = 0; k < chunks; ++k) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 16 * k + 4 * q + e;
+        v[e] = (j < p.r && s > 0.f) ? __uint_as_float(uint32_t(src[j]) << 16) / s : 0.f;
+      }
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);  // bytes 0, 1
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);     // bytes 2, 3
+      w[q] = static_cast<uint32_t>(word);
+    }
+    if (k == chunks - 1) w[3] = __float_as_uint(s);  // codes never reach the last word
+    dst[k] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantParams& p, hipStream_t stream) {
+  const long rows = static_cast<long>(p.B) * p.H * p.C;
+  const unsigned blocks = static_cast<unsigned>((rows + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3(blocks), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace lla

@@ -17,10 +17,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblla.so")
 
 LLA_OK, LLA_ERR_INVALID_ARG, LLA_ERR_UNSUPPORTED, LLA_ERR_WORKSPACE, LLA_ERR_HIP = range(5)
-LLA_F32, LLA_BF16 = 0, 1
+LLA_F32, LLA_BF16, LLA_BF16_Q8 = 0, 1, 2
 LLA_PER_HEAD, LLA_2D = 0, 1
 
-_TORCH_DTYPE = {LLA_F32: torch.float32, LLA_BF16: torch.bfloat16}
+# dtype of the arithmetic arrays (q, W, E, mu, x, self K/V, out); LLA_BF16_Q8 latent caches are
+# uint8 rows of lla_latent_row_bytes bytes
+_TORCH_DTYPE = {LLA_F32: torch.float32, LLA_BF16: torch.bfloat16, LLA_BF16_Q8: torch.bfloat16}
 
 
 class lla_desc(ctypes.Structure):
@@ -65,6 +67,10 @@ def _load():
     lib.lla_abi_version.argtypes = []
     lib.lla_status_string.restype = ctypes.c_char_p
     lib.lla_status_string.argtypes = [_I]
+    lib.lla_latent_row_bytes.restype = ctypes.c_size_t
+    lib.lla_latent_row_bytes.argtypes = [_I, _I]
+    lib.lla_quantize_latents.restype = _I
+    lib.lla_quantize_latents.argtypes = [_D, _I, _I, _P, _P, _P, _P, _P, _P]
     lib.lla_workspace_bytes.restype = ctypes.c_size_t
     lib.lla_workspace_bytes.argtypes = [_D, _I, _I]
     lib.lla_encode.restype = _I
@@ -124,13 +130,24 @@ def _ptr(t, name, shape, dtype, optional=False):
     return t.data_ptr()
 
 
+def _q8_row(r):
+    return (r + 4 + 15) // 16 * 16
+
+
 def _shapes(desc, B):
+    """Shapes of the descriptor's arrays; for LLA_BF16_Q8 the cache rows are bytes."""
     H, d, T, rk, rv, n = desc.H, desc.d_head, desc.T, desc.r_k, desc.r_v, desc.n_max
+    lk, lv = (_q8_row(rk), _q8_row(rv)) if desc.dtype == LLA_BF16_Q8 else (rk, rv)
     if desc.variant == LLA_PER_HEAD:
-        return dict(zk=(B, H, n, rk), zv=(B, H, n, rv), Wk=(T, H, d, rk), Wv=(T, H, d, rv),
+        return dict(zk=(B, H, n, lk), zv=(B, H, n, lv), Wk=(T, H, d, rk), Wv=(T, H, d, rv),
                     Ek=(H, rk, T * d), Ev=(H, rv, T * d), mu=(H, T * d))
-    return dict(zk=(B, n, rk), zv=(B, n, rv), Wk=(T, H * d, rk), Wv=(T, H * d, rv),
+    return dict(zk=(B, n, lk), zv=(B, n, lv), Wk=(T, H * d, rk), Wv=(T, H * d, rv),
                 Ek=(rk, T * H * d), Ev=(rv, T * H * d), mu=(T * H * d,))
+
+
+def _zdt(desc):
+    """dtype of the latent cache tensors."""
+    return torch.uint8 if desc.dtype == LLA_BF16_Q8 else _TORCH_DTYPE[desc.dtype]
 
 
 def _check(status, where):
@@ -150,6 +167,26 @@ def lla_status_string(status):
     return _load().lla_status_string(int(status)).decode()
 
 
+def lla_latent_row_bytes(dtype, r):
+    return int(_load().lla_latent_row_bytes(int(dtype), int(r)))
+
+
+def lla_quantize_latents(desc, B, C, zk_src, zv_src, pos, zk, zv, stream=None):
+    s = _shapes(desc, B)
+    if desc.variant == LLA_PER_HEAD:
+        sk, sv = (B, desc.H, C, desc.r_k), (B, desc.H, C, desc.r_v)
+    else:
+        sk, sv = (B, C, desc.r_k), (B, C, desc.r_v)
+    args = [
+        _ptr(zk_src, "zk_src", sk, torch.bfloat16), _ptr(zv_src, "zv_src", sv, torch.bfloat16),
+        _ptr(pos, "pos", (B,), torch.int32),
+        _ptr(zk, "zk", s["zk"], torch.uint8), _ptr(zv, "zv", s["zv"], torch.uint8),
+    ]
+    st = _load().lla_quantize_latents(ctypes.byref(desc), int(B), int(C), *args,
+                                      _stream_ptr(stream))
+    _check(st, "lla_quantize_latents")
+
+
 def lla_workspace_bytes(desc, B, C=1):
     return int(_load().lla_workspace_bytes(ctypes.byref(desc), int(B), int(C)))
 
@@ -163,7 +200,7 @@ def lla_encode(desc, B, C, xk, xv, Ek, Ev, mu_k, mu_v, pos, zk, zv, stream=None)
         _ptr(Ek, "Ek", s["Ek"], dt), _ptr(Ev, "Ev", s["Ev"], dt),
         _ptr(mu_k, "mu_k", s["mu"], dt, True), _ptr(mu_v, "mu_v", s["mu"], dt, True),
         _ptr(pos, "pos", (B,), torch.int32),
-        _ptr(zk, "zk", s["zk"], dt), _ptr(zv, "zv", s["zv"], dt),
+        _ptr(zk, "zk", s["zk"], _zdt(desc)), _ptr(zv, "zv", s["zv"], _zdt(desc)),
     ]
     st = _load().lla_encode(ctypes.byref(desc), int(B), int(C), *args, _stream_ptr(stream))
     _check(st, "lla_encode")
@@ -178,7 +215,7 @@ def lla_attend_decode(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_sel
     if ws is not None and (ws.device.type != "cuda" or not ws.is_contiguous()):
         raise ValueError("ws must be a contiguous device tensor")
     args = [
-        _ptr(q, "q", qs, dt), _ptr(zk, "zk", s["zk"], dt), _ptr(zv, "zv", s["zv"], dt),
+        _ptr(q, "q", qs, dt), _ptr(zk, "zk", s["zk"], _zdt(desc)), _ptr(zv, "zv", s["zv"], _zdt(desc)),
         _ptr(seq_lens, "seq_lens", (B,), torch.int32, True),
         _ptr(Wk, "Wk", s["Wk"], dt), _ptr(Wv, "Wv", s["Wv"], dt),
         _ptr(mu_k, "mu_k", s["mu"], dt, True), _ptr(mu_v, "mu_v", s["mu"], dt, True),
@@ -207,7 +244,7 @@ def lla_attend_decode_gather(desc, B, t, q, zk, zv, slots, counts, Wk, Wv, mu_k,
     if ws is not None and (ws.device.type != "cuda" or not ws.is_contiguous()):
         raise ValueError("ws must be a contiguous device tensor")
     args = [
-        _ptr(q, "q", qs, dt), _ptr(zk, "zk", s["zk"], dt), _ptr(zv, "zv", s["zv"], dt),
+        _ptr(q, "q", qs, dt), _ptr(zk, "zk", s["zk"], _zdt(desc)), _ptr(zv, "zv", s["zv"], _zdt(desc)),
         _ptr(slots, "slots", (B, budget), torch.int32), ctypes.c_int32(budget),
         _ptr(counts, "counts", (B,), torch.int32, True),
         _ptr(Wk, "Wk", s["Wk"], dt), _ptr(Wv, "Wv", s["Wv"], dt),
@@ -238,7 +275,7 @@ def lla_attend_prefill(desc, B, C, t, q, zk, zv, ctx_lens, Wk, Wv, mu_k, mu_v, o
     if ws is not None and (ws.device.type != "cuda" or not ws.is_contiguous()):
         raise ValueError("ws must be a contiguous device tensor")
     args = [
-        _ptr(q, "q", qs, dt), _ptr(zk, "zk", s["zk"], dt), _ptr(zv, "zv", s["zv"], dt),
+        _ptr(q, "q", qs, dt), _ptr(zk, "zk", s["zk"], _zdt(desc)), _ptr(zv, "zv", s["zv"], _zdt(desc)),
         _ptr(ctx_lens, "ctx_lens", (B,), torch.int32),
         _ptr(Wk, "Wk", s["Wk"], dt), _ptr(Wv, "Wv", s["Wv"], dt),
         _ptr(mu_k, "mu_k", s["mu"], dt, True), _ptr(mu_v, "mu_v", s["mu"], dt, True),

@@ -188,3 +188,38 @@ def test_gather_unsupported_and_workspace():
     assert lla.lla_gather_workspace_bytes(d, 2, 64) == 0
     assert lla.lla_gather_workspace_bytes(desc(H=0), 2, 64) == 0
     assert lla.lla_gather_workspace_bytes(d, 2, 0) == 0
+
+
+def test_latent_row_bytes():
+    f = lla.lla_latent_row_bytes
+    assert (f(lla.LLA_F32, 24), f(lla.LLA_BF16, 24), f(lla.LLA_BF16_Q8, 24)) == (96, 48, 32)
+    assert [f(lla.LLA_BF16_Q8, r) for r in (1, 8, 12, 13, 16, 28, 32, 256)] == \
+        [16, 16, 16, 32, 32, 32, 48, 272]
+    assert f(7, 8) == 0 and f(lla.LLA_BF16_Q8, 0) == 0
+
+
+def quantize(d, B=2, C=1, ks=A, vs=A, pos=A, zk=A, zv=A):
+    return lla.library().lla_quantize_latents(ctypes.byref(d), B, C, ks, vs, pos, zk, zv, S)
+
+
+@pytest.mark.parametrize("kw,dkw", [
+    (dict(), dict(dtype=lla.LLA_BF16)), (dict(B=0), {}), (dict(C=0), {}), (dict(C=101), {}),
+    (dict(ks=N), {}), (dict(vs=M), {}), (dict(pos=N), {}), (dict(zk=M), {}), (dict(zv=N), {}),
+    (dict(), dict(r_k=513)),
+])
+def test_quantize_rejects_bad_arguments(kw, dkw):
+    base = dict(dtype=lla.LLA_BF16_Q8, n_max=100, r_k=24, r_v=24)
+    base.update(dkw)
+    assert quantize(desc(**base), **kw) == lla.LLA_ERR_INVALID_ARG
+
+
+def test_low_bit_support_matrix():
+    q8 = dict(dtype=lla.LLA_BF16_Q8, n_max=100)
+    assert encode(desc(r_k=24, r_v=24, **q8)) == lla.LLA_ERR_UNSUPPORTED
+    assert decode(desc(r_k=64, r_v=64, **q8)) == lla.LLA_ERR_UNSUPPORTED
+    assert gather(desc(r_k=96, r_v=160, **q8)) == lla.LLA_ERR_UNSUPPORTED
+    assert prefill(desc(r_k=128, r_v=128, **q8)) == lla.LLA_ERR_UNSUPPORTED
+    assert decode(desc(variant=lla.LLA_2D, r_k=256, r_v=256, **q8)) == lla.LLA_ERR_UNSUPPORTED
+    # same split plan and workspace as bf16 storage on the streaming path
+    assert lla.lla_workspace_bytes(desc(r_k=32, r_v=32, dtype=lla.LLA_BF16_Q8), 32, 1) == \
+        lla.lla_workspace_bytes(desc(r_k=32, r_v=32), 32, 1)
