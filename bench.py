@@ -60,6 +60,8 @@ def parse():
                     help="measure only the gather-indexed (token-eviction) decode read")
     ap.add_argument("--only-low-bit", action="store_true",
                     help="measure only the capacity step with low-bit (E4M3 + scale) latent rows")
+    ap.add_argument("--only-long-context", action="store_true",
+                    help="measure only the 262k-token absorbed read against reconstruct-then-attend")
     return ap.parse_args()
 
 
@@ -110,6 +112,9 @@ def main():
         return
     if args.only_low_bit:
         print(json.dumps({"low_bit_capacity": low_bit_capacity(args, None)}), flush=True)
+        return
+    if args.only_long_context:
+        print(json.dumps({"long_context_262k": long_context(args)}), flush=True)
         return
     s = synth.CASES[args.workload]
     D = args.layers or s.D
@@ -225,7 +230,8 @@ def main():
         torch.cuda.empty_cache()
         extras = {"lla2d_decode": lla2d_decode(args), "lla2d_prefill": lla2d_prefill(args),
                   "eviction_decode": eviction_decode(args),
-                  "low_bit_capacity": low_bit_capacity(args, tokens_per_s)}
+                  "low_bit_capacity": low_bit_capacity(args, tokens_per_s),
+                  "long_context_262k": long_context(args)}
 
     res = {
         "metric": METRIC,
@@ -460,6 +466,51 @@ def low_bit_capacity(args, bf16_tokens_per_s):
     if bf16_tokens_per_s:
         res["speedup_vs_bf16_latents"] = round(B / (ms_step / 1e3) / bf16_tokens_per_s, 3)
     return res
+
+
+def long_context(args):
+    """The paper's only speed ratio (Section 7): at 262k cached tokens and the 4x geometry (H=16,
+    d=128, T=4, r_k/r_v = 96/160), one decode read in absorbed form (lla_attend_decode) against
+    reconstruct-then-attend (lla_attend_decode_reconstruct: rebuild K_t and V_t of every token in
+    bf16, then attend). B=1."""
+    import torch
+    from decode_attention_lla_amd import lla, synth
+    B, H, d, T, rk, rv, N = 1, 16, 128, 4, 96, 160, 262144
+    n_max = N + 1
+    bf = torch.bfloat16
+    desc = lla.make_desc(lla.LLA_PER_HEAD, lla.LLA_BF16, H, d, T, rk, rv, n_max)
+    sd = 9800
+    zk = synth.device_normal_(torch.empty(B, H, n_max, rk, dtype=bf, device="cuda"), sd + 1)
+    zv = synth.device_normal_(torch.empty(B, H, n_max, rv, dtype=bf, device="cuda"), sd + 2)
+    Wk = synth.device_normal_(torch.empty(T, H, d, rk, dtype=bf, device="cuda"), sd + 3, 1 / rk ** 0.5)
+    Wv = synth.device_normal_(torch.empty(T, H, d, rv, dtype=bf, device="cuda"), sd + 4, 1 / rv ** 0.5)
+    q = synth.device_normal_(torch.empty(B, H, d, dtype=bf, device="cuda"), sd + 5)
+    out = torch.empty_like(q)
+    lens = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    ws_a = lla.workspace(desc, B)
+    ws_r = lla.reconstruct_workspace(desc, B)
+
+    def absorbed():
+        lla.lla_attend_decode(desc, B, 1, q, zk, zv, lens, Wk, Wv, None, None, None, None, out,
+                              None, ws_a)
+
+    def rebuilt():
+        lla.lla_attend_decode_reconstruct(desc, B, 1, q, zk, zv, lens, Wk, Wv, None, None, None,
+                                          None, out, None, ws_r)
+
+    ms_a = _timed(absorbed, 20, 3)
+    ms_r = _timed(rebuilt, 10, 2)
+    latent = B * H * N * (rk + rv) * 2
+    kv = B * H * N * 2 * d * 2
+    return {"workload": f"one decode read at {N} cached tokens: B={B}, H={H}, d_head={d}, T={T}, "
+                        f"r_k={rk}, r_v={rv} (4x), bf16",
+            "absorbed_us": round(ms_a * 1e3, 2),
+            "absorbed_latent_GBps": round(latent / (ms_a / 1e3) / 1e9, 1),
+            "absorbed_frac_of_peak": round(latent / (ms_a / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "reconstruct_then_attend_us": round(ms_r * 1e3, 2),
+            "reconstruct_hbm_bytes_algorithmic": latent + 2 * kv,
+            "absorbed_speedup": round(ms_r / ms_a, 3),
+            "paper_absorbed_speedup_H200": 2.3}
 
 
 def lla2d_prefill(args):

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblla.so")
 
-SOURCES = ["abi.cpp", "decode.hip", "decode2d.hip", "encode.hip", "prefill.hip", "quant.hip"]
+SOURCES = ["abi.cpp", "decode.hip", "decode2d.hip", "encode.hip", "prefill.hip", "quant.hip",
+           "reconstruct.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

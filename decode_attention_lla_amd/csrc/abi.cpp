@@ -214,6 +214,30 @@ lla_status lla_attend_decode(const lla_desc* desc, int32_t B, int32_t t, const v
   return from_hip(lla::launch_decode(p, desc->dtype, static_cast<hipStream_t>(stream)));
 }
 
+size_t lla_reconstruct_workspace_bytes(const lla_desc* desc, int32_t B) {
+  if (!desc_ok(desc) || B <= 0) return 0;
+  return lla::reconstruct_workspace_bytes(*desc, B);
+}
+
+lla_status lla_attend_decode_reconstruct(const lla_desc* desc, int32_t B, int32_t t,
+                                         const void* q, const void* zk, const void* zv,
+                                         const int32_t* seq_lens, const void* Wk, const void* Wv,
+                                         const void* mu_k, const void* mu_v, const void* k_self,
+                                         const void* v_self, void* out, float* lse, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  const lla_status st = decode_args_ok(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v,
+                                       k_self, v_self, out, lse, ws);
+  if (st != LLA_OK) return st;
+  if (!lla::reconstruct_supported(*desc)) return LLA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(B) * desc->H * desc->n_max * desc->d_head >= (int64_t(1) << 40))
+    return LLA_ERR_INVALID_ARG;
+  const size_t need = lla::reconstruct_workspace_bytes(*desc, B);
+  if (ws == nullptr || ws_bytes < need) return LLA_ERR_WORKSPACE;
+  lla::DecodeParams p = decode_params(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_self,
+                                      v_self, out, lse, ws, ws_bytes);
+  return from_hip(lla::launch_decode_reconstruct(p, *desc, static_cast<hipStream_t>(stream)));
+}
+
 size_t lla_gather_workspace_bytes(const lla_desc* desc, int32_t B, int32_t budget) {
   if (!desc_ok(desc) || B <= 0 || budget <= 0) return 0;
   return lla::gather_workspace_bytes(*desc, B, budget);

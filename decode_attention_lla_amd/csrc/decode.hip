@@ -374,7 +374,7 @@ void valu_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
   int s = static_cast<int>((target_waves + units - 1) / units);
   const int max_by_len = desc.n_max / 256 > 0 ? desc.n_max / 256 : 1;
   if (s > max_by_len) s = max_by_len;
-  if (s > 64) s = 64;
+  if (s > 256) s = 256;  // long contexts at small B*H: up to 256 splits fill the chip
   if (s < 1) s = 1;
   // tokens per split, a multiple of 128 so every tile but the last is full
   int c = (desc.n_max + s - 1) / s;

@@ -49,6 +49,16 @@ struct EncodeParams {
   int32_t B, C, H, d, T, r, n_max;
 };
 
+// Rebuild of one axis's loop-t K or V for the reconstruct-then-attend comparator (per head).
+struct ReconParams {
+  const void* z;       // bf16 latents [B][H][n_max][r]
+  const void* W;       // bf16 [T][H][d][r]
+  const void* mu;      // bf16 [H][T*d] or NULL
+  const int32_t* seq_lens;
+  void* x;             // bf16 out [B][H][n_max][d], rows < N_b written
+  int32_t H, T, t, n_max, r;
+};
+
 // Quantisation of bf16 latent rows into a low-bit cache (lla_quantize_latents, one axis).
 struct QuantParams {
   const void* src;     // bf16 [B][H][C][r] (LLA-2D: H = 1)
@@ -101,6 +111,11 @@ size_t gather_workspace_bytes(const lla_desc& desc, int B, int budget);
 hipError_t launch_decode_gather(const DecodeParams& p, int dtype, hipStream_t s);
 hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t s);
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+// Reconstruct-then-attend comparator (reconstruct.hip).
+bool reconstruct_supported(const lla_desc& desc);
+void reconstruct_plan(const lla_desc& desc, int B, int* splits, int* chunk);
+size_t reconstruct_workspace_bytes(const lla_desc& desc, int B);
+hipError_t launch_decode_reconstruct(const DecodeParams& p, const lla_desc& desc, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, hipStream_t s);
 
 bool decode_supported(int variant, int dtype, int r_k, int r_v, int d_head);

@@ -78,6 +78,10 @@ def _load():
     lib.lla_attend_decode.restype = _I
     lib.lla_attend_decode.argtypes = [_D, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, ctypes.c_size_t, _P]
+    lib.lla_reconstruct_workspace_bytes.restype = ctypes.c_size_t
+    lib.lla_reconstruct_workspace_bytes.argtypes = [_D, _I]
+    lib.lla_attend_decode_reconstruct.restype = _I
+    lib.lla_attend_decode_reconstruct.argtypes = lib.lla_attend_decode.argtypes
     lib.lla_gather_workspace_bytes.restype = ctypes.c_size_t
     lib.lla_gather_workspace_bytes.argtypes = [_D, _I, _I]
     lib.lla_attend_decode_gather.restype = _I
@@ -207,7 +211,7 @@ def lla_encode(desc, B, C, xk, xv, Ek, Ev, mu_k, mu_v, pos, zk, zv, stream=None)
 
 
 def lla_attend_decode(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_self, v_self, out,
-                      lse=None, ws=None, stream=None):
+                      lse=None, ws=None, stream=None, _entry="lla_attend_decode"):
     dt = _TORCH_DTYPE[desc.dtype]
     s = _shapes(desc, B)
     qs = (B, desc.H, desc.d_head)
@@ -223,9 +227,27 @@ def lla_attend_decode(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_sel
         _ptr(out, "out", qs, dt), _ptr(lse, "lse", (B, desc.H), torch.float32, True),
         None if ws is None else ws.data_ptr(),
     ]
-    st = _load().lla_attend_decode(ctypes.byref(desc), int(B), int(t), *args,
-                                   ctypes.c_size_t(ws_bytes), _stream_ptr(stream))
-    _check(st, "lla_attend_decode")
+    st = getattr(_load(), _entry)(ctypes.byref(desc), int(B), int(t), *args,
+                                  ctypes.c_size_t(ws_bytes), _stream_ptr(stream))
+    _check(st, _entry)
+
+
+def lla_reconstruct_workspace_bytes(desc, B):
+    return int(_load().lla_reconstruct_workspace_bytes(ctypes.byref(desc), int(B)))
+
+
+def lla_attend_decode_reconstruct(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_self,
+                                  v_self, out, lse=None, ws=None, stream=None):
+    """The reconstruct-then-attend comparator; arguments as lla_attend_decode, workspace from
+    lla_reconstruct_workspace_bytes."""
+    lla_attend_decode(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_self, v_self, out, lse,
+                      ws, stream, _entry="lla_attend_decode_reconstruct")
+
+
+def reconstruct_workspace(desc, B, device="cuda"):
+    """A device workspace tensor of lla_reconstruct_workspace_bytes(desc, B) bytes."""
+    n = lla_reconstruct_workspace_bytes(desc, B)
+    return torch.empty((n + 3) // 4, dtype=torch.float32, device=device) if n else None
 
 
 def lla_gather_workspace_bytes(desc, B, budget):

@@ -159,6 +159,25 @@ lla_status lla_attend_decode(const lla_desc* desc, int32_t B, int32_t t, const v
                              const void* k_self, const void* v_self, void* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of device workspace that lla_attend_decode_reconstruct needs for B sequences: the rebuilt
+ * K and V of every slot ([B][H][n_max][d_head] bf16 each), identity factors and split partials.
+ * 0 for an invalid descriptor. */
+size_t lla_reconstruct_workspace_bytes(const lla_desc* desc, int32_t B);
+
+/* Reconstruct-then-attend comparator of lla_attend_decode (Section 7, "Per-head LLA versus LLA-2D
+ * at inference": the absorbed read is measured against this decoder). It rebuilds loop t's
+ * k_i = W^K_t z^K_i + mu^K_t and v_i = W^V_t z^V_i + mu^V_t (Eq. 3) of every visible cached token
+ * into the workspace as bf16 rows, then runs plain softmax attention over them (plus the optional
+ * self token). Same arguments and result as lla_attend_decode up to rounding (the rebuilt K/V are
+ * rounded to bf16 once). Per-head LLA, bf16 storage, d_head 64 or 128, r_k and r_v multiples of 32
+ * up to 256; otherwise LLA_ERR_UNSUPPORTED. ws: at least lla_reconstruct_workspace_bytes(desc, B). */
+lla_status lla_attend_decode_reconstruct(const lla_desc* desc, int32_t B, int32_t t,
+                                         const void* q, const void* zk, const void* zv,
+                                         const int32_t* seq_lens, const void* Wk, const void* Wv,
+                                         const void* mu_k, const void* mu_v, const void* k_self,
+                                         const void* v_self, void* out, float* lse, void* ws,
+                                         size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace that lla_attend_decode_gather needs for B rows of `budget` listed
  * slots. May be 0; 0 as well for an invalid descriptor or size. */
 size_t lla_gather_workspace_bytes(const lla_desc* desc, int32_t B, int32_t budget);

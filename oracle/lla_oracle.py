@@ -196,13 +196,23 @@ def _check_variant(variant):
         raise ValueError(variant)
 
 
+def round_bf16_via_f32(x):
+    """Round to float32, then to bfloat16 (both to nearest even): how a float32 accumulation that is
+    stored as bf16 rounds. Returns float64 values."""
+    import torch
+    t = torch.from_numpy(np.asarray(x, np.float64).astype(np.float32))
+    return t.to(torch.bfloat16).to(torch.float64).numpy()
+
+
 def attend_decode(q, zk, zv, Wk, Wv, t, seq_lens=None, mu_k=None, mu_v=None,
-                  k_self=None, v_self=None, scale=None, variant="per_head"):
+                  k_self=None, v_self=None, scale=None, variant="per_head", kv_round_bf16=False):
     """Decode-time attention of one new token per sequence at loop t, by explicit reconstruction.
 
     For each (b, h): rebuild k_i = W^K_t z^K_i + mu^K_t and v_i = W^V_t z^V_i + mu^V_t for every
     cached token i < N_b (Eq. 3), optionally append the token's own loop-t (k_self, v_self), and
-    run textbook softmax attention with q.
+    run textbook softmax attention with q. With kv_round_bf16 the rebuilt K and V are stored as
+    bf16 before attention (round_bf16_via_f32), as a reconstruct-then-attend decoder that
+    materialises them in bf16 does (Section 7's comparator).
 
     Shapes (per_head): q [B,H,d]; z* [B,H,n_max,r*]; W* [T,H,d,r*]; mu* [H,T*d];
                        k_self/v_self [B,H,d]; seq_lens [B] (None = n_max).
@@ -227,6 +237,8 @@ def attend_decode(q, zk, zv, Wk, Wv, t, seq_lens=None, mu_k=None, mu_v=None,
             lat_v = zv[b, h, :n] if variant == "per_head" else zv[b, :n]
             K = reconstruct(lat_k, wk, muk)
             V = reconstruct(lat_v, wv, muv)
+            if kv_round_bf16:
+                K, V = round_bf16_via_f32(K), round_bf16_via_f32(V)
             if k_self is not None:
                 K = np.concatenate([K, k_self[b, h][None, :]], axis=0)
                 V = np.concatenate([V, v_self[b, h][None, :]], axis=0)

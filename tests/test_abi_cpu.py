@@ -223,3 +223,30 @@ def test_low_bit_support_matrix():
     # same split plan and workspace as bf16 storage on the streaming path
     assert lla.lla_workspace_bytes(desc(r_k=32, r_v=32, dtype=lla.LLA_BF16_Q8), 32, 1) == \
         lla.lla_workspace_bytes(desc(r_k=32, r_v=32), 32, 1)
+
+
+def reconstruct(d, B=2, t=0, ws=N, wsb=0, **kw):
+    args = dict(q=A, zk=A, zv=A, lens=N, Wk=A, Wv=A, muk=N, muv=N, ks=N, vs=N, out=A, lse=N)
+    args.update(kw)
+    return lla.library().lla_attend_decode_reconstruct(
+        ctypes.byref(d), B, t, args["q"], args["zk"], args["zv"], args["lens"], args["Wk"],
+        args["Wv"], args["muk"], args["muv"], args["ks"], args["vs"], args["out"], args["lse"], ws,
+        ctypes.c_size_t(wsb), S)
+
+
+def test_reconstruct_support_and_workspace():
+    ok = dict(r_k=96, r_v=160, n_max=100)
+    assert reconstruct(desc(**ok), q=N) == lla.LLA_ERR_INVALID_ARG
+    assert reconstruct(desc(**ok), t=4) == lla.LLA_ERR_INVALID_ARG
+    for bad in (dict(d_head=96), dict(dtype=lla.LLA_F32), dict(variant=lla.LLA_2D),
+                dict(r_k=24, r_v=24), dict(r_k=512, r_v=32)):
+        base = dict(ok)
+        base.update(bad)
+        assert reconstruct(desc(**base)) == lla.LLA_ERR_UNSUPPORTED, bad
+    d = desc(**ok)
+    need = lla.lla_reconstruct_workspace_bytes(d, 2)
+    kv = 2 * 16 * 100 * 128 * 2
+    assert need >= 2 * kv + 16 * 128 * 128 * 2  # rebuilt K and V plus the identity factors
+    assert reconstruct(d) == lla.LLA_ERR_WORKSPACE
+    assert reconstruct(d, ws=A, wsb=need - 1) == lla.LLA_ERR_WORKSPACE
+    assert lla.lla_reconstruct_workspace_bytes(desc(H=0), 2) == 0

@@ -438,3 +438,23 @@ def test_brute_force_tiny():
         tot = sum(w)
         ref = [sum(w[i] * vals[i][j] for i in range(n + 1)) / tot for j in range(d)]
         np.testing.assert_allclose(o[0, h], ref, atol=1e-12, rtol=0)
+
+
+def test_bf16_rounding_of_rebuilt_kv():
+    """round_bf16_via_f32 keeps bf16 values, rounds halfway cases to even, and the rounded decode
+    equals the unrounded one when every rebuilt K/V value is already a bf16 value."""
+    v = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -7), 3.0 + 2.0 ** -20])
+    np.testing.assert_array_equal(O.round_bf16_via_f32(v),
+                                  [1.0, 1.0, 1.0 + 2.0 ** -6, -(1.0 + 2.0 ** -7), 3.0])
+    rng = np.random.default_rng(21)
+    c = _rand_case(rng)
+    for k in ("zk", "zv", "Wk", "Wv", "mu_k", "mu_v"):
+        c[k] = np.round(c[k] * 2) / 2  # small multiples of 1/2: every rebuilt value is exact in bf16
+    a = O.attend_decode(c["q"], c["zk"], c["zv"], c["Wk"], c["Wv"], 1, None, c["mu_k"], c["mu_v"])
+    b = O.attend_decode(c["q"], c["zk"], c["zv"], c["Wk"], c["Wv"], 1, None, c["mu_k"], c["mu_v"],
+                        kv_round_bf16=True)
+    np.testing.assert_array_equal(a[0], b[0])
+    c2 = _rand_case(rng)
+    a = O.attend_decode(c2["q"], c2["zk"], c2["zv"], c2["Wk"], c2["Wv"], 1)
+    b = O.attend_decode(c2["q"], c2["zk"], c2["zv"], c2["Wk"], c2["Wv"], 1, kv_round_bf16=True)
+    assert 0 < np.max(np.abs(a[0] - b[0])) < 2e-2 * np.max(np.abs(a[0]))
