@@ -431,3 +431,69 @@ def quantize_latent_rows(z):
 def dequantize_latent_rows(codes, scales):
     """The latent values a low-bit row stands for: code_j * s (exact in float64)."""
     return np.asarray(codes, np.float64) * np.asarray(scales, np.float64)[..., None]
+
+
+# --------------------------------------------------------------------------------------------
+# Decoupled RoPE branch (Section 7, "Per-head LLA versus LLA-2D at inference": an MLA-style split
+# into the NoPE latent content path and a small explicit rotary branch, shared across recurrence
+# steps for a token; Section 3, "RoPE and reconstruction")
+# --------------------------------------------------------------------------------------------
+
+def rope_rotate(x, pos, base=10000.0):
+    """Rotary position embedding (Su et al., 2021, RoFormer): channel pairs (2i, 2i+1) of a d-wide
+    vector at position p are rotated by the angle p * base^(-2i/d).
+
+    x [..., d] with d even; pos broadcastable to x.shape[:-1]. Returns float64.
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    theta = base ** (-2.0 * np.arange(d // 2) / d)
+    ang = np.asarray(pos, np.float64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    out[..., 1::2] = x[..., 0::2] * s + x[..., 1::2] * c
+    return out
+
+
+def attend_decode_rope(q, q_rope, zk, zv, k_rope, Wk, Wv, t, seq_lens=None, mu_k=None, mu_v=None,
+                       k_self=None, v_self=None, k_rope_self=None, base=10000.0, scale=None,
+                       variant="per_head"):
+    """Decode attention with the decoupled rotary branch, by explicit reconstruction.
+
+    Key i < N_b is the concatenation of its rebuilt content key k_i = W^K_t z^K_i + mu^K_t (Eq. 3)
+    and its cached rotary key k_rope[b, i], which is stored already rotated at position i. The
+    query is [q ; rope(q_rope, N_b)] (the decoding token sits at position N_b); the optional self
+    key is [k_self ; rope(k_rope_self, N_b)]. Values are the rebuilt content values only. Scale
+    defaults to 1/sqrt(d_head + d_rope) (the concatenated key width, as in MLA).
+
+    q_rope [B,H,d_r]; k_rope [B,n_max,d_r] (one rotary key per token, shared by heads and loops);
+    k_rope_self [B,d_r]; the rest as attend_decode. Returns (o [B,H,d], lse [B,H]).
+    """
+    _check_variant(variant)
+    q, q_rope = _f64(q), _f64(q_rope)
+    zk, zv, Wk, Wv, k_rope = _f64(zk), _f64(zv), _f64(Wk), _f64(Wv), _f64(k_rope)
+    mu_k, mu_v, k_self, v_self = _f64(mu_k), _f64(mu_v), _f64(k_self), _f64(v_self)
+    k_rope_self = _f64(k_rope_self)
+    B, H, d = q.shape
+    dr = q_rope.shape[-1]
+    n_max = zk.shape[2] if variant == "per_head" else zk.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d + dr)
+    o = np.zeros((B, H, d), dtype=np.float64)
+    lse = np.zeros((B, H), dtype=np.float64)
+    for b in range(B):
+        n = n_max if seq_lens is None else int(min(max(int(seq_lens[b]), 0), n_max))
+        qr = rope_rotate(q_rope[b], n, base)  # [H, d_r]
+        krs = None if k_rope_self is None else rope_rotate(k_rope_self[b], n, base)
+        for h in range(H):
+            wk, wv, muk, muv = _loop_slices(variant, Wk, Wv, mu_k, mu_v, t, h, H, d)
+            lat_k = zk[b, h, :n] if variant == "per_head" else zk[b, :n]
+            lat_v = zv[b, h, :n] if variant == "per_head" else zv[b, :n]
+            K = np.concatenate([reconstruct(lat_k, wk, muk), k_rope[b, :n]], axis=1)
+            V = reconstruct(lat_v, wv, muv)
+            if k_self is not None:
+                K = np.concatenate([K, np.concatenate([k_self[b, h], krs])[None, :]], axis=0)
+                V = np.concatenate([V, v_self[b, h][None, :]], axis=0)
+            o[b, h], lse[b, h] = softmax_attention(np.concatenate([q[b, h], qr[h]]), K, V, scale)
+    return o, lse

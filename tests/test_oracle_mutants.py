@@ -13,6 +13,7 @@ from oracle import lla_oracle as O
 import tests.test_oracle_pins as P
 import tests.test_oracle_gather as G
 import tests.test_oracle_q8 as Q
+import tests.test_oracle_rope as R
 
 
 def _encode_no_centre(x_stack, E, mu=None):
@@ -117,6 +118,35 @@ def _quantize_scale_for_240(z):
     return np.where((s > 0)[..., None], codes, 0.0), s.astype(np.float64)
 
 
+def _rope_half_split(x, pos, base=10000.0):
+    # pairs (i, i + d/2) instead of RoFormer's (2i, 2i + 1)
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    perm = np.empty(d, dtype=int)
+    perm[0::2], perm[1::2] = np.arange(d // 2), np.arange(d // 2) + d // 2
+    y = _orig["rope_rotate"](x[..., perm], pos, base)
+    out = np.empty_like(y)
+    out[..., perm] = y
+    return out
+
+
+def _rope_decode_query_one_back(q, q_rope, zk, zv, k_rope, Wk, Wv, t, seq_lens=None, mu_k=None,
+                                mu_v=None, k_self=None, v_self=None, k_rope_self=None,
+                                base=10000.0, scale=None, variant="per_head"):
+    return _orig["attend_decode_rope"](q, O.rope_rotate(q_rope, -1, base), zk, zv, k_rope, Wk, Wv,
+                                       t, seq_lens, mu_k, mu_v, k_self, v_self, k_rope_self, base,
+                                       scale, variant)
+
+
+def _rope_decode_content_scale(q, q_rope, zk, zv, k_rope, Wk, Wv, t, seq_lens=None, mu_k=None,
+                               mu_v=None, k_self=None, v_self=None, k_rope_self=None,
+                               base=10000.0, scale=None, variant="per_head"):
+    if scale is None:
+        scale = 1.0 / math.sqrt(np.asarray(q).shape[-1])
+    return _orig["attend_decode_rope"](q, q_rope, zk, zv, k_rope, Wk, Wv, t, seq_lens, mu_k, mu_v,
+                                       k_self, v_self, k_rope_self, base, scale, variant)
+
+
 _orig = {
     "encode_stack": O.encode_stack,
     "reconstruct": O.reconstruct,
@@ -125,6 +155,8 @@ _orig = {
     "attend_decode_gather": O.attend_decode_gather,
     "e4m3_round": O.e4m3_round,
     "quantize_latent_rows": O.quantize_latent_rows,
+    "rope_rotate": O.rope_rotate,
+    "attend_decode_rope": O.attend_decode_rope,
 }
 
 MUTANTS = {
@@ -144,6 +176,9 @@ MUTANTS = {
     "e4m3 truncates instead of rounding": ("e4m3_round", _e4m3_truncates),
     "e4m3 uses exponent bias 8": ("e4m3_round", _e4m3_bias8),
     "quantiser scales for 240 instead of 448": ("quantize_latent_rows", _quantize_scale_for_240),
+    "rope pairs channels i and i + d/2": ("rope_rotate", _rope_half_split),
+    "rope query rotated one position back": ("attend_decode_rope", _rope_decode_query_one_back),
+    "rope decode scales by the content width only": ("attend_decode_rope", _rope_decode_content_scale),
 }
 
 PINS = [
@@ -162,6 +197,9 @@ PINS = [
     Q.test_every_e4m3_value_rounds_to_itself,
     Q.test_rounding_matches_torch_float8_e4m3fn,
     Q.test_quantized_rows_bound_and_extremes,
+    R.test_rotation_closed_form_and_identity,
+    R.test_full_rank_codec_equals_sdpa_on_concatenated_keys,
+    R.test_common_position_shift_changes_nothing,
 ]
 
 
