@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblla.so")
 
 SOURCES = ["abi.cpp", "decode.hip", "decode2d.hip", "encode.hip", "prefill.hip", "quant.hip",
-           "reconstruct.hip"]
+           "reconstruct.hip", "rope.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

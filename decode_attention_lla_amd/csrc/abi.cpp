@@ -214,6 +214,68 @@ lla_status lla_attend_decode(const lla_desc* desc, int32_t B, int32_t t, const v
   return from_hip(lla::launch_decode(p, desc->dtype, static_cast<hipStream_t>(stream)));
 }
 
+lla_status lla_rope_write(const lla_desc* desc, int32_t B, int32_t C, int32_t d_rope, float base,
+                          const void* k_in, const int32_t* pos, void* k_rope, void* stream) {
+  if (!desc_ok(desc) || desc->dtype != LLA_BF16 || B <= 0 || C <= 0 || C > desc->n_max)
+    return LLA_ERR_INVALID_ARG;
+  if (d_rope <= 0 || d_rope > 256 || (d_rope % 2) != 0 || !(base >= 0.f) || std::isinf(base))
+    return LLA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * desc->n_max * d_rope >= (int64_t(1) << 40)) return LLA_ERR_INVALID_ARG;
+  if (!req_ok(k_in) || !req_ok(pos) || !req_ok(k_rope)) return LLA_ERR_INVALID_ARG;
+  lla::RopeWriteParams p{};
+  p.k_in = k_in;
+  p.pos = pos;
+  p.k_rope = k_rope;
+  p.B = B;
+  p.C = C;
+  p.n_max = desc->n_max;
+  p.d_r = d_rope;
+  p.base = base > 0.f ? base : 10000.0;
+  return from_hip(lla::launch_rope_write(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t lla_rope_workspace_bytes(const lla_desc* desc, int32_t B) {
+  if (!desc_ok(desc) || B <= 0) return 0;
+  return lla::rope_workspace_bytes(*desc, B);
+}
+
+lla_status lla_attend_decode_rope(const lla_desc* desc, int32_t B, int32_t t, const void* q,
+                                  const void* q_rope, const void* zk, const void* zv,
+                                  const void* k_rope, int32_t d_rope, float base,
+                                  const int32_t* seq_lens, const void* Wk, const void* Wv,
+                                  const void* mu_k, const void* mu_v, const void* k_self,
+                                  const void* v_self, const void* k_rope_self, void* out,
+                                  float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const lla_status st = decode_args_ok(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v,
+                                       k_self, v_self, out, lse, ws);
+  if (st != LLA_OK) return st;
+  if (!req_ok(q_rope) || !req_ok(k_rope) || !opt_ok(k_rope_self)) return LLA_ERR_INVALID_ARG;
+  if ((k_self == nullptr) != (k_rope_self == nullptr)) return LLA_ERR_INVALID_ARG;
+  if (!(base >= 0.f) || std::isinf(base)) return LLA_ERR_INVALID_ARG;
+  if (!lla::rope_supported(*desc, d_rope)) return LLA_ERR_UNSUPPORTED;
+  const size_t need = lla::rope_workspace_bytes(*desc, B);
+  if (ws == nullptr || ws_bytes < need) return LLA_ERR_WORKSPACE;
+  lla::DecodeParams p = decode_params(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_self,
+                                      v_self, out, lse, ws, ws_bytes);
+  // the concatenated (content, rotary) key is d_head + d_rope wide
+  const float sc = desc->scale > 0.f ? desc->scale
+                                     : 1.0f / std::sqrt(static_cast<float>(desc->d_head + d_rope));
+  p.scale_log2 = sc * 1.4426950408889634f;
+  lla::valu_plan(*desc, B, &p.splits, &p.chunk);
+  lla::RopeScoreParams rp{};
+  rp.q_rope = q_rope;
+  rp.k_rope = k_rope;
+  rp.k_rope_self = k_rope_self;
+  rp.seq_lens = seq_lens;
+  rp.B = B;
+  rp.H = desc->H;
+  rp.n_max = desc->n_max;
+  rp.d_r = d_rope;
+  rp.scale_log2 = p.scale_log2;
+  rp.base = base > 0.f ? base : 10000.0;
+  return from_hip(lla::launch_decode_rope(p, rp, desc->dtype, static_cast<hipStream_t>(stream)));
+}
+
 size_t lla_reconstruct_workspace_bytes(const lla_desc* desc, int32_t B) {
   if (!desc_ok(desc) || B <= 0) return 0;
   return lla::reconstruct_workspace_bytes(*desc, B);

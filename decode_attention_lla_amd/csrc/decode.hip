@@ -67,6 +67,7 @@ __device__ void finish_unit(const DecodeParams& p, int b, int h, float M, float 
     float part = 0.f;
     for (int j = lane; j < p.d; j += 64) part += q_s[j] * ld<S>(p.k_self, bh * p.d + j);
     s_self = wave_sum(part) * p.scale_log2;
+    if (p.sr_self != nullptr) s_self += p.sr_self[bh];  // the self token's rotary score
   }
   const float M2 = fmaxf(M, s_self);
   const float f_lat = (M == kNegInf) ? 0.f : fast_exp2(M - M2);
@@ -93,8 +94,9 @@ __device__ void finish_unit(const DecodeParams& p, int b, int h, float M, float 
 // split ranges over the row's slot list instead of its first N latents: each token's slot is read
 // first, and a slot outside [0, n_max) counts as masked. S is the storage of q, W, mu, the self
 // token and out; LS that of the latent rows (S itself, or Q8 low-bit rows read whole by one lane:
-// the K row scale multiplies the score, the V row scale the token's weight).
-template <class S, class LS, int RK, int RV, int LPT, int U, bool G>
+// the K row scale multiplies the score, the V row scale the token's weight). With R each token's
+// score also gets its precomputed base-2 rotary score p.sr[bh][slot] (decoupled RoPE branch).
+template <class S, class LS, int RK, int RV, int LPT, int U, bool G, bool R = false>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   constexpr bool kQ8 = std::is_same<LS, Q8>::value;
   constexpr int EK = RK / LPT;
@@ -167,6 +169,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     uint4 vr[U][VV];
     bool ok[U];
     int slot[U];
+    float srv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int tok = t0 + u * TPW + grp;
@@ -176,6 +179,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
         slot[u] = ok[u] ? srow[tok] : 0;
         ok[u] = ok[u] && static_cast<unsigned>(slot[u]) < static_cast<unsigned>(p.n_max);
       }
+      srv[u] = (R && ok[u]) ? p.sr[static_cast<size_t>(bh) * p.n_max + slot[u]] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -208,6 +212,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
       for (int o = 1; o < LPT; o <<= 1) sc += __shfl_xor(sc, o, 64);
       sc += beta;
+      if (R) sc += srv[u];
       if (ok[u]) {
         if (sc > m + kLazy) {
           const float c = fast_exp2(m - sc);
@@ -304,6 +309,10 @@ template <class S, int RK, int RV, int LPT, int U>
 PartialFn gather_fn() {
   return decode_partial_kernel<S, S, RK, RV, LPT, U, true>;
 }
+template <class S, int RK, int RV, int LPT, int U>
+PartialFn rope_fn() {
+  return decode_partial_kernel<S, S, RK, RV, LPT, U, false, true>;
+}
 template <int RK, int RV, int U>
 PartialFn q8_fn() {
   return decode_partial_kernel<BF16, Q8, RK, RV, 1, U, false>;
@@ -317,32 +326,42 @@ struct Entry {
   int dtype, r_k, r_v;
   PartialFn fn;   // contiguous read
   PartialFn gfn;  // gather-indexed read
+  PartialFn rfn;  // contiguous read with rotary scores (bf16 pairs only)
 };
 
 // Compiled (dtype, r_k, r_v) -> (lanes per token, tiles in flight).
 const Entry kTable[] = {
-    {LLA_BF16, 8, 8, partial_fn<BF16, 8, 8, 1, 4>(), gather_fn<BF16, 8, 8, 1, 4>()},
-    {LLA_BF16, 16, 16, partial_fn<BF16, 16, 16, 1, 4>(), gather_fn<BF16, 16, 16, 1, 4>()},
-    {LLA_BF16, 24, 24, partial_fn<BF16, 24, 24, 1, 2>(), gather_fn<BF16, 24, 24, 1, 2>()},
-    {LLA_BF16, 32, 32, partial_fn<BF16, 32, 32, 1, 2>(), gather_fn<BF16, 32, 32, 1, 2>()},
-    {LLA_BF16, 64, 64, partial_fn<BF16, 64, 64, 2, 2>(), gather_fn<BF16, 64, 64, 2, 2>()},
-    {LLA_BF16, 96, 96, partial_fn<BF16, 96, 96, 4, 2>(), gather_fn<BF16, 96, 96, 4, 2>()},
-    {LLA_BF16, 128, 128, partial_fn<BF16, 128, 128, 4, 2>(), gather_fn<BF16, 128, 128, 4, 2>()},
-    {LLA_BF16, 96, 160, partial_fn<BF16, 96, 160, 4, 2>(), gather_fn<BF16, 96, 160, 4, 2>()},
-    {LLA_BF16, 256, 256, partial_fn<BF16, 256, 256, 8, 2>(), gather_fn<BF16, 256, 256, 8, 2>()},
-    {LLA_F32, 8, 8, partial_fn<F32, 8, 8, 1, 2>(), gather_fn<F32, 8, 8, 1, 2>()},
-    {LLA_F32, 16, 16, partial_fn<F32, 16, 16, 1, 2>(), gather_fn<F32, 16, 16, 1, 2>()},
-    {LLA_F32, 24, 24, partial_fn<F32, 24, 24, 1, 1>(), gather_fn<F32, 24, 24, 1, 1>()},
-    {LLA_F32, 32, 32, partial_fn<F32, 32, 32, 2, 1>(), gather_fn<F32, 32, 32, 2, 1>()},
-    {LLA_F32, 64, 64, partial_fn<F32, 64, 64, 4, 1>(), gather_fn<F32, 64, 64, 4, 1>()},
-    {LLA_F32, 96, 96, partial_fn<F32, 96, 96, 4, 1>(), gather_fn<F32, 96, 96, 4, 1>()},
-    {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 8, 1>(), gather_fn<F32, 128, 128, 8, 1>()},
-    {LLA_F32, 96, 160, partial_fn<F32, 96, 160, 8, 1>(), gather_fn<F32, 96, 160, 8, 1>()},
-    {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 16, 1>(), gather_fn<F32, 256, 256, 16, 1>()},
-    {LLA_BF16_Q8, 8, 8, q8_fn<8, 8, 4>(), q8_gather_fn<8, 8, 4>()},
-    {LLA_BF16_Q8, 16, 16, q8_fn<16, 16, 4>(), q8_gather_fn<16, 16, 4>()},
-    {LLA_BF16_Q8, 24, 24, q8_fn<24, 24, 3>(), q8_gather_fn<24, 24, 3>()},
-    {LLA_BF16_Q8, 32, 32, q8_fn<32, 32, 2>(), q8_gather_fn<32, 32, 2>()},
+    {LLA_BF16, 8, 8, partial_fn<BF16, 8, 8, 1, 4>(), gather_fn<BF16, 8, 8, 1, 4>(),
+     rope_fn<BF16, 8, 8, 1, 4>()},
+    {LLA_BF16, 16, 16, partial_fn<BF16, 16, 16, 1, 4>(), gather_fn<BF16, 16, 16, 1, 4>(),
+     rope_fn<BF16, 16, 16, 1, 4>()},
+    {LLA_BF16, 24, 24, partial_fn<BF16, 24, 24, 1, 2>(), gather_fn<BF16, 24, 24, 1, 2>(),
+     rope_fn<BF16, 24, 24, 1, 2>()},
+    {LLA_BF16, 32, 32, partial_fn<BF16, 32, 32, 1, 2>(), gather_fn<BF16, 32, 32, 1, 2>(),
+     rope_fn<BF16, 32, 32, 1, 2>()},
+    {LLA_BF16, 64, 64, partial_fn<BF16, 64, 64, 2, 2>(), gather_fn<BF16, 64, 64, 2, 2>(),
+     rope_fn<BF16, 64, 64, 2, 2>()},
+    {LLA_BF16, 96, 96, partial_fn<BF16, 96, 96, 4, 2>(), gather_fn<BF16, 96, 96, 4, 2>(),
+     rope_fn<BF16, 96, 96, 4, 2>()},
+    {LLA_BF16, 128, 128, partial_fn<BF16, 128, 128, 4, 2>(), gather_fn<BF16, 128, 128, 4, 2>(),
+     rope_fn<BF16, 128, 128, 4, 2>()},
+    {LLA_BF16, 96, 160, partial_fn<BF16, 96, 160, 4, 2>(), gather_fn<BF16, 96, 160, 4, 2>(),
+     rope_fn<BF16, 96, 160, 4, 2>()},
+    {LLA_BF16, 256, 256, partial_fn<BF16, 256, 256, 8, 2>(), gather_fn<BF16, 256, 256, 8, 2>(),
+     rope_fn<BF16, 256, 256, 8, 2>()},
+    {LLA_F32, 8, 8, partial_fn<F32, 8, 8, 1, 2>(), gather_fn<F32, 8, 8, 1, 2>(), nullptr},
+    {LLA_F32, 16, 16, partial_fn<F32, 16, 16, 1, 2>(), gather_fn<F32, 16, 16, 1, 2>(), nullptr},
+    {LLA_F32, 24, 24, partial_fn<F32, 24, 24, 1, 1>(), gather_fn<F32, 24, 24, 1, 1>(), nullptr},
+    {LLA_F32, 32, 32, partial_fn<F32, 32, 32, 2, 1>(), gather_fn<F32, 32, 32, 2, 1>(), nullptr},
+    {LLA_F32, 64, 64, partial_fn<F32, 64, 64, 4, 1>(), gather_fn<F32, 64, 64, 4, 1>(), nullptr},
+    {LLA_F32, 96, 96, partial_fn<F32, 96, 96, 4, 1>(), gather_fn<F32, 96, 96, 4, 1>(), nullptr},
+    {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 8, 1>(), gather_fn<F32, 128, 128, 8, 1>(), nullptr},
+    {LLA_F32, 96, 160, partial_fn<F32, 96, 160, 8, 1>(), gather_fn<F32, 96, 160, 8, 1>(), nullptr},
+    {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 16, 1>(), gather_fn<F32, 256, 256, 16, 1>(), nullptr},
+    {LLA_BF16_Q8, 8, 8, q8_fn<8, 8, 4>(), q8_gather_fn<8, 8, 4>(), nullptr},
+    {LLA_BF16_Q8, 16, 16, q8_fn<16, 16, 4>(), q8_gather_fn<16, 16, 4>(), nullptr},
+    {LLA_BF16_Q8, 24, 24, q8_fn<24, 24, 3>(), q8_gather_fn<24, 24, 3>(), nullptr},
+    {LLA_BF16_Q8, 32, 32, q8_fn<32, 32, 2>(), q8_gather_fn<32, 32, 2>(), nullptr},
 };
 
 const Entry* find(int dtype, int r_k, int r_v) {
@@ -443,6 +462,45 @@ size_t gather_workspace_bytes(const lla_desc& desc, int B, int budget) {
   int s, c;
   gather_plan(desc, B, budget, &s, &c);
   return valu_workspace_bytes(desc, B, s);
+}
+
+bool rope_supported(const lla_desc& desc, int d_rope) {
+  const Entry* e = find(desc.dtype, desc.r_k, desc.r_v);
+  return desc.dtype == LLA_BF16 && e != nullptr && e->rfn != nullptr &&
+         (d_rope == 32 || d_rope == 64 || d_rope == 128) &&
+         static_cast<long>(desc.H) * d_rope * 4 <= 64 * 1024;
+}
+
+namespace {
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+}  // namespace
+
+size_t rope_workspace_bytes(const lla_desc& desc, int B) {
+  int s, c;
+  valu_plan(desc, B, &s, &c);
+  return align256(static_cast<size_t>(B) * desc.H * desc.n_max * 4) +
+         align256(static_cast<size_t>(B) * desc.H * 4) + valu_workspace_bytes(desc, B, s);
+}
+
+hipError_t launch_decode_rope(const DecodeParams& p, const RopeScoreParams& rp0, int dtype,
+                              hipStream_t stream) {
+  const Entry* e = find(dtype, p.r_k, p.r_v);
+  if (e == nullptr || e->rfn == nullptr) return hipErrorNotSupported;
+  const size_t a = align256(static_cast<size_t>(p.B) * p.H * p.n_max * 4);
+  const size_t b = align256(static_cast<size_t>(p.B) * p.H * 4);
+  if (a + b > p.ws_bytes) return hipErrorInvalidValue;
+  char* base = reinterpret_cast<char*>(p.ws);
+  RopeScoreParams rp = rp0;
+  rp.sr = reinterpret_cast<float*>(base);
+  rp.sr_self = reinterpret_cast<float*>(base + a);
+  hipError_t err = launch_rope_scores(rp, stream);
+  if (err != hipSuccess) return err;
+  DecodeParams q = p;
+  q.sr = rp.sr;
+  q.sr_self = rp.k_rope_self != nullptr ? rp.sr_self : nullptr;
+  q.ws = reinterpret_cast<float*>(base + a + b);
+  q.ws_bytes = p.ws_bytes - a - b;
+  return launch_valu(q, dtype, e->rfn, stream);
 }
 
 hipError_t launch_decode_gather(const DecodeParams& p, int dtype, hipStream_t stream) {

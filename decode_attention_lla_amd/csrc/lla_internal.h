@@ -33,6 +33,10 @@ struct DecodeParams {
   int32_t chunk;      // tokens per split
   float scale_log2;   // softmax scale * log2(e)
   size_t ws_bytes;    // bytes available at ws; launchers refuse a plan that does not fit
+  // Rotary branch (lla_attend_decode_rope): base-2 rotary scores added to the latent scores,
+  // sr [rows][H][n_max] by slot and sr_self [rows][H] for the self token; NULL when absent.
+  const float* sr;
+  const float* sr_self;
   // Gather-indexed read (lla_attend_decode_gather): row b attends the latents at
   // slots[b * budget + j], j < seq_lens[b] clamped to [0, budget] (all budget when seq_lens is
   // null); a slot outside [0, n_max) is skipped. slots == nullptr: the contiguous read above.
@@ -47,6 +51,28 @@ struct EncodeParams {
   const int32_t* pos; // [B]
   void* z;            // [B][H][n_max][r]
   int32_t B, C, H, d, T, r, n_max;
+};
+
+// Rotary key write (lla_rope_write): k_rope[b][pos[b]+c] = rope(k_in[b][c], pos[b]+c).
+struct RopeWriteParams {
+  const void* k_in;    // bf16 [B][C][d_r]
+  const int32_t* pos;  // [B]
+  void* k_rope;        // bf16 [B][n_max][d_r]
+  int32_t B, C, n_max, d_r;
+  double base;
+};
+
+// Rotary score pre-pass of one decode read (lla_attend_decode_rope).
+struct RopeScoreParams {
+  const void* q_rope;       // bf16 [B][H][d_r], unrotated (rotated at N_b inside)
+  const void* k_rope;       // bf16 [B][n_max][d_r], rotated at each slot
+  const void* k_rope_self;  // bf16 [B][d_r] or NULL
+  const int32_t* seq_lens;
+  float* sr;                // out [B][H][n_max], base-2 scale
+  float* sr_self;           // out [B][H] (when k_rope_self is given)
+  int32_t B, H, n_max, d_r;
+  float scale_log2;
+  double base;
 };
 
 // Rebuild of one axis's loop-t K or V for the reconstruct-then-attend comparator (per head).
@@ -111,6 +137,13 @@ size_t gather_workspace_bytes(const lla_desc& desc, int B, int budget);
 hipError_t launch_decode_gather(const DecodeParams& p, int dtype, hipStream_t s);
 hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t s);
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+// Decoupled rotary branch (rope.hip, decode.hip).
+hipError_t launch_rope_write(const RopeWriteParams& p, hipStream_t s);
+hipError_t launch_rope_scores(const RopeScoreParams& p, hipStream_t s);
+bool rope_supported(const lla_desc& desc, int d_rope);
+size_t rope_workspace_bytes(const lla_desc& desc, int B);
+hipError_t launch_decode_rope(const DecodeParams& p, const RopeScoreParams& rp, int dtype,
+                              hipStream_t s);
 // Reconstruct-then-attend comparator (reconstruct.hip).
 bool reconstruct_supported(const lla_desc& desc);
 void reconstruct_plan(const lla_desc& desc, int B, int* splits, int* chunk);

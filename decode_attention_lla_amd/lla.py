@@ -78,6 +78,14 @@ def _load():
     lib.lla_attend_decode.restype = _I
     lib.lla_attend_decode.argtypes = [_D, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, ctypes.c_size_t, _P]
+    lib.lla_rope_write.restype = _I
+    lib.lla_rope_write.argtypes = [_D, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P]
+    lib.lla_rope_workspace_bytes.restype = ctypes.c_size_t
+    lib.lla_rope_workspace_bytes.argtypes = [_D, _I]
+    lib.lla_attend_decode_rope.restype = _I
+    lib.lla_attend_decode_rope.argtypes = [_D, _I, _I, _P, _P, _P, _P, _P, _I, ctypes.c_float,
+                                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           ctypes.c_size_t, _P]
     lib.lla_reconstruct_workspace_bytes.restype = ctypes.c_size_t
     lib.lla_reconstruct_workspace_bytes.argtypes = [_D, _I]
     lib.lla_attend_decode_reconstruct.restype = _I
@@ -230,6 +238,51 @@ def lla_attend_decode(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_sel
     st = getattr(_load(), _entry)(ctypes.byref(desc), int(B), int(t), *args,
                                   ctypes.c_size_t(ws_bytes), _stream_ptr(stream))
     _check(st, _entry)
+
+
+def lla_rope_write(desc, B, C, d_rope, base, k_in, pos, k_rope, stream=None):
+    args = [_ptr(k_in, "k_in", (B, C, d_rope), torch.bfloat16), _ptr(pos, "pos", (B,), torch.int32),
+            _ptr(k_rope, "k_rope", (B, desc.n_max, d_rope), torch.bfloat16)]
+    st = _load().lla_rope_write(ctypes.byref(desc), int(B), int(C), int(d_rope),
+                                ctypes.c_float(base), *args, _stream_ptr(stream))
+    _check(st, "lla_rope_write")
+
+
+def lla_rope_workspace_bytes(desc, B):
+    return int(_load().lla_rope_workspace_bytes(ctypes.byref(desc), int(B)))
+
+
+def rope_workspace(desc, B, device="cuda"):
+    """A device workspace tensor of lla_rope_workspace_bytes(desc, B) bytes."""
+    n = lla_rope_workspace_bytes(desc, B)
+    return torch.empty((n + 3) // 4, dtype=torch.float32, device=device) if n else None
+
+
+def lla_attend_decode_rope(desc, B, t, q, q_rope, zk, zv, k_rope, d_rope, base, seq_lens, Wk, Wv,
+                           mu_k, mu_v, k_self, v_self, k_rope_self, out, lse=None, ws=None,
+                           stream=None):
+    dt = _TORCH_DTYPE[desc.dtype]
+    s = _shapes(desc, B)
+    qs = (B, desc.H, desc.d_head)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    if ws is not None and (ws.device.type != "cuda" or not ws.is_contiguous()):
+        raise ValueError("ws must be a contiguous device tensor")
+    args = [
+        _ptr(q, "q", qs, dt), _ptr(q_rope, "q_rope", (B, desc.H, d_rope), torch.bfloat16),
+        _ptr(zk, "zk", s["zk"], _zdt(desc)), _ptr(zv, "zv", s["zv"], _zdt(desc)),
+        _ptr(k_rope, "k_rope", (B, desc.n_max, d_rope), torch.bfloat16),
+        ctypes.c_int32(int(d_rope)), ctypes.c_float(base),
+        _ptr(seq_lens, "seq_lens", (B,), torch.int32, True),
+        _ptr(Wk, "Wk", s["Wk"], dt), _ptr(Wv, "Wv", s["Wv"], dt),
+        _ptr(mu_k, "mu_k", s["mu"], dt, True), _ptr(mu_v, "mu_v", s["mu"], dt, True),
+        _ptr(k_self, "k_self", qs, dt, True), _ptr(v_self, "v_self", qs, dt, True),
+        _ptr(k_rope_self, "k_rope_self", (B, d_rope), torch.bfloat16, True),
+        _ptr(out, "out", qs, dt), _ptr(lse, "lse", (B, desc.H), torch.float32, True),
+        None if ws is None else ws.data_ptr(),
+    ]
+    st = _load().lla_attend_decode_rope(ctypes.byref(desc), int(B), int(t), *args,
+                                        ctypes.c_size_t(ws_bytes), _stream_ptr(stream))
+    _check(st, "lla_attend_decode_rope")
 
 
 def lla_reconstruct_workspace_bytes(desc, B):

@@ -159,6 +159,42 @@ lla_status lla_attend_decode(const lla_desc* desc, int32_t B, int32_t t, const v
                              const void* k_self, const void* v_self, void* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Decoupled rotary branch (Section 7, "Per-head LLA versus LLA-2D at inference": RoPE cannot be
+ * absorbed, so the latent path carries the NoPE content and a small explicit rotary branch, shared
+ * across recurrence steps for a token, carries position, MLA-style). One rotary key of width d_rope
+ * is cached per token, shared by every head and loop: k_rope [device] bf16 [B][n_max][d_rope],
+ * stored already rotated at its slot position. Rotation (Su et al., 2021, RoFormer): channel
+ * pairs (2i, 2i+1) at position p turn by p * base^(-2i/d_rope), evaluated in float64; base 0
+ * means 10000. Positions are slot indices.
+ *
+ * lla_rope_write: rotate and store C rotary keys per sequence, k_in [device] bf16 [B][C][d_rope],
+ * row c of sequence b at slot pos[b] + c (a slot outside [0, n_max) is not written). desc->dtype
+ * must be LLA_BF16; d_rope even, <= 256. */
+lla_status lla_rope_write(const lla_desc* desc, int32_t B, int32_t C, int32_t d_rope, float base,
+                          const void* k_in, const int32_t* pos, void* k_rope, void* stream);
+
+/* Bytes of device workspace that lla_attend_decode_rope needs: the rotary scores
+ * [B][H][n_max] float32, the self token's [B][H], and split partials. 0 for an invalid descriptor. */
+size_t lla_rope_workspace_bytes(const lla_desc* desc, int32_t B);
+
+/* lla_attend_decode with the rotary branch: key i of row b is [k_i ; k_rope[b][i]] (k_i rebuilt
+ * content key, Eq. 3, absorbed as in lla_attend_decode), the query is [q ; rope(q_rope, N_b)] (the
+ * decoding token sits at position N_b), the optional self key is [k_self ; rope(k_rope_self, N_b)],
+ * values are the content values. The scale defaults (desc->scale == 0) to 1/sqrt(d_head + d_rope),
+ * the width of the concatenated key.
+ *   q_rope [device] bf16 [B][H][d_rope], unrotated; k_rope_self [device] bf16 [B][d_rope], given
+ *   exactly when k_self is; ws at least lla_rope_workspace_bytes(desc, B).
+ * The rotary scores of all heads are formed once per read (each rotary key read once) and added to
+ * the streamed latent scores. LLA_BF16, d_rope 32, 64 or 128, H * d_rope <= 16384, the streaming
+ * bf16 (r_k, r_v) pairs, both variants; otherwise LLA_ERR_UNSUPPORTED. */
+lla_status lla_attend_decode_rope(const lla_desc* desc, int32_t B, int32_t t, const void* q,
+                                  const void* q_rope, const void* zk, const void* zv,
+                                  const void* k_rope, int32_t d_rope, float base,
+                                  const int32_t* seq_lens, const void* Wk, const void* Wv,
+                                  const void* mu_k, const void* mu_v, const void* k_self,
+                                  const void* v_self, const void* k_rope_self, void* out,
+                                  float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace that lla_attend_decode_reconstruct needs for B sequences: the rebuilt
  * K and V of every slot ([B][H][n_max][d_head] bf16 each), identity factors and split partials.
  * 0 for an invalid descriptor. */

@@ -250,3 +250,35 @@ def test_reconstruct_support_and_workspace():
     assert reconstruct(d) == lla.LLA_ERR_WORKSPACE
     assert reconstruct(d, ws=A, wsb=need - 1) == lla.LLA_ERR_WORKSPACE
     assert lla.lla_reconstruct_workspace_bytes(desc(H=0), 2) == 0
+
+
+def rope_decode(d, B=2, t=0, d_rope=64, base=0.0, ws=N, wsb=0, **kw):
+    a = dict(q=A, qr=A, zk=A, zv=A, kr=A, lens=N, Wk=A, Wv=A, ks=N, vs=N, krs=N, out=A, lse=N)
+    a.update(kw)
+    return lla.library().lla_attend_decode_rope(
+        ctypes.byref(d), B, t, a["q"], a["qr"], a["zk"], a["zv"], a["kr"], d_rope,
+        ctypes.c_float(base), a["lens"], a["Wk"], a["Wv"], N, N, a["ks"], a["vs"], a["krs"],
+        a["out"], a["lse"], ws, ctypes.c_size_t(wsb), S)
+
+
+def test_rope_arguments_support_and_workspace():
+    d = desc(r_k=24, r_v=24, n_max=100)
+    for kw in (dict(qr=N), dict(kr=M), dict(ks=A, vs=A), dict(krs=A), dict(base=-1.0),
+               dict(base=float("inf")), dict(t=4)):
+        assert rope_decode(d, **kw) == lla.LLA_ERR_INVALID_ARG, kw
+    assert rope_decode(d, d_rope=48) == lla.LLA_ERR_UNSUPPORTED
+    assert rope_decode(desc(r_k=24, r_v=24, n_max=100, dtype=lla.LLA_F32)) == lla.LLA_ERR_UNSUPPORTED
+    assert rope_decode(desc(r_k=64, r_v=128, n_max=100)) == lla.LLA_ERR_UNSUPPORTED
+    assert rope_decode(desc(r_k=24, r_v=24, n_max=100, H=200), d_rope=128) == lla.LLA_ERR_UNSUPPORTED
+    need = lla.lla_rope_workspace_bytes(d, 2)
+    assert need >= 2 * 16 * 100 * 4  # rotary scores of every (b, h, slot)
+    assert rope_decode(d) == lla.LLA_ERR_WORKSPACE
+    assert rope_decode(d, ws=A, wsb=need - 1) == lla.LLA_ERR_WORKSPACE
+    lib = lla.library()
+    w = lambda dd, **k: lib.lla_rope_write(ctypes.byref(dd), k.get("B", 2), k.get("C", 1),
+                                           k.get("dr", 64), ctypes.c_float(k.get("base", 0.0)),
+                                           k.get("x", A), k.get("pos", A), k.get("kr", A), S)
+    assert w(d, dr=63) == lla.LLA_ERR_INVALID_ARG
+    assert w(d, C=101) == lla.LLA_ERR_INVALID_ARG
+    assert w(d, pos=N) == lla.LLA_ERR_INVALID_ARG
+    assert w(desc(dtype=lla.LLA_F32, n_max=100)) == lla.LLA_ERR_INVALID_ARG

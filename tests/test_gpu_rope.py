@@ -1,0 +1,150 @@
+"""GPU parity of the decoupled rotary branch (lla_rope_write, lla_attend_decode_rope).
+
+The rotary key write is compared with the oracle's RoFormer rotation rounded to bf16; the decode
+with the rotary branch is compared with the oracle's explicit attention over concatenated
+(content, rotary) keys, element by element, for both variants, three rotary widths, split-K, the
+self token, long positions, and the capacity shape at full size on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_lla_amd import lla, synth
+from oracle import lla_oracle as O
+from tests.gpu_util import assert_close, assert_lse, dev, host, require_gpu
+from tests.test_gpu_parity import _fill_device_case, mk_desc, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("d_rope,base", [(64, 0.0), (32, 500.0), (128, 10000.0)])
+def test_rope_write(d_rope, base):
+    rng = np.random.default_rng(9900 + d_rope)
+    B, C, n_max = 3, 6, 262150
+    desc = mk_desc("per_head", "bf16", 2, 64, 2, 24, 24, n_max)
+    k_in = synth.to_storage(rng.standard_normal((B, C, d_rope)).astype(np.float32), "bf16")
+    pos = np.array([0, 1000, 262146], np.int32)  # sequence 2: slots 262146..262149 written, then skipped
+    kr = torch.full((B, n_max, d_rope), 7.0, dtype=torch.bfloat16, device="cuda")
+    lla.lla_rope_write(desc, B, C, d_rope, base, dev(k_in, "bf16"), dev(pos), kr)
+    torch.cuda.synchronize()
+    b_eff = base if base > 0 else 10000.0
+    for b in range(B):
+        for c in range(C):
+            slot = int(pos[b]) + c
+            if slot >= n_max:
+                continue
+            want = O.round_bf16_via_f32(O.rope_rotate(k_in[b, c], slot, b_eff))
+            got = host(kr[b, slot])
+            # float64 trigonometry on both sides: equal up to a last-place difference in sin/cos,
+            # which can move a bf16 rounding by one step
+            ulp = np.maximum(np.abs(want), 1e-30) * 2.0 ** -7
+            assert np.all(np.abs(got - want) <= ulp), (b, c)
+            assert np.mean(got == want) >= 0.95, (b, c)
+    untouched = host(kr[0, 6:1000])
+    assert np.all(untouched == 7.0)
+
+
+def _rope_inputs(rng, B, H, n_max, d_rope):
+    q_rope = synth.to_storage(rng.standard_normal((B, H, d_rope)).astype(np.float32), "bf16")
+    k_rope = synth.to_storage(rng.standard_normal((B, n_max, d_rope)).astype(np.float32), "bf16")
+    krs = synth.to_storage(rng.standard_normal((B, d_rope)).astype(np.float32), "bf16")
+    return q_rope, k_rope, krs
+
+
+@pytest.mark.parametrize("variant,rk,rv,d_rope", [("per_head", 24, 24, 64), ("per_head", 96, 160, 32),
+                                                  ("per_head", 128, 128, 128), ("2d", 32, 32, 64),
+                                                  ("2d", 256, 256, 64)])
+def test_decode_rope(variant, rk, rv, d_rope):
+    B, H, d, T, n_max = 3, 2, 64, 2, 1301
+    lens = np.array([1301, 517, 0], np.int32)
+    desc = mk_desc(variant, "bf16", H, d, T, rk, rv, n_max)
+    ws = lla.rope_workspace(desc, B)
+    rng = np.random.default_rng(9950 + rk + d_rope)
+    q_rope, k_rope, krs = _rope_inputs(rng, B, H, n_max, d_rope)
+    d_qr, d_kr, d_krs = dev(q_rope, "bf16"), dev(k_rope, "bf16"), dev(krs, "bf16")
+    for gain, mu, self_token in ((1.0, True, True), (8.0, False, True), (1.0, True, False)):
+        c = upload(synth.random_case(variant, "bf16", B, H, d, T, rk, rv, n_max, 9960 + rk,
+                                     with_mu=mu, q_gain=gain), "bf16")
+        for t in range(T):
+            q = dev(c["q"][t], "bf16")
+            out = torch.empty_like(q)
+            lse = torch.empty(B, H, device="cuda")
+            lla.lla_attend_decode_rope(desc, B, t, q, d_qr, c["_zk"], c["_zv"], d_kr, d_rope, 0.0,
+                                       dev(lens), c["_Wk"], c["_Wv"], c["_muk"] if mu else None,
+                                       c["_muv"] if mu else None,
+                                       dev(c["k_self"][t], "bf16") if self_token else None,
+                                       dev(c["v_self"][t], "bf16") if self_token else None,
+                                       d_krs if self_token else None, out, lse, ws)
+            torch.cuda.synchronize()
+            ro, rl = O.attend_decode_rope(c["q"][t], q_rope, c["zk"], c["zv"], k_rope, c["Wk"],
+                                          c["Wv"], t, lens, c["mu_k"] if mu else None,
+                                          c["mu_v"] if mu else None,
+                                          c["k_self"][t] if self_token else None,
+                                          c["v_self"][t] if self_token else None,
+                                          krs if self_token else None, variant=variant)
+            what = f"rope {variant} r=({rk},{rv}) d_rope={d_rope} gain={gain} mu={mu} self={self_token} t={t}"
+            assert_close(host(out), ro, "bf16", what)
+            assert_lse(host(lse), rl, what)
+
+
+def test_decode_rope_long_positions_and_explicit_scale():
+    """One sequence at 70000 cached tokens (large rotation angles for the query) and a scale given
+    by the descriptor."""
+    B, H, d, T, n_max, r, d_rope = 1, 2, 64, 1, 70001, 24, 64
+    desc = mk_desc("per_head", "bf16", H, d, T, r, r, n_max, scale=0.07)
+    rng = np.random.default_rng(9970)
+    q_rope, k_rope, krs = _rope_inputs(rng, B, H, n_max, d_rope)
+    c = upload(synth.random_case("per_head", "bf16", B, H, d, T, r, r, n_max, 9971), "bf16")
+    lens = np.array([70000], np.int32)
+    q = dev(c["q"][0], "bf16")
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H, device="cuda")
+    lla.lla_attend_decode_rope(desc, B, 0, q, dev(q_rope, "bf16"), c["_zk"], c["_zv"],
+                               dev(k_rope, "bf16"), d_rope, 0.0, dev(lens), c["_Wk"], c["_Wv"], None,
+                               None, None, None, None, out, lse, lla.rope_workspace(desc, B))
+    torch.cuda.synchronize()
+    ro, rl = O.attend_decode_rope(c["q"][0], q_rope, c["zk"], c["zv"], k_rope, c["Wk"], c["Wv"], 0,
+                                  lens, scale=0.07)
+    assert_close(host(out), ro, "bf16", "rope 70k")
+    assert_lse(host(lse), rl, "rope 70k")
+
+
+def test_capacity_rope_full_size_sampled():
+    """Capacity shape (B=768, H=16, d=128, T=4, r=24, N=4096) with a 64-wide rotary branch, at the
+    benchmark's launch shape; sampled rows, all loops."""
+    s = synth.CASES["capacity"]
+    d_rope = 64
+    g = _fill_device_case(s)
+    desc = mk_desc(s.variant, s.dtype, s.H, s.d, s.T, s.r_k, s.r_v, s.n_max)
+    kr = synth.device_normal_(torch.empty(s.B, s.n_max, d_rope, dtype=torch.bfloat16, device="cuda"), 9980)
+    qr = synth.device_normal_(torch.empty(s.T, s.B, s.H, d_rope, dtype=torch.bfloat16, device="cuda"), 9981)
+    krs = synth.device_normal_(torch.empty(s.B, d_rope, dtype=torch.bfloat16, device="cuda"), 9982)
+    rows = sorted({0, 383, 767, *np.random.default_rng(synth.seed(s.case, synth.SEED_SAMPLE)).choice(768, 3, replace=False).tolist()})
+    zk_rows, zv_rows = host(g["zk"][rows]), host(g["zv"][rows])
+    kr_rows, krs_rows = host(kr[rows]), host(krs[rows])
+    lens = np.full(s.B, s.N, np.int32)
+    Wk, Wv = dev(g["Wk"], "bf16"), dev(g["Wv"], "bf16")
+    ws = lla.rope_workspace(desc, s.B)
+    for t in range(s.T):
+        q = dev(g["q"][t], "bf16")
+        out = torch.empty_like(q)
+        lse = torch.empty(s.B, s.H, device="cuda")
+        lla.lla_attend_decode_rope(desc, s.B, t, q, qr[t], g["zk"], g["zv"], kr, d_rope, 0.0,
+                                   dev(lens), Wk, Wv, None, None, dev(g["k_self"][t], "bf16"),
+                                   dev(g["v_self"][t], "bf16"), krs, out, lse, ws)
+        torch.cuda.synchronize()
+        ro, rl = O.attend_decode_rope(g["q"][t][rows], host(qr[t][rows]), zk_rows, zv_rows, kr_rows,
+                                      g["Wk"], g["Wv"], t, lens[rows], None, None,
+                                      g["k_self"][t][rows], g["v_self"][t][rows], krs_rows)
+        assert_close(host(out)[rows], ro, s.dtype, f"capacity rope t={t}")
+        assert_lse(host(lse)[rows], rl, f"capacity rope t={t}")
+    del g
+    torch.cuda.empty_cache()
