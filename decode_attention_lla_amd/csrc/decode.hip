@@ -263,40 +263,59 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   finish_unit<S>(p, b, h, M, l, a_s, q_s, lane);
 }
 
-// Log-sum-exp merge of the S split partials of one (b, h), then the same finish. One wave.
+// Log-sum-exp merge of the S split partials of one (b, h), then the same finish. 256 threads:
+// the split maximum and weighted sum are block reductions, each thread merges one latent entry
+// across every split (loads coalesced over entries), and wave 0 runs the finish. (With one wave
+// per (b, h), a long context at B = 1 -- 16 units, 256 splits -- left the merge latency-bound.)
+constexpr int kCombineThreads = 256;
+
 template <class S>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeParams p) {
   __shared__ float q_s[256];
   __shared__ float a_s[512];
   __shared__ float f_s[256];
-  const int lane = threadIdx.x;
+  __shared__ float red[kCombineThreads / 64];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int bh = blockIdx.x;
   const int h = bh % p.H;
   const int b = bh / p.H;
-  const int S_ = p.splits;
+  const int S_ = p.splits;  // <= 256 (valu_plan)
   const int stride = 2 + p.r_v;
   const float* w = p.ws + static_cast<size_t>(bh) * S_ * stride;
 
   float mloc = kNegInf;
-  for (int s = lane; s < S_; s += 64) mloc = fmaxf(mloc, w[static_cast<size_t>(s) * stride]);
-  const float M = wave_max(mloc);
+  for (int s = tid; s < S_; s += kCombineThreads) mloc = fmaxf(mloc, w[static_cast<size_t>(s) * stride]);
+  mloc = wave_max(mloc);
+  if (lane == 0) red[wave] = mloc;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int i = 1; i < kCombineThreads / 64; ++i) M = fmaxf(M, red[i]);
+  __syncthreads();  // red is reused below
   float lloc = 0.f;
-  for (int s = lane; s < S_; s += 64) {
+  for (int s = tid; s < S_; s += kCombineThreads) {
     const float ms = w[static_cast<size_t>(s) * stride];
     const float fs = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
     f_s[s] = fs;
     lloc += fs * w[static_cast<size_t>(s) * stride + 1];
   }
-  const float l = wave_sum(lloc);
-  for (int j = lane; j < p.d; j += 64) q_s[j] = ld<S>(p.q, static_cast<size_t>(bh) * p.d + j);
+  lloc = wave_sum(lloc);
+  if (lane == 0) red[wave] = lloc;
+  for (int j = tid; j < p.d; j += kCombineThreads) q_s[j] = ld<S>(p.q, static_cast<size_t>(bh) * p.d + j);
   __syncthreads();
-  for (int r = lane; r < p.r_v; r += 64) {
+  float l = 0.f;
+#pragma unroll
+  for (int i = 0; i < kCombineThreads / 64; ++i) l += red[i];
+  for (int r = tid; r < p.r_v; r += kCombineThreads) {
     float a = 0.f;
+#pragma unroll 8
     for (int s = 0; s < S_; ++s) a += f_s[s] * w[static_cast<size_t>(s) * stride + 2 + r];
     a_s[r] = a;
   }
   __syncthreads();
-  finish_unit<S>(p, b, h, M, l, a_s, q_s, lane);
+  if (wave == 0) finish_unit<S>(p, b, h, M, l, a_s, q_s, lane);
 }
 
 using PartialFn = void (*)(DecodeParams);
@@ -434,9 +453,9 @@ hipError_t launch_valu(const DecodeParams& p, int dtype, PartialFn fn, hipStream
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;
   if (dtype == LLA_BF16 || dtype == LLA_BF16_Q8)
-    hipLaunchKernelGGL(decode_combine_kernel<BF16>, dim3(p.B * p.H), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(decode_combine_kernel<BF16>, dim3(p.B * p.H), dim3(kCombineThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(decode_combine_kernel<F32>, dim3(p.B * p.H), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(decode_combine_kernel<F32>, dim3(p.B * p.H), dim3(kCombineThreads), 0, stream, p);
   return hipGetLastError();
 }
 

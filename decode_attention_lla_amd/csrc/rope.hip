@@ -11,8 +11,8 @@
 //
 // The rotary score of token i for head h, q_r(b,h) . k_r(b,i) with q_r rotated at the decoding
 // position N_b, depends on the head only through q_r, and k_r is shared by all heads: one pre-pass
-// per read forms every head's rotary scores (already in the base-2 softmax scale) reading each
-// rotary key once, and the streaming decode kernel adds them to the latent scores.
+// per read forms every head's rotary scores (already in the base-2 softmax scale) on MFMA, reading
+// each rotary key once, and the streaming decode kernel adds them to the latent scores.
 #include <hip/hip_runtime.h>
 
 #include "lla_device.h"
@@ -55,19 +55,32 @@ __global__ __launch_bounds__(256) void rope_write_kernel(RopeWriteParams p) {
   out[i] = f32x2_to_bf16x2(y0, y1);
 }
 
-constexpr int kTokTile = 256;
+constexpr int kTokTile = 256;  // tokens per workgroup: 4 waves x 4 blocks of 16
 
-// sr[b][h][i] = scale_log2 * rope(q_rope[b][h], N_b) . k_rope[b][i] for i < N_b; the workgroup of
-// tile 0 also writes sr_self[b][h] = scale_log2 * q_rope[b][h] . k_rope_self[b] (rotating both at
-// N_b leaves their dot product unchanged). One thread per token, every head; DR = d_r.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4_t mfma16(uint4 a, uint4 b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// sr[b][h][i] = scale_log2 * rope(q_rope[b][h], N_b) . k_rope[b][i] for i < N_b, on MFMA: per
+// 16-token block, S (16 heads x 16 tokens) = Q_r (16 heads x d_r, A operand) . K_rope^T (d_r x
+// 16 tokens, B operand straight from HBM, 16 bytes per lane along the key); each store then writes
+// 16 consecutive tokens of a head's score row. The rotated, scaled queries
+// are split into two bf16 parts (hi + lo) accumulated into the same result, so the queries keep
+// ~16 mantissa bits. The workgroup of tile 0 also writes sr_self[b][h] = scale_log2 *
+// q_rope[b][h] . k_rope_self[b] (rotating both at N_b leaves their dot product unchanged).
 template <int DR>
 __global__ __launch_bounds__(kTokTile) void rope_scores_kernel(RopeScoreParams p) {
-  extern __shared__ float q_s[];  // [H][d_r] rotated rotary queries, times scale_log2
+  extern __shared__ float q_s[];  // [H][DR] rotated rotary queries times scale_log2
+  constexpr int half = DR / 2;
+  constexpr int KS = DR / 32;
   const int b = blockIdx.y;
   int nb = p.seq_lens != nullptr ? p.seq_lens[b] : p.n_max;
   nb = min(max(nb, 0), p.n_max);
   const int tok0 = blockIdx.x * kTokTile;
-  constexpr int half = DR / 2;
   const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + static_cast<size_t>(b) * p.H * DR;
   if (blockIdx.x == 0 && p.k_rope_self != nullptr) {
     const uint16_t* ks = static_cast<const uint16_t*>(p.k_rope_self) + static_cast<size_t>(b) * DR;
@@ -88,27 +101,60 @@ __global__ __launch_bounds__(kTokTile) void rope_scores_kernel(RopeScoreParams p
     q_s[h * DR + 2 * i + 1] = y1 * p.scale_log2;
   }
   __syncthreads();
-  const int tok = tok0 + threadIdx.x;
-  if (tok >= nb) return;
-  const uint4* kr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k_rope) +
-                                                   (static_cast<size_t>(b) * p.n_max + tok) * DR);
-  float k[DR];
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const uint16_t* kbase = static_cast<const uint16_t*>(p.k_rope) + static_cast<size_t>(b) * p.n_max * DR;
+  float* sbase = p.sr + static_cast<size_t>(b) * p.H * p.n_max;
+  for (int hg = 0; hg < p.H; hg += 16) {
+    // A operand: lane (head hg + col, group g) holds q_r[head][32 ks + 8 g .. + 7], hi and lo
+    uint4 qh[KS], ql[KS];
+    const int head = hg + col;
 #pragma unroll
-  for (int cch = 0; cch < DR / 8; ++cch) {
-    const uint4 w = kr[cch];
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    for (int ks = 0; ks < KS; ++ks) {
+      uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      k[8 * cch + 2 * e] = bf16_lo(ws[e]);
-      k[8 * cch + 2 * e + 1] = bf16_hi(ws[e]);
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int j = 32 * ks + 8 * g + 2 * e2;
+        const float v0 = head < p.H ? q_s[head * DR + j] : 0.f;
+        const float v1 = head < p.H ? q_s[head * DR + j + 1] : 0.f;
+        hw[e2] = f32x2_to_bf16x2(v0, v1);
+        lw[e2] = f32x2_to_bf16x2(v0 - bf16_lo(hw[e2]), v1 - bf16_hi(hw[e2]));
+      }
+      qh[ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      ql[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
-  }
-  float* out = p.sr + static_cast<size_t>(b) * p.H * p.n_max + tok;
-  for (int h = 0; h < p.H; ++h) {
-    float acc = 0.f;
+    // every block's key operands are loaded before any is used (tokens past N_b read as zeros)
+    constexpr int NB = kTokTile / 64;  // 16-token blocks per wave
+    uint4 kb[NB][KS];
 #pragma unroll
-    for (int j = 0; j < DR; ++j) acc += q_s[h * DR + j] * k[j];
-    out[static_cast<size_t>(h) * p.n_max] = acc;
+    for (int blk = 0; blk < NB; ++blk) {
+      const int row = tok0 + (4 * wave + blk) * 16 + col;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kb[blk][ks] = row < nb ? *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(row) * DR + 32 * ks + 8 * g)
+                               : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const int row = tok0 + (4 * wave + blk) * 16 + col;  // B operand column (token) of this lane
+      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        acc = mfma16(qh[ks], kb[blk][ks], acc);
+        acc = mfma16(ql[ks], kb[blk][ks], acc);
+      }
+      // C: lane (token row, group g) holds heads hg + 4 g + e
+      if (row < nb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int hh = hg + 4 * g + e;
+          if (hh < p.H) sbase[static_cast<size_t>(hh) * p.n_max + row] = acc[e];
+        }
+      }
+    }
   }
 }
 
