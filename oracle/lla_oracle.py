@@ -497,3 +497,43 @@ def attend_decode_rope(q, q_rope, zk, zv, k_rope, Wk, Wv, t, seq_lens=None, mu_k
                 V = np.concatenate([V, v_self[b, h][None, :]], axis=0)
             o[b, h], lse[b, h] = softmax_attention(np.concatenate([q[b, h], qr[h]]), K, V, scale)
     return o, lse
+
+
+def attend_prefill_rope(q, q_rope, zk, zv, k_rope, Wk, Wv, t, ctx_lens, mu_k=None, mu_v=None,
+                        base=10000.0, scale=None, variant="per_head"):
+    """Chunked-prefill attention with the decoupled rotary branch, by explicit reconstruction.
+
+    Row j of sequence b sits at position ctx_lens[b] + j and attends latents 0 .. ctx_lens[b] + j
+    (the chunk's own latents and rotary keys are already cached, as in attend_prefill). Key i is
+    [rebuilt content key ; k_rope[b, i]] (rotary keys stored rotated at their slot), the row's
+    query is [q ; rope(q_rope, its position)], values are the content values. Scale defaults to
+    1/sqrt(d_head + d_rope).
+
+    q [B,C,H,d]; q_rope [B,C,H,d_r]; k_rope [B,n_max,d_r]; the rest as attend_prefill.
+    Returns o [B,C,H,d].
+    """
+    _check_variant(variant)
+    q, q_rope = _f64(q), _f64(q_rope)
+    zk, zv, Wk, Wv, k_rope = _f64(zk), _f64(zv), _f64(Wk), _f64(Wv), _f64(k_rope)
+    mu_k, mu_v = _f64(mu_k), _f64(mu_v)
+    B, C, H, d = q.shape
+    dr = q_rope.shape[-1]
+    n_max = zk.shape[2] if variant == "per_head" else zk.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d + dr)
+    o = np.zeros((B, C, H, d), dtype=np.float64)
+    for b in range(B):
+        base_pos = int(ctx_lens[b])
+        last = min(base_pos + C, n_max)
+        for h in range(H):
+            wk, wv, muk, muv = _loop_slices(variant, Wk, Wv, mu_k, mu_v, t, h, H, d)
+            lat_k = zk[b, h] if variant == "per_head" else zk[b]
+            lat_v = zv[b, h] if variant == "per_head" else zv[b]
+            K = np.concatenate([reconstruct(lat_k[:last], wk, muk), k_rope[b, :last]], axis=1)
+            V = reconstruct(lat_v[:last], wv, muv)
+            for j in range(C):
+                pos = base_pos + j
+                n = min(pos + 1, n_max)
+                qq = np.concatenate([q[b, j, h], rope_rotate(q_rope[b, j, h], pos, base)])
+                o[b, j, h], _ = softmax_attention(qq, K[:n], V[:n], scale)
+    return o

@@ -147,6 +147,17 @@ def _rope_decode_content_scale(q, q_rope, zk, zv, k_rope, Wk, Wv, t, seq_lens=No
                                        k_self, v_self, k_rope_self, base, scale, variant)
 
 
+def _rope_prefill_rows_at_context_start(q, q_rope, zk, zv, k_rope, Wk, Wv, t, ctx_lens,
+                                        mu_k=None, mu_v=None, base=10000.0, scale=None,
+                                        variant="per_head"):
+    # every row's rotary query rotated at ctx instead of ctx + j: undo the extra turn of row j
+    qr = np.asarray(q_rope, np.float64).copy()
+    for j in range(qr.shape[1]):
+        qr[:, j] = O.rope_rotate(qr[:, j], -j, base)
+    return _orig["attend_prefill_rope"](q, qr, zk, zv, k_rope, Wk, Wv, t, ctx_lens, mu_k, mu_v,
+                                        base, scale, variant)
+
+
 _orig = {
     "encode_stack": O.encode_stack,
     "reconstruct": O.reconstruct,
@@ -157,6 +168,7 @@ _orig = {
     "quantize_latent_rows": O.quantize_latent_rows,
     "rope_rotate": O.rope_rotate,
     "attend_decode_rope": O.attend_decode_rope,
+    "attend_prefill_rope": O.attend_prefill_rope,
 }
 
 MUTANTS = {
@@ -179,6 +191,7 @@ MUTANTS = {
     "rope pairs channels i and i + d/2": ("rope_rotate", _rope_half_split),
     "rope query rotated one position back": ("attend_decode_rope", _rope_decode_query_one_back),
     "rope decode scales by the content width only": ("attend_decode_rope", _rope_decode_content_scale),
+    "rope prefill rows rotated at the chunk start": ("attend_prefill_rope", _rope_prefill_rows_at_context_start),
 }
 
 PINS = [
@@ -200,6 +213,7 @@ PINS = [
     R.test_rotation_closed_form_and_identity,
     R.test_full_rank_codec_equals_sdpa_on_concatenated_keys,
     R.test_common_position_shift_changes_nothing,
+    R.test_prefill_full_rank_codec_equals_causal_sdpa_on_concatenated_keys,
 ]
 
 

@@ -110,3 +110,52 @@ def test_common_position_shift_changes_nothing():
                               c["mu_k"], c["mu_v"], c["ks"], c["vs"], krs1)
     np.testing.assert_allclose(a[0], b_[0], atol=1e-11, rtol=0)
     np.testing.assert_allclose(a[1], b_[1], atol=1e-11, rtol=0)
+
+
+def test_prefill_zero_rotary_query_is_the_content_prefill():
+    rng = np.random.default_rng(6)
+    B, C, H, d, T, r, n, dr = 2, 3, 2, 4, 2, 6, 9, 4
+    zk, zv = rng.standard_normal((B, H, n, r)), rng.standard_normal((B, H, n, r))
+    Wk, Wv = rng.standard_normal((T, H, d, r)), rng.standard_normal((T, H, d, r))
+    q = rng.standard_normal((B, C, H, d))
+    kr = rng.standard_normal((B, n, dr))
+    ctx = np.array([5, 0])
+    a = O.attend_prefill_rope(q, np.zeros((B, C, H, dr)), zk, zv, kr, Wk, Wv, 1, ctx, scale=0.4)
+    b_ = O.attend_prefill(q, zk, zv, Wk, Wv, 1, ctx, scale=0.4)
+    np.testing.assert_allclose(a, b_, atol=1e-12, rtol=0)
+
+
+def test_prefill_full_rank_codec_equals_causal_sdpa_on_concatenated_keys():
+    rng = np.random.default_rng(7)
+    B, C, H, d, T, dr = 2, 4, 2, 4, 2, 6
+    r = T * d
+    ctx = np.array([3, 0])
+    n = 8
+    E = np.zeros((H, r, r))
+    W = np.zeros((T, H, d, r))
+    for h in range(H):
+        V, _ = np.linalg.qr(rng.standard_normal((r, r)))
+        E[h] = V.T
+        for t in range(T):
+            W[t, h] = V[t * d:(t + 1) * d]
+    xk = rng.standard_normal((B, n, T, H, d))
+    xv = rng.standard_normal((B, n, T, H, d))
+    zk, zv = O.encode_into_cache(np.zeros((B, H, n, r)), np.zeros((B, H, n, r)), xk, xv, E, E,
+                                 np.zeros(B, dtype=np.int64))
+    kr_raw = rng.standard_normal((B, n, dr))
+    kr = O.rope_rotate(kr_raw, np.arange(n)[None, :])
+    q, qr = rng.standard_normal((B, C, H, d)), rng.standard_normal((B, C, H, dr))
+    t = 1
+    o = O.attend_prefill_rope(q, qr, zk, zv, kr, W, W, t, ctx)
+    for b in range(B):
+        m = int(ctx[b]) + C
+        for h in range(H):
+            K = np.concatenate([xk[b, :m, t, h], O.rope_rotate(kr_raw[b, :m], np.arange(m))], axis=1)
+            pos = int(ctx[b]) + np.arange(C)
+            Q = np.concatenate([q[b, :, h], O.rope_rotate(qr[b, :, h], pos)], axis=1)
+            mask = np.arange(m)[None, :] <= pos[:, None]
+            ref = F.scaled_dot_product_attention(
+                torch.from_numpy(Q)[None, None], torch.from_numpy(K)[None, None],
+                torch.from_numpy(xv[b, :m, t, h])[None, None],
+                attn_mask=torch.from_numpy(mask)[None, None])[0, 0].numpy()
+            np.testing.assert_allclose(o[b, :, h], ref, atol=1e-10, rtol=0)
