@@ -603,6 +603,12 @@ def lla2d_prefill(args):
     ms_enc = _timed(encode, 3, 1)
     ms_att = _timed(lambda: attend(0), 3, 1)
     ms_step = _timed(step, 2, 1)
+    # the same loop read with a 64-wide decoupled rotary branch (lla_attend_prefill_rope)
+    d_rope = 64
+    kr = synth.device_normal_(torch.empty(B, n_max, d_rope, dtype=bf, device="cuda"), 9997)
+    qr = synth.device_normal_(torch.empty(B, C, H, d_rope, dtype=bf, device="cuda"), 10001)
+    ms_rope = _timed(lambda: lla.lla_attend_prefill_rope(desc, B, C, 0, q[0], qr, zk, zv, kr, d_rope,
+                                                         0.0, ctx, Wk, Wv, None, None, out, ws), 3, 1)
     keys = sum(N + j + 1 for j in range(C))                  # per (sequence, head)
     att_flops = 2.0 * B * H * keys * 2 * r                   # scores + latent-V products
     proj_flops = 2.0 * B * C * H * d * 2 * r                 # q~ and output projections
@@ -611,6 +617,7 @@ def lla2d_prefill(args):
                         f"T={T}, r_k=r_v={r}, bf16",
             "tokens_per_s": round(B * C / (ms_step / 1e3), 1), "ms_per_chunk": round(ms_step, 3),
             "encode_ms": round(ms_enc, 3), "attend_ms_per_loop": round(ms_att, 3),
+            "attend_with_64_wide_rotary_branch_ms_per_loop": round(ms_rope, 3),
             "attend_TFLOPs": round((att_flops + proj_flops) / (ms_att / 1e3) / 1e12, 1),
             "attend_mfma_util_bf16_dense": round((att_flops + proj_flops) / (ms_att / 1e3) / 2.5e15, 4),
             "encode_TFLOPs": round(enc_flops / (ms_enc / 1e3) / 1e12, 1),

@@ -374,4 +374,56 @@ lla_status lla_attend_prefill(const lla_desc* desc, int32_t B, int32_t C, int32_
   return from_hip(lla::launch_prefill(p, desc->dtype, static_cast<hipStream_t>(stream)));
 }
 
+lla_status lla_attend_prefill_rope(const lla_desc* desc, int32_t B, int32_t C, int32_t t,
+                                   const void* q, const void* q_rope, const void* zk,
+                                   const void* zv, const void* k_rope, int32_t d_rope, float base,
+                                   const int32_t* ctx_lens, const void* Wk, const void* Wv,
+                                   const void* mu_k, const void* mu_v, void* out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  if (!desc_ok(desc) || B <= 0 || C <= 0 || t < 0 || t >= desc->T) return LLA_ERR_INVALID_ARG;
+  if (C > desc->n_max) return LLA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * C * desc->H >= (int64_t(1) << 31) / 64) return LLA_ERR_INVALID_ARG;
+  if (!req_ok(q) || !req_ok(q_rope) || !req_ok(zk) || !req_ok(zv) || !req_ok(k_rope) ||
+      !req_ok(ctx_lens) || !req_ok(Wk) || !req_ok(Wv) || !req_ok(out))
+    return LLA_ERR_INVALID_ARG;
+  if (!opt_ok(mu_k) || !opt_ok(mu_v) || !opt_ok(ws)) return LLA_ERR_INVALID_ARG;
+  if (!(base >= 0.f) || std::isinf(base)) return LLA_ERR_INVALID_ARG;
+  if (!lla::prefill_rope_supported(*desc, d_rope)) return LLA_ERR_UNSUPPORTED;
+  const size_t need = lla::prefill_workspace_bytes(*desc, B, C);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return LLA_ERR_WORKSPACE;
+
+  lla::PrefillParams p{};
+  p.q = q;
+  p.zk = zk;
+  p.zv = zv;
+  p.ctx_lens = ctx_lens;
+  p.Wk = Wk;
+  p.Wv = Wv;
+  p.mu_k = mu_k;
+  p.mu_v = mu_v;
+  p.out = out;
+  p.ws = ws;
+  p.B = B;
+  p.C = C;
+  p.H = desc->H;
+  p.d = desc->d_head;
+  p.T = desc->T;
+  p.t = t;
+  p.n_max = desc->n_max;
+  p.r_k = desc->r_k;
+  p.r_v = desc->r_v;
+  p.variant = desc->variant;
+  // the concatenated (content, rotary) key is d_head + d_rope wide
+  const float sc = desc->scale > 0.f ? desc->scale
+                                     : 1.0f / std::sqrt(static_cast<float>(desc->d_head + d_rope));
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.ws_bytes = ws == nullptr ? 0 : ws_bytes;
+  p.q_rope = q_rope;
+  p.k_rope = k_rope;
+  p.d_rope = d_rope;
+  p.rope_base = base > 0.f ? base : 10000.0;
+  lla::prefill_plan(*desc, B, C, &p.splits, &p.chunk);
+  return from_hip(lla::launch_prefill(p, desc->dtype, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

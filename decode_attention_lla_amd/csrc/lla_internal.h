@@ -108,6 +108,12 @@ struct PrefillParams {
   int32_t splits, chunk;  // from prefill_plan
   float scale_log2;
   size_t ws_bytes;
+  // Rotary branch (lla_attend_prefill_rope; d_rope == 0 without it): q_rope [B][C][H][d_rope]
+  // unrotated, k_rope [B][n_max][d_rope] rotated at each slot, RoFormer base.
+  const void* q_rope;
+  const void* k_rope;
+  int32_t d_rope;
+  double rope_base;
 };
 
 // Token-split plan of one lla_attend_decode call. The C ABI computes it once per call, sizes the
@@ -154,5 +160,6 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, hipStream_t s);
 bool decode_supported(int variant, int dtype, int r_k, int r_v, int d_head);
 bool encode_supported(int dtype, int r);
 bool prefill_supported(int variant, int dtype, int r_k, int r_v);
+bool prefill_rope_supported(const lla_desc& desc, int d_rope);
 
 }  // namespace lla

@@ -170,9 +170,18 @@ __device__ __forceinline__ void wait_vm_tiles(int ahead) {
   }
 }
 
-template <int RK, int RV>
+// DR > 0: the decoupled rotary branch. Each key also has a DR-wide rotary key (shared by heads,
+// rotated at its slot) in a third tile per ring stage, each row a rotary query rotated at the row's
+// position; KR = DR / 32 more contraction steps add q_r . k_r to the score accumulators.
+template <int RK, int RV, int DR = 0>
 __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, PrefillWs w) {
   constexpr int KS = RK / 32;
+  constexpr int KR = DR / 32;
+  constexpr int CPR = DR / 8;                 // 16-byte chunks per rotary row
+  constexpr int RR_BYTES = DR > 0 ? kKeyTile * DR * 2 : 1024;
+  constexpr int IR = RR_BYTES / 1024;
+  constexpr int LR = DR > 0 ? (IR >= 8 ? IR / 8 : 1) : 0;  // rotary loads per wave and tile
+  static_assert(DR == 0 || DR == 64 || DR == 128, "rotary rows of 8 or 16 chunks");
   constexpr int RT = RV / 16;
   constexpr int CPK = RK / 8;                 // 16-byte chunks per K row
   constexpr int NRQ = RV / 16;                // 16-entry blocks per key quad of a V tile
@@ -185,10 +194,12 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   static_assert(RK % 64 == 0 && RV % 64 == 0, "swizzle windows need 8 chunks per row");
   static_assert(IK % 8 == 0 || 8 % IK == 0, "K tile instructions spread evenly over 8 waves");
   static_assert(IV % 8 == 0 || 8 % IV == 0, "V tile instructions spread evenly over 8 waves");
-  static_assert(3 * (LK + LV) < 64, "vmcnt range");
+  static_assert(3 * (LK + LV + LR) < 64, "vmcnt range");
   // one __shared__ object per ring stage, always named statically (see StageIdx)
   __shared__ __attribute__((aligned(16))) char kb0[KT_BYTES], kb1[KT_BYTES], kb2[KT_BYTES], kb3[KT_BYTES];
   __shared__ __attribute__((aligned(16))) char vb0[VT_BYTES], vb1[VT_BYTES], vb2[VT_BYTES], vb3[VT_BYTES];
+  __shared__ __attribute__((aligned(16))) char rb0[DR > 0 ? RR_BYTES : 16], rb1[DR > 0 ? RR_BYTES : 16],
+      rb2[DR > 0 ? RR_BYTES : 16], rb3[DR > 0 ? RR_BYTES : 16];
   static_assert(kStages == 4, "four named stages");
   auto kstage = [&](auto S) -> char* {
     constexpr int st = decltype(S)::value;
@@ -199,6 +210,11 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     constexpr int st = decltype(S)::value;
     if constexpr (st == 0) return vb0; else if constexpr (st == 1) return vb1;
     else if constexpr (st == 2) return vb2; else return vb3;
+  };
+  auto rstage = [&](auto S) -> char* {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return rb0; else if constexpr (st == 1) return rb1;
+    else if constexpr (st == 2) return rb2; else return rb3;
   };
 
   const int tid = threadIdx.x;
@@ -276,6 +292,34 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
       ql[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
   }
+  // Rotary query fragments (B operand of the extra steps, same element order as the rotary tile's
+  // chunks): lane (row, g) holds channels 32 kr + 8 g .. + 7 of the row's rotary query, rotated at
+  // the row's position ctx + jr (float64 angles), times scale*log2e, as bf16 hi + lo.
+  uint4 qrh[KR > 0 ? KR : 1], qrl[KR > 0 ? KR : 1];
+  if constexpr (DR > 0) {
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + (tok * p.H + h) * DR;
+    const double pos = static_cast<double>(ctx) + (rvalid ? jr : 0);
+#pragma unroll
+    for (int kr = 0; kr < KR; ++kr) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(qr + 32 * kr + 8 * g);
+      const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int i = 16 * kr + 4 * g + e2;  // channel pair (2i, 2i + 1)
+        const double theta = pow(p.rope_base, -2.0 * i / DR);
+        double sn, cs;
+        sincos(pos * theta, &sn, &cs);
+        const float x0 = bf16_lo(rw[e2]), x1 = bf16_hi(rw[e2]);
+        const float y0 = static_cast<float>(x0 * cs - x1 * sn) * p.scale_log2;
+        const float y1 = static_cast<float>(x0 * sn + x1 * cs) * p.scale_log2;
+        hw[e2] = f32x2_to_bf16x2(y0, y1);
+        lw[e2] = f32x2_to_bf16x2(y0 - bf16_lo(hw[e2]), y1 - bf16_hi(hw[e2]));
+      }
+      qrh[kr] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      qrl[kr] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+  }
 
   // Cooperative tile fetch into ring stage (kd, vd) as buffer loads over this sequence's latents
   // 0 .. kmax: each lane's byte offset inside a tile is fixed, the tile's position moves in the
@@ -283,7 +327,18 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   // the end) land as zeros. Keys past a row's limit are masked, so those zeros are never weighed.
   const int kbytes = (kmax + 1) * RK * 2;
   const int vbytes = (kmax + 1) * RV * 2;
-  uint32_t koff[LK], voff[LV];
+  const int rbytes = (kmax + 1) * DR * 2;
+  const char* zr = DR > 0 ? static_cast<const char*>(p.k_rope) + static_cast<size_t>(b) * p.n_max * DR * 2
+                          : nullptr;
+  uint32_t koff[LK], voff[LV], roff[LR > 0 ? LR : 1];
+#pragma unroll
+  for (int u = 0; u < LR; ++u) {
+    const int i = IR >= 8 ? wave + 8 * u : wave % IR;
+    const int f = i * 64 + lane;
+    const int row = f / CPR;
+    const int pc = f - row * CPR;
+    roff[u] = (row * DR + k_chunk_slot<CPR>(row, pc) * 8) * 2;
+  }
 #pragma unroll
   for (int u = 0; u < LK; ++u) {
     const int i = IK >= 8 ? wave + 8 * u : wave % IK;
@@ -304,8 +359,13 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     const int r8 = 2 * rq + (U & 1);
     voff[u] = (key * RV + r8 * 8) * 2;
   }
-  auto issue = [&](int tile, char* kd, char* vd) {
+  auto issue = [&](int tile, char* kd, char* vd, char* rd) {
     const uint32_t key0 = tile * kKeyTile;
+#pragma unroll
+    for (int u = 0; u < LR; ++u) {
+      const int i = IR >= 8 ? wave + 8 * u : wave % IR;
+      buffer_lds16(zr, rbytes, (lptr_t)(rd + i * 1024), roff[u], key0 * DR * 2);
+    }
 #pragma unroll
     for (int u = 0; u < LK; ++u) {
       const int i = IK >= 8 ? wave + 8 * u : wave % IK;
@@ -343,13 +403,15 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   auto step = [&](auto S, int tile) {
     constexpr int st = decltype(S)::value;
     // this wave's loads of `tile` have landed (tiles + 1 and + 2 may still be in flight) ...
-    wait_vm_tiles<LK + LV>(kStages - 2);
+    wait_vm_tiles<LK + LV + LR>(kStages - 2);
     // ... and every other wave's; everyone has also finished computing tile - 1, whose stage is
     // the one refilled next
     ring_barrier();
     issue(tile + kStages - 1, kstage(StageIdx<(st + kStages - 1) % kStages>{}),
-          vstage(StageIdx<(st + kStages - 1) % kStages>{}));
+          vstage(StageIdx<(st + kStages - 1) % kStages>{}),
+          rstage(StageIdx<(st + kStages - 1) % kStages>{}));
     const char* kt = kstage(S);
+    const char* rt_ = rstage(S);
     const char* vt = vstage(S);
     const int key0 = tile * kKeyTile;
     float sc[2][4];
@@ -368,6 +430,13 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
         const uint4 a = *reinterpret_cast<const uint4*>(kt + row * RK * 2 + pc * 16);
         sh = mfma32(a, qh[ks], sh);
         sl = mfma32(a, ql[ks], sl);
+      }
+#pragma unroll
+      for (int kr = 0; kr < KR; ++kr) {
+        const int pc = k_chunk_slot<CPR>(row, 4 * kr + g);
+        const uint4 a = *reinterpret_cast<const uint4*>(rt_ + row * DR * 2 + pc * 16);
+        sh = mfma32(a, qrh[kr], sh);
+        sl = mfma32(a, qrl[kr], sl);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) sc[kt16][e] = sh[e] + sl[e];
@@ -409,6 +478,8 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     const bf16x8_t pb = __builtin_bit_cast(
         bf16x8_t, make_uint4(f32x2_to_bf16x2(pe[0][0], pe[0][1]), f32x2_to_bf16x2(pe[0][2], pe[0][3]),
                              f32x2_to_bf16x2(pe[1][0], pe[1][1]), f32x2_to_bf16x2(pe[1][2], pe[1][3])));
+    // the rotary fragments leave no room to hoist the P.V operand reads into the score phase
+    if constexpr (DR > 0) __builtin_amdgcn_sched_barrier(0);
     // A^T[r][row] += Z^V^T[r][keys] . P^T
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -422,9 +493,9 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     // the Q~ loads land before any tile is requested, so the tile loop never has to
     // wait for them
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-    issue(0, kb0, vb0);
-    issue(1, kb1, vb1);
-    issue(2, kb2, vb2);
+    issue(0, kb0, vb0, rb0);
+    issue(1, kb1, vb1, rb1);
+    issue(2, kb2, vb2, rb2);
     for (int tile = 0; tile < ntiles; tile += kStages) {
       step(StageIdx<0>{}, tile);
       step(StageIdx<1>{}, tile + 1);
@@ -493,11 +564,14 @@ struct EntryP {
   int r_k, r_v;
   void (*wkt)(PrefillParams, uint16_t*);
   void (*attn)(PrefillParams, PrefillWs);
+  void (*attn_r64)(PrefillParams, PrefillWs);   // with a 64-wide rotary branch
+  void (*attn_r128)(PrefillParams, PrefillWs);  // with a 128-wide rotary branch
 };
 
 template <int RK, int RV>
 constexpr EntryP entryP() {
-  return {RK, RV, wk_transpose_kernel<RK>, prefill_attn_kernel<RK, RV>};
+  return {RK, RV, wk_transpose_kernel<RK>, prefill_attn_kernel<RK, RV>,
+          prefill_attn_kernel<RK, RV, 64>, prefill_attn_kernel<RK, RV, 128>};
 }
 
 const EntryP kTableP[] = {
@@ -517,6 +591,12 @@ bool mfma_prefill(int dtype, int r_k, int r_v, int d_head, int n_max) {
 }
 
 }  // namespace
+
+bool prefill_rope_supported(const lla_desc& desc, int d_rope) {
+  return (d_rope == 64 || d_rope == 128) &&
+         mfma_prefill(desc.dtype, desc.r_k, desc.r_v, desc.d_head, desc.n_max) &&
+         static_cast<long>(desc.n_max) * d_rope * 2 < 0x7fffffffL;
+}
 
 bool prefill_supported(int variant, int dtype, int r_k, int r_v) {
   return valu_supported(variant, dtype, r_k, r_v) || (dtype == LLA_BF16 && findP(r_k, r_v) != nullptr);
@@ -549,7 +629,8 @@ hipError_t launch_prefill(const PrefillParams& pp, int dtype, hipStream_t stream
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const unsigned nwg = static_cast<unsigned>((pp.C + kRowsWG - 1) / kRowsWG) * pp.H * pp.B;
-    hipLaunchKernelGGL(e->attn, dim3(nwg), dim3(512), 0, stream, pp, w);
+    auto attn = pp.d_rope == 64 ? e->attn_r64 : pp.d_rope == 128 ? e->attn_r128 : e->attn;
+    hipLaunchKernelGGL(attn, dim3(nwg), dim3(512), 0, stream, pp, w);
     return hipGetLastError();
   }
   DecodeParams p{};

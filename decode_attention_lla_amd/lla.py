@@ -86,6 +86,9 @@ def _load():
     lib.lla_attend_decode_rope.argtypes = [_D, _I, _I, _P, _P, _P, _P, _P, _I, ctypes.c_float,
                                            _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.c_size_t, _P]
+    lib.lla_attend_prefill_rope.restype = _I
+    lib.lla_attend_prefill_rope.argtypes = [_D, _I, _I, _I, _P, _P, _P, _P, _P, _I, ctypes.c_float,
+                                            _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.lla_reconstruct_workspace_bytes.restype = ctypes.c_size_t
     lib.lla_reconstruct_workspace_bytes.argtypes = [_D, _I]
     lib.lla_attend_decode_reconstruct.restype = _I
@@ -283,6 +286,29 @@ def lla_attend_decode_rope(desc, B, t, q, q_rope, zk, zv, k_rope, d_rope, base, 
     st = _load().lla_attend_decode_rope(ctypes.byref(desc), int(B), int(t), *args,
                                         ctypes.c_size_t(ws_bytes), _stream_ptr(stream))
     _check(st, "lla_attend_decode_rope")
+
+
+def lla_attend_prefill_rope(desc, B, C, t, q, q_rope, zk, zv, k_rope, d_rope, base, ctx_lens,
+                            Wk, Wv, mu_k, mu_v, out, ws=None, stream=None):
+    dt = _TORCH_DTYPE[desc.dtype]
+    s = _shapes(desc, B)
+    qs = (B, C, desc.H, desc.d_head)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    if ws is not None and (ws.device.type != "cuda" or not ws.is_contiguous()):
+        raise ValueError("ws must be a contiguous device tensor")
+    args = [
+        _ptr(q, "q", qs, dt), _ptr(q_rope, "q_rope", (B, C, desc.H, d_rope), torch.bfloat16),
+        _ptr(zk, "zk", s["zk"], _zdt(desc)), _ptr(zv, "zv", s["zv"], _zdt(desc)),
+        _ptr(k_rope, "k_rope", (B, desc.n_max, d_rope), torch.bfloat16),
+        ctypes.c_int32(int(d_rope)), ctypes.c_float(base),
+        _ptr(ctx_lens, "ctx_lens", (B,), torch.int32),
+        _ptr(Wk, "Wk", s["Wk"], dt), _ptr(Wv, "Wv", s["Wv"], dt),
+        _ptr(mu_k, "mu_k", s["mu"], dt, True), _ptr(mu_v, "mu_v", s["mu"], dt, True),
+        _ptr(out, "out", qs, dt), None if ws is None else ws.data_ptr(),
+    ]
+    st = _load().lla_attend_prefill_rope(ctypes.byref(desc), int(B), int(C), int(t), *args,
+                                         ctypes.c_size_t(ws_bytes), _stream_ptr(stream))
+    _check(st, "lla_attend_prefill_rope")
 
 
 def lla_reconstruct_workspace_bytes(desc, B):

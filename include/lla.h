@@ -195,6 +195,22 @@ lla_status lla_attend_decode_rope(const lla_desc* desc, int32_t B, int32_t t, co
                                   const void* v_self, const void* k_rope_self, void* out,
                                   float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* lla_attend_prefill with the rotary branch: row j of sequence b sits at position ctx_lens[b] + j
+ * and attends latents 0 .. ctx_lens[b] + j, key i being [k_i ; k_rope[b][i]] and the row's query
+ * [q ; rope(q_rope, ctx_lens[b] + j)]; the chunk's rotary keys must already be in k_rope (written
+ * by lla_rope_write at slots ctx_lens[b] .. + C - 1, like its latents by lla_encode). Scale as in
+ * lla_attend_decode_rope (default 1/sqrt(d_head + d_rope)).
+ *   q_rope [device] bf16 [B][C][H][d_rope], unrotated; k_rope as above; ws at least
+ *   lla_workspace_bytes(desc, B, C).
+ * MFMA path only: LLA_BF16, the chunked-prefill MFMA (r_k, r_v) pairs, d_head a multiple of 32,
+ * d_rope 64 or 128; otherwise LLA_ERR_UNSUPPORTED. */
+lla_status lla_attend_prefill_rope(const lla_desc* desc, int32_t B, int32_t C, int32_t t,
+                                   const void* q, const void* q_rope, const void* zk,
+                                   const void* zv, const void* k_rope, int32_t d_rope, float base,
+                                   const int32_t* ctx_lens, const void* Wk, const void* Wv,
+                                   const void* mu_k, const void* mu_v, void* out, void* ws,
+                                   size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace that lla_attend_decode_reconstruct needs for B sequences: the rebuilt
  * K and V of every slot ([B][H][n_max][d_head] bf16 each), identity factors and split partials.
  * 0 for an invalid descriptor. */

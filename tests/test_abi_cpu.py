@@ -282,3 +282,21 @@ def test_rope_arguments_support_and_workspace():
     assert w(d, C=101) == lla.LLA_ERR_INVALID_ARG
     assert w(d, pos=N) == lla.LLA_ERR_INVALID_ARG
     assert w(desc(dtype=lla.LLA_F32, n_max=100)) == lla.LLA_ERR_INVALID_ARG
+
+
+def test_prefill_rope_arguments_and_support():
+    lib = lla.library()
+
+    def call(d, B=2, C=4, t=0, d_rope=64, base=0.0, **kw):
+        a = dict(q=A, qr=A, zk=A, zv=A, kr=A, ctx=A, Wk=A, Wv=A, out=A, ws=N, wsb=0)
+        a.update(kw)
+        return lib.lla_attend_prefill_rope(ctypes.byref(d), B, C, t, a["q"], a["qr"], a["zk"],
+                                           a["zv"], a["kr"], d_rope, ctypes.c_float(base),
+                                           a["ctx"], a["Wk"], a["Wv"], N, N, a["out"], a["ws"],
+                                           ctypes.c_size_t(a["wsb"]), S)
+    d = desc(variant=lla.LLA_2D, r_k=256, r_v=256, n_max=100)
+    for kw in (dict(qr=N), dict(kr=M), dict(ctx=N), dict(base=-2.0), dict(C=101), dict(t=4)):
+        assert call(d, **kw) == lla.LLA_ERR_INVALID_ARG, kw
+    assert call(d, d_rope=32) == lla.LLA_ERR_UNSUPPORTED
+    assert call(desc(r_k=24, r_v=24, n_max=100)) == lla.LLA_ERR_UNSUPPORTED  # no MFMA prefill
+    assert call(d) == lla.LLA_ERR_WORKSPACE

@@ -148,3 +148,58 @@ def test_capacity_rope_full_size_sampled():
         assert_lse(host(lse)[rows], rl, f"capacity rope t={t}")
     del g
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("variant,rk,rv,d_rope", [("per_head", 128, 128, 64), ("2d", 256, 256, 64),
+                                                  ("2d", 256, 256, 128), ("per_head", 64, 128, 128),
+                                                  ("2d", 128, 256, 64)])
+def test_prefill_rope(variant, rk, rv, d_rope):
+    """Chunked prefill with the rotary branch on the MFMA path: 150 rows (two row blocks, ragged),
+    three contexts (one empty), mu on, against the oracle."""
+    B, C, H, d, T, n_max = 3, 150, 2, 64, 2, 1200
+    desc = mk_desc(variant, "bf16", H, d, T, rk, rv, n_max)
+    rng = np.random.default_rng(9990 + rk + d_rope)
+    c = upload(synth.random_case(variant, "bf16", B, H, d, T, rk, rv, n_max, 9991 + rk), "bf16")
+    q = synth.to_storage(rng.standard_normal((B, C, H, d)).astype(np.float32), "bf16")
+    q_rope = synth.to_storage(rng.standard_normal((B, C, H, d_rope)).astype(np.float32), "bf16")
+    k_rope = synth.to_storage(rng.standard_normal((B, n_max, d_rope)).astype(np.float32), "bf16")
+    ctx = np.array([300, 0, 1000], np.int32)
+    out = torch.empty(B, C, H, d, dtype=torch.bfloat16, device="cuda")
+    for t in range(T):
+        lla.lla_attend_prefill_rope(desc, B, C, t, dev(q, "bf16"), dev(q_rope, "bf16"), c["_zk"],
+                                    c["_zv"], dev(k_rope, "bf16"), d_rope, 0.0, dev(ctx), c["_Wk"],
+                                    c["_Wv"], c["_muk"], c["_muv"], out, lla.workspace(desc, B, C))
+        torch.cuda.synchronize()
+        ref = O.attend_prefill_rope(q, q_rope, c["zk"], c["zv"], k_rope, c["Wk"], c["Wv"], t, ctx,
+                                    c["mu_k"], c["mu_v"], variant=variant)
+        assert_close(host(out), ref, "bf16", f"prefill rope {variant} ({rk},{rv}) d_rope={d_rope} t={t}")
+
+
+def test_lla2d_prefill_rope_full_size_sampled():
+    """The LLA-2D 512-token prefill benchmark shape (B=128, C=512, N_ctx=8192, r=256) with a
+    64-wide rotary branch; rows {0, 255, 511} of sequence 0, all heads."""
+    s = synth.CASES["lla2d"]
+    B, C, H, d, T, r, N = s.B, s.C, s.H, s.d, s.T, s.r_k, s.N
+    n_max = N + C
+    d_rope = 64
+    desc = mk_desc("2d", "bf16", H, d, T, r, r, n_max)
+    zk = synth.device_normal_(torch.empty(B, n_max, r, dtype=torch.bfloat16, device="cuda"), 9995)
+    zv = synth.device_normal_(torch.empty(B, n_max, r, dtype=torch.bfloat16, device="cuda"), 9996)
+    kr = synth.device_normal_(torch.empty(B, n_max, d_rope, dtype=torch.bfloat16, device="cuda"), 9997)
+    Wk = synth.orthonormal_W_2d(T, H, d, r, 9998, "bf16")
+    Wv = synth.orthonormal_W_2d(T, H, d, r, 9999, "bf16")
+    q = synth.device_normal_(torch.empty(B, C, H, d, dtype=torch.bfloat16, device="cuda"), 10000)
+    qr = synth.device_normal_(torch.empty(B, C, H, d_rope, dtype=torch.bfloat16, device="cuda"), 10001)
+    ctx = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, C, H, d, dtype=torch.bfloat16, device="cuda")
+    lla.lla_attend_prefill_rope(desc, B, C, 1, q, qr, zk, zv, kr, d_rope, 0.0, ctx, dev(Wk, "bf16"),
+                                dev(Wv, "bf16"), None, None, out, lla.workspace(desc, B, C))
+    torch.cuda.synchronize()
+    zk0, zv0, kr0 = host(zk[:1]), host(zv[:1]), host(kr[:1])
+    q0, qr0, o0 = host(q[:1]), host(qr[:1]), host(out[:1])
+    for j in (0, 255, 511):
+        ref = O.attend_prefill_rope(q0[:, j:j + 1], qr0[:, j:j + 1], zk0, zv0, kr0, Wk, Wv, 1,
+                                    [N + j], variant="2d")
+        assert_close(o0[:, j:j + 1], ref, "bf16", f"2d prefill rope row {j}")
+    del zk, zv, kr, q, qr, out
+    torch.cuda.empty_cache()
