@@ -475,49 +475,61 @@ def low_bit_capacity(args, bf16_tokens_per_s):
 
 
 def rope_decode(args):
-    """The decoupled rotary branch at the capacity shape (one layer: B=768, H=16, d=128, r=24/24,
-    4096 cached tokens, d_rope=64, one rotary key per token shared by heads and loops): a decode
-    read with the branch (rotary score pre-pass + streaming read) beside the same read without."""
+    """The decoupled rotary branch (d_rope=64, one rotary key per token shared by heads and loops)
+    on two decode reads, each beside the same read without the branch: the capacity layer (per
+    head, B=768, H=16, d=128, r=24/24, 4096 cached tokens; rotary score pre-pass + streaming read)
+    and the LLA-2D layer (B=128, H=16, d=128, r=256/256, 8192 cached tokens; pre-pass + MFMA read)."""
     import torch
     from decode_attention_lla_amd import lla, synth
-    s = synth.CASES["capacity"]
-    B, H, d, T, r, N = s.B, s.H, s.d, s.T, s.r_k, s.N
     d_rope = 64
-    n_max = N + 1
     bf = torch.bfloat16
-    desc = lla.make_desc(lla.LLA_PER_HEAD, lla.LLA_BF16, H, d, T, r, r, n_max)
-    zk = synth.device_normal_(torch.empty(B, H, n_max, r, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZK))
-    zv = synth.device_normal_(torch.empty(B, H, n_max, r, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZV))
-    Wk = torch.from_numpy(synth.orthonormal_W(T, H, d, r, synth.seed(s.case, synth.SEED_WK), "bf16")).to(bf).cuda()
-    Wv = torch.from_numpy(synth.orthonormal_W(T, H, d, r, synth.seed(s.case, synth.SEED_WV), "bf16")).to(bf).cuda()
-    q = synth.device_normal_(torch.empty(B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_Q))
-    ks = synth.device_normal_(torch.empty(B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF))
-    vs = synth.device_normal_(torch.empty(B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF) + 1)
-    kr = synth.device_normal_(torch.empty(B, n_max, d_rope, dtype=bf, device="cuda"), 9980)
-    qr = synth.device_normal_(torch.empty(B, H, d_rope, dtype=bf, device="cuda"), 9981)
-    krs = synth.device_normal_(torch.empty(B, d_rope, dtype=bf, device="cuda"), 9982)
-    out = torch.empty(B, H, d, dtype=bf, device="cuda")
-    lens = torch.full((B,), N, dtype=torch.int32, device="cuda")
-    ws = lla.workspace(desc, B)
-    ws_r = lla.rope_workspace(desc, B)
+    res = {}
+    for key in ("capacity", "lla2d"):
+        s = synth.CASES[key]
+        B, H, d, T, r, N = s.B, s.H, s.d, s.T, s.r_k, s.N
+        n_max = N + 1
+        two_d = s.variant == "2d"
+        desc = lla.make_desc(lla.LLA_2D if two_d else lla.LLA_PER_HEAD, lla.LLA_BF16, H, d, T, r, r,
+                             n_max)
+        zshape = (B, n_max, r) if two_d else (B, H, n_max, r)
+        zk = synth.device_normal_(torch.empty(zshape, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZK))
+        zv = synth.device_normal_(torch.empty(zshape, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZV))
+        mk_w = synth.orthonormal_W_2d if two_d else synth.orthonormal_W
+        Wk = torch.from_numpy(mk_w(T, H, d, r, synth.seed(s.case, synth.SEED_WK), "bf16")).to(bf).cuda()
+        Wv = torch.from_numpy(mk_w(T, H, d, r, synth.seed(s.case, synth.SEED_WV), "bf16")).to(bf).cuda()
+        q = synth.device_normal_(torch.empty(B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_Q))
+        ks = synth.device_normal_(torch.empty(B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF))
+        vs = synth.device_normal_(torch.empty(B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF) + 1)
+        kr = synth.device_normal_(torch.empty(B, n_max, d_rope, dtype=bf, device="cuda"), 9980)
+        qr = synth.device_normal_(torch.empty(B, H, d_rope, dtype=bf, device="cuda"), 9981)
+        krs = synth.device_normal_(torch.empty(B, d_rope, dtype=bf, device="cuda"), 9982)
+        out = torch.empty(B, H, d, dtype=bf, device="cuda")
+        lens = torch.full((B,), N, dtype=torch.int32, device="cuda")
+        ws = lla.workspace(desc, B)
+        ws_r = lla.rope_workspace(desc, B)
 
-    def plain():
-        lla.lla_attend_decode(desc, B, 0, q, zk, zv, lens, Wk, Wv, None, None, ks, vs, out, None, ws)
+        def plain():
+            lla.lla_attend_decode(desc, B, 0, q, zk, zv, lens, Wk, Wv, None, None, ks, vs, out, None, ws)
 
-    def with_rope():
-        lla.lla_attend_decode_rope(desc, B, 0, q, qr, zk, zv, kr, d_rope, 0.0, lens, Wk, Wv, None,
-                                   None, ks, vs, krs, out, None, ws_r)
+        def with_rope():
+            lla.lla_attend_decode_rope(desc, B, 0, q, qr, zk, zv, kr, d_rope, 0.0, lens, Wk, Wv,
+                                       None, None, ks, vs, krs, out, None, ws_r)
 
-    ms_p = _timed(plain, 20, 3)
-    ms_r = _timed(with_rope, 20, 3)
-    latent = B * H * N * 2 * r * 2
-    extra = B * N * d_rope * 2 + 2 * B * H * N * 4  # rotary keys once + scores written and read
-    return {"workload": f"capacity layer read with a {d_rope}-wide rotary branch: H={H}, "
-                        f"d_head={d}, r_k=r_v={r}, B={B}, N={N}, bf16",
+        ms_p = _timed(plain, 20, 3)
+        ms_r = _timed(with_rope, 20, 3)
+        latent = B * (1 if two_d else H) * N * 2 * r * 2
+        extra = B * N * d_rope * 2 + 2 * B * H * N * 4  # rotary keys once + scores written and read
+        name = "lla2d" if two_d else "capacity"
+        res[name] = {
+            "workload": f"{'LLA-2D' if two_d else 'capacity'} layer read with a {d_rope}-wide rotary "
+                        f"branch: H={H}, d_head={d}, r_k=r_v={r}, B={B}, N={N}, bf16",
             "read_us": round(ms_r * 1e3, 2), "read_without_rotary_us": round(ms_p * 1e3, 2),
             "algorithmic_GBps": round((latent + extra) / (ms_r / 1e3) / 1e9, 1),
             "algorithmic_frac_of_peak": round((latent + extra) / (ms_r / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "rotary_bytes_over_latent_bytes": round(extra / latent, 4)}
+        del zk, zv, kr, ws, ws_r
+        torch.cuda.empty_cache()
+    return res
 
 
 def long_context(args):

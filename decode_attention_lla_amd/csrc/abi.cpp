@@ -261,7 +261,7 @@ lla_status lla_attend_decode_rope(const lla_desc* desc, int32_t B, int32_t t, co
   const float sc = desc->scale > 0.f ? desc->scale
                                      : 1.0f / std::sqrt(static_cast<float>(desc->d_head + d_rope));
   p.scale_log2 = sc * 1.4426950408889634f;
-  lla::valu_plan(*desc, B, &p.splits, &p.chunk);
+  lla::decode_plan(*desc, B, &p.splits, &p.chunk);
   lla::RopeScoreParams rp{};
   rp.q_rope = q_rope;
   rp.k_rope = k_rope;

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
         slot[u] = ok[u] ? srow[tok] : 0;
         ok[u] = ok[u] && static_cast<unsigned>(slot[u]) < static_cast<unsigned>(p.n_max);
       }
-      srv[u] = (R && ok[u]) ? p.sr[static_cast<size_t>(bh) * p.n_max + slot[u]] : 0.f;
+      srv[u] = (R && ok[u]) ? p.sr[static_cast<size_t>(bh) * p.sr_stride + slot[u]] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -494,31 +494,40 @@ namespace {
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 }  // namespace
 
+int rope_sr_stride(int n_max) { return (n_max + 3) / 4 * 4; }
+
 size_t rope_workspace_bytes(const lla_desc& desc, int B) {
   int s, c;
-  valu_plan(desc, B, &s, &c);
-  return align256(static_cast<size_t>(B) * desc.H * desc.n_max * 4) +
-         align256(static_cast<size_t>(B) * desc.H * 4) + valu_workspace_bytes(desc, B, s);
+  decode_plan(desc, B, &s, &c);
+  const size_t tail = decode_uses_mfma2d(desc) ? decode2d_workspace_bytes(desc, B, s)
+                                               : valu_workspace_bytes(desc, B, s);
+  return align256(static_cast<size_t>(B) * desc.H * rope_sr_stride(desc.n_max) * 4) +
+         align256(static_cast<size_t>(B) * desc.H * 4) + tail;
 }
 
 hipError_t launch_decode_rope(const DecodeParams& p, const RopeScoreParams& rp0, int dtype,
                               hipStream_t stream) {
+  const bool mfma2d = p.variant == LLA_2D && decode2d_mfma_supported(dtype, p.r_k, p.r_v, p.d);
   const Entry* e = find(dtype, p.r_k, p.r_v);
-  if (e == nullptr || e->rfn == nullptr) return hipErrorNotSupported;
-  const size_t a = align256(static_cast<size_t>(p.B) * p.H * p.n_max * 4);
+  if (!mfma2d && (e == nullptr || e->rfn == nullptr)) return hipErrorNotSupported;
+  const int stride = rope_sr_stride(p.n_max);
+  const size_t a = align256(static_cast<size_t>(p.B) * p.H * stride * 4);
   const size_t b = align256(static_cast<size_t>(p.B) * p.H * 4);
   if (a + b > p.ws_bytes) return hipErrorInvalidValue;
   char* base = reinterpret_cast<char*>(p.ws);
   RopeScoreParams rp = rp0;
   rp.sr = reinterpret_cast<float*>(base);
   rp.sr_self = reinterpret_cast<float*>(base + a);
+  rp.sr_stride = stride;
   hipError_t err = launch_rope_scores(rp, stream);
   if (err != hipSuccess) return err;
   DecodeParams q = p;
   q.sr = rp.sr;
   q.sr_self = rp.k_rope_self != nullptr ? rp.sr_self : nullptr;
+  q.sr_stride = stride;
   q.ws = reinterpret_cast<float*>(base + a + b);
   q.ws_bytes = p.ws_bytes - a - b;
+  if (mfma2d) return launch_decode2d(q, stream);  // rotary scores added on the MFMA path
   return launch_valu(q, dtype, e->rfn, stream);
 }
 

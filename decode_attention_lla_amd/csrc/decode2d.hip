@@ -149,7 +149,10 @@ struct Cfg2d {
   static_assert(kRing >= 4 * kPart, "the final merge reuses the V rings");
 };
 
-template <int RK, int RV>
+// R: add each (token, head)'s precomputed base-2 rotary score p.sr (decoupled RoPE branch); a
+// lane's four tokens of one head are one aligned 16-byte load (rows padded to 4 tokens), issued
+// with the tile's other loads.
+template <int RK, int RV, bool R = false>
 __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, const float* qt,
                                                                const float* beta, float* part) {
   using CF = Cfg2d<RK, RV>;
@@ -196,9 +199,13 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
   const char* zvb = static_cast<const char*>(p.zv) + static_cast<size_t>(b) * p.n_max * RV * 2;
   char* myring = ring + wave * 2 * CF::kVTile;
 
-  // issue the loads of the tile starting at tok0 (tok0 < te): K into kr, V into ring half `buf`
-  auto issue = [&](int tok0, int buf, uint4 (&kr)[KS]) {
+  constexpr int NR = R ? 1 : 0;  // rotary score loads per tile and lane
+  const float* srow = R ? p.sr + (static_cast<size_t>(b) * p.H + (hvalid ? h : 0)) * p.sr_stride : nullptr;
+  // issue the loads of the tile starting at tok0 (tok0 < te): rotary scores into srt, V into ring
+  // half `buf`, K into kr
+  auto issue = [&](int tok0, int buf, uint4 (&kr)[KS], float4& srt) {
     const int last = te - 1;
+    if constexpr (R) srt = *reinterpret_cast<const float4*>(srow + min(tok0 + 4 * g, p.sr_stride - 4));
     char* dst = myring + buf * CF::kVTile;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
@@ -221,13 +228,15 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
   float l = 0.f;
 
   uint4 kc[KS];
+  float4 src = make_float4(0.f, 0.f, 0.f, 0.f);
   int tok0 = tb + wave * 16;
   int buf = 0;
-  if (tok0 < te) issue(tok0, 0, kc);
+  if (tok0 < te) issue(tok0, 0, kc, src);
   for (; tok0 < te; tok0 += 16 * kW) {
     uint4 kn[KS];
+    float4 srn = make_float4(0.f, 0.f, 0.f, 0.f);
     const bool more = tok0 + 16 * kW < te;
-    if (more) issue(tok0 + 16 * kW, buf ^ 1, kn);
+    if (more) issue(tok0 + 16 * kW, buf ^ 1, kn, srn);
     // scores S^T[token tok0 + i][head h0 + j]: hi and lo parts of q~ in two independent chains
     __asm__ volatile("" ::: "memory");
     floatx4_t sh = {0.f, 0.f, 0.f, 0.f};
@@ -245,7 +254,9 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool ok = hvalid && (tok0 + 4 * g + e) < te;
-      sc[e] = ok ? (sh[e] + sl[e]) + bt : kNegInf;
+      float srv = 0.f;
+      if constexpr (R) srv = e == 0 ? src.x : e == 1 ? src.y : e == 2 ? src.z : src.w;
+      sc[e] = ok ? (sh[e] + sl[e]) + bt + srv : kNegInf;
       tmax = fmaxf(tmax, sc[e]);
     }
     tmax = max_over_groups(tmax);
@@ -265,8 +276,8 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
     }
     // this tile's V must have landed in LDS: at most the next tile's loads may be outstanding
     if (more)
-      __builtin_amdgcn_s_waitcnt((KS + VPL) >= 16 ? 0x4f70 | (((KS + VPL) - 16) & 15)
-                                                  : 0x0f70 | (KS + VPL));
+      __builtin_amdgcn_s_waitcnt((KS + VPL + NR) >= 16 ? 0x4f70 | (((KS + VPL + NR) - 16) & 15)
+                                                       : 0x0f70 | (KS + VPL + NR));
     else
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __asm__ volatile("" ::: "memory");
@@ -279,6 +290,7 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
     wave_lds_sync();
 #pragma unroll
     for (int i = 0; i < KS; ++i) kc[i] = kn[i];
+    src = srn;
     buf ^= 1;
   }
   l = sum_over_groups(l);
@@ -396,7 +408,8 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
     const float M = wave_max(ms);
     const float fs = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
     const float l = wave_sum(fs * ls);
-    const float s_self = p.k_self != nullptr ? wave_sum(pt) * p.scale_log2 : kNegInf;
+    float s_self = p.k_self != nullptr ? wave_sum(pt) * p.scale_log2 : kNegInf;
+    if (p.k_self != nullptr && p.sr_self != nullptr) s_self += p.sr_self[bh];  // rotary part
     f_s[bb][lane] = fs;
     const float M2 = fmaxf(M, s_self);
     const float f_lat = (M == kNegInf) ? 0.f : fast_exp2(M - M2);
@@ -458,11 +471,13 @@ struct Entry2d {
   void (*qproj)(DecodeParams, float*, float*);
   void (*partial)(DecodeParams, const float*, const float*, float*);
   void (*combine)(DecodeParams, const float*);
+  void (*partial_r)(DecodeParams, const float*, const float*, float*);  // with rotary scores
 };
 
 template <int RK, int RV>
 constexpr Entry2d entry2d() {
-  return {RK, RV, qproj2d_kernel<RK>, decode2d_partial_kernel<RK, RV>, combine2d_kernel<RV>};
+  return {RK, RV, qproj2d_kernel<RK>, decode2d_partial_kernel<RK, RV>, combine2d_kernel<RV>,
+          decode2d_partial_kernel<RK, RV, true>};
 }
 
 const Entry2d kTable2d[] = {
@@ -524,8 +539,8 @@ hipError_t launch_decode2d(const DecodeParams& p0, hipStream_t stream) {
   hipLaunchKernelGGL(e->qproj, dim3(p.H, qb), dim3(256), 0, stream, p, qt, beta);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(e->partial, dim3(p.splits, p.B, (p.H + 15) / 16), dim3(64 * Cfg2d<64, 64>::kW), 0,
-                     stream, p, qt, beta, part);
+  hipLaunchKernelGGL(p.sr != nullptr ? e->partial_r : e->partial, dim3(p.splits, p.B, (p.H + 15) / 16),
+                     dim3(64 * Cfg2d<64, 64>::kW), 0, stream, p, qt, beta, part);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(e->combine, dim3(p.H, qb), dim3(256), 0, stream, p, part);

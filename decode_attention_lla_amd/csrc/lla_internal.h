@@ -37,6 +37,7 @@ struct DecodeParams {
   // sr [rows][H][n_max] by slot and sr_self [rows][H] for the self token; NULL when absent.
   const float* sr;
   const float* sr_self;
+  int32_t sr_stride;  // floats per (row, head) score row: n_max rounded up to a multiple of 4
   // Gather-indexed read (lla_attend_decode_gather): row b attends the latents at
   // slots[b * budget + j], j < seq_lens[b] clamped to [0, budget] (all budget when seq_lens is
   // null); a slot outside [0, n_max) is skipped. slots == nullptr: the contiguous read above.
@@ -68,7 +69,8 @@ struct RopeScoreParams {
   const void* k_rope;       // bf16 [B][n_max][d_r], rotated at each slot
   const void* k_rope_self;  // bf16 [B][d_r] or NULL
   const int32_t* seq_lens;
-  float* sr;                // out [B][H][n_max], base-2 scale
+  float* sr;                // out [B][H][sr_stride], base-2 scale
+  int32_t sr_stride;        // n_max rounded up to a multiple of 4 (16-byte aligned rows)
   float* sr_self;           // out [B][H] (when k_rope_self is given)
   int32_t B, H, n_max, d_r;
   float scale_log2;

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kTokTile) void rope_scores_kernel(RopeScoreParams p
   const int col = lane & 15;
   const int g = lane >> 4;
   const uint16_t* kbase = static_cast<const uint16_t*>(p.k_rope) + static_cast<size_t>(b) * p.n_max * DR;
-  float* sbase = p.sr + static_cast<size_t>(b) * p.H * p.n_max;
+  float* sbase = p.sr + static_cast<size_t>(b) * p.H * p.sr_stride;
   for (int hg = 0; hg < p.H; hg += 16) {
     // A operand: lane (head hg + col, group g) holds q_r[head][32 ks + 8 g .. + 7], hi and lo
     uint4 qh[KS], ql[KS];
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kTokTile) void rope_scores_kernel(RopeScoreParams p
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int hh = hg + 4 * g + e;
-          if (hh < p.H) sbase[static_cast<size_t>(hh) * p.n_max + row] = acc[e];
+          if (hh < p.H) sbase[static_cast<size_t>(hh) * p.sr_stride + row] = acc[e];
         }
       }
     }

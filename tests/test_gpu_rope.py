@@ -61,7 +61,8 @@ def _rope_inputs(rng, B, H, n_max, d_rope):
 
 @pytest.mark.parametrize("variant,rk,rv,d_rope", [("per_head", 24, 24, 64), ("per_head", 96, 160, 32),
                                                   ("per_head", 128, 128, 128), ("2d", 32, 32, 64),
-                                                  ("2d", 256, 256, 64)])
+                                                  ("2d", 256, 256, 64), ("2d", 128, 128, 32),
+                                                  ("2d", 64, 64, 128)])
 def test_decode_rope(variant, rk, rv, d_rope):
     B, H, d, T, n_max = 3, 2, 64, 2, 1301
     lens = np.array([1301, 517, 0], np.int32)
@@ -173,6 +174,45 @@ def test_prefill_rope(variant, rk, rv, d_rope):
         ref = O.attend_prefill_rope(q, q_rope, c["zk"], c["zv"], k_rope, c["Wk"], c["Wv"], t, ctx,
                                     c["mu_k"], c["mu_v"], variant=variant)
         assert_close(host(out), ref, "bf16", f"prefill rope {variant} ({rk},{rv}) d_rope={d_rope} t={t}")
+
+
+def test_lla2d_decode_rope_full_size_sampled():
+    """The LLA-2D decode benchmark shape (B=128, H=16, d=128, T=4, r=256, N=8192) on the MFMA
+    path with a 64-wide rotary branch and the self token; sequences {0, 77, 127}, all heads, all
+    loops."""
+    s = synth.CASES["lla2d"]
+    B, H, d, T, r, N = s.B, s.H, s.d, s.T, s.r_k, s.N
+    n_max = N + 1
+    d_rope = 64
+    desc = mk_desc("2d", "bf16", H, d, T, r, r, n_max)
+    zk = synth.device_normal_(torch.empty(B, n_max, r, dtype=torch.bfloat16, device="cuda"), 10010)
+    zv = synth.device_normal_(torch.empty(B, n_max, r, dtype=torch.bfloat16, device="cuda"), 10011)
+    kr = synth.device_normal_(torch.empty(B, n_max, d_rope, dtype=torch.bfloat16, device="cuda"), 10012)
+    krs = synth.device_normal_(torch.empty(B, d_rope, dtype=torch.bfloat16, device="cuda"), 10013)
+    Wk = synth.orthonormal_W_2d(T, H, d, r, 10014, "bf16")
+    Wv = synth.orthonormal_W_2d(T, H, d, r, 10015, "bf16")
+    q = synth.device_normal_(torch.empty(T, B, H, d, dtype=torch.bfloat16, device="cuda"), 10016)
+    qr = synth.device_normal_(torch.empty(T, B, H, d_rope, dtype=torch.bfloat16, device="cuda"), 10017)
+    ks = synth.device_normal_(torch.empty(T, B, H, d, dtype=torch.bfloat16, device="cuda"), 10018)
+    vs = synth.device_normal_(torch.empty(T, B, H, d, dtype=torch.bfloat16, device="cuda"), 10019)
+    lens = np.full(B, N, np.int32)
+    rows = [0, 77, 127]
+    zk0, zv0, kr0, krs0 = host(zk[rows]), host(zv[rows]), host(kr[rows]), host(krs[rows])
+    ws = lla.rope_workspace(desc, B)
+    dWk, dWv = dev(Wk, "bf16"), dev(Wv, "bf16")
+    for t in range(T):
+        out = torch.empty(B, H, d, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B, H, device="cuda")
+        lla.lla_attend_decode_rope(desc, B, t, q[t], qr[t], zk, zv, kr, d_rope, 0.0, dev(lens), dWk,
+                                   dWv, None, None, ks[t], vs[t], krs, out, lse, ws)
+        torch.cuda.synchronize()
+        ro, rl = O.attend_decode_rope(host(q[t][rows]), host(qr[t][rows]), zk0, zv0, kr0, Wk, Wv, t,
+                                      lens[rows], None, None, host(ks[t][rows]), host(vs[t][rows]),
+                                      krs0, variant="2d")
+        assert_close(host(out)[rows], ro, "bf16", f"2d decode rope t={t}")
+        assert_lse(host(lse)[rows], rl, f"2d decode rope t={t}")
+    del zk, zv, kr, out
+    torch.cuda.empty_cache()
 
 
 def test_lla2d_prefill_rope_full_size_sampled():
