@@ -23,8 +23,10 @@ bool desc_ok(const lla_desc* d) {
   if (d->H <= 0 || d->T <= 0 || d->r_k <= 0 || d->r_v <= 0 || d->n_max <= 0) return false;
   if (d->d_head <= 0 || d->d_head > 256 || (d->d_head % 8) != 0) return false;
   if (!(d->scale >= 0.f) || std::isinf(d->scale)) return false;
-  // every flattened index below stays inside int32 per sequence
-  const int64_t per_seq = static_cast<int64_t>(d->H) * d->n_max * (d->r_k > d->r_v ? d->r_k : d->r_v);
+  // H * n_max rows of the wider axis stay under 2 GiB: flattened per-sequence indices and the
+  // 32-bit byte offsets of the buffer loads never wrap
+  const int64_t row = static_cast<int64_t>(lla_latent_row_bytes(d->dtype, d->r_k > d->r_v ? d->r_k : d->r_v));
+  const int64_t per_seq = static_cast<int64_t>(d->H) * d->n_max * row;
   if (per_seq >= (int64_t(1) << 31)) return false;
   return true;
 }

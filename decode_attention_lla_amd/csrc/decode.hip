@@ -32,14 +32,14 @@ __device__ __forceinline__ size_t latent_row(const DecodeParams& p, int seq, int
 
 // Listed slots of a gather-indexed row, clamped to [0, budget].
 __device__ __forceinline__ int gather_keys(const DecodeParams& p, int row) {
-  const int n = p.seq_lens != nullptr ? p.seq_lens[row] : p.budget;
+  const int n = p.seq_lens != nullptr ? uniform(p.seq_lens[row]) : p.budget;
   return min(max(n, 0), p.budget);
 }
 
 // Keys visible to query row `row` (see DecodeParams), clamped to [0, n_max].
 __device__ __forceinline__ int row_keys(const DecodeParams& p, int row) {
   const int seq = row / p.rows_per_seq;
-  int n = p.seq_lens != nullptr ? p.seq_lens[seq] : p.n_max;
+  int n = p.seq_lens != nullptr ? uniform(p.seq_lens[seq]) : p.n_max;
   if (p.causal) n += row - seq * p.rows_per_seq + 1;
   return min(max(n, 0), p.n_max);
 }
@@ -104,12 +104,17 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   constexpr int TPW = 64 / LPT;
   constexpr int RKB = LS::row(RK);  // bytes per latent row
   constexpr int RVB = LS::row(RV);
-  constexpr int VK = kQ8 ? RKB / 16 : EK * LS::kBytes / 16;
-  constexpr int VV = kQ8 ? RVB / 16 : EV * LS::kBytes / 16;
+  constexpr int SK = EK * LS::kBytes;  // bytes of a lane's slice of a K row
+  constexpr int SV = EV * LS::kBytes;
+  // One load per lane and row when a slice is 4..16 whole words: the LPT lanes of a token then
+  // read its row as one run and each load instruction covers 64 / LPT consecutive whole rows,
+  // which lets the contiguous read stream past the caches (non-temporal) at full line use.
+  constexpr bool kOne = !kQ8 && SK % 4 == 0 && SV % 4 == 0 && SK <= 16 && SV <= 16;
+  constexpr int VK = kQ8 ? RKB / 16 : kOne ? 1 : SK / 16;
+  constexpr int VV = kQ8 ? RVB / 16 : kOne ? 1 : SV / 16;
   static_assert(EK * LPT == RK && EV * LPT == RV, "rank must split evenly over lanes");
   static_assert(!kQ8 || LPT == 1, "low-bit rows are read whole by one lane");
-  static_assert(kQ8 || (VK * 16 == EK * LS::kBytes && VV * 16 == EV * LS::kBytes),
-                "16-byte fragments");
+  static_assert(kQ8 || kOne || (VK * 16 == SK && VV * 16 == SV), "16-byte fragments");
 
   __shared__ float q_s[256];
   __shared__ float qt_s[RK];
@@ -123,8 +128,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   const int b = bh / p.H;
 
   const int nb = G ? gather_keys(p, b) : row_keys(p, b);
-  const int tb = split * p.chunk;
-  const int te = min(nb, tb + p.chunk);
+  const int tb = uniform(split * p.chunk);
+  const int te = uniform(min(nb, tb + p.chunk));
 
   // --- 1. query absorption ------------------------------------------------------------------
   const size_t qoff = static_cast<size_t>(bh) * p.d;
@@ -153,8 +158,16 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
 
   // --- 2-3. latent stream with online softmax -------------------------------------------------
   const size_t lrow = latent_row(p, b / p.rows_per_seq, h);
-  const char* zkp = static_cast<const char*>(p.zk) + lrow * RKB + sub * EK * LS::kBytes;
-  const char* zvp = static_cast<const char*>(p.zv) + lrow * RVB + sub * EV * LS::kBytes;
+  const char* zkp = static_cast<const char*>(p.zk) + lrow * RKB + sub * SK;
+  const char* zvp = static_cast<const char*>(p.zv) + lrow * RVB + sub * SV;
+  // kOne: buffer descriptors over the rows this wave may read (the gather read: all n_max slots;
+  // the contiguous read: its split [tb, te)); an offset at the end reads zeros
+  const int row0 = G ? 0 : tb;
+  const uint32_t nrows = static_cast<uint32_t>(uniform(G ? p.n_max : max(te - tb, 0)));
+  const __amdgpu_buffer_rsrc_t rsk = buffer_rsrc(static_cast<const char*>(p.zk) + (lrow + row0) * RKB, nrows * RKB);
+  const __amdgpu_buffer_rsrc_t rsv = buffer_rsrc(static_cast<const char*>(p.zv) + (lrow + row0) * RVB, nrows * RVB);
+  constexpr int kAux = G ? 0 : 2;  // non-temporal for the contiguous read
+  constexpr bool kPipe = kOne && !G;
 
   const int32_t* srow = G ? p.slots + static_cast<size_t>(b) * p.budget : nullptr;
 
@@ -164,39 +177,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
   for (int e = 0; e < EV; ++e) acc[e] = 0.f;
 
-  for (int t0 = tb; t0 < te; t0 += TPW * U) {
-    uint4 kr[U][VK];
-    uint4 vr[U][VV];
-    bool ok[U];
-    int slot[U];
-    float srv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int tok = t0 + u * TPW + grp;
-      ok[u] = tok < te;
-      slot[u] = tok;
-      if (G) {
-        slot[u] = ok[u] ? srow[tok] : 0;
-        ok[u] = ok[u] && static_cast<unsigned>(slot[u]) < static_cast<unsigned>(p.n_max);
-      }
-      srv[u] = (R && ok[u]) ? p.sr[static_cast<size_t>(bh) * p.sr_stride + slot[u]] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (ok[u]) {
-        const uint4* kp = reinterpret_cast<const uint4*>(zkp + static_cast<size_t>(slot[u]) * RKB);
-        const uint4* vp = reinterpret_cast<const uint4*>(zvp + static_cast<size_t>(slot[u]) * RVB);
-#pragma unroll
-        for (int i = 0; i < VK; ++i) kr[u][i] = kp[i];
-#pragma unroll
-        for (int i = 0; i < VV; ++i) vr[u][i] = vp[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < VK; ++i) kr[u][i] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < VV; ++i) vr[u][i] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  // fold one batch of U tiles (ok: token inside the split and valid) into (m, l, acc)
+  auto consume = [&](uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], const bool (&ok)[U], const float (&srv)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if constexpr (kQ8) {
@@ -209,8 +191,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
       for (int e = 0; e < EK; ++e) sc += qt[e] * frag_elem<LS>(kr[u], e);
       if (kQ8) sc *= q8_row_scale(kr[u], VK);
-#pragma unroll
-      for (int o = 1; o < LPT; o <<= 1) sc += __shfl_xor(sc, o, 64);
+      sc = group_sum<LPT>(sc);
       sc += beta;
       if (R) sc += srv[u];
       if (ok[u]) {
@@ -227,6 +208,82 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < EV; ++e) acc[e] += pv * frag_elem<LS>(vr[u], e);
       }
+    }
+  };
+
+  if constexpr (kPipe) {
+    // Contiguous one-load rows: two register batches in turn, the next batch's loads issued
+    // before the current one is consumed, so a wave always has a batch in flight. Rows past the
+    // split read as zeros through the descriptor bound (no memory access) and are masked; a
+    // batch wholly past the split costs only its masked arithmetic.
+    auto issue = [&](int t0, uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], float (&srv)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int tok = t0 + u * TPW + grp;
+        const uint32_t rr = static_cast<uint32_t>(min(tok, te) - row0);
+        kr[u][0] = buffer_words<SK / 4, kAux>(rsk, rr * RKB + sub * SK);
+        vr[u][0] = buffer_words<SV / 4, kAux>(rsv, rr * RVB + sub * SV);
+        srv[u] = (R && tok < te) ? p.sr[static_cast<size_t>(bh) * p.sr_stride + tok] : 0.f;
+      }
+    };
+    auto mask = [&](int t0, bool (&ok)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) ok[u] = t0 + u * TPW + grp < te;
+    };
+    constexpr int kStep = TPW * U;
+    uint4 ka[U][VK], va[U][VV], kb[U][VK], vb[U][VV];
+    float sa[U], sb[U];
+    bool ok[U];
+    if (tb < te) issue(tb, ka, va, sa);
+    for (int t0 = tb; t0 < te; t0 += 2 * kStep) {
+      issue(t0 + kStep, kb, vb, sb);
+      mask(t0, ok);
+      consume(ka, va, ok, sa);
+      // no early exit here: with one exit at the bottom the compiler's wait before the loop top
+      // leaves the batch just issued in flight (an exit here made it drain every load)
+      issue(t0 + 2 * kStep, ka, va, sa);
+      mask(t0 + kStep, ok);
+      consume(kb, vb, ok, sb);
+    }
+  } else {
+    for (int t0 = tb; t0 < te; t0 += TPW * U) {
+      uint4 kr[U][VK];
+      uint4 vr[U][VV];
+      bool ok[U];
+      int slot[U];
+      float srv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int tok = t0 + u * TPW + grp;
+        ok[u] = tok < te;
+        slot[u] = tok;
+        if (G) {
+          slot[u] = ok[u] ? srow[tok] : 0;
+          ok[u] = ok[u] && static_cast<unsigned>(slot[u]) < static_cast<unsigned>(p.n_max);
+        }
+        srv[u] = (R && ok[u]) ? p.sr[static_cast<size_t>(bh) * p.sr_stride + slot[u]] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if constexpr (kOne) {
+          const uint32_t rr = ok[u] ? static_cast<uint32_t>(slot[u] - row0) : nrows;
+          kr[u][0] = buffer_words<SK / 4, kAux>(rsk, rr * RKB + sub * SK);
+          vr[u][0] = buffer_words<SV / 4, kAux>(rsv, rr * RVB + sub * SV);
+        } else if (ok[u]) {
+          const uint4* kp = reinterpret_cast<const uint4*>(zkp + static_cast<size_t>(slot[u]) * RKB);
+          const uint4* vp = reinterpret_cast<const uint4*>(zvp + static_cast<size_t>(slot[u]) * RVB);
+#pragma unroll
+          for (int i = 0; i < VK; ++i) kr[u][i] = kp[i];
+#pragma unroll
+          for (int i = 0; i < VV; ++i) vr[u][i] = vp[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < VK; ++i) kr[u][i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < VV; ++i) vr[u][i] = make_uint4(0, 0, 0, 0);
+        }
+      }
+      consume(kr, vr, ok, srv);
     }
   }
 
@@ -348,35 +405,36 @@ struct Entry {
   PartialFn rfn;  // contiguous read with rotary scores (bf16 pairs only)
 };
 
-// Compiled (dtype, r_k, r_v) -> (lanes per token, tiles in flight).
+// Compiled (dtype, r_k, r_v) -> (lanes per token, tiles in flight). Lanes per token are chosen so
+// that a lane's slice of a row is one load of at most 16 bytes wherever the rank allows it.
 const Entry kTable[] = {
     {LLA_BF16, 8, 8, partial_fn<BF16, 8, 8, 1, 4>(), gather_fn<BF16, 8, 8, 1, 4>(),
      rope_fn<BF16, 8, 8, 1, 4>()},
-    {LLA_BF16, 16, 16, partial_fn<BF16, 16, 16, 1, 4>(), gather_fn<BF16, 16, 16, 1, 4>(),
-     rope_fn<BF16, 16, 16, 1, 4>()},
-    {LLA_BF16, 24, 24, partial_fn<BF16, 24, 24, 1, 2>(), gather_fn<BF16, 24, 24, 1, 2>(),
-     rope_fn<BF16, 24, 24, 1, 2>()},
-    {LLA_BF16, 32, 32, partial_fn<BF16, 32, 32, 1, 2>(), gather_fn<BF16, 32, 32, 1, 2>(),
-     rope_fn<BF16, 32, 32, 1, 2>()},
-    {LLA_BF16, 64, 64, partial_fn<BF16, 64, 64, 2, 2>(), gather_fn<BF16, 64, 64, 2, 2>(),
-     rope_fn<BF16, 64, 64, 2, 2>()},
-    {LLA_BF16, 96, 96, partial_fn<BF16, 96, 96, 4, 2>(), gather_fn<BF16, 96, 96, 4, 2>(),
-     rope_fn<BF16, 96, 96, 4, 2>()},
-    {LLA_BF16, 128, 128, partial_fn<BF16, 128, 128, 4, 2>(), gather_fn<BF16, 128, 128, 4, 2>(),
-     rope_fn<BF16, 128, 128, 4, 2>()},
+    {LLA_BF16, 16, 16, partial_fn<BF16, 16, 16, 2, 4>(), gather_fn<BF16, 16, 16, 2, 4>(),
+     rope_fn<BF16, 16, 16, 2, 4>()},
+    {LLA_BF16, 24, 24, partial_fn<BF16, 24, 24, 4, 8>(), gather_fn<BF16, 24, 24, 4, 8>(),
+     rope_fn<BF16, 24, 24, 4, 8>()},
+    {LLA_BF16, 32, 32, partial_fn<BF16, 32, 32, 4, 8>(), gather_fn<BF16, 32, 32, 4, 8>(),
+     rope_fn<BF16, 32, 32, 4, 8>()},
+    {LLA_BF16, 64, 64, partial_fn<BF16, 64, 64, 8, 8>(), gather_fn<BF16, 64, 64, 8, 8>(),
+     rope_fn<BF16, 64, 64, 8, 8>()},
+    {LLA_BF16, 96, 96, partial_fn<BF16, 96, 96, 16, 8>(), gather_fn<BF16, 96, 96, 16, 8>(),
+     rope_fn<BF16, 96, 96, 16, 8>()},
+    {LLA_BF16, 128, 128, partial_fn<BF16, 128, 128, 16, 8>(), gather_fn<BF16, 128, 128, 16, 8>(),
+     rope_fn<BF16, 128, 128, 16, 8>()},
     {LLA_BF16, 96, 160, partial_fn<BF16, 96, 160, 4, 2>(), gather_fn<BF16, 96, 160, 4, 2>(),
      rope_fn<BF16, 96, 160, 4, 2>()},
-    {LLA_BF16, 256, 256, partial_fn<BF16, 256, 256, 8, 2>(), gather_fn<BF16, 256, 256, 8, 2>(),
-     rope_fn<BF16, 256, 256, 8, 2>()},
-    {LLA_F32, 8, 8, partial_fn<F32, 8, 8, 1, 2>(), gather_fn<F32, 8, 8, 1, 2>(), nullptr},
-    {LLA_F32, 16, 16, partial_fn<F32, 16, 16, 1, 2>(), gather_fn<F32, 16, 16, 1, 2>(), nullptr},
-    {LLA_F32, 24, 24, partial_fn<F32, 24, 24, 1, 1>(), gather_fn<F32, 24, 24, 1, 1>(), nullptr},
-    {LLA_F32, 32, 32, partial_fn<F32, 32, 32, 2, 1>(), gather_fn<F32, 32, 32, 2, 1>(), nullptr},
-    {LLA_F32, 64, 64, partial_fn<F32, 64, 64, 4, 1>(), gather_fn<F32, 64, 64, 4, 1>(), nullptr},
-    {LLA_F32, 96, 96, partial_fn<F32, 96, 96, 4, 1>(), gather_fn<F32, 96, 96, 4, 1>(), nullptr},
-    {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 8, 1>(), gather_fn<F32, 128, 128, 8, 1>(), nullptr},
+    {LLA_BF16, 256, 256, partial_fn<BF16, 256, 256, 32, 8>(), gather_fn<BF16, 256, 256, 32, 8>(),
+     rope_fn<BF16, 256, 256, 32, 8>()},
+    {LLA_F32, 8, 8, partial_fn<F32, 8, 8, 2, 4>(), gather_fn<F32, 8, 8, 2, 4>(), nullptr},
+    {LLA_F32, 16, 16, partial_fn<F32, 16, 16, 4, 4>(), gather_fn<F32, 16, 16, 4, 4>(), nullptr},
+    {LLA_F32, 24, 24, partial_fn<F32, 24, 24, 8, 4>(), gather_fn<F32, 24, 24, 8, 4>(), nullptr},
+    {LLA_F32, 32, 32, partial_fn<F32, 32, 32, 8, 4>(), gather_fn<F32, 32, 32, 8, 4>(), nullptr},
+    {LLA_F32, 64, 64, partial_fn<F32, 64, 64, 16, 4>(), gather_fn<F32, 64, 64, 16, 4>(), nullptr},
+    {LLA_F32, 96, 96, partial_fn<F32, 96, 96, 32, 4>(), gather_fn<F32, 96, 96, 32, 4>(), nullptr},
+    {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 32, 4>(), gather_fn<F32, 128, 128, 32, 4>(), nullptr},
     {LLA_F32, 96, 160, partial_fn<F32, 96, 160, 8, 1>(), gather_fn<F32, 96, 160, 8, 1>(), nullptr},
-    {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 16, 1>(), gather_fn<F32, 256, 256, 16, 1>(), nullptr},
+    {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 64, 4>(), gather_fn<F32, 256, 256, 64, 4>(), nullptr},
     {LLA_BF16_Q8, 8, 8, q8_fn<8, 8, 4>(), q8_gather_fn<8, 8, 4>(), nullptr},
     {LLA_BF16_Q8, 16, 16, q8_fn<16, 16, 4>(), q8_gather_fn<16, 16, 4>(), nullptr},
     {LLA_BF16_Q8, 24, 24, q8_fn<24, 24, 3>(), q8_gather_fn<24, 24, 3>(), nullptr},

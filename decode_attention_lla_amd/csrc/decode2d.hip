@@ -70,7 +70,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 __device__ __forceinline__ int seq_keys(const DecodeParams& p, int b) {
-  int n = p.seq_lens != nullptr ? p.seq_lens[b] : p.n_max;
+  int n = p.seq_lens != nullptr ? uniform(p.seq_lens[b]) : p.n_max;
   return min(max(n, 0), p.n_max);
 }
 

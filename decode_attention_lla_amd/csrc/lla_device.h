@@ -27,6 +27,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// A value the caller knows to be the same in every lane (e.g. loaded from a wave-uniform address
+// through a generic pointer, which the compiler must assume may differ per lane), moved to a
+// scalar register so that what derives from it (loop bounds, buffer descriptors) stays scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -113,6 +118,29 @@ __device__ __forceinline__ float q8_row_scale(const uint4* f, int V) { return __
 // displacing reused data. Partial-line patterns must use ordinary loads, which let the next
 // instruction hit the same lines.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// W 32-bit words (1..4) at byte offset voff of a raw buffer, returned in the low words of a uint4
+// (the rest zero). An offset at or past the descriptor's size reads zeros. AUX is the cache policy
+// (2: non-temporal, for data read once by loads that cover whole lines).
+template <int W, int AUX>
+__device__ __forceinline__ uint4 buffer_words(__amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+  static_assert(W >= 1 && W <= 4, "1 to 4 words");
+  if constexpr (W == 4) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, AUX);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  } else if constexpr (W == 3) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(rs, voff, 0, AUX);
+    return make_uint4(v[0], v[1], v[2], 0u);
+  } else if constexpr (W == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, 0, AUX);
+    return make_uint4(v[0], v[1], 0u, 0u);
+  } else {
+    return make_uint4(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, AUX), 0u, 0u, 0u);
+  }
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
 __device__ __forceinline__ uint4 load_stream(const void* p) {
   const u32x4_t t = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
   return make_uint4(t.x, t.y, t.z, t.w);
@@ -146,6 +174,32 @@ __device__ __forceinline__ float sum_over_groups(float v) {
   v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Sum over aligned groups of N lanes (N a power of two, 1..64), VALU only: a butterfly whose
+// partner steps are DPP quad permutes (lane ^ 1, lane ^ 2), the half-row and row mirrors (which
+// pair each 4- and 8-lane group with its neighbour) and the two lane swaps. Every step adds two
+// values, so all lanes of a group end with the same bits.
+template <int DPP>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), DPP, 0xf, 0xf, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "power of two up to the wave");
+  if constexpr (N >= 2) v += dpp_f32<0xb1>(v);   // quad_perm(1, 0, 3, 2)
+  if constexpr (N >= 4) v += dpp_f32<0x4e>(v);   // quad_perm(2, 3, 0, 1)
+  if constexpr (N >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
+  if constexpr (N >= 16) v += dpp_f32<0x140>(v); // row_mirror
+  if constexpr (N >= 32) {
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  }
+  if constexpr (N >= 64) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  }
+  return v;
 }
 
 }  // namespace lla

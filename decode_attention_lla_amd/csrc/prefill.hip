@@ -236,7 +236,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   }
   const int h = k / RB;
   const int j0 = (k - h * RB) * kRowsWG;
-  const int ctx = p.ctx_lens[b];
+  const int ctx = uniform(p.ctx_lens[b]);
 
   // this lane's query row (for scores and accumulators): chunk row jr
   const int jr = j0 + wave * 16 + col;

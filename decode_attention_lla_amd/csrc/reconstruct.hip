@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(ReconParams p) {
   const int bh = blockIdx.y;
   const int h = bh % p.H;
   const int b = bh / p.H;
-  int nb = p.seq_lens != nullptr ? p.seq_lens[b] : p.n_max;
+  int nb = p.seq_lens != nullptr ? uniform(p.seq_lens[b]) : p.n_max;
   nb = min(max(nb, 0), p.n_max);
   const int tok0 = blockIdx.x * kTokWG;
   if (tok0 >= nb) return;  // workgroup-uniform, before any barrier

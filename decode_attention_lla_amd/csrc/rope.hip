@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kTokTile) void rope_scores_kernel(RopeScoreParams p
   constexpr int half = DR / 2;
   constexpr int KS = DR / 32;
   const int b = blockIdx.y;
-  int nb = p.seq_lens != nullptr ? p.seq_lens[b] : p.n_max;
+  int nb = p.seq_lens != nullptr ? uniform(p.seq_lens[b]) : p.n_max;
   nb = min(max(nb, 0), p.n_max);
   const int tok0 = blockIdx.x * kTokTile;
   const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + static_cast<size_t>(b) * p.H * DR;

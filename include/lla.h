@@ -77,7 +77,8 @@ typedef struct {
   int32_t T;       /* loops (recurrence steps) */
   int32_t r_k;     /* K latent rank */
   int32_t r_v;     /* V latent rank (the paper uses r_v > r_k; any compiled pair is allowed) */
-  int32_t n_max;   /* latent slots per sequence in the cache */
+  int32_t n_max;   /* latent slots per sequence in the cache; H * n_max rows of the wider axis
+                      (lla_latent_row_bytes each) must stay under 2 GiB */
   float scale;     /* softmax scale; 0 means 1/sqrt(d_head) */
 } lla_desc;
 

@@ -101,6 +101,27 @@ def test_decode_sweep_2d(dtype, rk, rv):
         assert_lse(lse, rl, f"2d {dtype} t={t}")
 
 
+@pytest.mark.parametrize("dtype,rk,rv", [("bf16", 24, 24), ("bf16", 8, 8), ("bf16", 256, 256),
+                                          ("f32", 24, 24), ("bf16", 96, 96), ("f32", 8, 8)])
+def test_decode_batch_and_split_boundaries(dtype, rk, rv):
+    """Sequence lengths just below, at and above multiples of the streaming kernel's batch
+    (64/lanes-per-token tokens per tile, several tiles per batch, two batches in flight) and of
+    the token split (two splits of 384 at n_max = 700), so every partly and wholly empty batch,
+    and a split that ends inside one, is exercised."""
+    H, d, T, n_max = 2, 64, 2, 700
+    lens = [1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 384, 385, 511, 512,
+            513, 640, 699, 700]
+    B = len(lens)
+    c = upload(synth.random_case("per_head", dtype, B, H, d, T, rk, rv, n_max, 7050 + rk,
+                                 q_gain=4.0), dtype)
+    desc = mk_desc("per_head", dtype, H, d, T, rk, rv, n_max)
+    for t in range(T):
+        o, lse = gpu_decode(desc, B, t, c, dtype, lens, self_token=(t == 0))
+        ro, rl = oracle_decode(c, t, lens, "per_head", self_token=(t == 0))
+        assert_close(o, ro, dtype, f"boundaries {dtype} r=({rk},{rv}) t={t}")
+        assert_lse(lse, rl, f"boundaries {dtype} r=({rk},{rv}) t={t}")
+
+
 def test_decode_empty_and_clamped_lengths():
     dtype = "f32"
     B, H, d, T, n_max = 4, 2, 16, 2, 40
