@@ -99,22 +99,25 @@ __device__ void finish_unit(const DecodeParams& p, int b, int h, float M, float 
 template <class S, class LS, int RK, int RV, int LPT, int U, bool G, bool R = false>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   constexpr bool kQ8 = std::is_same<LS, Q8>::value;
-  constexpr int EK = RK / LPT;
-  constexpr int EV = RV / LPT;
-  constexpr int TPW = 64 / LPT;
   constexpr int RKB = LS::row(RK);  // bytes per latent row
   constexpr int RVB = LS::row(RV);
+  // A lane's slice of a row: RK / LPT elements, or for low-bit rows RKB / LPT byte slots (codes,
+  // then the row's zero padding and, in the last lane of the token's group, its float32 scale).
+  constexpr int EK = kQ8 ? RKB / LPT : RK / LPT;
+  constexpr int EV = kQ8 ? RVB / LPT : RV / LPT;
+  constexpr int TPW = 64 / LPT;
   constexpr int SK = EK * LS::kBytes;  // bytes of a lane's slice of a K row
   constexpr int SV = EV * LS::kBytes;
   // One load per lane and row when a slice is 4..16 whole words: the LPT lanes of a token then
   // read its row as one run and each load instruction covers 64 / LPT consecutive whole rows,
   // which lets the contiguous read stream past the caches (non-temporal) at full line use.
-  constexpr bool kOne = !kQ8 && SK % 4 == 0 && SV % 4 == 0 && SK <= 16 && SV <= 16;
-  constexpr int VK = kQ8 ? RKB / 16 : kOne ? 1 : SK / 16;
-  constexpr int VV = kQ8 ? RVB / 16 : kOne ? 1 : SV / 16;
-  static_assert(EK * LPT == RK && EV * LPT == RV, "rank must split evenly over lanes");
-  static_assert(!kQ8 || LPT == 1, "low-bit rows are read whole by one lane");
-  static_assert(kQ8 || kOne || (VK * 16 == SK && VV * 16 == SV), "16-byte fragments");
+  constexpr bool kOne = SK % 4 == 0 && SV % 4 == 0 && SK <= 16 && SV <= 16;
+  constexpr int VK = kOne ? 1 : SK / 16;
+  constexpr int VV = kOne ? 1 : SV / 16;
+  static_assert(kQ8 ? (EK * LPT == RKB && EV * LPT == RVB) : (EK * LPT == RK && EV * LPT == RV),
+                "rows must split evenly over lanes");
+  static_assert(kOne || (VK * 16 == SK && VV * 16 == SV), "16-byte fragments");
+  static_assert(!kQ8 || kOne || LPT == 1, "a low-bit row is one lane's, or one load per lane");
 
   __shared__ float q_s[256];
   __shared__ float qt_s[RK];
@@ -154,7 +157,20 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   const int grp = lane / LPT;
   float qt[EK];
 #pragma unroll
-  for (int e = 0; e < EK; ++e) qt[e] = qt_s[sub * EK + e];
+  for (int e = 0; e < EK; ++e) {
+    const int c = sub * EK + e;  // low-bit slots past the codes take a zero query weight
+    qt[e] = (!kQ8 || c < RK) ? qt_s[min(c, RK - 1)] : 0.f;
+  }
+  // low-bit slices: the bytes of each of this lane's words that hold codes (padding and the scale
+  // must never be converted as codes: a scale byte can be an E4M3 NaN pattern)
+  uint32_t kmask[4], vmask[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int nk = min(max(RK - (sub * EK + 4 * k), 0), 4);
+    const int nv = min(max(RV - (sub * EV + 4 * k), 0), 4);
+    kmask[k] = nk == 4 ? 0xffffffffu : (1u << (8 * nk)) - 1u;
+    vmask[k] = nv == 4 ? 0xffffffffu : (1u << (8 * nv)) - 1u;
+  }
 
   // --- 2-3. latent stream with online softmax -------------------------------------------------
   const size_t lrow = latent_row(p, b / p.rows_per_seq, h);
@@ -181,17 +197,33 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   auto consume = [&](uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], const bool (&ok)[U], const float (&srv)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if constexpr (kQ8) {
+      float sk = 1.f, sv = 1.f;  // low-bit row scales
+      if constexpr (kQ8 && kOne) {
+        // the scale is the last word of the group's last lane; a zero-padded group sum gives it
+        // to every lane of the group exactly. Then the non-code bytes are cleared.
+        constexpr int WK = SK / 4 - 1, WV = SV / 4 - 1;
+        const uint32_t kw = WK == 0 ? kr[u][0].x : WK == 1 ? kr[u][0].y : WK == 2 ? kr[u][0].z : kr[u][0].w;
+        const uint32_t vw = WV == 0 ? vr[u][0].x : WV == 1 ? vr[u][0].y : WV == 2 ? vr[u][0].z : vr[u][0].w;
+        sk = group_sum<LPT>(sub == LPT - 1 ? __uint_as_float(kw) : 0.f);
+        sv = group_sum<LPT>(sub == LPT - 1 ? __uint_as_float(vw) : 0.f);
+        kr[u][0] = make_uint4(kr[u][0].x & kmask[0], kr[u][0].y & kmask[1], kr[u][0].z & kmask[2],
+                              kr[u][0].w & kmask[3]);
+        vr[u][0] = make_uint4(vr[u][0].x & vmask[0], vr[u][0].y & vmask[1], vr[u][0].z & vmask[2],
+                              vr[u][0].w & vmask[3]);
+      } else if constexpr (kQ8) {
         // the last 16 bytes of a low-bit row hold padding the arithmetic never reads; without
         // this the compiler narrows their load and a row takes three partial loads, not two
         asm("" : "+v"(kr[u][VK - 1].x), "+v"(kr[u][VK - 1].y), "+v"(kr[u][VK - 1].z));
         asm("" : "+v"(vr[u][VV - 1].x), "+v"(vr[u][VV - 1].y), "+v"(vr[u][VV - 1].z));
+        sk = q8_row_scale(kr[u], VK);
+        sv = q8_row_scale(vr[u], VV);
       }
       float sc = 0.f;
 #pragma unroll
-      for (int e = 0; e < EK; ++e) sc += qt[e] * frag_elem<LS>(kr[u], e);
-      if (kQ8) sc *= q8_row_scale(kr[u], VK);
+      for (int e = 0; e < EK; ++e)
+        if (!kQ8 || kOne || e < RK) sc += qt[e] * frag_elem<LS>(kr[u], e);
       sc = group_sum<LPT>(sc);
+      if (kQ8) sc *= sk;
       sc += beta;
       if (R) sc += srv[u];
       if (ok[u]) {
@@ -204,9 +236,10 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
         }
         const float pr = fast_exp2(sc - m);
         l += pr;
-        const float pv = kQ8 ? pr * q8_row_scale(vr[u], VV) : pr;
+        const float pv = kQ8 ? pr * sv : pr;
 #pragma unroll
-        for (int e = 0; e < EV; ++e) acc[e] += pv * frag_elem<LS>(vr[u], e);
+        for (int e = 0; e < EV; ++e)
+          if (!kQ8 || kOne || e < RV) acc[e] += pv * frag_elem<LS>(vr[u], e);
       }
     }
   };
@@ -308,13 +341,15 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     }
     if (lane < LPT) {
 #pragma unroll
-      for (int e = 0; e < EV; ++e) w[2 + lane * EV + e] = acc[e];
+      for (int e = 0; e < EV; ++e)
+        if (!kQ8 || lane * EV + e < RV) w[2 + lane * EV + e] = acc[e];
     }
     return;
   }
   if (lane < LPT) {
 #pragma unroll
-    for (int e = 0; e < EV; ++e) a_s[lane * EV + e] = acc[e];
+    for (int e = 0; e < EV; ++e)
+      if (!kQ8 || lane * EV + e < RV) a_s[lane * EV + e] = acc[e];
   }
   __syncthreads();
   finish_unit<S>(p, b, h, M, l, a_s, q_s, lane);
@@ -389,13 +424,13 @@ template <class S, int RK, int RV, int LPT, int U>
 PartialFn rope_fn() {
   return decode_partial_kernel<S, S, RK, RV, LPT, U, false, true>;
 }
-template <int RK, int RV, int U>
+template <int RK, int RV, int LPT, int U>
 PartialFn q8_fn() {
-  return decode_partial_kernel<BF16, Q8, RK, RV, 1, U, false>;
+  return decode_partial_kernel<BF16, Q8, RK, RV, LPT, U, false>;
 }
-template <int RK, int RV, int U>
+template <int RK, int RV, int LPT, int U>
 PartialFn q8_gather_fn() {
-  return decode_partial_kernel<BF16, Q8, RK, RV, 1, U, true>;
+  return decode_partial_kernel<BF16, Q8, RK, RV, LPT, U, true>;
 }
 
 struct Entry {
@@ -435,10 +470,10 @@ const Entry kTable[] = {
     {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 32, 4>(), gather_fn<F32, 128, 128, 32, 4>(), nullptr},
     {LLA_F32, 96, 160, partial_fn<F32, 96, 160, 8, 1>(), gather_fn<F32, 96, 160, 8, 1>(), nullptr},
     {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 64, 4>(), gather_fn<F32, 256, 256, 64, 4>(), nullptr},
-    {LLA_BF16_Q8, 8, 8, q8_fn<8, 8, 4>(), q8_gather_fn<8, 8, 4>(), nullptr},
-    {LLA_BF16_Q8, 16, 16, q8_fn<16, 16, 4>(), q8_gather_fn<16, 16, 4>(), nullptr},
-    {LLA_BF16_Q8, 24, 24, q8_fn<24, 24, 3>(), q8_gather_fn<24, 24, 3>(), nullptr},
-    {LLA_BF16_Q8, 32, 32, q8_fn<32, 32, 2>(), q8_gather_fn<32, 32, 2>(), nullptr},
+    {LLA_BF16_Q8, 8, 8, q8_fn<8, 8, 1, 4>(), q8_gather_fn<8, 8, 1, 4>(), nullptr},
+    {LLA_BF16_Q8, 16, 16, q8_fn<16, 16, 2, 4>(), q8_gather_fn<16, 16, 2, 4>(), nullptr},
+    {LLA_BF16_Q8, 24, 24, q8_fn<24, 24, 2, 4>(), q8_gather_fn<24, 24, 2, 4>(), nullptr},
+    {LLA_BF16_Q8, 32, 32, q8_fn<32, 32, 4, 8>(), q8_gather_fn<32, 32, 4, 8>(), nullptr},
 };
 
 const Entry* find(int dtype, int r_k, int r_v) {
