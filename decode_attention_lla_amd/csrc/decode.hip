@@ -184,6 +184,13 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   const __amdgpu_buffer_rsrc_t rsv = buffer_rsrc(static_cast<const char*>(p.zv) + (lrow + row0) * RVB, nrows * RVB);
   constexpr int kAux = G ? 0 : 2;  // non-temporal for the contiguous read
   constexpr bool kPipe = kOne && !G;
+  // Rotary scores (R). With at most 4 lanes per token the pipelined path loads them once per batch:
+  // lane `sub` of a group loads tile sub + LPT*k's score (one load covers 64 consecutive tokens)
+  // and each tile's score is broadcast inside the group (DPP) when the tile is consumed.
+  constexpr bool kSrB = kPipe && LPT <= 4;
+  constexpr int NSR = kSrB ? (U + LPT - 1) / LPT : U;  // score registers per batch
+  const __amdgpu_buffer_rsrc_t rss =
+      buffer_rsrc(R ? p.sr + static_cast<size_t>(bh) * p.sr_stride + row0 : nullptr, R ? nrows * 4 : 0);
 
   const int32_t* srow = G ? p.slots + static_cast<size_t>(b) * p.budget : nullptr;
 
@@ -194,7 +201,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   for (int e = 0; e < EV; ++e) acc[e] = 0.f;
 
   // fold one batch of U tiles (ok: token inside the split and valid) into (m, l, acc)
-  auto consume = [&](uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], const bool (&ok)[U], const float (&srv)[U]) {
+  auto consume = [&](uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], const bool (&ok)[U], const float (&srv)[NSR]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float sk = 1.f, sv = 1.f;  // low-bit row scales
@@ -225,7 +232,16 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
       sc = group_sum<LPT>(sc);
       if (kQ8) sc *= sk;
       sc += beta;
-      if (R) sc += srv[u];
+      if constexpr (R) {
+        if constexpr (kSrB && LPT == 2) {
+          sc += u % 2 == 0 ? dpp_f32<0xa0>(srv[u / 2]) : dpp_f32<0xf5>(srv[u / 2]);  // quad_perm(0,0,2,2) / (1,1,3,3)
+        } else if constexpr (kSrB && LPT == 4) {
+          const float x = srv[u / 4];  // quad_perm(s,s,s,s), s = u % 4 (a constant once unrolled)
+          sc += u % 4 == 0 ? dpp_f32<0x00>(x) : u % 4 == 1 ? dpp_f32<0x55>(x) : u % 4 == 2 ? dpp_f32<0xaa>(x) : dpp_f32<0xff>(x);
+        } else {
+          sc += srv[u];
+        }
+      }
       if (ok[u]) {
         if (sc > m + kLazy) {
           const float c = fast_exp2(m - sc);
@@ -249,14 +265,24 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     // before the current one is consumed, so a wave always has a batch in flight. Rows past the
     // split read as zeros through the descriptor bound (no memory access) and are masked; a
     // batch wholly past the split costs only its masked arithmetic.
-    auto issue = [&](int t0, uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], float (&srv)[U]) {
+    auto issue = [&](int t0, uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], float (&srv)[NSR]) {
+#pragma unroll
+      for (int k = 0; k < NSR; ++k) {
+        if constexpr (R) {
+          const int tile = kSrB ? sub + LPT * k : k;
+          const int tok = t0 + tile * TPW + grp;
+          const uint32_t rr = tile < U ? static_cast<uint32_t>(min(tok, te) - row0) : nrows;
+          srv[k] = __uint_as_float(buffer_words<1, kAux>(rss, rr * 4).x);
+        } else {
+          srv[k] = 0.f;
+        }
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int tok = t0 + u * TPW + grp;
         const uint32_t rr = static_cast<uint32_t>(min(tok, te) - row0);
         kr[u][0] = buffer_words<SK / 4, kAux>(rsk, rr * RKB + sub * SK);
         vr[u][0] = buffer_words<SV / 4, kAux>(rsv, rr * RVB + sub * SV);
-        srv[u] = (R && tok < te) ? p.sr[static_cast<size_t>(bh) * p.sr_stride + tok] : 0.f;
       }
     };
     auto mask = [&](int t0, bool (&ok)[U]) {
@@ -265,7 +291,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     };
     constexpr int kStep = TPW * U;
     uint4 ka[U][VK], va[U][VV], kb[U][VK], vb[U][VV];
-    float sa[U], sb[U];
+    float sa[NSR], sb[NSR];
     bool ok[U];
     if (tb < te) issue(tb, ka, va, sa);
     for (int t0 = tb; t0 < te; t0 += 2 * kStep) {
@@ -294,7 +320,11 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
           slot[u] = ok[u] ? srow[tok] : 0;
           ok[u] = ok[u] && static_cast<unsigned>(slot[u]) < static_cast<unsigned>(p.n_max);
         }
-        srv[u] = (R && ok[u]) ? p.sr[static_cast<size_t>(bh) * p.sr_stride + slot[u]] : 0.f;
+        if constexpr (R && kOne) {
+          srv[u] = __uint_as_float(buffer_words<1, kAux>(rss, (ok[u] ? static_cast<uint32_t>(slot[u] - row0) : nrows) * 4).x);
+        } else {
+          srv[u] = (R && ok[u]) ? p.sr[static_cast<size_t>(bh) * p.sr_stride + slot[u]] : 0.f;
+        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {

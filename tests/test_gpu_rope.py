@@ -62,7 +62,8 @@ def _rope_inputs(rng, B, H, n_max, d_rope):
 @pytest.mark.parametrize("variant,rk,rv,d_rope", [("per_head", 24, 24, 64), ("per_head", 96, 160, 32),
                                                   ("per_head", 128, 128, 128), ("2d", 32, 32, 64),
                                                   ("2d", 256, 256, 64), ("2d", 128, 128, 32),
-                                                  ("2d", 64, 64, 128)])
+                                                  ("2d", 64, 64, 128), ("per_head", 16, 16, 64),
+                                                  ("per_head", 8, 8, 32)])
 def test_decode_rope(variant, rk, rv, d_rope):
     B, H, d, T, n_max = 3, 2, 64, 2, 1301
     lens = np.array([1301, 517, 0], np.int32)
