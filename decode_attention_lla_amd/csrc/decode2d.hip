@@ -214,7 +214,8 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
       const int pc = f - row * CPR;
       const int lc = (pc & ~7) | ((pc & 7) ^ vswz(row));
       const char* src = zvb + (static_cast<size_t>(min(tok0 + row, last)) * RV + lc * 8) * 2;
-      __builtin_amdgcn_global_load_lds((const gptr_t)src, (lptr_t)(dst + i * 1024), 16, 0, 0);
+      // non-temporal: each instruction reads 1 KiB of whole rows that nothing reads again
+      __builtin_amdgcn_global_load_lds((const gptr_t)src, (lptr_t)(dst + i * 1024), 16, 0, 2);
     }
     const char* arow = zkb + static_cast<size_t>(min(tok0 + col, last)) * RK * 2;
 #pragma unroll
