@@ -134,6 +134,31 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   const int tb = uniform(split * p.chunk);
   const int te = uniform(min(nb, tb + p.chunk));
 
+  // One-load rows stream two register batches ahead. The gather read first stages its split's
+  // slot list in LDS (when it fits), so finding a row costs an LDS read rather than a memory round
+  // trip in front of every batch; longer splits take the one-batch loop below.
+  static_assert(!(G && R), "the rotary scores are read for contiguous rows only");
+  constexpr int kSlotCap = 2048;
+  __shared__ __attribute__((aligned(16))) int32_t slot_s[G ? kSlotCap : 4];
+  const int32_t* srow = G ? p.slots + static_cast<size_t>(b) * p.budget : nullptr;
+  const bool piped = kOne && (!G || te - tb <= kSlotCap);
+  if constexpr (G && kOne) {
+    if (piped) {
+      // every 16-byte load of the list issued before any is written to LDS (positions past the
+      // split read as zeros); visible to the other lanes after the barriers below
+      const int n = max(te - tb, 0);
+      const int nk = (n + 255) / 256;  // 256 positions per load instruction
+      const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(srow + tb, static_cast<uint32_t>(n) * 4);
+      uint4 sl[kSlotCap / 256];
+#pragma unroll
+      for (int k = 0; k < kSlotCap / 256; ++k)
+        if (k < nk) sl[k] = buffer_words<4, 0>(rl, static_cast<uint32_t>(k * 64 + lane) * 16);
+#pragma unroll
+      for (int k = 0; k < kSlotCap / 256; ++k)
+        if (k < nk) *reinterpret_cast<uint4*>(&slot_s[(k * 64 + lane) * 4]) = sl[k];
+    }
+  }
+
   // --- 1. query absorption ------------------------------------------------------------------
   const size_t qoff = static_cast<size_t>(bh) * p.d;
   for (int j = lane; j < p.d; j += 64) q_s[j] = ld<S>(p.q, qoff + j);
@@ -182,8 +207,11 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   const uint32_t nrows = static_cast<uint32_t>(uniform(G ? p.n_max : max(te - tb, 0)));
   const __amdgpu_buffer_rsrc_t rsk = buffer_rsrc(static_cast<const char*>(p.zk) + (lrow + row0) * RKB, nrows * RKB);
   const __amdgpu_buffer_rsrc_t rsv = buffer_rsrc(static_cast<const char*>(p.zv) + (lrow + row0) * RVB, nrows * RVB);
-  constexpr int kAux = G ? 0 : 2;  // non-temporal for the contiguous read
-  constexpr bool kPipe = kOne && !G;
+  // non-temporal: rows are read once. For the gather read this pays when listed slots run in
+  // order (a sink + window list: 248 -> 229 us at the capacity shape); a random list of 48-byte
+  // rows reads ~5% slower than with ordinary loads.
+  constexpr int kAux = 2;
+  constexpr bool kPipe = kOne && !G;  // contiguous one-load rows (scores broadcast below)
   // Rotary scores (R). With at most 4 lanes per token the pipelined path loads them once per batch:
   // lane `sub` of a group loads tile sub + LPT*k's score (one load covers 64 consecutive tokens)
   // and each tile's score is broadcast inside the group (DPP) when the tile is consumed.
@@ -191,8 +219,6 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   constexpr int NSR = kSrB ? (U + LPT - 1) / LPT : U;  // score registers per batch
   const __amdgpu_buffer_rsrc_t rss =
       buffer_rsrc(R ? p.sr + static_cast<size_t>(bh) * p.sr_stride + row0 : nullptr, R ? nrows * 4 : 0);
-
-  const int32_t* srow = G ? p.slots + static_cast<size_t>(b) * p.budget : nullptr;
 
   float m = kNegInf;
   float l = 0.f;
@@ -260,11 +286,12 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     }
   };
 
-  if constexpr (kPipe) {
-    // Contiguous one-load rows: two register batches in turn, the next batch's loads issued
-    // before the current one is consumed, so a wave always has a batch in flight. Rows past the
-    // split read as zeros through the descriptor bound (no memory access) and are masked; a
-    // batch wholly past the split costs only its masked arithmetic.
+  if (piped) {
+   if constexpr (kOne) {
+    // Two register batches in turn, the next batch's loads issued before the current one is
+    // consumed, so a wave always has a batch in flight. Rows past the split (or, gathered, with
+    // a slot outside the cache) read as zeros through the descriptor bound (no memory access)
+    // and are masked; a batch wholly past the split costs only its masked arithmetic.
     auto issue = [&](int t0, uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], float (&srv)[NSR]) {
 #pragma unroll
       for (int k = 0; k < NSR; ++k) {
@@ -280,14 +307,25 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int tok = t0 + u * TPW + grp;
-        const uint32_t rr = static_cast<uint32_t>(min(tok, te) - row0);
+        uint32_t rr;
+        if constexpr (G) {
+          const int s = tok < te ? slot_s[min(tok - tb, kSlotCap - 1)] : -1;
+          rr = static_cast<unsigned>(s) < static_cast<unsigned>(p.n_max) ? static_cast<uint32_t>(s) : nrows;
+        } else {
+          rr = static_cast<uint32_t>(min(tok, te) - row0);
+        }
         kr[u][0] = buffer_words<SK / 4, kAux>(rsk, rr * RKB + sub * SK);
         vr[u][0] = buffer_words<SV / 4, kAux>(rsv, rr * RVB + sub * SV);
       }
     };
     auto mask = [&](int t0, bool (&ok)[U]) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) ok[u] = t0 + u * TPW + grp < te;
+      for (int u = 0; u < U; ++u) {
+        const int tok = t0 + u * TPW + grp;
+        ok[u] = tok < te;
+        if constexpr (G)
+          ok[u] = ok[u] && static_cast<unsigned>(slot_s[min(tok - tb, kSlotCap - 1)]) < static_cast<unsigned>(p.n_max);
+      }
     };
     constexpr int kStep = TPW * U;
     uint4 ka[U][VK], va[U][VV], kb[U][VK], vb[U][VV];
@@ -304,7 +342,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
       mask(t0 + kStep, ok);
       consume(kb, vb, ok, sb);
     }
-  } else {
+   }
+  } else if constexpr (!kPipe) {  // the contiguous one-load read always takes the loop above
     for (int t0 = tb; t0 < te; t0 += TPW * U) {
       uint4 kr[U][VK];
       uint4 vr[U][VV];
@@ -598,6 +637,16 @@ void gather_plan(const lla_desc& desc, int B, int budget, int* splits, int* chun
   lla_desc g = desc;
   g.n_max = budget;  // splits range over list positions
   valu_plan(g, B, splits, chunk);
+  // at most 2048 positions per split where 256 splits allow it: such a split's slot list is staged
+  // in LDS by the kernel (a longer split is read without that staging)
+  if (*chunk > 2048 && *splits < 256) {
+    int s = (budget + 2047) / 2048;
+    if (s > 256) s = 256;
+    int c = (budget + s - 1) / s;
+    c = (c + 127) / 128 * 128;
+    *splits = (budget + c - 1) / c;
+    *chunk = c;
+  }
 }
 
 size_t gather_workspace_bytes(const lla_desc& desc, int B, int budget) {

@@ -190,6 +190,21 @@ def test_gather_unsupported_and_workspace():
     assert lla.lla_gather_workspace_bytes(d, 2, 0) == 0
 
 
+def test_gather_plan_keeps_splits_within_the_staged_list():
+    """The gather plan prefers splits of at most 2048 list positions (the kernel stages such a
+    split's slots in LDS) while 256 splits allow it; the workspace holds one partial per split."""
+    per_split = lambda d, B: B * d.H * (2 + d.r_v) * 4  # noqa: E731
+    d = desc(H=64, r_k=24, r_v=24, n_max=5200)
+    # 32 x 64 units: the streaming plan would take 2 splits of 2560 positions; 3 of 1792 instead
+    assert lla.lla_gather_workspace_bytes(d, 32, 5000) == 3 * per_split(d, 32)
+    # a list of 2048 positions fits one staged split: no split-K
+    assert lla.lla_gather_workspace_bytes(d, 64, 2048) == 0
+    # 600000 positions on 2 units: at most 256 splits (the combine's limit); 2344 positions
+    # rounded up to 2432 (whole 128-position tiles) give 247 splits, longer than the staged list
+    d1 = desc(H=2, r_k=8, r_v=8, n_max=5000)
+    assert lla.lla_gather_workspace_bytes(d1, 1, 600000) == 247 * per_split(d1, 1)
+
+
 def test_latent_row_bytes():
     f = lla.lla_latent_row_bytes
     assert (f(lla.LLA_F32, 24), f(lla.LLA_BF16, 24), f(lla.LLA_BF16_Q8, 24)) == (96, 48, 32)

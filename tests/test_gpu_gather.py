@@ -114,6 +114,38 @@ def test_gather_identity_list_matches_contiguous_read():
     assert_lse(host(l2), rl)
 
 
+def test_gather_long_list_takes_the_unstaged_loop():
+    """A 600000-entry list for one row (repeats and out-of-range slots): 247 splits of 2432
+    positions, longer than the kernel stages in LDS, so the one-batch loop runs."""
+    dtype = "bf16"
+    B, H, d, T, n_max, budget = 1, 2, 16, 1, 5000, 600000
+    desc = mk_desc("per_head", dtype, H, d, T, 8, 8, n_max)
+    c = upload(synth.random_case("per_head", dtype, B, H, d, T, 8, 8, n_max, 9250), dtype)
+    slots = synth.random_slots(B, budget, n_max, 9251, p_skip=0.02, p_repeat=0.3)
+    o, lse = gpu_gather(desc, B, 0, c, dtype, slots, [budget - 17])
+    ro, rl = oracle_gather(c, 0, slots, [budget - 17], "per_head")
+    assert_close(o, ro, dtype, "600k list")
+    assert_lse(lse, rl, "600k list")
+
+
+def test_gather_plan_resplit_for_the_staged_list():
+    """2048 (row, head) units and a 5000-entry list: the streaming plan's 2 splits of 2560
+    positions are re-planned as 3 splits of at most 2048, which the kernel stages in LDS."""
+    dtype = "bf16"
+    B, H, d, T, n_max, budget = 32, 64, 16, 1, 5200, 5000
+    desc = mk_desc("per_head", dtype, H, d, T, 24, 24, n_max)
+    ws_bytes = lla.lla_gather_workspace_bytes(desc, B, budget)
+    assert ws_bytes >= B * H * 3 * (2 + 24) * 4  # three splits' partials
+    c = upload(synth.random_case("per_head", dtype, B, H, d, T, 24, 24, n_max, 9260, q_gain=4.0), dtype)
+    slots = synth.random_slots(B, budget, n_max, 9261, p_skip=0.02, p_repeat=0.05)
+    counts = np.full(B, budget, np.int32)
+    counts[::5] = [4097, 2048, 2049, 1, 0, 3000, 5000][: len(counts[::5])]
+    o, lse = gpu_gather(desc, B, 0, c, dtype, slots, counts)
+    ro, rl = oracle_gather(c, 0, slots, counts, "per_head")
+    assert_close(o, ro, dtype, "re-split list")
+    assert_lse(lse, rl, "re-split list")
+
+
 def test_capacity_eviction_full_size_sampled():
     """Capacity shape (B=768, H=16, d=128, T=4, r=24, N=4096 cached) read through a 1024-slot
     StreamingLLM list (4 sinks + the 1020 most recent tokens), at the benchmark's launch shape."""
