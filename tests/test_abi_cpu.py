@@ -190,6 +190,18 @@ def test_gather_unsupported_and_workspace():
     assert lla.lla_gather_workspace_bytes(d, 2, 0) == 0
 
 
+def test_rope_workspace_is_scores_plus_the_decode_plan():
+    """The rotary read's workspace: the rotary scores (rows padded to 4 tokens), the self scores,
+    then the split partials of the decode plan (none when the plan has one split)."""
+    lib = lla.library()
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    scores = lambda d, B: al(B * d.H * ((d.n_max + 3) // 4 * 4) * 4) + al(B * d.H * 4)  # noqa: E731
+    for d, B in ((desc(H=64, r_k=8, r_v=8, n_max=5000), 64), (desc(H=16, r_k=24, r_v=24, n_max=4097), 768),
+                 (desc(H=16, r_k=24, r_v=24, n_max=4097), 2)):
+        need = lib.lla_rope_workspace_bytes(ctypes.byref(d), B)
+        assert need == scores(d, B) + lla.lla_workspace_bytes(d, B)
+
+
 def test_gather_plan_keeps_splits_within_the_staged_list():
     """The gather plan prefers splits of at most 2048 list positions (the kernel stages such a
     split's slots in LDS) while 256 splits allow it; the workspace holds one partial per split."""

@@ -97,6 +97,53 @@ def test_decode_rope(variant, rk, rv, d_rope):
             assert_lse(host(lse), rl, what)
 
 
+def test_decode_rope_many_units_ragged():
+    """4096 (row, head) units over 5000 cached tokens, one split per row, with ragged lengths
+    around multiples of 1024 and of the kernel's batch."""
+    B, H, d, T, n_max, r, d_rope = 64, 64, 16, 1, 5000, 8, 32
+    desc = mk_desc("per_head", "bf16", H, d, T, r, r, n_max)
+    rng = np.random.default_rng(9975)
+    q_rope, k_rope, krs = _rope_inputs(rng, B, H, n_max, d_rope)
+    c = upload(synth.random_case("per_head", "bf16", B, H, d, T, r, r, n_max, 9976, q_gain=4.0), "bf16")
+    lens = np.full(B, n_max, np.int32)
+    lens[::7] = [4096, 4097, 1, 0, 4999, 2048, 1023, 1025, 17, 4095][: len(lens[::7])]
+    q = dev(c["q"][0], "bf16")
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H, device="cuda")
+    lla.lla_attend_decode_rope(desc, B, 0, q, dev(q_rope, "bf16"), c["_zk"], c["_zv"],
+                               dev(k_rope, "bf16"), d_rope, 0.0, dev(lens), c["_Wk"], c["_Wv"],
+                               c["_muk"], c["_muv"], dev(c["k_self"][0], "bf16"),
+                               dev(c["v_self"][0], "bf16"), dev(krs, "bf16"), out, lse,
+                               lla.rope_workspace(desc, B))
+    torch.cuda.synchronize()
+    ro, rl = O.attend_decode_rope(c["q"][0], q_rope, c["zk"], c["zv"], k_rope, c["Wk"], c["Wv"], 0,
+                                  lens, c["mu_k"], c["mu_v"], c["k_self"][0], c["v_self"][0], krs)
+    assert_close(host(out), ro, "bf16", "rope long split")
+    assert_lse(host(lse), rl, "rope long split")
+
+
+def test_decode_rope_very_long_context():
+    """One sequence, 2 heads, 1.2M cached tokens: 254 splits of 4736 tokens."""
+    B, H, d, T, r, d_rope, N = 1, 2, 16, 1, 8, 32, 1200000
+    n_max = N + 3
+    desc = mk_desc("per_head", "bf16", H, d, T, r, r, n_max)
+    rng = np.random.default_rng(9977)
+    q_rope, k_rope, krs = _rope_inputs(rng, B, H, n_max, d_rope)
+    c = upload(synth.random_case("per_head", "bf16", B, H, d, T, r, r, n_max, 9978, q_gain=4.0), "bf16")
+    lens = np.array([N], np.int32)
+    q = dev(c["q"][0], "bf16")
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H, device="cuda")
+    lla.lla_attend_decode_rope(desc, B, 0, q, dev(q_rope, "bf16"), c["_zk"], c["_zv"],
+                               dev(k_rope, "bf16"), d_rope, 0.0, dev(lens), c["_Wk"], c["_Wv"],
+                               None, None, None, None, None, out, lse, lla.rope_workspace(desc, B))
+    torch.cuda.synchronize()
+    ro, rl = O.attend_decode_rope(c["q"][0], q_rope, c["zk"], c["zv"], k_rope, c["Wk"], c["Wv"], 0,
+                                  lens)
+    assert_close(host(out), ro, "bf16", "rope 1.2M")
+    assert_lse(host(lse), rl, "rope 1.2M")
+
+
 def test_decode_rope_long_positions_and_explicit_scale():
     """One sequence at 70000 cached tokens (large rotation angles for the query) and a scale given
     by the descriptor."""
