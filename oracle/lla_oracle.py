@@ -433,6 +433,25 @@ def dequantize_latent_rows(codes, scales):
     return np.asarray(codes, np.float64) * np.asarray(scales, np.float64)[..., None]
 
 
+INT8_MAX = 127.0
+
+
+def quantize_latent_rows_int8(z):
+    """Low-bit latent rows, integer form: each row of r latent values (the last axis) is stored as r
+    signed 8-bit codes and one float32 scale s = max|z| / 127, code_j = round(z_j / s) with halves
+    to even, both divisions in float32 (a row of zeros has s = 0 and zero codes). Symmetric: the
+    codes lie in [-127, 127]. Returns (codes as float64 values, scales as float64 holding float32
+    values)."""
+    z32 = np.asarray(z, np.float32)
+    amax = np.max(np.abs(z32), axis=-1)
+    s = (amax / np.float32(INT8_MAX)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    v = (z32 / safe[..., None]).astype(np.float32)
+    codes = np.clip(np.rint(v.astype(np.float64)), -INT8_MAX, INT8_MAX)  # rint: halves to even
+    codes = np.where((s > 0)[..., None], codes, 0.0)
+    return codes, s.astype(np.float64)
+
+
 # --------------------------------------------------------------------------------------------
 # Decoupled RoPE branch (Section 7, "Per-head LLA versus LLA-2D at inference": an MLA-style split
 # into the NoPE latent content path and a small explicit rotary branch, shared across recurrence

@@ -118,6 +118,30 @@ def _quantize_scale_for_240(z):
     return np.where((s > 0)[..., None], codes, 0.0), s.astype(np.float64)
 
 
+def _int8_scale_for_128(z):
+    z32 = np.asarray(z, np.float32)
+    s = (np.max(np.abs(z32), axis=-1) / np.float32(128.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    codes = np.clip(np.rint((z32 / safe[..., None]).astype(np.float64)), -127, 127)
+    return np.where((s > 0)[..., None], codes, 0.0), s.astype(np.float64)
+
+
+def _int8_rounds_half_up(z):
+    z32 = np.asarray(z, np.float32)
+    s = (np.max(np.abs(z32), axis=-1) / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    codes = np.clip(np.floor((z32 / safe[..., None]).astype(np.float64) + 0.5), -127, 127)
+    return np.where((s > 0)[..., None], codes, 0.0), s.astype(np.float64)
+
+
+def _int8_truncates(z):
+    z32 = np.asarray(z, np.float32)
+    s = (np.max(np.abs(z32), axis=-1) / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    codes = np.clip(np.trunc((z32 / safe[..., None]).astype(np.float64)), -127, 127)
+    return np.where((s > 0)[..., None], codes, 0.0), s.astype(np.float64)
+
+
 def _rope_half_split(x, pos, base=10000.0):
     # pairs (i, i + d/2) instead of RoFormer's (2i, 2i + 1)
     x = np.asarray(x, np.float64)
@@ -166,6 +190,7 @@ _orig = {
     "attend_decode_gather": O.attend_decode_gather,
     "e4m3_round": O.e4m3_round,
     "quantize_latent_rows": O.quantize_latent_rows,
+    "quantize_latent_rows_int8": O.quantize_latent_rows_int8,
     "rope_rotate": O.rope_rotate,
     "attend_decode_rope": O.attend_decode_rope,
     "attend_prefill_rope": O.attend_prefill_rope,
@@ -188,6 +213,9 @@ MUTANTS = {
     "e4m3 truncates instead of rounding": ("e4m3_round", _e4m3_truncates),
     "e4m3 uses exponent bias 8": ("e4m3_round", _e4m3_bias8),
     "quantiser scales for 240 instead of 448": ("quantize_latent_rows", _quantize_scale_for_240),
+    "int8 quantiser scales for 128": ("quantize_latent_rows_int8", _int8_scale_for_128),
+    "int8 quantiser rounds halves up": ("quantize_latent_rows_int8", _int8_rounds_half_up),
+    "int8 quantiser truncates": ("quantize_latent_rows_int8", _int8_truncates),
     "rope pairs channels i and i + d/2": ("rope_rotate", _rope_half_split),
     "rope query rotated one position back": ("attend_decode_rope", _rope_decode_query_one_back),
     "rope decode scales by the content width only": ("attend_decode_rope", _rope_decode_content_scale),
@@ -210,6 +238,8 @@ PINS = [
     Q.test_every_e4m3_value_rounds_to_itself,
     Q.test_rounding_matches_torch_float8_e4m3fn,
     Q.test_quantized_rows_bound_and_extremes,
+    Q.test_int8_rows_extremes_bound_and_symmetry,
+    Q.test_int8_integer_rows_and_ties_to_even,
     R.test_rotation_closed_form_and_identity,
     R.test_full_rank_codec_equals_sdpa_on_concatenated_keys,
     R.test_common_position_shift_changes_nothing,

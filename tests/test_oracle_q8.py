@@ -61,3 +61,44 @@ def test_quantized_rows_bound_and_extremes():
     assert np.all(err <= bound)
     # and every code is an E4M3 value
     assert np.isin(codes, _all_e4m3_values()).all()
+
+
+# --------------------------------------------------------------------------------------------
+# integer rows: symmetric int8 codes with one float32 scale per row
+# --------------------------------------------------------------------------------------------
+
+def test_int8_rows_extremes_bound_and_symmetry():
+    rng = np.random.default_rng(18)
+    z = (rng.standard_normal((64, 24)) * 10.0 ** rng.uniform(-3, 3, (64, 1))).astype(np.float32)
+    z[5] = 0.0
+    codes, s = O.quantize_latent_rows_int8(z)
+    assert s[5] == 0 and np.all(codes[5] == 0)
+    live = s > 0
+    # integer codes in [-127, 127]; the largest magnitude of each row lands on +-127 exactly
+    np.testing.assert_array_equal(codes, np.round(codes))
+    assert np.max(np.abs(codes)) <= 127
+    np.testing.assert_array_equal(np.max(np.abs(codes[live]), axis=1), 127.0)
+    np.testing.assert_array_equal(np.sign(codes[live][np.abs(codes[live]) == 127]),
+                                  np.sign(z[live][np.abs(codes[live]) == 127]))
+    # scales are float32 values equal to max|z| / 127 rounded to float32
+    np.testing.assert_array_equal(s, (np.max(np.abs(z), axis=1) / np.float32(127)).astype(np.float32))
+    # round to nearest: at most half a step from the value
+    err = np.abs(O.dequantize_latent_rows(codes, s) - z)
+    assert np.all(err <= s[:, None] * (0.5 + 1e-5))
+    # odd symmetry
+    cn, sn = O.quantize_latent_rows_int8(-z)
+    np.testing.assert_array_equal(sn, s)
+    np.testing.assert_array_equal(cn, -codes)
+
+
+def test_int8_integer_rows_and_ties_to_even():
+    # a row of integers whose largest magnitude is 127 has scale 1 and reproduces itself
+    z = np.array([[127, -3, 0, 64, -127, 1, 2, -100]], np.float32)
+    codes, s = O.quantize_latent_rows_int8(z)
+    assert s[0] == 1.0
+    np.testing.assert_array_equal(codes, z)
+    # scale 2 (max 254): z / s = k + 1/2 exactly, ties go to the even neighbour
+    z = np.array([[254, 1, 3, 5, -1, -3, -5, 7]], np.float32)
+    codes, s = O.quantize_latent_rows_int8(z)
+    assert s[0] == 2.0
+    np.testing.assert_array_equal(codes, [[127, 0, 2, 2, -0, -2, -2, 4]])
