@@ -405,72 +405,82 @@ def eviction_decode(args):
 
 def low_bit_capacity(args, bf16_tokens_per_s):
     """The capacity step (24 layers, H=16, d=128, T=4, r=24/24, B=768, 4096 cached tokens) with
-    low-bit latent rows (LLA_BF16_Q8: 24 E4M3 codes + a float32 scale, 32 bytes per row instead of
-    48): 96 decode reads, then per layer an encode of the new token into a bf16 staging row and its
-    quantisation into slot N."""
+    low-bit latent rows (24 codes + a float32 scale, 32 bytes per row instead of 48): 96 decode
+    reads, then per layer an encode of the new token into a bf16 staging row and its quantisation
+    into slot N. E4M3 codes (LLA_BF16_Q8) at the top level, int8 codes (LLA_BF16_I8) under "int8";
+    each form's caches are built and freed in turn."""
     import torch
     from decode_attention_lla_amd import lla, synth
     s = synth.CASES["capacity"]
     D, B, H, d, T, r, N = s.D, s.B, s.H, s.d, s.T, s.r_k, s.N
     n_max = N + 1
     bf = torch.bfloat16
-    desc = lla.make_desc(lla.LLA_PER_HEAD, lla.LLA_BF16_Q8, H, d, T, r, r, n_max)
-    desc_stage = lla.make_desc(lla.LLA_PER_HEAD, lla.LLA_BF16, H, d, T, r, r, 1)
-    rb = lla.lla_latent_row_bytes(lla.LLA_BF16_Q8, r)
-    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
-    stage = torch.empty(B, H, n_max, r, dtype=bf, device="cuda")
-    stage_v = torch.empty_like(stage)
-    ck, cv, Wk, Wv, Ek, Ev = [], [], [], [], [], []
-    for l in range(D):
-        synth.device_normal_(stage, synth.seed(s.case, synth.SEED_ZK, l))
-        synth.device_normal_(stage_v, synth.seed(s.case, synth.SEED_ZV, l))
-        ck.append(torch.empty(B, H, n_max, rb, dtype=torch.uint8, device="cuda"))
-        cv.append(torch.empty(B, H, n_max, rb, dtype=torch.uint8, device="cuda"))
-        lla.lla_quantize_latents(desc, B, n_max, stage, stage_v, zero, ck[l], cv[l])
-        wk = synth.orthonormal_W(T, H, d, r, synth.seed(s.case, synth.SEED_WK, l), "bf16")
-        wv = synth.orthonormal_W(T, H, d, r, synth.seed(s.case, synth.SEED_WV, l), "bf16")
-        Wk.append(torch.from_numpy(wk).to(bf).cuda())
-        Wv.append(torch.from_numpy(wv).to(bf).cuda())
-        Ek.append(torch.from_numpy(synth.pinv_E_from_W(wk, "bf16")).to(bf).cuda())
-        Ev.append(torch.from_numpy(synth.pinv_E_from_W(wv, "bf16")).to(bf).cuda())
-    del stage, stage_v
-    torch.cuda.empty_cache()
-    q = synth.device_normal_(torch.empty(T, D, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_Q))
-    kself = synth.device_normal_(torch.empty(T, D, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF))
-    vself = synth.device_normal_(torch.empty(T, D, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF) + 1)
-    xk = synth.device_normal_(torch.empty(D, B, 1, T, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_XK))
-    xv = synth.device_normal_(torch.empty(D, B, 1, T, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_XV))
-    sk = torch.empty(B, H, 1, r, dtype=bf, device="cuda")
-    sv = torch.empty_like(sk)
-    out = torch.empty(B, H, d, dtype=bf, device="cuda")
-    lens = torch.full((B,), N, dtype=torch.int32, device="cuda")
-    ws = lla.workspace(desc, B, 1)
-    stream = torch.cuda.current_stream()
 
-    def read(t, l):
-        lla.lla_attend_decode(desc, B, t, q[t, l], ck[l], cv[l], lens, Wk[l], Wv[l], None, None,
-                              kself[t, l], vself[t, l], out, None, ws, stream)
-
-    def step():
-        for t in range(T):
-            for l in range(D):
-                read(t, l)
+    def run(dtype):
+        desc = lla.make_desc(lla.LLA_PER_HEAD, dtype, H, d, T, r, r, n_max)
+        desc_stage = lla.make_desc(lla.LLA_PER_HEAD, lla.LLA_BF16, H, d, T, r, r, 1)
+        rb = lla.lla_latent_row_bytes(dtype, r)
+        zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+        stage = torch.empty(B, H, n_max, r, dtype=bf, device="cuda")
+        stage_v = torch.empty_like(stage)
+        ck, cv, Wk, Wv, Ek, Ev = [], [], [], [], [], []
         for l in range(D):
-            lla.lla_encode(desc_stage, B, 1, xk[l], xv[l], Ek[l], Ev[l], None, None, zero, sk, sv, stream)
-            lla.lla_quantize_latents(desc, B, 1, sk, sv, lens, ck[l], cv[l], stream)
+            synth.device_normal_(stage, synth.seed(s.case, synth.SEED_ZK, l))
+            synth.device_normal_(stage_v, synth.seed(s.case, synth.SEED_ZV, l))
+            ck.append(torch.empty(B, H, n_max, rb, dtype=torch.uint8, device="cuda"))
+            cv.append(torch.empty(B, H, n_max, rb, dtype=torch.uint8, device="cuda"))
+            lla.lla_quantize_latents(desc, B, n_max, stage, stage_v, zero, ck[l], cv[l])
+            wk = synth.orthonormal_W(T, H, d, r, synth.seed(s.case, synth.SEED_WK, l), "bf16")
+            wv = synth.orthonormal_W(T, H, d, r, synth.seed(s.case, synth.SEED_WV, l), "bf16")
+            Wk.append(torch.from_numpy(wk).to(bf).cuda())
+            Wv.append(torch.from_numpy(wv).to(bf).cuda())
+            Ek.append(torch.from_numpy(synth.pinv_E_from_W(wk, "bf16")).to(bf).cuda())
+            Ev.append(torch.from_numpy(synth.pinv_E_from_W(wv, "bf16")).to(bf).cuda())
+        del stage, stage_v
+        torch.cuda.empty_cache()
+        q = synth.device_normal_(torch.empty(T, D, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_Q))
+        kself = synth.device_normal_(torch.empty(T, D, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF))
+        vself = synth.device_normal_(torch.empty(T, D, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF) + 1)
+        xk = synth.device_normal_(torch.empty(D, B, 1, T, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_XK))
+        xv = synth.device_normal_(torch.empty(D, B, 1, T, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_XV))
+        sk = torch.empty(B, H, 1, r, dtype=bf, device="cuda")
+        sv = torch.empty_like(sk)
+        out = torch.empty(B, H, d, dtype=bf, device="cuda")
+        lens = torch.full((B,), N, dtype=torch.int32, device="cuda")
+        ws = lla.workspace(desc, B, 1)
+        stream = torch.cuda.current_stream()
 
-    ms_step = _timed(step, max(3, args.steps // 4), 1)
-    ms_read = _timed(lambda: read(0, 0), 20, 3)
-    row_bytes = B * H * N * 2 * rb
+        def read(t, l):
+            lla.lla_attend_decode(desc, B, t, q[t, l], ck[l], cv[l], lens, Wk[l], Wv[l], None, None,
+                                  kself[t, l], vself[t, l], out, None, ws, stream)
+
+        def step():
+            for t in range(T):
+                for l in range(D):
+                    read(t, l)
+            for l in range(D):
+                lla.lla_encode(desc_stage, B, 1, xk[l], xv[l], Ek[l], Ev[l], None, None, zero, sk, sv, stream)
+                lla.lla_quantize_latents(desc, B, 1, sk, sv, lens, ck[l], cv[l], stream)
+
+        ms_step = _timed(step, max(3, args.steps // 4), 1)
+        ms_read = _timed(lambda: read(0, 0), 20, 3)
+        row_bytes = B * H * N * 2 * rb
+        res = {"tokens_per_s": round(B / (ms_step / 1e3), 1), "ms_per_step": round(ms_step, 4),
+               "read_us": round(ms_read * 1e3, 2),
+               "row_GBps": round(row_bytes / (ms_read / 1e3) / 1e9, 1),
+               "row_frac_of_peak": round(row_bytes / (ms_read / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+               "resident_latent_bytes": sum(t.numel() for t in ck + cv)}
+        if bf16_tokens_per_s:
+            res["speedup_vs_bf16_latents"] = round(B / (ms_step / 1e3) / bf16_tokens_per_s, 3)
+        del ck, cv
+        torch.cuda.empty_cache()
+        return res, rb
+
+    res, rb = run(lla.LLA_BF16_Q8)
     res = {"workload": f"capacity with low-bit latents: {D} layers, H={H}, d_head={d}, T={T}, "
-                       f"r_k=r_v={r}, B={B}, N={N}; {rb}-byte rows (E4M3 codes + float32 scale)",
-           "tokens_per_s": round(B / (ms_step / 1e3), 1), "ms_per_step": round(ms_step, 4),
-           "read_us": round(ms_read * 1e3, 2),
-           "row_GBps": round(row_bytes / (ms_read / 1e3) / 1e9, 1),
-           "row_frac_of_peak": round(row_bytes / (ms_read / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-           "resident_latent_bytes": sum(t.numel() for t in ck + cv)}
-    if bf16_tokens_per_s:
-        res["speedup_vs_bf16_latents"] = round(B / (ms_step / 1e3) / bf16_tokens_per_s, 3)
+                       f"r_k=r_v={r}, B={B}, N={N}; {rb}-byte rows (E4M3 codes + float32 scale; "
+                       f"int8: int8 codes + float32 scale)", **res}
+    res["int8"] = run(lla.LLA_BF16_I8)[0]
     return res
 
 

@@ -19,7 +19,8 @@ bool req_ok(const void* p) { return p != nullptr && aligned16(p); }
 bool desc_ok(const lla_desc* d) {
   if (d == nullptr) return false;
   if (d->variant != LLA_PER_HEAD && d->variant != LLA_2D) return false;
-  if (d->dtype != LLA_F32 && d->dtype != LLA_BF16 && d->dtype != LLA_BF16_Q8) return false;
+  if (d->dtype != LLA_F32 && d->dtype != LLA_BF16 && d->dtype != LLA_BF16_Q8 && d->dtype != LLA_BF16_I8)
+    return false;
   if (d->H <= 0 || d->T <= 0 || d->r_k <= 0 || d->r_v <= 0 || d->n_max <= 0) return false;
   if (d->d_head <= 0 || d->d_head > 256 || (d->d_head % 8) != 0) return false;
   if (!(d->scale >= 0.f) || std::isinf(d->scale)) return false;
@@ -117,7 +118,8 @@ size_t lla_latent_row_bytes(int32_t dtype, int32_t r) {
   switch (dtype) {
     case LLA_F32: return 4 * static_cast<size_t>(r);
     case LLA_BF16: return 2 * static_cast<size_t>(r);
-    case LLA_BF16_Q8: return (static_cast<size_t>(r) + 4 + 15) / 16 * 16;
+    case LLA_BF16_Q8:
+    case LLA_BF16_I8: return (static_cast<size_t>(r) + 4 + 15) / 16 * 16;
   }
   return 0;
 }
@@ -125,7 +127,8 @@ size_t lla_latent_row_bytes(int32_t dtype, int32_t r) {
 lla_status lla_quantize_latents(const lla_desc* desc, int32_t B, int32_t C, const void* zk_src,
                                 const void* zv_src, const int32_t* pos, void* zk, void* zv,
                                 void* stream) {
-  if (!desc_ok(desc) || desc->dtype != LLA_BF16_Q8 || B <= 0 || C <= 0 || C > desc->n_max)
+  if (!desc_ok(desc) || (desc->dtype != LLA_BF16_Q8 && desc->dtype != LLA_BF16_I8) || B <= 0 ||
+      C <= 0 || C > desc->n_max)
     return LLA_ERR_INVALID_ARG;
   if (desc->r_k > 512 || desc->r_v > 512) return LLA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(B) * C * desc->H >= (int64_t(1) << 31)) return LLA_ERR_INVALID_ARG;
@@ -133,6 +136,7 @@ lla_status lla_quantize_latents(const lla_desc* desc, int32_t B, int32_t C, cons
     return LLA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   lla::QuantParams p{};
+  p.int8 = desc->dtype == LLA_BF16_I8;
   p.pos = pos;
   p.B = B;
   p.C = C;

@@ -98,7 +98,7 @@ __device__ void finish_unit(const DecodeParams& p, int b, int h, float M, float 
 // score also gets its precomputed base-2 rotary score p.sr[bh][slot] (decoupled RoPE branch).
 template <class S, class LS, int RK, int RV, int LPT, int U, bool G, bool R = false>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
-  constexpr bool kQ8 = std::is_same<LS, Q8>::value;
+  constexpr bool kQ8 = std::is_same<LS, Q8>::value || std::is_same<LS, I8>::value;  // low-bit rows
   constexpr int RKB = LS::row(RK);  // bytes per latent row
   constexpr int RVB = LS::row(RV);
   // A lane's slice of a row: RK / LPT elements, or for low-bit rows RKB / LPT byte slots (codes,
@@ -493,13 +493,13 @@ template <class S, int RK, int RV, int LPT, int U>
 PartialFn rope_fn() {
   return decode_partial_kernel<S, S, RK, RV, LPT, U, false, true>;
 }
-template <int RK, int RV, int LPT, int U>
+template <class LS, int RK, int RV, int LPT, int U>
 PartialFn q8_fn() {
-  return decode_partial_kernel<BF16, Q8, RK, RV, LPT, U, false>;
+  return decode_partial_kernel<BF16, LS, RK, RV, LPT, U, false>;
 }
-template <int RK, int RV, int LPT, int U>
+template <class LS, int RK, int RV, int LPT, int U>
 PartialFn q8_gather_fn() {
-  return decode_partial_kernel<BF16, Q8, RK, RV, LPT, U, true>;
+  return decode_partial_kernel<BF16, LS, RK, RV, LPT, U, true>;
 }
 
 struct Entry {
@@ -539,10 +539,14 @@ const Entry kTable[] = {
     {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 32, 4>(), gather_fn<F32, 128, 128, 32, 4>(), nullptr},
     {LLA_F32, 96, 160, partial_fn<F32, 96, 160, 8, 1>(), gather_fn<F32, 96, 160, 8, 1>(), nullptr},
     {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 64, 4>(), gather_fn<F32, 256, 256, 64, 4>(), nullptr},
-    {LLA_BF16_Q8, 8, 8, q8_fn<8, 8, 1, 4>(), q8_gather_fn<8, 8, 1, 4>(), nullptr},
-    {LLA_BF16_Q8, 16, 16, q8_fn<16, 16, 2, 4>(), q8_gather_fn<16, 16, 2, 4>(), nullptr},
-    {LLA_BF16_Q8, 24, 24, q8_fn<24, 24, 2, 4>(), q8_gather_fn<24, 24, 2, 4>(), nullptr},
-    {LLA_BF16_Q8, 32, 32, q8_fn<32, 32, 4, 8>(), q8_gather_fn<32, 32, 4, 8>(), nullptr},
+    {LLA_BF16_Q8, 8, 8, q8_fn<Q8, 8, 8, 1, 4>(), q8_gather_fn<Q8, 8, 8, 1, 4>(), nullptr},
+    {LLA_BF16_Q8, 16, 16, q8_fn<Q8, 16, 16, 2, 4>(), q8_gather_fn<Q8, 16, 16, 2, 4>(), nullptr},
+    {LLA_BF16_Q8, 24, 24, q8_fn<Q8, 24, 24, 2, 4>(), q8_gather_fn<Q8, 24, 24, 2, 4>(), nullptr},
+    {LLA_BF16_Q8, 32, 32, q8_fn<Q8, 32, 32, 4, 8>(), q8_gather_fn<Q8, 32, 32, 4, 8>(), nullptr},
+    {LLA_BF16_I8, 8, 8, q8_fn<I8, 8, 8, 1, 4>(), q8_gather_fn<I8, 8, 8, 1, 4>(), nullptr},
+    {LLA_BF16_I8, 16, 16, q8_fn<I8, 16, 16, 2, 4>(), q8_gather_fn<I8, 16, 16, 2, 4>(), nullptr},
+    {LLA_BF16_I8, 24, 24, q8_fn<I8, 24, 24, 2, 4>(), q8_gather_fn<I8, 24, 24, 2, 4>(), nullptr},
+    {LLA_BF16_I8, 32, 32, q8_fn<I8, 32, 32, 4, 8>(), q8_gather_fn<I8, 32, 32, 4, 8>(), nullptr},
 };
 
 const Entry* find(int dtype, int r_k, int r_v) {
@@ -614,7 +618,7 @@ hipError_t launch_valu(const DecodeParams& p, int dtype, PartialFn fn, hipStream
   hipLaunchKernelGGL(fn, dim3(units), dim3(64), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;
-  if (dtype == LLA_BF16 || dtype == LLA_BF16_Q8)
+  if (dtype == LLA_BF16 || dtype == LLA_BF16_Q8 || dtype == LLA_BF16_I8)
     hipLaunchKernelGGL(decode_combine_kernel<BF16>, dim3(p.B * p.H), dim3(kCombineThreads), 0, stream, p);
   else
     hipLaunchKernelGGL(decode_combine_kernel<F32>, dim3(p.B * p.H), dim3(kCombineThreads), 0, stream, p);

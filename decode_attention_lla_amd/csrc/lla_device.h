@@ -22,6 +22,11 @@ struct Q8 {
   static constexpr int kBytes = 1;
   static constexpr int row(int r) { return (r + 4 + 15) / 16 * 16; }
 };
+// The same rows with symmetric int8 codes (scale max|z| / 127).
+struct I8 {
+  static constexpr int kBytes = 1;
+  static constexpr int row(int r) { return Q8::row(r); }
+};
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -111,6 +116,14 @@ __device__ __forceinline__ float frag_elem<Q8>(const uint4* f, int e) {
   }
 }
 // The float32 scale of a low-bit row held as V 16-byte words.
+template <>
+__device__ __forceinline__ float frag_elem<I8>(const uint4* f, int e) {
+  const uint4 w = f[e >> 4];
+  const int k = (e & 15) >> 2;
+  const uint32_t x = k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w;
+  return static_cast<float>(static_cast<int8_t>(x >> (8 * (e & 3))));  // sign-extending byte extract
+}
+
 __device__ __forceinline__ float q8_row_scale(const uint4* f, int V) { return __uint_as_float(f[V - 1].w); }
 
 // 16-byte load of data that is read exactly once, for loads whose 64 lanes cover whole cache

@@ -93,6 +93,7 @@ struct QuantParams {
   void* dst;           // low-bit cache [B][H][n_max][Q8::row(r)] bytes
   const int32_t* pos;  // [B]
   int32_t B, C, H, r, n_max;
+  bool int8;           // LLA_BF16_I8 codes (else LLA_BF16_Q8)
 };
 
 struct PrefillParams {

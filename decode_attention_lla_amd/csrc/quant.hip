@@ -1,5 +1,5 @@
-// Low-bit latent rows (LLA_BF16_Q8): bf16 latent rows quantised to OCP FP8 E4M3 codes with one
-// float32 scale per row, written into a low-bit cache.
+// Low-bit latent rows (LLA_BF16_Q8, LLA_BF16_I8): bf16 latent rows quantised to OCP FP8 E4M3 or
+// symmetric int8 codes with one float32 scale per row, written into a low-bit cache.
 //
 // Method context: O'Neill & Reid, "Looped Latent Attention", arXiv 2607.15456. Section 8
 // ("Compositionality") notes that quantisation acts on a different tensor dimension than the loop
@@ -7,6 +7,8 @@
 // LLA_BF16_Q8 in lla.h: s = max|z| / 448, code_j = e4m3(z_j / s), both divisions in float32 and
 // rounded to nearest even (gfx950's v_cvt_pk_fp8_f32 rounds to nearest even in the OCP E4M3
 // format), codes at bytes [0, r), zero padding, s in the last 4 bytes of a 16-byte-aligned row.
+// LLA_BF16_I8: s = max|z| / 127, code_j = round(z_j / s) with halves to even (v_rndne_f32) as a
+// two's-complement byte, the division in float32; same layout.
 #include <hip/hip_runtime.h>
 
 #include "lla_device.h"
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QuantParams p) 
   const uint16_t* src = static_cast<const uint16_t*>(p.src) + row * p.r;
   float amax = 0.f;
   for (int j = 0; j < p.r; ++j) amax = fmaxf(amax, fabsf(__uint_as_float(uint32_t(src[j]) << 16)));
-  const float s = amax / 448.0f;
+  const float s = amax / (p.int8 ? 127.0f : 448.0f);
 
   const int row_bytes = Q8::row(p.r);
   uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(p.dst) +
@@ -48,9 +50,19 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QuantParams p) 
         const int j = 16 * k + 4 * q + e;
         v[e] = (j < p.r && s > 0.f) ? __uint_as_float(uint32_t(src[j]) << 16) / s : 0.f;
       }
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);  // bytes 0, 1
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);     // bytes 2, 3
-      w[q] = static_cast<uint32_t>(word);
+      if (p.int8) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float c = fminf(fmaxf(__builtin_rintf(v[e]), -127.f), 127.f);  // |v| <= 127 already
+          word |= (static_cast<uint32_t>(static_cast<int32_t>(c)) & 0xffu) << (8 * e);
+        }
+        w[q] = word;
+      } else {
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);  // bytes 0, 1
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);     // bytes 2, 3
+        w[q] = static_cast<uint32_t>(word);
+      }
     }
     if (k == chunks - 1) w[3] = __float_as_uint(s);  // codes never reach the last word
     dst[k] = make_uint4(w[0], w[1], w[2], w[3]);

@@ -17,12 +17,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblla.so")
 
 LLA_OK, LLA_ERR_INVALID_ARG, LLA_ERR_UNSUPPORTED, LLA_ERR_WORKSPACE, LLA_ERR_HIP = range(5)
-LLA_F32, LLA_BF16, LLA_BF16_Q8 = 0, 1, 2
+LLA_F32, LLA_BF16, LLA_BF16_Q8, LLA_BF16_I8 = 0, 1, 2, 3
+_LOW_BIT = (LLA_BF16_Q8, LLA_BF16_I8)
 LLA_PER_HEAD, LLA_2D = 0, 1
 
-# dtype of the arithmetic arrays (q, W, E, mu, x, self K/V, out); LLA_BF16_Q8 latent caches are
+# dtype of the arithmetic arrays (q, W, E, mu, x, self K/V, out); low-bit latent caches are
 # uint8 rows of lla_latent_row_bytes bytes
-_TORCH_DTYPE = {LLA_F32: torch.float32, LLA_BF16: torch.bfloat16, LLA_BF16_Q8: torch.bfloat16}
+_TORCH_DTYPE = {LLA_F32: torch.float32, LLA_BF16: torch.bfloat16, LLA_BF16_Q8: torch.bfloat16,
+                LLA_BF16_I8: torch.bfloat16}
 
 
 class lla_desc(ctypes.Structure):
@@ -150,9 +152,9 @@ def _q8_row(r):
 
 
 def _shapes(desc, B):
-    """Shapes of the descriptor's arrays; for LLA_BF16_Q8 the cache rows are bytes."""
+    """Shapes of the descriptor's arrays; for low-bit latents the cache rows are bytes."""
     H, d, T, rk, rv, n = desc.H, desc.d_head, desc.T, desc.r_k, desc.r_v, desc.n_max
-    lk, lv = (_q8_row(rk), _q8_row(rv)) if desc.dtype == LLA_BF16_Q8 else (rk, rv)
+    lk, lv = (_q8_row(rk), _q8_row(rv)) if desc.dtype in _LOW_BIT else (rk, rv)
     if desc.variant == LLA_PER_HEAD:
         return dict(zk=(B, H, n, lk), zv=(B, H, n, lv), Wk=(T, H, d, rk), Wv=(T, H, d, rv),
                     Ek=(H, rk, T * d), Ev=(H, rv, T * d), mu=(H, T * d))
@@ -162,7 +164,7 @@ def _shapes(desc, B):
 
 def _zdt(desc):
     """dtype of the latent cache tensors."""
-    return torch.uint8 if desc.dtype == LLA_BF16_Q8 else _TORCH_DTYPE[desc.dtype]
+    return torch.uint8 if desc.dtype in _LOW_BIT else _TORCH_DTYPE[desc.dtype]
 
 
 def _check(status, where):

@@ -15,8 +15,9 @@
  *   - Loops are numbered t = 0 .. T-1 (the paper counts 1 .. T).
  *   - Every array is dense, row-major and innermost-last, as written next to each argument.
  *   - Storage dtype: desc->dtype (LLA_F32 or LLA_BF16) applies to every floating-point array
- *     argument except `lse`, which is always float32. LLA_BF16_Q8 means bf16 for every array
- *     except the latent cache (zk, zv), whose rows are low-bit (see lla_latent_row_bytes). Accumulation is always float32. Stored
+ *     argument except `lse`, which is always float32. LLA_BF16_Q8 and LLA_BF16_I8 mean bf16 for
+ *     every array except the latent cache (zk, zv), whose rows are low-bit (see
+ *     lla_latent_row_bytes). Accumulation is always float32. Stored
  *     results are rounded to nearest-even once.
  *   - Pointers marked [device] are HIP device addresses (or managed memory). Device pointers must
  *     be 16-byte aligned. Pointers marked [host] are ordinary host memory.
@@ -59,8 +60,15 @@ typedef enum {
  * row is padded to a multiple of 16 bytes: codes at bytes [0, r), zeros, s in the last 4 bytes.
  * Rows are written by lla_quantize_latents and read by lla_attend_decode, lla_attend_decode_gather
  * and lla_attend_prefill, all on the streaming kernels; lla_encode returns LLA_ERR_UNSUPPORTED for
- * it (encode with a bf16 descriptor, then quantise). */
-typedef enum { LLA_F32 = 0, LLA_BF16 = 1, LLA_BF16_Q8 = 2 } lla_dtype;
+ * it (encode with a bf16 descriptor, then quantise).
+ *
+ * LLA_BF16_I8: the same rows with symmetric integer codes (the pages' 8-bit codec is not specified
+ * further; both common 8-bit forms are offered): s = max|z| / 127 and code_j = round(z_j / s) with
+ * halves to even, a two's-complement int8 in [-127, 127], both divisions in float32; same layout
+ * (codes at bytes [0, r), zeros, s in the last 4 bytes of a 16-byte-aligned row). Uniform steps
+ * of s across the row instead of E4M3's 3-bit mantissa: finer near the row maximum, coarser near
+ * zero. */
+typedef enum { LLA_F32 = 0, LLA_BF16 = 1, LLA_BF16_Q8 = 2, LLA_BF16_I8 = 3 } lla_dtype;
 
 /* LLA_PER_HEAD: one latent per (token, head, axis); Section 3, Eqs. 2-3.
  * LLA_2D:       one latent per (token, axis) that rebuilds every head; Section 3, "The LLA-2D
@@ -83,12 +91,13 @@ typedef struct {
 } lla_desc;
 
 /* Bytes of one cached latent row of r values for a storage dtype: 4r (LLA_F32), 2r (LLA_BF16),
- * r + 4 rounded up to a multiple of 16 (LLA_BF16_Q8). 0 for an unknown dtype or r <= 0. The cache
+ * r + 4 rounded up to a multiple of 16 (LLA_BF16_Q8, LLA_BF16_I8). 0 for an unknown dtype or
+ * r <= 0. The cache
  * is [B][H][n_max][row] per head and [B][n_max][row] for LLA-2D, rows of this many bytes. */
 size_t lla_latent_row_bytes(int32_t dtype, int32_t r);
 
-/* Write C latent rows per sequence (and head) into a low-bit cache (desc->dtype == LLA_BF16_Q8),
- * quantising each row as described at LLA_BF16_Q8.
+/* Write C latent rows per sequence (and head) into a low-bit cache (desc->dtype == LLA_BF16_Q8 or
+ * LLA_BF16_I8), quantising each row as described at that dtype.
  *
  *   zk_src, zv_src [device] bf16 rows: per-head [B][H][C][r], 2D [B][C][r] (for instance the
  *                  output of lla_encode with a bf16 descriptor, n_max = C and pos = 0).
@@ -107,8 +116,8 @@ lla_status lla_quantize_latents(const lla_desc* desc, int32_t B, int32_t C, cons
  *   Chunked prefill, bf16, d_head a multiple of 32, on MFMA:  (64,64) (128,128) (256,256)
  *                                                              (64,128) (128,256)
  *   Encode: any r <= 512 (bf16 on MFMA, fp32 on the VALU).
- *   Low-bit latents (LLA_BF16_Q8), decode, gather decode and prefill, both variants on the
- *   streaming kernels:                                        (8,8) (16,16) (24,24) (32,32)
+ *   Low-bit latents (LLA_BF16_Q8, LLA_BF16_I8), decode, gather decode and prefill, both
+ *   variants on the streaming kernels:                        (8,8) (16,16) (24,24) (32,32)
  * A decode or prefill call with a pair that none of these covers returns LLA_ERR_UNSUPPORTED. */
 
 /* Bytes of device workspace that lla_attend_decode (C == 1) or lla_attend_prefill (C > 1) needs

@@ -223,6 +223,7 @@ def test_latent_row_bytes():
     assert [f(lla.LLA_BF16_Q8, r) for r in (1, 8, 12, 13, 16, 28, 32, 256)] == \
         [16, 16, 16, 32, 32, 32, 48, 272]
     assert f(7, 8) == 0 and f(lla.LLA_BF16_Q8, 0) == 0
+    assert [f(lla.LLA_BF16_I8, r) for r in (1, 12, 13, 24, 32)] == [16, 16, 32, 32, 48]
 
 
 def quantize(d, B=2, C=1, ks=A, vs=A, pos=A, zk=A, zv=A):
@@ -234,22 +235,27 @@ def quantize(d, B=2, C=1, ks=A, vs=A, pos=A, zk=A, zv=A):
     (dict(ks=N), {}), (dict(vs=M), {}), (dict(pos=N), {}), (dict(zk=M), {}), (dict(zv=N), {}),
     (dict(), dict(r_k=513)),
 ])
-def test_quantize_rejects_bad_arguments(kw, dkw):
-    base = dict(dtype=lla.LLA_BF16_Q8, n_max=100, r_k=24, r_v=24)
+@pytest.mark.parametrize("low", ["LLA_BF16_Q8", "LLA_BF16_I8"])
+def test_quantize_rejects_bad_arguments(kw, dkw, low):
+    base = dict(dtype=getattr(lla, low), n_max=100, r_k=24, r_v=24)
     base.update(dkw)
     assert quantize(desc(**base), **kw) == lla.LLA_ERR_INVALID_ARG
 
 
-def test_low_bit_support_matrix():
-    q8 = dict(dtype=lla.LLA_BF16_Q8, n_max=100)
+@pytest.mark.parametrize("low", ["LLA_BF16_Q8", "LLA_BF16_I8"])
+def test_low_bit_support_matrix(low):
+    q8 = dict(dtype=getattr(lla, low), n_max=100)
     assert encode(desc(r_k=24, r_v=24, **q8)) == lla.LLA_ERR_UNSUPPORTED
     assert decode(desc(r_k=64, r_v=64, **q8)) == lla.LLA_ERR_UNSUPPORTED
     assert gather(desc(r_k=96, r_v=160, **q8)) == lla.LLA_ERR_UNSUPPORTED
     assert prefill(desc(r_k=128, r_v=128, **q8)) == lla.LLA_ERR_UNSUPPORTED
     assert decode(desc(variant=lla.LLA_2D, r_k=256, r_v=256, **q8)) == lla.LLA_ERR_UNSUPPORTED
     # same split plan and workspace as bf16 storage on the streaming path
-    assert lla.lla_workspace_bytes(desc(r_k=32, r_v=32, dtype=lla.LLA_BF16_Q8), 32, 1) == \
+    assert lla.lla_workspace_bytes(desc(r_k=32, r_v=32, dtype=q8["dtype"]), 32, 1) == \
         lla.lla_workspace_bytes(desc(r_k=32, r_v=32), 32, 1)
+    assert lla.lla_workspace_bytes(desc(r_k=24, r_v=24, dtype=q8["dtype"]), 2, 1) > 0  # compiled
+    # an unknown dtype is an invalid descriptor
+    assert decode(desc(r_k=24, r_v=24, dtype=4, n_max=100)) == lla.LLA_ERR_INVALID_ARG
 
 
 def reconstruct(d, B=2, t=0, ws=N, wsb=0, **kw):

@@ -1,9 +1,10 @@
-"""GPU parity of low-bit latent rows (LLA_BF16_Q8) against the oracle.
+"""GPU parity of low-bit latent rows (LLA_BF16_Q8: E4M3 codes; LLA_BF16_I8: int8 codes) against
+the oracle.
 
 The quantiser must be bit-exact: the codes and the float32 scale of every row equal the oracle's
-quantize_latent_rows of the same bf16 rows (both sides divide in float32 and round to nearest even).
-The reads (decode, gather decode, prefill on the streaming kernels) are compared with the oracle's
-attention over the dequantised rows, to the bf16 tolerance.
+quantize_latent_rows / quantize_latent_rows_int8 of the same bf16 rows (both sides divide in
+float32 and round to nearest even). The reads (decode, gather decode, prefill on the streaming
+kernels) are compared with the oracle's attention over the dequantised rows, to the bf16 tolerance.
 """
 import numpy as np
 import pytest
@@ -25,15 +26,24 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def q8_desc(variant, H, d, T, rk, rv, n_max):
+# low-bit format -> (descriptor dtype, oracle quantiser, code bytes -> values)
+FORMATS = {
+    "e4m3": (lla.LLA_BF16_Q8, O.quantize_latent_rows,
+             lambda b: torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64).numpy()),
+    "int8": (lla.LLA_BF16_I8, O.quantize_latent_rows_int8,
+             lambda b: b.view(np.int8).astype(np.float64)),
+}
+
+
+def q8_desc(variant, H, d, T, rk, rv, n_max, fmt="e4m3"):
     return lla.make_desc(lla.LLA_PER_HEAD if variant == "per_head" else lla.LLA_2D,
-                         lla.LLA_BF16_Q8, H, d, T, rk, rv, n_max)
+                         FORMATS[fmt][0], H, d, T, rk, rv, n_max)
 
 
-def unpack_rows(raw, r):
+def unpack_rows(raw, r, fmt="e4m3"):
     """uint8 rows [..., row_bytes] -> (code values [..., r] float64, scales [...] float64, padding)."""
     raw = np.ascontiguousarray(raw)
-    codes = torch.from_numpy(raw[..., :r].copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    codes = FORMATS[fmt][2](raw[..., :r].copy())
     scales = raw[..., -4:].copy().view(np.float32)[..., 0].astype(np.float64)
     return codes, scales, raw[..., r:-4]
 
@@ -46,12 +56,13 @@ def cache_rows(shape_src, n_max, rng, variant):
     return z
 
 
+@pytest.mark.parametrize("fmt", sorted(FORMATS))
 @pytest.mark.parametrize("variant", ["per_head", "2d"])
 @pytest.mark.parametrize("r", [8, 13, 24, 32, 96, 256])
-def test_quantize_bit_exact(variant, r):
+def test_quantize_bit_exact(variant, r, fmt):
     rng = np.random.default_rng(9400 + r)
     B, H, C, n_max = 3, 2, 5, 9
-    desc = q8_desc(variant, H, 16, 2, r, r, n_max)
+    desc = q8_desc(variant, H, 16, 2, r, r, n_max, fmt)
     src = (B, H, C, r) if variant == "per_head" else (B, C, r)
     zk = cache_rows(src, n_max, rng, variant)
     zv = cache_rows(src, n_max, rng, variant)
@@ -64,7 +75,7 @@ def test_quantize_bit_exact(variant, r):
     torch.cuda.synchronize()
     for z, cache in ((zk, ck), (zv, cv)):
         raw = cache.cpu().numpy()
-        want_codes, want_s = O.quantize_latent_rows(z)
+        want_codes, want_s = FORMATS[fmt][1](z)
         for b in range(B):
             for c in range(C):
                 slot = pos[b] + c
@@ -72,7 +83,7 @@ def test_quantize_bit_exact(variant, r):
                 if slot >= n_max:
                     continue
                 sel = (b, slice(None), slot) if variant == "per_head" else (b, slot)
-                codes, s, pad = unpack_rows(raw[sel], r)
+                codes, s, pad = unpack_rows(raw[sel], r, fmt)
                 np.testing.assert_array_equal(codes, want_codes[sel_src])
                 np.testing.assert_array_equal(s, want_s[sel_src])
                 assert np.all(pad == 0)
@@ -89,10 +100,10 @@ def test_quantize_bit_exact(variant, r):
                     assert np.all(raw[sel] == 0xAB)
 
 
-def _q8_case(variant, B, H, d, T, r, n_max, sd, gain=1.0):
+def _q8_case(variant, B, H, d, T, r, n_max, sd, gain=1.0, fmt="e4m3"):
     """bf16 case, its low-bit cache built on the device, and the oracle's dequantised rows."""
     c = synth.random_case(variant, "bf16", B, H, d, T, r, r, n_max, sd, q_gain=gain)
-    desc = q8_desc(variant, H, d, T, r, r, n_max)
+    desc = q8_desc(variant, H, d, T, r, r, n_max, fmt)
     rb = lla.lla_latent_row_bytes(lla.LLA_BF16_Q8, r)
     cshape = (B, H, n_max, rb) if variant == "per_head" else (B, n_max, rb)
     ck = torch.empty(cshape, dtype=torch.uint8, device="cuda")
@@ -101,20 +112,21 @@ def _q8_case(variant, B, H, d, T, r, n_max, sd, gain=1.0):
     lla.lla_quantize_latents(desc, B, n_max, dev(c["zk"], "bf16"), dev(c["zv"], "bf16"),
                              dev(np.zeros(B, np.int32)), ck, cv)
     c["_ck"], c["_cv"] = ck, cv
-    c["zk_dq"] = O.dequantize_latent_rows(*O.quantize_latent_rows(c["zk"]))
-    c["zv_dq"] = O.dequantize_latent_rows(*O.quantize_latent_rows(c["zv"]))
+    c["zk_dq"] = O.dequantize_latent_rows(*FORMATS[fmt][1](c["zk"]))
+    c["zv_dq"] = O.dequantize_latent_rows(*FORMATS[fmt][1](c["zv"]))
     for k in ("Wk", "Wv", "mu_k", "mu_v"):
         c["_" + k] = dev(c[k], "bf16")
     return c, desc
 
 
+@pytest.mark.parametrize("fmt", sorted(FORMATS))
 @pytest.mark.parametrize("variant,r", [("per_head", 8), ("per_head", 16), ("per_head", 24),
                                        ("per_head", 32), ("2d", 24), ("2d", 32)])
-def test_decode_q8(variant, r):
+def test_decode_q8(variant, r, fmt):
     B, H, d, T, n_max = 3, 2, 64, 2, 1301
     lens = np.array([1301, 517, 0], np.int32)
     for gain, mu, self_token in ((1.0, True, True), (8.0, False, True), (1.0, True, False)):
-        c, desc = _q8_case(variant, B, H, d, T, r, n_max, 9500 + r, gain)
+        c, desc = _q8_case(variant, B, H, d, T, r, n_max, 9500 + r, gain, fmt)
         assert lla.lla_workspace_bytes(desc, B) > 0  # split-K plus the combine
         for t in range(T):
             q = dev(c["q"][t], "bf16")
@@ -130,14 +142,15 @@ def test_decode_q8(variant, r):
                                      c["mu_k"] if mu else None, c["mu_v"] if mu else None,
                                      c["k_self"][t] if self_token else None,
                                      c["v_self"][t] if self_token else None, variant=variant)
-            what = f"q8 {variant} r={r} gain={gain} mu={mu} self={self_token} t={t}"
+            what = f"{fmt} {variant} r={r} gain={gain} mu={mu} self={self_token} t={t}"
             assert_close(host(out), ro, "bf16", what)
             assert_lse(host(lse), rl, what)
 
 
-def test_gather_and_prefill_q8():
+@pytest.mark.parametrize("fmt", sorted(FORMATS))
+def test_gather_and_prefill_q8(fmt):
     B, H, d, T, n_max, r = 2, 2, 64, 2, 700, 24
-    c, desc = _q8_case("per_head", B, H, d, T, r, n_max, 9600)
+    c, desc = _q8_case("per_head", B, H, d, T, r, n_max, 9600, fmt=fmt)
     slots = synth.random_slots(B, 400, n_max, 9601, p_skip=0.05, p_repeat=0.05)
     counts = np.array([400, 211], np.int32)
     q = dev(c["q"][1], "bf16")
@@ -164,20 +177,21 @@ def test_gather_and_prefill_q8():
     assert_close(host(outp), rp, "bf16", "q8 prefill")
 
 
-def test_capacity_q8_full_size_sampled():
+@pytest.mark.parametrize("fmt", sorted(FORMATS))
+def test_capacity_q8_full_size_sampled(fmt):
     """Capacity shape (B=768, H=16, d=128, T=4, r=24, N=4096) with low-bit rows quantised on the
     device from the bf16 cache, at the benchmark's launch shape; sampled rows, all loops."""
     s = synth.CASES["capacity"]
     g = _fill_device_case(s)
-    desc = q8_desc("per_head", s.H, s.d, s.T, s.r_k, s.r_v, s.n_max)
+    desc = q8_desc("per_head", s.H, s.d, s.T, s.r_k, s.r_v, s.n_max, fmt)
     rb = lla.lla_latent_row_bytes(lla.LLA_BF16_Q8, s.r_k)
     ck = torch.empty(s.B, s.H, s.n_max, rb, dtype=torch.uint8, device="cuda")
     cv = torch.empty_like(ck)
     lla.lla_quantize_latents(desc, s.B, s.n_max, g["zk"], g["zv"],
                              torch.zeros(s.B, dtype=torch.int32, device="cuda"), ck, cv)
     rows = sorted({0, 383, 767, *np.random.default_rng(synth.seed(s.case, synth.SEED_SAMPLE)).choice(768, 3, replace=False).tolist()})
-    zk_dq = O.dequantize_latent_rows(*O.quantize_latent_rows(host(g["zk"][rows]).astype(np.float32)))
-    zv_dq = O.dequantize_latent_rows(*O.quantize_latent_rows(host(g["zv"][rows]).astype(np.float32)))
+    zk_dq = O.dequantize_latent_rows(*FORMATS[fmt][1](host(g["zk"][rows]).astype(np.float32)))
+    zv_dq = O.dequantize_latent_rows(*FORMATS[fmt][1](host(g["zv"][rows]).astype(np.float32)))
     del g["zk"], g["zv"]
     torch.cuda.empty_cache()
     lens = np.full(s.B, s.N, np.int32)
@@ -193,5 +207,5 @@ def test_capacity_q8_full_size_sampled():
         ro, rl = O.attend_decode_absorbed(g["q"][t][rows], zk_dq, zv_dq, g["Wk"], g["Wv"], t,
                                           lens[rows], None, None, g["k_self"][t][rows],
                                           g["v_self"][t][rows])
-        assert_close(host(out)[rows], ro, "bf16", f"capacity q8 t={t}")
-        assert_lse(host(lse)[rows], rl, f"capacity q8 t={t}")
+        assert_close(host(out)[rows], ro, "bf16", f"capacity {fmt} t={t}")
+        assert_lse(host(lse)[rows], rl, f"capacity {fmt} t={t}")
