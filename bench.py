@@ -488,7 +488,8 @@ def rope_decode(args):
     """The decoupled rotary branch (d_rope=64, one rotary key per token shared by heads and loops)
     on two decode reads, each beside the same read without the branch: the capacity layer (per
     head, B=768, H=16, d=128, r=24/24, 4096 cached tokens; rotary score pre-pass + streaming read)
-    and the LLA-2D layer (B=128, H=16, d=128, r=256/256, 8192 cached tokens; pre-pass + MFMA read)."""
+    and the LLA-2D layer (B=128, H=16, d=128, r=256/256, 8192 cached tokens; the rotary keys are
+    extra MFMA k-steps of the read)."""
     import torch
     from decode_attention_lla_amd import lla, synth
     d_rope = 64
@@ -528,7 +529,9 @@ def rope_decode(args):
         ms_p = _timed(plain, 20, 3)
         ms_r = _timed(with_rope, 20, 3)
         latent = B * (1 if two_d else H) * N * 2 * r * 2
-        extra = B * N * d_rope * 2 + 2 * B * H * N * 4  # rotary keys once + scores written and read
+        # rotary keys once; the streaming read also writes and reads every head's rotary scores
+        # (the LLA-2D MFMA read forms them in its own accumulators)
+        extra = B * N * d_rope * 2 + (0 if two_d else 2 * B * H * N * 4)
         name = "lla2d" if two_d else "capacity"
         res[name] = {
             "workload": f"{'LLA-2D' if two_d else 'capacity'} layer read with a {d_rope}-wide rotary "

@@ -675,17 +675,27 @@ int rope_sr_stride(int n_max) { return (n_max + 3) / 4 * 4; }
 size_t rope_workspace_bytes(const lla_desc& desc, int B) {
   int s, c;
   decode_plan(desc, B, &s, &c);
-  const size_t tail = decode_uses_mfma2d(desc) ? decode2d_workspace_bytes(desc, B, s)
-                                               : valu_workspace_bytes(desc, B, s);
+  // LLA-2D on MFMA: the branch is fused into the read (q~ rows widened by up to 128 entries)
+  if (decode_uses_mfma2d(desc)) return decode2d_workspace_bytes(desc, B, s, 128);
+  // streaming read: the rotary scores of every (row, head, slot) and of the self token first
   return align256(static_cast<size_t>(B) * desc.H * rope_sr_stride(desc.n_max) * 4) +
-         align256(static_cast<size_t>(B) * desc.H * 4) + tail;
+         align256(static_cast<size_t>(B) * desc.H * 4) + valu_workspace_bytes(desc, B, s);
 }
 
 hipError_t launch_decode_rope(const DecodeParams& p, const RopeScoreParams& rp0, int dtype,
                               hipStream_t stream) {
   const bool mfma2d = p.variant == LLA_2D && decode2d_mfma_supported(dtype, p.r_k, p.r_v, p.d);
+  if (mfma2d) {  // rotary keys as extra MFMA k-steps of the read: no score pre-pass
+    DecodeParams q = p;
+    q.q_rope = rp0.q_rope;
+    q.k_rope = rp0.k_rope;
+    q.k_rope_self = rp0.k_rope_self;
+    q.d_rope = rp0.d_r;
+    q.rope_base = rp0.base;
+    return launch_decode2d(q, stream);
+  }
   const Entry* e = find(dtype, p.r_k, p.r_v);
-  if (!mfma2d && (e == nullptr || e->rfn == nullptr)) return hipErrorNotSupported;
+  if (e == nullptr || e->rfn == nullptr) return hipErrorNotSupported;
   const int stride = rope_sr_stride(p.n_max);
   const size_t a = align256(static_cast<size_t>(p.B) * p.H * stride * 4);
   const size_t b = align256(static_cast<size_t>(p.B) * p.H * 4);
@@ -703,7 +713,6 @@ hipError_t launch_decode_rope(const DecodeParams& p, const RopeScoreParams& rp0,
   q.sr_stride = stride;
   q.ws = reinterpret_cast<float*>(base + a + b);
   q.ws_bytes = p.ws_bytes - a - b;
-  if (mfma2d) return launch_decode2d(q, stream);  // rotary scores added on the MFMA path
   return launch_valu(q, dtype, e->rfn, stream);
 }
 

@@ -21,6 +21,11 @@
 //   3. combine2d_kernel: per (sequence, head); merges the split partials by log-sum-exp, adds the
 //      optional self token, projects once through W^V_t[h], adds mu^V_t, normalises, writes o
 //      and lse.
+// Decoupled rotary branch (DR = d_rope > 0, Section 7): the rotary query rotated at the decoding
+// position joins q~ as DR more contraction entries, and the tile's cached rotary keys (already
+// rotated at their slots) join its K rows as DR/32 more MFMA k-steps, so the rotary scores are
+// formed in the same accumulators; the self token's rotary score is q_rope . k_rope_self (rotating
+// both at the same position leaves their dot product unchanged).
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -77,8 +82,10 @@ __device__ __forceinline__ int seq_keys(const DecodeParams& p, int b) {
 // ---- 1. query absorption for every (b, h) ------------------------------------------------------
 // grid (H, ceil(B / kQB)), 256 threads. W^K_t[h] (d x RK bf16) is staged in LDS with one round of
 // 16-byte loads; thread k then forms q~[b][h][k] for kQB sequences from LDS.
-template <int RK>
+// qt rows hold RK + DR floats: q~, then the rotated rotary query (both times scale * log2 e).
+template <int RK, int DR>
 __global__ __launch_bounds__(256) void qproj2d_kernel(DecodeParams p, float* qt, float* beta) {
+  constexpr int QS = RK + DR;
   __shared__ float q_s[kQB][128];
   __shared__ __attribute__((aligned(16))) uint16_t w_s[128 * RK];
   const int h = blockIdx.x;
@@ -114,7 +121,25 @@ __global__ __launch_bounds__(256) void qproj2d_kernel(DecodeParams p, float* qt,
     }
 #pragma unroll
     for (int bb = 0; bb < kQB; ++bb)
-      if (b0 + bb < p.B) qt[(static_cast<size_t>(b0 + bb) * p.H + h) * RK + k] = acc[bb] * p.scale_log2;
+      if (b0 + bb < p.B) qt[(static_cast<size_t>(b0 + bb) * p.H + h) * QS + k] = acc[bb] * p.scale_log2;
+  }
+  if constexpr (DR > 0) {
+    // rotary query of each sequence rotated at its decoding position N_b (the sequence differs
+    // across the threads here, so its length is read per thread)
+    for (int i = tid; i < kQB * (DR / 2); i += 256) {
+      const int bb = i / (DR / 2);
+      const int pr = i - bb * (DR / 2);
+      const int b = b0 + bb;
+      if (b >= p.B) continue;
+      int n = p.seq_lens != nullptr ? p.seq_lens[b] : p.n_max;
+      n = min(max(n, 0), p.n_max);
+      const size_t row = static_cast<size_t>(b) * p.H + h;
+      float y0, y1;
+      rotate_pair(ld<BF16>(p.q_rope, row * DR + 2 * pr), ld<BF16>(p.q_rope, row * DR + 2 * pr + 1), pr, DR,
+                  n, p.rope_base, &y0, &y1);
+      qt[row * QS + RK + 2 * pr] = y0 * p.scale_log2;
+      qt[row * QS + RK + 2 * pr + 1] = y1 * p.scale_log2;
+    }
   }
   // beta = scale*log2e * q . mu^K_t (2D mu is [T*H*d], loop t head h at (t*H + h)*d)
   const int wave = tid >> 6;
@@ -149,22 +174,23 @@ struct Cfg2d {
   static_assert(kRing >= 4 * kPart, "the final merge reuses the V rings");
 };
 
-// R: add each (token, head)'s precomputed base-2 rotary score p.sr (decoupled RoPE branch); a
-// lane's four tokens of one head are one aligned 16-byte load (rows padded to 4 tokens), issued
-// with the tile's other loads.
-template <int RK, int RV, bool R = false>
+// DR: width of the fused rotary branch (0 without): DR / 32 more k-steps whose A fragments are the
+// tile's rotary key rows, loaded with its K rows.
+template <int RK, int RV, int DR = 0>
 __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, const float* qt,
                                                                const float* beta, float* part) {
   using CF = Cfg2d<RK, RV>;
   constexpr int kW = CF::kW;
   constexpr int KS = RK / 32;
+  constexpr int KT = KS + DR / 32;     // k-steps: the latent, then the rotary branch
+  constexpr int QS = RK + DR;          // q~ row (qproj2d_kernel's layout)
   constexpr int RT = RV / 16;
   constexpr int CPR = RV / 8;          // 16-byte chunks per V row
   constexpr int VPL = CPR / 4;         // chunks per lane for a 16-row tile (16*CPR / 64)
-  static_assert(RK % 32 == 0 && RV % 64 == 0, "r_k multiple of 32, r_v multiple of 64");
+  static_assert(RK % 32 == 0 && RV % 64 == 0 && DR % 32 == 0, "r_k, d_rope multiples of 32, r_v of 64");
 
-  __shared__ __attribute__((aligned(16))) uint16_t qhi[16 * RK];
-  __shared__ __attribute__((aligned(16))) uint16_t qlo[16 * RK];
+  __shared__ __attribute__((aligned(16))) uint16_t qhi[16 * QS];
+  __shared__ __attribute__((aligned(16))) uint16_t qlo[16 * QS];
   __shared__ float beta_s[16];
   __shared__ __attribute__((aligned(16))) char ring[CF::kRing];
 
@@ -183,10 +209,10 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
   const int tb = split * p.chunk;
   const int te = min(nb, tb + p.chunk);
 
-  for (int i = tid; i < 16 * RK; i += 64 * kW) {
-    const int hh = i / RK;
-    const int k = i - hh * RK;
-    const float v = (h0 + hh < p.H) ? qt[(static_cast<size_t>(b) * p.H + h0 + hh) * RK + k] : 0.f;
+  for (int i = tid; i < 16 * QS; i += 64 * kW) {
+    const int hh = i / QS;
+    const int k = i - hh * QS;
+    const float v = (h0 + hh < p.H) ? qt[(static_cast<size_t>(b) * p.H + h0 + hh) * QS + k] : 0.f;
     const uint16_t hi = f32_to_bf16(v);
     qhi[i] = hi;
     qlo[i] = f32_to_bf16(v - __uint_as_float(static_cast<uint32_t>(hi) << 16));
@@ -199,13 +225,11 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
   const char* zvb = static_cast<const char*>(p.zv) + static_cast<size_t>(b) * p.n_max * RV * 2;
   char* myring = ring + wave * 2 * CF::kVTile;
 
-  constexpr int NR = R ? 1 : 0;  // rotary score loads per tile and lane
-  const float* srow = R ? p.sr + (static_cast<size_t>(b) * p.H + (hvalid ? h : 0)) * p.sr_stride : nullptr;
-  // issue the loads of the tile starting at tok0 (tok0 < te): rotary scores into srt, V into ring
-  // half `buf`, K into kr
-  auto issue = [&](int tok0, int buf, uint4 (&kr)[KS], float4& srt) {
+  const char* krb = DR > 0 ? static_cast<const char*>(p.k_rope) + static_cast<size_t>(b) * p.n_max * DR * 2 : nullptr;
+  // issue the loads of the tile starting at tok0 (tok0 < te): V into ring half `buf`, K and the
+  // rotary keys into kr
+  auto issue = [&](int tok0, int buf, uint4 (&kr)[KT]) {
     const int last = te - 1;
-    if constexpr (R) srt = *reinterpret_cast<const float4*>(srow + min(tok0 + 4 * g, p.sr_stride - 4));
     char* dst = myring + buf * CF::kVTile;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
@@ -220,6 +244,12 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
     const char* arow = zkb + static_cast<size_t>(min(tok0 + col, last)) * RK * 2;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kr[ks] = *reinterpret_cast<const uint4*>(arow + (32 * ks + 8 * g) * 2);
+    if constexpr (DR > 0) {
+      const char* rrow = krb + static_cast<size_t>(min(tok0 + col, last)) * DR * 2;
+#pragma unroll
+      for (int ks = 0; ks < DR / 32; ++ks)
+        kr[KS + ks] = *reinterpret_cast<const uint4*>(rrow + (32 * ks + 8 * g) * 2);
+    }
   };
 
   floatx4_t D[RT];
@@ -228,24 +258,22 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
   float m = kNegInf;
   float l = 0.f;
 
-  uint4 kc[KS];
-  float4 src = make_float4(0.f, 0.f, 0.f, 0.f);
+  uint4 kc[KT];
   int tok0 = tb + wave * 16;
   int buf = 0;
-  if (tok0 < te) issue(tok0, 0, kc, src);
+  if (tok0 < te) issue(tok0, 0, kc);
   for (; tok0 < te; tok0 += 16 * kW) {
-    uint4 kn[KS];
-    float4 srn = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint4 kn[KT];
     const bool more = tok0 + 16 * kW < te;
-    if (more) issue(tok0 + 16 * kW, buf ^ 1, kn, srn);
+    if (more) issue(tok0 + 16 * kW, buf ^ 1, kn);
     // scores S^T[token tok0 + i][head h0 + j]: hi and lo parts of q~ in two independent chains
     __asm__ volatile("" ::: "memory");
     floatx4_t sh = {0.f, 0.f, 0.f, 0.f};
     floatx4_t sl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 bh = *reinterpret_cast<const uint4*>(&qhi[col * RK + 32 * ks + 8 * g]);
-      const uint4 bl = *reinterpret_cast<const uint4*>(&qlo[col * RK + 32 * ks + 8 * g]);
+    for (int ks = 0; ks < KT; ++ks) {
+      const uint4 bh = *reinterpret_cast<const uint4*>(&qhi[col * QS + 32 * ks + 8 * g]);
+      const uint4 bl = *reinterpret_cast<const uint4*>(&qlo[col * QS + 32 * ks + 8 * g]);
       const bf16x8_t av = __builtin_bit_cast(bf16x8_t, kc[ks]);
       sh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bh), sh, 0, 0, 0);
       sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bl), sl, 0, 0, 0);
@@ -255,9 +283,7 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool ok = hvalid && (tok0 + 4 * g + e) < te;
-      float srv = 0.f;
-      if constexpr (R) srv = e == 0 ? src.x : e == 1 ? src.y : e == 2 ? src.z : src.w;
-      sc[e] = ok ? (sh[e] + sl[e]) + bt + srv : kNegInf;
+      sc[e] = ok ? (sh[e] + sl[e]) + bt : kNegInf;
       tmax = fmaxf(tmax, sc[e]);
     }
     tmax = max_over_groups(tmax);
@@ -277,8 +303,7 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
     }
     // this tile's V must have landed in LDS: at most the next tile's loads may be outstanding
     if (more)
-      __builtin_amdgcn_s_waitcnt((KS + VPL + NR) >= 16 ? 0x4f70 | (((KS + VPL + NR) - 16) & 15)
-                                                       : 0x0f70 | (KS + VPL + NR));
+      __builtin_amdgcn_s_waitcnt((KT + VPL) >= 16 ? 0x4f70 | (((KT + VPL) - 16) & 15) : 0x0f70 | (KT + VPL));
     else
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __asm__ volatile("" ::: "memory");
@@ -290,8 +315,7 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
     // the ring half just read is refilled two tiles from now; finish the reads first
     wave_lds_sync();
 #pragma unroll
-    for (int i = 0; i < KS; ++i) kc[i] = kn[i];
-    src = srn;
+    for (int i = 0; i < KT; ++i) kc[i] = kn[i];
     buf ^= 1;
   }
   l = sum_over_groups(l);
@@ -406,11 +430,13 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
     }
     if (p.k_self != nullptr)
       for (int jj = lane; jj < p.d; jj += 64) pt += ld<BF16>(p.q, bh * p.d + jj) * ld<BF16>(p.k_self, bh * p.d + jj);
+    if (p.k_self != nullptr && p.d_rope > 0)  // the self key's rotary part (same position as q)
+      for (int jj = lane; jj < p.d_rope; jj += 64)
+        pt += ld<BF16>(p.q_rope, bh * p.d_rope + jj) * ld<BF16>(p.k_rope_self, static_cast<size_t>(b) * p.d_rope + jj);
     const float M = wave_max(ms);
     const float fs = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
     const float l = wave_sum(fs * ls);
-    float s_self = p.k_self != nullptr ? wave_sum(pt) * p.scale_log2 : kNegInf;
-    if (p.k_self != nullptr && p.sr_self != nullptr) s_self += p.sr_self[bh];  // rotary part
+    const float s_self = p.k_self != nullptr ? wave_sum(pt) * p.scale_log2 : kNegInf;
     f_s[bb][lane] = fs;
     const float M2 = fmaxf(M, s_self);
     const float f_lat = (M == kNegInf) ? 0.f : fast_exp2(M - M2);
@@ -467,18 +493,29 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
   }
 }
 
+// Rotary branch widths of the fused read, index 0 = none.
+constexpr int kRopeWidths[4] = {0, 32, 64, 128};
+
 struct Entry2d {
   int r_k, r_v;
-  void (*qproj)(DecodeParams, float*, float*);
-  void (*partial)(DecodeParams, const float*, const float*, float*);
+  void (*qproj[4])(DecodeParams, float*, float*);                     // by kRopeWidths
+  void (*partial[4])(DecodeParams, const float*, const float*, float*);
   void (*combine)(DecodeParams, const float*);
-  void (*partial_r)(DecodeParams, const float*, const float*, float*);  // with rotary scores
 };
 
 template <int RK, int RV>
 constexpr Entry2d entry2d() {
-  return {RK, RV, qproj2d_kernel<RK>, decode2d_partial_kernel<RK, RV>, combine2d_kernel<RV>,
-          decode2d_partial_kernel<RK, RV, true>};
+  return {RK, RV,
+          {qproj2d_kernel<RK, 0>, qproj2d_kernel<RK, 32>, qproj2d_kernel<RK, 64>, qproj2d_kernel<RK, 128>},
+          {decode2d_partial_kernel<RK, RV, 0>, decode2d_partial_kernel<RK, RV, 32>,
+           decode2d_partial_kernel<RK, RV, 64>, decode2d_partial_kernel<RK, RV, 128>},
+          combine2d_kernel<RV>};
+}
+
+int rope_index(int d_rope) {
+  for (int i = 0; i < 4; ++i)
+    if (kRopeWidths[i] == d_rope) return i;
+  return -1;
 }
 
 const Entry2d kTable2d[] = {
@@ -516,32 +553,34 @@ void decode2d_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
   *chunk = c;
 }
 
-size_t decode2d_workspace_bytes(const lla_desc& desc, int B, int splits) {
+size_t decode2d_workspace_bytes(const lla_desc& desc, int B, int splits, int d_rope) {
   const size_t bh = static_cast<size_t>(B) * desc.H;
-  return align256(bh * desc.r_k * 4) + align256(bh * 4) + bh * splits * (2 + desc.r_v) * 4;
+  return align256(bh * (desc.r_k + d_rope) * 4) + align256(bh * 4) + bh * splits * (2 + desc.r_v) * 4;
 }
 
-hipError_t launch_decode2d(const DecodeParams& p0, hipStream_t stream) {
-  const Entry2d* e = find2d(p0.r_k, p0.r_v);
-  if (e == nullptr || p0.d > 128) return hipErrorNotSupported;
-  const DecodeParams& p = p0;  // splits and chunk were planned by the caller with decode2d_plan
+hipError_t launch_decode2d(const DecodeParams& p, hipStream_t stream) {
+  const Entry2d* e = find2d(p.r_k, p.r_v);
+  const int ri = rope_index(p.d_rope);
+  if (e == nullptr || p.d > 128 || ri < 0) return hipErrorNotSupported;
+  // splits and chunk were planned by the caller with decode2d_plan
   lla_desc d{};
   d.H = p.H;
   d.r_k = p.r_k;
   d.r_v = p.r_v;
-  if (p.splits < 1 || p.splits > 64 || decode2d_workspace_bytes(d, p.B, p.splits) > p.ws_bytes)
+  if (p.splits < 1 || p.splits > 64 || decode2d_workspace_bytes(d, p.B, p.splits, p.d_rope) > p.ws_bytes)
     return hipErrorInvalidValue;  // the plan does not fit the workspace: never launch
   const size_t bh = static_cast<size_t>(p.B) * p.H;
   char* ws = reinterpret_cast<char*>(p.ws);
+  const size_t qt_bytes = align256(bh * (p.r_k + p.d_rope) * 4);
   float* qt = reinterpret_cast<float*>(ws);
-  float* beta = reinterpret_cast<float*>(ws + align256(bh * p.r_k * 4));
-  float* part = reinterpret_cast<float*>(ws + align256(bh * p.r_k * 4) + align256(bh * 4));
+  float* beta = reinterpret_cast<float*>(ws + qt_bytes);
+  float* part = reinterpret_cast<float*>(ws + qt_bytes + align256(bh * 4));
   const unsigned qb = (p.B + kQB - 1) / kQB;
-  hipLaunchKernelGGL(e->qproj, dim3(p.H, qb), dim3(256), 0, stream, p, qt, beta);
+  hipLaunchKernelGGL(e->qproj[ri], dim3(p.H, qb), dim3(256), 0, stream, p, qt, beta);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(p.sr != nullptr ? e->partial_r : e->partial, dim3(p.splits, p.B, (p.H + 15) / 16),
-                     dim3(64 * Cfg2d<64, 64>::kW), 0, stream, p, qt, beta, part);
+  hipLaunchKernelGGL(e->partial[ri], dim3(p.splits, p.B, (p.H + 15) / 16), dim3(64 * Cfg2d<64, 64>::kW), 0,
+                     stream, p, qt, beta, part);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(e->combine, dim3(p.H, qb), dim3(256), 0, stream, p, part);

@@ -189,6 +189,16 @@ __device__ __forceinline__ float sum_over_groups(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Rotate the pair (x0, x1) of channel pair i at position pos (float64 angle and trigonometry).
+__device__ __forceinline__ void rotate_pair(float x0, float x1, int i, int d, double pos,
+                                            double base, float* y0, float* y1) {
+  const double theta = pow(base, -2.0 * i / d);
+  double s, c;
+  sincos(pos * theta, &s, &c);
+  *y0 = static_cast<float>(x0 * c - x1 * s);
+  *y1 = static_cast<float>(x0 * s + x1 * c);
+}
+
 // Sum over aligned groups of N lanes (N a power of two, 1..64), VALU only: a butterfly whose
 // partner steps are DPP quad permutes (lane ^ 1, lane ^ 2), the half-row and row mirrors (which
 // pair each 4- and 8-lane group with its neighbour) and the two lane swaps. Every step adds two

@@ -43,6 +43,14 @@ struct DecodeParams {
   // null); a slot outside [0, n_max) is skipped. slots == nullptr: the contiguous read above.
   const int32_t* slots;
   int32_t budget;
+  // Rotary branch fused into the LLA-2D MFMA read (lla_attend_decode_rope; d_rope == 0 without):
+  // q_rope [rows][H][d_rope] unrotated, k_rope [B][n_max][d_rope] rotated at each slot,
+  // k_rope_self [B][d_rope] or NULL, RoFormer base.
+  const void* q_rope;
+  const void* k_rope;
+  const void* k_rope_self;
+  int32_t d_rope;
+  double rope_base;
 };
 
 struct EncodeParams {
@@ -133,7 +141,8 @@ bool decode_uses_mfma2d(const lla_desc& desc);
 // LLA-2D MFMA decode (decode2d.hip).
 bool decode2d_mfma_supported(int dtype, int r_k, int r_v, int d_head);
 void decode2d_plan(const lla_desc& desc, int B, int* splits, int* chunk);
-size_t decode2d_workspace_bytes(const lla_desc& desc, int B, int splits);
+// Workspace of the LLA-2D MFMA read; d_rope > 0 for the fused rotary branch.
+size_t decode2d_workspace_bytes(const lla_desc& desc, int B, int splits, int d_rope = 0);
 hipError_t launch_decode2d(const DecodeParams& p, hipStream_t s);
 size_t prefill_workspace_bytes(const lla_desc& desc, int B, int C);
 

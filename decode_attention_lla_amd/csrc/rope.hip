@@ -25,16 +25,6 @@ __device__ __forceinline__ float bf16_at(const uint16_t* p, size_t i) {
   return __uint_as_float(uint32_t(p[i]) << 16);
 }
 
-// Rotate the pair (x0, x1) of channel pair i at position pos (float64 angle and trigonometry).
-__device__ __forceinline__ void rotate_pair(float x0, float x1, int i, int d, double pos,
-                                            double base, float* y0, float* y1) {
-  const double theta = pow(base, -2.0 * i / d);
-  double s, c;
-  sincos(pos * theta, &s, &c);
-  *y0 = static_cast<float>(x0 * c - x1 * s);
-  *y1 = static_cast<float>(x0 * s + x1 * c);
-}
-
 // k_rope[b][pos[b] + c][:] = rotate(k_in[b][c][:], pos[b] + c); one thread per channel pair.
 __global__ __launch_bounds__(256) void rope_write_kernel(RopeWriteParams p) {
   const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
