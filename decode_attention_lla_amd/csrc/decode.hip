@@ -96,6 +96,14 @@ __device__ void finish_unit(const DecodeParams& p, int b, int h, float M, float 
 // token and out; LS that of the latent rows (S itself, or Q8 low-bit rows read whole by one lane:
 // the K row scale multiplies the score, the V row scale the token's weight). With R each token's
 // score also gets its precomputed base-2 rotary score p.sr[bh][slot] (decoupled RoPE branch).
+// A lane's S-byte row slice (whole words, S <= 32) at byte offset off of a raw buffer: one load of
+// up to 16 bytes into f[0], the rest into f[1].
+template <int S, int AUX>
+__device__ __forceinline__ void load_slice(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint4* f) {
+  f[0] = buffer_words<(S < 16 ? S : 16) / 4, AUX>(rs, off);
+  if constexpr (S > 16) f[1] = buffer_words<(S - 16) / 4, AUX>(rs, off + 16);
+}
+
 template <class S, class LS, int RK, int RV, int LPT, int U, bool G, bool R = false>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   constexpr bool kQ8 = std::is_same<LS, Q8>::value || std::is_same<LS, I8>::value;  // low-bit rows
@@ -108,12 +116,14 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   constexpr int TPW = 64 / LPT;
   constexpr int SK = EK * LS::kBytes;  // bytes of a lane's slice of a K row
   constexpr int SV = EV * LS::kBytes;
-  // One load per lane and row when a slice is 4..16 whole words: the LPT lanes of a token then
-  // read its row as one run and each load instruction covers 64 / LPT consecutive whole rows,
-  // which lets the contiguous read stream past the caches (non-temporal) at full line use.
-  constexpr bool kOne = SK % 4 == 0 && SV % 4 == 0 && SK <= 16 && SV <= 16;
-  constexpr int VK = kOne ? 1 : SK / 16;
-  constexpr int VV = kOne ? 1 : SV / 16;
+  // Buffer loads of whole-word slices of at most 32 bytes (one load of up to 16 bytes, a second
+  // for the rest): the LPT lanes of a token then read its row as one run, and each load
+  // instruction covers 64 / LPT consecutive rows without gaps (one load per slice) or leaves only
+  // the second load's bytes for the next instruction; the contiguous read streams past the caches
+  // (non-temporal). Low-bit slices stay within one load.
+  constexpr bool kOne = SK % 4 == 0 && SV % 4 == 0 && SK <= 32 && SV <= 32 && (!kQ8 || (SK <= 16 && SV <= 16));
+  constexpr int VK = kOne ? (SK + 15) / 16 : SK / 16;
+  constexpr int VV = kOne ? (SV + 15) / 16 : SV / 16;
   static_assert(kQ8 ? (EK * LPT == RKB && EV * LPT == RVB) : (EK * LPT == RK && EV * LPT == RV),
                 "rows must split evenly over lanes");
   static_assert(kOne || (VK * 16 == SK && VV * 16 == SV), "16-byte fragments");
@@ -314,8 +324,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
         } else {
           rr = static_cast<uint32_t>(min(tok, te) - row0);
         }
-        kr[u][0] = buffer_words<SK / 4, kAux>(rsk, rr * RKB + sub * SK);
-        vr[u][0] = buffer_words<SV / 4, kAux>(rsv, rr * RVB + sub * SV);
+        load_slice<SK, kAux>(rsk, rr * RKB + sub * SK, kr[u]);
+        load_slice<SV, kAux>(rsv, rr * RVB + sub * SV, vr[u]);
       }
     };
     auto mask = [&](int t0, bool (&ok)[U]) {
@@ -369,8 +379,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
       for (int u = 0; u < U; ++u) {
         if constexpr (kOne) {
           const uint32_t rr = ok[u] ? static_cast<uint32_t>(slot[u] - row0) : nrows;
-          kr[u][0] = buffer_words<SK / 4, kAux>(rsk, rr * RKB + sub * SK);
-          vr[u][0] = buffer_words<SV / 4, kAux>(rsv, rr * RVB + sub * SV);
+          load_slice<SK, kAux>(rsk, rr * RKB + sub * SK, kr[u]);
+          load_slice<SV, kAux>(rsv, rr * RVB + sub * SV, vr[u]);
         } else if (ok[u]) {
           const uint4* kp = reinterpret_cast<const uint4*>(zkp + static_cast<size_t>(slot[u]) * RKB);
           const uint4* vp = reinterpret_cast<const uint4*>(zvp + static_cast<size_t>(slot[u]) * RVB);
@@ -526,8 +536,8 @@ const Entry kTable[] = {
      rope_fn<BF16, 96, 96, 16, 8>()},
     {LLA_BF16, 128, 128, partial_fn<BF16, 128, 128, 16, 8>(), gather_fn<BF16, 128, 128, 16, 8>(),
      rope_fn<BF16, 128, 128, 16, 8>()},
-    {LLA_BF16, 96, 160, partial_fn<BF16, 96, 160, 4, 2>(), gather_fn<BF16, 96, 160, 4, 2>(),
-     rope_fn<BF16, 96, 160, 4, 2>()},
+    {LLA_BF16, 96, 160, partial_fn<BF16, 96, 160, 16, 8>(), gather_fn<BF16, 96, 160, 16, 8>(),
+     rope_fn<BF16, 96, 160, 16, 8>()},
     {LLA_BF16, 256, 256, partial_fn<BF16, 256, 256, 32, 8>(), gather_fn<BF16, 256, 256, 32, 8>(),
      rope_fn<BF16, 256, 256, 32, 8>()},
     {LLA_F32, 8, 8, partial_fn<F32, 8, 8, 2, 4>(), gather_fn<F32, 8, 8, 2, 4>(), nullptr},
@@ -572,9 +582,12 @@ bool decode_uses_mfma2d(const lla_desc& desc) {
 }
 
 void valu_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
-  // Enough waves to cover 256 CUs several times over, but no split shorter than 256 tokens.
+  // Few (row, head) units are split so the launch is about 2048 waves: one round for any of these
+  // kernels (all fit 8 waves per CU), each wave keeping two batches of rows in flight. More waves
+  // than fit at once leave a last, partly filled round that streams at a fraction of the bandwidth
+  // (4096 waves at 12 per CU: 410 us for the 262k-token read). No split shorter than 256 tokens.
   const long units = static_cast<long>(B) * desc.H;
-  const int target_waves = 4096;
+  const int target_waves = 2048;
   int s = static_cast<int>((target_waves + units - 1) / units);
   const int max_by_len = desc.n_max / 256 > 0 ? desc.n_max / 256 : 1;
   if (s > max_by_len) s = max_by_len;
