@@ -221,7 +221,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   // order (a sink + window list: 248 -> 229 us at the capacity shape); a random list of 48-byte
   // rows reads ~5% slower than with ordinary loads.
   constexpr int kAux = 2;
-  constexpr bool kPipe = kOne && !G;  // contiguous one-load rows (scores broadcast below)
+  constexpr bool kPipe = kOne && !G;  // the contiguous buffer-load read (always two batches ahead)
   // Rotary scores (R). With at most 4 lanes per token the pipelined path loads them once per batch:
   // lane `sub` of a group loads tile sub + LPT*k's score (one load covers 64 consecutive tokens)
   // and each tile's score is broadcast inside the group (DPP) when the tile is consumed.

@@ -33,8 +33,9 @@ struct DecodeParams {
   int32_t chunk;      // tokens per split
   float scale_log2;   // softmax scale * log2(e)
   size_t ws_bytes;    // bytes available at ws; launchers refuse a plan that does not fit
-  // Rotary branch (lla_attend_decode_rope): base-2 rotary scores added to the latent scores,
-  // sr [rows][H][n_max] by slot and sr_self [rows][H] for the self token; NULL when absent.
+  // Rotary branch of the streaming read (lla_attend_decode_rope): base-2 rotary scores added to
+  // the latent scores, sr [rows][H][sr_stride] by slot and sr_self [rows][H] for the self token;
+  // NULL when absent (the LLA-2D MFMA read fuses the branch instead: q_rope, k_rope below).
   const float* sr;
   const float* sr_self;
   int32_t sr_stride;  // floats per (row, head) score row: n_max rounded up to a multiple of 4
