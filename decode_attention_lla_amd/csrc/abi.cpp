@@ -155,8 +155,10 @@ lla_status lla_quantize_latents(const lla_desc* desc, int32_t B, int32_t C, cons
 
 size_t lla_workspace_bytes(const lla_desc* desc, int32_t B, int32_t C) {
   if (!desc_ok(desc) || B <= 0 || C <= 0) return 0;
-  if (C == 1) return lla::decode_workspace_bytes(*desc, B);
-  return lla::prefill_workspace_bytes(*desc, B, C);
+  const size_t pre = lla::prefill_workspace_bytes(*desc, B, C);
+  if (C > 1) return pre;
+  const size_t dec = lla::decode_workspace_bytes(*desc, B);  // decode and one-row prefill
+  return dec > pre ? dec : pre;
 }
 
 lla_status lla_encode(const lla_desc* desc, int32_t B, int32_t C, const void* xk, const void* xv,

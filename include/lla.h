@@ -120,9 +120,10 @@ lla_status lla_quantize_latents(const lla_desc* desc, int32_t B, int32_t C, cons
  *   variants on the streaming kernels:                        (8,8) (16,16) (24,24) (32,32)
  * A decode or prefill call with a pair that none of these covers returns LLA_ERR_UNSUPPORTED. */
 
-/* Bytes of device workspace that lla_attend_decode (C == 1) or lla_attend_prefill (C > 1) needs
- * for this descriptor and batch. May be 0. Returns 0 as well for an invalid descriptor (the
- * call itself then reports the error). */
+/* Bytes of device workspace that lla_attend_prefill with a chunk of C rows needs for this
+ * descriptor and batch; with C == 1 the larger of that and what lla_attend_decode needs, so one
+ * size serves a decode call and a one-row prefill chunk. May be 0. Returns 0 as well for an
+ * invalid descriptor (the call itself then reports the error). */
 size_t lla_workspace_bytes(const lla_desc* desc, int32_t B, int32_t C);
 
 /* Encode C finished tokens per sequence into the latent cache (Section 3, Eq. 2, applied after

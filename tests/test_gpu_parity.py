@@ -491,3 +491,97 @@ def test_lla2d_prefill_full_size_sampled():
         assert_close(o0[:, j:j + 1], ref, "bf16", f"2d prefill row {j}")
     del g, xk, xv, q, out
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------------------------
+# randomized configurations: combinations the sweeps above do not enumerate
+# --------------------------------------------------------------------------------------------
+
+MFMA_2D_PAIRS = [(64, 64), (128, 128), (256, 256)]
+
+
+def _random_configs(n, seed=7777):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        variant = "2d" if rng.random() < 0.35 else "per_head"
+        dtype = "bf16" if rng.random() < 0.75 else "f32"
+        pool = PAIRS + (MFMA_2D_PAIRS if variant == "2d" and dtype == "bf16" else [])
+        rk, rv = pool[rng.integers(len(pool))]
+        H = int(rng.choice([1, 3, 16, 17] if variant == "2d" else [1, 2, 5]))
+        d = int(rng.choice([16, 64, 128]))
+        T = int(rng.integers(1, 4))
+        B = int(rng.integers(1, 6))
+        n_max = int(rng.choice([1, 7, 255, 256, 257, 1000, 2500]))
+        lens = [int(x) for x in rng.integers(0, n_max + 2, B)]
+        out.append(dict(i=i, variant=variant, dtype=dtype, rk=int(rk), rv=int(rv), H=H, d=d, T=T,
+                        B=B, n_max=n_max, lens=lens, mu=bool(rng.random() < 0.5),
+                        self_token=bool(rng.random() < 0.7), gain=float(rng.choice([1.0, 8.0])),
+                        t=int(rng.integers(0, T))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(24), ids=lambda c: f"cfg{c['i']}")
+def test_decode_random_configurations(cfg):
+    """Seeded random draws over variant, storage, rank pair, heads (incl. a partial 16-head group),
+    head width, loop, batch, cache size (1 .. 2500 slots), ragged and out-of-range lengths, mu, the
+    self token and sharpened queries, each against the oracle. A row with no key and no self token
+    is skipped (the entry point fills it but the oracle has no defined value)."""
+    c = cfg
+    desc = mk_desc(c["variant"], c["dtype"], c["H"], c["d"], c["T"], c["rk"], c["rv"], c["n_max"])
+    case = upload(synth.random_case(c["variant"], c["dtype"], c["B"], c["H"], c["d"], c["T"], c["rk"],
+                                    c["rv"], c["n_max"], 12000 + c["i"], with_mu=c["mu"],
+                                    q_gain=c["gain"]), c["dtype"])
+    o, lse = gpu_decode(desc, c["B"], c["t"], case, c["dtype"], c["lens"], c["self_token"], c["mu"])
+    ro, rl = oracle_decode(case, c["t"], c["lens"], c["variant"], c["self_token"], c["mu"])
+    live = [b for b in range(c["B"]) if c["self_token"] or min(max(c["lens"][b], 0), c["n_max"]) > 0]
+    if live:
+        assert_close(o[live], ro[live], c["dtype"], str(c))
+        assert_lse(lse[live], rl[live], str(c))
+
+
+PREFILL_MFMA_PAIRS = [(64, 64), (128, 128), (256, 256), (64, 128), (128, 256)]
+
+
+def _random_prefill_configs(n, seed=8888):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        variant = "2d" if rng.random() < 0.4 else "per_head"
+        dtype = "bf16" if rng.random() < 0.8 else "f32"
+        mfma = dtype == "bf16" and rng.random() < 0.6
+        pool = PREFILL_MFMA_PAIRS if mfma else [p for p in PAIRS if p[0] <= 128]
+        rk, rv = pool[rng.integers(len(pool))]
+        d = int(rng.choice([32, 64, 128] if mfma else [16, 32, 64]))
+        H = int(rng.choice([1, 2, 3]))
+        B = int(rng.choice([1, 3, 8]))
+        C = int(rng.choice([1, 15, 16, 17, 128, 129, 200]))
+        ctx = [int(x) for x in rng.integers(0, 400, B)]
+        ctx[0] = 0
+        n_max = max(ctx) + C + int(rng.integers(0, 50))
+        out.append(dict(i=i, variant=variant, dtype=dtype, rk=int(rk), rv=int(rv), H=H, d=d, T=2,
+                        B=B, C=C, ctx=ctx, n_max=n_max, mu=bool(rng.random() < 0.5),
+                        gain=float(rng.choice([1.0, 8.0])), t=int(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_prefill_configs(16), ids=lambda c: f"cfg{c['i']}")
+def test_prefill_random_configurations(cfg):
+    """Seeded random chunked-prefill draws over variant, storage, MFMA and streaming rank pairs,
+    head width, heads, batch (8 takes the XCD-grouped workgroup order), chunk length around the
+    16- and 128-row block edges, context lengths (one empty), mu and sharpened queries."""
+    c = cfg
+    desc = mk_desc(c["variant"], c["dtype"], c["H"], c["d"], c["T"], c["rk"], c["rv"], c["n_max"])
+    case = upload(synth.random_case(c["variant"], c["dtype"], c["B"], c["H"], c["d"], c["T"], c["rk"],
+                                    c["rv"], c["n_max"], 13000 + c["i"], with_mu=c["mu"]), c["dtype"])
+    q = synth.to_storage(c["gain"] * synth.normal((c["B"], c["C"], c["H"], c["d"]), 13500 + c["i"]), c["dtype"])
+    ctx = np.array(c["ctx"], np.int32)
+    out = torch.empty(c["B"], c["C"], c["H"], c["d"], dtype=dev(q, c["dtype"]).dtype, device="cuda")
+    lla.lla_attend_prefill(desc, c["B"], c["C"], c["t"], dev(q, c["dtype"]), case["_zk"], case["_zv"],
+                           dev(ctx), case["_Wk"], case["_Wv"], case["_muk"] if c["mu"] else None,
+                           case["_muv"] if c["mu"] else None, out, lla.workspace(desc, c["B"], c["C"]))
+    torch.cuda.synchronize()
+    ref = O.attend_prefill(q, case["zk"], case["zv"], case["Wk"], case["Wv"], c["t"], ctx,
+                           case["mu_k"] if c["mu"] else None, case["mu_v"] if c["mu"] else None,
+                           variant=c["variant"])
+    assert_close(host(out), ref, c["dtype"], str(c))
