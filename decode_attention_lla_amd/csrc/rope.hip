@@ -141,7 +141,9 @@ __global__ __launch_bounds__(kTokTile) void rope_scores_kernel(RopeScoreParams p
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int hh = hg + 4 * g + e;
-          if (hh < p.H) sbase[static_cast<size_t>(hh) * p.sr_stride + row] = acc[e];
+          // non-temporal: the scores are read once, by the next kernel; left dirty in the caches
+          // they cost that read ~3% more
+          if (hh < p.H) __builtin_nontemporal_store(acc[e], &sbase[static_cast<size_t>(hh) * p.sr_stride + row]);
         }
       }
     }
