@@ -96,6 +96,13 @@ lla::DecodeParams decode_params(const lla_desc* desc, int32_t B, int32_t t, cons
 }
 
 
+// Row counts the calls accept: B (times C for prefill) times H below 2^31 / 64. The workspace
+// queries return 0 beyond them (the calls themselves refuse such sizes), which also keeps every
+// product below in range.
+bool rows_ok(const lla_desc* desc, int64_t rows) {
+  return rows > 0 && rows * desc->H < (int64_t(1) << 31) / 64;
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,7 +161,7 @@ lla_status lla_quantize_latents(const lla_desc* desc, int32_t B, int32_t C, cons
 }
 
 size_t lla_workspace_bytes(const lla_desc* desc, int32_t B, int32_t C) {
-  if (!desc_ok(desc) || B <= 0 || C <= 0) return 0;
+  if (!desc_ok(desc) || B <= 0 || C <= 0 || !rows_ok(desc, static_cast<int64_t>(B) * C)) return 0;
   const size_t pre = lla::prefill_workspace_bytes(*desc, B, C);
   if (C > 1) return pre;
   const size_t dec = lla::decode_workspace_bytes(*desc, B);  // decode and one-row prefill
@@ -243,7 +250,7 @@ lla_status lla_rope_write(const lla_desc* desc, int32_t B, int32_t C, int32_t d_
 }
 
 size_t lla_rope_workspace_bytes(const lla_desc* desc, int32_t B) {
-  if (!desc_ok(desc) || B <= 0) return 0;
+  if (!desc_ok(desc) || B <= 0 || !rows_ok(desc, B)) return 0;
   return lla::rope_workspace_bytes(*desc, B);
 }
 
@@ -285,7 +292,7 @@ lla_status lla_attend_decode_rope(const lla_desc* desc, int32_t B, int32_t t, co
 }
 
 size_t lla_reconstruct_workspace_bytes(const lla_desc* desc, int32_t B) {
-  if (!desc_ok(desc) || B <= 0) return 0;
+  if (!desc_ok(desc) || B <= 0 || !rows_ok(desc, B)) return 0;
   return lla::reconstruct_workspace_bytes(*desc, B);
 }
 
@@ -309,7 +316,8 @@ lla_status lla_attend_decode_reconstruct(const lla_desc* desc, int32_t B, int32_
 }
 
 size_t lla_gather_workspace_bytes(const lla_desc* desc, int32_t B, int32_t budget) {
-  if (!desc_ok(desc) || B <= 0 || budget <= 0) return 0;
+  if (!desc_ok(desc) || B <= 0 || budget <= 0 || !rows_ok(desc, B)) return 0;
+  if (static_cast<int64_t>(B) * budget >= (int64_t(1) << 31)) return 0;  // as the call
   return lla::gather_workspace_bytes(*desc, B, budget);
 }
 
