@@ -77,4 +77,4 @@ def test_workspace_queries_refuse_what_the_calls_refuse():
     assert lib.lla_reconstruct_workspace_bytes(ctypes.byref(d), 2**21) == 0
     # just inside the limit the queries answer
     assert lla.lla_workspace_bytes(d, 2**20 - 1, 1) >= 0
-    assert lla.lla_workspace_bytes(d, 2, 64) > 0
+    assert lla.lla_workspace_bytes(d, 1, 2) > 0  # a 2-row chunk over 4097 slots splits
