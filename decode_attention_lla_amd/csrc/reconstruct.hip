@@ -9,6 +9,9 @@
 // softmax attention over explicit K/V).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <utility>
+
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -25,87 +28,117 @@ __device__ __forceinline__ floatx4_t mfma16(uint4 a, uint4 b, floatx4_t c) {
 
 constexpr int kTokWave = 32;               // tokens per wave: two 16-token MFMA blocks
 constexpr int kWaves = 4;
-constexpr int kTokWG = kTokWave * kWaves;  // tokens per workgroup
+constexpr int kTokWG = kTokWave * kWaves;  // tokens per tile
 constexpr int kMaxR = 256;
+constexpr int kTargetWG = 3072;            // about four rounds of three workgroups per CU
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-// X^T = W_t (D x r) . Z^T (r x tokens) for one (b, h) and a 128-token tile, stored as bf16 rows
-// X[token][D] (+ mu_t). A operand: rows of W_t[h] (k = latent entry), staged in LDS with rows
-// padded by 16 bytes so the 16 rows of a ds_read_b128 fall on distinct banks for every r that is
-// a multiple of 32. B operand: each lane's 16 bytes of a latent row, straight from HBM. C: lane
-// (token j, group g) holds rows 4g .. 4g+3 of X^T, i.e. 4 consecutive channels of token j.
-template <int D>
-__global__ __launch_bounds__(256) void reconstruct_kernel(ReconParams p) {
-  __shared__ __attribute__((aligned(16))) char w_s[D * (kMaxR * 2 + 16)];
-  const int r = p.r;
-  const int RS = r * 2 + 16;
+// X^T = W_t (D x R) . Z^T (R x tokens) for one (b, h), stored as bf16 rows X[token][D] (+ mu_t).
+// A workgroup stages W_t[h] in LDS once and then walks 128-token tiles (tile = blockIdx.x,
+// blockIdx.x + gridDim.x, ...), so the factor is read once per workgroup rather than per tile.
+// A operand: rows of W_t[h] (k = latent entry) from LDS, rows padded by 16 bytes so the 16 rows of
+// a ds_read_b128 fall on distinct banks (R is a multiple of 32). B operand: each lane's 16 bytes
+// of a latent row, all R/32 k-steps issued before the first product, through a buffer descriptor
+// that ends at the sequence's last token (rows past it read zeros). C: lane (token j, group g)
+// holds channels 16*db + 4g .. +3 of token j; a row swap between lane groups g and g^1 of two
+// neighbouring blocks turns that into 8 consecutive channels, one 16-byte store per lane. The rows
+// are written non-temporally: the attention reads them back only after every row is written.
+template <int D, int R>
+__global__ __launch_bounds__(256, 3) void reconstruct_kernel(ReconParams p) {
+  constexpr int KS = R / 32;
+  constexpr int RS = R * 2 + 16;
+  __shared__ __attribute__((aligned(16))) char w_s[D * RS];
   const int bh = blockIdx.y;
   const int h = bh % p.H;
   const int b = bh / p.H;
   int nb = p.seq_lens != nullptr ? uniform(p.seq_lens[b]) : p.n_max;
   nb = min(max(nb, 0), p.n_max);
-  const int tok0 = blockIdx.x * kTokWG;
-  if (tok0 >= nb) return;  // workgroup-uniform, before any barrier
+  const int ntiles = (nb + kTokWG - 1) / kTokWG;
+  if (static_cast<int>(blockIdx.x) >= ntiles) return;  // workgroup-uniform, before any barrier
 
-  const uint16_t* W = static_cast<const uint16_t*>(p.W) + (static_cast<size_t>(p.t) * p.H + h) * D * r;
-  const int cpr = r / 8;  // 16-byte chunks per W row
+  const uint16_t* W = static_cast<const uint16_t*>(p.W) + (static_cast<size_t>(p.t) * p.H + h) * D * R;
+  constexpr int cpr = R / 8;  // 16-byte chunks per W row
   for (int idx = threadIdx.x; idx < D * cpr; idx += 256) {
     const int row = idx / cpr;
     const int c = idx - row * cpr;
     *reinterpret_cast<uint4*>(w_s + row * RS + c * 16) =
-        *reinterpret_cast<const uint4*>(W + static_cast<size_t>(row) * r + c * 8);
+        *reinterpret_cast<const uint4*>(W + static_cast<size_t>(row) * R + c * 8);
   }
-  __syncthreads();
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
-  const int wtok = tok0 + wave * kTokWave;
-  const uint16_t* Z = static_cast<const uint16_t*>(p.z) + static_cast<size_t>(bh) * p.n_max * r;
-
-  floatx4_t acc[D / 16][2];
+  // per-head mu [H][T*d] at (h, t*d): this lane's channels 16*db + 4g .. +3 as bf16 pairs
+  uint2 mu_r[D / 16];
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) {
-    acc[db][0] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    acc[db][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  for (int ks = 0; ks < r / 32; ++ks) {
-    uint4 bz[2];
+  for (int db = 0; db < D / 16; ++db)
+    mu_r[db] = p.mu != nullptr
+                   ? *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.mu) +
+                                                     (static_cast<size_t>(h) * p.T + p.t) * D + 16 * db + 4 * g)
+                   : make_uint2(0u, 0u);
+  const __amdgpu_buffer_rsrc_t zr =
+      buffer_rsrc(static_cast<const uint16_t*>(p.z) + static_cast<size_t>(bh) * p.n_max * R,
+                  static_cast<uint32_t>(nb) * R * 2);
+  uint16_t* X = static_cast<uint16_t*>(p.x) + static_cast<size_t>(bh) * p.n_max * D;
+  __syncthreads();
+
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int wtok = tile * kTokWG + wave * kTokWave;
+    uint4 bz[KS][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        bz[ks][tb] = buffer_words<4, 0>(
+            zr, static_cast<uint32_t>((wtok + 16 * tb + col) * R + 32 * ks + 8 * g) * 2u);
+    floatx4_t acc[D / 16][2];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      acc[db][0] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      acc[db][1] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const uint4 a = *reinterpret_cast<const uint4*>(w_s + (16 * db + col) * RS + (32 * ks + 8 * g) * 2);
+        acc[db][0] = mfma16(a, bz[ks][0], acc[db][0]);
+        acc[db][1] = mfma16(a, bz[ks][1], acc[db][1]);
+      }
+    }
+    // issue order: every latent load, then the W fragments two ahead of the products using them
+    // (left to itself the scheduler reads all fragments first, and the registers spill)
+    __builtin_amdgcn_sched_group_barrier(0x020, 2 * KS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < KS * (D / 16) - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       const int tok = wtok + 16 * tb + col;
-      bz[tb] = tok < nb ? *reinterpret_cast<const uint4*>(Z + static_cast<size_t>(tok) * r + 32 * ks + 8 * g)
-                        : make_uint4(0, 0, 0, 0);
-    }
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      const uint4 a = *reinterpret_cast<const uint4*>(w_s + (16 * db + col) * RS + (32 * ks + 8 * g) * 2);
-      acc[db][0] = mfma16(a, bz[0], acc[db][0]);
-      acc[db][1] = mfma16(a, bz[1], acc[db][1]);
-    }
-  }
-
-  // per-head mu [H][T*d] at (h, t*d)
-  const uint16_t* mu = p.mu != nullptr
-                           ? static_cast<const uint16_t*>(p.mu) + (static_cast<size_t>(h) * p.T + p.t) * D
-                           : nullptr;
-  uint16_t* X = static_cast<uint16_t*>(p.x) + static_cast<size_t>(bh) * p.n_max * D;
+      for (int dp = 0; dp < D / 32; ++dp) {
+        uint32_t w[2][2];  // [block 2dp, 2dp+1][channel pair]
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const int tok = wtok + 16 * tb + col;
-    if (tok >= nb) continue;
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      float v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ch = 16 * db + 4 * g + e;
-        v[e] = acc[db][tb][e] + (mu != nullptr ? __uint_as_float(uint32_t(mu[ch]) << 16) : 0.f);
+        for (int k = 0; k < 2; ++k) {
+          const floatx4_t& a = acc[2 * dp + k][tb];
+          const uint2 m = mu_r[2 * dp + k];
+          w[k][0] = f32x2_to_bf16x2(a[0] + bf16_lo(m.x), a[1] + bf16_hi(m.x));
+          w[k][1] = f32x2_to_bf16x2(a[2] + bf16_lo(m.y), a[3] + bf16_hi(m.y));
+        }
+        // lane groups 1 and 3 trade their block-2dp words for groups 0 and 2's block-2dp+1 words
+        const auto s0 = __builtin_amdgcn_permlane16_swap(w[0][0], w[1][0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(w[0][1], w[1][1], false, false);
+        const int ch = 32 * dp + 16 * (g & 1) + 8 * (g >> 1);
+        if (tok < nb)
+          __builtin_nontemporal_store(u32x4_t{s0[0], s1[0], s0[1], s1[1]},
+                                      reinterpret_cast<u32x4_t*>(X + static_cast<size_t>(tok) * D + ch));
       }
-      *reinterpret_cast<uint2*>(X + static_cast<size_t>(tok) * D + 16 * db + 4 * g) =
-          make_uint2(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]));
     }
   }
 }
@@ -136,6 +169,21 @@ ReconWs carve(const lla_desc& desc, int B, void* ws, size_t ws_bytes) {
   w.partials = reinterpret_cast<float*>(base + 2 * kv + id);
   w.partial_bytes = ws_bytes > 2 * kv + id ? ws_bytes - 2 * kv - id : 0;
   return w;
+}
+
+typedef void (*ReconFn)(ReconParams);
+
+template <int D, int... Rs>
+ReconFn recon_pick(int r, std::integer_sequence<int, Rs...>) {
+  ReconFn f = nullptr;
+  ((r == 32 * (Rs + 1) ? (f = reconstruct_kernel<D, 32 * (Rs + 1)>, 0) : 0), ...);
+  return f;
+}
+
+// ranks 32, 64, ..., 256 for d_head 64 and 128
+ReconFn recon_fn(int D, int r) {
+  constexpr auto ranks = std::make_integer_sequence<int, kMaxR / 32>{};
+  return D == 128 ? recon_pick<128>(r, ranks) : D == 64 ? recon_pick<64>(r, ranks) : nullptr;
 }
 
 lla_desc attend_desc(const lla_desc& desc) {
@@ -171,7 +219,9 @@ hipError_t launch_decode_reconstruct(const DecodeParams& p, const lla_desc& desc
   if (reconstruct_workspace_bytes(desc, p.B) > p.ws_bytes) return hipErrorInvalidValue;
   const ReconWs w = carve(desc, p.B, p.ws, p.ws_bytes);
   const int D = p.d;
-  const dim3 grid((p.n_max + kTokWG - 1) / kTokWG, p.B * p.H);
+  const int tiles = (p.n_max + kTokWG - 1) / kTokWG;
+  const int per_seq = (kTargetWG + p.B * p.H - 1) / (p.B * p.H);
+  const dim3 grid(std::max(1, std::min(tiles, per_seq)), p.B * p.H);
   ReconParams rp{};
   rp.seq_lens = p.seq_lens;
   rp.H = p.H;
@@ -184,10 +234,9 @@ hipError_t launch_decode_reconstruct(const DecodeParams& p, const lla_desc& desc
     rp.mu = axis == 0 ? p.mu_k : p.mu_v;
     rp.x = axis == 0 ? w.k : w.v;
     rp.r = axis == 0 ? p.r_k : p.r_v;
-    if (D == 128)
-      hipLaunchKernelGGL(reconstruct_kernel<128>, grid, dim3(256), 0, stream, rp);
-    else
-      hipLaunchKernelGGL(reconstruct_kernel<64>, grid, dim3(256), 0, stream, rp);
+    const auto fn = recon_fn(D, rp.r);
+    if (fn == nullptr) return hipErrorNotSupported;
+    hipLaunchKernelGGL(fn, grid, dim3(256), 0, stream, rp);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
