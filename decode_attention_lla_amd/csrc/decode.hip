@@ -96,12 +96,25 @@ __device__ void finish_unit(const DecodeParams& p, int b, int h, float M, float 
 // token and out; LS that of the latent rows (S itself, or Q8 low-bit rows read whole by one lane:
 // the K row scale multiplies the score, the V row scale the token's weight). With R each token's
 // score also gets its precomputed base-2 rotary score p.sr[bh][slot] (decoupled RoPE branch).
-// A lane's S-byte row slice (whole words, S <= 32) at byte offset off of a raw buffer: one load of
-// up to 16 bytes into f[0], the rest into f[1].
-template <int S, int AUX>
-__device__ __forceinline__ void load_slice(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint4* f) {
-  f[0] = buffer_words<(S < 16 ? S : 16) / 4, AUX>(rs, off);
-  if constexpr (S > 16) f[1] = buffer_words<(S - 16) / 4, AUX>(rs, off + 16);
+// A lane's S-byte row slice (whole words, S <= 32) of the row at byte offset row of a raw buffer,
+// for lane sub of the LPT lanes that share the row. Up to 16 bytes: one load at S*sub. Longer
+// slices are split: the first 16 bytes at 16*sub (into f[0]), the rest at 16*LPT + (S-16)*sub
+// (into f[1]), so each of the two load instructions reads every row as one run without gaps.
+template <int S, int AUX, int LPT>
+__device__ __forceinline__ void load_slice(__amdgpu_buffer_rsrc_t rs, uint32_t row, int sub, uint4* f) {
+  if constexpr (S <= 16) {
+    f[0] = buffer_words<S / 4, AUX>(rs, row + S * sub);
+  } else {
+    f[0] = buffer_words<4, AUX>(rs, row + 16 * sub);
+    f[1] = buffer_words<(S - 16) / 4, AUX>(rs, row + 16 * LPT + (S - 16) * sub);
+  }
+}
+// The latent entry that element e of lane sub's slice holds (E elements per slice, E16 of them in
+// the first 16 bytes; SPLIT: the slice is split as load_slice splits slices over 16 bytes).
+template <bool SPLIT, int E, int E16, int LPT>
+__device__ __forceinline__ int slice_entry(int sub, int e) {
+  if constexpr (SPLIT) return e < E16 ? sub * E16 + e : LPT * E16 + sub * (E - E16) + (e - E16);
+  return sub * E + e;
 }
 
 template <class S, class LS, int RK, int RV, int LPT, int U, bool G, bool R = false>
@@ -128,6 +141,10 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
                 "rows must split evenly over lanes");
   static_assert(kOne || (VK * 16 == SK && VV * 16 == SV), "16-byte fragments");
   static_assert(!kQ8 || kOne || LPT == 1, "a low-bit row is one lane's, or one load per lane");
+  constexpr int E16 = 16 / LS::kBytes;                // elements in a slice's first 16 bytes
+  constexpr bool kSplitK = kOne && SK > 16;          // slices read by two loads (load_slice)
+  constexpr bool kSplitV = kOne && SV > 16;
+  static_assert(!kQ8 || !(kSplitK || kSplitV), "low-bit slices are one load");
 
   __shared__ float q_s[256];
   __shared__ float qt_s[RK];
@@ -193,7 +210,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   float qt[EK];
 #pragma unroll
   for (int e = 0; e < EK; ++e) {
-    const int c = sub * EK + e;  // low-bit slots past the codes take a zero query weight
+    const int c = slice_entry<kSplitK, EK, E16, LPT>(sub, e);  // low-bit slots past the codes take a zero query weight
     qt[e] = (!kQ8 || c < RK) ? qt_s[min(c, RK - 1)] : 0.f;
   }
   // low-bit slices: the bytes of each of this lane's words that hold codes (padding and the scale
@@ -324,8 +341,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
         } else {
           rr = static_cast<uint32_t>(min(tok, te) - row0);
         }
-        load_slice<SK, kAux>(rsk, rr * RKB + sub * SK, kr[u]);
-        load_slice<SV, kAux>(rsv, rr * RVB + sub * SV, vr[u]);
+        load_slice<SK, kAux, LPT>(rsk, rr * RKB, sub, kr[u]);
+        load_slice<SV, kAux, LPT>(rsv, rr * RVB, sub, vr[u]);
       }
     };
     auto mask = [&](int t0, bool (&ok)[U]) {
@@ -379,8 +396,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
       for (int u = 0; u < U; ++u) {
         if constexpr (kOne) {
           const uint32_t rr = ok[u] ? static_cast<uint32_t>(slot[u] - row0) : nrows;
-          load_slice<SK, kAux>(rsk, rr * RKB + sub * SK, kr[u]);
-          load_slice<SV, kAux>(rsv, rr * RVB + sub * SV, vr[u]);
+          load_slice<SK, kAux, LPT>(rsk, rr * RKB, sub, kr[u]);
+          load_slice<SV, kAux, LPT>(rsv, rr * RVB, sub, vr[u]);
         } else if (ok[u]) {
           const uint4* kp = reinterpret_cast<const uint4*>(zkp + static_cast<size_t>(slot[u]) * RKB);
           const uint4* vp = reinterpret_cast<const uint4*>(zvp + static_cast<size_t>(slot[u]) * RVB);
@@ -421,14 +438,14 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     if (lane < LPT) {
 #pragma unroll
       for (int e = 0; e < EV; ++e)
-        if (!kQ8 || lane * EV + e < RV) w[2 + lane * EV + e] = acc[e];
+        if (!kQ8 || lane * EV + e < RV) w[2 + slice_entry<kSplitV, EV, E16, LPT>(lane, e)] = acc[e];
     }
     return;
   }
   if (lane < LPT) {
 #pragma unroll
     for (int e = 0; e < EV; ++e)
-      if (!kQ8 || lane * EV + e < RV) a_s[lane * EV + e] = acc[e];
+      if (!kQ8 || lane * EV + e < RV) a_s[slice_entry<kSplitV, EV, E16, LPT>(lane, e)] = acc[e];
   }
   __syncthreads();
   finish_unit<S>(p, b, h, M, l, a_s, q_s, lane);
