@@ -169,21 +169,15 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) int32_t slot_s[G ? kSlotCap : 4];
   const int32_t* srow = G ? p.slots + static_cast<size_t>(b) * p.budget : nullptr;
   const bool piped = kOne && (!G || te - tb <= kSlotCap);
+  // every 16-byte load of the list is issued here (positions past the split read as zeros) and
+  // written to LDS after the query absorption below, whose own loads then overlap the list's
+  const int nsl = G && kOne && piped ? (max(te - tb, 0) + 255) / 256 : 0;  // 256 positions per load
+  uint4 sl[G && kOne ? kSlotCap / 256 : 1];
   if constexpr (G && kOne) {
-    if (piped) {
-      // every 16-byte load of the list issued before any is written to LDS (positions past the
-      // split read as zeros); visible to the other lanes after the barriers below
-      const int n = max(te - tb, 0);
-      const int nk = (n + 255) / 256;  // 256 positions per load instruction
-      const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(srow + tb, static_cast<uint32_t>(n) * 4);
-      uint4 sl[kSlotCap / 256];
+    const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(srow + tb, static_cast<uint32_t>(max(te - tb, 0)) * 4);
 #pragma unroll
-      for (int k = 0; k < kSlotCap / 256; ++k)
-        if (k < nk) sl[k] = buffer_words<4, 0>(rl, static_cast<uint32_t>(k * 64 + lane) * 16);
-#pragma unroll
-      for (int k = 0; k < kSlotCap / 256; ++k)
-        if (k < nk) *reinterpret_cast<uint4*>(&slot_s[(k * 64 + lane) * 4]) = sl[k];
-    }
+    for (int k = 0; k < kSlotCap / 256; ++k)
+      if (k < nsl) sl[k] = buffer_words<4, 0>(rl, static_cast<uint32_t>(k * 64 + lane) * 16);
   }
 
   // --- 1. query absorption ------------------------------------------------------------------
@@ -203,7 +197,12 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     for (int j = lane; j < p.d; j += 64) part += q_s[j] * ld<S>(p.mu_k, moff + j);
     beta = wave_sum(part) * p.scale_log2;
   }
-  __syncthreads();
+  if constexpr (G && kOne) {
+#pragma unroll
+    for (int k = 0; k < kSlotCap / 256; ++k)
+      if (k < nsl) *reinterpret_cast<uint4*>(&slot_s[(k * 64 + lane) * 4]) = sl[k];
+  }
+  __syncthreads();  // the slot list is visible to every lane from here
 
   const int sub = lane % LPT;
   const int grp = lane / LPT;
