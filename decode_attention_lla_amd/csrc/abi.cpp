@@ -22,6 +22,7 @@ bool desc_ok(const lla_desc* d) {
   if (d->dtype != LLA_F32 && d->dtype != LLA_BF16 && d->dtype != LLA_BF16_Q8 && d->dtype != LLA_BF16_I8)
     return false;
   if (d->H <= 0 || d->T <= 0 || d->r_k <= 0 || d->r_v <= 0 || d->n_max <= 0) return false;
+  if (d->H > 65535) return false;  // heads index a launch dimension of at most 65535
   if (d->d_head <= 0 || d->d_head > 256 || (d->d_head % 8) != 0) return false;
   if (!(d->scale >= 0.f) || std::isinf(d->scale)) return false;
   // H * n_max rows of the wider axis stay under 2 GiB: flattened per-sequence indices and the

@@ -88,8 +88,8 @@ __global__ __launch_bounds__(256) void qproj2d_kernel(DecodeParams p, float* qt,
   constexpr int QS = RK + DR;
   __shared__ float q_s[kQB][128];
   __shared__ __attribute__((aligned(16))) uint16_t w_s[128 * RK];
-  const int h = blockIdx.x;
-  const int b0 = blockIdx.y * kQB;
+  const int h = blockIdx.x % p.H;  // one-dimensional grid: (block of kQB sequences) * H + head
+  const int b0 = blockIdx.x / p.H * kQB;
   const int tid = threadIdx.x;
   const size_t wrow = (static_cast<size_t>(p.t) * p.H + h) * p.d;  // rows of W^K_t for head h
   const uint4* wsrc = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.Wk) + wrow * RK);
@@ -199,9 +199,9 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
   const int lane = tid & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
-  const int split = blockIdx.x;
-  const int b = blockIdx.y;
-  const int h0 = blockIdx.z * 16;
+  const int split = blockIdx.x % p.splits;  // grid x: b * splits + split; y: head group
+  const int b = blockIdx.x / p.splits;
+  const int h0 = blockIdx.y * 16;
   const int h = h0 + col;
   const bool hvalid = h < p.H;
 
@@ -382,8 +382,8 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
   __shared__ float a_s[kQB][RV];
   __shared__ float f_s[kQB][64];
   __shared__ float fin_s[kQB][4];  // f_lat, p_self, 1/den, l
-  const int h = blockIdx.x;
-  const int b0 = blockIdx.y * kQB;
+  const int h = blockIdx.x % p.H;  // one-dimensional grid: (block of kQB sequences) * H + head
+  const int b0 = blockIdx.x / p.H * kQB;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -576,14 +576,14 @@ hipError_t launch_decode2d(const DecodeParams& p, hipStream_t stream) {
   float* beta = reinterpret_cast<float*>(ws + qt_bytes);
   float* part = reinterpret_cast<float*>(ws + qt_bytes + align256(bh * 4));
   const unsigned qb = (p.B + kQB - 1) / kQB;
-  hipLaunchKernelGGL(e->qproj[ri], dim3(p.H, qb), dim3(256), 0, stream, p, qt, beta);
+  hipLaunchKernelGGL(e->qproj[ri], dim3(p.H * qb), dim3(256), 0, stream, p, qt, beta);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(e->partial[ri], dim3(p.splits, p.B, (p.H + 15) / 16), dim3(64 * Cfg2d<64, 64>::kW), 0,
+  hipLaunchKernelGGL(e->partial[ri], dim3(p.splits * p.B, (p.H + 15) / 16), dim3(64 * Cfg2d<64, 64>::kW), 0,
                      stream, p, qt, beta, part);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(e->combine, dim3(p.H, qb), dim3(256), 0, stream, p, part);
+  hipLaunchKernelGGL(e->combine, dim3(p.H * qb), dim3(256), 0, stream, p, part);
   return hipGetLastError();
 }
 

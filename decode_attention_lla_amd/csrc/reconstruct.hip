@@ -35,8 +35,9 @@ constexpr int kTargetWG = 3072;            // about four rounds of three workgro
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 // X^T = W_t (D x R) . Z^T (R x tokens) for one (b, h), stored as bf16 rows X[token][D] (+ mu_t).
-// A workgroup stages W_t[h] in LDS once and then walks 128-token tiles (tile = blockIdx.x,
-// blockIdx.x + gridDim.x, ...), so the factor is read once per workgroup rather than per tile.
+// A workgroup (x: b * H + h) stages W_t[h] in LDS once and then walks 128-token tiles (tile =
+// blockIdx.y, blockIdx.y + gridDim.y, ...), so the factor is read once per workgroup rather than
+// per tile.
 // A operand: rows of W_t[h] (k = latent entry) from LDS, rows padded by 16 bytes so the 16 rows of
 // a ds_read_b128 fall on distinct banks (R is a multiple of 32). B operand: each lane's 16 bytes
 // of a latent row, all R/32 k-steps issued before the first product, through a buffer descriptor
@@ -49,13 +50,13 @@ __global__ __launch_bounds__(256, 3) void reconstruct_kernel(ReconParams p) {
   constexpr int KS = R / 32;
   constexpr int RS = R * 2 + 16;
   __shared__ __attribute__((aligned(16))) char w_s[D * RS];
-  const int bh = blockIdx.y;
+  const int bh = blockIdx.x;
   const int h = bh % p.H;
   const int b = bh / p.H;
   int nb = p.seq_lens != nullptr ? uniform(p.seq_lens[b]) : p.n_max;
   nb = min(max(nb, 0), p.n_max);
   const int ntiles = (nb + kTokWG - 1) / kTokWG;
-  if (static_cast<int>(blockIdx.x) >= ntiles) return;  // workgroup-uniform, before any barrier
+  if (static_cast<int>(blockIdx.y) >= ntiles) return;  // workgroup-uniform, before any barrier
 
   const uint16_t* W = static_cast<const uint16_t*>(p.W) + (static_cast<size_t>(p.t) * p.H + h) * D * R;
   constexpr int cpr = R / 8;  // 16-byte chunks per W row
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256, 3) void reconstruct_kernel(ReconParams p) {
   uint16_t* X = static_cast<uint16_t*>(p.x) + static_cast<size_t>(bh) * p.n_max * D;
   __syncthreads();
 
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
     const int wtok = tile * kTokWG + wave * kTokWave;
     uint4 bz[KS][2];
 #pragma unroll
@@ -221,7 +222,7 @@ hipError_t launch_decode_reconstruct(const DecodeParams& p, const lla_desc& desc
   const int D = p.d;
   const int tiles = (p.n_max + kTokWG - 1) / kTokWG;
   const int per_seq = (kTargetWG + p.B * p.H - 1) / (p.B * p.H);
-  const dim3 grid(std::max(1, std::min(tiles, per_seq)), p.B * p.H);
+  const dim3 grid(p.B * p.H, std::max(1, std::min(tiles, per_seq)));
   ReconParams rp{};
   rp.seq_lens = p.seq_lens;
   rp.H = p.H;

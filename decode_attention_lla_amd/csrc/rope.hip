@@ -67,12 +67,14 @@ __global__ __launch_bounds__(kTokTile) void rope_scores_kernel(RopeScoreParams p
   extern __shared__ float q_s[];  // [H][DR] rotated rotary queries times scale_log2
   constexpr int half = DR / 2;
   constexpr int KS = DR / 32;
-  const int b = blockIdx.y;
+  const int tiles = (p.n_max + kTokTile - 1) / kTokTile;  // one-dimensional grid: b * tiles + tile
+  const int b = blockIdx.x / tiles;
+  const int tile = blockIdx.x - b * tiles;
   int nb = p.seq_lens != nullptr ? uniform(p.seq_lens[b]) : p.n_max;
   nb = min(max(nb, 0), p.n_max);
-  const int tok0 = blockIdx.x * kTokTile;
+  const int tok0 = tile * kTokTile;
   const uint16_t* qr = static_cast<const uint16_t*>(p.q_rope) + static_cast<size_t>(b) * p.H * DR;
-  if (blockIdx.x == 0 && p.k_rope_self != nullptr) {
+  if (tile == 0 && p.k_rope_self != nullptr) {
     const uint16_t* ks = static_cast<const uint16_t*>(p.k_rope_self) + static_cast<size_t>(b) * DR;
     for (int h = threadIdx.x; h < p.H; h += kTokTile) {
       float acc = 0.f;
@@ -160,7 +162,9 @@ hipError_t launch_rope_write(const RopeWriteParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_rope_scores(const RopeScoreParams& p, hipStream_t stream) {
-  const dim3 grid((p.n_max + kTokTile - 1) / kTokTile, p.B);
+  const int64_t blocks = static_cast<int64_t>((p.n_max + kTokTile - 1) / kTokTile) * p.B;
+  if (blocks >= (int64_t(1) << 31)) return hipErrorNotSupported;
+  const dim3 grid(static_cast<unsigned>(blocks));
   const size_t lds = static_cast<size_t>(p.H) * p.d_r * sizeof(float);
   switch (p.d_r) {
     case 32: hipLaunchKernelGGL(rope_scores_kernel<32>, grid, dim3(kTokTile), lds, stream, p); break;

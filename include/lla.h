@@ -80,7 +80,7 @@ typedef enum { LLA_PER_HEAD = 0, LLA_2D = 1 } lla_variant;
 typedef struct {
   int32_t variant; /* lla_variant */
   int32_t dtype;   /* lla_dtype */
-  int32_t H;       /* heads */
+  int32_t H;       /* heads, 1 .. 65535 */
   int32_t d_head;  /* channels per head, multiple of 8, <= 256 */
   int32_t T;       /* loops (recurrence steps) */
   int32_t r_k;     /* K latent rank */
