@@ -80,7 +80,7 @@ __device__ __forceinline__ int seq_keys(const DecodeParams& p, int b) {
 }
 
 // ---- 1. query absorption for every (b, h) ------------------------------------------------------
-// grid (H, ceil(B / kQB)), 256 threads. W^K_t[h] (d x RK bf16) is staged in LDS with one round of
+// grid H * ceil(B / kQB) (x), 256 threads. W^K_t[h] (d x RK bf16) is staged in LDS with one round of
 // 16-byte loads; thread k then forms q~[b][h][k] for kQB sequences from LDS.
 // qt rows hold RK + DR floats: q~, then the rotated rotary query (both times scale * log2 e).
 template <int RK, int DR>
