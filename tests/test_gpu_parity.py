@@ -12,7 +12,7 @@ import torch
 
 from decode_attention_lla_amd import lla, synth
 from oracle import lla_oracle as O
-from tests.gpu_util import (LLA_DT, LLA_VAR, assert_close, assert_lse, dev, host, rel_err,
+from tests.gpu_util import (LLA_DT, LLA_VAR, assert_close, assert_lse, dev, host, mfma_lse_slack, rel_err,
                             require_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -537,7 +537,10 @@ def test_decode_random_configurations(cfg):
     live = [b for b in range(c["B"]) if c["self_token"] or min(max(c["lens"][b], 0), c["n_max"]) > 0]
     if live:
         assert_close(o[live], ro[live], c["dtype"], str(c))
-        assert_lse(lse[live], rl[live], str(c))
+        mfma = (c["variant"] == "2d" and c["dtype"] == "bf16" and (c["rk"], c["rv"]) in MFMA_2D_PAIRS
+                and c["d"] <= 128)
+        slack = mfma_lse_slack(case["q"][c["t"]], case["zk"], case["Wk"], c["t"], c["lens"])[live] if mfma else None
+        assert_lse(lse[live], rl[live], str(c), slack)
 
 
 PREFILL_MFMA_PAIRS = [(64, 64), (128, 128), (256, 256), (64, 128), (128, 256)]
