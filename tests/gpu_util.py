@@ -71,22 +71,34 @@ def assert_lse(got, ref, what="", slack=None):
         assert err <= LSE_TOL, f"{what}: lse error {err:.3e}"
 
 
-def mfma_lse_slack(q, zk, Wk, t, lens, scale=None):
+def mfma_lse_slack(q, zk, Wk, t, lens, scale=None, q_rope=None, k_rope=None):
     """Absolute lse slack per (b, h) for the LLA-2D MFMA read. Its scores take q~ = W^K_t[h]^T q as
     a bf16 pair (hi + lo: each entry within 2^-18 of q~_j, relative) times bf16 latents, summed in
     fp32, so |ds_i| <= 2^-16 * scale * sum_j |q~_j z_ij| <= 2^-16 * scale * |q~| * |z_i| (Cauchy-
     Schwarz), and the lse moves by at most max_i |ds_i|. With a few keys and a sharpened query
     sum_j |q~_j z_ij| can exceed |lse| many times over, which a bound relative to |lse| misses.
-    q [B][H][d], zk [B][n][r], Wk [T][H*d][r] (float64 copies of the device values)."""
+    With the fused rotary branch the rotated rotary query is split the same way, adding
+    |q_R| * |k_R,i| per key (rotation keeps norms), and the default scale is 1/sqrt(d + d_rope).
+    q [B][H][d], zk [B][n][r], Wk [T][H*d][r], q_rope [B][H][d_rope], k_rope [B][n][d_rope]
+    (float64 copies of the device values)."""
     B, H, d = q.shape
     qt = np.einsum("bhd,hdr->bhr", np.asarray(q, np.float64), np.asarray(Wk[t], np.float64).reshape(H, d, -1))
+    qn = np.linalg.norm(qt, axis=-1)
     zn = np.linalg.norm(np.asarray(zk, np.float64), axis=-1)
+    rope = q_rope is not None
+    if rope:
+        qrn = np.linalg.norm(np.asarray(q_rope, np.float64), axis=-1)
+        krn = np.linalg.norm(np.asarray(k_rope, np.float64), axis=-1)
     out = np.zeros((B, H))
     for b in range(B):
         n = min(max(int(lens[b]), 0), zk.shape[1])
         if n:
-            out[b] = np.linalg.norm(qt[b], axis=-1) * zn[b, :n].max()
-    return 2.0 ** -16 * (scale if scale else 1.0 / np.sqrt(d)) * out
+            per_key = qn[b][:, None] * zn[b, :n][None, :]
+            if rope:
+                per_key = per_key + qrn[b][:, None] * krn[b, :n][None, :]
+            out[b] = per_key.max(axis=1)
+    d_all = d + (np.asarray(q_rope).shape[-1] if rope else 0)
+    return 2.0 ** -16 * (scale if scale else 1.0 / np.sqrt(d_all)) * out
 
 
 def desc_for(s, n_max=None, scale=0.0):

@@ -11,7 +11,7 @@ import torch
 
 from decode_attention_lla_amd import lla, synth
 from oracle import lla_oracle as O
-from tests.gpu_util import assert_close, assert_lse, dev, host, require_gpu
+from tests.gpu_util import assert_close, assert_lse, dev, host, mfma_lse_slack, require_gpu
 from tests.test_gpu_parity import PAIRS, mk_desc, upload
 
 pytestmark = pytest.mark.gpu
@@ -153,7 +153,10 @@ def test_rope_decode_random(cfg):
     live = _live(c["lens"], c["n_max"], st)
     if live:
         assert_close(host(out)[live], ro[live], "bf16", str(c))
-        assert_lse(host(lse)[live], rl[live], str(c))
+        mfma = c["variant"] == "2d" and (c["rk"], c["rv"]) in MFMA_2D_PAIRS and c["d"] <= 128
+        slack = mfma_lse_slack(case["q"][t], case["zk"], case["Wk"], t, c["lens"], q_rope=qr,
+                               k_rope=kr)[live] if mfma else None
+        assert_lse(host(lse)[live], rl[live], str(c), slack)
 
 
 def _rope_prefill_configs(n, seed=23000):
