@@ -104,3 +104,41 @@ def mfma_lse_slack(q, zk, Wk, t, lens, scale=None, q_rope=None, k_rope=None):
 def desc_for(s, n_max=None, scale=0.0):
     return lla.make_desc(LLA_VAR[s.variant], LLA_DT[s.dtype], s.H, s.d, s.T, s.r_k, s.r_v,
                          s.n_max if n_max is None else n_max, scale)
+
+
+def _bf16_rne(x):
+    """float64 -> float32 -> bf16 (round to nearest even), returned as float64."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def rebuild_flip_lse_slack(q, zk, Wk, t, lens, mu_k=None, scale=None):
+    """Absolute lse slack per (b, h) for reconstruct-then-attend. The comparator rounds each rebuilt
+    K entry k = W^K_t z + mu to bf16 from an fp32 MFMA sum; the oracle rounds the exact value. The
+    two can land one bf16 step apart only where k lies within the fp32 sum's error bound
+    (r * 2^-24 * sum_l |W_jl z_l|, plus 2^-24 |k| for adding mu) of a rounding midpoint. Such
+    entries may move score i by scale * sum_j |q_j| * step(k_ij), and the lse by at most the largest
+    such move. q [B][H][d], zk [B][H][n][r], Wk [T][H][d][r], mu_k [H][T*d] or None (float64)."""
+    q = np.asarray(q, np.float64)
+    B, H, d = q.shape
+    W = np.asarray(Wk[t], np.float64)                     # [H][d][r]
+    r = W.shape[-1]
+    out = np.zeros((B, H))
+    for b in range(B):
+        n = min(max(int(lens[b]), 0), zk.shape[2])
+        if n == 0:
+            continue
+        z = np.asarray(zk[b, :, :n], np.float64)          # [H][n][r]
+        k = np.einsum("hdr,hnr->hnd", W, z)
+        mag = np.einsum("hdr,hnr->hnd", np.abs(W), np.abs(z))
+        if mu_k is not None:
+            k = k + np.asarray(mu_k, np.float64)[:, t * d:(t + 1) * d][:, None, :]
+        kb = _bf16_rne(k)
+        e = np.floor(np.log2(np.maximum(np.abs(kb), np.finfo(np.float32).tiny)))
+        step = 2.0 ** (e - 7)                              # one bf16 step at kb's binade
+        dist = np.minimum(np.abs(k - (kb - step / 2)), np.abs(k - (kb + step / 2)))
+        flip = dist <= r * 2.0 ** -24 * mag + 2.0 ** -24 * np.abs(k)
+        per_key = np.einsum("hd,hnd->hn", np.abs(q[b]), np.where(flip, 2 * step, 0.0))
+        out[b] = per_key.max(axis=1)
+    return (scale if scale else 1.0 / np.sqrt(d)) * out

@@ -11,7 +11,8 @@ import torch
 
 from decode_attention_lla_amd import lla, synth
 from oracle import lla_oracle as O
-from tests.gpu_util import assert_close, assert_lse, dev, host, mfma_lse_slack, require_gpu
+from tests.gpu_util import (assert_close, assert_lse, dev, host, mfma_lse_slack, rebuild_flip_lse_slack,
+                            require_gpu)
 from tests.test_gpu_parity import PAIRS, mk_desc, upload
 
 pytestmark = pytest.mark.gpu
@@ -328,3 +329,55 @@ def test_low_bit_decode_random(cfg):
     if live:
         assert_close(host(out)[live], ro[live], "bf16", str(c))
         assert_lse(host(lse)[live], rl[live], str(c))
+
+
+# --------------------------------------------------------------------------------------------
+# reconstruct-then-attend comparator
+# --------------------------------------------------------------------------------------------
+
+def _reconstruct_configs(n, seed=26000):
+    rng = np.random.default_rng(seed)
+    ranks = [32 * k for k in range(1, 9)]  # every compiled rank of the rebuild kernel
+    out = []
+    for i in range(n):
+        n_max = int(rng.choice([1, 100, 129, 700]))
+        B = int(rng.integers(1, 5))
+        out.append(dict(i=i, d=int(rng.choice([64, 128])), rk=int(rng.choice(ranks)),
+                        rv=int(rng.choice(ranks)), H=int(rng.choice([1, 2, 3])), T=int(rng.integers(1, 3)),
+                        B=B, n_max=n_max, lens=[int(x) for x in rng.integers(0, n_max + 2, B)],
+                        mu=bool(rng.random() < 0.5), self_token=bool(rng.random() < 0.6),
+                        gain=float(rng.choice([1.0, 8.0]))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _reconstruct_configs(16), ids=lambda c: f"cfg{c['i']}")
+def test_reconstruct_random(cfg):
+    """Seeded draws over head width, both ranks (32 .. 256, so every rebuild tile shape), heads,
+    batch, cache size, ragged and out-of-range lengths, mu, the self token and sharpened queries:
+    the comparator against the oracle's explicit decode with the rebuilt K/V rounded to bf16."""
+    c = cfg
+    desc = mk_desc("per_head", "bf16", c["H"], c["d"], c["T"], c["rk"], c["rv"], c["n_max"])
+    case = upload(synth.random_case("per_head", "bf16", c["B"], c["H"], c["d"], c["T"], c["rk"], c["rv"],
+                                    c["n_max"], 26100 + c["i"], with_mu=c["mu"], q_gain=c["gain"]), "bf16")
+    t = c["T"] - 1
+    st = c["self_token"]
+    q = dev(case["q"][t], "bf16")
+    out = torch.empty_like(q)
+    lse = torch.empty(c["B"], c["H"], device="cuda")
+    lla.lla_attend_decode_reconstruct(desc, c["B"], t, q, case["_zk"], case["_zv"],
+                                      dev(np.array(c["lens"], np.int32)), case["_Wk"], case["_Wv"],
+                                      case["_muk"] if c["mu"] else None, case["_muv"] if c["mu"] else None,
+                                      dev(case["k_self"][t], "bf16") if st else None,
+                                      dev(case["v_self"][t], "bf16") if st else None, out, lse,
+                                      lla.reconstruct_workspace(desc, c["B"]))
+    torch.cuda.synchronize()
+    ro, rl = O.attend_decode(case["q"][t], case["zk"], case["zv"], case["Wk"], case["Wv"], t, c["lens"],
+                             case["mu_k"] if c["mu"] else None, case["mu_v"] if c["mu"] else None,
+                             case["k_self"][t] if st else None, case["v_self"][t] if st else None,
+                             kv_round_bf16=True)
+    live = _live(c["lens"], c["n_max"], st)
+    if live:
+        assert_close(host(out)[live], ro[live], "bf16", str(c))
+        slack = rebuild_flip_lse_slack(case["q"][t], case["zk"], case["Wk"], t, c["lens"],
+                                       case["mu_k"] if c["mu"] else None)[live]
+        assert_lse(host(lse)[live], rl[live], str(c), slack)
