@@ -35,9 +35,9 @@ constexpr int kTargetWG = 3072;            // about four rounds of three workgro
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 // X^T = W_t (D x R) . Z^T (R x tokens) for one (b, h), stored as bf16 rows X[token][D] (+ mu_t).
-// A workgroup (x: b * H + h) stages W_t[h] in LDS once and then walks 128-token tiles (tile =
-// blockIdx.y, blockIdx.y + gridDim.y, ...), so the factor is read once per workgroup rather than
-// per tile.
+// A workgroup (one-dimensional grid: (b * H + h) * slots + slot) stages W_t[h] in LDS once and
+// then walks 128-token tiles (tile = slot, slot + slots, ...), so the factor is read once per
+// workgroup rather than per tile; neighbouring workgroups take neighbouring tiles of one head.
 // A operand: rows of W_t[h] (k = latent entry) from LDS, rows padded by 16 bytes so the 16 rows of
 // a ds_read_b128 fall on distinct banks (R is a multiple of 32). B operand: each lane's 16 bytes
 // of a latent row, all R/32 k-steps issued before the first product, through a buffer descriptor
@@ -46,17 +46,18 @@ size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 // neighbouring blocks turns that into 8 consecutive channels, one 16-byte store per lane. The rows
 // are written non-temporally: the attention reads them back only after every row is written.
 template <int D, int R>
-__global__ __launch_bounds__(256, 3) void reconstruct_kernel(ReconParams p) {
+__global__ __launch_bounds__(256, 3) void reconstruct_kernel(ReconParams p, int slots) {
   constexpr int KS = R / 32;
   constexpr int RS = R * 2 + 16;
   __shared__ __attribute__((aligned(16))) char w_s[D * RS];
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / slots;
+  const int slot = blockIdx.x - bh * slots;
   const int h = bh % p.H;
   const int b = bh / p.H;
   int nb = p.seq_lens != nullptr ? uniform(p.seq_lens[b]) : p.n_max;
   nb = min(max(nb, 0), p.n_max);
   const int ntiles = (nb + kTokWG - 1) / kTokWG;
-  if (static_cast<int>(blockIdx.y) >= ntiles) return;  // workgroup-uniform, before any barrier
+  if (slot >= ntiles) return;  // workgroup-uniform, before any barrier
 
   const uint16_t* W = static_cast<const uint16_t*>(p.W) + (static_cast<size_t>(p.t) * p.H + h) * D * R;
   constexpr int cpr = R / 8;  // 16-byte chunks per W row
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256, 3) void reconstruct_kernel(ReconParams p) {
   uint16_t* X = static_cast<uint16_t*>(p.x) + static_cast<size_t>(bh) * p.n_max * D;
   __syncthreads();
 
-  for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
+  for (int tile = slot; tile < ntiles; tile += slots) {
     const int wtok = tile * kTokWG + wave * kTokWave;
     uint4 bz[KS][2];
 #pragma unroll
@@ -172,7 +173,7 @@ ReconWs carve(const lla_desc& desc, int B, void* ws, size_t ws_bytes) {
   return w;
 }
 
-typedef void (*ReconFn)(ReconParams);
+typedef void (*ReconFn)(ReconParams, int);
 
 template <int D, int... Rs>
 ReconFn recon_pick(int r, std::integer_sequence<int, Rs...>) {
@@ -222,7 +223,8 @@ hipError_t launch_decode_reconstruct(const DecodeParams& p, const lla_desc& desc
   const int D = p.d;
   const int tiles = (p.n_max + kTokWG - 1) / kTokWG;
   const int per_seq = (kTargetWG + p.B * p.H - 1) / (p.B * p.H);
-  const dim3 grid(p.B * p.H, std::max(1, std::min(tiles, per_seq)));
+  const int slots = std::max(1, std::min(tiles, per_seq));
+  const dim3 grid(static_cast<unsigned>(p.B * p.H * slots));
   ReconParams rp{};
   rp.seq_lens = p.seq_lens;
   rp.H = p.H;
@@ -237,7 +239,7 @@ hipError_t launch_decode_reconstruct(const DecodeParams& p, const lla_desc& desc
     rp.r = axis == 0 ? p.r_k : p.r_v;
     const auto fn = recon_fn(D, rp.r);
     if (fn == nullptr) return hipErrorNotSupported;
-    hipLaunchKernelGGL(fn, grid, dim3(256), 0, stream, rp);
+    hipLaunchKernelGGL(fn, grid, dim3(256), 0, stream, rp, slots);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
