@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "lla.h"
 #include "lla_internal.h"
@@ -104,6 +105,33 @@ bool rows_ok(const lla_desc* desc, int64_t rows) {
   return rows > 0 && rows * desc->H < (int64_t(1) << 31) / 64;
 }
 
+// Scratch of lla_attend_decode_noalloc: the split partials (and, on the LLA-2D MFMA read, the
+// absorbed queries) of one call live here instead of a caller-given workspace. Every GPU the
+// library runs on holds its own copy for the life of the process. In host code `scratch` names a
+// host-side stand-in, never the device memory: kernels receive the address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[LLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on `dev`, which must be the current device. Looked up once per
+// device; no allocation happens here (the array is part of the loaded code object).
+hipError_t noalloc_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 255u) != 0) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,6 +145,8 @@ const char* lla_status_string(lla_status s) {
     case LLA_ERR_UNSUPPORTED: return "unsupported configuration";
     case LLA_ERR_WORKSPACE: return "workspace too small";
     case LLA_ERR_HIP: return "HIP launch error";
+    case LLA_ERR_SCRATCH_LIMIT:
+      return "call needs more scratch than the library's static buffer holds (LLA_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -228,6 +258,36 @@ lla_status lla_attend_decode(const lla_desc* desc, int32_t B, int32_t t, const v
                                       v_self, out, lse, ws, ws_bytes);
   lla::decode_plan(*desc, B, &p.splits, &p.chunk);
   return from_hip(lla::launch_decode(p, desc->dtype, static_cast<hipStream_t>(stream)));
+}
+
+lla_status lla_attend_decode_noalloc(const lla_desc* desc, int32_t B, int32_t t, const void* q,
+                                     const void* zk, const void* zv, const int32_t* seq_lens,
+                                     const void* Wk, const void* Wv, const void* mu_k,
+                                     const void* mu_v, const void* k_self, const void* v_self,
+                                     void* out, float* lse, void* stream) {
+  const lla_status st = decode_args_ok(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v,
+                                       k_self, v_self, out, lse, nullptr);
+  if (st != LLA_OK) return st;
+  if (!lla::decode_supported(desc->variant, desc->dtype, desc->r_k, desc->r_v, desc->d_head))
+    return LLA_ERR_UNSUPPORTED;
+  const size_t need = lla::decode_workspace_bytes(*desc, B);
+  if (need > LLA_NOALLOC_SCRATCH_BYTES) return LLA_ERR_SCRATCH_LIMIT;
+  // the scratch used is the one of the device the kernels run on: the stream's, which must be
+  // the current device (the array's address is looked up with that device current)
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LLA_ERR_HIP;
+  if (s != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return LLA_ERR_HIP;
+    if (sdev != dev) return LLA_ERR_INVALID_ARG;
+  }
+  void* ws = nullptr;
+  if (need > 0 && noalloc_scratch(dev, &ws) != hipSuccess) return LLA_ERR_HIP;
+  lla::DecodeParams p = decode_params(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_self,
+                                      v_self, out, lse, ws, need > 0 ? LLA_NOALLOC_SCRATCH_BYTES : 0);
+  lla::decode_plan(*desc, B, &p.splits, &p.chunk);
+  return from_hip(lla::launch_decode(p, desc->dtype, s));
 }
 
 lla_status lla_rope_write(const lla_desc* desc, int32_t B, int32_t C, int32_t d_rope, float base,

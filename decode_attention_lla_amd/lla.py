@@ -16,7 +16,9 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblla.so")
 
-LLA_OK, LLA_ERR_INVALID_ARG, LLA_ERR_UNSUPPORTED, LLA_ERR_WORKSPACE, LLA_ERR_HIP = range(5)
+(LLA_OK, LLA_ERR_INVALID_ARG, LLA_ERR_UNSUPPORTED, LLA_ERR_WORKSPACE, LLA_ERR_HIP,
+ LLA_ERR_SCRATCH_LIMIT) = range(6)
+LLA_NOALLOC_SCRATCH_BYTES = 16 << 20
 LLA_F32, LLA_BF16, LLA_BF16_Q8, LLA_BF16_I8 = 0, 1, 2, 3
 _LOW_BIT = (LLA_BF16_Q8, LLA_BF16_I8)
 LLA_PER_HEAD, LLA_2D = 0, 1
@@ -80,6 +82,9 @@ def _load():
     lib.lla_attend_decode.restype = _I
     lib.lla_attend_decode.argtypes = [_D, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, ctypes.c_size_t, _P]
+    lib.lla_attend_decode_noalloc.restype = _I
+    lib.lla_attend_decode_noalloc.argtypes = [_D, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                              _P, _P, _P]
     lib.lla_rope_write.restype = _I
     lib.lla_rope_write.argtypes = [_D, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P]
     lib.lla_rope_workspace_bytes.restype = ctypes.c_size_t
@@ -243,6 +248,24 @@ def lla_attend_decode(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_sel
     st = getattr(_load(), _entry)(ctypes.byref(desc), int(B), int(t), *args,
                                   ctypes.c_size_t(ws_bytes), _stream_ptr(stream))
     _check(st, _entry)
+
+
+def lla_attend_decode_noalloc(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_self, v_self,
+                              out, lse=None, stream=None):
+    dt = _TORCH_DTYPE[desc.dtype]
+    s = _shapes(desc, B)
+    qs = (B, desc.H, desc.d_head)
+    args = [
+        _ptr(q, "q", qs, dt), _ptr(zk, "zk", s["zk"], _zdt(desc)), _ptr(zv, "zv", s["zv"], _zdt(desc)),
+        _ptr(seq_lens, "seq_lens", (B,), torch.int32, True),
+        _ptr(Wk, "Wk", s["Wk"], dt), _ptr(Wv, "Wv", s["Wv"], dt),
+        _ptr(mu_k, "mu_k", s["mu"], dt, True), _ptr(mu_v, "mu_v", s["mu"], dt, True),
+        _ptr(k_self, "k_self", qs, dt, True), _ptr(v_self, "v_self", qs, dt, True),
+        _ptr(out, "out", qs, dt), _ptr(lse, "lse", (B, desc.H), torch.float32, True),
+    ]
+    st = _load().lla_attend_decode_noalloc(ctypes.byref(desc), int(B), int(t), *args,
+                                           _stream_ptr(stream))
+    _check(st, "lla_attend_decode_noalloc")
 
 
 def lla_rope_write(desc, B, C, d_rope, base, k_in, pos, k_rope, stream=None):

@@ -43,15 +43,20 @@
 extern "C" {
 #endif
 
-#define LLA_ABI_VERSION 1
+#define LLA_ABI_VERSION 2
 
 typedef enum {
   LLA_OK = 0,
   LLA_ERR_INVALID_ARG = 1, /* a null required pointer, bad size, t >= T, misaligned pointer */
   LLA_ERR_UNSUPPORTED = 2, /* a (variant, dtype, d_head, r_k, r_v) combination not compiled in */
   LLA_ERR_WORKSPACE = 3,   /* ws_bytes smaller than lla_workspace_bytes() */
-  LLA_ERR_HIP = 4          /* the HIP runtime refused a launch */
+  LLA_ERR_HIP = 4,         /* the HIP runtime refused a launch */
+  LLA_ERR_SCRATCH_LIMIT = 5 /* lla_attend_decode_noalloc: the call needs more than
+                               LLA_NOALLOC_SCRATCH_BYTES of scratch */
 } lla_status;
+
+/* Size of the library's static per-device scratch buffer (lla_attend_decode_noalloc). */
+#define LLA_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /* LLA_BF16_Q8: the precision axis stacked on the loop axis (Section 8, "Compositionality";
  * Appendix C evaluates an 8-bit codec). Each cached latent row of r values is stored as r OCP FP8
@@ -169,6 +174,26 @@ lla_status lla_attend_decode(const lla_desc* desc, int32_t B, int32_t t, const v
                              const void* Wk, const void* Wv, const void* mu_k, const void* mu_v,
                              const void* k_self, const void* v_self, void* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* lla_attend_decode for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments (minus ws, ws_bytes), same
+ * arithmetic and same kernels as lla_attend_decode, so the results are identical to a
+ * lla_attend_decode call with a fresh workspace. The split partials (and the LLA-2D MFMA read's
+ * absorbed queries) go to a static device array of LLA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends; nothing is allocated or freed, by this
+ * call or any routine it calls.
+ *   - A call whose plan needs more than LLA_NOALLOC_SCRATCH_BYTES returns LLA_ERR_SCRATCH_LIMIT and
+ *     enqueues nothing; what a plan needs is at most lla_workspace_bytes(desc, B, 1).
+ *   - The scratch of a GPU is shared by every call on it and keeps the last call's contents. Calls
+ *     that may overlap on one GPU (different streams without ordering, other host threads) race on
+ *     it and give wrong results; serialise them (one stream, or events).
+ *   - `stream` must belong to the current device (NULL: the current device's default stream);
+ *     otherwise LLA_ERR_INVALID_ARG. */
+lla_status lla_attend_decode_noalloc(const lla_desc* desc, int32_t B, int32_t t, const void* q,
+                                     const void* zk, const void* zv, const int32_t* seq_lens,
+                                     const void* Wk, const void* Wv, const void* mu_k,
+                                     const void* mu_v, const void* k_self, const void* v_self,
+                                     void* out, float* lse, void* stream);
 
 /* Decoupled rotary branch (Section 7, "Per-head LLA versus LLA-2D at inference": RoPE cannot be
  * absorbed, so the latent path carries the NoPE content and a small explicit rotary branch, shared

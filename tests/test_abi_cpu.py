@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert lla.lla_abi_version() == 1
+    assert lla.lla_abi_version() == 2
     assert lla.lla_status_string(lla.LLA_OK) == "ok"
     assert "workspace" in lla.lla_status_string(lla.LLA_ERR_WORKSPACE)
     assert lla.lla_status_string(99) == "unknown status"
@@ -333,3 +333,21 @@ def test_prefill_rope_arguments_and_support():
     assert call(d, d_rope=32) == lla.LLA_ERR_UNSUPPORTED
     assert call(desc(r_k=24, r_v=24, n_max=100)) == lla.LLA_ERR_UNSUPPORTED  # no MFMA prefill
     assert call(d) == lla.LLA_ERR_WORKSPACE
+
+
+def test_noalloc_decode_refusals_on_the_host():
+    """lla_attend_decode_noalloc validates like lla_attend_decode and refuses a plan larger than
+    its static scratch before touching the GPU."""
+    lib = lla.library()
+
+    def call(d, B=2, t=0, q=A, out=A):
+        return lib.lla_attend_decode_noalloc(ctypes.byref(d), B, t, q, A, A, N, A, A, N, N, N, N,
+                                             out, N, S)
+    assert call(desc(n_max=100), t=4) == lla.LLA_ERR_INVALID_ARG
+    assert call(desc(n_max=100), q=M) == lla.LLA_ERR_INVALID_ARG
+    assert call(desc(n_max=100, r_k=40, r_v=40)) == lla.LLA_ERR_UNSUPPORTED
+    # LLA-2D MFMA read at B = 4096: 64 MiB of absorbed queries alone
+    big = desc(variant=lla.LLA_2D, r_k=256, r_v=256, n_max=8193)
+    assert lla.lla_workspace_bytes(big, 4096) > lla.LLA_NOALLOC_SCRATCH_BYTES
+    assert call(big, B=4096) == lla.LLA_ERR_SCRATCH_LIMIT
+    assert "scratch" in lla.lla_status_string(lla.LLA_ERR_SCRATCH_LIMIT)
