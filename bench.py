@@ -64,6 +64,8 @@ def parse():
                     help="measure only the decode read with the decoupled rotary branch")
     ap.add_argument("--only-long-context", action="store_true",
                     help="measure only the 262k-token absorbed read against reconstruct-then-attend")
+    ap.add_argument("--only-small", action="store_true",
+                    help="measure only the one-layer Ouro-shaped and deep-recurrence decode steps")
     return ap.parse_args()
 
 
@@ -120,6 +122,10 @@ def main():
         return
     if args.only_long_context:
         print(json.dumps({"long_context_262k": long_context(args)}), flush=True)
+        return
+    if args.only_small:
+        print(json.dumps({"ouro_layer": per_head_layer(args, "ouro_layer"),
+                          "deep_loop": per_head_layer(args, "deep_loop")}), flush=True)
         return
     s = synth.CASES[args.workload]
     D = args.layers or s.D
@@ -233,7 +239,9 @@ def main():
     if not args.no_extras and args.workload == "capacity":
         del zk, zv, q, kself, vself, xk, xv, out
         torch.cuda.empty_cache()
-        extras = {"lla2d_decode": lla2d_decode(args), "lla2d_prefill": lla2d_prefill(args),
+        extras = {"ouro_layer": per_head_layer(args, "ouro_layer"),
+                  "deep_loop": per_head_layer(args, "deep_loop"),
+                  "lla2d_decode": lla2d_decode(args), "lla2d_prefill": lla2d_prefill(args),
                   "eviction_decode": eviction_decode(args),
                   "low_bit_capacity": low_bit_capacity(args, tokens_per_s),
                   "long_context_262k": long_context(args),
@@ -297,6 +305,68 @@ def _timed(fn, steps, warmup):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
+
+
+def per_head_layer(args, name):
+    """Decode step of a one-layer per-head workload at full size: T loop reads (each with the
+    token's own loop-t K/V, its own W^K_t/W^V_t), then the encode of the new token into slot N.
+    ouro_layer: H=16, d=128, T=4, r=32/32, B=32, N=4096 (one Ouro-1.4B-shaped layer, 16x);
+    deep_loop: H=40, d=96, T=32, r=96/96, B=64, N=4096 (square 96x96 factors, 32x).
+    read_us is the mean over the step's T reads (HIP events on the launch stream)."""
+    import torch
+    from decode_attention_lla_amd import lla, synth
+    s = synth.CASES[name]
+    B, H, d, T, rk, rv, N = s.B, s.H, s.d, s.T, s.r_k, s.r_v, s.N
+    n_max = N + 1
+    bf = torch.bfloat16
+    desc = lla.make_desc(lla.LLA_PER_HEAD, lla.LLA_BF16, H, d, T, rk, rv, n_max)
+    zk = synth.device_normal_(torch.empty(B, H, n_max, rk, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZK))
+    zv = synth.device_normal_(torch.empty(B, H, n_max, rv, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZV))
+    wk = synth.orthonormal_W(T, H, d, rk, synth.seed(s.case, synth.SEED_WK), "bf16")
+    wv = synth.orthonormal_W(T, H, d, rv, synth.seed(s.case, synth.SEED_WV), "bf16")
+    Wk, Wv = torch.from_numpy(wk).to(bf).cuda(), torch.from_numpy(wv).to(bf).cuda()
+    Ek = torch.from_numpy(synth.pinv_E_from_W(wk, "bf16")).to(bf).cuda()
+    Ev = torch.from_numpy(synth.pinv_E_from_W(wv, "bf16")).to(bf).cuda()
+    q = synth.device_normal_(torch.empty(T, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_Q))
+    ks = synth.device_normal_(torch.empty(T, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF))
+    vs = synth.device_normal_(torch.empty(T, B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF) + 1)
+    x = synth.device_normal_(torch.empty(2, B, 1, T, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_XK))
+    out = torch.empty(T, B, H, d, dtype=bf, device="cuda")
+    lens = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    ws = lla.workspace(desc, B, 1)
+    stream = torch.cuda.current_stream()
+    pairs = []
+
+    def step(record=False):
+        for t in range(T):
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            lla.lla_attend_decode(desc, B, t, q[t], zk, zv, lens, Wk, Wv, None, None, ks[t], vs[t],
+                                  out[t], None, ws, stream)
+            if record:
+                e1 = torch.cuda.Event(enable_timing=True)
+                e1.record(stream)
+                pairs.append((e0, e1))
+        lla.lla_encode(desc, B, 1, x[0], x[1], Ek, Ev, None, None, lens, zk, zv, stream)
+
+    steps = 20 if T <= 4 else 5
+    ms_step = _timed(step, steps, 2)
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms_read = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    latent = B * H * N * (rk + rv) * 2
+    res = {"workload": f"{name}: 1 layer, H={H}, d_head={d}, T={T}, r_k={rk}, r_v={rv}, B={B}, "
+                       f"N={N}, bf16",
+           "tokens_per_s": round(B / (ms_step / 1e3), 1), "ms_per_step": round(ms_step, 4),
+           "read_us": round(ms_read * 1e3, 2),
+           "latent_GBps": round(latent / (ms_read / 1e3) / 1e9, 1),
+           "latent_frac_of_peak": round(latent / (ms_read / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+           "latent_bytes_per_read": latent}
+    del zk, zv, x, q, ks, vs, out, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def lla2d_decode(args):
@@ -649,13 +719,26 @@ def lla2d_prefill(args):
             "encode_mfma_util_bf16_dense": round(enc_flops / (ms_enc / 1e3) / 2.5e15, 4)}
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(args, s, D, zk, zv, Wk, Wv, Ek, Ev, q, kself, vself, xk, xv, lens):
     """The CPU oracle on one sequence's decode step (all layers and loops, then the encodes),
     stopped after about --cpu-seconds and extrapolated to the full step; tokens/s = 1 / step time
     (each step emits one token for this sequence)."""
     from oracle import lla_oracle as O
-    try:
+    affinity = len(os.sched_getaffinity(0))
+    limiter = None
+    try:  # BLAS threads = the CPUs this process may run on
         import threadpoolctl
+        limiter = threadpoolctl.threadpool_limits(limits=affinity, user_api="blas")
         info = threadpoolctl.threadpool_info()
         cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
     except Exception:  # noqa: BLE001
@@ -695,6 +778,8 @@ def cpu_baseline(args, s, D, zk, zv, Wk, Wv, Ek, Ev, q, kself, vself, xk, xv, le
     O.encode_into_cache(zkh, zvh, xkh, xvh, Ek[0].float().cpu().numpy(), Ev[0].float().cpu().numpy(), lens_h)
     enc_time = time.perf_counter() - c0
     step_s = t_read / reads * (T * D) + enc_time * D
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {
         "value": round(1.0 / step_s, 4),
         "unit": "tokens/s",
@@ -704,7 +789,8 @@ def cpu_baseline(args, s, D, zk, zv, Wk, Wv, Ek, Ev, q, kself, vself, xk, xv, le
                   f"float64, {t_read:.1f} s) plus one layer's encode, extrapolated to the full "
                   f"step of one sequence ({step_s:.1f} s per token)",
         "host_cpus": os.cpu_count(),
-        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "affinity_cpus": affinity,
+        "cpu_model": _cpu_model(),
     }
 
 
