@@ -203,6 +203,8 @@ lla_status lla_encode(const lla_desc* desc, int32_t B, int32_t C, const void* xk
                       const void* Ek, const void* Ev, const void* mu_k, const void* mu_v,
                       const int32_t* pos, void* zk, void* zv, void* stream) {
   if (!desc_ok(desc) || B <= 0 || C <= 0) return LLA_ERR_INVALID_ARG;
+  // the encode kernels count tokens (B * C) in 32-bit integers and launch grids from that count
+  if (static_cast<int64_t>(B) * C >= (int64_t(1) << 31)) return LLA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(B) * C * desc->T * desc->H * desc->d_head >= (int64_t(1) << 40))
     return LLA_ERR_INVALID_ARG;
   if (C > desc->n_max) return LLA_ERR_INVALID_ARG;
@@ -256,7 +258,7 @@ lla_status lla_attend_decode(const lla_desc* desc, int32_t B, int32_t t, const v
 
   lla::DecodeParams p = decode_params(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_self,
                                       v_self, out, lse, ws, ws_bytes);
-  lla::decode_plan(*desc, B, &p.splits, &p.chunk);
+  lla::decode_plan(*desc, B, &p.splits, &p.chunk, &p.wg_waves);
   return from_hip(lla::launch_decode(p, desc->dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -286,7 +288,7 @@ lla_status lla_attend_decode_noalloc(const lla_desc* desc, int32_t B, int32_t t,
   if (need > 0 && noalloc_scratch(dev, &ws) != hipSuccess) return LLA_ERR_HIP;
   lla::DecodeParams p = decode_params(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_self,
                                       v_self, out, lse, ws, need > 0 ? LLA_NOALLOC_SCRATCH_BYTES : 0);
-  lla::decode_plan(*desc, B, &p.splits, &p.chunk);
+  lla::decode_plan(*desc, B, &p.splits, &p.chunk, &p.wg_waves);
   return from_hip(lla::launch_decode(p, desc->dtype, s));
 }
 
@@ -337,7 +339,7 @@ lla_status lla_attend_decode_rope(const lla_desc* desc, int32_t B, int32_t t, co
   const float sc = desc->scale > 0.f ? desc->scale
                                      : 1.0f / std::sqrt(static_cast<float>(desc->d_head + d_rope));
   p.scale_log2 = sc * 1.4426950408889634f;
-  lla::decode_plan(*desc, B, &p.splits, &p.chunk);
+  lla::decode_plan(*desc, B, &p.splits, &p.chunk, &p.wg_waves);
   lla::RopeScoreParams rp{};
   rp.q_rope = q_rope;
   rp.k_rope = k_rope;
@@ -447,7 +449,7 @@ lla_status lla_attend_prefill(const lla_desc* desc, int32_t B, int32_t C, int32_
   p.variant = desc->variant;
   p.scale_log2 = scale_log2(desc);
   p.ws_bytes = ws == nullptr ? 0 : ws_bytes;
-  lla::prefill_plan(*desc, B, C, &p.splits, &p.chunk);
+  lla::prefill_plan(*desc, B, C, &p.splits, &p.chunk, &p.wg_waves);
   return from_hip(lla::launch_prefill(p, desc->dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -499,7 +501,7 @@ lla_status lla_attend_prefill_rope(const lla_desc* desc, int32_t B, int32_t C, i
   p.k_rope = k_rope;
   p.d_rope = d_rope;
   p.rope_base = base > 0.f ? base : 10000.0;
-  lla::prefill_plan(*desc, B, C, &p.splits, &p.chunk);
+  lla::prefill_plan(*desc, B, C, &p.splits, &p.chunk, &p.wg_waves);
   return from_hip(lla::launch_prefill(p, desc->dtype, static_cast<hipStream_t>(stream)));
 }
 

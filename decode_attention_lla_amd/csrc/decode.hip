@@ -11,6 +11,7 @@
 //   4. merge lanes, then either write a split partial (m, l, a) or finish: merge the optional
 //      self token, apply W^V_t once, add l * mu^V_t, normalise and store o and lse.
 // The reconstructed K/V of cached tokens are never formed.
+#include <algorithm>
 #include <type_traits>
 
 #include "lla_device.h"
@@ -76,10 +77,20 @@ __device__ void finish_unit(const DecodeParams& p, int b, int h, float M, float 
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   const size_t woff = w_offset(p, h, p.r_v);
   const size_t moff = mu_offset(p, h);
+  constexpr int VE = 16 / S::kBytes;  // values per 16-byte piece of a W^V row
   for (int j = lane; j < p.d; j += 64) {
     float o = 0.f;
     const size_t row = woff + static_cast<size_t>(j) * p.r_v;
-    for (int r = 0; r < p.r_v; ++r) o += ld<S>(p.Wv, row + r) * a_s[r];
+    // rows of r_v values start 16-byte aligned (r_v is a multiple of VE for every compiled pair):
+    // each lane reads its row as whole 16-byte pieces, all issued before the sums
+    const uint4* wr = reinterpret_cast<const uint4*>(static_cast<const char*>(p.Wv) + row * S::kBytes);
+    int r = 0;
+    for (; r + VE <= p.r_v; r += VE) {
+      const uint4 w = wr[r / VE];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) o += frag_elem<S>(&w, e) * a_s[r + e];
+    }
+    for (; r < p.r_v; ++r) o += ld<S>(p.Wv, row + r) * a_s[r];
     if (p.mu_v != nullptr) o += l * ld<S>(p.mu_v, moff + j);
     o *= f_lat;
     if (p.v_self != nullptr) o += p_self * ld<S>(p.v_self, bh * p.d + j);
@@ -117,8 +128,52 @@ __device__ __forceinline__ int slice_entry(int sub, int e) {
   return sub * E + e;
 }
 
+// Waves per workgroup of the streaming kernels (all on one (row, head, split)).
+constexpr int kMaxWaves = 4;
+
+// q~ = scale*log2(e) * W^K_t[h]^T q of one (row, head) into qt_s[RK], by the nw waves of the
+// workgroup (q in q_s). Each lane owns one 16-byte piece of the W^K rows (VE consecutive r) and a
+// residue class of rows j: every load it makes is issued before the sums and the whole slice
+// arrives in about one memory round trip. Lanes sharing a piece add up in registers (DPP), the
+// waves through LDS (red_s [kMaxWaves][RK]).
+template <class S, int RK>
+__device__ __forceinline__ void absorb_query(const DecodeParams& p, int h, int nw, int wave, int lane,
+                                             const float* q_s, float* red_s, float* qt_s) {
+  constexpr int VE = 16 / S::kBytes;
+  constexpr int NRB = RK / VE;  // 16-byte pieces per W^K row
+  static_assert(RK % VE == 0 && NRB <= 64, "W^K rows of whole 16-byte pieces");
+  constexpr int GL = NRB > 32 ? 1 : NRB > 16 ? 2 : NRB > 8 ? 4 : NRB > 4 ? 8 : NRB > 2 ? 16 : NRB > 1 ? 32 : 64;
+  const int rb = lane / GL;
+  const int jg = lane % GL;
+  float acc[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+  if (rb < NRB) {
+    const uint4* wk = reinterpret_cast<const uint4*>(static_cast<const char*>(p.Wk) +
+                                                     w_offset(p, h, RK) * S::kBytes) + rb;
+    for (int j = wave * GL + jg; j < p.d; j += GL * nw) {
+      const uint4 w = wk[static_cast<size_t>(j) * NRB];
+      const float qj = q_s[j];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[e] += frag_elem<S>(&w, e) * qj;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = group_sum<GL>(acc[e]);
+  if (rb < NRB && jg == 0) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) red_s[wave * RK + rb * VE + e] = acc[e];
+  }
+  __syncthreads();
+  for (int r = wave * 64 + lane; r < RK; r += 64 * nw) {
+    float v = 0.f;
+    for (int w = 0; w < nw; ++w) v += red_s[w * RK + r];
+    qt_s[r] = v * p.scale_log2;
+  }
+}
+
 template <class S, class LS, int RK, int RV, int LPT, int U, bool G, bool R = false>
-__global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeParams p) {
   constexpr bool kQ8 = std::is_same<LS, Q8>::value || std::is_same<LS, I8>::value;  // low-bit rows
   constexpr int RKB = LS::row(RK);  // bytes per latent row
   constexpr int RVB = LS::row(RV);
@@ -149,8 +204,14 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   __shared__ float q_s[256];
   __shared__ float qt_s[RK];
   __shared__ float a_s[RV];
+  // the waves' partial sums of q~ (absorb_query), later their (m, l, a) partials (merge below)
+  __shared__ float xs_s[(kMaxWaves * RK > (kMaxWaves - 1) * (2 + RV)) ? kMaxWaves * RK : (kMaxWaves - 1) * (2 + RV)];
 
-  const int lane = threadIdx.x;
+  // nw waves share one (row, head, split): wave w streams the w-th of nw equal parts of the
+  // split's tokens (the gather read keeps one wave: its slot list is staged per wave)
+  const int nw = G ? 1 : min(max(p.wg_waves, 1), kMaxWaves);
+  const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
   const int unit = blockIdx.x;
   const int split = unit % p.splits;
   const int bh = unit / p.splits;
@@ -158,8 +219,9 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   const int b = bh / p.H;
 
   const int nb = G ? gather_keys(p, b) : row_keys(p, b);
-  const int tb = uniform(split * p.chunk);
-  const int te = uniform(min(nb, tb + p.chunk));
+  const int cw = p.chunk / nw;  // the plan keeps chunk a multiple of 128, nw a power of two <= 4
+  const int tb = uniform(split * p.chunk + wave * cw);
+  const int te = uniform(min(nb, min(split * p.chunk + p.chunk, tb + cw)));
 
   // One-load rows stream two register batches ahead. The gather read first stages its split's
   // slot list in LDS (when it fits), so finding a row costs an LDS read rather than a memory round
@@ -180,38 +242,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
       if (k < nsl) sl[k] = buffer_words<4, 0>(rl, static_cast<uint32_t>(k * 64 + lane) * 16);
   }
 
-  // --- 1. query absorption ------------------------------------------------------------------
-  const size_t qoff = static_cast<size_t>(bh) * p.d;
-  for (int j = lane; j < p.d; j += 64) q_s[j] = ld<S>(p.q, qoff + j);
-  __syncthreads();
-  const size_t wk = w_offset(p, h, RK);
-  for (int r = lane; r < RK; r += 64) {
-    float acc = 0.f;
-    for (int j = 0; j < p.d; ++j) acc += ld<S>(p.Wk, wk + static_cast<size_t>(j) * RK + r) * q_s[j];
-    qt_s[r] = acc * p.scale_log2;
-  }
-  float beta = 0.f;
-  if (p.mu_k != nullptr) {
-    const size_t moff = mu_offset(p, h);
-    float part = 0.f;
-    for (int j = lane; j < p.d; j += 64) part += q_s[j] * ld<S>(p.mu_k, moff + j);
-    beta = wave_sum(part) * p.scale_log2;
-  }
-  if constexpr (G && kOne) {
-#pragma unroll
-    for (int k = 0; k < kSlotCap / 256; ++k)
-      if (k < nsl) *reinterpret_cast<uint4*>(&slot_s[(k * 64 + lane) * 4]) = sl[k];
-  }
-  __syncthreads();  // the slot list is visible to every lane from here
-
   const int sub = lane % LPT;
   const int grp = lane / LPT;
-  float qt[EK];
-#pragma unroll
-  for (int e = 0; e < EK; ++e) {
-    const int c = slice_entry<kSplitK, EK, E16, LPT>(sub, e);  // low-bit slots past the codes take a zero query weight
-    qt[e] = (!kQ8 || c < RK) ? qt_s[min(c, RK - 1)] : 0.f;
-  }
   // low-bit slices: the bytes of each of this lane's words that hold codes (padding and the scale
   // must never be converted as codes: a scale byte can be an E4M3 NaN pattern)
   uint32_t kmask[4], vmask[4];
@@ -245,6 +277,35 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   constexpr int NSR = kSrB ? (U + LPT - 1) / LPT : U;  // score registers per batch
   const __amdgpu_buffer_rsrc_t rss =
       buffer_rsrc(R ? p.sr + static_cast<size_t>(bh) * p.sr_stride + row0 : nullptr, R ? nrows * 4 : 0);
+
+  // --- 1. query absorption (prologue): q~ and beta, then (gather read) the slot list in LDS.
+  // The contiguous read issues its first batch of latent loads before it (they do not depend on
+  // q~), so the absorption's memory round trips overlap the stream's first one.
+  float qt[EK];
+  float beta = 0.f;
+  auto prologue = [&]() {
+    const size_t qoff = static_cast<size_t>(bh) * p.d;
+    for (int j = wave * 64 + lane; j < p.d; j += 64 * nw) q_s[j] = ld<S>(p.q, qoff + j);
+    __syncthreads();
+    absorb_query<S, RK>(p, h, nw, wave, lane, q_s, xs_s, qt_s);
+    if (p.mu_k != nullptr) {
+      const size_t moff = mu_offset(p, h);
+      float part = 0.f;
+      for (int j = lane; j < p.d; j += 64) part += q_s[j] * ld<S>(p.mu_k, moff + j);
+      beta = wave_sum(part) * p.scale_log2;
+    }
+    if constexpr (G && kOne) {
+#pragma unroll
+      for (int k = 0; k < kSlotCap / 256; ++k)
+        if (k < nsl) *reinterpret_cast<uint4*>(&slot_s[(k * 64 + lane) * 4]) = sl[k];
+    }
+    __syncthreads();  // q~ and the slot list are visible to every lane from here
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+      const int c = slice_entry<kSplitK, EK, E16, LPT>(sub, e);  // low-bit slots past the codes take a zero query weight
+      qt[e] = (!kQ8 || c < RK) ? qt_s[min(c, RK - 1)] : 0.f;
+    }
+  };
 
   float m = kNegInf;
   float l = 0.f;
@@ -357,7 +418,13 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     uint4 ka[U][VK], va[U][VV], kb[U][VK], vb[U][VV];
     float sa[NSR], sb[NSR];
     bool ok[U];
-    if (tb < te) issue(tb, ka, va, sa);
+    if constexpr (G) {  // the first rows' slots come from the list the prologue stages
+      prologue();
+      if (tb < te) issue(tb, ka, va, sa);
+    } else {
+      if (tb < te) issue(tb, ka, va, sa);
+      prologue();
+    }
     for (int t0 = tb; t0 < te; t0 += 2 * kStep) {
       issue(t0 + kStep, kb, vb, sb);
       mask(t0, ok);
@@ -370,6 +437,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     }
    }
   } else if constexpr (!kPipe) {  // the contiguous one-load read always takes the loop above
+    prologue();
     for (int t0 = tb; t0 < te; t0 += TPW * U) {
       uint4 kr[U][VK];
       uint4 vr[U][VV];
@@ -428,26 +496,60 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     for (int e = 0; e < EV; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
   }
 
+  // --- merge the workgroup's waves: waves 1.. hand (M, l, a) to wave 0 through LDS -----------
+  float Mt = M;
+  if (nw > 1) {
+    __syncthreads();  // every wave is past its last read of xs_s (absorb_query)
+    if (wave > 0) {
+      float* xw = xs_s + (wave - 1) * (2 + RV);
+      if (lane == 0) {
+        xw[0] = M;
+        xw[1] = l;
+      }
+      if (lane < LPT) {
+#pragma unroll
+        for (int e = 0; e < EV; ++e)
+          if (!kQ8 || lane * EV + e < RV) xw[2 + slice_entry<kSplitV, EV, E16, LPT>(lane, e)] = acc[e];
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int w = 1; w < nw; ++w) Mt = fmaxf(Mt, xs_s[(w - 1) * (2 + RV)]);
+      const float f0 = (M == kNegInf) ? 0.f : fast_exp2(M - Mt);
+      l *= f0;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[e] *= f0;
+      for (int w = 1; w < nw; ++w) {
+        const float* xv = xs_s + (w - 1) * (2 + RV);
+        const float fw = (xv[0] == kNegInf) ? 0.f : fast_exp2(xv[0] - Mt);
+        l += fw * xv[1];
+#pragma unroll
+        for (int e = 0; e < EV; ++e)
+          if (!kQ8 || sub * EV + e < RV) acc[e] += fw * xv[2 + slice_entry<kSplitV, EV, E16, LPT>(sub, e)];
+      }
+    }
+  }
+
   if (p.splits > 1) {
     float* w = p.ws + (static_cast<size_t>(bh) * p.splits + split) * (2 + RV);
-    if (lane == 0) {
-      w[0] = M;
+    if (wave == 0 && lane == 0) {
+      w[0] = Mt;
       w[1] = l;
     }
-    if (lane < LPT) {
+    if (wave == 0 && lane < LPT) {
 #pragma unroll
       for (int e = 0; e < EV; ++e)
         if (!kQ8 || lane * EV + e < RV) w[2 + slice_entry<kSplitV, EV, E16, LPT>(lane, e)] = acc[e];
     }
     return;
   }
-  if (lane < LPT) {
+  if (wave == 0 && lane < LPT) {
 #pragma unroll
     for (int e = 0; e < EV; ++e)
       if (!kQ8 || lane * EV + e < RV) a_s[slice_entry<kSplitV, EV, E16, LPT>(lane, e)] = acc[e];
   }
   __syncthreads();
-  finish_unit<S>(p, b, h, M, l, a_s, q_s, lane);
+  if (wave == 0) finish_unit<S>(p, b, h, Mt, l, a_s, q_s, lane);
 }
 
 // Log-sum-exp merge of the S split partials of one (b, h), then the same finish. 256 threads:
@@ -597,31 +699,39 @@ bool decode_uses_mfma2d(const lla_desc& desc) {
   return desc.variant == LLA_2D && decode2d_mfma_supported(desc.dtype, desc.r_k, desc.r_v, desc.d_head);
 }
 
-void valu_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
-  // Few (row, head) units are split so the launch is about 2048 waves: one round for any of these
-  // kernels (all fit 8 waves per CU), each wave keeping two batches of rows in flight. More waves
-  // than fit at once leave a last, partly filled round that streams at a fraction of the bandwidth
-  // (4096 waves at 12 per CU: 410 us for the 262k-token read). No split shorter than 256 tokens.
+void valu_plan(const lla_desc& desc, int B, int* splits, int* chunk, int* wg_waves) {
+  // About 2048 waves per launch: one round for any of these kernels (each wave keeping two
+  // batches of rows in flight). More waves than fit at once leave a last, partly filled round that
+  // streams at a fraction of the bandwidth (4096 waves at 12 per CU: 410 us for the 262k-token
+  // read). Few (row, head) units are therefore cut into parts of at least 256 tokens: first into
+  // up to 4 waves of one workgroup, which merge in LDS (no workspace, no combine launch), then
+  // into token splits merged by the combine kernel.
   const long units = static_cast<long>(B) * desc.H;
   const int target_waves = 2048;
-  int s = static_cast<int>((target_waves + units - 1) / units);
+  int want = static_cast<int>((target_waves + units - 1) / units);
   const int max_by_len = desc.n_max / 256 > 0 ? desc.n_max / 256 : 1;
-  if (s > max_by_len) s = max_by_len;
+  if (want > max_by_len) want = max_by_len;
+  if (want < 1) want = 1;
+  int nw = 1;
+  if (wg_waves != nullptr) nw = want >= 4 ? 4 : want >= 2 ? 2 : 1;
+  int s = (want + nw - 1) / nw;
   if (s > 256) s = 256;  // long contexts at small B*H: up to 256 splits fill the chip
-  if (s < 1) s = 1;
-  // tokens per split, a multiple of 128 so every tile but the last is full
+  // tokens per split, a multiple of 128 so every tile but the last is full (and nw | chunk / 32)
   int c = (desc.n_max + s - 1) / s;
   c = (c + 127) / 128 * 128;
   s = (desc.n_max + c - 1) / c;
   *splits = s;
   *chunk = c;
+  if (wg_waves != nullptr) *wg_waves = nw;
 }
 
-void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
-  if (decode_uses_mfma2d(desc))
+void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk, int* wg_waves) {
+  if (decode_uses_mfma2d(desc)) {
     decode2d_plan(desc, B, splits, chunk);
-  else
-    valu_plan(desc, B, splits, chunk);
+    if (wg_waves != nullptr) *wg_waves = 1;
+  } else {
+    valu_plan(desc, B, splits, chunk, wg_waves);
+  }
 }
 
 size_t decode_workspace_bytes(const lla_desc& desc, int B) {
@@ -644,7 +754,9 @@ hipError_t launch_valu(const DecodeParams& p, int dtype, PartialFn fn, hipStream
       static_cast<size_t>(p.B) * p.H * p.splits * (2 + p.r_v) * sizeof(float) > p.ws_bytes)
     return hipErrorInvalidValue;  // the plan does not fit the workspace: never launch
   const unsigned units = static_cast<unsigned>(p.B) * p.H * p.splits;
-  hipLaunchKernelGGL(fn, dim3(units), dim3(64), 0, stream, p);
+  const int nw = p.slots != nullptr ? 1 : std::min(std::max(p.wg_waves, 1), kMaxWaves);
+  if (p.chunk % (32 * nw) != 0) return hipErrorInvalidValue;  // waves take whole 32-token parts
+  hipLaunchKernelGGL(fn, dim3(units), dim3(64 * nw), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;
   if (dtype == LLA_BF16 || dtype == LLA_BF16_Q8 || dtype == LLA_BF16_I8)
@@ -689,10 +801,12 @@ size_t gather_workspace_bytes(const lla_desc& desc, int B, int budget) {
 }
 
 bool rope_supported(const lla_desc& desc, int d_rope) {
+  if (desc.dtype != LLA_BF16 || !(d_rope == 32 || d_rope == 64 || d_rope == 128)) return false;
+  // the LLA-2D MFMA read takes the branch as extra k-steps of its own contraction
+  if (decode_uses_mfma2d(desc)) return true;
+  // the streaming read's score pre-pass holds every head's rotated query in LDS
   const Entry* e = find(desc.dtype, desc.r_k, desc.r_v);
-  return desc.dtype == LLA_BF16 && e != nullptr && e->rfn != nullptr &&
-         (d_rope == 32 || d_rope == 64 || d_rope == 128) &&
-         static_cast<long>(desc.H) * d_rope * 4 <= 64 * 1024;
+  return e != nullptr && e->rfn != nullptr && static_cast<long>(desc.H) * d_rope * 4 <= 64 * 1024;
 }
 
 namespace {

@@ -31,6 +31,9 @@ struct DecodeParams {
   int32_t variant;    // LLA_PER_HEAD or LLA_2D
   int32_t splits;     // S: token-range splits per (b, h), from decode_plan / prefill_plan
   int32_t chunk;      // tokens per split
+  // Waves of one workgroup that share a (row, head, split): each takes chunk / wg_waves of the
+  // split's tokens and the partials merge in LDS (streaming kernels; 0 or 1: one wave).
+  int32_t wg_waves;
   float scale_log2;   // softmax scale * log2(e)
   size_t ws_bytes;    // bytes available at ws; launchers refuse a plan that does not fit
   // Rotary branch of the streaming read (lla_attend_decode_rope): base-2 rotary scores added to
@@ -118,6 +121,7 @@ struct PrefillParams {
   void* ws;
   int32_t B, C, H, d, T, t, n_max, r_k, r_v, variant;
   int32_t splits, chunk;  // from prefill_plan
+  int32_t wg_waves;       // streaming path: waves per (row, head, split), from prefill_plan
   float scale_log2;
   size_t ws_bytes;
   // Rotary branch (lla_attend_prefill_rope; d_rope == 0 without it): q_rope [B][C][H][d_rope]
@@ -130,9 +134,10 @@ struct PrefillParams {
 
 // Token-split plan of one lla_attend_decode call. The C ABI computes it once per call, sizes the
 // workspace from it and hands it to the launchers, which never re-plan.
-void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk);
-void valu_plan(const lla_desc& desc, int rows, int* splits, int* chunk);
-void prefill_plan(const lla_desc& desc, int B, int C, int* splits, int* chunk);
+// wg_waves (optional): waves per workgroup of the streaming kernels; without it the plan uses one.
+void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk, int* wg_waves = nullptr);
+void valu_plan(const lla_desc& desc, int rows, int* splits, int* chunk, int* wg_waves = nullptr);
+void prefill_plan(const lla_desc& desc, int B, int C, int* splits, int* chunk, int* wg_waves = nullptr);
 // Workspace of one lla_attend_decode call under decode_plan.
 size_t decode_workspace_bytes(const lla_desc& desc, int B);
 // Workspace of the streaming decode kernels for `rows` query rows and a given split count.
@@ -165,7 +170,7 @@ hipError_t launch_decode_rope(const DecodeParams& p, const RopeScoreParams& rp, 
                               hipStream_t s);
 // Reconstruct-then-attend comparator (reconstruct.hip).
 bool reconstruct_supported(const lla_desc& desc);
-void reconstruct_plan(const lla_desc& desc, int B, int* splits, int* chunk);
+void reconstruct_plan(const lla_desc& desc, int B, int* splits, int* chunk, int* wg_waves = nullptr);
 size_t reconstruct_workspace_bytes(const lla_desc& desc, int B);
 hipError_t launch_decode_reconstruct(const DecodeParams& p, const lla_desc& desc, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, hipStream_t s);

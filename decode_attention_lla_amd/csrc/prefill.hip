@@ -602,13 +602,14 @@ bool prefill_supported(int variant, int dtype, int r_k, int r_v) {
   return valu_supported(variant, dtype, r_k, r_v) || (dtype == LLA_BF16 && findP(r_k, r_v) != nullptr);
 }
 
-void prefill_plan(const lla_desc& desc, int B, int C, int* splits, int* chunk) {
+void prefill_plan(const lla_desc& desc, int B, int C, int* splits, int* chunk, int* wg_waves) {
   if (mfma_prefill(desc.dtype, desc.r_k, desc.r_v, desc.d_head, desc.n_max)) {
     *splits = 1;
     *chunk = desc.n_max;
+    if (wg_waves != nullptr) *wg_waves = 1;
     return;
   }
-  valu_plan(desc, B * C, splits, chunk);
+  valu_plan(desc, B * C, splits, chunk, wg_waves);
 }
 
 size_t prefill_workspace_bytes(const lla_desc& desc, int B, int C) {
@@ -658,6 +659,7 @@ hipError_t launch_prefill(const PrefillParams& pp, int dtype, hipStream_t stream
   p.scale_log2 = pp.scale_log2;
   p.splits = pp.splits;  // planned by the caller with prefill_plan
   p.chunk = pp.chunk;
+  p.wg_waves = pp.wg_waves;
   p.ws_bytes = pp.ws_bytes;
   return launch_decode(p, dtype, stream);
 }

@@ -204,8 +204,8 @@ bool reconstruct_supported(const lla_desc& desc) {
          desc.r_k <= kMaxR && desc.r_v <= kMaxR;
 }
 
-void reconstruct_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
-  valu_plan(attend_desc(desc), B, splits, chunk);
+void reconstruct_plan(const lla_desc& desc, int B, int* splits, int* chunk, int* wg_waves) {
+  valu_plan(attend_desc(desc), B, splits, chunk, wg_waves);
 }
 
 size_t reconstruct_workspace_bytes(const lla_desc& desc, int B) {
@@ -261,7 +261,7 @@ hipError_t launch_decode_reconstruct(const DecodeParams& p, const lla_desc& desc
   a.t = 0;
   a.ws = w.partials;
   a.ws_bytes = w.partial_bytes;
-  reconstruct_plan(desc, p.B, &a.splits, &a.chunk);
+  reconstruct_plan(desc, p.B, &a.splits, &a.chunk, &a.wg_waves);
   return launch_decode(a, LLA_BF16, stream);
 }
 

@@ -221,8 +221,9 @@ size_t lla_rope_workspace_bytes(const lla_desc* desc, int32_t B);
  *   q_rope [device] bf16 [B][H][d_rope], unrotated; k_rope_self [device] bf16 [B][d_rope], given
  *   exactly when k_self is; ws at least lla_rope_workspace_bytes(desc, B).
  * The rotary scores of all heads are formed once per read (each rotary key read once) and added to
- * the streamed latent scores. LLA_BF16, d_rope 32, 64 or 128, H * d_rope <= 16384, the streaming
- * bf16 (r_k, r_v) pairs, both variants; otherwise LLA_ERR_UNSUPPORTED. */
+ * the streamed latent scores; the LLA-2D MFMA read forms them in its own contraction instead.
+ * LLA_BF16, d_rope 32, 64 or 128, the streaming bf16 (r_k, r_v) pairs with H * d_rope <= 16384
+ * (both variants), or the LLA-2D MFMA pairs at any H; otherwise LLA_ERR_UNSUPPORTED. */
 lla_status lla_attend_decode_rope(const lla_desc* desc, int32_t B, int32_t t, const void* q,
                                   const void* q_rope, const void* zk, const void* zv,
                                   const void* k_rope, int32_t d_rope, float base,

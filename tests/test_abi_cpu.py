@@ -119,6 +119,9 @@ def test_encode_rejects_bad_arguments():
     assert encode(d, xk=M) == lla.LLA_ERR_INVALID_ARG
     assert encode(d, muk=M) == lla.LLA_ERR_INVALID_ARG
     assert encode(d, zv=N) == lla.LLA_ERR_INVALID_ARG
+    # B * C tokens are counted in 32-bit integers by the encode kernels: 2^31 of them are refused
+    small = desc(H=1, d_head=8, T=1, r_k=8, r_v=8, n_max=1024)
+    assert encode(small, B=2 ** 21, C=1024) == lla.LLA_ERR_INVALID_ARG
 
 
 def test_prefill_rejects_bad_arguments():
@@ -303,6 +306,12 @@ def test_rope_arguments_support_and_workspace():
     assert rope_decode(desc(r_k=24, r_v=24, n_max=100, dtype=lla.LLA_F32)) == lla.LLA_ERR_UNSUPPORTED
     assert rope_decode(desc(r_k=64, r_v=128, n_max=100)) == lla.LLA_ERR_UNSUPPORTED
     assert rope_decode(desc(r_k=24, r_v=24, n_max=100, H=200), d_rope=128) == lla.LLA_ERR_UNSUPPORTED
+    # the LLA-2D MFMA read fuses the branch and has no per-head LDS cap: H * d_rope > 16384 is
+    # accepted (the call then stops at the workspace check)
+    big2d = desc(variant=lla.LLA_2D, r_k=64, r_v=64, d_head=32, n_max=100, H=200)
+    assert rope_decode(big2d, d_rope=128) == lla.LLA_ERR_WORKSPACE
+    assert rope_decode(desc(variant=lla.LLA_2D, r_k=32, r_v=32, d_head=32, n_max=100, H=200),
+                       d_rope=128) == lla.LLA_ERR_UNSUPPORTED  # LLA-2D on the streaming read
     need = lla.lla_rope_workspace_bytes(d, 2)
     assert need >= 2 * 16 * 100 * 4  # rotary scores of every (b, h, slot)
     assert rope_decode(d) == lla.LLA_ERR_WORKSPACE

@@ -61,16 +61,18 @@ def _row_check(got, ref, what):
 # decode: the last visible key, split and tile edges, and the first key past the end
 # --------------------------------------------------------------------------------------------
 
-# streaming read: splits of a multiple of 128 tokens (here 384), tiles of 8 to 64 rows; LLA-2D MFMA
-# read: splits of a multiple of 64 tokens (here 320), 16-token tiles
-DEC_LENS = [1, 2, 16, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 320, 321, 383, 384, 385, 511,
-            512, 640, 641, 767, 768, 769, 960, 961, 1099, 1100]
-DEC_EDGES = [0, 1, 15, 16, 63, 64, 127, 128, 255, 256, 319, 320, 383, 384, 511, 512, 639, 640, 767,
-             768, 959, 960]
+# Token ranges of the reads start at multiples of 32 (streaming read: splits of a multiple of 128
+# tokens cut into up to 4 per-wave parts, tiles of 8 to 64 rows; LLA-2D MFMA read: splits of a
+# multiple of 64 tokens, 16-token tiles), so lengths and marked keys sit at and beside every
+# multiple of 32 up to the cache size.
+N_MAX_DEC = 1100
+DEC_LENS = sorted({1, 2, 15, 16, 17, N_MAX_DEC - 1, N_MAX_DEC} |
+                  {32 * k + e for k in range(1, 35) for e in (0, 1)})
+DEC_EDGES = sorted({0, 1, 15, 16} | {32 * k + e for k in range(1, 35) for e in (-1, 0)})
 
 
 def _decode_case(variant, rk, rv, H, seed):
-    d, T, t, n_max = 64, 2, 1, 1100
+    d, T, t, n_max = 64, 2, 1, N_MAX_DEC
     B = len(DEC_LENS)
     c = synth.random_case(variant, "bf16", B, H, d, T, rk, rv, n_max, seed, with_mu=False,
                           with_self=False)
@@ -78,14 +80,20 @@ def _decode_case(variant, rk, rv, H, seed):
     zk, zv = c["zk"], c["zv"]
     g = np.random.default_rng(seed + 1)
     marks = {}
+    turn = 0
     for b, n in enumerate(DEC_LENS):
         heads = range(H) if variant == "per_head" else [b % H]
         for h in heads:
             qt = _w_head(c["Wk"], t, h, d, variant).astype(np.float64).T @ c["q"][t][b, h].astype(np.float64)
-            # the marked key: the last visible one for even (b + h), else the furthest split or
-            # tile edge inside the row
+            # the marked key: the row's last visible key (head 0 of a per-head row, even rows of
+            # LLA-2D), else the next edge inside the row in turn
             inner = [e for e in DEC_EDGES if e < n - 1]
-            m = n - 1 if (b + h) % 2 == 0 or not inner else inner[-1]
+            last = (h == 0) if variant == "per_head" else (b % 2 == 0)
+            if last or not inner:
+                m = n - 1
+            else:
+                m = inner[turn % len(inner)]
+                turn += 1
             kz = zk[b, h] if variant == "per_head" else zk[b]
             vz = zv[b, h] if variant == "per_head" else zv[b]
             others = np.delete(np.arange(n), m)
@@ -100,8 +108,8 @@ def _decode_case(variant, rk, rv, H, seed):
 
 
 @pytest.mark.parametrize("variant,rk,rv,H", [
-    ("per_head", 8, 8, 2), ("per_head", 24, 24, 2), ("per_head", 32, 32, 2), ("per_head", 96, 96, 2),
-    ("per_head", 96, 160, 2), ("per_head", 256, 256, 2),
+    ("per_head", 8, 8, 4), ("per_head", 24, 24, 4), ("per_head", 32, 32, 4), ("per_head", 96, 96, 4),
+    ("per_head", 96, 160, 4), ("per_head", 256, 256, 4),
     ("2d", 32, 32, 3),                                           # LLA-2D on the streaming read
     ("2d", 64, 64, 20), ("2d", 128, 128, 16), ("2d", 256, 256, 16),  # LLA-2D on MFMA
 ])

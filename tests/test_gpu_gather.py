@@ -12,7 +12,7 @@ import torch
 
 from decode_attention_lla_amd import lla, synth
 from oracle import lla_oracle as O
-from tests.gpu_util import assert_close, assert_lse, dev, host, require_gpu
+from tests.gpu_util import assert_close, assert_lse, dev, host, rel_err, require_gpu
 from tests.test_gpu_parity import _fill_device_case, mk_desc, upload
 
 pytestmark = pytest.mark.gpu
@@ -89,8 +89,10 @@ def test_gather_short_lists_null_counts_and_empty_rows():
 
 
 def test_gather_identity_list_matches_contiguous_read():
-    """A list 0 .. n_max-1 with counts = lengths is the contiguous read, planned the same way:
-    the two entry points must give identical bits."""
+    """A list 0 .. n_max-1 with counts = lengths reads exactly the contiguous read's keys. The two
+    entry points agree to rounding: the contiguous read may cut a row's tokens among the waves of
+    one workgroup while the gather read keeps one wave per split, so the sums run in another order
+    (o within one bf16 step, lse within 1e-6)."""
     dtype = "bf16"
     B, H, d, T, n_max = 3, 4, 128, 2, 2000
     desc = mk_desc("per_head", dtype, H, d, T, 24, 24, n_max)
@@ -108,7 +110,8 @@ def test_gather_identity_list_matches_contiguous_read():
                                  c["_Wk"], c["_Wv"], c["_muk"], c["_muv"], ks, vs, o2, l2,
                                  lla.gather_workspace(desc, B, n_max))
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert rel_err(host(o1), host(o2)) <= 2.0 ** -8
+    np.testing.assert_allclose(host(l1), host(l2), rtol=1e-6, atol=1e-6)
     ro, rl = oracle_gather(c, 1, slots, lens, "per_head")
     assert_close(host(o2), ro, dtype)
     assert_lse(host(l2), rl)

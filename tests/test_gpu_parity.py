@@ -106,8 +106,8 @@ def test_decode_sweep_2d(dtype, rk, rv):
 def test_decode_batch_and_split_boundaries(dtype, rk, rv):
     """Sequence lengths just below, at and above multiples of the streaming kernel's batch
     (64/lanes-per-token tokens per tile, several tiles per batch, two batches in flight) and of
-    the token split (two splits of 384 at n_max = 700), so every partly and wholly empty batch,
-    and a split that ends inside one, is exercised."""
+    the per-wave token range (two waves of 384 tokens at n_max = 700, merged in LDS), so every
+    partly and wholly empty batch, and a wave's range that ends inside one, is exercised."""
     H, d, T, n_max = 2, 64, 2, 700
     lens = [1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 384, 385, 511, 512,
             513, 640, 699, 700]

@@ -11,7 +11,7 @@ import torch
 
 from decode_attention_lla_amd import lla, synth
 from oracle import lla_oracle as O
-from tests.gpu_util import assert_close, assert_lse, dev, host, require_gpu
+from tests.gpu_util import assert_close, assert_lse, dev, host, mfma_lse_slack, require_gpu
 from tests.test_gpu_parity import _fill_device_case, mk_desc, upload
 
 pytestmark = pytest.mark.gpu
@@ -95,6 +95,34 @@ def test_decode_rope(variant, rk, rv, d_rope):
             what = f"rope {variant} r=({rk},{rv}) d_rope={d_rope} gain={gain} mu={mu} self={self_token} t={t}"
             assert_close(host(out), ro, "bf16", what)
             assert_lse(host(lse), rl, what)
+
+
+def test_lla2d_decode_rope_many_heads():
+    """LLA-2D on MFMA with H * d_rope above the streaming pre-pass's LDS cap (H = 144, d_rope =
+    128): the branch is fused into the MFMA read, so the call is accepted and matches the oracle
+    (nine 16-head groups, ragged lengths, self token, mu)."""
+    B, H, d, T, n_max, r, d_rope = 3, 144, 32, 2, 700, 64, 128
+    lens = np.array([700, 333, 1], np.int32)
+    desc = mk_desc("2d", "bf16", H, d, T, r, r, n_max)
+    ws = lla.rope_workspace(desc, B)
+    rng = np.random.default_rng(9990)
+    q_rope, k_rope, krs = _rope_inputs(rng, B, H, n_max, d_rope)
+    c = upload(synth.random_case("2d", "bf16", B, H, d, T, r, r, n_max, 9991), "bf16")
+    t = 1
+    q = dev(c["q"][t], "bf16")
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H, device="cuda")
+    lla.lla_attend_decode_rope(desc, B, t, q, dev(q_rope, "bf16"), c["_zk"], c["_zv"],
+                               dev(k_rope, "bf16"), d_rope, 0.0, dev(lens), c["_Wk"], c["_Wv"],
+                               c["_muk"], c["_muv"], dev(c["k_self"][t], "bf16"),
+                               dev(c["v_self"][t], "bf16"), dev(krs, "bf16"), out, lse, ws)
+    torch.cuda.synchronize()
+    ro, rl = O.attend_decode_rope(c["q"][t], q_rope, c["zk"], c["zv"], k_rope, c["Wk"], c["Wv"], t,
+                                  lens, c["mu_k"], c["mu_v"], c["k_self"][t], c["v_self"][t], krs,
+                                  variant="2d")
+    assert_close(host(out), ro, "bf16", "2d rope H=144")
+    slack = mfma_lse_slack(c["q"][t], c["zk"], c["Wk"], t, lens, q_rope=q_rope, k_rope=k_rope)
+    assert_lse(host(lse), rl, "2d rope H=144", slack)
 
 
 def test_decode_rope_many_units_ragged():
