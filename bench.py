@@ -557,9 +557,9 @@ def low_bit_capacity(args, bf16_tokens_per_s):
 def rope_decode(args):
     """The decoupled rotary branch (d_rope=64, one rotary key per token shared by heads and loops)
     on two decode reads, each beside the same read without the branch: the capacity layer (per
-    head, B=768, H=16, d=128, r=24/24, 4096 cached tokens; rotary score pre-pass + streaming read)
-    and the LLA-2D layer (B=128, H=16, d=128, r=256/256, 8192 cached tokens; the rotary keys are
-    extra MFMA k-steps of the read)."""
+    head, B=768, H=16, d=128, r=24/24, 4096 cached tokens; the streaming read dots each token's
+    rotary key in the token's lane group) and the LLA-2D layer (B=128, H=16, d=128, r=256/256,
+    8192 cached tokens; the rotary keys are extra MFMA k-steps of the read)."""
     import torch
     from decode_attention_lla_amd import lla, synth
     d_rope = 64
@@ -599,9 +599,9 @@ def rope_decode(args):
         ms_p = _timed(plain, 20, 3)
         ms_r = _timed(with_rope, 20, 3)
         latent = B * (1 if two_d else H) * N * 2 * r * 2
-        # rotary keys once; the streaming read also writes and reads every head's rotary scores
-        # (the LLA-2D MFMA read forms them in its own accumulators)
-        extra = B * N * d_rope * 2 + (0 if two_d else 2 * B * H * N * 4)
+        # the rotary keys, once per sequence (both reads form the rotary scores inside the read;
+        # the heads of a sequence share its keys through L2)
+        extra = B * N * d_rope * 2
         name = "lla2d" if two_d else "capacity"
         res[name] = {
             "workload": f"{'LLA-2D' if two_d else 'capacity'} layer read with a {d_rope}-wide rotary "

@@ -332,7 +332,7 @@ lla_status lla_attend_decode_rope(const lla_desc* desc, int32_t B, int32_t t, co
   if (!(base >= 0.f) || std::isinf(base)) return LLA_ERR_INVALID_ARG;
   if (!lla::rope_supported(*desc, d_rope)) return LLA_ERR_UNSUPPORTED;
   const size_t need = lla::rope_workspace_bytes(*desc, B);
-  if (ws == nullptr || ws_bytes < need) return LLA_ERR_WORKSPACE;
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return LLA_ERR_WORKSPACE;
   lla::DecodeParams p = decode_params(desc, B, t, q, zk, zv, seq_lens, Wk, Wv, mu_k, mu_v, k_self,
                                       v_self, out, lse, ws, ws_bytes);
   // the concatenated (content, rotary) key is d_head + d_rope wide
@@ -340,18 +340,12 @@ lla_status lla_attend_decode_rope(const lla_desc* desc, int32_t B, int32_t t, co
                                      : 1.0f / std::sqrt(static_cast<float>(desc->d_head + d_rope));
   p.scale_log2 = sc * 1.4426950408889634f;
   lla::decode_plan(*desc, B, &p.splits, &p.chunk, &p.wg_waves);
-  lla::RopeScoreParams rp{};
-  rp.q_rope = q_rope;
-  rp.k_rope = k_rope;
-  rp.k_rope_self = k_rope_self;
-  rp.seq_lens = seq_lens;
-  rp.B = B;
-  rp.H = desc->H;
-  rp.n_max = desc->n_max;
-  rp.d_r = d_rope;
-  rp.scale_log2 = p.scale_log2;
-  rp.base = base > 0.f ? base : 10000.0;
-  return from_hip(lla::launch_decode_rope(p, rp, desc->dtype, static_cast<hipStream_t>(stream)));
+  p.q_rope = q_rope;
+  p.k_rope = k_rope;
+  p.k_rope_self = k_rope_self;
+  p.d_rope = d_rope;
+  p.rope_base = base > 0.f ? base : 10000.0;
+  return from_hip(lla::launch_decode_rope(p, desc->dtype, static_cast<hipStream_t>(stream)));
 }
 
 size_t lla_reconstruct_workspace_bytes(const lla_desc* desc, int32_t B) {

@@ -67,8 +67,14 @@ __device__ void finish_unit(const DecodeParams& p, int b, int h, float M, float 
   if (p.k_self != nullptr) {
     float part = 0.f;
     for (int j = lane; j < p.d; j += 64) part += q_s[j] * ld<S>(p.k_self, bh * p.d + j);
+    // decoupled rotary branch: the self key's rotary part, q_rope . k_rope_self (both would be
+    // rotated at the same position N_b, which leaves their dot product unchanged)
+    if (p.d_rope > 0 && p.k_rope_self != nullptr) {
+      const size_t seq = static_cast<size_t>(b) / p.rows_per_seq;
+      for (int j = lane; j < p.d_rope; j += 64)
+        part += ld<BF16>(p.q_rope, bh * p.d_rope + j) * ld<BF16>(p.k_rope_self, seq * p.d_rope + j);
+    }
     s_self = wave_sum(part) * p.scale_log2;
-    if (p.sr_self != nullptr) s_self += p.sr_self[bh];  // the self token's rotary score
   }
   const float M2 = fmaxf(M, s_self);
   const float f_lat = (M == kNegInf) ? 0.f : fast_exp2(M - M2);
@@ -105,8 +111,11 @@ __device__ void finish_unit(const DecodeParams& p, int b, int h, float M, float 
 // split ranges over the row's slot list instead of its first N latents: each token's slot is read
 // first, and a slot outside [0, n_max) counts as masked. S is the storage of q, W, mu, the self
 // token and out; LS that of the latent rows (S itself, or Q8 low-bit rows read whole by one lane:
-// the K row scale multiplies the score, the V row scale the token's weight). With R each token's
-// score also gets its precomputed base-2 rotary score p.sr[bh][slot] (decoupled RoPE branch).
+// the K row scale multiplies the score, the V row scale the token's weight). With DR > 0 each
+// token's score also gets its rotary part q_R . k_R (decoupled RoPE branch): q_R (the head's
+// rotary query, rotated at the decoding position, scaled) is formed in the prologue, and each
+// token's DR-wide rotary key, shared by every head of the sequence, is streamed beside its latent
+// rows and dotted in the same lane group.
 // A lane's S-byte row slice (whole words, S <= 32) of the row at byte offset row of a raw buffer,
 // for lane sub of the LPT lanes that share the row. Up to 16 bytes: one load at S*sub. Longer
 // slices are split: the first 16 bytes at 16*sub (into f[0]), the rest at 16*LPT + (S-16)*sub
@@ -129,7 +138,7 @@ __device__ __forceinline__ int slice_entry(int sub, int e) {
 }
 
 // Waves per workgroup of the streaming kernels (all on one (row, head, split)).
-constexpr int kMaxWaves = 4;
+constexpr int kMaxWaves = 8;
 
 // q~ = scale*log2(e) * W^K_t[h]^T q of one (row, head) into qt_s[RK], by the nw waves of the
 // workgroup (q in q_s). Each lane owns one 16-byte piece of the W^K rows (VE consecutive r) and a
@@ -172,8 +181,11 @@ __device__ __forceinline__ void absorb_query(const DecodeParams& p, int h, int n
   }
 }
 
-template <class S, class LS, int RK, int RV, int LPT, int U, bool G, bool R = false>
+template <class S, class LS, int RK, int RV, int LPT, int U, bool G, int DR = 0>
 __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeParams p) {
+  constexpr bool R = DR > 0;
+  constexpr int RPC = R ? DR / 8 : 1;          // 16-byte pieces of a rotary key row
+  constexpr int NRP = (RPC + LPT - 1) / LPT;   // pieces per lane (piece sub + LPT * k)
   constexpr bool kQ8 = std::is_same<LS, Q8>::value || std::is_same<LS, I8>::value;  // low-bit rows
   constexpr int RKB = LS::row(RK);  // bytes per latent row
   constexpr int RVB = LS::row(RV);
@@ -203,6 +215,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
 
   __shared__ float q_s[256];
   __shared__ float qt_s[RK];
+  __shared__ float qr_s[R ? DR : 1];  // rotated rotary query times scale * log2(e)
   __shared__ float a_s[RV];
   // the waves' partial sums of q~ (absorb_query), later their (m, l, a) partials (merge below)
   __shared__ float xs_s[(kMaxWaves * RK > (kMaxWaves - 1) * (2 + RV)) ? kMaxWaves * RK : (kMaxWaves - 1) * (2 + RV)];
@@ -212,21 +225,30 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   const int nw = G ? 1 : min(max(p.wg_waves, 1), kMaxWaves);
   const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x;
+  // Sequences whose heads share what they stream (the rotary keys; LLA-2D: the latents too) keep
+  // all their workgroups on one XCD when B is a multiple of 8: workgroups are dispatched round-
+  // robin over the 8 XCDs, so unit (x % 8) + 8 * k runs on XCD x % 8, and consecutive k there
+  // are the heads and splits of one sequence, co-resident and sharing that XCD's L2.
+  int unit = blockIdx.x;
+  if ((R || p.variant == LLA_2D) && (p.B & 7) == 0) {
+    const int per = p.H * p.splits;  // units of one row
+    const int k = unit >> 3;
+    unit = ((k / per) * 8 + (unit & 7)) * per + k % per;
+  }
   const int split = unit % p.splits;
   const int bh = unit / p.splits;
   const int h = bh % p.H;
   const int b = bh / p.H;
 
   const int nb = G ? gather_keys(p, b) : row_keys(p, b);
-  const int cw = p.chunk / nw;  // the plan keeps chunk a multiple of 128, nw a power of two <= 4
+  const int cw = p.chunk / nw;  // the plan keeps chunk a multiple of 32 * nw
   const int tb = uniform(split * p.chunk + wave * cw);
   const int te = uniform(min(nb, min(split * p.chunk + p.chunk, tb + cw)));
 
   // One-load rows stream two register batches ahead. The gather read first stages its split's
   // slot list in LDS (when it fits), so finding a row costs an LDS read rather than a memory round
   // trip in front of every batch; longer splits take the one-batch loop below.
-  static_assert(!(G && R), "the rotary scores are read for contiguous rows only");
+  static_assert(!(G && R), "the rotary branch is read for contiguous rows only");
   constexpr int kSlotCap = 2048;
   __shared__ __attribute__((aligned(16))) int32_t slot_s[G ? kSlotCap : 4];
   const int32_t* srow = G ? p.slots + static_cast<size_t>(b) * p.budget : nullptr;
@@ -270,18 +292,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   // rows reads ~5% slower than with ordinary loads.
   constexpr int kAux = 2;
   constexpr bool kPipe = kOne && !G;  // the contiguous buffer-load read (always two batches ahead)
-  // Rotary scores (R). With at most 4 lanes per token the pipelined path loads them once per batch:
-  // lane `sub` of a group loads tile sub + LPT*k's score (one load covers 64 consecutive tokens)
-  // and each tile's score is broadcast inside the group (DPP) when the tile is consumed.
-  constexpr bool kSrB = kPipe && LPT <= 4;
-  constexpr int NSR = kSrB ? (U + LPT - 1) / LPT : U;  // score registers per batch
-  const __amdgpu_buffer_rsrc_t rss =
-      buffer_rsrc(R ? p.sr + static_cast<size_t>(bh) * p.sr_stride + row0 : nullptr, R ? nrows * 4 : 0);
+  // Rotary keys (R): [B][n_max][DR] bf16, one row per token shared by every head of the sequence.
+  // Lane `sub` of a token's group holds pieces sub + LPT * k of the row (16 bytes each); ordinary
+  // loads, so the row stays in L2 for the sequence's other heads.
+  static_assert(!R || kPipe, "the rotary branch takes the pipelined contiguous read");
+  constexpr int NSR = R ? NRP : 1;
+  const __amdgpu_buffer_rsrc_t rss = buffer_rsrc(
+      R ? static_cast<const char*>(p.k_rope) + (static_cast<size_t>(b / p.rows_per_seq) * p.n_max + row0) * DR * 2 : nullptr,
+      R ? nrows * DR * 2 : 0);
 
   // --- 1. query absorption (prologue): q~ and beta, then (gather read) the slot list in LDS.
   // The contiguous read issues its first batch of latent loads before it (they do not depend on
   // q~), so the absorption's memory round trips overlap the stream's first one.
   float qt[EK];
+  float qr[NRP][R ? 8 : 1];
   float beta = 0.f;
   auto prologue = [&]() {
     const size_t qoff = static_cast<size_t>(bh) * p.d;
@@ -299,11 +323,30 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
       for (int k = 0; k < kSlotCap / 256; ++k)
         if (k < nsl) *reinterpret_cast<uint4*>(&slot_s[(k * 64 + lane) * 4]) = sl[k];
     }
+    if constexpr (R) {  // rotary query of this head rotated at the decoding position N_b
+      const size_t qro = static_cast<size_t>(bh) * DR;
+      for (int i = wave * 64 + lane; i < DR / 2; i += 64 * nw) {
+        float y0, y1;
+        rotate_pair(ld<BF16>(p.q_rope, qro + 2 * i), ld<BF16>(p.q_rope, qro + 2 * i + 1), i, DR, nb,
+                    p.rope_base, &y0, &y1);
+        qr_s[2 * i] = y0 * p.scale_log2;
+        qr_s[2 * i + 1] = y1 * p.scale_log2;
+      }
+    }
     __syncthreads();  // q~ and the slot list are visible to every lane from here
 #pragma unroll
     for (int e = 0; e < EK; ++e) {
       const int c = slice_entry<kSplitK, EK, E16, LPT>(sub, e);  // low-bit slots past the codes take a zero query weight
       qt[e] = (!kQ8 || c < RK) ? qt_s[min(c, RK - 1)] : 0.f;
+    }
+    if constexpr (R) {
+#pragma unroll
+      for (int k = 0; k < NRP; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = sub + LPT * k;
+          qr[k][e] = c < RPC ? qr_s[c * 8 + e] : 0.f;
+        }
     }
   };
 
@@ -314,7 +357,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   for (int e = 0; e < EV; ++e) acc[e] = 0.f;
 
   // fold one batch of U tiles (ok: token inside the split and valid) into (m, l, acc)
-  auto consume = [&](uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], const bool (&ok)[U], const float (&srv)[NSR]) {
+  auto consume = [&](uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], const bool (&ok)[U], uint4 (&srv)[U][NSR]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float sk = 1.f, sv = 1.f;  // low-bit row scales
@@ -342,19 +385,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
 #pragma unroll
       for (int e = 0; e < EK; ++e)
         if (!kQ8 || kOne || e < RK) sc += qt[e] * frag_elem<LS>(kr[u], e);
+      if constexpr (R) {  // this lane's pieces of the token's rotary key
+#pragma unroll
+        for (int k = 0; k < NRP; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc += qr[k][e] * frag_elem<BF16>(&srv[u][k], e);
+      }
       sc = group_sum<LPT>(sc);
       if (kQ8) sc *= sk;
       sc += beta;
-      if constexpr (R) {
-        if constexpr (kSrB && LPT == 2) {
-          sc += u % 2 == 0 ? dpp_f32<0xa0>(srv[u / 2]) : dpp_f32<0xf5>(srv[u / 2]);  // quad_perm(0,0,2,2) / (1,1,3,3)
-        } else if constexpr (kSrB && LPT == 4) {
-          const float x = srv[u / 4];  // quad_perm(s,s,s,s), s = u % 4 (a constant once unrolled)
-          sc += u % 4 == 0 ? dpp_f32<0x00>(x) : u % 4 == 1 ? dpp_f32<0x55>(x) : u % 4 == 2 ? dpp_f32<0xaa>(x) : dpp_f32<0xff>(x);
-        } else {
-          sc += srv[u];
-        }
-      }
       if (ok[u]) {
         if (sc > m + kLazy) {
           const float c = fast_exp2(m - sc);
@@ -379,18 +418,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
     // consumed, so a wave always has a batch in flight. Rows past the split (or, gathered, with
     // a slot outside the cache) read as zeros through the descriptor bound (no memory access)
     // and are masked; a batch wholly past the split costs only its masked arithmetic.
-    auto issue = [&](int t0, uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], float (&srv)[NSR]) {
-#pragma unroll
-      for (int k = 0; k < NSR; ++k) {
-        if constexpr (R) {
-          const int tile = kSrB ? sub + LPT * k : k;
-          const int tok = t0 + tile * TPW + grp;
-          const uint32_t rr = tile < U ? static_cast<uint32_t>(min(tok, te) - row0) : nrows;
-          srv[k] = __uint_as_float(buffer_words<1, kAux>(rss, rr * 4).x);
-        } else {
-          srv[k] = 0.f;
-        }
-      }
+    auto issue = [&](int t0, uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], uint4 (&srv)[U][NSR]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int tok = t0 + u * TPW + grp;
@@ -403,6 +431,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
         }
         load_slice<SK, kAux, LPT>(rsk, rr * RKB, sub, kr[u]);
         load_slice<SV, kAux, LPT>(rsv, rr * RVB, sub, vr[u]);
+#pragma unroll
+        for (int k = 0; k < NSR; ++k) {
+          const int c = sub + LPT * k;
+          srv[u][k] = (R && c < RPC) ? buffer_words<4, 0>(rss, rr * (DR * 2) + c * 16) : make_uint4(0, 0, 0, 0);
+        }
       }
     };
     auto mask = [&](int t0, bool (&ok)[U]) {
@@ -416,7 +449,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
     };
     constexpr int kStep = TPW * U;
     uint4 ka[U][VK], va[U][VV], kb[U][VK], vb[U][VV];
-    float sa[NSR], sb[NSR];
+    uint4 sa[U][NSR], sb[U][NSR];
     bool ok[U];
     if constexpr (G) {  // the first rows' slots come from the list the prologue stages
       prologue();
@@ -443,7 +476,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
       uint4 vr[U][VV];
       bool ok[U];
       int slot[U];
-      float srv[U];
+      uint4 srv[U][NSR];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int tok = t0 + u * TPW + grp;
@@ -453,11 +486,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
           slot[u] = ok[u] ? srow[tok] : 0;
           ok[u] = ok[u] && static_cast<unsigned>(slot[u]) < static_cast<unsigned>(p.n_max);
         }
-        if constexpr (R && kOne) {
-          srv[u] = __uint_as_float(buffer_words<1, kAux>(rss, (ok[u] ? static_cast<uint32_t>(slot[u] - row0) : nrows) * 4).x);
-        } else {
-          srv[u] = (R && ok[u]) ? p.sr[static_cast<size_t>(bh) * p.sr_stride + slot[u]] : 0.f;
-        }
+#pragma unroll
+        for (int k = 0; k < NSR; ++k) srv[u][k] = make_uint4(0, 0, 0, 0);  // no rotary branch here
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -617,9 +647,16 @@ template <class S, int RK, int RV, int LPT, int U>
 PartialFn gather_fn() {
   return decode_partial_kernel<S, S, RK, RV, LPT, U, true>;
 }
+// the contiguous read with the rotary branch, one instance per rotary width (32, 64, 128); the
+// rotary pieces take registers beside the latent slices, so fewer tiles are in flight per batch
+struct RopeFns {
+  PartialFn w32, w64, w128;
+};
 template <class S, int RK, int RV, int LPT, int U>
-PartialFn rope_fn() {
-  return decode_partial_kernel<S, S, RK, RV, LPT, U, false, true>;
+RopeFns rope_fns() {
+  return {decode_partial_kernel<S, S, RK, RV, LPT, U, false, 32>,
+          decode_partial_kernel<S, S, RK, RV, LPT, U, false, 64>,
+          decode_partial_kernel<S, S, RK, RV, LPT, (U > 2 ? U / 2 : 1), false, 128>};
 }
 template <class LS, int RK, int RV, int LPT, int U>
 PartialFn q8_fn() {
@@ -634,47 +671,47 @@ struct Entry {
   int dtype, r_k, r_v;
   PartialFn fn;   // contiguous read
   PartialFn gfn;  // gather-indexed read
-  PartialFn rfn;  // contiguous read with rotary scores (bf16 pairs only)
+  RopeFns rfn;    // contiguous read with the rotary branch (bf16 pairs only)
 };
 
 // Compiled (dtype, r_k, r_v) -> (lanes per token, tiles in flight). Lanes per token are chosen so
 // that a lane's slice of a row is one load of at most 16 bytes wherever the rank allows it.
 const Entry kTable[] = {
     {LLA_BF16, 8, 8, partial_fn<BF16, 8, 8, 1, 4>(), gather_fn<BF16, 8, 8, 1, 4>(),
-     rope_fn<BF16, 8, 8, 1, 4>()},
+     rope_fns<BF16, 8, 8, 4, 4>()},
     {LLA_BF16, 16, 16, partial_fn<BF16, 16, 16, 2, 4>(), gather_fn<BF16, 16, 16, 2, 4>(),
-     rope_fn<BF16, 16, 16, 2, 4>()},
+     rope_fns<BF16, 16, 16, 4, 4>()},
     {LLA_BF16, 24, 24, partial_fn<BF16, 24, 24, 4, 8>(), gather_fn<BF16, 24, 24, 4, 8>(),
-     rope_fn<BF16, 24, 24, 4, 8>()},
+     rope_fns<BF16, 24, 24, 4, 4>()},
     {LLA_BF16, 32, 32, partial_fn<BF16, 32, 32, 4, 8>(), gather_fn<BF16, 32, 32, 4, 8>(),
-     rope_fn<BF16, 32, 32, 4, 8>()},
+     rope_fns<BF16, 32, 32, 4, 4>()},
     {LLA_BF16, 64, 64, partial_fn<BF16, 64, 64, 8, 8>(), gather_fn<BF16, 64, 64, 8, 8>(),
-     rope_fn<BF16, 64, 64, 8, 8>()},
+     rope_fns<BF16, 64, 64, 8, 4>()},
     {LLA_BF16, 96, 96, partial_fn<BF16, 96, 96, 16, 8>(), gather_fn<BF16, 96, 96, 16, 8>(),
-     rope_fn<BF16, 96, 96, 16, 8>()},
+     rope_fns<BF16, 96, 96, 16, 4>()},
     {LLA_BF16, 128, 128, partial_fn<BF16, 128, 128, 16, 8>(), gather_fn<BF16, 128, 128, 16, 8>(),
-     rope_fn<BF16, 128, 128, 16, 8>()},
+     rope_fns<BF16, 128, 128, 16, 4>()},
     {LLA_BF16, 96, 160, partial_fn<BF16, 96, 160, 16, 8>(), gather_fn<BF16, 96, 160, 16, 8>(),
-     rope_fn<BF16, 96, 160, 16, 8>()},
+     rope_fns<BF16, 96, 160, 16, 4>()},
     {LLA_BF16, 256, 256, partial_fn<BF16, 256, 256, 32, 8>(), gather_fn<BF16, 256, 256, 32, 8>(),
-     rope_fn<BF16, 256, 256, 32, 8>()},
-    {LLA_F32, 8, 8, partial_fn<F32, 8, 8, 2, 4>(), gather_fn<F32, 8, 8, 2, 4>(), nullptr},
-    {LLA_F32, 16, 16, partial_fn<F32, 16, 16, 4, 4>(), gather_fn<F32, 16, 16, 4, 4>(), nullptr},
-    {LLA_F32, 24, 24, partial_fn<F32, 24, 24, 8, 4>(), gather_fn<F32, 24, 24, 8, 4>(), nullptr},
-    {LLA_F32, 32, 32, partial_fn<F32, 32, 32, 8, 4>(), gather_fn<F32, 32, 32, 8, 4>(), nullptr},
-    {LLA_F32, 64, 64, partial_fn<F32, 64, 64, 16, 4>(), gather_fn<F32, 64, 64, 16, 4>(), nullptr},
-    {LLA_F32, 96, 96, partial_fn<F32, 96, 96, 32, 4>(), gather_fn<F32, 96, 96, 32, 4>(), nullptr},
-    {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 32, 4>(), gather_fn<F32, 128, 128, 32, 4>(), nullptr},
-    {LLA_F32, 96, 160, partial_fn<F32, 96, 160, 8, 1>(), gather_fn<F32, 96, 160, 8, 1>(), nullptr},
-    {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 64, 4>(), gather_fn<F32, 256, 256, 64, 4>(), nullptr},
-    {LLA_BF16_Q8, 8, 8, q8_fn<Q8, 8, 8, 1, 4>(), q8_gather_fn<Q8, 8, 8, 1, 4>(), nullptr},
-    {LLA_BF16_Q8, 16, 16, q8_fn<Q8, 16, 16, 2, 4>(), q8_gather_fn<Q8, 16, 16, 2, 4>(), nullptr},
-    {LLA_BF16_Q8, 24, 24, q8_fn<Q8, 24, 24, 2, 4>(), q8_gather_fn<Q8, 24, 24, 2, 4>(), nullptr},
-    {LLA_BF16_Q8, 32, 32, q8_fn<Q8, 32, 32, 4, 8>(), q8_gather_fn<Q8, 32, 32, 4, 8>(), nullptr},
-    {LLA_BF16_I8, 8, 8, q8_fn<I8, 8, 8, 1, 4>(), q8_gather_fn<I8, 8, 8, 1, 4>(), nullptr},
-    {LLA_BF16_I8, 16, 16, q8_fn<I8, 16, 16, 2, 4>(), q8_gather_fn<I8, 16, 16, 2, 4>(), nullptr},
-    {LLA_BF16_I8, 24, 24, q8_fn<I8, 24, 24, 2, 4>(), q8_gather_fn<I8, 24, 24, 2, 4>(), nullptr},
-    {LLA_BF16_I8, 32, 32, q8_fn<I8, 32, 32, 4, 8>(), q8_gather_fn<I8, 32, 32, 4, 8>(), nullptr},
+     rope_fns<BF16, 256, 256, 32, 4>()},
+    {LLA_F32, 8, 8, partial_fn<F32, 8, 8, 2, 4>(), gather_fn<F32, 8, 8, 2, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_F32, 16, 16, partial_fn<F32, 16, 16, 4, 4>(), gather_fn<F32, 16, 16, 4, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_F32, 24, 24, partial_fn<F32, 24, 24, 8, 4>(), gather_fn<F32, 24, 24, 8, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_F32, 32, 32, partial_fn<F32, 32, 32, 8, 4>(), gather_fn<F32, 32, 32, 8, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_F32, 64, 64, partial_fn<F32, 64, 64, 16, 4>(), gather_fn<F32, 64, 64, 16, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_F32, 96, 96, partial_fn<F32, 96, 96, 32, 4>(), gather_fn<F32, 96, 96, 32, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 32, 4>(), gather_fn<F32, 128, 128, 32, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_F32, 96, 160, partial_fn<F32, 96, 160, 8, 1>(), gather_fn<F32, 96, 160, 8, 1>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 64, 4>(), gather_fn<F32, 256, 256, 64, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_BF16_Q8, 8, 8, q8_fn<Q8, 8, 8, 1, 4>(), q8_gather_fn<Q8, 8, 8, 1, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_BF16_Q8, 16, 16, q8_fn<Q8, 16, 16, 2, 4>(), q8_gather_fn<Q8, 16, 16, 2, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_BF16_Q8, 24, 24, q8_fn<Q8, 24, 24, 2, 4>(), q8_gather_fn<Q8, 24, 24, 2, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_BF16_Q8, 32, 32, q8_fn<Q8, 32, 32, 4, 8>(), q8_gather_fn<Q8, 32, 32, 4, 8>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_BF16_I8, 8, 8, q8_fn<I8, 8, 8, 1, 4>(), q8_gather_fn<I8, 8, 8, 1, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_BF16_I8, 16, 16, q8_fn<I8, 16, 16, 2, 4>(), q8_gather_fn<I8, 16, 16, 2, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_BF16_I8, 24, 24, q8_fn<I8, 24, 24, 2, 4>(), q8_gather_fn<I8, 24, 24, 2, 4>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_BF16_I8, 32, 32, q8_fn<I8, 32, 32, 4, 8>(), q8_gather_fn<I8, 32, 32, 4, 8>(), RopeFns{nullptr, nullptr, nullptr}},
 };
 
 const Entry* find(int dtype, int r_k, int r_v) {
@@ -704,7 +741,7 @@ void valu_plan(const lla_desc& desc, int B, int* splits, int* chunk, int* wg_wav
   // batches of rows in flight). More waves than fit at once leave a last, partly filled round that
   // streams at a fraction of the bandwidth (4096 waves at 12 per CU: 410 us for the 262k-token
   // read). Few (row, head) units are therefore cut into parts of at least 256 tokens: first into
-  // up to 4 waves of one workgroup, which merge in LDS (no workspace, no combine launch), then
+  // up to 8 waves of one workgroup, which merge in LDS (no workspace, no combine launch), then
   // into token splits merged by the combine kernel.
   const long units = static_cast<long>(B) * desc.H;
   const int target_waves = 2048;
@@ -713,12 +750,13 @@ void valu_plan(const lla_desc& desc, int B, int* splits, int* chunk, int* wg_wav
   if (want > max_by_len) want = max_by_len;
   if (want < 1) want = 1;
   int nw = 1;
-  if (wg_waves != nullptr) nw = want >= 4 ? 4 : want >= 2 ? 2 : 1;
+  if (wg_waves != nullptr) nw = want < kMaxWaves ? want : kMaxWaves;
   int s = (want + nw - 1) / nw;
   if (s > 256) s = 256;  // long contexts at small B*H: up to 256 splits fill the chip
-  // tokens per split, a multiple of 128 so every tile but the last is full (and nw | chunk / 32)
+  // tokens per split: a multiple of 128 for one wave, of 32 * nw for nw waves (each wave's part a
+  // multiple of 32 tokens), so every batch but a part's last is full
   int c = (desc.n_max + s - 1) / s;
-  c = (c + 127) / 128 * 128;
+  c = nw == 1 ? (c + 127) / 128 * 128 : (c + 32 * nw - 1) / (32 * nw) * (32 * nw);
   s = (desc.n_max + c - 1) / c;
   *splits = s;
   *chunk = c;
@@ -735,8 +773,8 @@ void decode_plan(const lla_desc& desc, int B, int* splits, int* chunk, int* wg_w
 }
 
 size_t decode_workspace_bytes(const lla_desc& desc, int B) {
-  int s, c;
-  decode_plan(desc, B, &s, &c);
+  int s, c, nw;
+  decode_plan(desc, B, &s, &c, &nw);  // the plan the call runs
   if (decode_uses_mfma2d(desc)) return decode2d_workspace_bytes(desc, B, s);
   return valu_workspace_bytes(desc, B, s);
 }
@@ -804,59 +842,27 @@ bool rope_supported(const lla_desc& desc, int d_rope) {
   if (desc.dtype != LLA_BF16 || !(d_rope == 32 || d_rope == 64 || d_rope == 128)) return false;
   // the LLA-2D MFMA read takes the branch as extra k-steps of its own contraction
   if (decode_uses_mfma2d(desc)) return true;
-  // the streaming read's score pre-pass holds every head's rotated query in LDS
   const Entry* e = find(desc.dtype, desc.r_k, desc.r_v);
-  return e != nullptr && e->rfn != nullptr && static_cast<long>(desc.H) * d_rope * 4 <= 64 * 1024;
+  return e != nullptr && e->rfn.w64 != nullptr;
 }
-
-namespace {
-size_t align256(size_t n) { return (n + 255) / 256 * 256; }
-}  // namespace
-
-int rope_sr_stride(int n_max) { return (n_max + 3) / 4 * 4; }
 
 size_t rope_workspace_bytes(const lla_desc& desc, int B) {
-  int s, c;
-  decode_plan(desc, B, &s, &c);
+  int s, c, nw;
+  decode_plan(desc, B, &s, &c, &nw);
   // LLA-2D on MFMA: the branch is fused into the read (q~ rows widened by up to 128 entries)
   if (decode_uses_mfma2d(desc)) return decode2d_workspace_bytes(desc, B, s, 128);
-  // streaming read: the rotary scores of every (row, head, slot) and of the self token first
-  return align256(static_cast<size_t>(B) * desc.H * rope_sr_stride(desc.n_max) * 4) +
-         align256(static_cast<size_t>(B) * desc.H * 4) + valu_workspace_bytes(desc, B, s);
+  // streaming read: the rotary scores are formed in the read; only its split partials
+  return valu_workspace_bytes(desc, B, s);
 }
 
-hipError_t launch_decode_rope(const DecodeParams& p, const RopeScoreParams& rp0, int dtype,
-                              hipStream_t stream) {
-  const bool mfma2d = p.variant == LLA_2D && decode2d_mfma_supported(dtype, p.r_k, p.r_v, p.d);
-  if (mfma2d) {  // rotary keys as extra MFMA k-steps of the read: no score pre-pass
-    DecodeParams q = p;
-    q.q_rope = rp0.q_rope;
-    q.k_rope = rp0.k_rope;
-    q.k_rope_self = rp0.k_rope_self;
-    q.d_rope = rp0.d_r;
-    q.rope_base = rp0.base;
-    return launch_decode2d(q, stream);
-  }
+hipError_t launch_decode_rope(const DecodeParams& p, int dtype, hipStream_t stream) {
+  if (p.variant == LLA_2D && decode2d_mfma_supported(dtype, p.r_k, p.r_v, p.d))
+    return launch_decode2d(p, stream);  // rotary keys as extra MFMA k-steps of the read
   const Entry* e = find(dtype, p.r_k, p.r_v);
-  if (e == nullptr || e->rfn == nullptr) return hipErrorNotSupported;
-  const int stride = rope_sr_stride(p.n_max);
-  const size_t a = align256(static_cast<size_t>(p.B) * p.H * stride * 4);
-  const size_t b = align256(static_cast<size_t>(p.B) * p.H * 4);
-  if (a + b > p.ws_bytes) return hipErrorInvalidValue;
-  char* base = reinterpret_cast<char*>(p.ws);
-  RopeScoreParams rp = rp0;
-  rp.sr = reinterpret_cast<float*>(base);
-  rp.sr_self = reinterpret_cast<float*>(base + a);
-  rp.sr_stride = stride;
-  hipError_t err = launch_rope_scores(rp, stream);
-  if (err != hipSuccess) return err;
-  DecodeParams q = p;
-  q.sr = rp.sr;
-  q.sr_self = rp.k_rope_self != nullptr ? rp.sr_self : nullptr;
-  q.sr_stride = stride;
-  q.ws = reinterpret_cast<float*>(base + a + b);
-  q.ws_bytes = p.ws_bytes - a - b;
-  return launch_valu(q, dtype, e->rfn, stream);
+  if (e == nullptr) return hipErrorNotSupported;
+  const PartialFn fn = p.d_rope == 32 ? e->rfn.w32 : p.d_rope == 64 ? e->rfn.w64 : p.d_rope == 128 ? e->rfn.w128 : nullptr;
+  if (fn == nullptr) return hipErrorNotSupported;
+  return launch_valu(p, dtype, fn, stream);
 }
 
 hipError_t launch_decode_gather(const DecodeParams& p, int dtype, hipStream_t stream) {

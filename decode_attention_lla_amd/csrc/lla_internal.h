@@ -36,20 +36,15 @@ struct DecodeParams {
   int32_t wg_waves;
   float scale_log2;   // softmax scale * log2(e)
   size_t ws_bytes;    // bytes available at ws; launchers refuse a plan that does not fit
-  // Rotary branch of the streaming read (lla_attend_decode_rope): base-2 rotary scores added to
-  // the latent scores, sr [rows][H][sr_stride] by slot and sr_self [rows][H] for the self token;
-  // NULL when absent (the LLA-2D MFMA read fuses the branch instead: q_rope, k_rope below).
-  const float* sr;
-  const float* sr_self;
-  int32_t sr_stride;  // floats per (row, head) score row: n_max rounded up to a multiple of 4
   // Gather-indexed read (lla_attend_decode_gather): row b attends the latents at
   // slots[b * budget + j], j < seq_lens[b] clamped to [0, budget] (all budget when seq_lens is
   // null); a slot outside [0, n_max) is skipped. slots == nullptr: the contiguous read above.
   const int32_t* slots;
   int32_t budget;
-  // Rotary branch fused into the LLA-2D MFMA read (lla_attend_decode_rope; d_rope == 0 without):
-  // q_rope [rows][H][d_rope] unrotated, k_rope [B][n_max][d_rope] rotated at each slot,
-  // k_rope_self [B][d_rope] or NULL, RoFormer base.
+  // Decoupled rotary branch (lla_attend_decode_rope; d_rope == 0 without), formed inside the read
+  // (streaming and LLA-2D MFMA kernels alike): q_rope [rows][H][d_rope] unrotated (rotated at the
+  // row's key count N_b), k_rope [B][n_max][d_rope] rotated at each slot, k_rope_self [B][d_rope]
+  // or NULL, RoFormer base.
   const void* q_rope;
   const void* k_rope;
   const void* k_rope_self;
@@ -72,20 +67,6 @@ struct RopeWriteParams {
   const int32_t* pos;  // [B]
   void* k_rope;        // bf16 [B][n_max][d_r]
   int32_t B, C, n_max, d_r;
-  double base;
-};
-
-// Rotary score pre-pass of one decode read (lla_attend_decode_rope).
-struct RopeScoreParams {
-  const void* q_rope;       // bf16 [B][H][d_r], unrotated (rotated at N_b inside)
-  const void* k_rope;       // bf16 [B][n_max][d_r], rotated at each slot
-  const void* k_rope_self;  // bf16 [B][d_r] or NULL
-  const int32_t* seq_lens;
-  float* sr;                // out [B][H][sr_stride], base-2 scale
-  int32_t sr_stride;        // n_max rounded up to a multiple of 4 (16-byte aligned rows)
-  float* sr_self;           // out [B][H] (when k_rope_self is given)
-  int32_t B, H, n_max, d_r;
-  float scale_log2;
   double base;
 };
 
@@ -163,11 +144,9 @@ hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t s);
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 // Decoupled rotary branch (rope.hip, decode.hip).
 hipError_t launch_rope_write(const RopeWriteParams& p, hipStream_t s);
-hipError_t launch_rope_scores(const RopeScoreParams& p, hipStream_t s);
 bool rope_supported(const lla_desc& desc, int d_rope);
 size_t rope_workspace_bytes(const lla_desc& desc, int B);
-hipError_t launch_decode_rope(const DecodeParams& p, const RopeScoreParams& rp, int dtype,
-                              hipStream_t s);
+hipError_t launch_decode_rope(const DecodeParams& p, int dtype, hipStream_t s);
 // Reconstruct-then-attend comparator (reconstruct.hip).
 bool reconstruct_supported(const lla_desc& desc);
 void reconstruct_plan(const lla_desc& desc, int B, int* splits, int* chunk, int* wg_waves = nullptr);

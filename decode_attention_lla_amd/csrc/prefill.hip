@@ -617,8 +617,8 @@ void prefill_plan(const lla_desc& desc, int B, int C, int* splits, int* chunk, i
 size_t prefill_workspace_bytes(const lla_desc& desc, int B, int C) {
   if (mfma_prefill(desc.dtype, desc.r_k, desc.r_v, desc.d_head, desc.n_max))
     return prefill_mfma_bytes(B, C, desc.H, desc.d_head, desc.r_k, desc.r_v);
-  int s, c;
-  prefill_plan(desc, B, C, &s, &c);
+  int s, c, nw;
+  prefill_plan(desc, B, C, &s, &c, &nw);  // the plan the call runs
   return valu_workspace_bytes(desc, B * C, s);
 }
 

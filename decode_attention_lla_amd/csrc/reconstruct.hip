@@ -211,8 +211,8 @@ void reconstruct_plan(const lla_desc& desc, int B, int* splits, int* chunk, int*
 size_t reconstruct_workspace_bytes(const lla_desc& desc, int B) {
   const size_t kv = align256(static_cast<size_t>(B) * desc.H * desc.n_max * desc.d_head * 2);
   const size_t id = align256(static_cast<size_t>(desc.H) * desc.d_head * desc.d_head * 2);
-  int s, c;
-  reconstruct_plan(desc, B, &s, &c);
+  int s, c, nw;
+  reconstruct_plan(desc, B, &s, &c, &nw);  // the plan the call runs
   return 2 * kv + id + valu_workspace_bytes(attend_desc(desc), B, s);
 }
 

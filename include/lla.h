@@ -209,8 +209,9 @@ lla_status lla_attend_decode_noalloc(const lla_desc* desc, int32_t B, int32_t t,
 lla_status lla_rope_write(const lla_desc* desc, int32_t B, int32_t C, int32_t d_rope, float base,
                           const void* k_in, const int32_t* pos, void* k_rope, void* stream);
 
-/* Bytes of device workspace that lla_attend_decode_rope needs: the rotary scores
- * [B][H][n_max] float32, the self token's [B][H], and split partials. 0 for an invalid descriptor. */
+/* Bytes of device workspace that lla_attend_decode_rope needs: the split partials of its plan (and
+ * on the LLA-2D MFMA read the absorbed queries). May be 0 (then ws may be NULL); 0 as well for an
+ * invalid descriptor. */
 size_t lla_rope_workspace_bytes(const lla_desc* desc, int32_t B);
 
 /* lla_attend_decode with the rotary branch: key i of row b is [k_i ; k_rope[b][i]] (k_i rebuilt
@@ -219,11 +220,13 @@ size_t lla_rope_workspace_bytes(const lla_desc* desc, int32_t B);
  * values are the content values. The scale defaults (desc->scale == 0) to 1/sqrt(d_head + d_rope),
  * the width of the concatenated key.
  *   q_rope [device] bf16 [B][H][d_rope], unrotated; k_rope_self [device] bf16 [B][d_rope], given
- *   exactly when k_self is; ws at least lla_rope_workspace_bytes(desc, B).
- * The rotary scores of all heads are formed once per read (each rotary key read once) and added to
- * the streamed latent scores; the LLA-2D MFMA read forms them in its own contraction instead.
- * LLA_BF16, d_rope 32, 64 or 128, the streaming bf16 (r_k, r_v) pairs with H * d_rope <= 16384
- * (both variants), or the LLA-2D MFMA pairs at any H; otherwise LLA_ERR_UNSUPPORTED. */
+ *   exactly when k_self is; ws at least lla_rope_workspace_bytes(desc, B) bytes (NULL if 0).
+ * The rotary scores are formed inside the read: each token's rotary key is streamed beside its
+ * latent rows and dotted with the head's rotated rotary query (LLA-2D on MFMA: extra contraction
+ * steps of the read). All heads of a sequence read the same rotary keys; when B is a multiple of 8
+ * they run on one XCD, so the keys come from HBM about once per sequence.
+ * LLA_BF16, d_rope 32, 64 or 128, the streaming bf16 (r_k, r_v) pairs (both variants) or the
+ * LLA-2D MFMA pairs; otherwise LLA_ERR_UNSUPPORTED. */
 lla_status lla_attend_decode_rope(const lla_desc* desc, int32_t B, int32_t t, const void* q,
                                   const void* q_rope, const void* zk, const void* zv,
                                   const void* k_rope, int32_t d_rope, float base,

@@ -94,20 +94,22 @@ def test_unsupported_ranks():
 
 
 def test_workspace_checked_before_launch():
-    d = desc()  # 32 x 16 units over 4097 slots: split-K, needs a workspace
-    need = lla.lla_workspace_bytes(d, 32, 1)
+    d = desc(n_max=16385)  # 2 x 16 units over 16385 slots: more parts than a workgroup's waves
+    need = lla.lla_workspace_bytes(d, 2, 1)
     assert need > 0
-    assert decode(d, B=32) == lla.LLA_ERR_WORKSPACE
-    assert decode(d, B=32, ws=A, wsb=need - 4) == lla.LLA_ERR_WORKSPACE
+    assert decode(d, B=2) == lla.LLA_ERR_WORKSPACE
+    assert decode(d, B=2, ws=A, wsb=need - 4) == lla.LLA_ERR_WORKSPACE
 
 
 def test_workspace_sizes():
     # no split when B*H alone fills the chip (capacity shape)
     assert lla.lla_workspace_bytes(desc(r_k=24, r_v=24), 768, 1) == 0
+    # the Ouro-shaped layer (512 units) splits its tokens among the waves of one workgroup only
+    assert lla.lla_workspace_bytes(desc(), 32, 1) == 0
     # split partials are (m, l, a[r_v]) floats per (b, h, split)
-    n = lla.lla_workspace_bytes(desc(), 32, 1)
-    assert n % (32 * 16 * (2 + 32) * 4) == 0
-    splits = n // (32 * 16 * (2 + 32) * 4)
+    n = lla.lla_workspace_bytes(desc(n_max=16385), 2, 1)
+    assert n % (2 * 16 * (2 + 32) * 4) == 0
+    splits = n // (2 * 16 * (2 + 32) * 4)
     assert 2 <= splits <= 64
 
 
@@ -193,16 +195,15 @@ def test_gather_unsupported_and_workspace():
     assert lla.lla_gather_workspace_bytes(d, 2, 0) == 0
 
 
-def test_rope_workspace_is_scores_plus_the_decode_plan():
-    """The rotary read's workspace: the rotary scores (rows padded to 4 tokens), the self scores,
-    then the split partials of the decode plan (none when the plan has one split)."""
+def test_rope_workspace_is_the_decode_plan():
+    """The rotary read forms its rotary scores inside the read, so its workspace is the split
+    partials of the decode plan (none when the plan has one split per row and head)."""
     lib = lla.library()
-    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    scores = lambda d, B: al(B * d.H * ((d.n_max + 3) // 4 * 4) * 4) + al(B * d.H * 4)  # noqa: E731
     for d, B in ((desc(H=64, r_k=8, r_v=8, n_max=5000), 64), (desc(H=16, r_k=24, r_v=24, n_max=4097), 768),
-                 (desc(H=16, r_k=24, r_v=24, n_max=4097), 2)):
+                 (desc(H=16, r_k=24, r_v=24, n_max=4097), 2), (desc(H=2, r_k=24, r_v=24, n_max=70000), 3)):
         need = lib.lla_rope_workspace_bytes(ctypes.byref(d), B)
-        assert need == scores(d, B) + lla.lla_workspace_bytes(d, B)
+        assert need == lla.lla_workspace_bytes(d, B)
+    assert lib.lla_rope_workspace_bytes(ctypes.byref(desc(H=2, r_k=24, r_v=24, n_max=70000)), 3) > 0
 
 
 def test_gather_plan_keeps_splits_within_the_staged_list():
@@ -305,17 +306,21 @@ def test_rope_arguments_support_and_workspace():
     assert rope_decode(d, d_rope=48) == lla.LLA_ERR_UNSUPPORTED
     assert rope_decode(desc(r_k=24, r_v=24, n_max=100, dtype=lla.LLA_F32)) == lla.LLA_ERR_UNSUPPORTED
     assert rope_decode(desc(r_k=64, r_v=128, n_max=100)) == lla.LLA_ERR_UNSUPPORTED
-    assert rope_decode(desc(r_k=24, r_v=24, n_max=100, H=200), d_rope=128) == lla.LLA_ERR_UNSUPPORTED
+    # no per-head LDS cap on the streaming read any more: a long cache with many heads stops at the
+    # workspace check
+    assert rope_decode(desc(r_k=24, r_v=24, n_max=70000, H=200), B=1, d_rope=128) == lla.LLA_ERR_WORKSPACE
     # the LLA-2D MFMA read fuses the branch and has no per-head LDS cap: H * d_rope > 16384 is
     # accepted (the call then stops at the workspace check)
     big2d = desc(variant=lla.LLA_2D, r_k=64, r_v=64, d_head=32, n_max=100, H=200)
     assert rope_decode(big2d, d_rope=128) == lla.LLA_ERR_WORKSPACE
-    assert rope_decode(desc(variant=lla.LLA_2D, r_k=32, r_v=32, d_head=32, n_max=100, H=200),
-                       d_rope=128) == lla.LLA_ERR_UNSUPPORTED  # LLA-2D on the streaming read
-    need = lla.lla_rope_workspace_bytes(d, 2)
-    assert need >= 2 * 16 * 100 * 4  # rotary scores of every (b, h, slot)
-    assert rope_decode(d) == lla.LLA_ERR_WORKSPACE
-    assert rope_decode(d, ws=A, wsb=need - 1) == lla.LLA_ERR_WORKSPACE
+    # the rotary scores are formed inside the read: the workspace holds only split partials, and
+    # a long cache at small B * H needs them
+    dl = desc(r_k=24, r_v=24, n_max=5000)
+    need = lla.lla_rope_workspace_bytes(dl, 2)
+    assert need > 0 and need == lla.lla_workspace_bytes(dl, 2, 1)
+    assert need % (2 * 16 * (2 + 24) * 4) == 0
+    assert rope_decode(dl) == lla.LLA_ERR_WORKSPACE
+    assert rope_decode(dl, ws=A, wsb=need - 1) == lla.LLA_ERR_WORKSPACE
     lib = lla.library()
     w = lambda dd, **k: lib.lla_rope_write(ctypes.byref(dd), k.get("B", 2), k.get("C", 1),
                                            k.get("dr", 64), ctypes.c_float(k.get("base", 0.0)),
@@ -360,3 +365,15 @@ def test_noalloc_decode_refusals_on_the_host():
     assert lla.lla_workspace_bytes(big, 4096) > lla.LLA_NOALLOC_SCRATCH_BYTES
     assert call(big, B=4096) == lla.LLA_ERR_SCRATCH_LIMIT
     assert "scratch" in lla.lla_status_string(lla.LLA_ERR_SCRATCH_LIMIT)
+
+
+def test_noalloc_cases_use_the_scratch():
+    """Every call of the no-alloc GPU test plans token splits (so the static scratch is written and
+    then reused by the smaller second call) within the scratch limit."""
+    from tests.test_zz_no_alloc import CASES
+    for variant, H, d, T, rk, rv, calls in CASES:
+        for B, n_max, _ in calls:
+            v = lla.LLA_PER_HEAD if variant == "per_head" else lla.LLA_2D
+            d_ = lla.make_desc(v, lla.LLA_BF16, H, d, T, rk, rv, n_max)
+            assert 0 < lla.lla_workspace_bytes(d_, B, 1) <= lla.LLA_NOALLOC_SCRATCH_BYTES, \
+                (variant, rk, rv, B, n_max)

@@ -82,11 +82,12 @@ def test_workspace_queries_refuse_what_the_calls_refuse():
 
 def test_heads_past_a_launch_dimension_are_refused():
     """Heads index a launch dimension of at most 65535 workgroups: H = 65536 is an invalid
-    descriptor (every query answers 0), H = 65535 is accepted (the rotary score array and the
-    rebuilt K/V always need workspace)."""
+    descriptor (every query answers 0), H = 65535 is accepted (the rebuilt K/V always need
+    workspace; the LLA-2D rotary read always holds its absorbed queries there)."""
     lib = lla.library()
     for H, ok in ((65535, True), (65536, False)):
         d = lla.make_desc(lla.LLA_PER_HEAD, lla.LLA_BF16, H, 64, 1, 32, 32, 16)
-        assert (lib.lla_rope_workspace_bytes(ctypes.byref(d), 1) > 0) == ok
+        d2 = lla.make_desc(lla.LLA_2D, lla.LLA_BF16, H, 64, 1, 64, 64, 16)
+        assert (lib.lla_rope_workspace_bytes(ctypes.byref(d2), 1) > 0) == ok
         assert (lib.lla_reconstruct_workspace_bytes(ctypes.byref(d), 1) > 0) == ok
         assert lla.lla_workspace_bytes(d, 1, 2) == 0 or ok

@@ -72,13 +72,13 @@ def oracle_decode(c, t, lens, variant, self_token=True, mu=True, b_sel=None, abs
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("rk,rv", PAIRS)
 def test_decode_sweep_per_head(dtype, rk, rv):
-    B, H, d, T, n_max = 3, 2, 64, 3, 1301
-    lens = [1301, 517, 0]
+    B, H, d, T, n_max = 3, 2, 64, 3, 3001
+    lens = [3001, 517, 0]
     for gain, mu, self_token in ((1.0, True, True), (8.0, False, True), (1.0, True, False)):
         c = upload(synth.random_case("per_head", dtype, B, H, d, T, rk, rv, n_max,
                                      7000 + rk + rv, with_mu=mu, q_gain=gain), dtype)
         desc = mk_desc("per_head", dtype, H, d, T, rk, rv, n_max)
-        assert lla.lla_workspace_bytes(desc, B) > 0  # this shape runs split-K plus the combine
+        assert lla.lla_workspace_bytes(desc, B) > 0  # 8-wave workgroups, split-K and the combine
         for t in range(T):
             o, lse = gpu_decode(desc, B, t, c, dtype, lens, self_token, mu)
             ro, rl = oracle_decode(c, t, lens, "per_head", self_token, mu)
@@ -99,6 +99,20 @@ def test_decode_sweep_2d(dtype, rk, rv):
         ro, rl = oracle_decode(c, t, lens, "2d")
         assert_close(o, ro, dtype, f"2d {dtype} t={t}")
         assert_lse(lse, rl, f"2d {dtype} t={t}")
+
+
+@pytest.mark.parametrize("dtype,rk,rv", [("bf16", 32, 32), ("f32", 8, 8), ("bf16", 96, 160)])
+def test_decode_2d_streaming_xcd_grouped(dtype, rk, rv):
+    """LLA-2D on the streaming read with B a multiple of 8: every head of a sequence is launched
+    onto one XCD (they all stream the same latents); ragged lengths, mu, self token."""
+    B, H, d, T, n_max = 16, 5, 32, 2, 1500
+    lens = [1500, 1499, 0, 1, 700, 256, 257, 1024, 33, 1200, 64, 65, 900, 5, 511, 512]
+    c = upload(synth.random_case("2d", dtype, B, H, d, T, rk, rv, n_max, 7150 + rk + rv, q_gain=4.0), dtype)
+    desc = mk_desc("2d", dtype, H, d, T, rk, rv, n_max)
+    o, lse = gpu_decode(desc, B, 1, c, dtype, lens)
+    ro, rl = oracle_decode(c, 1, lens, "2d")
+    assert_close(o, ro, dtype, f"2d streaming xcd {dtype} r=({rk},{rv})")
+    assert_lse(lse, rl, f"2d streaming xcd {dtype} r=({rk},{rv})")
 
 
 @pytest.mark.parametrize("dtype,rk,rv", [("bf16", 24, 24), ("bf16", 8, 8), ("bf16", 256, 256),

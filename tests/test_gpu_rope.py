@@ -98,9 +98,8 @@ def test_decode_rope(variant, rk, rv, d_rope):
 
 
 def test_lla2d_decode_rope_many_heads():
-    """LLA-2D on MFMA with H * d_rope above the streaming pre-pass's LDS cap (H = 144, d_rope =
-    128): the branch is fused into the MFMA read, so the call is accepted and matches the oracle
-    (nine 16-head groups, ragged lengths, self token, mu)."""
+    """LLA-2D on MFMA with many heads and a wide branch (H = 144, d_rope = 128; nine 16-head
+    groups), ragged lengths, self token, mu."""
     B, H, d, T, n_max, r, d_rope = 3, 144, 32, 2, 700, 64, 128
     lens = np.array([700, 333, 1], np.int32)
     desc = mk_desc("2d", "bf16", H, d, T, r, r, n_max)
@@ -123,6 +122,37 @@ def test_lla2d_decode_rope_many_heads():
     assert_close(host(out), ro, "bf16", "2d rope H=144")
     slack = mfma_lse_slack(c["q"][t], c["zk"], c["Wk"], t, lens, q_rope=q_rope, k_rope=k_rope)
     assert_lse(host(lse), rl, "2d rope H=144", slack)
+
+
+@pytest.mark.parametrize("variant,rk,rv,d_rope,H", [("per_head", 24, 24, 128, 130), ("2d", 32, 32, 64, 40),
+                                                      ("per_head", 96, 160, 64, 9)])
+def test_decode_rope_xcd_grouped(variant, rk, rv, d_rope, H):
+    """B a multiple of 8: every head (and split) of a sequence is launched onto one XCD, where they
+    share the sequence's rotary keys (LLA-2D on the streaming read: its latents too). Many heads
+    with a wide branch (H * d_rope = 16640), ragged lengths around the per-wave token parts,
+    sharpened queries, self token."""
+    B, d, T, n_max = 16, 32, 2, 2600
+    lens = np.array([2600, 2599, 1, 0, 1300, 257, 1024, 1025, 31, 2048, 640, 641, 2000, 7, 99, 1555],
+                    np.int32)
+    desc = mk_desc(variant, "bf16", H, d, T, rk, rv, n_max)
+    ws = lla.rope_workspace(desc, B)
+    rng = np.random.default_rng(9970 + H)
+    q_rope, k_rope, krs = _rope_inputs(rng, B, H, n_max, d_rope)
+    c = upload(synth.random_case(variant, "bf16", B, H, d, T, rk, rv, n_max, 9971 + H, q_gain=4.0), "bf16")
+    t = 1
+    q = dev(c["q"][t], "bf16")
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H, device="cuda")
+    lla.lla_attend_decode_rope(desc, B, t, q, dev(q_rope, "bf16"), c["_zk"], c["_zv"], dev(k_rope, "bf16"),
+                               d_rope, 0.0, dev(lens), c["_Wk"], c["_Wv"], c["_muk"], c["_muv"],
+                               dev(c["k_self"][t], "bf16"), dev(c["v_self"][t], "bf16"), dev(krs, "bf16"),
+                               out, lse, ws)
+    torch.cuda.synchronize()
+    ro, rl = O.attend_decode_rope(c["q"][t], q_rope, c["zk"], c["zv"], k_rope, c["Wk"], c["Wv"], t, lens,
+                                  c["mu_k"], c["mu_v"], c["k_self"][t], c["v_self"][t], krs, variant=variant)
+    what = f"rope xcd-grouped {variant} r=({rk},{rv}) d_rope={d_rope} H={H}"
+    assert_close(host(out), ro, "bf16", what)
+    assert_lse(host(lse), rl, what)
 
 
 def test_decode_rope_many_units_ragged():

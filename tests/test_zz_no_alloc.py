@@ -41,8 +41,8 @@ def _run(entry, desc, B, t, c, lens, mu, self_token):
 
 # (variant, H, d, T, r_k, r_v, [(B, n_max, lens), (smaller B, n_max, lens)])
 CASES = [
-    ("per_head", 16, 128, 4, 32, 32, [(4, 8193, None), (3, 1500, [1500, 3, 777])]),
-    ("per_head", 2, 64, 2, 96, 160, [(3, 3000, [3000, 2999, 129]), (2, 900, [900, 1])]),
+    ("per_head", 16, 128, 4, 32, 32, [(4, 8193, None), (3, 3000, [3000, 3, 777])]),
+    ("per_head", 2, 64, 2, 96, 160, [(3, 3000, [3000, 2999, 129]), (2, 2400, [2400, 1])]),
     ("2d", 16, 128, 2, 256, 256, [(8, 2048, None), (3, 700, [700, 65, 1])]),
     ("2d", 20, 64, 2, 64, 64, [(6, 1000, [1000, 999, 17, 0, 640, 1]), (2, 300, [300, 299])]),
 ]
