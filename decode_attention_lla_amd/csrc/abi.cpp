@@ -339,7 +339,7 @@ lla_status lla_attend_decode_rope(const lla_desc* desc, int32_t B, int32_t t, co
   const float sc = desc->scale > 0.f ? desc->scale
                                      : 1.0f / std::sqrt(static_cast<float>(desc->d_head + d_rope));
   p.scale_log2 = sc * 1.4426950408889634f;
-  lla::decode_plan(*desc, B, &p.splits, &p.chunk, &p.wg_waves);
+  lla::rope_plan(*desc, B, &p.splits, &p.chunk, &p.wg_waves, &p.wg_heads);
   p.q_rope = q_rope;
   p.k_rope = k_rope;
   p.k_rope_self = k_rope_self;

@@ -114,8 +114,12 @@ __device__ void finish_unit(const DecodeParams& p, int b, int h, float M, float 
 // the K row scale multiplies the score, the V row scale the token's weight). With DR > 0 each
 // token's score also gets its rotary part q_R . k_R (decoupled RoPE branch): q_R (the head's
 // rotary query, rotated at the decoding position, scaled) is formed in the prologue, and each
-// token's DR-wide rotary key, shared by every head of the sequence, is streamed beside its latent
-// rows and dotted in the same lane group.
+// token's DR-wide rotary key, shared by every head of the sequence, is dotted in the token's lane
+// group beside its latent slices. HG == 1: every wave loads the rotary rows of its tokens itself.
+// HG > 1 (head groups): the HG waves of a workgroup are HG heads of one sequence over the same
+// tokens; each batch's rotary rows are loaded once, an HG-th by each wave, and handed over in LDS,
+// so the rows cross the L2 once per head group rather than once per head (a head past H is a
+// placeholder wave: it loads its share of the rotary rows, reads no latents and writes nothing).
 // A lane's S-byte row slice (whole words, S <= 32) of the row at byte offset row of a raw buffer,
 // for lane sub of the LPT lanes that share the row. Up to 16 bytes: one load at S*sub. Longer
 // slices are split: the first 16 bytes at 16*sub (into f[0]), the rest at 16*LPT + (S-16)*sub
@@ -181,9 +185,11 @@ __device__ __forceinline__ void absorb_query(const DecodeParams& p, int h, int n
   }
 }
 
-template <class S, class LS, int RK, int RV, int LPT, int U, bool G, int DR = 0>
+template <class S, class LS, int RK, int RV, int LPT, int U, bool G, int DR = 0, int HG = 1>
 __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodeParams p) {
   constexpr bool R = DR > 0;
+  constexpr bool kHG = HG > 1;
+  static_assert(!kHG || (R && HG <= kMaxWaves), "head groups share rotary rows");
   constexpr int RPC = R ? DR / 8 : 1;          // 16-byte pieces of a rotary key row
   constexpr int NRP = (RPC + LPT - 1) / LPT;   // pieces per lane (piece sub + LPT * k)
   constexpr bool kQ8 = std::is_same<LS, Q8>::value || std::is_same<LS, I8>::value;  // low-bit rows
@@ -213,36 +219,50 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   constexpr bool kSplitV = kOne && SV > 16;
   static_assert(!kQ8 || !(kSplitK || kSplitV), "low-bit slices are one load");
 
-  __shared__ float q_s[256];
-  __shared__ float qt_s[RK];
-  __shared__ float qr_s[R ? DR : 1];  // rotated rotary query times scale * log2(e)
-  __shared__ float a_s[RV];
+  // per (row, head): one copy, or one per wave of a head group
+  __shared__ float q_a[HG][256];
+  __shared__ float qt_a[HG][RK];
+  __shared__ float qr_a[HG][R ? DR : 1];  // rotated rotary query times scale * log2(e)
+  __shared__ float a_a[HG][RV];
   // the waves' partial sums of q~ (absorb_query), later their (m, l, a) partials (merge below)
   __shared__ float xs_s[(kMaxWaves * RK > (kMaxWaves - 1) * (2 + RV)) ? kMaxWaves * RK : (kMaxWaves - 1) * (2 + RV)];
 
   // nw waves share one (row, head, split): wave w streams the w-th of nw equal parts of the
-  // split's tokens (the gather read keeps one wave: its slot list is staged per wave)
-  const int nw = G ? 1 : min(max(p.wg_waves, 1), kMaxWaves);
+  // split's tokens (the gather read keeps one wave: its slot list is staged per wave). A head
+  // group's HG waves each take one head over the whole split.
+  const int nw = G ? 1 : kHG ? HG : min(max(p.wg_waves, 1), kMaxWaves);
   const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
+  const int hw = kHG ? wave : 0;  // this wave's copy of the per-head LDS arrays
+  float* const q_s = q_a[hw];
+  float* const qt_s = qt_a[hw];
+  float* const qr_s = qr_a[hw];
+  float* const a_s = a_a[hw];
+  // the prologue's work is divided over pn waves (a head group's waves each do their own)
+  const int pw = kHG ? 0 : wave;
+  const int pn = kHG ? 1 : nw;
   // Sequences whose heads share what they stream (the rotary keys; LLA-2D: the latents too) keep
   // all their workgroups on one XCD when B is a multiple of 8: workgroups are dispatched round-
   // robin over the 8 XCDs, so unit (x % 8) + 8 * k runs on XCD x % 8, and consecutive k there
   // are the heads and splits of one sequence, co-resident and sharing that XCD's L2.
+  const int ng = kHG ? (p.H + HG - 1) / HG : p.H;  // head units of one row
   int unit = blockIdx.x;
   if ((R || p.variant == LLA_2D) && (p.B & 7) == 0) {
-    const int per = p.H * p.splits;  // units of one row
+    const int per = ng * p.splits;  // units of one row
     const int k = unit >> 3;
     unit = ((k / per) * 8 + (unit & 7)) * per + k % per;
   }
   const int split = unit % p.splits;
-  const int bh = unit / p.splits;
-  const int h = bh % p.H;
-  const int b = bh / p.H;
+  const int b = unit / p.splits / ng;
+  int h = unit / p.splits % ng;
+  if (kHG) h = h * HG + wave;
+  const bool live = !kHG || h < p.H;  // a placeholder wave past H reads and writes no head
+  if (kHG) h = min(h, p.H - 1);
+  const int bh = b * p.H + h;
 
   const int nb = G ? gather_keys(p, b) : row_keys(p, b);
-  const int cw = p.chunk / nw;  // the plan keeps chunk a multiple of 32 * nw
-  const int tb = uniform(split * p.chunk + wave * cw);
+  const int cw = kHG ? p.chunk : p.chunk / nw;  // the plan keeps chunk a multiple of 32 * nw
+  const int tb = uniform(split * p.chunk + (kHG ? 0 : wave * cw));
   const int te = uniform(min(nb, min(split * p.chunk + p.chunk, tb + cw)));
 
   // One-load rows stream two register batches ahead. The gather read first stages its split's
@@ -285,8 +305,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   // the contiguous read: its split [tb, te)); an offset at the end reads zeros
   const int row0 = G ? 0 : tb;
   const uint32_t nrows = static_cast<uint32_t>(uniform(G ? p.n_max : max(te - tb, 0)));
-  const __amdgpu_buffer_rsrc_t rsk = buffer_rsrc(static_cast<const char*>(p.zk) + (lrow + row0) * RKB, nrows * RKB);
-  const __amdgpu_buffer_rsrc_t rsv = buffer_rsrc(static_cast<const char*>(p.zv) + (lrow + row0) * RVB, nrows * RVB);
+  const uint32_t nlat = live ? nrows : 0;  // a placeholder wave's latent loads all read zeros
+  const __amdgpu_buffer_rsrc_t rsk = buffer_rsrc(static_cast<const char*>(p.zk) + (lrow + row0) * RKB, nlat * RKB);
+  const __amdgpu_buffer_rsrc_t rsv = buffer_rsrc(static_cast<const char*>(p.zv) + (lrow + row0) * RVB, nlat * RVB);
   // non-temporal: rows are read once. For the gather read this pays when listed slots run in
   // order (a sink + window list: 248 -> 229 us at the capacity shape); a random list of 48-byte
   // rows reads ~5% slower than with ordinary loads.
@@ -296,7 +317,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   // Lane `sub` of a token's group holds pieces sub + LPT * k of the row (16 bytes each); ordinary
   // loads, so the row stays in L2 for the sequence's other heads.
   static_assert(!R || kPipe, "the rotary branch takes the pipelined contiguous read");
-  constexpr int NSR = R ? NRP : 1;
+  // registers of a batch's rotary loads: per tile NRP pieces (HG == 1), or the wave's share of
+  // the batch's pieces, NSH per lane (HG > 1), which the batch's consume hands over in LDS
+  constexpr int kStep = TPW * U;        // tokens per batch
+  constexpr int PB = kStep * RPC;       // 16-byte rotary pieces of a batch
+  constexpr int NSH = kHG ? (PB + 64 * HG - 1) / (64 * HG) : 1;
+  constexpr int SRU = kHG ? 1 : U;
+  constexpr int NSR = kHG ? NSH : R ? NRP : 1;
+  // batch rotary tiles in LDS (HG > 1), two in turn: piece k of lane sub of tile u's token grp at
+  // [k][u * 64 + lane], so each read instruction of the consume covers 1 KiB without gaps
+  __shared__ uint4 rt_s[kHG ? 2 : 1][kHG ? NRP * kStep * LPT : 1];
   const __amdgpu_buffer_rsrc_t rss = buffer_rsrc(
       R ? static_cast<const char*>(p.k_rope) + (static_cast<size_t>(b / p.rows_per_seq) * p.n_max + row0) * DR * 2 : nullptr,
       R ? nrows * DR * 2 : 0);
@@ -309,9 +339,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   float beta = 0.f;
   auto prologue = [&]() {
     const size_t qoff = static_cast<size_t>(bh) * p.d;
-    for (int j = wave * 64 + lane; j < p.d; j += 64 * nw) q_s[j] = ld<S>(p.q, qoff + j);
+    for (int j = pw * 64 + lane; j < p.d; j += 64 * pn) q_s[j] = ld<S>(p.q, qoff + j);
     __syncthreads();
-    absorb_query<S, RK>(p, h, nw, wave, lane, q_s, xs_s, qt_s);
+    absorb_query<S, RK>(p, h, pn, pw, lane, q_s, xs_s + (kHG ? wave * RK : 0), qt_s);
     if (p.mu_k != nullptr) {
       const size_t moff = mu_offset(p, h);
       float part = 0.f;
@@ -325,7 +355,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
     }
     if constexpr (R) {  // rotary query of this head rotated at the decoding position N_b
       const size_t qro = static_cast<size_t>(bh) * DR;
-      for (int i = wave * 64 + lane; i < DR / 2; i += 64 * nw) {
+      for (int i = pw * 64 + lane; i < DR / 2; i += 64 * pn) {
         float y0, y1;
         rotate_pair(ld<BF16>(p.q_rope, qro + 2 * i), ld<BF16>(p.q_rope, qro + 2 * i + 1), i, DR, nb,
                     p.rope_base, &y0, &y1);
@@ -357,7 +387,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   for (int e = 0; e < EV; ++e) acc[e] = 0.f;
 
   // fold one batch of U tiles (ok: token inside the split and valid) into (m, l, acc)
-  auto consume = [&](uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], const bool (&ok)[U], uint4 (&srv)[U][NSR]) {
+  auto consume = [&](uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], const bool (&ok)[U], uint4 (&srv)[SRU][NSR],
+                     uint4* tile) {
+    if constexpr (kHG) {  // hand this wave's share of the batch's rotary rows to the group
+#pragma unroll
+      for (int k = 0; k < NSH; ++k) {
+        const int i = (wave + HG * k) * 64 + lane;  // piece c of the batch's row li
+        const int li = i / RPC, c = i % RPC;
+        if (PB % (64 * HG) == 0 || i < PB) tile[((c / LPT) * kStep + li) * LPT + c % LPT] = srv[0][k];
+      }
+      // every share is in LDS; the tile written here two batches ago has been read by all waves
+      // (each passed the barrier of the batch in between only after its reads)
+      lds_barrier();
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float sk = 1.f, sv = 1.f;  // low-bit row scales
@@ -387,9 +429,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
         if (!kQ8 || kOne || e < RK) sc += qt[e] * frag_elem<LS>(kr[u], e);
       if constexpr (R) {  // this lane's pieces of the token's rotary key
 #pragma unroll
-        for (int k = 0; k < NRP; ++k)
+        for (int k = 0; k < NRP; ++k) {
+          uint4 pc;
+          if constexpr (kHG)
+            pc = (sub + LPT * k < RPC) ? tile[(k * kStep + u * TPW) * LPT + lane] : make_uint4(0, 0, 0, 0);
+          else
+            pc = srv[u][k];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sc += qr[k][e] * frag_elem<BF16>(&srv[u][k], e);
+          for (int e = 0; e < 8; ++e) sc += qr[k][e] * frag_elem<BF16>(&pc, e);
+        }
       }
       sc = group_sum<LPT>(sc);
       if (kQ8) sc *= sk;
@@ -418,7 +466,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
     // consumed, so a wave always has a batch in flight. Rows past the split (or, gathered, with
     // a slot outside the cache) read as zeros through the descriptor bound (no memory access)
     // and are masked; a batch wholly past the split costs only its masked arithmetic.
-    auto issue = [&](int t0, uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], uint4 (&srv)[U][NSR]) {
+    auto issue = [&](int t0, uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], uint4 (&srv)[SRU][NSR]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int tok = t0 + u * TPW + grp;
@@ -431,10 +479,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
         }
         load_slice<SK, kAux, LPT>(rsk, rr * RKB, sub, kr[u]);
         load_slice<SV, kAux, LPT>(rsv, rr * RVB, sub, vr[u]);
+        if constexpr (!kHG) {
 #pragma unroll
-        for (int k = 0; k < NSR; ++k) {
-          const int c = sub + LPT * k;
-          srv[u][k] = (R && c < RPC) ? buffer_words<4, 0>(rss, rr * (DR * 2) + c * 16) : make_uint4(0, 0, 0, 0);
+          for (int k = 0; k < NSR; ++k) {
+            const int c = sub + LPT * k;
+            srv[u][k] = (R && c < RPC) ? buffer_words<4, 0>(rss, rr * (DR * 2) + c * 16) : make_uint4(0, 0, 0, 0);
+          }
+        }
+      }
+      if constexpr (kHG) {  // this wave's share: 1 KiB runs of the batch's rows (zeros past te)
+#pragma unroll
+        for (int k = 0; k < NSH; ++k) {
+          const int i = (wave + HG * k) * 64 + lane;
+          const int li = i / RPC, c = i % RPC;
+          const uint32_t rr = static_cast<uint32_t>(min(t0 + li, te) - row0);
+          srv[0][k] = (PB % (64 * HG) == 0 || i < PB) ? buffer_words<4, 0>(rss, rr * (DR * 2) + c * 16)
+                                                      : make_uint4(0, 0, 0, 0);
         }
       }
     };
@@ -447,9 +507,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
           ok[u] = ok[u] && static_cast<unsigned>(slot_s[min(tok - tb, kSlotCap - 1)]) < static_cast<unsigned>(p.n_max);
       }
     };
-    constexpr int kStep = TPW * U;
     uint4 ka[U][VK], va[U][VV], kb[U][VK], vb[U][VV];
-    uint4 sa[U][NSR], sb[U][NSR];
+    uint4 sa[SRU][NSR], sb[SRU][NSR];
     bool ok[U];
     if constexpr (G) {  // the first rows' slots come from the list the prologue stages
       prologue();
@@ -461,12 +520,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
     for (int t0 = tb; t0 < te; t0 += 2 * kStep) {
       issue(t0 + kStep, kb, vb, sb);
       mask(t0, ok);
-      consume(ka, va, ok, sa);
+      consume(ka, va, ok, sa, rt_s[0]);
       // no early exit here: with one exit at the bottom the compiler's wait before the loop top
       // leaves the batch just issued in flight (an exit here made it drain every load)
       issue(t0 + 2 * kStep, ka, va, sa);
       mask(t0 + kStep, ok);
-      consume(kb, vb, ok, sb);
+      consume(kb, vb, ok, sb, rt_s[kHG ? 1 : 0]);
     }
    }
   } else if constexpr (!kPipe) {  // the contiguous one-load read always takes the loop above
@@ -476,7 +535,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
       uint4 vr[U][VV];
       bool ok[U];
       int slot[U];
-      uint4 srv[U][NSR];
+      uint4 srv[SRU][NSR];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int tok = t0 + u * TPW + grp;
@@ -509,7 +568,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
           for (int i = 0; i < VV; ++i) vr[u][i] = make_uint4(0, 0, 0, 0);
         }
       }
-      consume(kr, vr, ok, srv);
+      consume(kr, vr, ok, srv, rt_s[0]);
     }
   }
 
@@ -528,7 +587,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
 
   // --- merge the workgroup's waves: waves 1.. hand (M, l, a) to wave 0 through LDS -----------
   float Mt = M;
-  if (nw > 1) {
+  if (!kHG && nw > 1) {
     __syncthreads();  // every wave is past its last read of xs_s (absorb_query)
     if (wave > 0) {
       float* xw = xs_s + (wave - 1) * (2 + RV);
@@ -560,26 +619,27 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
     }
   }
 
+  const bool out_wave = kHG ? live : wave == 0;  // the wave that holds the unit's merged partial
   if (p.splits > 1) {
     float* w = p.ws + (static_cast<size_t>(bh) * p.splits + split) * (2 + RV);
-    if (wave == 0 && lane == 0) {
+    if (out_wave && lane == 0) {
       w[0] = Mt;
       w[1] = l;
     }
-    if (wave == 0 && lane < LPT) {
+    if (out_wave && lane < LPT) {
 #pragma unroll
       for (int e = 0; e < EV; ++e)
         if (!kQ8 || lane * EV + e < RV) w[2 + slice_entry<kSplitV, EV, E16, LPT>(lane, e)] = acc[e];
     }
     return;
   }
-  if (wave == 0 && lane < LPT) {
+  if (out_wave && lane < LPT) {
 #pragma unroll
     for (int e = 0; e < EV; ++e)
       if (!kQ8 || lane * EV + e < RV) a_s[slice_entry<kSplitV, EV, E16, LPT>(lane, e)] = acc[e];
   }
   __syncthreads();
-  if (wave == 0) finish_unit<S>(p, b, h, Mt, l, a_s, q_s, lane);
+  if (out_wave) finish_unit<S>(p, b, h, Mt, l, a_s, q_s, lane);
 }
 
 // Log-sum-exp merge of the S split partials of one (b, h), then the same finish. 256 threads:
@@ -647,16 +707,23 @@ template <class S, int RK, int RV, int LPT, int U>
 PartialFn gather_fn() {
   return decode_partial_kernel<S, S, RK, RV, LPT, U, true>;
 }
-// the contiguous read with the rotary branch, one instance per rotary width (32, 64, 128); the
-// rotary pieces take registers beside the latent slices, so fewer tiles are in flight per batch
+// the contiguous read with the rotary branch, one instance per rotary width (32, 64, 128), one
+// wave per head (w*) or head groups of kRopeGroup waves (g*); a wave's own rotary pieces take
+// registers beside the latent slices, so fewer tiles are in flight per batch
+constexpr int kRopeGroup = 8;
 struct RopeFns {
   PartialFn w32, w64, w128;
+  PartialFn g32, g64, g128;
 };
 template <class S, int RK, int RV, int LPT, int U>
 RopeFns rope_fns() {
+  constexpr int U2 = U > 2 ? U / 2 : 1;
   return {decode_partial_kernel<S, S, RK, RV, LPT, U, false, 32>,
           decode_partial_kernel<S, S, RK, RV, LPT, U, false, 64>,
-          decode_partial_kernel<S, S, RK, RV, LPT, (U > 2 ? U / 2 : 1), false, 128>};
+          decode_partial_kernel<S, S, RK, RV, LPT, U2, false, 128>,
+          decode_partial_kernel<S, S, RK, RV, LPT, U, false, 32, kRopeGroup>,
+          decode_partial_kernel<S, S, RK, RV, LPT, U, false, 64, kRopeGroup>,
+          decode_partial_kernel<S, S, RK, RV, LPT, U2, false, 128, kRopeGroup>};
 }
 template <class LS, int RK, int RV, int LPT, int U>
 PartialFn q8_fn() {
@@ -695,23 +762,23 @@ const Entry kTable[] = {
      rope_fns<BF16, 96, 160, 16, 4>()},
     {LLA_BF16, 256, 256, partial_fn<BF16, 256, 256, 32, 8>(), gather_fn<BF16, 256, 256, 32, 8>(),
      rope_fns<BF16, 256, 256, 32, 4>()},
-    {LLA_F32, 8, 8, partial_fn<F32, 8, 8, 2, 4>(), gather_fn<F32, 8, 8, 2, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_F32, 16, 16, partial_fn<F32, 16, 16, 4, 4>(), gather_fn<F32, 16, 16, 4, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_F32, 24, 24, partial_fn<F32, 24, 24, 8, 4>(), gather_fn<F32, 24, 24, 8, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_F32, 32, 32, partial_fn<F32, 32, 32, 8, 4>(), gather_fn<F32, 32, 32, 8, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_F32, 64, 64, partial_fn<F32, 64, 64, 16, 4>(), gather_fn<F32, 64, 64, 16, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_F32, 96, 96, partial_fn<F32, 96, 96, 32, 4>(), gather_fn<F32, 96, 96, 32, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 32, 4>(), gather_fn<F32, 128, 128, 32, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_F32, 96, 160, partial_fn<F32, 96, 160, 8, 1>(), gather_fn<F32, 96, 160, 8, 1>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 64, 4>(), gather_fn<F32, 256, 256, 64, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_BF16_Q8, 8, 8, q8_fn<Q8, 8, 8, 1, 4>(), q8_gather_fn<Q8, 8, 8, 1, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_BF16_Q8, 16, 16, q8_fn<Q8, 16, 16, 2, 4>(), q8_gather_fn<Q8, 16, 16, 2, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_BF16_Q8, 24, 24, q8_fn<Q8, 24, 24, 2, 4>(), q8_gather_fn<Q8, 24, 24, 2, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_BF16_Q8, 32, 32, q8_fn<Q8, 32, 32, 4, 8>(), q8_gather_fn<Q8, 32, 32, 4, 8>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_BF16_I8, 8, 8, q8_fn<I8, 8, 8, 1, 4>(), q8_gather_fn<I8, 8, 8, 1, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_BF16_I8, 16, 16, q8_fn<I8, 16, 16, 2, 4>(), q8_gather_fn<I8, 16, 16, 2, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_BF16_I8, 24, 24, q8_fn<I8, 24, 24, 2, 4>(), q8_gather_fn<I8, 24, 24, 2, 4>(), RopeFns{nullptr, nullptr, nullptr}},
-    {LLA_BF16_I8, 32, 32, q8_fn<I8, 32, 32, 4, 8>(), q8_gather_fn<I8, 32, 32, 4, 8>(), RopeFns{nullptr, nullptr, nullptr}},
+    {LLA_F32, 8, 8, partial_fn<F32, 8, 8, 2, 4>(), gather_fn<F32, 8, 8, 2, 4>(), RopeFns{}},
+    {LLA_F32, 16, 16, partial_fn<F32, 16, 16, 4, 4>(), gather_fn<F32, 16, 16, 4, 4>(), RopeFns{}},
+    {LLA_F32, 24, 24, partial_fn<F32, 24, 24, 8, 4>(), gather_fn<F32, 24, 24, 8, 4>(), RopeFns{}},
+    {LLA_F32, 32, 32, partial_fn<F32, 32, 32, 8, 4>(), gather_fn<F32, 32, 32, 8, 4>(), RopeFns{}},
+    {LLA_F32, 64, 64, partial_fn<F32, 64, 64, 16, 4>(), gather_fn<F32, 64, 64, 16, 4>(), RopeFns{}},
+    {LLA_F32, 96, 96, partial_fn<F32, 96, 96, 32, 4>(), gather_fn<F32, 96, 96, 32, 4>(), RopeFns{}},
+    {LLA_F32, 128, 128, partial_fn<F32, 128, 128, 32, 4>(), gather_fn<F32, 128, 128, 32, 4>(), RopeFns{}},
+    {LLA_F32, 96, 160, partial_fn<F32, 96, 160, 8, 1>(), gather_fn<F32, 96, 160, 8, 1>(), RopeFns{}},
+    {LLA_F32, 256, 256, partial_fn<F32, 256, 256, 64, 4>(), gather_fn<F32, 256, 256, 64, 4>(), RopeFns{}},
+    {LLA_BF16_Q8, 8, 8, q8_fn<Q8, 8, 8, 1, 4>(), q8_gather_fn<Q8, 8, 8, 1, 4>(), RopeFns{}},
+    {LLA_BF16_Q8, 16, 16, q8_fn<Q8, 16, 16, 2, 4>(), q8_gather_fn<Q8, 16, 16, 2, 4>(), RopeFns{}},
+    {LLA_BF16_Q8, 24, 24, q8_fn<Q8, 24, 24, 2, 4>(), q8_gather_fn<Q8, 24, 24, 2, 4>(), RopeFns{}},
+    {LLA_BF16_Q8, 32, 32, q8_fn<Q8, 32, 32, 4, 8>(), q8_gather_fn<Q8, 32, 32, 4, 8>(), RopeFns{}},
+    {LLA_BF16_I8, 8, 8, q8_fn<I8, 8, 8, 1, 4>(), q8_gather_fn<I8, 8, 8, 1, 4>(), RopeFns{}},
+    {LLA_BF16_I8, 16, 16, q8_fn<I8, 16, 16, 2, 4>(), q8_gather_fn<I8, 16, 16, 2, 4>(), RopeFns{}},
+    {LLA_BF16_I8, 24, 24, q8_fn<I8, 24, 24, 2, 4>(), q8_gather_fn<I8, 24, 24, 2, 4>(), RopeFns{}},
+    {LLA_BF16_I8, 32, 32, q8_fn<I8, 32, 32, 4, 8>(), q8_gather_fn<I8, 32, 32, 4, 8>(), RopeFns{}},
 };
 
 const Entry* find(int dtype, int r_k, int r_v) {
@@ -791,9 +858,12 @@ hipError_t launch_valu(const DecodeParams& p, int dtype, PartialFn fn, hipStream
   if (p.splits > 1 &&
       static_cast<size_t>(p.B) * p.H * p.splits * (2 + p.r_v) * sizeof(float) > p.ws_bytes)
     return hipErrorInvalidValue;  // the plan does not fit the workspace: never launch
-  const unsigned units = static_cast<unsigned>(p.B) * p.H * p.splits;
-  const int nw = p.slots != nullptr ? 1 : std::min(std::max(p.wg_waves, 1), kMaxWaves);
-  if (p.chunk % (32 * nw) != 0) return hipErrorInvalidValue;  // waves take whole 32-token parts
+  const int hg = p.wg_heads > 1 ? p.wg_heads : 1;
+  if (hg > 1 && (hg != kRopeGroup || p.d_rope == 0 || p.slots != nullptr || p.wg_waves > 1))
+    return hipErrorInvalidValue;  // head groups: the compiled size, rotary read only
+  const unsigned units = static_cast<unsigned>(p.B) * ((p.H + hg - 1) / hg) * p.splits;
+  const int nw = hg > 1 ? hg : p.slots != nullptr ? 1 : std::min(std::max(p.wg_waves, 1), kMaxWaves);
+  if (hg == 1 && p.chunk % (32 * nw) != 0) return hipErrorInvalidValue;  // waves take whole 32-token parts
   hipLaunchKernelGGL(fn, dim3(units), dim3(64 * nw), 0, stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;
@@ -846,9 +916,23 @@ bool rope_supported(const lla_desc& desc, int d_rope) {
   return e != nullptr && e->rfn.w64 != nullptr;
 }
 
+// Head groups pay where the rotary rows, not the latents, set the L2 traffic, so whenever groups
+// of kRopeGroup heads leave at most a quarter of the waves as placeholders (H = 8, 16, 40, 130 ...).
+void rope_plan(const lla_desc& desc, int B, int* splits, int* chunk, int* wg_waves, int* wg_heads) {
+  const int padded = (desc.H + kRopeGroup - 1) / kRopeGroup * kRopeGroup;
+  if (!decode_uses_mfma2d(desc) && desc.H >= kRopeGroup && 4 * padded <= 5 * desc.H) {
+    valu_plan(desc, B, splits, chunk);  // one wave per (row, head, split): no wave token parts
+    *wg_waves = 1;
+    *wg_heads = kRopeGroup;
+    return;
+  }
+  decode_plan(desc, B, splits, chunk, wg_waves);
+  *wg_heads = 1;
+}
+
 size_t rope_workspace_bytes(const lla_desc& desc, int B) {
-  int s, c, nw;
-  decode_plan(desc, B, &s, &c, &nw);
+  int s, c, nw, hg;
+  rope_plan(desc, B, &s, &c, &nw, &hg);
   // LLA-2D on MFMA: the branch is fused into the read (q~ rows widened by up to 128 entries)
   if (decode_uses_mfma2d(desc)) return decode2d_workspace_bytes(desc, B, s, 128);
   // streaming read: the rotary scores are formed in the read; only its split partials
@@ -860,7 +944,10 @@ hipError_t launch_decode_rope(const DecodeParams& p, int dtype, hipStream_t stre
     return launch_decode2d(p, stream);  // rotary keys as extra MFMA k-steps of the read
   const Entry* e = find(dtype, p.r_k, p.r_v);
   if (e == nullptr) return hipErrorNotSupported;
-  const PartialFn fn = p.d_rope == 32 ? e->rfn.w32 : p.d_rope == 64 ? e->rfn.w64 : p.d_rope == 128 ? e->rfn.w128 : nullptr;
+  const bool grp = p.wg_heads > 1;
+  const PartialFn fn = p.d_rope == 32 ? (grp ? e->rfn.g32 : e->rfn.w32)
+                     : p.d_rope == 64 ? (grp ? e->rfn.g64 : e->rfn.w64)
+                     : p.d_rope == 128 ? (grp ? e->rfn.g128 : e->rfn.w128) : nullptr;
   if (fn == nullptr) return hipErrorNotSupported;
   return launch_valu(p, dtype, fn, stream);
 }

@@ -291,16 +291,6 @@ __device__ __forceinline__ floatx16_t mfma3232(uint4 a, uint4 b, floatx16_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// workgroup barrier of the ring: this wave's LDS reads have returned, then all waves arrive. It
-// does not wait for the global_load_lds transfers in flight into other stages (a workgroup-scope
-// release fence, as in __syncthreads(), would count them as pending LDS writes).
-__device__ __forceinline__ void ring_barrier_g() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
 __device__ __forceinline__ int gswz(int row, int c) { return c ^ ((row >> 2) & 3); }
 
 // An LDS offset the compiler must treat as unknown. Reads of a ring stage whose addresses it
@@ -441,7 +431,7 @@ __global__ __launch_bounds__(512) void encode_gemm_kernel(EncodeParams p) {
   auto step = [&](auto S, int s) {
     constexpr int st = decltype(S)::value;
     __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * LPW));  // vmcnt(2 * LPW)
-    ring_barrier_g();
+    lds_barrier();  // (lla_device.h) not a full fence: later stages stay in flight
     issue(s + 3, astage(GStage<(st + 3) % kGStages>{}), bstage(GStage<(st + 3) % kGStages>{}));
     const char* at = astage(S);
     const char* bt = bstage(S);

@@ -50,6 +50,18 @@ __device__ __forceinline__ void buffer_lds16(const void* base, int bytes, __attr
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voffset, soffset, 0, 0);
 }
 
+// Workgroup barrier for LDS hand-offs: this wave's LDS accesses have completed (lgkmcnt(0)), then
+// every wave arrives. Unlike __syncthreads() it neither waits for this wave's global loads still in
+// flight into registers nor for global_load_lds transfers into other buffers (a workgroup-scope
+// release fence counts those as pending LDS writes and waits for all of them). The memory clobbers
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // float32 -> bf16 bits, round to nearest, ties to even; NaN stays NaN (gfx950's v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));

@@ -34,6 +34,9 @@ struct DecodeParams {
   // Waves of one workgroup that share a (row, head, split): each takes chunk / wg_waves of the
   // split's tokens and the partials merge in LDS (streaming kernels; 0 or 1: one wave).
   int32_t wg_waves;
+  // Rotary read (streaming): heads of one row per workgroup (0 or 1: one; else the compiled head
+  // group), which share each batch's rotary rows through LDS. Excludes wg_waves > 1.
+  int32_t wg_heads;
   float scale_log2;   // softmax scale * log2(e)
   size_t ws_bytes;    // bytes available at ws; launchers refuse a plan that does not fit
   // Gather-indexed read (lla_attend_decode_gather): row b attends the latents at
@@ -145,6 +148,8 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 // Decoupled rotary branch (rope.hip, decode.hip).
 hipError_t launch_rope_write(const RopeWriteParams& p, hipStream_t s);
 bool rope_supported(const lla_desc& desc, int d_rope);
+// Plan of one lla_attend_decode_rope call (decode_plan, or head groups for the streaming read).
+void rope_plan(const lla_desc& desc, int B, int* splits, int* chunk, int* wg_waves, int* wg_heads);
 size_t rope_workspace_bytes(const lla_desc& desc, int B);
 hipError_t launch_decode_rope(const DecodeParams& p, int dtype, hipStream_t s);
 // Reconstruct-then-attend comparator (reconstruct.hip).

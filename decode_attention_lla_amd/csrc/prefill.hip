@@ -148,17 +148,6 @@ struct StageIdx {
   static constexpr int value = N;
 };
 
-// Workgroup barrier of the ring: this wave's LDS reads have all returned, then every wave arrives.
-// Unlike __syncthreads() it does not wait for the global_load_lds transfers still in flight into
-// later stages (a workgroup-scope release fence counts them as pending LDS writes and waits for
-// all of them). The memory clobbers keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void ring_barrier() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vm_tiles(int ahead) {
   // vmcnt(ahead * N) for ahead in 0..kStages-1, N loads per tile and wave
@@ -407,7 +396,7 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     // ... and every other wave's; everyone has also finished computing tile - 1, whose stage is
     // refilled once this tile's score MFMAs are issued (requested right after the barrier, the
     // transfers contend with the score phase's K reads: 2-3% slower at r = 256)
-    ring_barrier();
+    lds_barrier();  // (lla_device.h) not a full fence: later stages stay in flight
     const char* kt = kstage(S);
     const char* rt_ = rstage(S);
     const char* vt = vstage(S);

@@ -195,15 +195,33 @@ def test_gather_unsupported_and_workspace():
     assert lla.lla_gather_workspace_bytes(d, 2, 0) == 0
 
 
-def test_rope_workspace_is_the_decode_plan():
-    """The rotary read forms its rotary scores inside the read, so its workspace is the split
-    partials of the decode plan (none when the plan has one split per row and head)."""
+def _one_wave_splits(H, B, n_max):
+    """Token splits of the streaming plan with one wave per (row, head, split): about 2048 waves,
+    parts of at least 256 tokens, at most 256 splits, chunks a multiple of 128 tokens."""
+    want = min(-(-2048 // (B * H)), max(n_max // 256, 1))
+    s = min(max(want, 1), 256)
+    c = -(-n_max // s)
+    c = -(-c // 128) * 128
+    return -(-n_max // c)
+
+
+def test_rope_workspace_follows_the_rope_plan():
+    """The rotary read forms its rotary scores inside the read, so its workspace holds only split
+    partials: under the decode plan where heads are not grouped (H < 8, or groups of 8 that would
+    leave more than a quarter of the waves as placeholders), else under the one-wave plan of the
+    head-group read (none when that plan has one split per row and head)."""
     lib = lla.library()
-    for d, B in ((desc(H=64, r_k=8, r_v=8, n_max=5000), 64), (desc(H=16, r_k=24, r_v=24, n_max=4097), 768),
-                 (desc(H=16, r_k=24, r_v=24, n_max=4097), 2), (desc(H=2, r_k=24, r_v=24, n_max=70000), 3)):
+    for d, B in ((desc(H=2, r_k=24, r_v=24, n_max=70000), 3), (desc(H=9, r_k=24, r_v=24, n_max=9000), 2),
+                 (desc(H=5, r_k=96, r_v=160, n_max=70000), 1)):
         need = lib.lla_rope_workspace_bytes(ctypes.byref(d), B)
-        assert need == lla.lla_workspace_bytes(d, B)
-    assert lib.lla_rope_workspace_bytes(ctypes.byref(desc(H=2, r_k=24, r_v=24, n_max=70000)), 3) > 0
+        assert need == lla.lla_workspace_bytes(d, B) > 0
+    for H, r, n_max, B in ((16, 24, 4097, 768), (16, 24, 4097, 2), (64, 8, 5000, 64), (40, 32, 9000, 3),
+                           (130, 24, 3000, 1)):
+        d = desc(H=H, r_k=r, r_v=r, n_max=n_max)
+        s = _one_wave_splits(H, B, n_max)
+        want = 0 if s == 1 else B * H * s * (2 + r) * 4
+        assert lib.lla_rope_workspace_bytes(ctypes.byref(d), B) == want, (H, r, n_max, B)
+    assert lib.lla_rope_workspace_bytes(ctypes.byref(desc(H=16, r_k=24, r_v=24, n_max=4097)), 2) > 0
 
 
 def test_gather_plan_keeps_splits_within_the_staged_list():
@@ -317,7 +335,7 @@ def test_rope_arguments_support_and_workspace():
     # a long cache at small B * H needs them
     dl = desc(r_k=24, r_v=24, n_max=5000)
     need = lla.lla_rope_workspace_bytes(dl, 2)
-    assert need > 0 and need == lla.lla_workspace_bytes(dl, 2, 1)
+    assert need == 2 * 16 * _one_wave_splits(16, 2, 5000) * (2 + 24) * 4 > 0  # head groups of 8
     assert need % (2 * 16 * (2 + 24) * 4) == 0
     assert rope_decode(dl) == lla.LLA_ERR_WORKSPACE
     assert rope_decode(dl, ws=A, wsb=need - 1) == lla.LLA_ERR_WORKSPACE

@@ -155,6 +155,41 @@ def test_decode_rope_xcd_grouped(variant, rk, rv, d_rope, H):
     assert_lse(host(lse), rl, what)
 
 
+@pytest.mark.parametrize("variant,rk,rv,d_rope,H,lens", [
+    ("per_head", 96, 160, 128, 8, [3001, 0]),                # one group, token splits, partial shares
+    ("per_head", 24, 24, 64, 20, [2000, 777, 1]),            # 3 groups, 4 placeholder waves
+    ("2d", 32, 32, 32, 8, [1500, 100]),                      # LLA-2D on the streaming read
+    ("per_head", 8, 8, 128, 16, [1000, 999, 1, 0, 513, 512, 64, 65]),  # B = 8: XCD-grouped
+])
+def test_decode_rope_head_groups(variant, rk, rv, d_rope, H, lens):
+    """The rotary read with workgroups of 8 heads of one sequence sharing each batch's rotary rows
+    through LDS: with token splits, with placeholder waves past H, for both variants and the three
+    rotary widths, ragged lengths, sharpened queries, self token and mu."""
+    B, d, T = len(lens), 32, 2
+    n_max = max(lens)
+    lens = np.array(lens, np.int32)
+    desc = mk_desc(variant, "bf16", H, d, T, rk, rv, n_max)
+    ws = lla.rope_workspace(desc, B)
+    rng = np.random.default_rng(9960 + H + d_rope)
+    q_rope, k_rope, krs = _rope_inputs(rng, B, H, n_max, d_rope)
+    c = upload(synth.random_case(variant, "bf16", B, H, d, T, rk, rv, n_max, 9961 + H + rk, q_gain=4.0), "bf16")
+    t = 1
+    q = dev(c["q"][t], "bf16")
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H), float("nan"), device="cuda")
+    print(f"head groups {variant} r=({rk},{rv}) d_rope={d_rope} H={H} B={B}", flush=True)
+    lla.lla_attend_decode_rope(desc, B, t, q, dev(q_rope, "bf16"), c["_zk"], c["_zv"], dev(k_rope, "bf16"),
+                               d_rope, 0.0, dev(lens), c["_Wk"], c["_Wv"], c["_muk"], c["_muv"],
+                               dev(c["k_self"][t], "bf16"), dev(c["v_self"][t], "bf16"), dev(krs, "bf16"),
+                               out, lse, ws)
+    torch.cuda.synchronize()
+    ro, rl = O.attend_decode_rope(c["q"][t], q_rope, c["zk"], c["zv"], k_rope, c["Wk"], c["Wv"], t, lens,
+                                  c["mu_k"], c["mu_v"], c["k_self"][t], c["v_self"][t], krs, variant=variant)
+    what = f"rope head groups {variant} r=({rk},{rv}) d_rope={d_rope} H={H}"
+    assert_close(host(out), ro, "bf16", what)
+    assert_lse(host(lse), rl, what)
+
+
 def test_decode_rope_many_units_ragged():
     """4096 (row, head) units over 5000 cached tokens, one split per row, with ragged lengths
     around multiples of 1024 and of the kernel's batch."""
