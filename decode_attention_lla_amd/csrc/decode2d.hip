@@ -80,48 +80,88 @@ __device__ __forceinline__ int seq_keys(const DecodeParams& p, int b) {
 }
 
 // ---- 1. query absorption for every (b, h) ------------------------------------------------------
-// grid H * ceil(B / kQB) (x), 256 threads. W^K_t[h] (d x RK bf16) is staged in LDS with one round of
-// 16-byte loads; thread k then forms q~[b][h][k] for kQB sequences from LDS.
+// grid H * ceil(B / kQB) (x), 256 threads. Wave w takes rows j in [32 w, 32 w + 32) of W^K_t[h]
+// (d <= 128), lane l the CPL = RK / 64 columns l * CPL .. of each of those rows, so every load
+// instruction reads one whole W^K row and a thread's 32 loads are all issued before its sums. Each
+// thread forms its columns' partial q~ over its rows for kQB sequences; the four waves' partials
+// meet in LDS.
 // qt rows hold RK + DR floats: q~, then the rotated rotary query (both times scale * log2 e).
+template <int CPL>
+struct WSlice;  // CPL consecutive bf16 of a W^K row
+template <>
+struct WSlice<1> { using T = uint16_t; };
+template <>
+struct WSlice<2> { using T = uint32_t; };
+template <>
+struct WSlice<4> { using T = uint2; };
+template <int CPL>
+__device__ __forceinline__ float wslice_elem(const typename WSlice<CPL>::T& w, int e) {
+  if constexpr (CPL == 1) return __uint_as_float(static_cast<uint32_t>(w) << 16);
+  else if constexpr (CPL == 2) return e == 0 ? bf16_lo(w) : bf16_hi(w);
+  else return e == 0 ? bf16_lo(w.x) : e == 1 ? bf16_hi(w.x) : e == 2 ? bf16_lo(w.y) : bf16_hi(w.y);
+}
+
 template <int RK, int DR>
 __global__ __launch_bounds__(256) void qproj2d_kernel(DecodeParams p, float* qt, float* beta) {
   constexpr int QS = RK + DR;
-  __shared__ float q_s[kQB][128];
-  __shared__ __attribute__((aligned(16))) uint16_t w_s[128 * RK];
+  constexpr int CPL = RK / 64;
+  constexpr int JQ = 32;  // rows of W^K per wave
+  static_assert(CPL == 1 || CPL == 2 || CPL == 4, "r_k of 64, 128 or 256");
+  using WT = typename WSlice<CPL>::T;
+  __shared__ __attribute__((aligned(16))) float q_s[kQB][128];
+  __shared__ float red_s[4][kQB][RK];
   const int h = blockIdx.x % p.H;  // one-dimensional grid: (block of kQB sequences) * H + head
   const int b0 = blockIdx.x / p.H * kQB;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const size_t wrow = (static_cast<size_t>(p.t) * p.H + h) * p.d;  // rows of W^K_t for head h
-  const uint4* wsrc = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.Wk) + wrow * RK);
-  constexpr int kChunks = 128 * RK / 8;
-  const int nchunk = p.d * RK / 8;
-  uint4 wreg[kChunks / 256 > 0 ? kChunks / 256 : 1];
+  const WT* wsrc = reinterpret_cast<const WT*>(static_cast<const uint16_t*>(p.Wk) + wrow * RK) + lane;
+  WT wv[JQ];
 #pragma unroll
-  for (int i = 0; i < kChunks / 256; ++i) {
-    const int c = i * 256 + tid;
-    wreg[i] = c < nchunk ? wsrc[c] : make_uint4(0, 0, 0, 0);
+  for (int jj = 0; jj < JQ; ++jj) {
+    const int j = wave * JQ + jj;
+    wv[jj] = j < p.d ? wsrc[static_cast<size_t>(j) * 64] : WT{};
   }
-  for (int i = tid; i < kQB * p.d; i += 256) {
-    const int bb = i / p.d;
-    const int j = i - bb * p.d;
+  // q of the block's sequences, zero past d and past B
+  for (int i = tid; i < kQB * 128; i += 256) {
+    const int bb = i >> 7;
+    const int j = i & 127;
     const int b = b0 + bb;
-    q_s[bb][j] = b < p.B ? ld<BF16>(p.q, (static_cast<size_t>(b) * p.H + h) * p.d + j) : 0.f;
+    q_s[bb][j] = (b < p.B && j < p.d) ? ld<BF16>(p.q, (static_cast<size_t>(b) * p.H + h) * p.d + j) : 0.f;
+  }
+  __syncthreads();
+  float acc[kQB][CPL];
+#pragma unroll
+  for (int bb = 0; bb < kQB; ++bb)
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) acc[bb][e] = 0.f;
+#pragma unroll
+  for (int j4 = 0; j4 < JQ; j4 += 4) {
+    float4 qv[kQB];
+#pragma unroll
+    for (int bb = 0; bb < kQB; ++bb) qv[bb] = *reinterpret_cast<const float4*>(&q_s[bb][wave * JQ + j4]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        const float w = wslice_elem<CPL>(wv[j4 + u], e);
+#pragma unroll
+        for (int bb = 0; bb < kQB; ++bb)
+          acc[bb][e] += w * (u == 0 ? qv[bb].x : u == 1 ? qv[bb].y : u == 2 ? qv[bb].z : qv[bb].w);
+      }
   }
 #pragma unroll
-  for (int i = 0; i < kChunks / 256; ++i) reinterpret_cast<uint4*>(w_s)[i * 256 + tid] = wreg[i];
+  for (int bb = 0; bb < kQB; ++bb)
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) red_s[wave][bb][lane * CPL + e] = acc[bb][e];
   __syncthreads();
-  for (int k = tid; k < RK; k += 256) {
-    float acc[kQB];
-#pragma unroll
-    for (int bb = 0; bb < kQB; ++bb) acc[bb] = 0.f;
-    for (int j = 0; j < p.d; ++j) {
-      const float w = __uint_as_float(static_cast<uint32_t>(w_s[j * RK + k]) << 16);
-#pragma unroll
-      for (int bb = 0; bb < kQB; ++bb) acc[bb] += w * q_s[bb][j];
-    }
-#pragma unroll
-    for (int bb = 0; bb < kQB; ++bb)
-      if (b0 + bb < p.B) qt[(static_cast<size_t>(b0 + bb) * p.H + h) * QS + k] = acc[bb] * p.scale_log2;
+  for (int i = tid; i < kQB * RK; i += 256) {
+    const int bb = i / RK;
+    const int k = i - bb * RK;
+    if (b0 + bb < p.B)
+      qt[(static_cast<size_t>(b0 + bb) * p.H + h) * QS + k] =
+          ((red_s[0][bb][k] + red_s[1][bb][k]) + (red_s[2][bb][k] + red_s[3][bb][k])) * p.scale_log2;
   }
   if constexpr (DR > 0) {
     // rotary query of each sequence rotated at its decoding position N_b (the sequence differs
@@ -142,8 +182,6 @@ __global__ __launch_bounds__(256) void qproj2d_kernel(DecodeParams p, float* qt,
     }
   }
   // beta = scale*log2e * q . mu^K_t (2D mu is [T*H*d], loop t head h at (t*H + h)*d)
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
   for (int bb = wave; bb < kQB; bb += 4) {
     float part = 0.f;
     if (p.mu_k != nullptr)
@@ -368,18 +406,20 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
 }
 
 // ---- 3. merge splits, project once through W^V_t[h], finish ------------------------------------
-// One 256-thread workgroup per (head, block of kQB sequences): W^V_t[h] is read once for the block
-// (thread pair (j, half) holds half of row j in registers). Every load that does not depend on the
-// merge (W^V rows, the split partials of all kQB sequences, q, the self K/V, mu^V_t) is issued
-// first; wave w merges sequences w, w + 4, ... (log-sum-exp over the splits, the self token), the
-// merged latent sums go to LDS, and each thread pair dots its row with every sequence's sum.
+// One 256-thread workgroup per (head, block of kQB sequences): W^V_t[h] is read once for the block.
+// Thread (grp, sub) = (tid / 16, tid % 16) holds rows grp + 16 i (i < 8: d <= 128) of it, 16-byte
+// chunks sub + 16 k of each, so each load instruction reads whole runs of four consecutive rows.
+// Every load that does not depend on the merge (W^V, the first split partials of all kQB
+// sequences, mu^V_t) is issued first; wave w merges sequences w, w + 4, ... (log-sum-exp over the
+// splits, the self token), the merged latent sums go to LDS, each thread dots its row slices with
+// them, 16 lanes sum each row, and lane sub writes row grp + 16 sub.
 template <int RV>
 __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const float* part) {
-  constexpr int HALF = RV / 2;
-  static_assert(HALF % 8 == 0, "half a W^V row must be whole 16-byte runs");
-  constexpr int RPT = (RV + 255) / 256;  // latent entries per thread
+  constexpr int CPR = RV / 8;            // 16-byte chunks of a W^V row
+  constexpr int NC = (CPR + 15) / 16;    // chunks per thread and row
+  constexpr int RPT = (RV + 255) / 256;  // latent entries per thread in the merge
   constexpr int kPre = 2;                // splits whose partial sums are loaded up front
-  __shared__ float a_s[kQB][RV];
+  __shared__ __attribute__((aligned(16))) float a_s[kQB][RV];
   __shared__ float f_s[kQB][64];
   __shared__ float fin_s[kQB][4];  // f_lat, p_self, 1/den, l
   const int h = blockIdx.x % p.H;  // one-dimensional grid: (block of kQB sequences) * H + head
@@ -390,19 +430,25 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
   const int S_ = p.splits;
   const size_t wrow = (static_cast<size_t>(p.t) * p.H + h) * p.d;  // W^V_t rows of head h; mu offset
 
-  // ---- issue: W^V row half of this thread (d <= 128: one row per thread pair) ----
-  const int half = tid & 1;
-  const int j = tid >> 1;
-  const bool jok = j < p.d;
-  uint4 w[HALF / 8];
+  // ---- issue: this thread's slices of W^V_t[h] ----
+  const int grp = tid >> 4;
+  const int sub = tid & 15;
+  uint4 w[8][NC];
   {
-    const uint4* wr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.Wv) +
-                                                     (wrow + (jok ? j : 0)) * RV + half * HALF);
+    const uint4* wr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.Wv) + wrow * RV);
 #pragma unroll
-    for (int i = 0; i < HALF / 8; ++i) w[i] = wr[i];
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        const int j = grp + 16 * i;
+        const int c = sub + 16 * k;
+        w[i][k] = (j < p.d && c < CPR) ? wr[static_cast<size_t>(j) * CPR + c] : make_uint4(0, 0, 0, 0);
+      }
   }
+  const int jw = grp + 16 * sub;  // the row this thread writes (sub < 8)
+  const bool jok = sub < 8 && jw < p.d;
   float mu_j = 0.f;
-  if (jok && half == 0 && p.mu_v != nullptr) mu_j = ld<BF16>(p.mu_v, wrow + j);
+  if (jok && p.mu_v != nullptr) mu_j = ld<BF16>(p.mu_v, wrow + jw);
   // split latent sums of the first kPre splits for every sequence of the block
   float pa[kQB][RPT][kPre];
 #pragma unroll
@@ -473,22 +519,35 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
   for (int bb = 0; bb < kQB; ++bb) {
     const int b = b0 + bb;
     if (b >= p.B) break;
-    const float* ah = a_s[bb] + half * HALF;
-    float o = 0.f;
+    float av[NC][8];
 #pragma unroll
-    for (int i = 0; i < HALF / 8; ++i) {
-      o += bf16_lo(w[i].x) * ah[8 * i + 0] + bf16_hi(w[i].x) * ah[8 * i + 1];
-      o += bf16_lo(w[i].y) * ah[8 * i + 2] + bf16_hi(w[i].y) * ah[8 * i + 3];
-      o += bf16_lo(w[i].z) * ah[8 * i + 4] + bf16_hi(w[i].z) * ah[8 * i + 5];
-      o += bf16_lo(w[i].w) * ah[8 * i + 6] + bf16_hi(w[i].w) * ah[8 * i + 7];
+    for (int k = 0; k < NC; ++k) {
+      const int c = min(sub + 16 * k, CPR - 1);  // chunks past the row hold zero weights
+      const float4 x0 = *reinterpret_cast<const float4*>(&a_s[bb][8 * c]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&a_s[bb][8 * c + 4]);
+      av[k][0] = x0.x; av[k][1] = x0.y; av[k][2] = x0.z; av[k][3] = x0.w;
+      av[k][4] = x1.x; av[k][5] = x1.y; av[k][6] = x1.z; av[k][7] = x1.w;
     }
-    o += __shfl_xor(o, 1, 64);
-    if (jok && half == 0) {
+    float mine = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float o = 0.f;
+#pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        o += bf16_lo(w[i][k].x) * av[k][0] + bf16_hi(w[i][k].x) * av[k][1];
+        o += bf16_lo(w[i][k].y) * av[k][2] + bf16_hi(w[i][k].y) * av[k][3];
+        o += bf16_lo(w[i][k].z) * av[k][4] + bf16_hi(w[i][k].z) * av[k][5];
+        o += bf16_lo(w[i][k].w) * av[k][6] + bf16_hi(w[i][k].w) * av[k][7];
+      }
+      o = group_sum<16>(o);
+      if (sub == i) mine = o;
+    }
+    if (jok) {
       const size_t bh = static_cast<size_t>(b) * p.H + h;
-      o += fin_s[bb][3] * mu_j;
+      float o = mine + fin_s[bb][3] * mu_j;
       o *= fin_s[bb][0];
-      if (p.v_self != nullptr) o += fin_s[bb][1] * ld<BF16>(p.v_self, bh * p.d + j);
-      st<BF16>(p.out, bh * p.d + j, o * fin_s[bb][2]);
+      if (p.v_self != nullptr) o += fin_s[bb][1] * ld<BF16>(p.v_self, bh * p.d + jw);
+      st<BF16>(p.out, bh * p.d + jw, o * fin_s[bb][2]);
     }
   }
 }
