@@ -410,9 +410,9 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
 // Thread (grp, sub) = (tid / 16, tid % 16) holds rows grp + 16 i (i < 8: d <= 128) of it, 16-byte
 // chunks sub + 16 k of each, so each load instruction reads whole runs of four consecutive rows.
 // Every load that does not depend on the merge (W^V, the first split partials of all kQB
-// sequences, mu^V_t) is issued first; wave w merges sequences w, w + 4, ... (log-sum-exp over the
-// splits, the self token), the merged latent sums go to LDS, each thread dots its row slices with
-// them, 16 lanes sum each row, and lane sub writes row grp + 16 sub.
+// sequences, mu^V_t, the self values) is issued first; wave w merges sequences w, w + 4, ...
+// (log-sum-exp over the splits, the self token), the merged latent sums go to LDS, each thread
+// dots its row slices with them, 16 lanes sum each row, and lane sub writes row grp + 16 sub.
 template <int RV>
 __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const float* part) {
   constexpr int CPR = RV / 8;            // 16-byte chunks of a W^V row
@@ -449,6 +449,11 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
   const bool jok = sub < 8 && jw < p.d;
   float mu_j = 0.f;
   if (jok && p.mu_v != nullptr) mu_j = ld<BF16>(p.mu_v, wrow + jw);
+  float vself[kQB];  // this thread's row of each sequence's self value
+#pragma unroll
+  for (int bb = 0; bb < kQB; ++bb)
+    vself[bb] = (jok && p.v_self != nullptr && b0 + bb < p.B)
+                    ? ld<BF16>(p.v_self, (static_cast<size_t>(b0 + bb) * p.H + h) * p.d + jw) : 0.f;
   // split latent sums of the first kPre splits for every sequence of the block
   float pa[kQB][RPT][kPre];
 #pragma unroll
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(256) void combine2d_kernel(DecodeParams p, const fl
       const size_t bh = static_cast<size_t>(b) * p.H + h;
       float o = mine + fin_s[bb][3] * mu_j;
       o *= fin_s[bb][0];
-      if (p.v_self != nullptr) o += fin_s[bb][1] * ld<BF16>(p.v_self, bh * p.d + jw);
+      o += fin_s[bb][1] * vself[bb];
       st<BF16>(p.out, bh * p.d + jw, o * fin_s[bb][2]);
     }
   }

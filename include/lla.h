@@ -221,10 +221,12 @@ size_t lla_rope_workspace_bytes(const lla_desc* desc, int32_t B);
  * the width of the concatenated key.
  *   q_rope [device] bf16 [B][H][d_rope], unrotated; k_rope_self [device] bf16 [B][d_rope], given
  *   exactly when k_self is; ws at least lla_rope_workspace_bytes(desc, B) bytes (NULL if 0).
- * The rotary scores are formed inside the read: each token's rotary key is streamed beside its
- * latent rows and dotted with the head's rotated rotary query (LLA-2D on MFMA: extra contraction
- * steps of the read). All heads of a sequence read the same rotary keys; when B is a multiple of 8
- * they run on one XCD, so the keys come from HBM about once per sequence.
+ * The rotary scores are formed inside the read: each token's rotary key is read beside its latent
+ * rows and dotted with the head's rotated rotary query (LLA-2D on MFMA: extra contraction steps of
+ * the read). All heads of a sequence read the same rotary keys: on the streaming read, workgroups
+ * of 8 heads load each rotary row once and share it (when H >= 8 groups well), and when B is a
+ * multiple of 8 a sequence's workgroups run on one XCD, so the keys come from HBM about once per
+ * sequence.
  * LLA_BF16, d_rope 32, 64 or 128, the streaming bf16 (r_k, r_v) pairs (both variants) or the
  * LLA-2D MFMA pairs; otherwise LLA_ERR_UNSUPPORTED. */
 lla_status lla_attend_decode_rope(const lla_desc* desc, int32_t B, int32_t t, const void* q,

@@ -4,7 +4,7 @@ HIP caps the y and z grid dimensions at 65535 workgroups, so every launch keeps 
 counts in x. These cases put the batch-dependent count of each multi-dimensional launch past
 that cap, with short ragged caches, and compare sampled sequences with the oracle:
 the LLA-2D MFMA read (its query projection, split read and merge, with and without the fused
-rotary branch) at B = 270000, the per-head rotary score pre-pass at B = 70000, and the
+rotary branch) at B = 270000, the per-head rotary read at B = 70000, and the
 reconstruct comparator at B * H = 67200.
 """
 import numpy as np
@@ -80,7 +80,7 @@ def test_lla2d_decode_batch_past_grid_limit(rope):
     assert_lse(host(lse[rows]), rl, what)
 
 
-def test_per_head_rope_scores_batch_past_grid_limit():
+def test_per_head_rope_batch_past_grid_limit():
     B, H, d, T, r, n_max, d_rope = 70000, 1, 64, 1, 24, 17, 32
     rng = np.random.default_rng(20101)
     desc = mk_desc("per_head", "bf16", H, d, T, r, r, n_max)
