@@ -312,7 +312,8 @@ def per_head_layer(args, name):
     token's own loop-t K/V, its own W^K_t/W^V_t), then the encode of the new token into slot N.
     ouro_layer: H=16, d=128, T=4, r=32/32, B=32, N=4096 (one Ouro-1.4B-shaped layer, 16x);
     deep_loop: H=40, d=96, T=32, r=96/96, B=64, N=4096 (square 96x96 factors, 32x).
-    read_us is the mean over the step's T reads (HIP events on the launch stream)."""
+    read_us is the time of a step's T back-to-back reads divided by T (HIP events on the launch
+    stream before the first read and after the last, so no event sits between two reads)."""
     import torch
     from decode_attention_lla_amd import lla, synth
     s = synth.CASES[name]
@@ -338,16 +339,16 @@ def per_head_layer(args, name):
     pairs = []
 
     def step(record=False):
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
         for t in range(T):
-            if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
             lla.lla_attend_decode(desc, B, t, q[t], zk, zv, lens, Wk, Wv, None, None, ks[t], vs[t],
                                   out[t], None, ws, stream)
-            if record:
-                e1 = torch.cuda.Event(enable_timing=True)
-                e1.record(stream)
-                pairs.append((e0, e1))
+        if record:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record(stream)
+            pairs.append((e0, e1))
         lla.lla_encode(desc, B, 1, x[0], x[1], Ek, Ev, None, None, lens, zk, zv, stream)
 
     steps = 20 if T <= 4 else 5
@@ -355,7 +356,7 @@ def per_head_layer(args, name):
     for _ in range(steps):
         step(True)
     torch.cuda.synchronize()
-    ms_read = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    ms_read = float(np.mean([a.elapsed_time(b) for a, b in pairs])) / T
     latent = B * H * N * (rk + rv) * 2
     res = {"workload": f"{name}: 1 layer, H={H}, d_head={d}, T={T}, r_k={rk}, r_v={rv}, B={B}, "
                        f"N={N}, bf16",

@@ -145,13 +145,15 @@ __device__ __forceinline__ int slice_entry(int sub, int e) {
 constexpr int kMaxWaves = 8;
 
 // q~ = scale*log2(e) * W^K_t[h]^T q of one (row, head) into qt_s[RK], by the nw waves of the
-// workgroup (q in q_s). Each lane owns one 16-byte piece of the W^K rows (VE consecutive r) and a
-// residue class of rows j: every load it makes is issued before the sums and the whole slice
-// arrives in about one memory round trip. Lanes sharing a piece add up in registers (DPP), the
-// waves through LDS (red_s [kMaxWaves][RK]).
+// workgroup (q at element qoff of p.q). Each lane owns one 16-byte piece of the W^K rows (VE
+// consecutive r) and a residue class of rows j, and loads those rows' q entries itself: every load
+// it makes is issued before the sums and the whole slice arrives in one memory round trip (no
+// wait for q to be staged first). Lanes sharing a piece add up in registers (DPP), the waves
+// through LDS (red_s [kMaxWaves][RK]); the barrier before that also publishes what the caller
+// wrote to LDS before the call.
 template <class S, int RK>
 __device__ __forceinline__ void absorb_query(const DecodeParams& p, int h, int nw, int wave, int lane,
-                                             const float* q_s, float* red_s, float* qt_s) {
+                                             size_t qoff, float* red_s, float* qt_s) {
   constexpr int VE = 16 / S::kBytes;
   constexpr int NRB = RK / VE;  // 16-byte pieces per W^K row
   static_assert(RK % VE == 0 && NRB <= 64, "W^K rows of whole 16-byte pieces");
@@ -166,7 +168,7 @@ __device__ __forceinline__ void absorb_query(const DecodeParams& p, int h, int n
                                                      w_offset(p, h, RK) * S::kBytes) + rb;
     for (int j = wave * GL + jg; j < p.d; j += GL * nw) {
       const uint4 w = wk[static_cast<size_t>(j) * NRB];
-      const float qj = q_s[j];
+      const float qj = ld<S>(p.q, qoff + j);
 #pragma unroll
       for (int e = 0; e < VE; ++e) acc[e] += frag_elem<S>(&w, e) * qj;
     }
@@ -339,9 +341,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   float beta = 0.f;
   auto prologue = [&]() {
     const size_t qoff = static_cast<size_t>(bh) * p.d;
+    // q in LDS for the mu^K and self-key scores (read after the absorption's barrier)
     for (int j = pw * 64 + lane; j < p.d; j += 64 * pn) q_s[j] = ld<S>(p.q, qoff + j);
-    __syncthreads();
-    absorb_query<S, RK>(p, h, pn, pw, lane, q_s, xs_s + (kHG ? wave * RK : 0), qt_s);
+    absorb_query<S, RK>(p, h, pn, pw, lane, qoff, xs_s + (kHG ? wave * RK : 0), qt_s);
     if (p.mu_k != nullptr) {
       const size_t moff = mu_offset(p, h);
       float part = 0.f;
@@ -750,7 +752,7 @@ const Entry kTable[] = {
      rope_fns<BF16, 16, 16, 4, 4>()},
     {LLA_BF16, 24, 24, partial_fn<BF16, 24, 24, 4, 8>(), gather_fn<BF16, 24, 24, 4, 8>(),
      rope_fns<BF16, 24, 24, 4, 4>()},
-    {LLA_BF16, 32, 32, partial_fn<BF16, 32, 32, 4, 8>(), gather_fn<BF16, 32, 32, 4, 8>(),
+    {LLA_BF16, 32, 32, partial_fn<BF16, 32, 32, 4, 4>(), gather_fn<BF16, 32, 32, 4, 8>(),
      rope_fns<BF16, 32, 32, 4, 4>()},
     {LLA_BF16, 64, 64, partial_fn<BF16, 64, 64, 8, 8>(), gather_fn<BF16, 64, 64, 8, 8>(),
      rope_fns<BF16, 64, 64, 8, 4>()},
