@@ -45,6 +45,15 @@ __device__ __forceinline__ int row_keys(const DecodeParams& p, int row) {
   return min(max(n, 0), p.n_max);
 }
 
+// Position of query row `row` for the rotary branch: a decode row sits at its key count nb (after
+// the cached keys); a causal (prefill) row j of a chunk at ctx + j, the slot of its own key.
+__device__ __forceinline__ double row_position(const DecodeParams& p, int row, int nb) {
+  if (!p.causal) return nb;
+  const int seq = row / p.rows_per_seq;
+  const int ctx = p.seq_lens != nullptr ? uniform(p.seq_lens[seq]) : p.n_max;
+  return static_cast<double>(ctx) + (row - seq * p.rows_per_seq);
+}
+
 // Offset of mu_t restricted to head h: per-head [H][T*d] at (h, t*d); 2D [T*H*d] at t*H*d + h*d.
 __device__ __forceinline__ size_t mu_offset(const DecodeParams& p, int h) {
   return p.variant == LLA_2D ? (static_cast<size_t>(p.t) * p.H + h) * p.d
@@ -355,11 +364,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
       for (int k = 0; k < kSlotCap / 256; ++k)
         if (k < nsl) *reinterpret_cast<uint4*>(&slot_s[(k * 64 + lane) * 4]) = sl[k];
     }
-    if constexpr (R) {  // rotary query of this head rotated at the decoding position N_b
+    if constexpr (R) {  // rotary query of this head rotated at the row's position
       const size_t qro = static_cast<size_t>(bh) * DR;
+      const double rpos = row_position(p, b, nb);
       for (int i = pw * 64 + lane; i < DR / 2; i += 64 * pn) {
         float y0, y1;
-        rotate_pair(ld<BF16>(p.q_rope, qro + 2 * i), ld<BF16>(p.q_rope, qro + 2 * i + 1), i, DR, nb,
+        rotate_pair(ld<BF16>(p.q_rope, qro + 2 * i), ld<BF16>(p.q_rope, qro + 2 * i + 1), i, DR, rpos,
                     p.rope_base, &y0, &y1);
         qr_s[2 * i] = y0 * p.scale_log2;
         qr_s[2 * i + 1] = y1 * p.scale_log2;
@@ -910,6 +920,12 @@ size_t gather_workspace_bytes(const lla_desc& desc, int B, int budget) {
   return valu_workspace_bytes(desc, B, s);
 }
 
+bool rope_valu_supported(int dtype, int r_k, int r_v, int d_rope) {
+  if (dtype != LLA_BF16 || !(d_rope == 32 || d_rope == 64 || d_rope == 128)) return false;
+  const Entry* e = find(dtype, r_k, r_v);
+  return e != nullptr && e->rfn.w64 != nullptr;
+}
+
 bool rope_supported(const lla_desc& desc, int d_rope) {
   if (desc.dtype != LLA_BF16 || !(d_rope == 32 || d_rope == 64 || d_rope == 128)) return false;
   // the LLA-2D MFMA read takes the branch as extra k-steps of its own contraction
@@ -942,7 +958,8 @@ size_t rope_workspace_bytes(const lla_desc& desc, int B) {
 }
 
 hipError_t launch_decode_rope(const DecodeParams& p, int dtype, hipStream_t stream) {
-  if (p.variant == LLA_2D && decode2d_mfma_supported(dtype, p.r_k, p.r_v, p.d))
+  if (p.variant == LLA_2D && p.rows_per_seq == 1 && !p.causal &&
+      decode2d_mfma_supported(dtype, p.r_k, p.r_v, p.d))
     return launch_decode2d(p, stream);  // rotary keys as extra MFMA k-steps of the read
   const Entry* e = find(dtype, p.r_k, p.r_v);
   if (e == nullptr) return hipErrorNotSupported;

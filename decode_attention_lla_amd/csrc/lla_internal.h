@@ -148,6 +148,8 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 // Decoupled rotary branch (rope.hip, decode.hip).
 hipError_t launch_rope_write(const RopeWriteParams& p, hipStream_t s);
 bool rope_supported(const lla_desc& desc, int d_rope);
+// The streaming read has instances with the rotary branch for (dtype, r_k, r_v) and d_rope.
+bool rope_valu_supported(int dtype, int r_k, int r_v, int d_rope);
 // Plan of one lla_attend_decode_rope call (decode_plan, or head groups for the streaming read).
 void rope_plan(const lla_desc& desc, int B, int* splits, int* chunk, int* wg_waves, int* wg_heads);
 size_t rope_workspace_bytes(const lla_desc& desc, int B);

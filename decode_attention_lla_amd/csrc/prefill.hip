@@ -583,10 +583,13 @@ bool mfma_prefill(int dtype, int r_k, int r_v, int d_head, int n_max) {
 
 }  // namespace
 
+// MFMA path: d_rope 64 or 128; streaming path (pairs without the MFMA prefill): the streaming
+// read's rotary instances, each causal row a query with its own key count and position
 bool prefill_rope_supported(const lla_desc& desc, int d_rope) {
-  return (d_rope == 64 || d_rope == 128) &&
-         mfma_prefill(desc.dtype, desc.r_k, desc.r_v, desc.d_head, desc.n_max) &&
-         static_cast<long>(desc.n_max) * d_rope * 2 < 0x7fffffffL;
+  if (static_cast<long>(desc.n_max) * d_rope * 2 >= 0x7fffffffL) return false;
+  if (mfma_prefill(desc.dtype, desc.r_k, desc.r_v, desc.d_head, desc.n_max))
+    return d_rope == 64 || d_rope == 128;
+  return rope_valu_supported(desc.dtype, desc.r_k, desc.r_v, d_rope);
 }
 
 bool prefill_supported(int variant, int dtype, int r_k, int r_v) {
@@ -652,6 +655,13 @@ hipError_t launch_prefill(const PrefillParams& pp, int dtype, hipStream_t stream
   p.chunk = pp.chunk;
   p.wg_waves = pp.wg_waves;
   p.ws_bytes = pp.ws_bytes;
+  if (pp.d_rope > 0) {  // rotary branch: one wave per head (no head groups), the same plan
+    p.q_rope = pp.q_rope;
+    p.k_rope = pp.k_rope;
+    p.d_rope = pp.d_rope;
+    p.rope_base = pp.rope_base;
+    return launch_decode_rope(p, dtype, stream);
+  }
   return launch_decode(p, dtype, stream);
 }
 

@@ -244,8 +244,10 @@ lla_status lla_attend_decode_rope(const lla_desc* desc, int32_t B, int32_t t, co
  * lla_attend_decode_rope (default 1/sqrt(d_head + d_rope)).
  *   q_rope [device] bf16 [B][C][H][d_rope], unrotated; k_rope as above; ws at least
  *   lla_workspace_bytes(desc, B, C).
- * MFMA path only: LLA_BF16, the chunked-prefill MFMA (r_k, r_v) pairs, d_head a multiple of 32,
- * d_rope 64 or 128; otherwise LLA_ERR_UNSUPPORTED. */
+ * LLA_BF16 only. The chunked-prefill MFMA (r_k, r_v) pairs (d_head a multiple of 32) take d_rope 64
+ * or 128 on the MFMA path; the other streaming bf16 pairs (both variants) take d_rope 32, 64 or 128
+ * on the streaming path (each chunk row a query with its own key count and position, the rotary
+ * scores formed in the read); otherwise LLA_ERR_UNSUPPORTED. */
 lla_status lla_attend_prefill_rope(const lla_desc* desc, int32_t B, int32_t C, int32_t t,
                                    const void* q, const void* q_rope, const void* zk,
                                    const void* zv, const void* k_rope, int32_t d_rope, float base,

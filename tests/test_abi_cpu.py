@@ -362,9 +362,16 @@ def test_prefill_rope_arguments_and_support():
     d = desc(variant=lla.LLA_2D, r_k=256, r_v=256, n_max=100)
     for kw in (dict(qr=N), dict(kr=M), dict(ctx=N), dict(base=-2.0), dict(C=101), dict(t=4)):
         assert call(d, **kw) == lla.LLA_ERR_INVALID_ARG, kw
-    assert call(d, d_rope=32) == lla.LLA_ERR_UNSUPPORTED
-    assert call(desc(r_k=24, r_v=24, n_max=100)) == lla.LLA_ERR_UNSUPPORTED  # no MFMA prefill
+    assert call(d, d_rope=32) == lla.LLA_ERR_UNSUPPORTED  # MFMA path: 64 or 128
     assert call(d) == lla.LLA_ERR_WORKSPACE
+    # pairs without the MFMA prefill take the streaming path: d_rope 32, 64 or 128, bf16 only
+    dl = desc(r_k=24, r_v=24, n_max=70000)
+    for dr in (32, 64, 128):
+        assert call(dl, B=1, C=2, d_rope=dr) == lla.LLA_ERR_WORKSPACE  # supported; needs split partials
+    assert call(dl, B=1, C=2, d_rope=48) == lla.LLA_ERR_UNSUPPORTED
+    assert call(desc(r_k=24, r_v=24, n_max=70000, dtype=lla.LLA_F32), B=1, C=2) == lla.LLA_ERR_UNSUPPORTED
+    assert call(desc(variant=lla.LLA_2D, r_k=32, r_v=32, n_max=70000), B=1, C=2, d_rope=32) == \
+        lla.LLA_ERR_WORKSPACE
 
 
 def test_noalloc_decode_refusals_on_the_host():

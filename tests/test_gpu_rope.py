@@ -317,6 +317,39 @@ def test_prefill_rope(variant, rk, rv, d_rope):
         assert_close(host(out), ref, "bf16", f"prefill rope {variant} ({rk},{rv}) d_rope={d_rope} t={t}")
 
 
+@pytest.mark.parametrize("variant,rk,rv,d_rope,d", [("per_head", 24, 24, 64, 64), ("per_head", 96, 160, 32, 64),
+                                                    ("2d", 32, 32, 128, 64), ("per_head", 8, 8, 32, 64),
+                                                    ("per_head", 64, 64, 64, 48), ("2d", 256, 256, 32, 48)])
+def test_prefill_rope_streaming(variant, rk, rv, d_rope, d):
+    """Chunked prefill with the rotary branch on the streaming path (pairs and head widths without
+    the MFMA prefill): each chunk row is a query at position ctx + j over latents 0 .. ctx + j,
+    70 rows, three contexts (one empty), mu on, sharpened queries, against the oracle."""
+    B, C, H, T, n_max = 3, 70, 2, 2, 1200
+    desc = mk_desc(variant, "bf16", H, d, T, rk, rv, n_max)
+    rng = np.random.default_rng(9890 + rk + d_rope + d)
+    c = upload(synth.random_case(variant, "bf16", B, H, d, T, rk, rv, n_max, 9891 + rk + d), "bf16")
+    q = synth.to_storage(4.0 * rng.standard_normal((B, C, H, d)).astype(np.float32), "bf16")
+    q_rope = synth.to_storage(2.0 * rng.standard_normal((B, C, H, d_rope)).astype(np.float32), "bf16")
+    k_rope = synth.to_storage(rng.standard_normal((B, n_max, d_rope)).astype(np.float32), "bf16")
+    ctx = np.array([300, 0, 1000], np.int32)
+    out = torch.full((B, C, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    print(f"streaming prefill rope {variant} ({rk},{rv}) d_rope={d_rope} d={d}", flush=True)
+    for t in range(T):
+        lla.lla_attend_prefill_rope(desc, B, C, t, dev(q, "bf16"), dev(q_rope, "bf16"), c["_zk"],
+                                    c["_zv"], dev(k_rope, "bf16"), d_rope, 0.0, dev(ctx), c["_Wk"],
+                                    c["_Wv"], c["_muk"], c["_muv"], out, lla.workspace(desc, B, C))
+        torch.cuda.synchronize()
+        ref = O.attend_prefill_rope(q, q_rope, c["zk"], c["zv"], k_rope, c["Wk"], c["Wv"], t, ctx,
+                                    c["mu_k"], c["mu_v"], variant=variant)
+        what = f"streaming prefill rope {variant} ({rk},{rv}) d_rope={d_rope} d={d} t={t}"
+        assert_close(host(out), ref, "bf16", what)
+        # row by row as well: a position or mask slip on one row must not hide under the global max
+        o = host(out).astype(np.float64)
+        for b in range(B):
+            for j in range(C):
+                assert_close(o[b, j], ref[b, j], "bf16", f"{what} row ({b}, {j})")
+
+
 def test_lla2d_decode_rope_full_size_sampled():
     """The LLA-2D decode benchmark shape (B=128, H=16, d=128, T=4, r=256, N=8192) on the MFMA
     path with a 64-wide rotary branch and the self token; sequences {0, 77, 127}, all heads, all
