@@ -217,8 +217,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   // for the rest): the LPT lanes of a token then read its row as one run, and each load
   // instruction covers 64 / LPT consecutive rows without gaps (one load per slice) or leaves only
   // the second load's bytes for the next instruction; the contiguous read streams past the caches
-  // (non-temporal). Low-bit slices stay within one load.
-  constexpr bool kOne = SK % 4 == 0 && SV % 4 == 0 && SK <= 32 && SV <= 32 && (!kQ8 || (SK <= 16 && SV <= 16));
+  // (non-temporal). Low-bit slices follow the same map (a 112-byte r = 96 row: 4 lanes x 28 bytes).
+  constexpr bool kOne = SK % 4 == 0 && SV % 4 == 0 && SK <= 32 && SV <= 32;
   constexpr int VK = kOne ? (SK + 15) / 16 : SK / 16;
   constexpr int VV = kOne ? (SV + 15) / 16 : SV / 16;
   static_assert(kQ8 ? (EK * LPT == RKB && EV * LPT == RVB) : (EK * LPT == RK && EV * LPT == RV),
@@ -228,7 +228,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   constexpr int E16 = 16 / LS::kBytes;                // elements in a slice's first 16 bytes
   constexpr bool kSplitK = kOne && SK > 16;          // slices read by two loads (load_slice)
   constexpr bool kSplitV = kOne && SV > 16;
-  static_assert(!kQ8 || !(kSplitK || kSplitV), "low-bit slices are one load");
 
   // per (row, head): one copy, or one per wave of a head group
   __shared__ float q_a[HG][256];
@@ -297,16 +296,24 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
 
   const int sub = lane % LPT;
   const int grp = lane / LPT;
-  // low-bit slices: the bytes of each of this lane's words that hold codes (padding and the scale
-  // must never be converted as codes: a scale byte can be an E4M3 NaN pattern)
-  uint32_t kmask[4], vmask[4];
+  // low-bit slices: the bytes of each of this lane's words (load f, word k) that hold codes
+  // (padding and the scale must never be converted as codes: a scale byte can be an E4M3 NaN
+  // pattern); byte e of the slice holds row entry slice_entry(sub, e)
+  uint32_t kmask[2][4], vmask[2][4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int nk = min(max(RK - (sub * EK + 4 * k), 0), 4);
-    const int nv = min(max(RV - (sub * EV + 4 * k), 0), 4);
-    kmask[k] = nk == 4 ? 0xffffffffu : (1u << (8 * nk)) - 1u;
-    vmask[k] = nv == 4 ? 0xffffffffu : (1u << (8 * nv)) - 1u;
-  }
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t mk = 0, mv = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 16 * f + 4 * k + i;
+        if (e < EK && slice_entry<kSplitK, EK, E16, LPT>(sub, e) < RK) mk |= 0xffu << (8 * i);
+        if (e < EV && slice_entry<kSplitV, EV, E16, LPT>(sub, e) < RV) mv |= 0xffu << (8 * i);
+      }
+      kmask[f][k] = mk;
+      vmask[f][k] = mv;
+    }
 
   // --- 2-3. latent stream with online softmax -------------------------------------------------
   const size_t lrow = latent_row(p, b / p.rows_per_seq, h);
@@ -418,15 +425,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
       if constexpr (kQ8 && kOne) {
         // the scale is the last word of the group's last lane; a zero-padded group sum gives it
         // to every lane of the group exactly. Then the non-code bytes are cleared.
-        constexpr int WK = SK / 4 - 1, WV = SV / 4 - 1;
-        const uint32_t kw = WK == 0 ? kr[u][0].x : WK == 1 ? kr[u][0].y : WK == 2 ? kr[u][0].z : kr[u][0].w;
-        const uint32_t vw = WV == 0 ? vr[u][0].x : WV == 1 ? vr[u][0].y : WV == 2 ? vr[u][0].z : vr[u][0].w;
+        // (a split slice ends in its second load)
+        constexpr int FK = kSplitK ? 1 : 0, FV = kSplitV ? 1 : 0;
+        constexpr int WK = (kSplitK ? SK - 16 : SK) / 4 - 1, WV = (kSplitV ? SV - 16 : SV) / 4 - 1;
+        const uint4 kl = kr[u][FK], vl = vr[u][FV];
+        const uint32_t kw = WK == 0 ? kl.x : WK == 1 ? kl.y : WK == 2 ? kl.z : kl.w;
+        const uint32_t vw = WV == 0 ? vl.x : WV == 1 ? vl.y : WV == 2 ? vl.z : vl.w;
         sk = group_sum<LPT>(sub == LPT - 1 ? __uint_as_float(kw) : 0.f);
         sv = group_sum<LPT>(sub == LPT - 1 ? __uint_as_float(vw) : 0.f);
-        kr[u][0] = make_uint4(kr[u][0].x & kmask[0], kr[u][0].y & kmask[1], kr[u][0].z & kmask[2],
-                              kr[u][0].w & kmask[3]);
-        vr[u][0] = make_uint4(vr[u][0].x & vmask[0], vr[u][0].y & vmask[1], vr[u][0].z & vmask[2],
-                              vr[u][0].w & vmask[3]);
+#pragma unroll
+        for (int f = 0; f < VK; ++f)
+          kr[u][f] = make_uint4(kr[u][f].x & kmask[f][0], kr[u][f].y & kmask[f][1], kr[u][f].z & kmask[f][2],
+                                kr[u][f].w & kmask[f][3]);
+#pragma unroll
+        for (int f = 0; f < VV; ++f)
+          vr[u][f] = make_uint4(vr[u][f].x & vmask[f][0], vr[u][f].y & vmask[f][1], vr[u][f].z & vmask[f][2],
+                                vr[u][f].w & vmask[f][3]);
       } else if constexpr (kQ8) {
         // the last 16 bytes of a low-bit row hold padding the arithmetic never reads; without
         // this the compiler narrows their load and a row takes three partial loads, not two
@@ -610,7 +624,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
       if (lane < LPT) {
 #pragma unroll
         for (int e = 0; e < EV; ++e)
-          if (!kQ8 || lane * EV + e < RV) xw[2 + slice_entry<kSplitV, EV, E16, LPT>(lane, e)] = acc[e];
+          if (!kQ8 || slice_entry<kSplitV, EV, E16, LPT>(lane, e) < RV) xw[2 + slice_entry<kSplitV, EV, E16, LPT>(lane, e)] = acc[e];
       }
     }
     __syncthreads();
@@ -626,7 +640,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
         l += fw * xv[1];
 #pragma unroll
         for (int e = 0; e < EV; ++e)
-          if (!kQ8 || sub * EV + e < RV) acc[e] += fw * xv[2 + slice_entry<kSplitV, EV, E16, LPT>(sub, e)];
+          if (!kQ8 || slice_entry<kSplitV, EV, E16, LPT>(sub, e) < RV) acc[e] += fw * xv[2 + slice_entry<kSplitV, EV, E16, LPT>(sub, e)];
       }
     }
   }
@@ -641,14 +655,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
     if (out_wave && lane < LPT) {
 #pragma unroll
       for (int e = 0; e < EV; ++e)
-        if (!kQ8 || lane * EV + e < RV) w[2 + slice_entry<kSplitV, EV, E16, LPT>(lane, e)] = acc[e];
+        if (!kQ8 || slice_entry<kSplitV, EV, E16, LPT>(lane, e) < RV) w[2 + slice_entry<kSplitV, EV, E16, LPT>(lane, e)] = acc[e];
     }
     return;
   }
   if (out_wave && lane < LPT) {
 #pragma unroll
     for (int e = 0; e < EV; ++e)
-      if (!kQ8 || lane * EV + e < RV) a_s[slice_entry<kSplitV, EV, E16, LPT>(lane, e)] = acc[e];
+      if (!kQ8 || slice_entry<kSplitV, EV, E16, LPT>(lane, e) < RV) a_s[slice_entry<kSplitV, EV, E16, LPT>(lane, e)] = acc[e];
   }
   __syncthreads();
   if (out_wave) finish_unit<S>(p, b, h, Mt, l, a_s, q_s, lane);
@@ -787,10 +801,12 @@ const Entry kTable[] = {
     {LLA_BF16_Q8, 16, 16, q8_fn<Q8, 16, 16, 2, 4>(), q8_gather_fn<Q8, 16, 16, 2, 4>(), RopeFns{}},
     {LLA_BF16_Q8, 24, 24, q8_fn<Q8, 24, 24, 2, 4>(), q8_gather_fn<Q8, 24, 24, 2, 4>(), RopeFns{}},
     {LLA_BF16_Q8, 32, 32, q8_fn<Q8, 32, 32, 4, 8>(), q8_gather_fn<Q8, 32, 32, 4, 8>(), RopeFns{}},
+    {LLA_BF16_Q8, 96, 96, q8_fn<Q8, 96, 96, 4, 2>(), q8_gather_fn<Q8, 96, 96, 4, 2>(), RopeFns{}},
     {LLA_BF16_I8, 8, 8, q8_fn<I8, 8, 8, 1, 4>(), q8_gather_fn<I8, 8, 8, 1, 4>(), RopeFns{}},
     {LLA_BF16_I8, 16, 16, q8_fn<I8, 16, 16, 2, 4>(), q8_gather_fn<I8, 16, 16, 2, 4>(), RopeFns{}},
     {LLA_BF16_I8, 24, 24, q8_fn<I8, 24, 24, 2, 4>(), q8_gather_fn<I8, 24, 24, 2, 4>(), RopeFns{}},
     {LLA_BF16_I8, 32, 32, q8_fn<I8, 32, 32, 4, 8>(), q8_gather_fn<I8, 32, 32, 4, 8>(), RopeFns{}},
+    {LLA_BF16_I8, 96, 96, q8_fn<I8, 96, 96, 4, 2>(), q8_gather_fn<I8, 96, 96, 4, 2>(), RopeFns{}},
 };
 
 const Entry* find(int dtype, int r_k, int r_v) {

@@ -123,6 +123,7 @@ lla_status lla_quantize_latents(const lla_desc* desc, int32_t B, int32_t C, cons
  *   Encode: any r <= 512 (bf16 on MFMA, fp32 on the VALU).
  *   Low-bit latents (LLA_BF16_Q8, LLA_BF16_I8), decode, gather decode and prefill, both
  *   variants on the streaming kernels:                        (8,8) (16,16) (24,24) (32,32)
+ *                                                              (96,96)
  * A decode or prefill call with a pair that none of these covers returns LLA_ERR_UNSUPPORTED. */
 
 /* Bytes of device workspace that lla_attend_prefill with a chunk of C rows needs for this

@@ -276,6 +276,8 @@ def test_low_bit_support_matrix(low):
     assert lla.lla_workspace_bytes(desc(r_k=32, r_v=32, dtype=q8["dtype"]), 32, 1) == \
         lla.lla_workspace_bytes(desc(r_k=32, r_v=32), 32, 1)
     assert lla.lla_workspace_bytes(desc(r_k=24, r_v=24, dtype=q8["dtype"]), 2, 1) > 0  # compiled
+    assert lla.lla_workspace_bytes(desc(r_k=96, r_v=96, dtype=q8["dtype"]), 2, 1) > 0  # 112-byte rows
+    assert decode(desc(r_k=96, r_v=96, dtype=q8["dtype"], n_max=70000)) == lla.LLA_ERR_WORKSPACE  # supported
     # an unknown dtype is an invalid descriptor
     assert decode(desc(r_k=24, r_v=24, dtype=4, n_max=100)) == lla.LLA_ERR_INVALID_ARG
 

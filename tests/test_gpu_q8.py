@@ -121,7 +121,8 @@ def _q8_case(variant, B, H, d, T, r, n_max, sd, gain=1.0, fmt="e4m3"):
 
 @pytest.mark.parametrize("fmt", sorted(FORMATS))
 @pytest.mark.parametrize("variant,r", [("per_head", 8), ("per_head", 16), ("per_head", 24),
-                                       ("per_head", 32), ("2d", 24), ("2d", 32)])
+                                       ("per_head", 32), ("2d", 24), ("2d", 32), ("per_head", 96),
+                                       ("2d", 96)])
 def test_decode_q8(variant, r, fmt):
     B, H, d, T, n_max = 3, 2, 64, 2, 3001
     lens = np.array([3001, 517, 0], np.int32)
@@ -148,9 +149,10 @@ def test_decode_q8(variant, r, fmt):
 
 
 @pytest.mark.parametrize("fmt", sorted(FORMATS))
-def test_gather_and_prefill_q8(fmt):
-    B, H, d, T, n_max, r = 2, 2, 64, 2, 700, 24
-    c, desc = _q8_case("per_head", B, H, d, T, r, n_max, 9600, fmt=fmt)
+@pytest.mark.parametrize("r", [24, 96])
+def test_gather_and_prefill_q8(fmt, r):
+    B, H, d, T, n_max = 2, 2, 64, 2, 700
+    c, desc = _q8_case("per_head", B, H, d, T, r, n_max, 9600 + r, fmt=fmt)
     slots = synth.random_slots(B, 400, n_max, 9601, p_skip=0.05, p_repeat=0.05)
     counts = np.array([400, 211], np.int32)
     q = dev(c["q"][1], "bf16")
@@ -162,8 +164,8 @@ def test_gather_and_prefill_q8(fmt):
     torch.cuda.synchronize()
     ro, rl = O.attend_decode_gather(c["q"][1], c["zk_dq"], c["zv_dq"], c["Wk"], c["Wv"], 1, slots,
                                     counts, c["mu_k"], c["mu_v"])
-    assert_close(host(out), ro, "bf16", "q8 gather")
-    assert_lse(host(lse), rl, "q8 gather")
+    assert_close(host(out), ro, "bf16", f"{fmt} r={r} gather")
+    assert_lse(host(lse), rl, f"{fmt} r={r} gather")
     # chunked prefill on the streaming path: 37 rows per sequence after contexts 600 and 0
     C = 37
     ctx = np.array([600, 0], np.int32)
@@ -174,7 +176,7 @@ def test_gather_and_prefill_q8(fmt):
                            c["_Wv"], c["_mu_k"], c["_mu_v"], outp, lla.workspace(desc, B, C))
     torch.cuda.synchronize()
     rp = O.attend_prefill(qp, c["zk_dq"], c["zv_dq"], c["Wk"], c["Wv"], 0, ctx, c["mu_k"], c["mu_v"])
-    assert_close(host(outp), rp, "bf16", "q8 prefill")
+    assert_close(host(outp), rp, "bf16", f"{fmt} r={r} prefill")
 
 
 @pytest.mark.parametrize("fmt", sorted(FORMATS))
@@ -209,3 +211,40 @@ def test_capacity_q8_full_size_sampled(fmt):
                                           g["v_self"][t][rows])
         assert_close(host(out)[rows], ro, "bf16", f"capacity {fmt} t={t}")
         assert_lse(host(lse)[rows], rl, f"capacity {fmt} t={t}")
+
+
+@pytest.mark.parametrize("fmt", sorted(FORMATS))
+def test_deep_loop_q8_full_size_sampled(fmt):
+    """Deep-recurrence shape (B=64, H=40, d=96, T=32, r=96, N=4096) with 112-byte low-bit rows
+    (4 lanes x 28 bytes per row, two loads per lane) quantised on the device, at the benchmark's
+    launch shape; sampled rows (all heads), loops 0, 17 and 31, against the explicit oracle on the
+    dequantised rows."""
+    s = synth.CASES["deep_loop"]
+    g = _fill_device_case(s)
+    desc = q8_desc("per_head", s.H, s.d, s.T, s.r_k, s.r_v, s.n_max, fmt)
+    rb = lla.lla_latent_row_bytes(lla.LLA_BF16_Q8, s.r_k)
+    assert rb == 112
+    ck = torch.empty(s.B, s.H, s.n_max, rb, dtype=torch.uint8, device="cuda")
+    cv = torch.empty_like(ck)
+    lla.lla_quantize_latents(desc, s.B, s.n_max, g["zk"], g["zv"],
+                             torch.zeros(s.B, dtype=torch.int32, device="cuda"), ck, cv)
+    rows = sorted({0, 63, *np.random.default_rng(synth.seed(s.case, synth.SEED_SAMPLE)).choice(64, 2, replace=False).tolist()})
+    zk_dq = O.dequantize_latent_rows(*FORMATS[fmt][1](host(g["zk"][rows]).astype(np.float32)))
+    zv_dq = O.dequantize_latent_rows(*FORMATS[fmt][1](host(g["zv"][rows]).astype(np.float32)))
+    del g["zk"], g["zv"]
+    torch.cuda.empty_cache()
+    lens = np.full(s.B, s.N, np.int32)
+    Wk, Wv = dev(g["Wk"], "bf16"), dev(g["Wv"], "bf16")
+    ws = lla.workspace(desc, s.B, 1)
+    for t in (0, 17, 31):
+        q = dev(g["q"][t], "bf16")
+        out = torch.empty_like(q)
+        lse = torch.empty(s.B, s.H, device="cuda")
+        print(f"deep loop {fmt} t={t}", flush=True)
+        lla.lla_attend_decode(desc, s.B, t, q, ck, cv, dev(lens), Wk, Wv, None, None,
+                              dev(g["k_self"][t], "bf16"), dev(g["v_self"][t], "bf16"), out, lse, ws)
+        torch.cuda.synchronize()
+        ro, rl = O.attend_decode(g["q"][t][rows], zk_dq, zv_dq, g["Wk"], g["Wv"], t, lens[rows],
+                                 None, None, g["k_self"][t][rows], g["v_self"][t][rows])
+        assert_close(host(out)[rows], ro, "bf16", f"deep loop {fmt} t={t}")
+        assert_lse(host(lse)[rows], rl, f"deep loop {fmt} t={t}")
