@@ -64,6 +64,8 @@ def parse():
                     help="measure only the decode read with the decoupled rotary branch")
     ap.add_argument("--only-long-context", action="store_true",
                     help="measure only the 262k-token absorbed read against reconstruct-then-attend")
+    ap.add_argument("--only-lla2d", action="store_true",
+                    help="measure only the LLA-2D decode step (the MFMA read and its encode)")
     ap.add_argument("--only-small", action="store_true",
                     help="measure only the one-layer Ouro-shaped and deep-recurrence decode steps")
     return ap.parse_args()
@@ -120,6 +122,9 @@ def main():
         return
     if args.only_rope:
         print(json.dumps({"rope_decode": rope_decode(args)}), flush=True)
+        return
+    if args.only_lla2d:
+        print(json.dumps({"lla2d_decode": lla2d_decode(args)}), flush=True)
         return
     if args.only_long_context:
         print(json.dumps({"long_context_262k": long_context(args)}), flush=True)

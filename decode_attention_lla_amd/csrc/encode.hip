@@ -363,11 +363,20 @@ __global__ __launch_bounds__(512) void encode_gemm_kernel(EncodeParams p) {
     for (int grp = wave; grp < TN / 16; grp += 8) {
       const int er = min(r0 + 16 * grp + col, p.r - 1);
       const uint16_t* erow = E + static_cast<size_t>(er) * K;
+      // the loads of 8 steps are issued before their products (K is a multiple of 128 here), so
+      // the walk over E's rows is not one memory round trip per step
       floatx4_t am = {0.f, 0.f, 0.f, 0.f};
-      for (int k = 0; k < K; k += 32) {
-        const uint4 a = col == 0 ? *reinterpret_cast<const uint4*>(mu + k + 8 * g) : make_uint4(0, 0, 0, 0);
-        const uint4 bb = *reinterpret_cast<const uint4*>(erow + k + 8 * g);
-        am = mfma(a, bb, am);
+      for (int k = 0; k < K; k += 32 * 8) {
+        uint4 a[8], bb[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int kk = min(k + 32 * u, K - 32);
+          a[u] = col == 0 ? *reinterpret_cast<const uint4*>(mu + kk + 8 * g) : make_uint4(0, 0, 0, 0);
+          bb[u] = *reinterpret_cast<const uint4*>(erow + kk + 8 * g);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (k + 32 * u < K) am = mfma(a[u], bb[u], am);
       }
       if (g == 0) emu_s[16 * grp + col] = am[0];  // row 0 of C: lane j, element 0
     }
