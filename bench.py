@@ -118,7 +118,8 @@ def main():
         return
     if args.only_low_bit:
         print(json.dumps({"low_bit_capacity": low_bit_capacity(args, None),
-                          "low_bit_deep_loop": low_bit_deep_loop(args)}), flush=True)
+                          "low_bit_deep_loop": low_bit_deep_loop(args),
+                          "low_bit_lla2d": low_bit_lla2d(args)}), flush=True)
         return
     if args.only_rope:
         print(json.dumps({"rope_decode": rope_decode(args)}), flush=True)
@@ -251,6 +252,7 @@ def main():
                   "eviction_decode": eviction_decode(args),
                   "low_bit_capacity": low_bit_capacity(args, tokens_per_s),
                   "low_bit_deep_loop": low_bit_deep_loop(args),
+                  "low_bit_lla2d": low_bit_lla2d(args),
                   "long_context_262k": long_context(args),
                   "rope_decode": rope_decode(args)}
 
@@ -601,6 +603,58 @@ def low_bit_deep_loop(args):
         lla.lla_quantize_latents(desc, B, n_max, zk, zv, zero, ck, cv)
         ms = timed_read(desc, ck, cv)
         row_bytes = B * H * N * 2 * rb
+        sub = {"read_us": round(ms * 1e3, 2),
+               "row_GBps": round(row_bytes / (ms / 1e3) / 1e9, 1),
+               "row_frac_of_peak": round(row_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+               "speedup_vs_bf16_read": round(ms_bf16 / ms, 3)}
+        if key == "e4m3":
+            res.update(sub)
+        else:
+            res["int8"] = sub
+    del zk, zv, ck, cv
+    torch.cuda.empty_cache()
+    return res
+
+
+def low_bit_lla2d(args):
+    """One LLA-2D decode read (H=16, d=128, r=256/256, B=128, 8192 cached tokens) on the MFMA path
+    with low-bit rows (256 codes + a float32 scale in 272 bytes; codes converted to bf16 on the way
+    to the MFMA) beside the same read on bf16 latents (512-byte rows). E4M3 codes at the top level,
+    int8 codes under "int8"."""
+    import torch
+    from decode_attention_lla_amd import lla, synth
+    s = synth.CASES["lla2d"]
+    B, H, d, T, r, N = s.B, s.H, s.d, s.T, s.r_k, s.N
+    n_max = N + 1
+    bf = torch.bfloat16
+    zk = synth.device_normal_(torch.empty(B, n_max, r, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZK))
+    zv = synth.device_normal_(torch.empty(B, n_max, r, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_ZV))
+    Wk = torch.from_numpy(synth.orthonormal_W_2d(T, H, d, r, synth.seed(s.case, synth.SEED_WK), "bf16")).to(bf).cuda()
+    Wv = torch.from_numpy(synth.orthonormal_W_2d(T, H, d, r, synth.seed(s.case, synth.SEED_WV), "bf16")).to(bf).cuda()
+    q = synth.device_normal_(torch.empty(B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_Q))
+    ks = synth.device_normal_(torch.empty(B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF))
+    vs = synth.device_normal_(torch.empty(B, H, d, dtype=bf, device="cuda"), synth.seed(s.case, synth.SEED_SELF) + 1)
+    out = torch.empty(B, H, d, dtype=bf, device="cuda")
+    lens = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+
+    def timed_read(desc, ck, cv):
+        ws = lla.workspace(desc, B, 1)
+        return _timed(lambda: lla.lla_attend_decode(desc, B, 0, q, ck, cv, lens, Wk, Wv, None, None,
+                                                    ks, vs, out, None, ws), 20, 3)
+
+    ms_bf16 = timed_read(lla.make_desc(lla.LLA_2D, lla.LLA_BF16, H, d, T, r, r, n_max), zk, zv)
+    rb = lla.lla_latent_row_bytes(lla.LLA_BF16_Q8, r)
+    ck = torch.empty(B, n_max, rb, dtype=torch.uint8, device="cuda")
+    cv = torch.empty_like(ck)
+    res = {"workload": f"LLA-2D read with low-bit latents on MFMA: H={H}, d_head={d}, r_k=r_v={r}, B={B}, "
+                       f"N={N}; {rb}-byte rows (codes + float32 scale) vs {2 * r}-byte bf16 rows",
+           "bf16_read_us": round(ms_bf16 * 1e3, 2)}
+    for key, dtype in (("e4m3", lla.LLA_BF16_Q8), ("int8", lla.LLA_BF16_I8)):
+        desc = lla.make_desc(lla.LLA_2D, dtype, H, d, T, r, r, n_max)
+        lla.lla_quantize_latents(desc, B, n_max, zk, zv, zero, ck, cv)
+        ms = timed_read(desc, ck, cv)
+        row_bytes = B * N * 2 * rb
         sub = {"read_us": round(ms * 1e3, 2),
                "row_GBps": round(row_bytes / (ms / 1e3) / 1e9, 1),
                "row_frac_of_peak": round(row_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),

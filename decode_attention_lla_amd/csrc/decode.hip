@@ -908,7 +908,7 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream) {
   // LLA-2D decode rows (one query per sequence) take the MFMA path when it is compiled
   if (p.variant == LLA_2D && p.rows_per_seq == 1 && !p.causal &&
       decode2d_mfma_supported(dtype, p.r_k, p.r_v, p.d))
-    return launch_decode2d(p, stream);
+    return launch_decode2d(p, dtype, stream);
   const Entry* e = find(dtype, p.r_k, p.r_v);
   if (e == nullptr) return hipErrorNotSupported;
   return launch_valu(p, dtype, e->fn, stream);
@@ -976,7 +976,7 @@ size_t rope_workspace_bytes(const lla_desc& desc, int B) {
 hipError_t launch_decode_rope(const DecodeParams& p, int dtype, hipStream_t stream) {
   if (p.variant == LLA_2D && p.rows_per_seq == 1 && !p.causal &&
       decode2d_mfma_supported(dtype, p.r_k, p.r_v, p.d))
-    return launch_decode2d(p, stream);  // rotary keys as extra MFMA k-steps of the read
+    return launch_decode2d(p, dtype, stream);  // rotary keys as extra MFMA k-steps of the read
   const Entry* e = find(dtype, p.r_k, p.r_v);
   if (e == nullptr) return hipErrorNotSupported;
   const bool grp = p.wg_heads > 1;

@@ -405,6 +405,248 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
     for (int e = 0; e < 4; ++e) w[2 + 16 * rt + 4 * g + e] = D[rt][e];
 }
 
+// ---- 2b. MFMA latent stream over low-bit rows -----------------------------------------------------
+// The contraction of decode2d_partial_kernel (bf16 MFMA, q~ as hi + lo) over LLA-2D rows of LS
+// codes (E4M3 or int8) with a float32 row scale (the low-bit layout of lla.h). Every code is
+// exactly a bf16 value, so codes are converted to bf16 on the way to the MFMA and the row scales
+// are applied outside the products: the K scale multiplies the token's score, the V scale its
+// weight in P (l sums the unscaled weights).
+//   * K: inside each pair of 32-wide k-steps the contraction order is permuted so that a lane's
+//     operands for both steps are one 16-byte run of its token's codes: lane (i, g) of step
+//     2 m + hh holds entries 64 m + 16 g + 8 hh .. + 7, and reads q~ in the same order.
+//   * V: each wave loads its next tile's codes into registers one tile ahead; at the top of an
+//     iteration it converts the current tile's codes to bf16 and writes them to its own LDS tile
+//     in the XOR-swizzled layout of the bf16 kernel, so the transposed operand reads are the same.
+//     The tile is written and read in the same iteration (one LDS tile per wave).
+//   * scales: lanes 0..15 load their token's two scales; the score layout (head per lane, four
+//     tokens) takes them by lane shuffles.
+// Every load of the next tile is unconditional (rows past the split are clamped to its last
+// token and masked), so no wait depends on a branch.
+template <class LS>
+__device__ __forceinline__ float code_value(uint32_t w, int e);  // byte e (literal) of w as a float
+template <>
+__device__ __forceinline__ float code_value<Q8>(uint32_t w, int e) {
+  switch (e) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), 3);
+  }
+}
+template <>
+__device__ __forceinline__ float code_value<I8>(uint32_t w, int e) {
+  return static_cast<float>(static_cast<int8_t>(w >> (8 * e)));
+}
+// four codes (one word) -> four bf16 (two words), exactly
+template <class LS>
+__device__ __forceinline__ uint2 codes4_bf16(uint32_t w) {
+  return make_uint2(f32x2_to_bf16x2(code_value<LS>(w, 0), code_value<LS>(w, 1)),
+                    f32x2_to_bf16x2(code_value<LS>(w, 2), code_value<LS>(w, 3)));
+}
+
+template <class LS, int RK, int RV>
+__global__ __launch_bounds__(512) void decode2d_lowbit_kernel(DecodeParams p, const float* qt,
+                                                              const float* beta, float* part) {
+  constexpr int kW = 8;
+  constexpr int KS = RK / 32;
+  constexpr int KP = KS / 2;            // 16-byte K code runs per lane (pairs of k-steps)
+  constexpr int QS = RK;
+  constexpr int RT = RV / 16;
+  constexpr int RKB = LS::row(RK);      // bytes per cached row
+  constexpr int RVB = LS::row(RV);
+  constexpr int CPR = RV / 16;          // 16-byte code chunks per V row
+  constexpr int VPL = CPR / 4;          // code chunks per lane for a 16-row tile (16 * CPR / 64)
+  constexpr int kVTile = 16 * RV * 2;   // bytes of one bf16 tile
+  constexpr int kPart = 16 * (2 + RV) * 4;
+  constexpr int kTiles = kW * kVTile > 4 * kPart ? kW * kVTile : 4 * kPart;  // the merge reuses it
+  static_assert(RK % 64 == 0 && RV % 64 == 0, "r_k and r_v multiples of 64");
+
+  __shared__ __attribute__((aligned(16))) uint16_t qhi[16 * QS];
+  __shared__ __attribute__((aligned(16))) uint16_t qlo[16 * QS];
+  __shared__ float beta_s[16];
+  __shared__ __attribute__((aligned(16))) char tiles[kTiles];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int split = blockIdx.x % p.splits;  // grid x: b * splits + split; y: head group
+  const int b = blockIdx.x / p.splits;
+  const int h0 = blockIdx.y * 16;
+  const int h = h0 + col;
+  const bool hvalid = h < p.H;
+
+  const int nb = seq_keys(p, b);
+  const int tb = split * p.chunk;
+  const int te = min(nb, tb + p.chunk);
+
+  for (int i = tid; i < 16 * QS; i += 64 * kW) {
+    const int hh = i / QS;
+    const int k = i - hh * QS;
+    const float v = (h0 + hh < p.H) ? qt[(static_cast<size_t>(b) * p.H + h0 + hh) * QS + k] : 0.f;
+    const uint16_t hi = f32_to_bf16(v);
+    qhi[i] = hi;
+    qlo[i] = f32_to_bf16(v - __uint_as_float(static_cast<uint32_t>(hi) << 16));
+  }
+  if (tid < 16) beta_s[tid] = (h0 + tid < p.H) ? beta[static_cast<size_t>(b) * p.H + h0 + tid] : 0.f;
+  __syncthreads();
+
+  const float bt = beta_s[col];
+  const char* zkb = static_cast<const char*>(p.zk) + static_cast<size_t>(b) * p.n_max * RKB;
+  const char* zvb = static_cast<const char*>(p.zv) + static_cast<size_t>(b) * p.n_max * RVB;
+  char* mytile = tiles + wave * kVTile;
+
+  // the loads of the tile starting at tok0 (tok0 < te): K code runs, V code chunks, row scales
+  auto issue = [&](int tok0, uint4 (&kc)[KP], uint4 (&vc)[VPL], float& sk, float& sv) {
+    const int last = te - 1;
+    const size_t krow = static_cast<size_t>(min(tok0 + col, last));
+    const char* kr = zkb + krow * RKB;
+#pragma unroll
+    for (int m = 0; m < KP; ++m) kc[m] = *reinterpret_cast<const uint4*>(kr + 64 * m + 16 * g);
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+      const int c = u * 64 + lane;
+      const int row = c / CPR;
+      vc[u] = *reinterpret_cast<const uint4*>(zvb + static_cast<size_t>(min(tok0 + row, last)) * RVB +
+                                              16 * (c - row * CPR));
+    }
+    sk = *reinterpret_cast<const float*>(kr + RKB - 4);
+    sv = *reinterpret_cast<const float*>(zvb + krow * RVB + RVB - 4);
+  };
+
+  floatx4_t D[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) D[rt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf;
+  float l = 0.f;
+
+  uint4 kc[KP], vc[VPL];
+  float skr = 0.f, svr = 0.f;  // lane i < 16: the scales of the tile's token i
+  int tok0 = tb + wave * 16;
+  if (tok0 < te) issue(tok0, kc, vc, skr, svr);
+  for (; tok0 < te; tok0 += 16 * kW) {
+    uint4 kn[KP], vn[VPL];
+    float skn, svn;
+    issue(min(tok0 + 16 * kW, te - 1), kn, vn, skn, svn);  // the last tile re-reads its own rows
+    // this tile's V codes -> bf16 in the wave's LDS tile (chunk c of row rho: bf16 chunks 2c, 2c + 1)
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+      const int c = u * 64 + lane;
+      const int row = c / CPR;
+      const int cc = c - row * CPR;
+      const uint2 a0 = codes4_bf16<LS>(vc[u].x), a1 = codes4_bf16<LS>(vc[u].y);
+      const uint2 a2 = codes4_bf16<LS>(vc[u].z), a3 = codes4_bf16<LS>(vc[u].w);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int lc = 2 * cc + half;
+        const int pc = (lc & ~7) | ((lc & 7) ^ vswz(row));
+        *reinterpret_cast<uint4*>(mytile + row * RV * 2 + pc * 16) =
+            half == 0 ? make_uint4(a0.x, a0.y, a1.x, a1.y) : make_uint4(a2.x, a2.y, a3.x, a3.y);
+      }
+    }
+    // scores S^T[token tok0 + i][head h0 + j], hi and lo parts of q~ in two chains
+    floatx4_t sh = {0.f, 0.f, 0.f, 0.f};
+    floatx4_t sl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int mm = ks >> 1;
+      const int hh = ks & 1;
+      const uint2 k0 = codes4_bf16<LS>(hh ? kc[mm].z : kc[mm].x);
+      const uint2 k1 = codes4_bf16<LS>(hh ? kc[mm].w : kc[mm].y);
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(k0.x, k0.y, k1.x, k1.y));
+      const int e0 = 64 * mm + 16 * g + 8 * hh;
+      const uint4 bh = *reinterpret_cast<const uint4*>(&qhi[col * QS + e0]);
+      const uint4 bl = *reinterpret_cast<const uint4*>(&qlo[col * QS + e0]);
+      sh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bh), sh, 0, 0, 0);
+      sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bl), sl, 0, 0, 0);
+    }
+    float sc[4], svs[4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float skt = __shfl(skr, 4 * g + e, 64);  // lane 4g + e holds token 4g + e's scales
+      svs[e] = __shfl(svr, 4 * g + e, 64);
+      const bool ok = hvalid && (tok0 + 4 * g + e) < te;
+      sc[e] = ok ? (sh[e] + sl[e]) * skt + bt : kNegInf;
+      tmax = fmaxf(tmax, sc[e]);
+    }
+    tmax = max_over_groups(tmax);
+    if (tmax > m + kLazy2d) {
+      const float c = fast_exp2(m - tmax);
+      l *= c;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) D[rt] *= c;
+      m = tmax;
+    }
+    short4_t bp;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pe = (sc[e] == kNegInf) ? 0.f : fast_exp2(sc[e] - m);
+      l += pe;
+      bp[e] = static_cast<short>(f32_to_bf16(pe * svs[e]));
+    }
+    wave_lds_sync();  // the tile's bf16 rows are in LDS before the transposed reads
+    // A^T[r][head] += Z^V^T[r][tokens 4g+e] . (P^T scaled by the V row scales)[tokens][head]
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+      D[rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v_operand_tr<RV>(mytile, 0, 16 * rt, lane), bp, D[rt], 0, 0, 0);
+    wave_lds_sync();  // the reads are done before the next tile's rows are written
+#pragma unroll
+    for (int i = 0; i < KP; ++i) kc[i] = kn[i];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) vc[i] = vn[i];
+    skr = skn;
+    svr = svn;
+  }
+  l = sum_over_groups(l);
+
+  // merge the waves through LDS (the tiles are free now): 8 -> 4 -> 2 -> 1
+  __syncthreads();
+  float* ps = reinterpret_cast<float*>(tiles);
+  constexpr int PS = 16 * (2 + RV);
+  auto put = [&](float* dst) {
+    if (g == 0) {
+      dst[col * (2 + RV)] = m;
+      dst[col * (2 + RV) + 1] = l;
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[col * (2 + RV) + 2 + 16 * rt + 4 * g + e] = D[rt][e];
+  };
+  auto take = [&](const float* src) {
+    const float mo = src[col * (2 + RV)];
+    const float lo = src[col * (2 + RV) + 1];
+    const float M = fmaxf(m, mo);
+    const float fa = (m == kNegInf) ? 0.f : fast_exp2(m - M);
+    const float fb = (mo == kNegInf) ? 0.f : fast_exp2(mo - M);
+    l = l * fa + lo * fb;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) D[rt][e] = D[rt][e] * fa + src[col * (2 + RV) + 2 + 16 * rt + 4 * g + e] * fb;
+    m = M;
+  };
+#pragma unroll
+  for (int half = kW / 2; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half) put(ps + (wave - half) * PS);
+    __syncthreads();
+    if (wave < half) take(ps + wave * PS);
+    __syncthreads();
+  }
+  if (wave != 0 || !hvalid) return;
+  float* w = part + ((static_cast<size_t>(b) * p.H + h) * p.splits + split) * (2 + RV);
+  if (g == 0) {
+    w[0] = m;
+    w[1] = l;
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[2 + 16 * rt + 4 * g + e] = D[rt][e];
+}
+
 // ---- 3. merge splits, project once through W^V_t[h], finish ------------------------------------
 // One 256-thread workgroup per (head, block of kQB sequences): W^V_t[h] is read once for the block.
 // Thread (grp, sub) = (tid / 16, tid % 16) holds rows grp + 16 i (i < 8: d <= 128) of it, 16-byte
@@ -565,6 +807,7 @@ struct Entry2d {
   void (*qproj[4])(DecodeParams, float*, float*);                     // by kRopeWidths
   void (*partial[4])(DecodeParams, const float*, const float*, float*);
   void (*combine)(DecodeParams, const float*);
+  void (*lowbit[2])(DecodeParams, const float*, const float*, float*);  // E4M3, int8 rows
 };
 
 template <int RK, int RV>
@@ -573,7 +816,8 @@ constexpr Entry2d entry2d() {
           {qproj2d_kernel<RK, 0>, qproj2d_kernel<RK, 32>, qproj2d_kernel<RK, 64>, qproj2d_kernel<RK, 128>},
           {decode2d_partial_kernel<RK, RV, 0>, decode2d_partial_kernel<RK, RV, 32>,
            decode2d_partial_kernel<RK, RV, 64>, decode2d_partial_kernel<RK, RV, 128>},
-          combine2d_kernel<RV>};
+          combine2d_kernel<RV>,
+          {decode2d_lowbit_kernel<Q8, RK, RV>, decode2d_lowbit_kernel<I8, RK, RV>}};
 }
 
 int rope_index(int d_rope) {
@@ -597,7 +841,8 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
 bool decode2d_mfma_supported(int dtype, int r_k, int r_v, int d_head) {
-  return dtype == LLA_BF16 && d_head <= 128 && find2d(r_k, r_v) != nullptr;
+  return (dtype == LLA_BF16 || dtype == LLA_BF16_Q8 || dtype == LLA_BF16_I8) && d_head <= 128 &&
+         find2d(r_k, r_v) != nullptr;
 }
 
 void decode2d_plan(const lla_desc& desc, int B, int* splits, int* chunk) {
@@ -622,10 +867,12 @@ size_t decode2d_workspace_bytes(const lla_desc& desc, int B, int splits, int d_r
   return align256(bh * (desc.r_k + d_rope) * 4) + align256(bh * 4) + bh * splits * (2 + desc.r_v) * 4;
 }
 
-hipError_t launch_decode2d(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_decode2d(const DecodeParams& p, int dtype, hipStream_t stream) {
   const Entry2d* e = find2d(p.r_k, p.r_v);
   const int ri = rope_index(p.d_rope);
   if (e == nullptr || p.d > 128 || ri < 0) return hipErrorNotSupported;
+  const bool low = dtype == LLA_BF16_Q8 || dtype == LLA_BF16_I8;
+  if (low && p.d_rope != 0) return hipErrorNotSupported;  // low-bit rows: no rotary branch here
   // splits and chunk were planned by the caller with decode2d_plan
   lla_desc d{};
   d.H = p.H;
@@ -643,7 +890,8 @@ hipError_t launch_decode2d(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(e->qproj[ri], dim3(p.H * qb), dim3(256), 0, stream, p, qt, beta);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(e->partial[ri], dim3(p.splits * p.B, (p.H + 15) / 16), dim3(64 * Cfg2d<64, 64>::kW), 0,
+  auto partial = low ? e->lowbit[dtype == LLA_BF16_I8 ? 1 : 0] : e->partial[ri];
+  hipLaunchKernelGGL(partial, dim3(p.splits * p.B, (p.H + 15) / 16), dim3(64 * Cfg2d<64, 64>::kW), 0,
                      stream, p, qt, beta, part);
   err = hipGetLastError();
   if (err != hipSuccess) return err;

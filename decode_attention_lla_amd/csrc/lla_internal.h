@@ -133,7 +133,8 @@ bool decode2d_mfma_supported(int dtype, int r_k, int r_v, int d_head);
 void decode2d_plan(const lla_desc& desc, int B, int* splits, int* chunk);
 // Workspace of the LLA-2D MFMA read; d_rope > 0 for the fused rotary branch.
 size_t decode2d_workspace_bytes(const lla_desc& desc, int B, int splits, int d_rope = 0);
-hipError_t launch_decode2d(const DecodeParams& p, hipStream_t s);
+// dtype LLA_BF16, or LLA_BF16_Q8 / LLA_BF16_I8 rows (no rotary branch with those)
+hipError_t launch_decode2d(const DecodeParams& p, int dtype, hipStream_t s);
 size_t prefill_workspace_bytes(const lla_desc& desc, int B, int C);
 
 // Launchers: return hipSuccess, or hipErrorNotSupported when no kernel is compiled for the

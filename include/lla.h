@@ -64,7 +64,9 @@ typedef enum {
  * divisions in float32 and rounded to nearest even (a zero row has s = 0 and zero codes). The
  * row is padded to a multiple of 16 bytes: codes at bytes [0, r), zeros, s in the last 4 bytes.
  * Rows are written by lla_quantize_latents and read by lla_attend_decode, lla_attend_decode_gather
- * and lla_attend_prefill, all on the streaming kernels; lla_encode returns LLA_ERR_UNSUPPORTED for
+ * and lla_attend_prefill on the streaming kernels, and by the LLA-2D MFMA decode (codes converted to
+ * bf16 exactly on the way to the MFMA, the K scale applied to each score, the V scale to each
+ * weight; no rotary branch with low-bit rows); lla_encode returns LLA_ERR_UNSUPPORTED for
  * it (encode with a bf16 descriptor, then quantise).
  *
  * LLA_BF16_I8: the same rows with symmetric integer codes (the pages' 8-bit codec is not specified
@@ -124,6 +126,7 @@ lla_status lla_quantize_latents(const lla_desc* desc, int32_t B, int32_t C, cons
  *   Low-bit latents (LLA_BF16_Q8, LLA_BF16_I8), decode, gather decode and prefill, both
  *   variants on the streaming kernels:                        (8,8) (16,16) (24,24) (32,32)
  *                                                              (96,96)
+ *   Low-bit LLA-2D decode on MFMA, d_head <= 128:              (64,64) (128,128) (256,256)
  * A decode or prefill call with a pair that none of these covers returns LLA_ERR_UNSUPPORTED. */
 
 /* Bytes of device workspace that lla_attend_prefill with a chunk of C rows needs for this

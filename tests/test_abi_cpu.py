@@ -271,7 +271,12 @@ def test_low_bit_support_matrix(low):
     assert decode(desc(r_k=64, r_v=64, **q8)) == lla.LLA_ERR_UNSUPPORTED
     assert gather(desc(r_k=96, r_v=160, **q8)) == lla.LLA_ERR_UNSUPPORTED
     assert prefill(desc(r_k=128, r_v=128, **q8)) == lla.LLA_ERR_UNSUPPORTED
-    assert decode(desc(variant=lla.LLA_2D, r_k=256, r_v=256, **q8)) == lla.LLA_ERR_UNSUPPORTED
+    # LLA-2D low-bit rows on the MFMA read (d_head <= 128): supported, it needs its workspace
+    assert decode(desc(variant=lla.LLA_2D, r_k=256, r_v=256, **q8)) == lla.LLA_ERR_WORKSPACE
+    # the absorbed queries, beta and one split's partials: 2*16*256*4 + 256 + 2*16*(2+256)*4 bytes
+    assert lla.lla_workspace_bytes(desc(variant=lla.LLA_2D, r_k=256, r_v=256, **q8), 2, 1) == \
+        2 * 16 * 256 * 4 + 256 + 2 * 16 * 258 * 4
+    assert decode(desc(variant=lla.LLA_2D, r_k=256, r_v=256, d_head=160, **q8)) == lla.LLA_ERR_UNSUPPORTED
     # same split plan and workspace as bf16 storage on the streaming path
     assert lla.lla_workspace_bytes(desc(r_k=32, r_v=32, dtype=q8["dtype"]), 32, 1) == \
         lla.lla_workspace_bytes(desc(r_k=32, r_v=32), 32, 1)

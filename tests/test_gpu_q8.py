@@ -12,7 +12,7 @@ import torch
 
 from decode_attention_lla_amd import lla, synth
 from oracle import lla_oracle as O
-from tests.gpu_util import assert_close, assert_lse, dev, host, require_gpu
+from tests.gpu_util import assert_close, assert_lse, dev, host, mfma_lse_slack, require_gpu
 from tests.test_gpu_parity import _fill_device_case, mk_desc
 
 pytestmark = pytest.mark.gpu
@@ -248,3 +248,71 @@ def test_deep_loop_q8_full_size_sampled(fmt):
                                  None, None, g["k_self"][t][rows], g["v_self"][t][rows])
         assert_close(host(out)[rows], ro, "bf16", f"deep loop {fmt} t={t}")
         assert_lse(host(lse)[rows], rl, f"deep loop {fmt} t={t}")
+
+
+@pytest.mark.parametrize("fmt", sorted(FORMATS))
+@pytest.mark.parametrize("r", [64, 128, 256])
+def test_decode_q8_lla2d_mfma(r, fmt):
+    """LLA-2D decode over low-bit rows on the MFMA read (codes converted to bf16, the K scale on each
+    score, the V scale on each weight): 20 heads (two 16-head groups, the second ragged), split-K,
+    ragged and empty sequences, sharpened queries, mu and the self token; lse within the MFMA
+    read's q~-rounding slack on the dequantised rows."""
+    B, H, d, T, n_max = 3, 20, 64, 2, 1500
+    lens = np.array([1500, 517, 0], np.int32)
+    for gain, mu, self_token in ((1.0, True, True), (8.0, False, True)):
+        c, desc = _q8_case("2d", B, H, d, T, r, n_max, 9700 + r, gain, fmt)
+        assert lla.lla_workspace_bytes(desc, B) > 0
+        for t in range(T):
+            q = dev(c["q"][t], "bf16")
+            out = torch.full_like(q, float("nan"))
+            lse = torch.full((B, H), float("nan"), device="cuda")
+            print(f"2d mfma {fmt} r={r} gain={gain} t={t}", flush=True)
+            lla.lla_attend_decode(desc, B, t, q, c["_ck"], c["_cv"], dev(lens), c["_Wk"], c["_Wv"],
+                                  c["_mu_k"] if mu else None, c["_mu_v"] if mu else None,
+                                  dev(c["k_self"][t], "bf16") if self_token else None,
+                                  dev(c["v_self"][t], "bf16") if self_token else None, out, lse,
+                                  lla.workspace(desc, B))
+            torch.cuda.synchronize()
+            ro, rl = O.attend_decode(c["q"][t], c["zk_dq"], c["zv_dq"], c["Wk"], c["Wv"], t, lens,
+                                     c["mu_k"] if mu else None, c["mu_v"] if mu else None,
+                                     c["k_self"][t] if self_token else None,
+                                     c["v_self"][t] if self_token else None, variant="2d")
+            what = f"2d mfma {fmt} r={r} gain={gain} mu={mu} t={t}"
+            assert_close(host(out), ro, "bf16", what)
+            assert_lse(host(lse), rl, what, mfma_lse_slack(c["q"][t], c["zk_dq"], c["Wk"], t, lens))
+
+
+@pytest.mark.parametrize("fmt", sorted(FORMATS))
+def test_lla2d_q8_full_size_sampled(fmt):
+    """The LLA-2D decode benchmark shape (B=128, H=16, d=128, T=4, r=256/256, N=8192) with low-bit
+    rows quantised on the device, at the benchmark's launch shape; sequences 0 and 127 (all heads),
+    loop 1, against the explicit oracle on the dequantised rows."""
+    s = synth.CASES["lla2d"]
+    g = _fill_device_case(s)
+    desc = q8_desc("2d", s.H, s.d, s.T, s.r_k, s.r_v, s.n_max, fmt)
+    rb = lla.lla_latent_row_bytes(lla.LLA_BF16_Q8, s.r_k)
+    ck = torch.empty(s.B, s.n_max, rb, dtype=torch.uint8, device="cuda")
+    cv = torch.empty_like(ck)
+    lla.lla_quantize_latents(desc, s.B, s.n_max, g["zk"], g["zv"],
+                             torch.zeros(s.B, dtype=torch.int32, device="cuda"), ck, cv)
+    rows = [0, 127]
+    zk_dq = O.dequantize_latent_rows(*FORMATS[fmt][1](host(g["zk"][rows]).astype(np.float32)))
+    zv_dq = O.dequantize_latent_rows(*FORMATS[fmt][1](host(g["zv"][rows]).astype(np.float32)))
+    del g["zk"], g["zv"]
+    torch.cuda.empty_cache()
+    lens = np.full(s.B, s.N, np.int32)
+    Wk, Wv = dev(g["Wk"], "bf16"), dev(g["Wv"], "bf16")
+    ws = lla.workspace(desc, s.B, 1)
+    t = 1
+    q = dev(g["q"][t], "bf16")
+    out = torch.empty_like(q)
+    lse = torch.empty(s.B, s.H, device="cuda")
+    print(f"lla2d full size {fmt}", flush=True)
+    lla.lla_attend_decode(desc, s.B, t, q, ck, cv, dev(lens), Wk, Wv, None, None,
+                          dev(g["k_self"][t], "bf16"), dev(g["v_self"][t], "bf16"), out, lse, ws)
+    torch.cuda.synchronize()
+    ro, rl = O.attend_decode(g["q"][t][rows], zk_dq, zv_dq, g["Wk"], g["Wv"], t, lens[rows],
+                             None, None, g["k_self"][t][rows], g["v_self"][t][rows], variant="2d")
+    assert_close(host(out)[rows], ro, "bf16", f"lla2d {fmt}")
+    assert_lse(host(lse)[rows], rl, f"lla2d {fmt}",
+               mfma_lse_slack(g["q"][t][rows], zk_dq, g["Wk"], t, lens[rows]))
