@@ -26,6 +26,8 @@
 // rotated at their slots) join its K rows as DR/32 more MFMA k-steps, so the rotary scores are
 // formed in the same accumulators; the self token's rotary score is q_rope . k_rope_self (rotating
 // both at the same position leaves their dot product unchanged).
+#include <type_traits>
+
 #include "lla_device.h"
 #include "lla_internal.h"
 
@@ -405,23 +407,28 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
     for (int e = 0; e < 4; ++e) w[2 + 16 * rt + 4 * g + e] = D[rt][e];
 }
 
-// ---- 2b. MFMA latent stream over low-bit rows -----------------------------------------------------
-// The contraction of decode2d_partial_kernel (bf16 MFMA, q~ as hi + lo) over LLA-2D rows of LS
-// codes (E4M3 or int8) with a float32 row scale (the low-bit layout of lla.h). Every code is
-// exactly a bf16 value, so codes are converted to bf16 on the way to the MFMA and the row scales
-// are applied outside the products: the K scale multiplies the token's score, the V scale its
-// weight in P (l sums the unscaled weights).
-//   * K: inside each pair of 32-wide k-steps the contraction order is permuted so that a lane's
-//     operands for both steps are one 16-byte run of its token's codes: lane (i, g) of step
-//     2 m + hh holds entries 64 m + 16 g + 8 hh .. + 7, and reads q~ in the same order.
-//   * V: each wave loads its next tile's codes into registers one tile ahead; at the top of an
-//     iteration it converts the current tile's codes to bf16 and writes them to its own LDS tile
-//     in the XOR-swizzled layout of the bf16 kernel, so the transposed operand reads are the same.
-//     The tile is written and read in the same iteration (one LDS tile per wave).
-//   * scales: lanes 0..15 load their token's two scales; the score layout (head per lane, four
-//     tokens) takes them by lane shuffles.
-// Every load of the next tile is unconditional (rows past the split are clamped to its last
-// token and masked), so no wait depends on a branch.
+// ---- 2b. MFMA latent stream with register-staged tiles -----------------------------------------
+// The contraction of decode2d_partial_kernel (bf16 MFMA, q~ as hi + lo, same score layout and
+// online softmax) with the tiles staged through registers instead of an LDS-DMA ring. Instantiated
+// for low-bit rows (LS = Q8 or I8: LLA-2D rows of E4M3 or int8 codes with a float32 row scale, the
+// low-bit layout of lla.h), whose codes must be converted before the MFMA; it also reads bf16 rows
+// (LS = BF16), but there the LDS-DMA ring is faster (190 vs 222-231 us per read at B = 128,
+// N = 8192, r = 256: the staged bf16 tiles need 256 registers and spill).
+//   * Two register sets per wave hold the loads of the next two 16-token tiles; a tile's set is
+//     refilled with the tile two ahead as soon as its registers have been consumed (after its V
+//     rows are in LDS and its score MFMAs are issued), so every tile's loads have about one and a
+//     half iterations to land. The loads are unconditional (rows past the split are clamped to its
+//     last token and masked; a wave may run one wholly masked tile at its end).
+//   * V: the wave writes the tile's rows to its own LDS tile in the XOR-swizzled layout of the ring
+//     kernel, so the transposed operand reads are the same; written and read in one iteration.
+//   * Low-bit rows: every code is exactly a bf16 value, so codes are converted to bf16 on the way
+//     to the MFMA and the row scales stay outside the products -- the K scale multiplies the
+//     token's score, the V scale its weight in P (the softmax denominator sums unscaled weights).
+//     Inside each pair of 32-wide k-steps the contraction order is permuted so that a lane's
+//     operands for both steps are one 16-byte run of its token's codes (lane (i, g) of step 2 m + hh
+//     holds entries 64 m + 16 g + 8 hh .. + 7; q~ is read in the same order). Lanes 0..15 load
+//     their token's two scales; the score layout (head per lane, four tokens) takes them by lane
+//     shuffles.
 template <class LS>
 __device__ __forceinline__ float code_value(uint32_t w, int e);  // byte e (literal) of w as a float
 template <>
@@ -445,18 +452,19 @@ __device__ __forceinline__ uint2 codes4_bf16(uint32_t w) {
 }
 
 template <class LS, int RK, int RV>
-__global__ __launch_bounds__(512) void decode2d_lowbit_kernel(DecodeParams p, const float* qt,
+__global__ __launch_bounds__(512) void decode2d_staged_kernel(DecodeParams p, const float* qt,
                                                               const float* beta, float* part) {
+  constexpr bool kLow = !std::is_same<LS, BF16>::value;
   constexpr int kW = 8;
   constexpr int KS = RK / 32;
-  constexpr int KP = KS / 2;            // 16-byte K code runs per lane (pairs of k-steps)
+  constexpr int NK = kLow ? KS / 2 : KS;        // 16-byte K loads per lane and tile
   constexpr int QS = RK;
   constexpr int RT = RV / 16;
-  constexpr int RKB = LS::row(RK);      // bytes per cached row
-  constexpr int RVB = LS::row(RV);
-  constexpr int CPR = RV / 16;          // 16-byte code chunks per V row
-  constexpr int VPL = CPR / 4;          // code chunks per lane for a 16-row tile (16 * CPR / 64)
-  constexpr int kVTile = 16 * RV * 2;   // bytes of one bf16 tile
+  constexpr int RKB = kLow ? LS::row(RK) : RK * 2;  // bytes per cached row
+  constexpr int RVB = kLow ? LS::row(RV) : RV * 2;
+  constexpr int CPR = (kLow ? RV : 2 * RV) / 16;    // 16-byte chunks of a row's V codes or values
+  constexpr int NV = CPR / 4;                       // V loads per lane and tile (16 * CPR / 64)
+  constexpr int kVTile = 16 * RV * 2;               // bytes of one bf16 tile in LDS
   constexpr int kPart = 16 * (2 + RV) * 4;
   constexpr int kTiles = kW * kVTile > 4 * kPart ? kW * kVTile : 4 * kPart;  // the merge reuses it
   static_assert(RK % 64 == 0 && RV % 64 == 0, "r_k and r_v multiples of 64");
@@ -497,22 +505,29 @@ __global__ __launch_bounds__(512) void decode2d_lowbit_kernel(DecodeParams p, co
   const char* zvb = static_cast<const char*>(p.zv) + static_cast<size_t>(b) * p.n_max * RVB;
   char* mytile = tiles + wave * kVTile;
 
-  // the loads of the tile starting at tok0 (tok0 < te): K code runs, V code chunks, row scales
-  auto issue = [&](int tok0, uint4 (&kc)[KP], uint4 (&vc)[VPL], float& sk, float& sv) {
+  struct Set {
+    uint4 k[NK];
+    uint4 v[NV];
+    float sk, sv;  // low-bit: the scales of token col of the tile
+  };
+  // the loads of the tile starting at tok0 (tok0 <= te - 1): K runs, V chunks, row scales
+  auto issue = [&](int tok0, Set& st) {
     const int last = te - 1;
     const size_t krow = static_cast<size_t>(min(tok0 + col, last));
     const char* kr = zkb + krow * RKB;
 #pragma unroll
-    for (int m = 0; m < KP; ++m) kc[m] = *reinterpret_cast<const uint4*>(kr + 64 * m + 16 * g);
+    for (int i = 0; i < NK; ++i) st.k[i] = *reinterpret_cast<const uint4*>(kr + 64 * i + 16 * g);
 #pragma unroll
-    for (int u = 0; u < VPL; ++u) {
+    for (int u = 0; u < NV; ++u) {
       const int c = u * 64 + lane;
       const int row = c / CPR;
-      vc[u] = *reinterpret_cast<const uint4*>(zvb + static_cast<size_t>(min(tok0 + row, last)) * RVB +
-                                              16 * (c - row * CPR));
+      st.v[u] = *reinterpret_cast<const uint4*>(zvb + static_cast<size_t>(min(tok0 + row, last)) * RVB +
+                                                16 * (c - row * CPR));
     }
-    sk = *reinterpret_cast<const float*>(kr + RKB - 4);
-    sv = *reinterpret_cast<const float*>(zvb + krow * RVB + RVB - 4);
+    if constexpr (kLow) {
+      st.sk = *reinterpret_cast<const float*>(kr + RKB - 4);
+      st.sv = *reinterpret_cast<const float*>(zvb + krow * RVB + RVB - 4);
+    }
   };
 
   floatx4_t D[RT];
@@ -521,28 +536,27 @@ __global__ __launch_bounds__(512) void decode2d_lowbit_kernel(DecodeParams p, co
   float m = kNegInf;
   float l = 0.f;
 
-  uint4 kc[KP], vc[VPL];
-  float skr = 0.f, svr = 0.f;  // lane i < 16: the scales of the tile's token i
-  int tok0 = tb + wave * 16;
-  if (tok0 < te) issue(tok0, kc, vc, skr, svr);
-  for (; tok0 < te; tok0 += 16 * kW) {
-    uint4 kn[KP], vn[VPL];
-    float skn, svn;
-    issue(min(tok0 + 16 * kW, te - 1), kn, vn, skn, svn);  // the last tile re-reads its own rows
-    // this tile's V codes -> bf16 in the wave's LDS tile (chunk c of row rho: bf16 chunks 2c, 2c + 1)
+  // one tile: its V rows into LDS, its scores, the refill of its set with tile tnext, then the
+  // softmax and the P.V products
+  auto run = [&](Set& st, int tok0, int tnext) {
 #pragma unroll
-    for (int u = 0; u < VPL; ++u) {
+    for (int u = 0; u < NV; ++u) {
       const int c = u * 64 + lane;
       const int row = c / CPR;
       const int cc = c - row * CPR;
-      const uint2 a0 = codes4_bf16<LS>(vc[u].x), a1 = codes4_bf16<LS>(vc[u].y);
-      const uint2 a2 = codes4_bf16<LS>(vc[u].z), a3 = codes4_bf16<LS>(vc[u].w);
+      if constexpr (kLow) {  // 16 codes -> bf16 chunks 2 cc and 2 cc + 1 of the row
+        const uint2 a0 = codes4_bf16<LS>(st.v[u].x), a1 = codes4_bf16<LS>(st.v[u].y);
+        const uint2 a2 = codes4_bf16<LS>(st.v[u].z), a3 = codes4_bf16<LS>(st.v[u].w);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int lc = 2 * cc + half;
-        const int pc = (lc & ~7) | ((lc & 7) ^ vswz(row));
-        *reinterpret_cast<uint4*>(mytile + row * RV * 2 + pc * 16) =
-            half == 0 ? make_uint4(a0.x, a0.y, a1.x, a1.y) : make_uint4(a2.x, a2.y, a3.x, a3.y);
+        for (int half = 0; half < 2; ++half) {
+          const int lc = 2 * cc + half;
+          const int pc = (lc & ~7) | ((lc & 7) ^ vswz(row));
+          *reinterpret_cast<uint4*>(mytile + row * RV * 2 + pc * 16) =
+              half == 0 ? make_uint4(a0.x, a0.y, a1.x, a1.y) : make_uint4(a2.x, a2.y, a3.x, a3.y);
+        }
+      } else {
+        const int pc = (cc & ~7) | ((cc & 7) ^ vswz(row));
+        *reinterpret_cast<uint4*>(mytile + row * RV * 2 + pc * 16) = st.v[u];
       }
     }
     // scores S^T[token tok0 + i][head h0 + j], hi and lo parts of q~ in two chains
@@ -550,25 +564,37 @@ __global__ __launch_bounds__(512) void decode2d_lowbit_kernel(DecodeParams p, co
     floatx4_t sl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int mm = ks >> 1;
-      const int hh = ks & 1;
-      const uint2 k0 = codes4_bf16<LS>(hh ? kc[mm].z : kc[mm].x);
-      const uint2 k1 = codes4_bf16<LS>(hh ? kc[mm].w : kc[mm].y);
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(k0.x, k0.y, k1.x, k1.y));
-      const int e0 = 64 * mm + 16 * g + 8 * hh;
+      uint4 a;
+      int e0;
+      if constexpr (kLow) {
+        const uint4 w = st.k[ks >> 1];
+        const uint2 k0 = codes4_bf16<LS>((ks & 1) ? w.z : w.x);
+        const uint2 k1 = codes4_bf16<LS>((ks & 1) ? w.w : w.y);
+        a = make_uint4(k0.x, k0.y, k1.x, k1.y);
+        e0 = 64 * (ks >> 1) + 16 * g + 8 * (ks & 1);
+      } else {
+        a = st.k[ks];
+        e0 = 32 * ks + 8 * g;
+      }
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
       const uint4 bh = *reinterpret_cast<const uint4*>(&qhi[col * QS + e0]);
       const uint4 bl = *reinterpret_cast<const uint4*>(&qlo[col * QS + e0]);
       sh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bh), sh, 0, 0, 0);
       sl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bl), sl, 0, 0, 0);
     }
-    float sc[4], svs[4];
+    float sks[4], svs[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {  // lane 4g + e holds token 4g + e's scales
+      sks[e] = kLow ? __shfl(st.sk, 4 * g + e, 64) : 1.f;
+      svs[e] = kLow ? __shfl(st.sv, 4 * g + e, 64) : 1.f;
+    }
+    issue(min(tnext, te - 1), st);
+    float sc[4];
     float tmax = kNegInf;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float skt = __shfl(skr, 4 * g + e, 64);  // lane 4g + e holds token 4g + e's scales
-      svs[e] = __shfl(svr, 4 * g + e, 64);
       const bool ok = hvalid && (tok0 + 4 * g + e) < te;
-      sc[e] = ok ? (sh[e] + sl[e]) * skt + bt : kNegInf;
+      sc[e] = ok ? (sh[e] + sl[e]) * sks[e] + bt : kNegInf;
       tmax = fmaxf(tmax, sc[e]);
     }
     tmax = max_over_groups(tmax);
@@ -587,17 +613,23 @@ __global__ __launch_bounds__(512) void decode2d_lowbit_kernel(DecodeParams p, co
       bp[e] = static_cast<short>(f32_to_bf16(pe * svs[e]));
     }
     wave_lds_sync();  // the tile's bf16 rows are in LDS before the transposed reads
-    // A^T[r][head] += Z^V^T[r][tokens 4g+e] . (P^T scaled by the V row scales)[tokens][head]
+    // A^T[r][head] += Z^V^T[r][tokens 4g+e] . (P^T, times the V row scales)[tokens][head]
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
       D[rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v_operand_tr<RV>(mytile, 0, 16 * rt, lane), bp, D[rt], 0, 0, 0);
     wave_lds_sync();  // the reads are done before the next tile's rows are written
-#pragma unroll
-    for (int i = 0; i < KP; ++i) kc[i] = kn[i];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) vc[i] = vn[i];
-    skr = skn;
-    svr = svn;
+  };
+
+  constexpr int kStep = 16 * kW;
+  Set s0, s1;
+  int tok0 = tb + wave * 16;
+  if (tok0 < te) {
+    issue(tok0, s0);
+    issue(min(tok0 + kStep, te - 1), s1);
+  }
+  for (; tok0 < te; tok0 += 2 * kStep) {
+    run(s0, tok0, tok0 + 2 * kStep);
+    run(s1, tok0 + kStep, tok0 + 3 * kStep);  // wholly masked when past the split
   }
   l = sum_over_groups(l);
 
@@ -807,7 +839,7 @@ struct Entry2d {
   void (*qproj[4])(DecodeParams, float*, float*);                     // by kRopeWidths
   void (*partial[4])(DecodeParams, const float*, const float*, float*);
   void (*combine)(DecodeParams, const float*);
-  void (*lowbit[2])(DecodeParams, const float*, const float*, float*);  // E4M3, int8 rows
+  void (*staged[2])(DecodeParams, const float*, const float*, float*);  // E4M3, int8 rows
 };
 
 template <int RK, int RV>
@@ -817,7 +849,7 @@ constexpr Entry2d entry2d() {
           {decode2d_partial_kernel<RK, RV, 0>, decode2d_partial_kernel<RK, RV, 32>,
            decode2d_partial_kernel<RK, RV, 64>, decode2d_partial_kernel<RK, RV, 128>},
           combine2d_kernel<RV>,
-          {decode2d_lowbit_kernel<Q8, RK, RV>, decode2d_lowbit_kernel<I8, RK, RV>}};
+          {decode2d_staged_kernel<Q8, RK, RV>, decode2d_staged_kernel<I8, RK, RV>}};
 }
 
 int rope_index(int d_rope) {
@@ -890,7 +922,7 @@ hipError_t launch_decode2d(const DecodeParams& p, int dtype, hipStream_t stream)
   hipLaunchKernelGGL(e->qproj[ri], dim3(p.H * qb), dim3(256), 0, stream, p, qt, beta);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  auto partial = low ? e->lowbit[dtype == LLA_BF16_I8 ? 1 : 0] : e->partial[ri];
+  auto partial = low ? e->staged[dtype == LLA_BF16_I8 ? 1 : 0] : e->partial[ri];
   hipLaunchKernelGGL(partial, dim3(p.splits * p.B, (p.H + 15) / 16), dim3(64 * Cfg2d<64, 64>::kW), 0,
                      stream, p, qt, beta, part);
   err = hipGetLastError();
