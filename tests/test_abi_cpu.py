@@ -11,7 +11,7 @@ from decode_attention_lla_amd import lla
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 if not os.path.exists(lla.LIB_PATH):
-    pytest.skip("liblla.so not built (run __graft_entry__.build())", allow_module_level=True)
+    pytest.skip("liblla.so not built (run python -m decode_attention_lla_amd.build)", allow_module_level=True)
 
 
 def declared_functions():
