@@ -271,9 +271,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   const int bh = b * p.H + h;
 
   const int nb = G ? gather_keys(p, b) : row_keys(p, b);
-  const int cw = kHG ? p.chunk : p.chunk / nw;  // the plan keeps chunk a multiple of 32 * nw
-  const int tb = uniform(split * p.chunk + (kHG ? 0 : wave * cw));
-  const int te = uniform(min(nb, min(split * p.chunk + p.chunk, tb + cw)));
+  // the split's keys [s0, s1); nw > 1 waves divide the keys the row actually has (not the planned
+  // chunk) into parts of a multiple of 32 tokens, so no wave streams more than its share
+  const int s0 = split * p.chunk;
+  const int s1 = min(nb, s0 + p.chunk);
+  const int cw = (kHG || nw == 1) ? p.chunk : (max(s1 - s0, 0) + 32 * nw - 1) / (32 * nw) * 32;
+  const int tb = uniform(s0 + (kHG ? 0 : wave * cw));
+  const int te = uniform(min(s1, tb + cw));
 
   // One-load rows stream two register batches ahead. The gather read first stages its split's
   // slot list in LDS (when it fits), so finding a row costs an LDS read rather than a memory round
