@@ -199,12 +199,33 @@ __global__ __launch_bounds__(256) void qproj2d_kernel(DecodeParams p, float* qt,
 //   * the next tile's K rows are loaded into registers and its V rows go straight to LDS with
 //     global_load_lds (each lane's 16 bytes land at base + 16*lane), into the other half of the
 //     wave's double-buffered ring, so both loads overlap the current tile's MFMAs;
+//   * K is loaded as whole 128-byte lines (see k_lines_to_operands) with a non-temporal hint and
+//     put into the MFMA operand layout when the tile is consumed;
 //   * V rows are stored unpadded with 16-byte chunks XOR-swizzled by the row: chunk c of row rho
 //     sits at (c & ~7) | ((c & 7) ^ vswz(rho)), so the transposed reads of the MFMA's V operand
 //     (ds_read_b64_tr_b16, 16 rows x 32 bytes per read) spread evenly over the banks. The swizzle
 //     is applied by choosing each lane's global source address;
 //   * rows past the valid range are clamped to the last valid token (finite data times a zero
 //     weight), so a partial tail tile needs no separate zeroing.
+// K tiles are loaded as whole 128-byte lines. The pair of 32-wide k-steps (2m, 2m + 1) covers
+// bytes [128 m, 128 m + 128) of each token row. In the first of its two loads lane (i, g) reads
+// token i & 7 and in the second token 8 + (i & 7); the lane takes 16 bytes at 16 g of the line's
+// first half when the token's half of the tile (token < 8 or not) matches the lane's half of its
+// row of 16 (i < 8 or not), else of the second half. Each load then reads 8 whole lines, where
+// the MFMA layout (token i at lane (i, g), one 64-byte half per load) would read 16 half lines.
+// The A operand of step 2m (token i, first half) is a lane select between the two loads; that of
+// step 2m + 1 (token i, second half) is the opposite select moved by 8 lanes within each row of
+// 16 (DPP row_ror:8, lane i <-> i ^ 8).
+__device__ __forceinline__ uint32_t row_ror8(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xf, 0xf, false));
+}
+__device__ __forceinline__ void k_lines_to_operands(uint4& a, uint4& b, bool lo) {
+  const uint4 x = lo ? a : b;
+  const uint4 z = lo ? b : a;
+  a = x;
+  b = make_uint4(row_ror8(z.x), row_ror8(z.y), row_ror8(z.z), row_ror8(z.w));
+}
+
 template <int RK, int RV>
 struct Cfg2d {
   static constexpr int kW = 8;                          // waves per workgroup
@@ -227,7 +248,7 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
   constexpr int RT = RV / 16;
   constexpr int CPR = RV / 8;          // 16-byte chunks per V row
   constexpr int VPL = CPR / 4;         // chunks per lane for a 16-row tile (16*CPR / 64)
-  static_assert(RK % 32 == 0 && RV % 64 == 0 && DR % 32 == 0, "r_k, d_rope multiples of 32, r_v of 64");
+  static_assert(RK % 64 == 0 && RV % 64 == 0 && DR % 32 == 0, "r_k, r_v multiples of 64, d_rope of 32");
 
   __shared__ __attribute__((aligned(16))) uint16_t qhi[16 * QS];
   __shared__ __attribute__((aligned(16))) uint16_t qlo[16 * QS];
@@ -249,18 +270,6 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
   const int tb = split * p.chunk;
   const int te = min(nb, tb + p.chunk);
 
-  for (int i = tid; i < 16 * QS; i += 64 * kW) {
-    const int hh = i / QS;
-    const int k = i - hh * QS;
-    const float v = (h0 + hh < p.H) ? qt[(static_cast<size_t>(b) * p.H + h0 + hh) * QS + k] : 0.f;
-    const uint16_t hi = f32_to_bf16(v);
-    qhi[i] = hi;
-    qlo[i] = f32_to_bf16(v - __uint_as_float(static_cast<uint32_t>(hi) << 16));
-  }
-  if (tid < 16) beta_s[tid] = (h0 + tid < p.H) ? beta[static_cast<size_t>(b) * p.H + h0 + tid] : 0.f;
-  __syncthreads();
-
-  const float bt = beta_s[col];
   const char* zkb = static_cast<const char*>(p.zk) + static_cast<size_t>(b) * p.n_max * RK * 2;
   const char* zvb = static_cast<const char*>(p.zv) + static_cast<size_t>(b) * p.n_max * RV * 2;
   char* myring = ring + wave * 2 * CF::kVTile;
@@ -281,9 +290,14 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
       // non-temporal: each instruction reads 1 KiB of whole rows that nothing reads again
       __builtin_amdgcn_global_load_lds((const gptr_t)src, (lptr_t)(dst + i * 1024), 16, 0, 2);
     }
-    const char* arow = zkb + static_cast<size_t>(min(tok0 + col, last)) * RK * 2;
+    // whole 128-byte lines of tokens 0..7 (first load of a pair) and 8..15 (second)
+    const char* ra = zkb + static_cast<size_t>(min(tok0 + (col & 7), last)) * RK * 2 + (col >= 8 ? 64 : 0) + 16 * g;
+    const char* rb = zkb + static_cast<size_t>(min(tok0 + 8 + (col & 7), last)) * RK * 2 + (col < 8 ? 64 : 0) + 16 * g;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kr[ks] = *reinterpret_cast<const uint4*>(arow + (32 * ks + 8 * g) * 2);
+    for (int m = 0; m < KS / 2; ++m) {
+      kr[2 * m] = load_stream(ra + 128 * m);
+      kr[2 * m + 1] = load_stream(rb + 128 * m);
+    }
     if constexpr (DR > 0) {
       const char* rrow = krb + static_cast<size_t>(min(tok0 + col, last)) * DR * 2;
 #pragma unroll
@@ -301,13 +315,28 @@ __global__ __launch_bounds__(512) void decode2d_partial_kernel(DecodeParams p, c
   uint4 kc[KT];
   int tok0 = tb + wave * 16;
   int buf = 0;
+  // the first tile is requested before q~ is staged, so the two latencies overlap
   if (tok0 < te) issue(tok0, 0, kc);
+  for (int i = tid; i < 16 * QS; i += 64 * kW) {
+    const int hh = i / QS;
+    const int k = i - hh * QS;
+    const float v = (h0 + hh < p.H) ? qt[(static_cast<size_t>(b) * p.H + h0 + hh) * QS + k] : 0.f;
+    const uint16_t hi = f32_to_bf16(v);
+    qhi[i] = hi;
+    qlo[i] = f32_to_bf16(v - __uint_as_float(static_cast<uint32_t>(hi) << 16));
+  }
+  if (tid < 16) beta_s[tid] = (h0 + tid < p.H) ? beta[static_cast<size_t>(b) * p.H + h0 + tid] : 0.f;
+  __syncthreads();
+
+  const float bt = beta_s[col];
   for (; tok0 < te; tok0 += 16 * kW) {
     uint4 kn[KT];
     const bool more = tok0 + 16 * kW < te;
     if (more) issue(tok0 + 16 * kW, buf ^ 1, kn);
     // scores S^T[token tok0 + i][head h0 + j]: hi and lo parts of q~ in two independent chains
     __asm__ volatile("" ::: "memory");
+#pragma unroll
+    for (int m = 0; m < KS / 2; ++m) k_lines_to_operands(kc[2 * m], kc[2 * m + 1], col < 8);
     floatx4_t sh = {0.f, 0.f, 0.f, 0.f};
     floatx4_t sl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
