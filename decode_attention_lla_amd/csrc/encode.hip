@@ -293,14 +293,6 @@ __device__ __forceinline__ floatx16_t mfma3232(uint4 a, uint4 b, floatx16_t c) {
 
 __device__ __forceinline__ int gswz(int row, int c) { return c ^ ((row >> 2) & 3); }
 
-// An LDS offset the compiler must treat as unknown. Reads of a ring stage whose addresses it
-// derives from one another lose the information that tells that stage from the stages still
-// being filled, and the compiler then waits for every outstanding transfer before them.
-__device__ __forceinline__ int opaque(int v) {
-  __asm__ volatile("" : "+v"(v));
-  return v;
-}
-
 template <int TN>
 __global__ __launch_bounds__(512) void encode_gemm_kernel(EncodeParams p) {
   constexpr int WN = TN / 2;           // latent rows per wave

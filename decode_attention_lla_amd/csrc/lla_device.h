@@ -55,6 +55,15 @@ __device__ __forceinline__ void buffer_lds16(const void* base, int bytes, __attr
 // flight into registers nor for global_load_lds transfers into other buffers (a workgroup-scope
 // release fence counts those as pending LDS writes and waits for all of them). The memory clobbers
 // keep the compiler from moving memory accesses across it.
+// A value the compiler must treat as unknown (and as new at every evaluation), for LDS offsets:
+// it keeps the compiler from deriving the addresses of one ring stage from another's (which loses
+// the information that tells the stage read from the stages still being filled, so that it waits
+// for every outstanding transfer) and from hoisting every stage's addresses out of a loop.
+__device__ __forceinline__ int opaque(int v) {
+  __asm__ volatile("" : "+v"(v));
+  return v;
+}
+
 __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)

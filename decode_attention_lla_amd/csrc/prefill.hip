@@ -128,6 +128,63 @@ __global__ __launch_bounds__(256) void wk_transpose_kernel(PrefillParams p, uint
   }
 }
 
+// Epilogue of the attention kernels: O = A . W^V_t[h]^T (+ mu^V_t when the row saw any latent),
+// A = D / l, on MFMA as O^T[j][row] = W^V . A^T. The B operand of each 32-wide r chunk comes
+// straight from the accumulator layout: lane (row + 16 g) holds r = 16 rt + 4 g + (0..3), so
+// elements 0-3 take chunk half rt = 2 ks and elements 4-7 rt = 2 ks + 1 (the order of r inside a
+// contraction is free); the A operand, rows j of W^V_t[h], is read in the same order as two 8-byte
+// pieces. A is split into bf16 hi + lo parts, like q~.
+__device__ __forceinline__ void a_hi_lo(const floatx4_t& d0, const floatx4_t& d1, float inv, uint4& hi,
+                                        uint4& lo) {
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = d0[e] * inv;
+    v[4 + e] = d1[e] * inv;
+  }
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    hw[e2] = f32x2_to_bf16x2(v[2 * e2], v[2 * e2 + 1]);
+    lw[e2] = f32x2_to_bf16x2(v[2 * e2] - bf16_lo(hw[e2]), v[2 * e2 + 1] - bf16_hi(hw[e2]));
+  }
+  hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  lo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+}
+
+template <int RV>
+__device__ __forceinline__ void project_rows(const PrefillParams& p, int h, size_t tok, bool rvalid, float l,
+                                             const uint4 (&ahv)[RV / 32], const uint4 (&alv)[RV / 32], int col,
+                                             int g) {
+  const uint16_t* wv = static_cast<const uint16_t*>(p.Wv) + wofs(p, h, RV);
+  const float wr = l > 0.f ? 1.f : 0.f;
+  const size_t mo = mofs(p, h);
+  uint16_t* orow = static_cast<uint16_t*>(p.out) + (tok * p.H + h) * p.d;
+  for (int j0 = 0; j0 < p.d; j0 += 16) {
+    // A operand rows: output channel j0 + col
+    const uint16_t* wrow_j = wv + static_cast<size_t>(j0 + col) * RV + 4 * g;
+    floatx4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < RV / 32; ++ks) {
+      const uint2 p0 = *reinterpret_cast<const uint2*>(wrow_j + 32 * ks);
+      const uint2 p1 = *reinterpret_cast<const uint2*>(wrow_j + 32 * ks + 16);
+      const uint4 aw = make_uint4(p0.x, p0.y, p1.x, p1.y);
+      o = mfma32(aw, ahv[ks], o);
+      o = mfma32(aw, alv[ks], o);
+    }
+    // C layout: lane (row + 16 g) holds channels j0 + 4 g + (0..3) of its row
+    if (rvalid) {
+      float r4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r4[e] = o[e];
+        if (p.mu_v != nullptr) r4[e] += wr * ld<BF16>(p.mu_v, mo + j0 + 4 * g + e);
+      }
+      *reinterpret_cast<uint2*>(orow + j0 + 4 * g) = make_uint2(f32x2_to_bf16x2(r4[0], r4[1]), f32x2_to_bf16x2(r4[2], r4[3]));
+    }
+  }
+}
+
 // ---- P2: causal flash attention over the latents ----------------------------------------------
 // 1D grid of RB*H*B workgroups (RB = ceil(C / 128) row blocks), 512 threads; wave w owns chunk
 // rows j0 + 16 w .. + 15. Workgroups are dispatched round-robin over the 8 XCDs; when B is a
@@ -496,60 +553,346 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     __builtin_amdgcn_s_waitcnt(0x0f70);  // the spare fetches have landed before the wave ends
   }
   l = sum_over_groups(l);
-  // O = A . W^V_t[h]^T (+ mu^V_t when the row saw any latent), A = D / l, on MFMA as
-  // O^T[j][row] = W^V . A^T. The B operand of each 32-wide r chunk comes straight from the
-  // accumulators: lane (row + 16 g) holds r = 16 rt + 4 g + (0..3), so elements 0-3 take chunk half
-  // rt = 2 ks and elements 4-7 rt = 2 ks + 1 (the order of r inside a contraction is free); the
-  // A operand, rows j of W^V_t[h], is read in the same order as two 8-byte pieces. A is split into
-  // bf16 hi + lo parts, like q~.
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   uint4 ahv[RT / 2], alv[RT / 2];
 #pragma unroll
-  for (int ks = 0; ks < RT / 2; ++ks) {
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = D[2 * ks][e] * inv;
-      v[4 + e] = D[2 * ks + 1][e] * inv;
-    }
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      hw[e2] = f32x2_to_bf16x2(v[2 * e2], v[2 * e2 + 1]);
-      lw[e2] = f32x2_to_bf16x2(v[2 * e2] - bf16_lo(hw[e2]), v[2 * e2 + 1] - bf16_hi(hw[e2]));
-    }
-    ahv[ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    alv[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  for (int ks = 0; ks < RT / 2; ++ks) a_hi_lo(D[2 * ks], D[2 * ks + 1], inv, ahv[ks], alv[ks]);
+  project_rows<RV>(p, h, tok, rvalid, l, ahv, alv, col, g);
+}
+// ---- P2w: the attention kernel with specialised waves (r_k = r_v, no rotary branch) -----------
+// Same workgroup rows (128 chunk rows of one head), tiles, scores, softmax and epilogue as
+// prefill_attn_kernel (and the same results, bit for bit), with 16 waves in two roles:
+//   * score waves 0..7 own rows j0 + 16 w .. + 15 as before, q~ in registers: at step t they form
+//     the scores of tile t, the online softmax, and P^T(t) (the bf16 B-operand fragments) with each
+//     row's accumulator rescale factor in a double-buffered LDS slot;
+//   * product waves 8..15 own 64 rows (half p / 4) x RV / 4 latent entries (quarter p % 4,
+//     p = w - 8): at step t they rescale and accumulate A^T += Z^V^T(t - 1) . P^T(t - 1) for four
+//     row blocks, so each transposed V read feeds four MFMAs instead of one (the single-role kernel
+//     reads a whole V tile per 16 rows). They also issue every tile load.
+// Ring (4 stages each): at step t the score waves read K(t) (stage t % 4), the product waves read
+// V(t - 1) (stage (t + 3) % 4), and K(t + 3) and V(t + 2) are requested into the stages read at
+// step t - 1; the loads issued at step t - 3 have landed at step t. Four waves per SIMD, two of each
+// role. At the end the product waves hand A over through the eight ring stages (one 64-row x RV / 4
+// piece per stage, in the accumulator layout) and the score waves run the projection.
+template <int RK, int RV>
+__global__ __launch_bounds__(1024) void prefill_attn_ws_kernel(PrefillParams p, PrefillWs w) {
+  static_assert(RK == RV, "the A hand-off fills the eight ring stages exactly");
+  constexpr int KS = RK / 32;
+  constexpr int RT = RV / 16;
+  constexpr int RQ = RT / 4;                  // 16-entry blocks per product wave
+  constexpr int CPK = RK / 8;
+  constexpr int NRQ = RV / 16;
+  constexpr int KT_BYTES = kKeyTile * RK * 2;
+  constexpr int VT_BYTES = kKeyTile * RV * 2;
+  constexpr int IK = KT_BYTES / 1024;
+  constexpr int IV = VT_BYTES / 1024;
+  constexpr int LK = IK >= 8 ? IK / 8 : 1;    // loads per product wave and tile
+  constexpr int LV = IV >= 8 ? IV / 8 : 1;
+  static_assert(RQ >= 1 && 4 * RQ * 64 * 16 == KT_BYTES, "one 64-row A piece per ring stage");
+  static_assert(IK % 8 == 0 || 8 % IK == 0, "K tile instructions spread evenly over 8 waves");
+  static_assert(IV % 8 == 0 || 8 % IV == 0, "V tile instructions spread evenly over 8 waves");
+  static_assert(3 * (LK + LV) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) char kb0[KT_BYTES], kb1[KT_BYTES], kb2[KT_BYTES], kb3[KT_BYTES];
+  __shared__ __attribute__((aligned(16))) char vb0[VT_BYTES], vb1[VT_BYTES], vb2[VT_BYTES], vb3[VT_BYTES];
+  __shared__ uint4 pt_s[2][8][64];    // P^T fragments of the 8 row blocks, by step parity
+  __shared__ float cf_s[2][kRowsWG];  // accumulator rescale factor of each row, by step parity
+  auto kstage = [&](auto S) -> char* {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return kb0; else if constexpr (st == 1) return kb1;
+    else if constexpr (st == 2) return kb2; else return kb3;
+  };
+  auto vstage = [&](auto S) -> char* {
+    constexpr int st = decltype(S)::value;
+    if constexpr (st == 0) return vb0; else if constexpr (st == 1) return vb1;
+    else if constexpr (st == 2) return vb2; else return vb3;
+  };
+  // ring stage o of the A hand-off: 0..3 the K stages, 4..7 the V stages
+  auto stage_obj = [&](int o) -> char* {
+    return o == 0 ? kb0 : o == 1 ? kb1 : o == 2 ? kb2 : o == 3 ? kb3
+         : o == 4 ? vb0 : o == 5 ? vb1 : o == 6 ? vb2 : vb3;
+  };
+
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const bool scorer = wave < 8;
+  const int RB = (p.C + kRowsWG - 1) / kRowsWG;
+  const int NB = RB * p.H;
+  int b, k;
+  if ((p.B & 7) == 0) {
+    const int P = blockIdx.x;
+    const int rest = P >> 3;
+    k = rest % NB;
+    b = (rest / NB) * 8 + (P & 7);
+  } else {
+    b = blockIdx.x / NB;
+    k = blockIdx.x - b * NB;
   }
-  const uint16_t* wv = static_cast<const uint16_t*>(p.Wv) + wofs(p, h, RV);
-  const float wr = l > 0.f ? 1.f : 0.f;
-  const size_t mo = mofs(p, h);
-  uint16_t* orow = static_cast<uint16_t*>(p.out) + (tok * p.H + h) * p.d;
-  for (int j0 = 0; j0 < p.d; j0 += 16) {
-    // A operand rows: output channel j0 + col
-    const uint16_t* wrow_j = wv + static_cast<size_t>(j0 + col) * RV + 4 * g;
-    floatx4_t o = {0.f, 0.f, 0.f, 0.f};
+  const int h = k / RB;
+  const int j0 = (k - h * RB) * kRowsWG;
+  const int ctx = uniform(p.ctx_lens[b]);
+  const int j_last = min(j0 + kRowsWG, p.C) - 1;
+  const int kmax = min(ctx + j_last, p.n_max - 1);
+  const int ntiles = kmax >= 0 ? kmax / kKeyTile + 1 : 0;
+
+  const size_t lat = p.variant == LLA_2D ? static_cast<size_t>(b) * p.n_max
+                                         : (static_cast<size_t>(b) * p.H + h) * p.n_max;
+  const char* zk = static_cast<const char*>(p.zk) + lat * RK * 2;
+  const char* zv = static_cast<const char*>(p.zv) + lat * RV * 2;
+
+  // step 0's products read the odd slot: P^T(-1) = 0 with factors 1 (published by step 0's barrier)
+  for (int i = tid; i < 8 * 64; i += 1024) pt_s[1][i >> 6][i & 63] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < kRowsWG; i += 1024) cf_s[1][i] = 1.f;
+
+  if (scorer) {
+    // ---- score wave: chunk row jr of this lane (row block sw)
+    const int sw = wave;
+    const int jr = j0 + sw * 16 + col;
+    const bool rvalid = jr < p.C;
+    const int lim = rvalid ? min(ctx + jr, p.n_max - 1) : -1;
+    const size_t tok = static_cast<size_t>(b) * p.C + (rvalid ? jr : 0);
+    const int jw = j0 + sw * 16;
+    const int wave_lim = (jw + 15 < p.C) ? min(ctx + jw, p.n_max - 1) : -1;
+    uint4 qh[KS], ql[KS];  // q~, formed as in prefill_attn_kernel
+    {
+      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (tok * p.H + h) * p.d;
+      const uint16_t* wkt = w.wkt + static_cast<size_t>(h) * RK * p.d;
+      for (int ks = 0; ks < KS; ++ks) {
+        floatx4_t c0 = {0.f, 0.f, 0.f, 0.f};
+        floatx4_t c1 = {0.f, 0.f, 0.f, 0.f};
+        const int k0 = 32 * ks + 8 * (col >> 2) + (col & 3);
+        for (int dd = 0; dd < p.d; dd += 32) {
+          const uint4 bq = *reinterpret_cast<const uint4*>(qrow + dd + 8 * g);
+          const uint4 a0 = *reinterpret_cast<const uint4*>(wkt + static_cast<size_t>(k0) * p.d + dd + 8 * g);
+          const uint4 a1 = *reinterpret_cast<const uint4*>(wkt + static_cast<size_t>(k0 + 4) * p.d + dd + 8 * g);
+          c0 = mfma32(a0, bq, c0);
+          c1 = mfma32(a1, bq, c1);
+        }
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = c0[e] * p.scale_log2;
+          v[4 + e] = c1[e] * p.scale_log2;
+        }
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          hw[e2] = f32x2_to_bf16x2(v[2 * e2], v[2 * e2 + 1]);
+          lw[e2] = f32x2_to_bf16x2(v[2 * e2] - bf16_lo(hw[e2]), v[2 * e2 + 1] - bf16_hi(hw[e2]));
+        }
+        qh[ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        ql[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      }
+    }
+    // running maximum of the row as the accumulators' starting offset (see prefill_attn_kernel)
+    float bm = 0.f;
+    bool based = false;
+    float l = 0.f;
+    auto score_step = [&](auto S, int t) {
+      constexpr int st = decltype(S)::value;
+      lds_barrier();  // K(t) has landed; P^T(t - 2)'s slot has been read
+      const char* kt = kstage(S);
+      const int key0 = t * kKeyTile;
+      float sc[2][4];
+      float tmax = kNegInf;
+      const bool masked = key0 + kKeyTile - 1 > wave_lim;  // wave-uniform
+#pragma unroll
+      for (int kt16 = 0; kt16 < 2; ++kt16) {
+        const int row = 16 * kt16 + col;
+        floatx4_t sh = {bm, bm, bm, bm};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int pc = k_chunk_slot<CPK>(row, 4 * ks + g);
+          const uint4 a = *reinterpret_cast<const uint4*>(kt + row * RK * 2 + pc * 16);
+          sh = mfma32(a, qh[ks], sh);
+          sh = mfma32(a, ql[ks], sh);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[kt16][e] = sh[e];
+        if (masked) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (key0 + 16 * kt16 + 4 * g + e > lim) sc[kt16][e] = kNegInf;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, sc[kt16][e]);
+      }
+      tmax = max_over_groups(tmax);
+      float c = 1.f;
+      if (tmax > kLazyP || (!based && tmax > kNegInf)) {
+        if (based) {
+          c = fast_exp2(-tmax);
+          l *= c;
+        }
+        based = true;
+        bm -= tmax;
+#pragma unroll
+        for (int kt16 = 0; kt16 < 2; ++kt16)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[kt16][e] -= tmax;
+      }
+      float pe[2][4];
+#pragma unroll
+      for (int kt16 = 0; kt16 < 2; ++kt16)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pe[kt16][e] = fast_exp2(sc[kt16][e]);
+          l += pe[kt16][e];
+        }
+      pt_s[st & 1][sw][lane] =
+          make_uint4(f32x2_to_bf16x2(pe[0][0], pe[0][1]), f32x2_to_bf16x2(pe[0][2], pe[0][3]),
+                     f32x2_to_bf16x2(pe[1][0], pe[1][1]), f32x2_to_bf16x2(pe[1][2], pe[1][3]));
+      if (g == 0) cf_s[st & 1][sw * 16 + col] = c;
+    };
+    // one step more than the tiles (the product waves finish the last tile there), in whole
+    // groups of four; both roles pass the same barriers
+    if (ntiles > 0) {
+      for (int t = 0; t <= ntiles; t += kStages) {
+        score_step(StageIdx<0>{}, t);
+        score_step(StageIdx<1>{}, t + 1);
+        score_step(StageIdx<2>{}, t + 2);
+        score_step(StageIdx<3>{}, t + 3);
+      }
+    }
+    __syncthreads();  // the product waves are past the ring
+    __syncthreads();  // A is in the ring stages
+    l = sum_over_groups(l);
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    uint4 ahv[RT / 2], alv[RT / 2];
 #pragma unroll
     for (int ks = 0; ks < RT / 2; ++ks) {
-      const uint2 p0 = *reinterpret_cast<const uint2*>(wrow_j + 32 * ks);
-      const uint2 p1 = *reinterpret_cast<const uint2*>(wrow_j + 32 * ks + 16);
-      const uint4 aw = make_uint4(p0.x, p0.y, p1.x, p1.y);
-      o = mfma32(aw, ahv[ks], o);
-      o = mfma32(aw, alv[ks], o);
-    }
-    // C layout: lane (row + 16 g) holds channels j0 + 4 g + (0..3) of its row
-    if (rvalid) {
-      float r4[4];
+      floatx4_t d2[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        r4[e] = o[e];
-        if (p.mu_v != nullptr) r4[e] += wr * ld<BF16>(p.mu_v, mo + j0 + 4 * g + e);
+      for (int v = 0; v < 2; ++v) {
+        const int rt = 2 * ks + v;
+        const char* src = stage_obj(2 * (rt / RQ) + (sw >> 2));
+        d2[v] = *reinterpret_cast<const floatx4_t*>(src + (((sw & 3) * RQ + rt % RQ) * 64 + lane) * 16);
       }
-      *reinterpret_cast<uint2*>(orow + j0 + 4 * g) = make_uint2(f32x2_to_bf16x2(r4[0], r4[1]), f32x2_to_bf16x2(r4[2], r4[3]));
+      a_hi_lo(d2[0], d2[1], inv, ahv[ks], alv[ks]);
     }
+    project_rows<RV>(p, h, tok, rvalid, l, ahv, alv, col, g);
+    return;
   }
-}
 
+  const int sw = wave - 8;  // product wave index: its load share
+  // ---- product wave: rows 64 half .. + 63, latent entries 16 RQ quarter ..
+  const int half = sw >> 2;
+  const int quarter = sw & 3;
+  const int kbytes = (kmax + 1) * RK * 2;
+  const int vbytes = (kmax + 1) * RV * 2;
+  uint32_t koff[LK], voff[LV];
+#pragma unroll
+  for (int u = 0; u < LK; ++u) {
+    const int i = IK >= 8 ? sw + 8 * u : sw % IK;
+    const int f = i * 64 + lane;
+    const int row = f / CPK;
+    const int pc = f - row * CPK;
+    koff[u] = (row * RK + k_chunk_slot<CPK>(row, pc) * 8) * 2;
+  }
+#pragma unroll
+  for (int u = 0; u < LV; ++u) {
+    const int i = IV >= 8 ? sw + 8 * u : sw % IV;
+    const int U = i * 64 + lane;
+    const int block = U >> 3;
+    const int kq = block / NRQ;
+    const int rq = (block - kq * NRQ) ^ (kq & 1);
+    const int key = 4 * kq + ((U >> 1) & 3);
+    const int r8 = 2 * rq + (U & 1);
+    voff[u] = (key * RV + r8 * 8) * 2;
+  }
+  // K tile tk into kd, V tile tv into vd (tiles past kmax read as zeros)
+  auto issue_k = [&](int tk, char* kd) {
+#pragma unroll
+    for (int u = 0; u < LK; ++u) {
+      const int i = IK >= 8 ? sw + 8 * u : sw % IK;
+      buffer_lds16(zk, kbytes, (lptr_t)(kd + i * 1024), koff[u], tk * kKeyTile * RK * 2);
+    }
+  };
+  auto issue_v = [&](int tv, char* vd) {
+#pragma unroll
+    for (int u = 0; u < LV; ++u) {
+      const int i = IV >= 8 ? sw + 8 * u : sw % IV;
+      buffer_lds16(zv, vbytes, (lptr_t)(vd + i * 1024), voff[u], tv * kKeyTile * RV * 2);
+    }
+  };
+  // lane offsets of the transposed V reads inside a stage (keys 0-15; keys 16-31 sit 4 NRQ 128-byte
+  // blocks further); they pass through opaque() at every step so the compiler forms each stage's
+  // addresses where they are used instead of keeping all of them live across the loop
+  int vlo[RQ];
+#pragma unroll
+  for (int j = 0; j < RQ; ++j) vlo[j] = v_unit_offset<RV>(4 * g, 2 * (RQ * quarter + j)) + 8 * col;
+  floatx4_t D[4][RQ];  // row block 4 half + i, latent block RQ quarter + j
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < RQ; ++j) D[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  auto product_step = [&](auto S, int t) {
+    constexpr int st = decltype(S)::value;
+    // this wave's loads of K(t) and V(t - 1) (step t - 3) have landed; the barrier publishes
+    // everyone's, and P^T(t - 1), and frees the stages read at step t - 1
+    wait_vm_tiles<LK + LV>(kStages - 2);
+    lds_barrier();
+    issue_k(t + kStages - 1, kstage(StageIdx<(st + kStages - 1) % kStages>{}));
+    issue_v(t + kStages - 2, vstage(StageIdx<(st + kStages - 2) % kStages>{}));
+    // A^T += Z^V^T(t - 1) . P^T(t - 1) for the four row blocks (P^T(-1) = 0, factors 1)
+    const char* vt = vstage(StageIdx<(st + kStages - 1) % kStages>{});
+    uint4 pb[4];
+    float cv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pb[i] = pt_s[(st + 1) & 1][4 * half + i][lane];
+      cv[i] = cf_s[(st + 1) & 1][(4 * half + i) * 16 + col];
+    }
+    const bool rescale = cv[0] != 1.f || cv[1] != 1.f || cv[2] != 1.f || cv[3] != 1.f;
+    if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < RQ; ++j) D[i][j] *= cv[i];
+    }
+#pragma unroll
+    for (int j = 0; j < RQ; ++j) {
+      // v_operand_tr<RV>(vt, 0 / 16, 16 (RQ quarter + j), lane), with the lane offset precomputed
+      const char* va = vt + opaque(vlo[j]);
+      const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_ptr)va);
+      const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_ptr)(va + 4 * NRQ * 128));
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        D[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, pb[i]), D[i][j], 0, 0, 0);
+      // one V block at a time: hoisting every block's reads ran the wave out of registers, and the
+      // spilled load offsets were then reloaded (and waited for) at every step
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if (ntiles > 0) {
+    // the loads of steps -3 .. -1: K(0..2) with V(-1..1) (V(-1) a placeholder never read)
+    issue_k(0, kb0);
+    issue_v(0, vb3);
+    issue_k(1, kb1);
+    issue_v(0, vb0);
+    issue_k(2, kb2);
+    issue_v(1, vb1);
+    for (int t = 0; t <= ntiles; t += kStages) {
+      product_step(StageIdx<0>{}, t);
+      product_step(StageIdx<1>{}, t + 1);
+      product_step(StageIdx<2>{}, t + 2);
+      product_step(StageIdx<3>{}, t + 3);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // the spare fetches have landed
+  }
+  __syncthreads();  // every wave is past its last ring read
+  // hand A over: row half `half` of quarter `quarter` goes to ring stage 2 quarter + half, in the
+  // accumulator layout
+  char* dst = stage_obj(2 * quarter + half);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < RQ; ++j) *reinterpret_cast<floatx4_t*>(dst + ((i * RQ + j) * 64 + lane) * 16) = D[i][j];
+  __syncthreads();
+}
 
 struct EntryP {
   int r_k, r_v;
@@ -557,12 +900,21 @@ struct EntryP {
   void (*attn)(PrefillParams, PrefillWs);
   void (*attn_r64)(PrefillParams, PrefillWs);   // with a 64-wide rotary branch
   void (*attn_r128)(PrefillParams, PrefillWs);  // with a 128-wide rotary branch
+  void (*attn_ws)(PrefillParams, PrefillWs);    // specialised waves (r_k = r_v, no rotary branch)
 };
+
+// the specialised-wave kernel where it is faster: r_k = r_v of 128 and 256 (10.2-10.8 vs 11.9-12.2 ms
+// per LLA-2D loop at 256, 6.5-6.6 vs 7.2-7.3 at 128); at 64 the single-role kernel is (3.5 vs 4.9)
+template <int RK, int RV>
+constexpr void (*ws_kernel())(PrefillParams, PrefillWs) {
+  if constexpr (RK == RV && RK >= 128) return prefill_attn_ws_kernel<RK, RV>;
+  else return nullptr;
+}
 
 template <int RK, int RV>
 constexpr EntryP entryP() {
   return {RK, RV, wk_transpose_kernel<RK>, prefill_attn_kernel<RK, RV>,
-          prefill_attn_kernel<RK, RV, 64>, prefill_attn_kernel<RK, RV, 128>};
+          prefill_attn_kernel<RK, RV, 64>, prefill_attn_kernel<RK, RV, 128>, ws_kernel<RK, RV>()};
 }
 
 const EntryP kTableP[] = {
@@ -624,6 +976,10 @@ hipError_t launch_prefill(const PrefillParams& pp, int dtype, hipStream_t stream
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const unsigned nwg = static_cast<unsigned>((pp.C + kRowsWG - 1) / kRowsWG) * pp.H * pp.B;
+    if (pp.d_rope == 0 && e->attn_ws != nullptr) {
+      hipLaunchKernelGGL(e->attn_ws, dim3(nwg), dim3(1024), 0, stream, pp, w);
+      return hipGetLastError();
+    }
     auto attn = pp.d_rope == 64 ? e->attn_r64 : pp.d_rope == 128 ? e->attn_r128 : e->attn;
     hipLaunchKernelGGL(attn, dim3(nwg), dim3(512), 0, stream, pp, w);
     return hipGetLastError();
