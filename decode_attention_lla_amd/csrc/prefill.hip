@@ -185,6 +185,69 @@ __device__ __forceinline__ void project_rows(const PrefillParams& p, int h, size
   }
 }
 
+// Q~ = scale*log2e * W^K_t[h]^T q of a wave's 16 rows (this lane's row at chunk token `tok`),
+// formed on MFMA as Q~^T[k][row] = W^K_t^T . Q^T over d. For each 32-wide k chunk ks two 16x16
+// accumulator tiles take the k-values 32 ks + 8 m + (0..3) and 32 ks + 8 m + 4 + (0..3) as their rows
+// 4 m + (0..3); lane (row + 16 g) then holds elements g of both, k = 32 ks + 8 g + (0..7): exactly the
+// B-operand fragment of the score product. Rows of the transposed W^K are picked in that order.
+// q~ is kept as bf16 hi + lo, so scores keep float32 accuracy.
+template <int RK>
+__device__ __forceinline__ void form_qtilde(const PrefillParams& p, const PrefillWs& w, int h, size_t tok,
+                                            int col, int g, uint4 (&qh)[RK / 32], uint4 (&ql)[RK / 32]) {
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (tok * p.H + h) * p.d;
+  const uint16_t* wkt = w.wkt + static_cast<size_t>(h) * RK * p.d;
+  for (int ks = 0; ks < RK / 32; ++ks) {
+    floatx4_t c0 = {0.f, 0.f, 0.f, 0.f};
+    floatx4_t c1 = {0.f, 0.f, 0.f, 0.f};
+    const int k0 = 32 * ks + 8 * (col >> 2) + (col & 3);  // tile row col of the first tile
+    for (int dd = 0; dd < p.d; dd += 32) {
+      const uint4 bq = *reinterpret_cast<const uint4*>(qrow + dd + 8 * g);
+      const uint4 a0 = *reinterpret_cast<const uint4*>(wkt + static_cast<size_t>(k0) * p.d + dd + 8 * g);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(wkt + static_cast<size_t>(k0 + 4) * p.d + dd + 8 * g);
+      c0 = mfma32(a0, bq, c0);
+      c1 = mfma32(a1, bq, c1);
+    }
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = c0[e] * p.scale_log2;
+      v[4 + e] = c1[e] * p.scale_log2;
+    }
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      hw[e2] = f32x2_to_bf16x2(v[2 * e2], v[2 * e2 + 1]);
+      lw[e2] = f32x2_to_bf16x2(v[2 * e2] - bf16_lo(hw[e2]), v[2 * e2 + 1] - bf16_hi(hw[e2]));
+    }
+    qh[ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    ql[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
+}
+
+// Source byte offset, inside a K tile (kKeyTile rows of RK bf16), of the 16 bytes that land in LDS
+// slot f (= 64 i + lane of the i-th 1 KiB load): chunk slots are XOR-placed by row (the slot map is
+// an involution).
+template <int RK>
+__device__ __forceinline__ uint32_t k_tile_offset(int f) {
+  constexpr int CPK = RK / 8;
+  const int row = f / CPK;
+  const int pc = f - row * CPK;
+  return (row * RK + k_chunk_slot<CPK>(row, pc) * 8) * 2;
+}
+
+// Source byte offset, inside a V tile, of LDS unit U of the blocked V layout (see v_unit_offset):
+// its (key, 8-entry group).
+template <int RV>
+__device__ __forceinline__ uint32_t v_tile_offset(int U) {
+  constexpr int NRQ = RV / 16;
+  const int block = U >> 3;
+  const int kq = block / NRQ;
+  const int rq = (block - kq * NRQ) ^ (kq & 1);  // inverse of the block XOR of v_unit_offset
+  const int key = 4 * kq + ((U >> 1) & 3);
+  const int r8 = 2 * rq + (U & 1);
+  return (key * RV + r8 * 8) * 2;
+}
+
 // ---- P2: causal flash attention over the latents ----------------------------------------------
 // 1D grid of RB*H*B workgroups (RB = ceil(C / 128) row blocks), 512 threads; wave w owns chunk
 // rows j0 + 16 w .. + 15. Workgroups are dispatched round-robin over the 8 XCDs; when B is a
@@ -298,46 +361,12 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
   const char* zk = static_cast<const char*>(p.zk) + lat * RK * 2;
   const char* zv = static_cast<const char*>(p.zv) + lat * RV * 2;
 
-  // Q~ = scale*log2e * W^K_t[h]^T q of this wave's 16 rows, formed here on MFMA as
-  // Q~^T[k][row] = W^K_t^T . Q^T over d. For each 32-wide k chunk ks two 16x16 accumulator tiles
-  // take the k-values 32 ks + 8 m + (0..3) and 32 ks + 8 m + 4 + (0..3) as their rows 4 m + (0..3);
-  // lane (row + 16 g) then holds elements g of both, k = 32 ks + 8 g + (0..7): exactly the B-operand
-  // fragment of the score product. Rows of the transposed W^K are picked in that order. q~ is kept
-  // as bf16 hi + lo (two MFMA chains), so scores keep float32 accuracy. The mu^K_t part of every
-  // score of a row, scale*log2e * q . mu^K_t, is one constant per row: softmax does not depend on
-  // it and this path returns no log-sum-exp, so it is never formed.
+  // q~ of this wave's 16 rows (form_qtilde). The mu^K_t part of every score of a row,
+  // scale*log2e * q . mu^K_t, is one constant per row: softmax does not depend on it and this path
+  // returns no log-sum-exp, so it is never formed.
   const size_t tok = static_cast<size_t>(b) * p.C + (rvalid ? jr : 0);  // (b, chunk row) of this lane
   uint4 qh[KS], ql[KS];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (tok * p.H + h) * p.d;
-    const uint16_t* wkt = w.wkt + static_cast<size_t>(h) * RK * p.d;
-    for (int ks = 0; ks < KS; ++ks) {
-      floatx4_t c0 = {0.f, 0.f, 0.f, 0.f};
-      floatx4_t c1 = {0.f, 0.f, 0.f, 0.f};
-      const int k0 = 32 * ks + 8 * (col >> 2) + (col & 3);  // tile row col of the first tile
-      for (int dd = 0; dd < p.d; dd += 32) {
-        const uint4 bq = *reinterpret_cast<const uint4*>(qrow + dd + 8 * g);
-        const uint4 a0 = *reinterpret_cast<const uint4*>(wkt + static_cast<size_t>(k0) * p.d + dd + 8 * g);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(wkt + static_cast<size_t>(k0 + 4) * p.d + dd + 8 * g);
-        c0 = mfma32(a0, bq, c0);
-        c1 = mfma32(a1, bq, c1);
-      }
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = c0[e] * p.scale_log2;
-        v[4 + e] = c1[e] * p.scale_log2;
-      }
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        hw[e2] = f32x2_to_bf16x2(v[2 * e2], v[2 * e2 + 1]);
-        lw[e2] = f32x2_to_bf16x2(v[2 * e2] - bf16_lo(hw[e2]), v[2 * e2 + 1] - bf16_hi(hw[e2]));
-      }
-      qh[ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      ql[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-    }
-  }
+  form_qtilde<RK>(p, w, h, tok, col, g, qh, ql);
   // Rotary query fragments (B operand of the extra steps, same element order as the rotary tile's
   // chunks): lane (row, g) holds channels 32 kr + 8 g .. + 7 of the row's rotary query, rotated at
   // the row's position ctx + jr (float64 angles), times scale*log2e, as bf16 hi + lo.
@@ -386,25 +415,9 @@ __global__ __launch_bounds__(512) void prefill_attn_kernel(PrefillParams p, Pref
     roff[u] = (row * DR + k_chunk_slot<CPR>(row, pc) * 8) * 2;
   }
 #pragma unroll
-  for (int u = 0; u < LK; ++u) {
-    const int i = IK >= 8 ? wave + 8 * u : wave % IK;
-    const int f = i * 64 + lane;
-    const int row = f / CPK;
-    const int pc = f - row * CPK;
-    koff[u] = (row * RK + k_chunk_slot<CPK>(row, pc) * 8) * 2;  // the slot map is an involution
-  }
+  for (int u = 0; u < LK; ++u) koff[u] = k_tile_offset<RK>((IK >= 8 ? wave + 8 * u : wave % IK) * 64 + lane);
 #pragma unroll
-  for (int u = 0; u < LV; ++u) {
-    // LDS unit U = 64 i + lane of the blocked V layout; its source is (key, 8-entry group)
-    const int i = IV >= 8 ? wave + 8 * u : wave % IV;
-    const int U = i * 64 + lane;
-    const int block = U >> 3;
-    const int kq = block / NRQ;
-    const int rq = (block - kq * NRQ) ^ (kq & 1);  // inverse of the block XOR of v_unit_offset
-    const int key = 4 * kq + ((U >> 1) & 3);
-    const int r8 = 2 * rq + (U & 1);
-    voff[u] = (key * RV + r8 * 8) * 2;
-  }
+  for (int u = 0; u < LV; ++u) voff[u] = v_tile_offset<RV>((IV >= 8 ? wave + 8 * u : wave % IV) * 64 + lane);
   auto issue = [&](int tile, char* kd, char* vd, char* rd) {
     const uint32_t key0 = tile * kKeyTile;
 #pragma unroll
@@ -655,37 +668,8 @@ __global__ __launch_bounds__(1024) void prefill_attn_ws_kernel(PrefillParams p, 
     const size_t tok = static_cast<size_t>(b) * p.C + (rvalid ? jr : 0);
     const int jw = j0 + sw * 16;
     const int wave_lim = (jw + 15 < p.C) ? min(ctx + jw, p.n_max - 1) : -1;
-    uint4 qh[KS], ql[KS];  // q~, formed as in prefill_attn_kernel
-    {
-      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (tok * p.H + h) * p.d;
-      const uint16_t* wkt = w.wkt + static_cast<size_t>(h) * RK * p.d;
-      for (int ks = 0; ks < KS; ++ks) {
-        floatx4_t c0 = {0.f, 0.f, 0.f, 0.f};
-        floatx4_t c1 = {0.f, 0.f, 0.f, 0.f};
-        const int k0 = 32 * ks + 8 * (col >> 2) + (col & 3);
-        for (int dd = 0; dd < p.d; dd += 32) {
-          const uint4 bq = *reinterpret_cast<const uint4*>(qrow + dd + 8 * g);
-          const uint4 a0 = *reinterpret_cast<const uint4*>(wkt + static_cast<size_t>(k0) * p.d + dd + 8 * g);
-          const uint4 a1 = *reinterpret_cast<const uint4*>(wkt + static_cast<size_t>(k0 + 4) * p.d + dd + 8 * g);
-          c0 = mfma32(a0, bq, c0);
-          c1 = mfma32(a1, bq, c1);
-        }
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = c0[e] * p.scale_log2;
-          v[4 + e] = c1[e] * p.scale_log2;
-        }
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          hw[e2] = f32x2_to_bf16x2(v[2 * e2], v[2 * e2 + 1]);
-          lw[e2] = f32x2_to_bf16x2(v[2 * e2] - bf16_lo(hw[e2]), v[2 * e2 + 1] - bf16_hi(hw[e2]));
-        }
-        qh[ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        ql[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      }
-    }
+    uint4 qh[KS], ql[KS];
+    form_qtilde<RK>(p, w, h, tok, col, g, qh, ql);
     // running maximum of the row as the accumulators' starting offset (see prefill_attn_kernel)
     float bm = 0.f;
     bool based = false;
@@ -784,24 +768,9 @@ __global__ __launch_bounds__(1024) void prefill_attn_ws_kernel(PrefillParams p, 
   const int vbytes = (kmax + 1) * RV * 2;
   uint32_t koff[LK], voff[LV];
 #pragma unroll
-  for (int u = 0; u < LK; ++u) {
-    const int i = IK >= 8 ? sw + 8 * u : sw % IK;
-    const int f = i * 64 + lane;
-    const int row = f / CPK;
-    const int pc = f - row * CPK;
-    koff[u] = (row * RK + k_chunk_slot<CPK>(row, pc) * 8) * 2;
-  }
+  for (int u = 0; u < LK; ++u) koff[u] = k_tile_offset<RK>((IK >= 8 ? sw + 8 * u : sw % IK) * 64 + lane);
 #pragma unroll
-  for (int u = 0; u < LV; ++u) {
-    const int i = IV >= 8 ? sw + 8 * u : sw % IV;
-    const int U = i * 64 + lane;
-    const int block = U >> 3;
-    const int kq = block / NRQ;
-    const int rq = (block - kq * NRQ) ^ (kq & 1);
-    const int key = 4 * kq + ((U >> 1) & 3);
-    const int r8 = 2 * rq + (U & 1);
-    voff[u] = (key * RV + r8 * 8) * 2;
-  }
+  for (int u = 0; u < LV; ++u) voff[u] = v_tile_offset<RV>((IV >= 8 ? sw + 8 * u : sw % IV) * 64 + lane);
   // K tile tk into kd, V tile tv into vd (tiles past kmax read as zeros)
   auto issue_k = [&](int tk, char* kd) {
 #pragma unroll
