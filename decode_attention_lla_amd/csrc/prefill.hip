@@ -18,6 +18,8 @@
 //      v_mfma_f32_16x16x32_bf16 with P taken straight from the S^T accumulators (two 16-key halves
 //      form one K=32 step) and Z^V^T read with the transposing ds_read_b64_tr_b16; finally
 //      O = A . W^V_t[h]^T (+ mu^V_t when the row saw any latent) on MFMA from the accumulators.
+//      For r_k = r_v of 128 or 256 without the rotary branch, P1 runs as prefill_attn_ws_kernel:
+//      the same arithmetic with score waves and product waves (see there), fewer LDS reads per MFMA.
 // LLA-2D and per-head differ only in which latent sequence a head reads (b, or (b, h)) and in the
 // factor and mu offsets.
 //
