@@ -335,6 +335,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
   // rows reads ~5% slower than with ordinary loads.
   constexpr int kAux = 2;
   constexpr bool kPipe = kOne && !G;  // the contiguous buffer-load read (always two batches ahead)
+  // the gather read's one-batch-ahead row lookup (below), where its registers keep the occupancy
+  constexpr bool kAhead = G && kOne &&
+                          (std::is_same<S, F32>::value || (kQ8 && RK >= 16) || (RK == 24 && RV == 24) ||
+                           (RK == 96 && RV == 96));
   // Rotary keys (R): [B][n_max][DR] bf16, one row per token shared by every head of the sequence.
   // Lane `sub` of a token's group holds pieces sub + LPT * k of the row (16 bytes each); ordinary
   // loads, so the row stays in L2 for the sequence's other heads.
@@ -496,17 +500,30 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
     // consumed, so a wave always has a batch in flight. Rows past the split (or, gathered, with
     // a slot outside the cache) read as zeros through the descriptor bound (no memory access)
     // and are masked; a batch wholly past the split costs only its masked arithmetic.
-    auto issue = [&](int t0, uint4 (&kr)[U][VK], uint4 (&vr)[U][VV], uint4 (&srv)[SRU][NSR]) {
+    // A gathered row comes from the staged list (nrows: past the split, or a slot outside the
+    // cache). With kAhead the gather read looks a batch's rows up one batch before its loads are
+    // issued, so the LDS read's latency overlaps the batch consumed in between instead of delaying
+    // the issue (sink + window list at the capacity shape: 210-212 -> 203-206 us); it costs 2 U
+    // registers, so it is kept where the kernel's occupancy stays the same.
+    auto gathered_row = [&](int tok) -> uint32_t {
+      const int s = tok < te ? slot_s[min(tok - tb, kSlotCap - 1)] : -1;
+      return static_cast<unsigned>(s) < static_cast<unsigned>(p.n_max) ? static_cast<uint32_t>(s) : nrows;
+    };
+    auto lookup = [&](int t0, uint32_t (&rr)[U]) {
+      if constexpr (kAhead) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) rr[u] = gathered_row(t0 + u * TPW + grp);
+      }
+    };
+    auto issue = [&](int t0, const uint32_t (&rrs)[U], uint4 (&kr)[U][VK], uint4 (&vr)[U][VV],
+                     uint4 (&srv)[SRU][NSR]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int tok = t0 + u * TPW + grp;
         uint32_t rr;
-        if constexpr (G) {
-          const int s = tok < te ? slot_s[min(tok - tb, kSlotCap - 1)] : -1;
-          rr = static_cast<unsigned>(s) < static_cast<unsigned>(p.n_max) ? static_cast<uint32_t>(s) : nrows;
-        } else {
-          rr = static_cast<uint32_t>(min(tok, te) - row0);
-        }
+        if constexpr (kAhead) rr = rrs[u];
+        else if constexpr (G) rr = gathered_row(tok);
+        else rr = static_cast<uint32_t>(min(tok, te) - row0);
         load_slice<SK, kAux, LPT>(rsk, rr * RKB, sub, kr[u]);
         load_slice<SV, kAux, LPT>(rsv, rr * RVB, sub, vr[u]);
         if constexpr (!kHG) {
@@ -528,33 +545,42 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_partial_kernel(DecodePa
         }
       }
     };
-    auto mask = [&](int t0, bool (&ok)[U]) {
+    auto mask = [&](int t0, const uint32_t (&rrs)[U], bool (&ok)[U]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int tok = t0 + u * TPW + grp;
-        ok[u] = tok < te;
-        if constexpr (G)
-          ok[u] = ok[u] && static_cast<unsigned>(slot_s[min(tok - tb, kSlotCap - 1)]) < static_cast<unsigned>(p.n_max);
+        if constexpr (kAhead) {
+          ok[u] = rrs[u] != nrows;
+        } else {
+          ok[u] = tok < te;
+          if constexpr (G)
+            ok[u] = ok[u] && static_cast<unsigned>(slot_s[min(tok - tb, kSlotCap - 1)]) < static_cast<unsigned>(p.n_max);
+        }
       }
     };
     uint4 ka[U][VK], va[U][VV], kb[U][VK], vb[U][VV];
     uint4 sa[SRU][NSR], sb[SRU][NSR];
+    uint32_t ra[U], rb[U];  // kAhead: the looked-up rows of the batches in ka and kb
     bool ok[U];
     if constexpr (G) {  // the first rows' slots come from the list the prologue stages
       prologue();
-      if (tb < te) issue(tb, ka, va, sa);
+      lookup(tb, ra);
+      if (tb < te) issue(tb, ra, ka, va, sa);
     } else {
-      if (tb < te) issue(tb, ka, va, sa);
+      if (tb < te) issue(tb, ra, ka, va, sa);
       prologue();
     }
+    lookup(tb + kStep, rb);
     for (int t0 = tb; t0 < te; t0 += 2 * kStep) {
-      issue(t0 + kStep, kb, vb, sb);
-      mask(t0, ok);
+      issue(t0 + kStep, rb, kb, vb, sb);
+      mask(t0, ra, ok);
+      lookup(t0 + 2 * kStep, ra);
       consume(ka, va, ok, sa, rt_s[0]);
       // no early exit here: with one exit at the bottom the compiler's wait before the loop top
       // leaves the batch just issued in flight (an exit here made it drain every load)
-      issue(t0 + 2 * kStep, ka, va, sa);
-      mask(t0 + kStep, ok);
+      issue(t0 + 2 * kStep, ra, ka, va, sa);
+      mask(t0 + kStep, rb, ok);
+      lookup(t0 + 3 * kStep, rb);
       consume(kb, vb, ok, sb, rt_s[kHG ? 1 : 0]);
     }
    }
