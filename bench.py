@@ -223,10 +223,14 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    copy_gbs = device_copy_ceiling(stream)
 
     tokens_per_s = B / (ms_step / 1e3)
     H_lat = 1 if two_d else H
     latent_bytes = B * H_lat * N * (rk + rv) * 2  # per read: every cached latent pair, once
+    # everything else a read must move: q, the self K/V and out (B*H*d each), W^K_t and W^V_t, the
+    # lengths, and the split partials written and read back when the plan splits the tokens
+    other_bytes = 4 * B * H * d * 2 + H * d * (rk + rv) * 2 + B * 4 + 2 * lla.lla_workspace_bytes(desc, B, 1)
     achieved = latent_bytes / (avg_launch_ms / 1e3) / 1e9
     traffic = load_traffic() if args.workload == "capacity" and D == s.D else None
 
@@ -280,6 +284,10 @@ def main():
         },
         "latent_GBps": round(achieved, 1),
         "latent_frac_of_peak": round(achieved / HBM_PEAK_GBS, 4),
+        "total_GBps": round((latent_bytes + other_bytes) / (avg_launch_ms / 1e3) / 1e9, 1),
+        "total_bytes_per_read": latent_bytes + other_bytes,
+        "device_copy_GBps": round(copy_gbs, 1),
+        "device_copy_frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
             "kernel": (f"decode2d qproj + partial<{rk},{rv}> (MFMA) + combine per read" if two_d else
@@ -295,6 +303,8 @@ def main():
         "cpu_baseline": cpu,
     }
     res.update(res_extra)
+    if cpu is not None:
+        res["gpu_over_cpu"] = round(tokens_per_s / cpu["value"], 1)
     if extras is not None:
         res["extras"] = extras
     print(json.dumps(res), flush=True)
@@ -841,6 +851,27 @@ def _cpu_model():
     except OSError:
         pass
     return None
+
+
+def device_copy_ceiling(stream, gib=4, reps=5):
+    """Measured device-to-device copy rate (bytes read + bytes written per second, GB/s) of a
+    `gib` GiB buffer: the ceiling a plain copy reaches on this part, beside the datasheet peak."""
+    import torch
+    a = torch.empty(gib * 2 ** 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    b.copy_(a)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * gib * 2 ** 30 / (ms / 1e3) / 1e9
 
 
 def cpu_baseline(args, s, D, zk, zv, Wk, Wv, Ek, Ev, q, kself, vself, xk, xv, lens):
