@@ -13,7 +13,7 @@ import torch
 from decode_attention_lla_amd import lla, synth
 from oracle import lla_oracle as O
 from tests.gpu_util import assert_close, assert_lse, dev, host, rel_err, require_gpu
-from tests.test_gpu_parity import _fill_device_case, mk_desc, upload
+from tests.test_gpu_parity import PAIRS, _fill_device_case, mk_desc, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -50,9 +50,8 @@ def oracle_gather(c, t, slots, counts, variant, self_token=True, mu=True):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("variant,rk,rv", [("per_head", 8, 8), ("per_head", 24, 24),
-                                           ("per_head", 96, 160), ("per_head", 256, 256),
-                                           ("2d", 32, 32), ("2d", 128, 128)])
+@pytest.mark.parametrize("variant,rk,rv", [("per_head", rk, rv) for rk, rv in PAIRS] +
+                         [("2d", 32, 32), ("2d", 128, 128)])
 def test_gather_sweep(dtype, variant, rk, rv):
     B, H, d, T, n_max, budget = 3, 2, 64, 2, 1301, 700
     desc = mk_desc(variant, dtype, H, d, T, rk, rv, n_max)

@@ -149,7 +149,7 @@ def test_decode_q8(variant, r, fmt):
 
 
 @pytest.mark.parametrize("fmt", sorted(FORMATS))
-@pytest.mark.parametrize("r", [24, 96])
+@pytest.mark.parametrize("r", [8, 16, 24, 32, 96])
 def test_gather_and_prefill_q8(fmt, r):
     B, H, d, T, n_max = 2, 2, 64, 2, 700
     c, desc = _q8_case("per_head", B, H, d, T, r, n_max, 9600 + r, fmt=fmt)
