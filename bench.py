@@ -99,7 +99,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the LLA latent-cache path runs on a single MI355X "
-              "here (see DESIGN.md for how it would shard); run with --gpus 1.", file=sys.stderr)
+              "here (the library has no multi-GPU path); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
