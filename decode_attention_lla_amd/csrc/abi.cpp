@@ -227,19 +227,18 @@ lla_status lla_encode(const lla_desc* desc, int32_t B, int32_t C, const void* xk
     p.H = 1;
     p.d = desc->H * desc->d_head;
   }
+  lla::EncodeParams pv = p;
   p.x = xk;
   p.E = Ek;
   p.mu = mu_k;
   p.z = zk;
   p.r = desc->r_k;
-  lla_status st = from_hip(lla::launch_encode(p, desc->dtype, s));
-  if (st != LLA_OK) return st;
-  p.x = xv;
-  p.E = Ev;
-  p.mu = mu_v;
-  p.z = zv;
-  p.r = desc->r_v;
-  return from_hip(lla::launch_encode(p, desc->dtype, s));
+  pv.x = xv;
+  pv.E = Ev;
+  pv.mu = mu_v;
+  pv.z = zv;
+  pv.r = desc->r_v;
+  return from_hip(lla::launch_encode_kv(p, pv, desc->dtype, s));
 }
 
 

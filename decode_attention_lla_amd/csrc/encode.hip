@@ -95,11 +95,36 @@ __device__ __forceinline__ floatx4_t mfma(uint4 a, uint4 b, floatx4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// The parameters of one axis: the second (pv) for workgroups in the upper half of a two-axis grid.
+// Field by field, so each stays a scalar.
+__device__ __forceinline__ EncodeParams pick_axis(const EncodeParams& pk, const EncodeParams& pv, bool v) {
+  EncodeParams p;
+  p.x = v ? pv.x : pk.x;
+  p.E = v ? pv.E : pk.E;
+  p.mu = v ? pv.mu : pk.mu;
+  p.pos = v ? pv.pos : pk.pos;
+  p.z = v ? pv.z : pk.z;
+  p.B = v ? pv.B : pk.B;
+  p.C = v ? pv.C : pk.C;
+  p.H = v ? pv.H : pk.H;
+  p.d = v ? pv.d : pk.d;
+  p.T = v ? pv.T : pk.T;
+  p.r = v ? pv.r : pk.r;
+  p.n_max = v ? pv.n_max : pk.n_max;
+  return p;
+}
+
 // NT: 16-column latent tiles per wave; MT: 16-token tiles per wave. KSPLIT 1: each of the 4 waves
 // owns its own 16*MT tokens over the whole K; KSPLIT 4 or 8: that many waves share 16*MT tokens
-// and split K, reducing through LDS (KSPLIT 8 runs 8-wave workgroups).
+// and split K, reducing through LDS (KSPLIT 8 runs 8-wave workgroups). Grid y is the latent tiles
+// of one axis (ytiles of them), or of both axes when the K and V encodes share a launch (pk's in
+// the lower half, pv's in the upper half): a dependent launch costs a few microseconds on its own,
+// as much as a decode-size encode's work.
 template <int NT, int MT, int KSPLIT>
-__global__ __launch_bounds__(KSPLIT == 8 ? 512 : 256) void encode_mfma_kernel(EncodeParams p) {
+__global__ __launch_bounds__(KSPLIT == 8 ? 512 : 256) void encode_mfma_kernel(EncodeParams pk, EncodeParams pv,
+                                                                            int ytiles) {
+  const bool second = static_cast<int>(blockIdx.y) >= ytiles;
+  const EncodeParams p = pick_axis(pk, pv, second);
   constexpr int U = 4;  // k-steps whose loads are issued together
   constexpr int NW = KSPLIT == 8 ? 8 : 4;  // waves per workgroup
   constexpr int TOK_WG = KSPLIT == 1 ? NW * 16 * MT : 16 * MT;
@@ -116,7 +141,7 @@ __global__ __launch_bounds__(KSPLIT == 8 ? 512 : 256) void encode_mfma_kernel(En
   const int nk = (K + 31) / 32;
   const int ntok = p.B * p.C;
   const int h = blockIdx.z;
-  const int r0 = blockIdx.y * 16 * NT;
+  const int r0 = (static_cast<int>(blockIdx.y) - (second ? ytiles : 0)) * 16 * NT;
   const int n_base = blockIdx.x * TOK_WG + (KSPLIT == 1 ? wave * 16 * MT : 0);
   const size_t HD = static_cast<size_t>(p.H) * p.d;
   const uint16_t* x = static_cast<const uint16_t*>(p.x);
@@ -246,19 +271,22 @@ __global__ __launch_bounds__(KSPLIT == 8 ? 512 : 256) void encode_mfma_kernel(En
     }
 }
 
+// pv: the second axis sharing the launch (same shape and rank as p), or null for p alone
 template <int MT, int KSPLIT>
-hipError_t launch_encode_mfma(const EncodeParams& p, int nt_tiles, hipStream_t stream) {
+hipError_t launch_encode_mfma(const EncodeParams& p, const EncodeParams* pv, int nt_tiles, hipStream_t stream) {
   constexpr int NW = KSPLIT == 8 ? 8 : 4;
   constexpr int TOK_WG = KSPLIT == 1 ? NW * 16 * MT : 16 * MT;
   const unsigned ntok = static_cast<unsigned>(p.B) * p.C;
-  dim3 grid((ntok + TOK_WG - 1) / TOK_WG, (p.r + 16 * nt_tiles - 1) / (16 * nt_tiles), p.H);
+  const int ytiles = (p.r + 16 * nt_tiles - 1) / (16 * nt_tiles);
+  dim3 grid((ntok + TOK_WG - 1) / TOK_WG, ytiles * (pv != nullptr ? 2 : 1), p.H);
   dim3 block(64 * NW);
+  const EncodeParams& q = pv != nullptr ? *pv : p;
   if (nt_tiles == 1)
-    hipLaunchKernelGGL((encode_mfma_kernel<1, MT, KSPLIT>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((encode_mfma_kernel<1, MT, KSPLIT>), grid, block, 0, stream, p, q, ytiles);
   else if (nt_tiles == 2)
-    hipLaunchKernelGGL((encode_mfma_kernel<2, MT, KSPLIT>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((encode_mfma_kernel<2, MT, KSPLIT>), grid, block, 0, stream, p, q, ytiles);
   else
-    hipLaunchKernelGGL((encode_mfma_kernel<4, MT, KSPLIT>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((encode_mfma_kernel<4, MT, KSPLIT>), grid, block, 0, stream, p, q, ytiles);
   return hipGetLastError();
 }
 
@@ -511,24 +539,34 @@ bool encode_supported(int dtype, int r) {
   return (dtype == LLA_F32 || dtype == LLA_BF16) && r >= 1 && r <= 512;
 }
 
+namespace {
+
+// bf16 encode on the MFMA kernel for token counts below the tiled GEMM's (pv: a second axis of
+// the same shape and rank in the same launch, or null)
+hipError_t launch_encode_small(const EncodeParams& p, const EncodeParams* pv, hipStream_t stream) {
+  int nt_tiles = p.r <= 16 ? 1 : p.r <= 32 ? 2 : 4;
+  const long ntok = static_cast<long>(p.B) * p.C;
+  // few workgroups with whole-K waves would leave most of the chip idle: split K instead,
+  // eight ways for decode-size token counts, and narrow the latent tiles until the launch has a
+  // workgroup per CU (fewer latent rows per workgroup re-read x more often, from L2)
+  if (ntok <= 256) {
+    auto wgs = [&](int nt) { return (ntok + 15) / 16 * ((p.r + 16 * nt - 1) / (16 * nt)) * p.H; };
+    while (nt_tiles > 1 && wgs(nt_tiles) < 256) nt_tiles /= 2;
+    return launch_encode_mfma<1, 8>(p, pv, nt_tiles, stream);
+  }
+  const long wgs1 = (ntok + 127) / 128 * ((p.r + 16 * nt_tiles - 1) / (16 * nt_tiles)) * p.H;
+  return wgs1 < 1024 ? launch_encode_mfma<2, 4>(p, pv, nt_tiles, stream)
+                     : launch_encode_mfma<2, 1>(p, pv, nt_tiles, stream);
+}
+
+}  // namespace
+
 hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t stream) {
   const int K = p.T * p.d;
   if (dtype == LLA_BF16) {
     if (encode_gemm_ok(p))
       return p.r % 256 == 0 ? launch_encode_gemm<256>(p, stream) : launch_encode_gemm<128>(p, stream);
-    int nt_tiles = p.r <= 16 ? 1 : p.r <= 32 ? 2 : 4;
-    const long ntok = static_cast<long>(p.B) * p.C;
-    // few workgroups with whole-K waves would leave most of the chip idle: split K instead,
-    // eight ways for decode-size token counts, and narrow the latent tiles until the launch has a
-    // workgroup per CU (fewer latent rows per workgroup re-read x more often, from L2)
-    if (ntok <= 256) {
-      auto wgs = [&](int nt) { return (ntok + 15) / 16 * ((p.r + 16 * nt - 1) / (16 * nt)) * p.H; };
-      while (nt_tiles > 1 && wgs(nt_tiles) < 256) nt_tiles /= 2;
-      return launch_encode_mfma<1, 8>(p, nt_tiles, stream);
-    }
-    const long wgs1 = (ntok + 127) / 128 * ((p.r + 16 * nt_tiles - 1) / (16 * nt_tiles)) * p.H;
-    return wgs1 < 1024 ? launch_encode_mfma<2, 4>(p, nt_tiles, stream)
-                       : launch_encode_mfma<2, 1>(p, nt_tiles, stream);
+    return launch_encode_small(p, nullptr, stream);
   }
   if (K > kMaxK) return hipErrorNotSupported;
   const unsigned ntok = static_cast<unsigned>(p.B) * p.C;
@@ -544,6 +582,17 @@ hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t stream) {
        : nt == 2 ? encode_valu_kernel<F32, 2> : encode_valu_kernel<F32, 1>;
   hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, stream, p);
   return hipGetLastError();
+}
+
+// Both axes of a token's encode (K then V). Where the two take the same decode-size MFMA plan
+// (bf16, equal ranks, below the tiled GEMM's token counts) they share one launch, else each has its
+// own.
+hipError_t launch_encode_kv(const EncodeParams& pk, const EncodeParams& pv, int dtype, hipStream_t stream) {
+  if (dtype == LLA_BF16 && pk.r == pv.r && !encode_gemm_ok(pk) && !encode_gemm_ok(pv))
+    return launch_encode_small(pk, &pv, stream);
+  const hipError_t e = launch_encode(pk, dtype, stream);
+  if (e != hipSuccess) return e;
+  return launch_encode(pv, dtype, stream);
 }
 
 }  // namespace lla

@@ -145,6 +145,8 @@ void gather_plan(const lla_desc& desc, int B, int budget, int* splits, int* chun
 size_t gather_workspace_bytes(const lla_desc& desc, int B, int budget);
 hipError_t launch_decode_gather(const DecodeParams& p, int dtype, hipStream_t s);
 hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t s);
+// both axes of one encode call (one launch where their plans match)
+hipError_t launch_encode_kv(const EncodeParams& pk, const EncodeParams& pv, int dtype, hipStream_t s);
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 // Decoupled rotary branch (rope.hip, decode.hip).
 hipError_t launch_rope_write(const RopeWriteParams& p, hipStream_t s);
