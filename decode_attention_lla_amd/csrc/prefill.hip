@@ -118,15 +118,31 @@ __device__ __forceinline__ size_t mofs(const PrefillParams& p, int h) {
 }
 
 // ---- P0: W^K_t[h] [d][RK] -> [RK][d] ------------------------------------------------------------
+// One 32 x 32 tile per workgroup (grid: head, d / 32, RK / 32; d and RK are multiples of 32 on this
+// path) through LDS, so the reads run along RK and the writes along d, 8 bytes per thread each.
 template <int RK>
 __global__ __launch_bounds__(256) void wk_transpose_kernel(PrefillParams p, uint16_t* wkt) {
+  __shared__ uint16_t tile[32][32 + 4];
   const int h = blockIdx.x;
+  const int j0 = blockIdx.y * 32;
+  const int k0 = blockIdx.z * 32;
   const uint16_t* src = static_cast<const uint16_t*>(p.Wk) + wofs(p, h, RK);
   uint16_t* dst = wkt + static_cast<size_t>(h) * RK * p.d;
-  for (int i = threadIdx.x; i < p.d * RK; i += 256) {
-    const int j = i / RK;
-    const int k = i - j * RK;
-    dst[static_cast<size_t>(k) * p.d + j] = src[i];
+  const int t = threadIdx.x;
+  {
+    const int jj = t >> 3, kk = (t & 7) * 4;
+    const uint2 v = *reinterpret_cast<const uint2*>(src + static_cast<size_t>(j0 + jj) * RK + k0 + kk);
+    tile[jj][kk] = static_cast<uint16_t>(v.x);
+    tile[jj][kk + 1] = static_cast<uint16_t>(v.x >> 16);
+    tile[jj][kk + 2] = static_cast<uint16_t>(v.y);
+    tile[jj][kk + 3] = static_cast<uint16_t>(v.y >> 16);
+  }
+  __syncthreads();
+  {
+    const int kk = t >> 3, jj = (t & 7) * 4;
+    const uint2 v = make_uint2(tile[jj][kk] | (static_cast<uint32_t>(tile[jj + 1][kk]) << 16),
+                               tile[jj + 2][kk] | (static_cast<uint32_t>(tile[jj + 3][kk]) << 16));
+    *reinterpret_cast<uint2*>(dst + static_cast<size_t>(k0 + kk) * p.d + j0 + jj) = v;
   }
 }
 
@@ -943,7 +959,7 @@ hipError_t launch_prefill(const PrefillParams& pp, int dtype, hipStream_t stream
     if (prefill_mfma_bytes(pp.B, pp.C, pp.H, pp.d, pp.r_k, pp.r_v) > pp.ws_bytes)
       return hipErrorInvalidValue;  // the plan does not fit the workspace: never launch
     const PrefillWs w = carve(pp.ws);
-    hipLaunchKernelGGL(e->wkt, dim3(pp.H), dim3(256), 0, stream, pp, w.wkt);
+    hipLaunchKernelGGL(e->wkt, dim3(pp.H, pp.d / 32, pp.r_k / 32), dim3(256), 0, stream, pp, w.wkt);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const unsigned nwg = static_cast<unsigned>((pp.C + kRowsWG - 1) / kRowsWG) * pp.H * pp.B;
