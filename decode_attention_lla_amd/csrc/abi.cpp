@@ -180,15 +180,14 @@ lla_status lla_quantize_latents(const lla_desc* desc, int32_t B, int32_t C, cons
   p.C = C;
   p.H = desc->variant == LLA_PER_HEAD ? desc->H : 1;
   p.n_max = desc->n_max;
+  lla::QuantParams pv = p;
   p.src = zk_src;
   p.dst = zk;
   p.r = desc->r_k;
-  lla_status st = from_hip(lla::launch_quantize(p, s));
-  if (st != LLA_OK) return st;
-  p.src = zv_src;
-  p.dst = zv;
-  p.r = desc->r_v;
-  return from_hip(lla::launch_quantize(p, s));
+  pv.src = zv_src;
+  pv.dst = zv;
+  pv.r = desc->r_v;
+  return from_hip(lla::launch_quantize(p, pv, s));
 }
 
 size_t lla_workspace_bytes(const lla_desc* desc, int32_t B, int32_t C) {

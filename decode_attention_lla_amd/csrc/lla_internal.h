@@ -147,7 +147,7 @@ hipError_t launch_decode_gather(const DecodeParams& p, int dtype, hipStream_t s)
 hipError_t launch_encode(const EncodeParams& p, int dtype, hipStream_t s);
 // both axes of one encode call (one launch where their plans match)
 hipError_t launch_encode_kv(const EncodeParams& pk, const EncodeParams& pv, int dtype, hipStream_t s);
-hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+hipError_t launch_quantize(const QuantParams& pk, const QuantParams& pv, hipStream_t stream);
 // Decoupled rotary branch (rope.hip, decode.hip).
 hipError_t launch_rope_write(const RopeWriteParams& p, hipStream_t s);
 bool rope_supported(const lla_desc& desc, int d_rope);

@@ -19,8 +19,20 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One thread per source row (b, h, c): per-head source [B][H][C][r] (LLA-2D: H = 1).
-__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QuantParams p) {
+// One thread per source row (b, h, c): per-head source [B][H][C][r] (LLA-2D: H = 1). Grid y is
+// the axis: the K rows (pk) and the V rows (pv) of one call share a launch.
+__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QuantParams pk, QuantParams pv) {
+  const bool v = blockIdx.y != 0;
+  QuantParams p;  // field by field, so each stays a scalar
+  p.src = v ? pv.src : pk.src;
+  p.dst = v ? pv.dst : pk.dst;
+  p.pos = v ? pv.pos : pk.pos;
+  p.B = v ? pv.B : pk.B;
+  p.C = v ? pv.C : pk.C;
+  p.H = v ? pv.H : pk.H;
+  p.r = v ? pv.r : pk.r;
+  p.n_max = v ? pv.n_max : pk.n_max;
+  p.int8 = v ? pv.int8 : pk.int8;
   const long row = static_cast<long>(blockIdx.x) * kThreads + threadIdx.x;
   const long rows = static_cast<long>(p.B) * p.H * p.C;
   if (row >= rows) return;
@@ -71,10 +83,11 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QuantParams p) 
 
 }  // namespace
 
-hipError_t launch_quantize(const QuantParams& p, hipStream_t stream) {
-  const long rows = static_cast<long>(p.B) * p.H * p.C;
+// pk and pv: the K and V rows of one call (the same B, C, H, n_max and positions)
+hipError_t launch_quantize(const QuantParams& pk, const QuantParams& pv, hipStream_t stream) {
+  const long rows = static_cast<long>(pk.B) * pk.H * pk.C;
   const unsigned blocks = static_cast<unsigned>((rows + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(quantize_rows_kernel, dim3(blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3(blocks, 2), dim3(kThreads), 0, stream, pk, pv);
   return hipGetLastError();
 }
 
