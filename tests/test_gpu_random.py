@@ -220,51 +220,59 @@ def _encode_configs(n, seed=24000):
         B = int(rng.integers(1, 5))
         C = int(rng.choice([1, 3, 64, 300]))
         n_max = C + int(rng.integers(0, 40))
+        r = int(rng.choice([8, 24, 96, 128, 256]))
+        # unequal ranks in some draws: the two axes then take separate launches instead of one
+        rv = r if rng.random() < 0.7 else int(rng.choice([16, 32, 160]))
         out.append(dict(i=i, variant=variant, dtype="bf16" if rng.random() < 0.75 else "f32",
                         H=int(rng.choice([1, 2, 3])), d=int(rng.choice([16, 64, 128])),
-                        T=int(rng.choice([1, 2, 4])), r=int(rng.choice([8, 24, 96, 128, 256])),
+                        T=int(rng.choice([1, 2, 4])), r=r, rv=rv,
                         B=B, C=C, n_max=n_max,
                         pos=[int(x) for x in rng.integers(-3, n_max + 3, B)],
-                        mu=bool(rng.random() < 0.5)))
+                        mu_k=bool(rng.random() < 0.5), mu_v=bool(rng.random() < 0.5)))
     return out
 
 
-@pytest.mark.parametrize("cfg", _encode_configs(12), ids=lambda c: f"cfg{c['i']}")
+@pytest.mark.parametrize("cfg", _encode_configs(16), ids=lambda c: f"cfg{c['i']}")
 def test_encode_random(cfg):
     """Random encode shapes, including write positions before the cache and past its end (rows
     whose slot falls outside [0, n_max) are not written; untouched slots keep their contents)."""
     c = cfg
-    dtype, variant, H, d, T, r, B, C, n_max = (c[k] for k in ("dtype", "variant", "H", "d", "T", "r",
-                                                           "B", "C", "n_max"))
+    dtype, variant, H, d, T, r, rv, B, C, n_max = (c[k] for k in ("dtype", "variant", "H", "d", "T", "r",
+                                                               "rv", "B", "C", "n_max"))
     base = 24100 + 10 * c["i"]
     K = T * d if variant == "per_head" else T * H * d
-    es = (H, r, K) if variant == "per_head" else (r, K)
     ms = (H, K) if variant == "per_head" else (K,)
-    zs = (B, H, n_max, r) if variant == "per_head" else (B, n_max, r)
+
+    def zshape(rank):
+        return (B, H, n_max, rank) if variant == "per_head" else (B, n_max, rank)
+
+    def eshape(rank):
+        return (H, rank, K) if variant == "per_head" else (rank, K)
+
     xk = synth.normal((B, C, T, H, d), base + 1, dtype)
     xv = synth.normal((B, C, T, H, d), base + 2, dtype)
-    Ek = synth.normal(es, base + 3, dtype, 1 / math.sqrt(K))
-    Ev = synth.normal(es, base + 4, dtype, 1 / math.sqrt(K))
-    mk = synth.normal(ms, base + 5, dtype, 0.5)
-    mv = synth.normal(ms, base + 6, dtype, 0.5)
-    z0 = synth.normal(zs, base + 7, dtype)
+    Ek = synth.normal(eshape(r), base + 3, dtype, 1 / math.sqrt(K))
+    Ev = synth.normal(eshape(rv), base + 4, dtype, 1 / math.sqrt(K))
+    mk = synth.normal(ms, base + 5, dtype, 0.5) if c["mu_k"] else None
+    mv = synth.normal(ms, base + 6, dtype, 0.5) if c["mu_v"] else None
+    zk0 = synth.normal(zshape(r), base + 7, dtype)
+    zv0 = synth.normal(zshape(rv), base + 8, dtype)
     pos = np.array(c["pos"], np.int32)
-    desc = mk_desc(variant, dtype, H, d, T, r, r, n_max)
-    zk, zv = dev(z0, dtype), dev(z0, dtype)
+    desc = mk_desc(variant, dtype, H, d, T, r, rv, n_max)
+    zk, zv = dev(zk0, dtype), dev(zv0, dtype)
     lla.lla_encode(desc, B, C, dev(xk, dtype), dev(xv, dtype), dev(Ek, dtype), dev(Ev, dtype),
-                   dev(mk, dtype) if c["mu"] else None, dev(mv, dtype) if c["mu"] else None, dev(pos),
+                   None if mk is None else dev(mk, dtype), None if mv is None else dev(mv, dtype), dev(pos),
                    zk, zv)
     torch.cuda.synchronize()
-    want_k, want_v = z0.astype(np.float64).copy(), z0.astype(np.float64).copy()
-    written = np.zeros(zs[:-1], bool)
+    want_k, want_v = zk0.astype(np.float64).copy(), zv0.astype(np.float64).copy()
+    written = np.zeros(zshape(r)[:-1], bool)
     for b in range(B):
         c0, c1 = max(0, -int(pos[b])), min(C, n_max - int(pos[b]))  # chunk rows whose slot is in range
         if c0 >= c1:
             continue
         sub = slice(b, b + 1)
-        ak, av = O.encode_into_cache(z0[sub], z0[sub], xk[sub, c0:c1], xv[sub, c0:c1], Ek, Ev,
-                                     np.array([pos[b] + c0]), mk if c["mu"] else None,
-                                     mv if c["mu"] else None, variant)
+        ak, av = O.encode_into_cache(zk0[sub], zv0[sub], xk[sub, c0:c1], xv[sub, c0:c1], Ek, Ev,
+                                     np.array([pos[b] + c0]), mk, mv, variant)
         want_k[sub], want_v[sub] = ak, av
         slots = slice(int(pos[b]) + c0, int(pos[b]) + c1)
         if variant == "per_head":
@@ -275,8 +283,8 @@ def test_encode_random(cfg):
     if written.any():
         assert_close(gk[written], want_k[written], dtype, f"encode zk {c}")
         assert_close(gv[written], want_v[written], dtype, f"encode zv {c}")
-    assert np.array_equal(gk[~written], z0.astype(np.float64)[~written])
-    assert np.array_equal(gv[~written], z0.astype(np.float64)[~written])
+    assert np.array_equal(gk[~written], zk0.astype(np.float64)[~written])
+    assert np.array_equal(gv[~written], zv0.astype(np.float64)[~written])
 
 
 # --------------------------------------------------------------------------------------------
