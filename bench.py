@@ -832,6 +832,9 @@ def lla2d_prefill(args):
     att_flops = 2.0 * B * H * keys * 2 * r                   # scores + latent-V products
     proj_flops = 2.0 * B * C * H * d * 2 * r                 # q~ and output projections
     enc_flops = 2.0 * B * C * 2 * r * T * H * d              # both axes
+    # what the kernel issues: q~ and the latent sums enter their products as bf16 hi + lo pairs, so
+    # the score products and the output projection run twice
+    issued_flops = att_flops + proj_flops + 2.0 * B * H * keys * r + 2.0 * B * C * H * d * r
     return {"workload": f"lla2d prefill: C={C} per sequence, B={B}, N_ctx={N}, H={H}, d_head={d}, "
                         f"T={T}, r_k=r_v={r}, bf16",
             "tokens_per_s": round(B * C / (ms_step / 1e3), 1), "ms_per_chunk": round(ms_step, 3),
@@ -839,6 +842,8 @@ def lla2d_prefill(args):
             "attend_with_64_wide_rotary_branch_ms_per_loop": round(ms_rope, 3),
             "attend_TFLOPs": round((att_flops + proj_flops) / (ms_att / 1e3) / 1e12, 1),
             "attend_mfma_util_bf16_dense": round((att_flops + proj_flops) / (ms_att / 1e3) / 2.5e15, 4),
+            "attend_issued_TFLOPs_q_hi_lo": round(issued_flops / (ms_att / 1e3) / 1e12, 1),
+            "attend_issued_frac_bf16_dense": round(issued_flops / (ms_att / 1e3) / 2.5e15, 4),
             "encode_TFLOPs": round(enc_flops / (ms_enc / 1e3) / 1e12, 1),
             "encode_mfma_util_bf16_dense": round(enc_flops / (ms_enc / 1e3) / 2.5e15, 4)}
 
