@@ -377,6 +377,33 @@ def per_head_layer(args, name):
     torch.cuda.synchronize()
     ms_read = float(np.mean([a.elapsed_time(b) for a, b in pairs])) / T
     latent = B * H * N * (rk + rv) * 2
+    # A layer's loop reads re-stream the same latents back to back; when they are about the size of
+    # the 256 MB last-level cache, part of a read comes from it. The same read after a 1 GiB
+    # read-only sweep of another buffer shows the cold figure.
+    # Both are one read timed alone (events around it), after the same read or after the sweep.
+    single = None
+    if latent <= 2 ** 30:
+        sweep = torch.zeros(2 ** 28, dtype=torch.float32, device="cuda")
+
+        def read0():
+            lla.lla_attend_decode(desc, B, 0, q[0], zk, zv, lens, Wk, Wv, None, None, ks[0], vs[0], out[0],
+                                  None, ws, stream)
+
+        def one(before):
+            ts = []
+            for _ in range(20):
+                before()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                read0()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return float(np.median(ts)) * 1e3
+
+        single = (one(read0), one(lambda: sweep.sum()))
+        del sweep
     res = {"workload": f"{name}: 1 layer, H={H}, d_head={d}, T={T}, r_k={rk}, r_v={rv}, B={B}, "
                        f"N={N}, bf16",
            "tokens_per_s": round(B / (ms_step / 1e3), 1), "ms_per_step": round(ms_step, 4),
@@ -384,6 +411,10 @@ def per_head_layer(args, name):
            "latent_GBps": round(latent / (ms_read / 1e3) / 1e9, 1),
            "latent_frac_of_peak": round(latent / (ms_read / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
            "latent_bytes_per_read": latent}
+    if single is not None:
+        res["single_read_us_after_same_read"] = round(single[0], 2)
+        res["single_read_us_after_cache_sweep"] = round(single[1], 2)
+        res["latent_frac_of_peak_after_cache_sweep"] = round(latent / (single[1] / 1e6) / 1e9 / HBM_PEAK_GBS, 4)
     del zk, zv, x, q, ks, vs, out, ws
     torch.cuda.empty_cache()
     return res
